@@ -1,0 +1,464 @@
+"""Pins for the CPU oracle: facts the pages and the mathematics fix, checked
+without trusting the oracle's own formulas (worked examples, closed forms,
+special cases, library routines, brute force on tiny inputs)."""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16_torch(x):
+    """Library route: torch's fp32 -> bf16 conversion (round to nearest even)."""
+    t = torch.from_numpy(np.asarray(x, dtype=np.float32).copy()).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ----------------------------------------------------------------------------- bf16
+def test_bf16_known_values():
+    cases = [(1.0, 0x3F80), (1 + 2 ** -8, 0x3F80), (1 + 3 * 2 ** -8, 0x3F82), (-2.5, 0xC020),
+             (float("inf"), 0x7F80), (-float("inf"), 0xFF80), (3.4e38, 0x7F80), (3.38e38, 0x7F7E),
+             (2.0 ** -133, 0x0001), (2.0 ** -134, 0x0000), (3 * 2.0 ** -134, 0x0002), (0.0, 0x0000),
+             (-0.0, 0x8000), (2.0 ** -126, 0x0080)]
+    for v, want in cases:
+        assert int(oracle.f64_to_bf16(v)) == want, (v, hex(int(oracle.f64_to_bf16(v))))
+    assert int(oracle.f64_to_bf16(float("nan"))) == 0x7FC0
+
+
+def test_bf16_rounding_matches_torch():
+    g = np.random.default_rng(1)
+    x = (g.standard_normal(200000) * np.exp2(g.integers(-140, 128, 200000))).astype(np.float32)
+    # exact ties, to exercise round-half-to-even
+    ties = (np.arange(1, 20001, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    x = x[np.isfinite(x)]
+    assert np.array_equal(oracle.f64_to_bf16(x), bf16_torch(x))
+    assert np.array_equal(oracle.bf16_to_f32(bf16_torch(x)), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+# ----------------------------------------------------------------------------- unpack / dequant
+def _golden_handpacked():
+    rows = []
+    for line in open(os.path.join(GOLD, "handpacked_codes.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        bits, words, codes, deq = [p.strip() for p in line.split("|")]
+        rows.append((int(bits), [int(w, 16) for w in words.split()], [int(c) for c in codes.split()],
+                     [float(d) for d in deq.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("row", _golden_handpacked())
+def test_handpacked_words(row):
+    bits, words, codes, deq = row
+    w = np.array([words], dtype=np.uint32)
+    K = len(codes)
+    assert oracle.unpack(w, K, bits)[0].tolist() == codes
+    # one group covering the row needs K to be a valid group size; use 32 and repeat
+    reps = 32 // K if K < 32 else 1
+    ww = np.tile(w, (1, reps))
+    s = oracle.f64_to_bf16(np.full((1, 1), 0.5))
+    b = oracle.f64_to_bf16(np.full((1, 1), -4.0))
+    got = oracle.dequant(ww, s, b, 32, bits, K * reps)[0]
+    assert got.tolist() == deq * reps
+
+
+def test_dequant_unit_scale_zero_bias_returns_codes():
+    # nuvec "quantize_snaps_zero...": dequantize with ones/zeros yields the raw codes
+    g = np.random.default_rng(2)
+    for bits in (4, 8):
+        for gs in (32, 64, 128):
+            codes = g.integers(0, 1 << bits, size=(5, 256))
+            w = synth.pack(codes, bits)
+            one = oracle.f64_to_bf16(np.ones((5, 256 // gs)))
+            zero = oracle.f64_to_bf16(np.zeros((5, 256 // gs)))
+            assert np.array_equal(oracle.dequant(w, one, zero, gs, bits, 256), codes)
+
+
+def test_dequant_constant_group_and_group_index():
+    # constant group: scale 0, bias c gives c exactly (nuvec: constant groups are exact)
+    w = synth.pack(np.full((2, 128), 7), 4)
+    s = oracle.f64_to_bf16(np.zeros((2, 2)))
+    b = oracle.f64_to_bf16(np.array([[0.75, -1.25], [3.0, 0.0]]))
+    d = oracle.dequant(w, s, b, 64, 4, 128)
+    assert (d[0, :64] == 0.75).all() and (d[0, 64:] == -1.25).all() and (d[1, :64] == 3).all()
+    # element k uses group k // gs: distinct scales per group, code 1 everywhere
+    w = synth.pack(np.ones((1, 256), dtype=np.int64), 4)
+    s = oracle.f64_to_bf16(np.arange(1, 5)[None, :].astype(float))
+    d = oracle.dequant(w, s, oracle.f64_to_bf16(np.zeros((1, 4))), 64, 4, 256)
+    assert d[0].tolist() == [float(k // 64 + 1) for k in range(256)]
+
+
+def test_straddling_widths_unpack():
+    # 3-, 5- and 6-bit codes straddle words; a known bit stream pins them
+    g = np.random.default_rng(3)
+    for bits in (1, 2, 3, 5, 6):
+        codes = g.integers(0, 1 << bits, size=(2, 64))
+        w = synth.pack(codes, bits)
+        stream = "".join(format(int(x), "032b")[::-1] for x in w[0])   # LSB-first bits
+        want = [int(stream[k * bits:(k + 1) * bits][::-1], 2) for k in range(64)]
+        assert oracle.unpack(w, 64, bits)[0].tolist() == want == codes[0].tolist()
+
+
+# ----------------------------------------------------------------------------- quantized matmul
+def _brute_qmm(x_u16, words, s_u16, b_u16, gs, bits, transpose=True):
+    """Triple loop in exact rational arithmetic, codes read off the bit string."""
+    xv = [[Fraction(float(v)) for v in row] for row in oracle.bf16_to_f64(x_u16)]
+    sv = oracle.bf16_to_f64(s_u16)
+    bv = oracle.bf16_to_f64(b_u16)
+    rows = []
+    for wr in words:
+        stream = "".join(format(int(v), "032b")[::-1] for v in wr)
+        rows.append(stream)
+    if transpose:
+        N, K = len(words), len(xv[0])
+        W = [[Fraction(int(rows[n][k * bits:(k + 1) * bits][::-1], 2)) * Fraction(float(sv[n][k // gs]))
+              + Fraction(float(bv[n][k // gs])) for k in range(K)] for n in range(N)]
+        out = [[float(sum(xv[m][k] * W[n][k] for k in range(K))) for n in range(N)] for m in range(len(xv))]
+    else:
+        K = len(words)
+        N = len(words[0]) * 32 // bits
+        W = [[Fraction(int(rows[k][n * bits:(n + 1) * bits][::-1], 2)) * Fraction(float(sv[k][n // gs]))
+              + Fraction(float(bv[k][n // gs])) for n in range(N)] for k in range(K)]
+        out = [[float(sum(xv[m][k] * W[k][n] for k in range(K))) for n in range(N)] for m in range(len(xv))]
+    return oracle.f64_to_bf16(np.array(out))
+
+
+@pytest.mark.parametrize("bits,gs,M,N,K", [(4, 32, 2, 5, 64), (4, 64, 3, 4, 128), (8, 32, 1, 3, 96),
+                                           (8, 128, 2, 2, 128), (3, 32, 1, 3, 64)])
+def test_qmm_brute_force(bits, gs, M, N, K):
+    g = np.random.default_rng(bits * 100 + gs + K)
+    x = synth.to_bf16(g.standard_normal((M, K)))
+    w, s, b = synth.drawn_matrix(g, N, K, gs, bits)
+    got = oracle.quantized_matmul(x, w, s, b, True, gs, bits)
+    assert np.array_equal(got, _brute_qmm(x, w, s, b, gs, bits))
+    # transpose=False: w is [K, N] with groups along N
+    w2, s2, b2 = synth.drawn_matrix(g, K // 2, 64, 32, bits)       # K' = K//2 rows, N' = 64
+    x2 = synth.to_bf16(g.standard_normal((M, K // 2)))
+    got2 = oracle.quantized_matmul(x2, w2, s2, b2, False, 32, bits)
+    assert got2.shape == (M, 64)
+    assert np.array_equal(got2, _brute_qmm(x2, w2, s2, b2, 32, bits, transpose=False))
+
+
+def test_qmm_group_factored_identity():
+    # sum_k x (q s + b) = sum_g ( s_g * sum_{k in g} x q + b_g * sum_{k in g} x )
+    g = np.random.default_rng(5)
+    for bits, gs in ((4, 64), (8, 128), (4, 32)):
+        M, N, K = 3, 40, 512
+        x = synth.to_bf16(g.standard_normal((M, K)))
+        w, s, b = synth.drawn_matrix(g, N, K, gs, bits)
+        codes = np.array([[int(format(int(v), "032b")[::-1][j * bits:(j + 1) * bits][::-1], 2)
+                           for v in row for j in range(32 // bits)] for row in w], dtype=np.float64)
+        xf = synth.from_bf16(x).astype(np.float64)
+        sf = synth.from_bf16(s).astype(np.float64)
+        bf = synth.from_bf16(b).astype(np.float64)
+        G = K // gs
+        xq = np.einsum("mgk,ngk->mng", xf.reshape(M, G, gs), codes.reshape(N, G, gs))
+        sx = xf.reshape(M, G, gs).sum(-1)
+        y = (xq * sf[None]).sum(-1) + sx @ bf.T
+        assert np.array_equal(oracle.quantized_matmul(x, w, s, b, True, gs, bits), oracle.f64_to_bf16(y))
+
+
+def test_qmm_integer_exact_closed_form():
+    g = np.random.default_rng(6)
+    for bits, gs in ((4, 64), (8, 128)):
+        M, N, K = 2, 8, 256
+        w, s, b = synth.integer_exact(g, N, K, gs, bits)
+        x = synth.integer_x(g, M, K)
+        codes = oracle.unpack(w, K, bits)                  # pinned above
+        xi = synth.from_bf16(x).astype(np.int64)
+        bi = (synth.from_bf16(b) * 4).astype(np.int64)     # biases are integers * 2^-2
+        want4 = xi @ codes.T + (xi.reshape(M, K // gs, gs).sum(-1)) @ bi.T   # 4 * exact result
+        want = oracle.f64_to_bf16(want4.astype(np.float64) / 4)
+        assert np.array_equal(oracle.quantized_matmul(x, w, s, b, True, gs, bits), want)
+
+
+def test_expert_routing_closed_form():
+    # expert e has scale 0, bias e+1: y = (e+1) * sum(x), any wrong expert shows bitwise
+    E, N, K, gs = 5, 4, 128, 64
+    w = np.zeros((E, N, K // 8), dtype=np.uint32)
+    s = oracle.f64_to_bf16(np.zeros((E, N, K // gs)))
+    b = oracle.f64_to_bf16(np.broadcast_to(np.arange(1, E + 1)[:, None, None], (E, N, K // gs)).astype(float))
+    g = np.random.default_rng(7)
+    x = synth.integer_x(g, 3, K)
+    rhs = np.array([4, 0, 2, 2, 1])
+    lhs = np.array([0, 1, 2, 0, 1])
+    out = oracle.gather_qmm(x[:, None, :], w, s, b, lhs=lhs, rhs=rhs, gs=gs, bits=4)
+    xs = synth.from_bf16(x).astype(np.float64).sum(-1)
+    for j in range(5):
+        assert np.all(out[j, 0] == oracle.f64_to_bf16((rhs[j] + 1) * xs[lhs[j]]))
+
+
+def test_gather_qmm_selects_batches_and_broadcasts():
+    # nuvec "gather_qmm_selects_batches"
+    g = np.random.default_rng(8)
+    E, N, K = 3, 8, 64
+    W = [synth.drawn_matrix(g, N, K, 32, 4) for _ in range(E)]
+    w, s, b = (np.stack([m[i] for m in W]) for i in range(3))
+    x = synth.to_bf16(g.standard_normal((4, 2, K)))
+    got = oracle.gather_qmm(x, w, s, b, lhs=[3, 0, 2], rhs=[1, 2, 0], gs=32, bits=4)
+    assert got.shape == (3, 2, N)
+    for j, (l, r) in enumerate(zip([3, 0, 2], [1, 2, 0])):
+        assert np.array_equal(got[j], oracle.quantized_matmul(x[l], w[r], s[r], b[r], True, 32, 4))
+    x1 = synth.to_bf16(g.standard_normal((1, 1, K)))
+    assert oracle.gather_qmm(x1, w, s, b, gs=32, bits=4).shape == (3, 1, N)
+    x3 = synth.to_bf16(g.standard_normal((3, 1, K)))
+    got = oracle.gather_qmm(x3, w[:, :, :], s, b, lhs=np.array([[2, 0], [1, 1]]), rhs=np.array([[2, 1]]),
+                            gs=32, bits=4)
+    assert got.shape == (2, 2, 1, N)
+    assert np.array_equal(got[1, 0], oracle.quantized_matmul(x3[1], w[2], s[2], b[2], True, 32, 4))
+    with pytest.raises(ValueError):
+        oracle.gather_qmm(x, w, s, b, lhs=np.array([0.0]), gs=32, bits=4)
+    with pytest.raises(ValueError):
+        oracle.gather_qmm(x, w, s, b, lhs=[3, 0, 2], rhs=[0, 1], gs=32, bits=4)
+
+
+def test_invalid_arguments():
+    # nuvec "invalid_arguments_are_rejected"
+    for kw in (dict(K=64, gs=48, bits=4), dict(K=64, gs=64, bits=7), dict(K=96, gs=64, bits=4),
+               dict(K=64, gs=64, bits=4, packed_cols=4), dict(K=64, gs=32, bits=4, n_groups=1)):
+        with pytest.raises(ValueError):
+            oracle.validate_quant_args(**kw)
+    oracle.validate_quant_args(64, 64, 4, 8, 1)
+
+
+def test_empty_product():
+    # nuvec: an empty product keeps its shape [0, N]
+    g = np.random.default_rng(9)
+    w, s, b = synth.drawn_matrix(g, 16, 64, 64, 4)
+    assert oracle.quantized_matmul(np.zeros((0, 64), np.uint16), w, s, b, True, 64, 4).shape == (0, 16)
+
+
+def test_quantizer_round_trip_bounds():
+    # nuvec "round_trip_error_is_about_half_a_step": single error <= 1.0001 step, mean <= step/2
+    g = np.random.default_rng(10)
+    for bits in (4, 8):
+        for gs in (32, 64, 128):
+            wf = (g.standard_normal((3, 2 * gs)) / 4).astype(np.float32)
+            w, s, b = synth.minmax_quantize(wf, gs, bits)
+            back = oracle.dequant(w, s, b, gs, bits, 2 * gs)
+            orig = synth.from_bf16(synth.to_bf16(wf)).astype(np.float64)
+            step = np.repeat(np.abs(oracle.bf16_to_f64(s)), gs, axis=-1)
+            err = np.abs(back - orig)
+            assert (err <= step * 1.0001).all()
+            assert err.sum() <= step.sum() / 2
+
+
+# ----------------------------------------------------------------------------- SwitchGLU
+def _brute_switch_glu(x, idx, gate, up, down, gs, bits):
+    """Per pair, per output, with math.fsum (correctly rounded sums) and the
+    page's three steps written as scalar Python."""
+    T, H = x.shape
+    top_k = idx.shape[1]
+    xf = oracle.bf16_to_f64(x)
+    out = np.zeros((T, top_k, H), dtype=np.uint16)
+    for t in range(T):
+        for k in range(top_k):
+            e = int(idx[t, k])
+            Wg = oracle.dequant(gate[0][e], gate[1][e], gate[2][e], gs, bits, H)
+            Wu = oracle.dequant(up[0][e], up[1][e], up[2][e], gs, bits, H)
+            I = Wg.shape[0]
+            hv = []
+            for n in range(I):
+                gv = float(oracle.bf16_to_f64(oracle.f64_to_bf16(math.fsum(xf[t] * Wg[n]))))
+                uv = float(oracle.bf16_to_f64(oracle.f64_to_bf16(math.fsum(xf[t] * Wu[n]))))
+                hv.append(float(oracle.bf16_to_f64(oracle.f64_to_bf16(gv / (1.0 + math.exp(-gv)) * uv))))
+            Wd = oracle.dequant(down[0][e], down[1][e], down[2][e], gs, bits, I)
+            out[t, k] = oracle.f64_to_bf16([math.fsum(np.array(hv) * Wd[j]) for j in range(H)])
+    return out
+
+
+def test_switch_glu_tiny_brute_force():
+    sh = synth.TINY
+    ex = synth.expert_set(0, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode="drawn")
+    x = synth.activations(0, 4, sh.H)
+    idx = synth.sorted_topk(0, 4, sh.E, sh.top_k)
+    got = oracle.switch_glu(x, idx, *ex, gs=sh.gs, bits=sh.bits)
+    assert np.array_equal(got, _brute_switch_glu(x, idx, *ex, sh.gs, sh.bits))
+
+
+def test_switch_glu_special_cases():
+    sh = synth.TINY
+    ex = list(synth.expert_set(0, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode="drawn"))
+    x = synth.activations(0, 4, sh.H)
+    idx = synth.sorted_topk(0, 4, sh.E, sh.top_k)
+    # gate = 0 -> silu(0) = 0 -> h = 0 -> y = 0
+    zg = (ex[0][0], np.zeros_like(ex[0][1]), np.zeros_like(ex[0][2]))
+    assert not oracle.switch_glu(x, idx, zg, ex[1], ex[2], gs=sh.gs, bits=sh.bits).any()
+    # silu(g) = g for large g (1 + e^-40 == 1 in float64): constant gate 40 -> h = bf16(40 * u)
+    cg = (ex[0][0], np.zeros_like(ex[0][1]), np.full_like(ex[0][2], oracle.f64_to_bf16(40.0 / sh.H)))
+    xo = oracle.f64_to_bf16(np.ones((4, sh.H)))
+    y1 = oracle.switch_glu(xo, idx, cg, ex[1], ex[2], gs=sh.gs, bits=sh.bits)
+    for t in range(4):
+        for k in range(sh.top_k):
+            e = idx[t, k]
+            Wu = oracle.dequant(ex[1][0][e], ex[1][1][e], ex[1][2][e], sh.gs, sh.bits, sh.H)
+            u = oracle.bf16_to_f64(oracle.f64_to_bf16(Wu.sum(-1)))
+            h = oracle.f64_to_bf16(40.0 * u)
+            Wd = oracle.dequant(ex[2][0][e], ex[2][1][e], ex[2][2][e], sh.gs, sh.bits, sh.I)
+            assert np.array_equal(y1[t, k], oracle.f64_to_bf16(Wd @ oracle.bf16_to_f64(h)))
+
+
+# ----------------------------------------------------------------------------- sort and schedule
+def test_sort_pairs_brute_force_and_invariants():
+    g = np.random.default_rng(11)
+    for T, top_k, E in ((1, 8, 288), (7, 2, 8), (64, 8, 16), (33, 4, 300)):
+        idx = np.stack([np.sort(g.choice(E, top_k, replace=False)) for _ in range(T)])
+        order, lhs, srhs, inv, counts, offsets = oracle.sort_pairs(idx, E)
+        flat = idx.reshape(-1).tolist()
+        want = sorted(range(len(flat)), key=lambda p: (flat[p], p))     # stable by pair index
+        assert order.tolist() == want
+        assert lhs.tolist() == [p // top_k for p in want]
+        assert srhs.tolist() == [flat[p] for p in want]
+        assert (order[inv] == np.arange(len(flat))).all() and (inv[order] == np.arange(len(flat))).all()
+        assert counts.sum() == len(flat) and offsets[-1] == len(flat) and (np.diff(offsets) >= 0).all()
+        assert all(counts[e] == flat.count(e) for e in range(E))
+
+
+def test_schedule_worked_example():
+    lines = {l.split()[0]: l for l in open(os.path.join(GOLD, "schedule_mlx4567.txt")) if not l.startswith("#")}
+    bm = int(lines["bm"].split()[1])
+    counts = [int(v) for v in lines["counts"].split()[1:]]
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    sched = oracle.schedule_tiles(offsets, bm)
+    want = [tuple(int(v) for v in t.split(",")) for t in lines["scheduled"].split(")", 1)[1].split("|")]
+    assert [tuple(t) for t in sched.tolist()] == want
+    tiles, passes = oracle.naive_tiles(offsets, bm)
+    assert passes.tolist() == [int(v) for v in lines["naive_passes"].split()[1:]]
+    assert passes.sum() == 6 and len(sched) == 4
+    per = [[int(v) for v in grp.split(",")] for grp in lines["naive_rows_per_expert"].split(None, 1)[1].split("|")]
+    assert [sum(p) for p in per] == tiles[:, 1].tolist()
+
+
+def test_schedule_random_invariants():
+    g = np.random.default_rng(12)
+    for _ in range(50):
+        E = int(g.integers(1, 40))
+        bm = int(g.choice([16, 32, 64, 128]))
+        counts = g.integers(0, 300, E) * (g.random(E) < 0.7)
+        offsets = np.concatenate([[0], np.cumsum(counts)])
+        P = int(offsets[-1])
+        sched = oracle.schedule_tiles(offsets, bm)
+        assert sched[:, 2].sum() == P if len(sched) else P == 0
+        assert (sched[:, 2] <= bm).all() and (sched[:, 2] > 0).all()
+        for r0, e, v in sched:
+            assert offsets[e] <= r0 and r0 + v <= offsets[e + 1]
+        assert len(sched) == sum(-(-int(c) // bm) for c in counts)
+        _, passes = oracle.naive_tiles(offsets, bm)
+        assert len(sched) <= passes.sum()
+        assert len(sched) <= P // bm + int((counts > 0).sum())
+
+
+# ----------------------------------------------------------------------------- combine
+def _torch_combine(y_sorted, inv, scores, shared):
+    """Library route: torch bf16 arithmetic on the CPU (each op computes in fp32
+    and rounds to bf16; the sum is an explicit fp32 loop)."""
+    T, top_k = scores.shape
+    ys = torch.from_numpy(y_sorted.astype(np.int16)).view(torch.bfloat16)
+    sc = torch.from_numpy(scores.astype(np.int16)).view(torch.bfloat16)
+    iv = torch.from_numpy(inv.astype(np.int64)).view(T, top_k)
+    acc = None
+    for k in range(top_k):
+        p = ys[iv[:, k]] * sc[:, k:k + 1]
+        acc = p.float() if acc is None else acc + p.float()
+    out = acc.to(torch.bfloat16)
+    if shared is not None:
+        out = (out.float() + torch.from_numpy(shared.astype(np.int16)).view(torch.bfloat16).float()).to(torch.bfloat16)
+    return out.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("T,top_k,H", [(5, 8, 64), (3, 1, 16), (17, 2, 40)])
+def test_combine_matches_torch_bf16(T, top_k, H):
+    g = np.random.default_rng(T * 7 + top_k)
+    P = T * top_k
+    y = synth.to_bf16(g.standard_normal((P, H)) * 3)
+    inv = g.permutation(P).astype(np.int32)
+    sc = synth.to_bf16(g.random((T, top_k)))
+    sh = synth.to_bf16(g.standard_normal((T, H)))
+    assert np.array_equal(oracle.combine(y, inv, sc, sh), _torch_combine(y, inv, sc, sh))
+    assert np.array_equal(oracle.combine(y, inv, sc, None), _torch_combine(y, inv, sc, None))
+
+
+def test_combine_special_cases():
+    g = np.random.default_rng(13)
+    T, top_k, H = 6, 4, 32
+    P = T * top_k
+    y = synth.to_bf16(g.standard_normal((P, H)))
+    inv = g.permutation(P).astype(np.int32)
+    # one-hot scores, no shared: the chosen slot's row comes back exactly
+    sc = np.zeros((T, top_k), np.uint16)
+    slot = g.integers(0, top_k, T)
+    sc[np.arange(T), slot] = synth.to_bf16(np.float32(1.0))
+    out = oracle.combine(y, inv, sc, None)
+    for t in range(T):
+        assert np.array_equal(out[t], y[inv[t * top_k + slot[t]]])
+    # top_k = 1 with score 1 is a pure permutation
+    inv1 = g.permutation(T).astype(np.int32)
+    y1 = y[:T]
+    out1 = oracle.combine(y1, inv1, synth.to_bf16(np.ones((T, 1), np.float32)), None)
+    assert np.array_equal(out1, y1[inv1])
+
+
+# ----------------------------------------------------------------------------- rms_norm, shared expert, chain
+def test_rms_norm_against_torch():
+    g = np.random.default_rng(14)
+    x = synth.to_bf16(g.standard_normal((4, 256)) * 3)
+    w = synth.to_bf16(g.standard_normal(256))
+    xt = torch.from_numpy(synth.from_bf16(x).astype(np.float64))
+    wt = torch.from_numpy(synth.from_bf16(w).astype(np.float64))
+    ref = torch.nn.functional.rms_norm(xt, (256,), wt, eps=1e-6).numpy()
+    assert np.array_equal(oracle.rms_norm(x, w, 1e-6), oracle.f64_to_bf16(ref))
+    # constant row c: c / sqrt(c^2 + eps) * w
+    c = oracle.f64_to_bf16(np.full((1, 256), 2.0))
+    assert np.array_equal(oracle.rms_norm(c, w, 1e-6)[0], oracle.f64_to_bf16(2.0 / math.sqrt(4 + 1e-6) * synth.from_bf16(w)))
+
+
+def test_shared_expert_gate_closed_form():
+    # gate row with scale 0, bias 0 -> z = 0 -> sigmoid = 1/2 -> shared = bf16(s / 2) exactly
+    sh = synth.PREFILL
+    g = np.random.default_rng(15)
+    H, I = 128, 64
+    gate, up, down, grow = (synth.drawn_matrix(g, I, H, 64, 4), synth.drawn_matrix(g, I, H, 64, 4),
+                            synth.drawn_matrix(g, H, I, 64, 4), synth.drawn_matrix(g, 1, H, 64, 4))
+    grow0 = (grow[0], np.zeros_like(grow[1]), np.zeros_like(grow[2]))
+    x = synth.to_bf16(g.standard_normal((3, H)))
+    full = oracle.shared_expert(x, gate, up, down, grow0, 64, 4)
+    swiglu = oracle.switch_glu(x, np.zeros((3, 1), np.int32), *[tuple(a[None] for a in m) for m in (gate, up, down)],
+                               gs=64, bits=4)[:, 0]
+    assert np.array_equal(full, oracle.f64_to_bf16(oracle.bf16_to_f64(swiglu) / 2))
+
+
+def test_dense_forward_constant_weights_closed_form():
+    """One layer with constant weights (scale 0, bias c): every projection is
+    c * sum(input) broadcast along N, so the chain reduces to scalars per row."""
+    d = dict(hidden=64, q_out=128, kv_out=64, inter=96, layers=1, sets=1)
+    dims = synth.dense_dims(d)
+    consts = {"q": 0.5, "k": 0.25, "v": -0.125, "o": 0.0625, "g": 0.03125, "u": -0.5, "dn": 0.25}
+    L = {}
+    for name, (N, K) in dims.items():
+        L[name] = (np.zeros((N, K // 8), np.uint32), oracle.f64_to_bf16(np.zeros((N, K // 32))),
+                   oracle.f64_to_bf16(np.full((N, K // 32), consts[name])))
+    g = np.random.default_rng(16)
+    h0 = synth.to_bf16(g.standard_normal((2, 64)))
+    nw = oracle.f64_to_bf16(np.ones(64))
+    got = oracle.dense_forward(h0, [L], 1, nw, gs=32, bits=4)
+    r = lambda v: float(oracle.bf16_to_f64(oracle.f64_to_bf16(v)))
+    for m in range(2):
+        hrow = oracle.bf16_to_f64(h0[m])
+        xs = oracle.bf16_to_f64(oracle.rms_norm(h0[m:m + 1], nw))[0].sum()
+        q, k, v = r(0.5 * xs), r(0.25 * xs), r(-0.125 * xs)
+        oin = r(q + r(k + v))
+        o = r(0.0625 * oin * 128)
+        h1 = oracle.bf16_to_f64(oracle.f64_to_bf16(hrow + o))
+        x2 = oracle.bf16_to_f64(oracle.rms_norm(oracle.f64_to_bf16(h1)[None], nw))[0].sum()
+        gg, uu = r(0.03125 * x2), r(-0.5 * x2)
+        a = r(gg / (1 + math.exp(-gg)) * uu)
+        dn = r(0.25 * a * 96)
+        assert np.array_equal(got[m], oracle.f64_to_bf16(h1 + dn))

@@ -1,0 +1,264 @@
+/*
+ * moegq -- gathered affine-quantized MoE expert matmul for AMD MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument is a device pointer owned by the caller unless
+ * stated otherwise; the library never allocates, frees or retains memory.  Every entry
+ * point except moegq_selfcheck and moegq_validate_indices is asynchronous on
+ * `stream` (a hipStream_t passed as void*; NULL = the default stream): it only
+ * validates its arguments on the host and enqueues kernels; it never
+ * synchronizes and never reads device memory back.  Outputs are valid once the
+ * stream reaches that point.
+ *
+ * Errors: the return value is MOEGQ_OK (0) or a negative moegq_status.  On any
+ * argument error nothing is launched and outputs are untouched.  Empty inputs
+ * (zero pairs / rows / tokens) return MOEGQ_OK with no launch.
+ *
+ * Index preconditions that would need a device->host read to check are the
+ * caller's: 0 <= expert index < E, 0 <= row index < rows of x, and a truthful
+ * `sorted_indices` hint.  moegq_validate_indices checks them (synchronizing).
+ *
+ * Formats (the pages' packed affine layout):
+ *   packed weights  uint32 [E, N, K*bits/32]; code k of a row sits at bit
+ *                   offset k*bits of the row's little-endian word stream
+ *                   (LSB first);
+ *   scales, biases  bf16   [E, N, K/group_size]; w = q*scale + bias;
+ *   activations     bf16, row-major.
+ * Sources: nuvec-core tests/quantized.rs ("round_trip_error_is_about_half_a_step",
+ * "composed"); MLX issue 4509 (benchmark script, gq()).
+ */
+#ifndef MOEGQ_H
+#define MOEGQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOEGQ_OK = 0,
+  MOEGQ_ERR_NULL_ARG = -1,     /* a required pointer is NULL                       */
+  MOEGQ_ERR_BITS = -2,         /* bit width outside the supported set              */
+  MOEGQ_ERR_GROUP_SIZE = -3,   /* group size outside {32, 64, 128}                 */
+  MOEGQ_ERR_SHAPE = -4,        /* K % group_size, packed width, inner size, counts */
+  MOEGQ_ERR_DTYPE = -5,        /* integer activations, non-u32 packed words,
+                                  float indices                                    */
+  MOEGQ_ERR_UNSUPPORTED = -6,  /* valid for the format but not built here
+                                  (transpose=0, f16/f32/f64 activations)           */
+  MOEGQ_ERR_WORKSPACE = -7,    /* workspace NULL or smaller than required          */
+  MOEGQ_ERR_LAUNCH = -8,       /* a kernel launch failed (hipGetLastError)         */
+  MOEGQ_ERR_SELFCHECK = -9,    /* fused combine differs from the unfused tail      */
+  MOEGQ_ERR_INDEX = -10,       /* moegq_validate_indices found a bad index         */
+  MOEGQ_ERR_ALIGN = -11        /* activations, packed weights, outputs and
+                                  workspaces must be 16-byte aligned               */
+} moegq_status;
+
+/* dtype codes for the checked operands */
+typedef enum {
+  MOEGQ_BF16 = 0, MOEGQ_F16 = 1, MOEGQ_F32 = 2, MOEGQ_F64 = 3,
+  MOEGQ_I32 = 4, MOEGQ_U32 = 5, MOEGQ_I64 = 6
+} moegq_dtype;
+
+/* switch_glu modes */
+enum { MOEGQ_MODE_AUTO = 0, MOEGQ_MODE_DECODE = 1, MOEGQ_MODE_SORTED = 2 };
+/* row-tile modes of the sorted route */
+enum { MOEGQ_TILES_SCHEDULED = 0, MOEGQ_TILES_NAIVE = 1 };
+/* operations whose workspace can be queried */
+enum { MOEGQ_OP_GATHER_QMM = 0, MOEGQ_OP_SWITCH_GLU_DECODE = 1, MOEGQ_OP_SWITCH_GLU_SORTED = 2,
+       MOEGQ_OP_COMBINE_UNFUSED = 3, MOEGQ_OP_SELFCHECK = 4, MOEGQ_OP_SORT_PAIRS = 5 };
+
+const char* moegq_status_string(int status);
+const char* moegq_version(void);
+
+/* Bytes of workspace an operation needs.  Arguments not used by `op` are
+ * ignored: GATHER_QMM(P, E, N=M rows per batch, bm ignored),
+ * SWITCH_GLU_DECODE(P pairs, E, N = I, bm), SWITCH_GLU_SORTED(P, E, N = I, bm; bm 0 = auto),
+ * COMBINE_UNFUSED(P = T*top_k, E ignored, N = H), SELFCHECK(all ignored),
+ * SORT_PAIRS(P, E).  Returns 0 for an unknown op. */
+size_t moegq_workspace_bytes(int op, int64_t P, int64_t E, int64_t N, int bm);
+
+/*
+ * gather_qmm: out[p] = x[lhs(p)] . dequant(w[rhs[p]])^T  for p in [0, P).
+ *   MLX issue 4509, gq(): gather_qmm(x, w, scales, biases, rhs_indices,
+ *   transpose, group_size, bits, sorted_indices); nuvec "gather_qmm_selects_batches"
+ *   adds lhs_indices (each output batch = quantized_matmul of the selected x
+ *   batch and weight batch).
+ * x        [X, M, K] activations (x_dtype; bf16 only here).
+ * w        [E, N, K*bits/32] uint32 (w_dtype must be MOEGQ_U32);
+ * scales, biases [E, N, K/group_size] bf16.
+ * lhs_indices [P] (idx_dtype I32 or U32) or NULL -> lhs(p) = p / lhs_div
+ *          (lhs_div >= 1; P1's x[M,1,1,K] with idx[M,top_k] is lhs_div = top_k).
+ * rhs_indices [P] expert per pair (same idx_dtype), required.
+ * sorted_indices  hint that rhs is non-decreasing; with M == 1 it selects the
+ *          expert-grouped MFMA route (needs workspace).
+ * transpose must be 1 (0 -> MOEGQ_ERR_UNSUPPORTED).
+ * out      [P, M, N] bf16.
+ * workspace/workspace_bytes: moegq_workspace_bytes(MOEGQ_OP_GATHER_QMM, P, E, M, 0)
+ *          bytes (0 when the route needs none; then NULL is accepted).
+ */
+int moegq_gather_qmm(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K,
+                     const void* w, int w_dtype, const void* scales, const void* biases,
+                     int64_t E, int64_t N,
+                     const void* lhs_indices, int64_t lhs_div, const void* rhs_indices,
+                     int idx_dtype, int64_t P, int sorted_indices, int transpose,
+                     int group_size, int bits, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gather_qmm_glu: h[p] = bf16( silu(g) * u ) with g = x[lhs(p)] . dequant(wg[rhs[p]])^T
+ * and u = x[lhs(p)] . dequant(wu[rhs[p]])^T, g and u rounded to bf16 first:
+ * the gate/up half of SwitchGLU over gathered experts (MLX issue 4509, moe():
+ * up and gate are gather_qmm outputs, then g * sigmoid(g) * u).  Arguments as
+ * moegq_gather_qmm with two weight triples (both [E, N, K*bits/32] u32 and
+ * [E, N, K/group_size] bf16); out [P, M, N] bf16; transpose is implied.
+ */
+int moegq_gather_qmm_glu(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K,
+                         const void* wg, const void* sg, const void* bg,
+                         const void* wu, const void* su, const void* bu,
+                         int64_t E, int64_t N, const void* lhs_indices, int64_t lhs_div,
+                         const void* rhs_indices, int idx_dtype, int64_t P, int sorted_indices,
+                         int group_size, int bits, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * affine_qmm: out = x . dequant(w)^T, x [M, K] bf16, w [N, K*bits/32] u32,
+ * scales/biases [N, K/group_size] bf16, out [M, N] bf16.
+ *   nuvec "quantized_matmul_equals_the_dequantized_product"; MLX PR 4787
+ *   (few-row affine quantized_matmul, 3-16 rows).
+ * residual: NULL, or [M, N] bf16 added after rounding:
+ *   out = bf16(residual + bf16(x . W^T)) (the decoder chain's residual add,
+ *   MLX PR 4787 benchmark script).  out may alias residual.
+ */
+int moegq_affine_qmm(const void* x, int x_dtype, int64_t M, int64_t K,
+                     const void* w, int w_dtype, const void* scales, const void* biases,
+                     int64_t N, int transpose, int group_size, int bits,
+                     const void* residual, void* out, void* stream);
+
+/*
+ * affine_qmm_glu: out = bf16( silu(x . Wg^T) * (x . Wu^T) ), the dense SwiGLU
+ * front half (MLX issue 4509: "up, gate, silu(gate)*up"; MLX PR 4787 script:
+ * g * sigmoid(g) * u).  Wg, Wu [N, K*bits/32], scales/biases [N, K/gs].
+ */
+int moegq_affine_qmm_glu(const void* x, int64_t M, int64_t K,
+                         const void* wg, const void* sg, const void* bg,
+                         const void* wu, const void* su, const void* bu,
+                         int64_t N, int group_size, int bits, void* out, void* stream);
+
+/*
+ * switch_glu: the routed-expert chain of a MoE layer (MLX issue 4509, moe():
+ * up, gate, silu(gate)*up, down over gathered experts; MTPLX PR 558 Change:
+ * the sorted chain sorts the (token, slot) pairs by expert, runs the experts on
+ * the sorted rows and returns the sorted output with its inverse permutation).
+ * x [T, H] bf16; idx [T, top_k] int32 expert ids (0 <= id < E);
+ * gate/up: w [E, I, H*bits/32] u32, s/b [E, I, H/gs] bf16;
+ * down:    w [E, H, I*bits/32] u32, s/b [E, H, I/gs] bf16.
+ * mode DECODE: y [T*top_k, H] in token order (pair p = t*top_k + k); inv, if
+ *   not NULL, receives the identity permutation.
+ * mode SORTED: y [T*top_k, H] in expert-sorted order; inv [T*top_k] receives
+ *   the inverse permutation (pair -> sorted row), required.
+ * mode AUTO: resolves to DECODE or SORTED as moegq_switch_glu_mode() says;
+ *   inv is then required, so the caller's combine works for either layout.
+ * tile_mode: SCHEDULED (expert-aware tiles, MLX PR 4567) or NAIVE (fixed row
+ *   tiles, one K pass per expert present); bm: row-tile height (16/32/64/128),
+ *   0 = auto.
+ * workspace: moegq_workspace_bytes(MOEGQ_OP_SWITCH_GLU_{DECODE,SORTED}, T*top_k, E, I, bm).
+ */
+int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
+                     const int32_t* idx, int64_t top_k,
+                     const void* wg, const void* sg, const void* bg,
+                     const void* wu, const void* su, const void* bu,
+                     const void* wd, const void* sd, const void* bd,
+                     int group_size, int bits, int mode, int tile_mode, int bm,
+                     void* y, int32_t* inv, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* The mode AUTO resolves to for T*top_k pairs over E experts (DECODE or SORTED). */
+int moegq_switch_glu_mode(int64_t T, int64_t top_k, int64_t E);
+
+/*
+ * moe_combine (fused, one pass): MTPLX PR 558 Summary/Motivation -- unsort,
+ * multiply by the routing scores, sum over top_k and add the gated shared
+ * expert in one pass, with the rounding of the unfused tail:
+ *   out[t] = bf16( bf16( sum_k bf16(y[inv[t*top_k+k]] * score[t,k]) ) + shared[t] )
+ * Each bf16 op is evaluated in fp32 and rounded to nearest even; the sum over
+ * k starts at slot 0 and adds slots in order in fp32.
+ * y [T*top_k, H] bf16; inv [T*top_k] int32 or NULL (= identity, token order);
+ * scores [T, top_k] bf16; shared [T, H] bf16 or NULL; out [T, H] bf16.
+ * Bit-identical to moegq_moe_combine_unfused on the same inputs.
+ */
+int moegq_moe_combine(const void* y, const int32_t* inv, const void* scores, const void* shared,
+                      int64_t T, int64_t top_k, int64_t H, void* out, void* stream);
+
+/*
+ * moe_combine_unfused: the same arithmetic as four kernels that each write a
+ * bf16 tensor (unsort -> [T, top_k, H], x score -> [T, top_k, H], sum -> [T, H],
+ * + shared -> out), as the stock tail does (MTPLX PR 558 Motivation).
+ * scratch: moegq_workspace_bytes(MOEGQ_OP_COMBINE_UNFUSED, T*top_k, 0, H, 0) bytes.
+ */
+int moegq_moe_combine_unfused(const void* y, const int32_t* inv, const void* scores,
+                              const void* shared, int64_t T, int64_t top_k, int64_t H,
+                              void* out, void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * sort_pairs: stable sort of the flattened (token, slot) pairs by expert
+ * (MTPLX PR 558 Change, "_gather_sort"; MLX PR 4567: offsets precomputed from
+ * rhs_indices).  idx [T, top_k] (I32/U32).  Outputs (all int32, device):
+ * order [P] (sorted row -> pair p = t*top_k + k; ties keep pair order),
+ * lhs [P] = order / top_k, sorted_rhs [P], inv [P] (pair -> sorted row),
+ * counts [E], offsets [E+1] (exclusive prefix of counts).  Any output except
+ * inv, counts and offsets may be NULL.  E <= 1024.
+ * workspace: moegq_workspace_bytes(MOEGQ_OP_SORT_PAIRS, P, E, 0, 0) (0 today).
+ */
+int moegq_sort_pairs(const void* idx, int idx_dtype, int64_t T, int64_t top_k, int64_t E,
+                     int32_t* order, int32_t* lhs, int32_t* sorted_rhs, int32_t* inv,
+                     int32_t* counts, int32_t* offsets, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * schedule_tiles: row tiles over expert-sorted rows from offsets [E+1].
+ * SCHEDULED (MLX PR 4567 Proposed changes, schedule_row_tile): for e ascending
+ *   and j < ceil(c_e/bm): tile = (offsets[e] + j*bm, e, min(bm, c_e - j*bm)).
+ * NAIVE: tile t = (t*bm, -1, min(bm, P - t*bm)).
+ * tiles [cap, 3] int32 (row_start, expert, valid_rows); *n_tiles (device int32)
+ * receives the tile count.  cap must be >= the upper bound
+ * ceil(P/bm) + min(E, P) (P = offsets[E] is not known on the host: pass P_max).
+ */
+int moegq_schedule_tiles(const int32_t* offsets, int64_t E, int64_t P_max, int bm, int tile_mode,
+                         int32_t* tiles, int64_t cap, int32_t* n_tiles, void* stream);
+
+/* rms_norm: out = bf16( x / sqrt(mean(x^2) + eps) * w ), x [M, K], w [K]
+ * (MLX PR 4787 benchmark script, mx.fast.rms_norm). */
+int moegq_rms_norm(const void* x, const void* w, int64_t M, int64_t K, float eps, void* out,
+                   void* stream);
+
+/* sigmoid_gate: out = bf16( sigmoid(z[t]) * s[t, :] ), z [T] (stride z_stride) bf16,
+ * s [T, H] bf16: the shared expert's sigmoid gate (MTPLX PR 558 Summary). */
+int moegq_sigmoid_gate(const void* s, const void* z, int64_t z_stride, int64_t T, int64_t H,
+                       void* out, void* stream);
+
+/* kv_feed: out = bf16( q + bf16(k[:, 0] + v[:, 0]) ), q [M, Nq], k [M, Nk], v [M, Nv]
+ * (MLX PR 4787 benchmark script: o is applied to q + (k[:, :1] + v[:, :1])). */
+int moegq_kv_feed(const void* q, const void* k, const void* v, int64_t M, int64_t Nq,
+                  int64_t Nk, int64_t Nv, void* out, void* stream);
+
+/*
+ * selfcheck: runs the fused and the unfused combine on seeded data of 128
+ * rows, top-8, hidden 2048 (MTPLX PR 558: the bitwise self-check lane at that
+ * geometry) and compares them bit for bit.  Synchronizes.  Returns MOEGQ_OK or
+ * MOEGQ_ERR_SELFCHECK.  workspace: moegq_workspace_bytes(MOEGQ_OP_SELFCHECK,...).
+ * Setting the environment variable MOEGQ_FORCE_SELFCHECK_FAIL=1 makes it
+ * report a failure (for testing the fallback).
+ */
+int moegq_selfcheck(void* workspace, size_t workspace_bytes, void* stream);
+
+/* validate_indices: synchronizing debug check that every idx[i] (i < n,
+ * int32) lies in [0, E); if `sorted` also that idx is non-decreasing.
+ * workspace: 4 bytes of device memory.  Returns MOEGQ_OK or MOEGQ_ERR_INDEX. */
+int moegq_validate_indices(const int32_t* idx, int64_t n, int64_t E, int sorted,
+                           int32_t* workspace, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEGQ_H */

@@ -1,0 +1,358 @@
+"""Python binding of libmoegq (gathered affine-quantized MoE expert path, gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libmoegq.so``.  PyTorch supplies device memory (tensors) and the
+current HIP stream.  There is no CPU fallback: without the built library the
+import of any op raises.
+
+Tensor conventions: bf16 activations/scales/biases are ``torch.bfloat16``;
+packed words are ``torch.int32`` or ``torch.uint32`` holding the uint32 bit
+patterns; indices are ``torch.int32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
+           "switch_glu", "switch_glu_mode", "moe_combine", "moe_combine_unfused", "sort_pairs",
+           "schedule_tiles", "rms_norm", "sigmoid_gate", "kv_feed", "selfcheck",
+           "validate_indices", "workspace_bytes", "MODE_AUTO", "MODE_DECODE", "MODE_SORTED",
+           "TILES_SCHEDULED", "TILES_NAIVE"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmoegq.so")
+
+OK = 0
+BF16, F16, F32, F64, I32, U32, I64 = range(7)
+MODE_AUTO, MODE_DECODE, MODE_SORTED = 0, 1, 2
+TILES_SCHEDULED, TILES_NAIVE = 0, 1
+OP_GATHER_QMM, OP_SWITCH_GLU_DECODE, OP_SWITCH_GLU_SORTED, OP_COMBINE_UNFUSED, OP_SELFCHECK, OP_SORT_PAIRS = range(6)
+
+_DTYPE = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.float64: F64,
+          torch.int32: I32, torch.int64: I64}
+if hasattr(torch, "uint32"):
+    _DTYPE[torch.uint32] = U32
+
+
+class MoegqError(ValueError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {lib().moegq_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+_LIB = None
+_i64, _int, _p, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGS = {
+    "moegq_status_string": ([_int], ctypes.c_char_p),
+    "moegq_version": ([], ctypes.c_char_p),
+    "moegq_workspace_bytes": ([_int, _i64, _i64, _i64, _int], _sz),
+    "moegq_gather_qmm": ([_p, _int, _i64, _i64, _i64, _p, _int, _p, _p, _i64, _i64, _p, _i64, _p, _int, _i64,
+                          _int, _int, _int, _int, _p, _p, _sz, _p], _int),
+    "moegq_gather_qmm_glu": ([_p, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _int,
+                              _i64, _int, _int, _int, _p, _p, _sz, _p], _int),
+    "moegq_affine_qmm": ([_p, _int, _i64, _i64, _p, _int, _p, _p, _i64, _int, _int, _int, _p, _p, _p], _int),
+    "moegq_affine_qmm_glu": ([_p, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _int, _int, _p, _p], _int),
+    "moegq_switch_glu": ([_p, _i64, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _int, _int,
+                          _int, _int, _int, _p, _p, _p, _sz, _p], _int),
+    "moegq_switch_glu_mode": ([_i64, _i64, _i64], _int),
+    "moegq_moe_combine": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _p], _int),
+    "moegq_moe_combine_unfused": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _sz, _p], _int),
+    "moegq_sort_pairs": ([_p, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _sz, _p], _int),
+    "moegq_schedule_tiles": ([_p, _i64, _i64, _int, _int, _p, _i64, _p, _p], _int),
+    "moegq_rms_norm": ([_p, _p, _i64, _i64, ctypes.c_float, _p, _p], _int),
+    "moegq_sigmoid_gate": ([_p, _p, _i64, _i64, _i64, _p, _p], _int),
+    "moegq_kv_feed": ([_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p], _int),
+    "moegq_selfcheck": ([_p, _sz, _p], _int),
+    "moegq_validate_indices": ([_p, _i64, _i64, _int, _p, _p], _int),
+}
+
+
+def lib():
+    """The loaded libmoegq.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise ImportError(f"{library_path} is missing: build it with "
+                              "`python -m moe_expert_gathered_amd.build` (there is no CPU fallback)")
+        L = ctypes.CDLL(library_path)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise MoegqError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t) -> int:
+    return _DTYPE.get(t.dtype, -1)
+
+
+def _wdt(t) -> int:
+    # packed words travel as int32 or uint32 tensors holding the uint32 bits
+    return U32 if t.dtype in (torch.int32, getattr(torch, "uint32", torch.int32)) else _dt(t)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("moegq ops take device tensors")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("moegq ops take contiguous tensors")
+
+
+def workspace_bytes(op: int, P: int, E: int, N: int, bm: int = 0) -> int:
+    return int(lib().moegq_workspace_bytes(op, P, E, N, bm))
+
+
+def _workspace(nbytes: int, device):
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+# ----------------------------------------------------------------------------- ops
+def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, transpose=True,
+               group_size=64, bits=4, sorted_indices=False, out=None):
+    """out[j] = x[lhs[j]] . dequant(w[rhs[j]])^T over the broadcast index shape.
+
+    x: [*bx, M, K]; w: [E, N, K*bits/32] (or [*bw, N, Kw], flattened to E).
+    With x of shape [B, 1, 1, K] and rhs [B, top_k] (the MoE decode layout)
+    the x row of pair (b, k) is b, passed as lhs_div = top_k without building
+    an index array.  Otherwise indices are broadcast (marshalling only).
+    Output: index shape + [M, N].
+    """
+    _dev(x, w, scales, biases, rhs_indices, lhs_indices)
+    M, K = x.shape[-2], x.shape[-1]
+    xb, wb = tuple(x.shape[:-2]), tuple(w.shape[:-2])
+    X = 1
+    for d in xb:
+        X *= d
+    E = 1
+    for d in wb:
+        E *= d
+    N = w.shape[-2] if transpose else w.shape[-1] * 32 // bits
+    lhs_div = 1
+    li = None
+    if rhs_indices is None:
+        rhs_indices = torch.arange(E, dtype=torch.int32, device=x.device).reshape(wb if wb else (1,))
+    if lhs_indices is None:
+        shape = tuple(torch.broadcast_shapes(xb, tuple(rhs_indices.shape)))
+        bxp = (1,) * (len(shape) - len(xb)) + xb
+        j = len(shape)
+        while j > 0 and bxp[j - 1] == 1:
+            j -= 1
+        if tuple(bxp[:j]) == tuple(shape[:j]):
+            # x's batch is a prefix of the index shape: the x row of flat pair p is p // prod(shape[j:])
+            d = 1
+            for v in shape[j:]:
+                d *= v
+            lhs_div = d
+        else:
+            lhs_full = torch.arange(X, dtype=rhs_indices.dtype, device=x.device).reshape(xb if xb else (1,))
+            li = lhs_full.expand(shape).reshape(-1).contiguous()
+        ri = rhs_indices.expand(shape).reshape(-1).contiguous()
+    else:
+        lb, rb = torch.broadcast_tensors(lhs_indices, rhs_indices)
+        shape = tuple(lb.shape)
+        li, ri = lb.reshape(-1).contiguous(), rb.reshape(-1).contiguous()
+    P = int(ri.numel())
+    idx_dt = _dt(ri)
+    if li is not None and li.dtype != ri.dtype:
+        raise ValueError("lhs and rhs indices must share a dtype")
+    if out is None:
+        out = torch.empty(shape + (M, N), dtype=torch.bfloat16, device=x.device)
+    ws, wsb = _workspace(workspace_bytes(OP_GATHER_QMM, P, E, M, 0), x.device)
+    st = lib().moegq_gather_qmm(_ptr(x), _dt(x), X, M, K, _ptr(w), _wdt(w), _ptr(scales), _ptr(biases), E, N,
+                                _ptr(li), lhs_div, _ptr(ri), idx_dt, P, int(bool(sorted_indices)),
+                                int(bool(transpose)), group_size, bits, _ptr(out), _ptr(ws), wsb, _stream())
+    _check(st, "gather_qmm")
+    return out
+
+
+def gather_qmm_glu(x, gate, up, rhs_indices, lhs_indices=None, lhs_div=1, group_size=64, bits=4,
+                   sorted_indices=False, out=None):
+    """h[p] = bf16(silu(g) * u) over gathered experts, g/u = x[row(p)] . W[rhs[p]]^T.
+    x: [X, M, K] (or [X, K] for M = 1); gate/up: (words [E, N, Kw], scales, biases);
+    rhs_indices [P]; the x row of pair p is lhs_indices[p], or p // lhs_div."""
+    _dev(x, *gate, *up, rhs_indices, lhs_indices)
+    if x.dim() == 2:
+        X, K = x.shape
+        M = 1
+    else:
+        X, M, K = x.shape
+    E, N = gate[0].shape[0], gate[0].shape[1]
+    P = rhs_indices.numel()
+    if out is None:
+        out = torch.empty((P, M, N), dtype=torch.bfloat16, device=x.device)
+    ws, wsb = _workspace(workspace_bytes(OP_GATHER_QMM, P, E, M, 0), x.device)
+    st = lib().moegq_gather_qmm_glu(_ptr(x), _dt(x), X, M, K, *[_ptr(t) for t in gate], *[_ptr(t) for t in up], E,
+                                    N, _ptr(lhs_indices), lhs_div, _ptr(rhs_indices), _dt(rhs_indices), P,
+                                    int(bool(sorted_indices)), group_size, bits, _ptr(out), _ptr(ws), wsb,
+                                    _stream())
+    _check(st, "gather_qmm_glu")
+    return out
+
+
+def affine_qmm(x, w, scales, biases, group_size=64, bits=4, transpose=True, residual=None, out=None):
+    """out = x . dequant(w)^T (+ residual after rounding).  x [M, K], w [N, Kw]."""
+    _dev(x, w, scales, biases, residual)
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    st = lib().moegq_affine_qmm(_ptr(x), _dt(x), M, K, _ptr(w), _wdt(w), _ptr(scales), _ptr(biases), N,
+                                int(bool(transpose)), group_size, bits, _ptr(residual), _ptr(out), _stream())
+    _check(st, "affine_qmm")
+    return out
+
+
+def affine_qmm_glu(x, gate, up, group_size=64, bits=4, out=None):
+    """bf16(silu(x . Wg^T) * (x . Wu^T)); gate/up are (words, scales, biases)."""
+    _dev(x, *gate, *up)
+    M, K = x.shape
+    N = gate[0].shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    st = lib().moegq_affine_qmm_glu(_ptr(x), M, K, *[_ptr(t) for t in gate], *[_ptr(t) for t in up], N,
+                                    group_size, bits, _ptr(out), _stream())
+    _check(st, "affine_qmm_glu")
+    return out
+
+
+def switch_glu_mode(T: int, top_k: int, E: int) -> int:
+    return int(lib().moegq_switch_glu_mode(T, top_k, E))
+
+
+def switch_glu(x, idx, gate, up, down, group_size=64, bits=4, mode=MODE_AUTO, tile_mode=TILES_SCHEDULED,
+               bm=0, y=None, inv=None):
+    """Routed SwitchGLU.  Returns (y [T*top_k, H], inv [T*top_k] or None, mode used).
+    DECODE: y in token order; SORTED: y expert-sorted and inv the inverse permutation."""
+    _dev(x, idx, *gate, *up, *down)
+    T, H = x.shape
+    top_k = idx.shape[1]
+    E, I = gate[0].shape[0], gate[0].shape[1]
+    P = T * top_k
+    if mode == MODE_AUTO:
+        mode = switch_glu_mode(T, top_k, E)
+    if y is None:
+        y = torch.empty((P, H), dtype=torch.bfloat16, device=x.device)
+    if inv is None and mode == MODE_SORTED:
+        inv = torch.empty(P, dtype=torch.int32, device=x.device)
+    op = OP_SWITCH_GLU_SORTED if mode == MODE_SORTED else OP_SWITCH_GLU_DECODE
+    ws, wsb = _workspace(workspace_bytes(op, P, E, I, bm), x.device)
+    st = lib().moegq_switch_glu(_ptr(x), T, H, I, E, _ptr(idx), top_k, *[_ptr(t) for t in gate],
+                                *[_ptr(t) for t in up], *[_ptr(t) for t in down], group_size, bits, mode,
+                                tile_mode, bm, _ptr(y), _ptr(inv), _ptr(ws), wsb, _stream())
+    _check(st, "switch_glu")
+    return y, inv, mode
+
+
+def moe_combine(y, inv, scores, shared=None, out=None):
+    """Fused unsort * score, sum over top_k, + shared (one pass)."""
+    _dev(y, inv, scores, shared)
+    T, top_k = scores.shape
+    H = y.shape[-1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    st = lib().moegq_moe_combine(_ptr(y), _ptr(inv), _ptr(scores), _ptr(shared), T, top_k, H, _ptr(out),
+                                 _stream())
+    _check(st, "moe_combine")
+    return out
+
+
+def moe_combine_unfused(y, inv, scores, shared=None, out=None):
+    """The same tail as four kernels, each writing a bf16 tensor."""
+    _dev(y, inv, scores, shared)
+    T, top_k = scores.shape
+    H = y.shape[-1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    ws, wsb = _workspace(workspace_bytes(OP_COMBINE_UNFUSED, T * top_k, 0, H, 0), y.device)
+    st = lib().moegq_moe_combine_unfused(_ptr(y), _ptr(inv), _ptr(scores), _ptr(shared), T, top_k, H, _ptr(out),
+                                         _ptr(ws), wsb, _stream())
+    _check(st, "moe_combine_unfused")
+    return out
+
+
+def sort_pairs(idx, E: int):
+    """(order, lhs, sorted_rhs, inv, counts, offsets), all int32 device tensors."""
+    _dev(idx)
+    T, top_k = idx.shape
+    P = T * top_k
+    mk = lambda n: torch.empty(n, dtype=torch.int32, device=idx.device)
+    order, lhs, srhs, inv, counts, offsets = mk(P), mk(P), mk(P), mk(P), mk(E), mk(E + 1)
+    st = lib().moegq_sort_pairs(_ptr(idx), _dt(idx), T, top_k, E, _ptr(order), _ptr(lhs), _ptr(srhs), _ptr(inv),
+                                _ptr(counts), _ptr(offsets), None, 0, _stream())
+    _check(st, "sort_pairs")
+    return order, lhs, srhs, inv, counts, offsets
+
+
+def schedule_tiles(offsets, E: int, P_max: int, bm: int, tile_mode=TILES_SCHEDULED):
+    """(tiles [cap, 3], n_tiles [1]) device int32."""
+    _dev(offsets)
+    cap = (P_max + bm - 1) // bm + min(E, P_max)
+    tiles = torch.full((max(cap, 1), 3), -7, dtype=torch.int32, device=offsets.device)
+    n = torch.zeros(1, dtype=torch.int32, device=offsets.device)
+    st = lib().moegq_schedule_tiles(_ptr(offsets), E, P_max, bm, tile_mode, _ptr(tiles), cap, _ptr(n), _stream())
+    _check(st, "schedule_tiles")
+    return tiles, n
+
+
+def rms_norm(x, w, eps=1e-6, out=None):
+    _dev(x, w)
+    M, K = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().moegq_rms_norm(_ptr(x), _ptr(w), M, K, eps, _ptr(out), _stream()), "rms_norm")
+    return out
+
+
+def sigmoid_gate(s, z, out=None):
+    """bf16(sigmoid(z[t]) * s[t, :]); z [T, 1] or [T]."""
+    _dev(s, z)
+    T, H = s.shape
+    zs = z.stride(0) if z.dim() >= 1 else 1
+    if out is None:
+        out = torch.empty_like(s)
+    _check(lib().moegq_sigmoid_gate(_ptr(s), _ptr(z), zs, T, H, _ptr(out), _stream()), "sigmoid_gate")
+    return out
+
+
+def kv_feed(q, k, v, out=None):
+    """bf16(q + bf16(k[:, :1] + v[:, :1]))."""
+    _dev(q, k, v)
+    M, Nq = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().moegq_kv_feed(_ptr(q), _ptr(k), _ptr(v), M, Nq, k.shape[1], v.shape[1], _ptr(out), _stream()),
+           "kv_feed")
+    return out
+
+
+def selfcheck(device="cuda") -> int:
+    """Fused vs unfused combine, bit for bit (synchronizes).  Returns the status."""
+    ws, wsb = _workspace(workspace_bytes(OP_SELFCHECK, 0, 0, 0, 0), device)
+    return int(lib().moegq_selfcheck(_ptr(ws), wsb, _stream()))
+
+
+def validate_indices(idx, E: int, sorted_=False) -> int:
+    _dev(idx)
+    flag = torch.zeros(1, dtype=torch.int32, device=idx.device)
+    return int(lib().moegq_validate_indices(_ptr(idx), idx.numel(), E, int(sorted_), _ptr(flag), _stream()))

@@ -1,0 +1,538 @@
+// C ABI of the moegq library: argument validation (the format's error
+// catalogue, nuvec-core tests/quantized.rs "invalid_arguments_are_rejected" and
+// "gather_qmm_selects_batches"), workspace sizing and kernel dispatch.  No
+// allocation, no synchronization (except the two documented checks).
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/moegq.h"
+#include "launch.h"
+
+using namespace moegq;
+
+namespace {
+
+constexpr int kMaxExperts = 1024;     // single-workgroup sort
+constexpr int64_t kMaxQmvK = 32768;   // activation row staged in 64 KiB of LDS
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOEGQ_OK : MOEGQ_ERR_LAUNCH; }
+
+// bit width / group size / quantized length checks
+int check_quant(int64_t K, int gs, int bits) {
+  if (!(bits == 4 || bits == 8)) {
+    if (bits == 1 || bits == 2 || bits == 3 || bits == 5 || bits == 6) return MOEGQ_ERR_UNSUPPORTED;
+    return MOEGQ_ERR_BITS;
+  }
+  if (!(gs == 32 || gs == 64 || gs == 128)) return MOEGQ_ERR_GROUP_SIZE;
+  if (K <= 0 || K > kMaxDim || K % gs != 0) return MOEGQ_ERR_SHAPE;
+  return MOEGQ_OK;
+}
+
+int check_act_dtype(int d) {
+  if (d == MOEGQ_BF16) return MOEGQ_OK;
+  if (d == MOEGQ_F16 || d == MOEGQ_F32) return MOEGQ_ERR_UNSUPPORTED;
+  return MOEGQ_ERR_DTYPE;   // f64 and integer activations are rejected by the format
+}
+
+int check_idx_dtype(int d) {
+  if (d == MOEGQ_I32 || d == MOEGQ_U32) return MOEGQ_OK;
+  if (d == MOEGQ_I64) return MOEGQ_ERR_UNSUPPORTED;
+  return MOEGQ_ERR_DTYPE;   // float indices are rejected
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int auto_bm(int64_t P, int64_t E) {
+  const int64_t active = P < E ? P : E;
+  const int64_t mean = active > 0 ? P / active : 0;
+  if (mean >= 96) return 64;
+  if (mean >= 24) return 32;
+  return 16;
+}
+
+int64_t tile_cap(int64_t P, int64_t E, int bm) { return (P + bm - 1) / bm + (P < E ? P : E); }
+
+// sorted-route workspace layout
+struct SortedWs {
+  int32_t* order; int32_t* lhs; int32_t* srhs; int32_t* counts; int32_t* offsets;
+  int32_t* tiles; int32_t* n_tiles; uint16_t* h;
+  size_t bytes;
+};
+SortedWs sorted_layout(char* base, int64_t P, int64_t E, int64_t I, int bm) {
+  SortedWs w{};
+  size_t off = 0;
+  auto take = [&](size_t b) { char* p = base ? base + off : nullptr; off += align256(b); return p; };
+  w.order = (int32_t*)take(4 * P);
+  w.lhs = (int32_t*)take(4 * P);
+  w.srhs = (int32_t*)take(4 * P);
+  w.counts = (int32_t*)take(4 * E);
+  w.offsets = (int32_t*)take(4 * (E + 1));
+  w.tiles = (int32_t*)take(12 * tile_cap(P, E, bm));
+  w.n_tiles = (int32_t*)take(4);
+  w.h = (uint16_t*)take(2 * P * I);
+  w.bytes = off;
+  return w;
+}
+
+// generic gather (M > 16 rows per batch): pair-major virtual rows
+__global__ void pair_tiles_kernel(const int32_t* rhs, int64_t P, int M, int bm, int32_t* tiles,
+                                  int32_t* n_tiles) {
+  const int ntm = (M + bm - 1) / bm;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t == 0) *n_tiles = (int32_t)(P * ntm);
+  if (t >= P * ntm) return;
+  const int64_t p = t / ntm, mt = t % ntm;
+  tiles[3 * t] = (int32_t)(p * M + mt * bm);
+  tiles[3 * t + 1] = rhs[p];
+  tiles[3 * t + 2] = (int32_t)min((int64_t)bm, (int64_t)M - mt * bm);
+}
+
+// offsets of a non-decreasing expert list: offsets[e] = first p with rhs[p] >= e
+__global__ void offsets_from_sorted_kernel(const int32_t* rhs, int64_t P, int E, int32_t* offsets) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e > E) return;
+  int64_t lo = 0, hi = P;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if (rhs[mid] < e) lo = mid + 1; else hi = mid;
+  }
+  offsets[e] = (int32_t)lo;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moegq_status_string(int s) {
+  switch (s) {
+    case MOEGQ_OK: return "ok";
+    case MOEGQ_ERR_NULL_ARG: return "null argument";
+    case MOEGQ_ERR_BITS: return "unsupported bit width";
+    case MOEGQ_ERR_GROUP_SIZE: return "group size must be 32, 64 or 128";
+    case MOEGQ_ERR_SHAPE: return "shape mismatch";
+    case MOEGQ_ERR_DTYPE: return "invalid dtype";
+    case MOEGQ_ERR_UNSUPPORTED: return "valid but not supported by this build";
+    case MOEGQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOEGQ_ERR_LAUNCH: return "kernel launch failed";
+    case MOEGQ_ERR_SELFCHECK: return "fused combine differs from the unfused tail";
+    case MOEGQ_ERR_INDEX: return "index out of range or not sorted";
+    case MOEGQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+  }
+  return "unknown status";
+}
+
+const char* moegq_version(void) { return "moegq 0.1 gfx950"; }
+
+size_t moegq_workspace_bytes(int op, int64_t P, int64_t E, int64_t N, int bm) {
+  if (P < 0 || E < 0 || N < 0) return 0;
+  switch (op) {
+    case MOEGQ_OP_GATHER_QMM: {
+      // M > 16 rows per batch (N carries M here): tile table; M == 1 sorted: offsets + tiles
+      const int64_t M = N;
+      const int b = 64;
+      if (M > 16) return align256(12 * (P * ((M + b - 1) / b))) + 256;
+      if (M == 1) return align256(4 * (E + 1)) + align256(12 * tile_cap(P, E, 16)) + 256;
+      return 0;
+    }
+    case MOEGQ_OP_SWITCH_GLU_DECODE: return align256(2 * P * N);
+    case MOEGQ_OP_SWITCH_GLU_SORTED: {
+      const int b = bm > 0 ? bm : 16;   // the smallest tile has the largest table
+      return sorted_layout(nullptr, P, E, N, b).bytes;
+    }
+    case MOEGQ_OP_COMBINE_UNFUSED: {
+      // N = H, P = T*top_k; T*H <= P*H
+      return align256(2 * (2 * P * N + P * N));
+    }
+    case MOEGQ_OP_SELFCHECK: {
+      const int64_t T = 128, K = 8, H = 2048;
+      return align256(2 * T * K * H) + align256(4 * T * K) + align256(2 * T * K) + align256(2 * T * H) * 3 +
+             align256(2 * 3 * T * K * H) + 256;
+    }
+    case MOEGQ_OP_SORT_PAIRS: return 0;
+  }
+  return 0;
+}
+
+static int gather_impl(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K, const void* w,
+                       int w_dtype, const void* scales, const void* biases, const void* w1, const void* s1,
+                       const void* b1, bool glu, int64_t E, int64_t N, const void* lhs_indices,
+                       int64_t lhs_div, const void* rhs_indices, int idx_dtype, int64_t P, int sorted_indices,
+                       int transpose, int group_size, int bits, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int st;
+  if ((st = check_act_dtype(x_dtype))) return st;
+  if (w_dtype != MOEGQ_U32) return MOEGQ_ERR_DTYPE;
+  if ((st = check_idx_dtype(idx_dtype))) return st;
+  if ((st = check_quant(K, group_size, bits))) return st;
+  if (!transpose) return MOEGQ_ERR_UNSUPPORTED;
+  if (X < 0 || M < 0 || E <= 0 || N < 0 || P < 0 || X > kMaxDim || N > kMaxDim || P > kMaxDim)
+    return MOEGQ_ERR_SHAPE;
+  if (!lhs_indices && lhs_div < 1) return MOEGQ_ERR_SHAPE;
+  if (P == 0 || M == 0 || N == 0) return MOEGQ_OK;
+  if (!x || !w || !scales || !biases || !rhs_indices || !out) return MOEGQ_ERR_NULL_ARG;
+  if (glu && (!w1 || !s1 || !b1)) return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out) || (glu && !aligned16(w1))) return MOEGQ_ERR_ALIGN;
+  if (!lhs_indices && (P - 1) / lhs_div >= X) return MOEGQ_ERR_SHAPE;
+  const int32_t* lhs = (const int32_t*)lhs_indices;
+  const int32_t* rhs = (const int32_t*)rhs_indices;
+  hipStream_t s = S(stream);
+  const size_t need = moegq_workspace_bytes(MOEGQ_OP_GATHER_QMM, P, E, M, 0);
+  if (M == 1 && sorted_indices && P >= 64 && E <= kMaxExperts) {
+    if (!workspace || workspace_bytes < need) return MOEGQ_ERR_WORKSPACE;
+    char* base = (char*)workspace;
+    int32_t* offsets = (int32_t*)base;
+    int32_t* tiles = (int32_t*)(base + align256(4 * (E + 1)));
+    int32_t* n_tiles = (int32_t*)(base + align256(4 * (E + 1)) + align256(12 * tile_cap(P, E, 16)));
+    const int bm = auto_bm(P, E);
+    hipLaunchKernelGGL(offsets_from_sorted_kernel, dim3((unsigned)((E + 1 + 255) / 256)), dim3(256), 0, s,
+                       rhs, P, (int)E, offsets);
+    hipError_t e = launch_schedule(offsets, (int)E, bm, 0, tiles, n_tiles, s);
+    if (e != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    TileArgs a{};
+    a.x = (const uint16_t*)x; a.lhs = lhs; a.lhs_div = lhs_div; a.rows_per_batch = 1;
+    a.tiles = tiles; a.n_tiles = n_tiles; a.P = P; a.E = (int)E;
+    a.w0 = (const uint32_t*)w; a.s0 = (const uint16_t*)scales; a.b0 = (const uint16_t*)biases;
+    a.w1 = (const uint32_t*)w1; a.s1 = (const uint16_t*)s1; a.b1 = (const uint16_t*)b1;
+    a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out; a.bm = bm; a.tile_mode = 0;
+    a.grid_tiles = tile_cap(P, E, bm);
+    return status_of(launch_tiles(a, bits, group_size, glu, s));
+  }
+  if (M == 1) {
+    if (K > kMaxQmvK) return MOEGQ_ERR_UNSUPPORTED;
+    QmvArgs a{};
+    a.x = (const uint16_t*)x; a.lhs = lhs; a.lhs_div = lhs_div; a.rhs = rhs;
+    a.w0 = (const uint32_t*)w; a.s0 = (const uint16_t*)scales; a.b0 = (const uint16_t*)biases;
+    a.w1 = (const uint32_t*)w1; a.s1 = (const uint16_t*)s1; a.b1 = (const uint16_t*)b1;
+    a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out;
+    return status_of(launch_qmv(a, bits, group_size, glu, P, s));
+  }
+  if (M <= 16) {
+    SkinnyArgs a{};
+    a.x = (const uint16_t*)x; a.lhs = lhs; a.lhs_div = lhs_div; a.rhs = rhs;
+    a.w0 = (const uint32_t*)w; a.s0 = (const uint16_t*)scales; a.b0 = (const uint16_t*)biases;
+    a.w1 = (const uint32_t*)w1; a.s1 = (const uint16_t*)s1; a.b1 = (const uint16_t*)b1;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out;
+    return status_of(launch_skinny(a, bits, group_size, glu, P, s));
+  }
+  // M > 16: per-pair tiles over pair-major virtual rows
+  if (!workspace || workspace_bytes < need) return MOEGQ_ERR_WORKSPACE;
+  const int bm = 64;
+  const int64_t nt = P * ((M + bm - 1) / bm);
+  int32_t* tiles = (int32_t*)workspace;
+  int32_t* n_tiles = (int32_t*)((char*)workspace + align256(12 * nt));
+  hipLaunchKernelGGL(pair_tiles_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, rhs, P, (int)M,
+                     bm, tiles, n_tiles);
+  TileArgs a{};
+  a.x = (const uint16_t*)x; a.lhs = lhs; a.lhs_div = lhs_div; a.rows_per_batch = M;
+  a.tiles = tiles; a.n_tiles = n_tiles; a.P = P * M; a.E = (int)E;
+  a.w0 = (const uint32_t*)w; a.s0 = (const uint16_t*)scales; a.b0 = (const uint16_t*)biases;
+  a.w1 = (const uint32_t*)w1; a.s1 = (const uint16_t*)s1; a.b1 = (const uint16_t*)b1;
+  a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out; a.bm = bm; a.tile_mode = 0; a.grid_tiles = nt;
+  return status_of(launch_tiles(a, bits, group_size, glu, s));
+}
+
+int moegq_gather_qmm(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K, const void* w,
+                     int w_dtype, const void* scales, const void* biases, int64_t E, int64_t N,
+                     const void* lhs_indices, int64_t lhs_div, const void* rhs_indices, int idx_dtype,
+                     int64_t P, int sorted_indices, int transpose, int group_size, int bits, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return gather_impl(x, x_dtype, X, M, K, w, w_dtype, scales, biases, nullptr, nullptr, nullptr, false, E, N,
+                     lhs_indices, lhs_div, rhs_indices, idx_dtype, P, sorted_indices, transpose, group_size,
+                     bits, out, workspace, workspace_bytes, stream);
+}
+
+int moegq_gather_qmm_glu(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K, const void* wg,
+                         const void* sg, const void* bg, const void* wu, const void* su, const void* bu,
+                         int64_t E, int64_t N, const void* lhs_indices, int64_t lhs_div,
+                         const void* rhs_indices, int idx_dtype, int64_t P, int sorted_indices, int group_size,
+                         int bits, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return gather_impl(x, x_dtype, X, M, K, wg, MOEGQ_U32, sg, bg, wu, su, bu, true, E, N, lhs_indices, lhs_div,
+                     rhs_indices, idx_dtype, P, sorted_indices, 1, group_size, bits, out, workspace,
+                     workspace_bytes, stream);
+}
+
+int moegq_affine_qmm(const void* x, int x_dtype, int64_t M, int64_t K, const void* w, int w_dtype,
+                     const void* scales, const void* biases, int64_t N, int transpose, int group_size,
+                     int bits, const void* residual, void* out, void* stream) {
+  int st;
+  if ((st = check_act_dtype(x_dtype))) return st;
+  if (w_dtype != MOEGQ_U32) return MOEGQ_ERR_DTYPE;
+  if ((st = check_quant(K, group_size, bits))) return st;
+  if (!transpose) return MOEGQ_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return MOEGQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MOEGQ_OK;
+  if (!x || !w || !scales || !biases || !out) return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return MOEGQ_ERR_ALIGN;
+  hipStream_t s = S(stream);
+  if (M == 1 && K <= kMaxQmvK) {
+    QmvArgs a{};
+    a.x = (const uint16_t*)x; a.lhs_div = 1;
+    a.w0 = (const uint32_t*)w; a.s0 = (const uint16_t*)scales; a.b0 = (const uint16_t*)biases;
+    a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out; a.residual = (const uint16_t*)residual;
+    return status_of(launch_qmv(a, bits, group_size, false, 1, s));
+  }
+  if (M <= 16) {
+    SkinnyArgs a{};
+    a.x = (const uint16_t*)x; a.lhs_div = 1;
+    a.w0 = (const uint32_t*)w; a.s0 = (const uint16_t*)scales; a.b0 = (const uint16_t*)biases;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out; a.residual = (const uint16_t*)residual;
+    return status_of(launch_skinny(a, bits, group_size, false, 1, s));
+  }
+  if (residual) return MOEGQ_ERR_UNSUPPORTED;
+  // many rows: one "expert", tiles over M on the device-free path
+  const int bm = M >= 1024 ? 64 : 32;
+  static_assert(sizeof(int32_t) == 4, "");
+  TileArgs a{};
+  a.x = (const uint16_t*)x; a.lhs = nullptr; a.lhs_div = 1; a.rows_per_batch = 1;
+  a.P = M; a.E = 1; a.tile_mode = 2;        // dense: tiles over the rows, one weight matrix
+  a.w0 = (const uint32_t*)w; a.s0 = (const uint16_t*)scales; a.b0 = (const uint16_t*)biases;
+  a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out; a.bm = bm;
+  a.grid_tiles = (M + bm - 1) / bm;
+  a.sorted_rhs = nullptr;
+  return status_of(launch_tiles(a, bits, group_size, false, s));
+}
+
+int moegq_affine_qmm_glu(const void* x, int64_t M, int64_t K, const void* wg, const void* sg,
+                         const void* bg, const void* wu, const void* su, const void* bu, int64_t N,
+                         int group_size, int bits, void* out, void* stream) {
+  int st;
+  if ((st = check_quant(K, group_size, bits))) return st;
+  if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return MOEGQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MOEGQ_OK;
+  if (!x || !wg || !sg || !bg || !wu || !su || !bu || !out) return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(x) || !aligned16(wg) || !aligned16(wu) || !aligned16(out)) return MOEGQ_ERR_ALIGN;
+  hipStream_t s = S(stream);
+  if (M == 1 && K <= kMaxQmvK) {
+    QmvArgs a{};
+    a.x = (const uint16_t*)x; a.lhs_div = 1;
+    a.w0 = (const uint32_t*)wg; a.s0 = (const uint16_t*)sg; a.b0 = (const uint16_t*)bg;
+    a.w1 = (const uint32_t*)wu; a.s1 = (const uint16_t*)su; a.b1 = (const uint16_t*)bu;
+    a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out;
+    return status_of(launch_qmv(a, bits, group_size, true, 1, s));
+  }
+  if (M <= 16) {
+    SkinnyArgs a{};
+    a.x = (const uint16_t*)x; a.lhs_div = 1;
+    a.w0 = (const uint32_t*)wg; a.s0 = (const uint16_t*)sg; a.b0 = (const uint16_t*)bg;
+    a.w1 = (const uint32_t*)wu; a.s1 = (const uint16_t*)su; a.b1 = (const uint16_t*)bu;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out;
+    return status_of(launch_skinny(a, bits, group_size, true, 1, s));
+  }
+  const int bm = M >= 1024 ? 64 : 32;
+  TileArgs a{};
+  a.x = (const uint16_t*)x; a.lhs_div = 1; a.rows_per_batch = 1;
+  a.P = M; a.E = 1; a.tile_mode = 2;
+  a.w0 = (const uint32_t*)wg; a.s0 = (const uint16_t*)sg; a.b0 = (const uint16_t*)bg;
+  a.w1 = (const uint32_t*)wu; a.s1 = (const uint16_t*)su; a.b1 = (const uint16_t*)bu;
+  a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out; a.bm = bm;
+  a.grid_tiles = (M + bm - 1) / bm;
+  return status_of(launch_tiles(a, bits, group_size, true, s));
+}
+
+int moegq_switch_glu_mode(int64_t T, int64_t top_k, int64_t E) {
+  // the sorted route pays off once experts see several rows each; decode
+  // (a handful of tokens) streams each pair's expert once
+  const int64_t P = T * top_k;
+  (void)E;
+  return (T >= 32 && P >= 256) ? MOEGQ_MODE_SORTED : MOEGQ_MODE_DECODE;
+}
+
+int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, const int32_t* idx,
+                     int64_t top_k, const void* wg, const void* sg, const void* bg, const void* wu,
+                     const void* su, const void* bu, const void* wd, const void* sd, const void* bd,
+                     int group_size, int bits, int mode, int tile_mode, int bm, void* y, int32_t* inv,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int st;
+  if ((st = check_quant(H, group_size, bits))) return st;
+  if ((st = check_quant(I, group_size, bits))) return st;
+  if (T < 0 || top_k <= 0 || E <= 0 || T > kMaxDim || top_k > 64) return MOEGQ_ERR_SHAPE;
+  if (!(mode == MOEGQ_MODE_AUTO || mode == MOEGQ_MODE_DECODE || mode == MOEGQ_MODE_SORTED))
+    return MOEGQ_ERR_SHAPE;
+  if (!(tile_mode == MOEGQ_TILES_SCHEDULED || tile_mode == MOEGQ_TILES_NAIVE)) return MOEGQ_ERR_SHAPE;
+  if (!(bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128)) return MOEGQ_ERR_SHAPE;
+  if (T == 0) return MOEGQ_OK;
+  if (!x || !idx || !wg || !sg || !bg || !wu || !su || !bu || !wd || !sd || !bd || !y)
+    return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(x) || !aligned16(wg) || !aligned16(wu) || !aligned16(wd) || !aligned16(y))
+    return MOEGQ_ERR_ALIGN;
+  const int64_t P = T * top_k;
+  if (mode == MOEGQ_MODE_AUTO) {
+    if (!inv) return MOEGQ_ERR_NULL_ARG;
+    mode = moegq_switch_glu_mode(T, top_k, E);
+  }
+  hipStream_t s = S(stream);
+  if (mode == MOEGQ_MODE_SORTED && (E > kMaxExperts)) return MOEGQ_ERR_UNSUPPORTED;
+  if (mode == MOEGQ_MODE_SORTED && !inv) return MOEGQ_ERR_NULL_ARG;
+  if (mode == MOEGQ_MODE_DECODE) {
+    if (H > kMaxQmvK || I > kMaxQmvK) return MOEGQ_ERR_UNSUPPORTED;
+    const size_t need = moegq_workspace_bytes(MOEGQ_OP_SWITCH_GLU_DECODE, P, E, I, 0);
+    if (!workspace || workspace_bytes < need) return MOEGQ_ERR_WORKSPACE;
+    uint16_t* h = (uint16_t*)workspace;
+    QmvArgs a{};
+    a.x = (const uint16_t*)x; a.lhs = nullptr; a.lhs_div = top_k; a.rhs = idx;
+    a.w0 = (const uint32_t*)wg; a.s0 = (const uint16_t*)sg; a.b0 = (const uint16_t*)bg;
+    a.w1 = (const uint32_t*)wu; a.s1 = (const uint16_t*)su; a.b1 = (const uint16_t*)bu;
+    a.N = (int)I; a.K = (int)H; a.out = h;
+    hipError_t e = launch_qmv(a, bits, group_size, true, P, s);
+    if (e != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    QmvArgs d{};
+    d.x = h; d.lhs = nullptr; d.lhs_div = 1; d.rhs = idx;
+    d.w0 = (const uint32_t*)wd; d.s0 = (const uint16_t*)sd; d.b0 = (const uint16_t*)bd;
+    d.N = (int)H; d.K = (int)I; d.out = (uint16_t*)y;
+    e = launch_qmv(d, bits, group_size, false, P, s);
+    if (e != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    if (inv) e = launch_iota(inv, P, s);
+    return status_of(e);
+  }
+  // sorted route
+  if (bm == 0) bm = auto_bm(P, E);
+  const SortedWs ws = sorted_layout((char*)workspace, P, E, I, bm);
+  if (!workspace || workspace_bytes < ws.bytes) return MOEGQ_ERR_WORKSPACE;
+  SortArgs sa{};
+  sa.idx = idx; sa.P = P; sa.top_k = (int)top_k; sa.E = (int)E;
+  sa.order = ws.order; sa.lhs = ws.lhs; sa.sorted_rhs = ws.srhs; sa.inv = inv;
+  sa.counts = ws.counts; sa.offsets = ws.offsets;
+  sa.tiles = ws.tiles; sa.n_tiles = ws.n_tiles; sa.bm = bm; sa.tile_mode = tile_mode;
+  hipError_t e = launch_sort(sa, s);
+  if (e != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  TileArgs g{};
+  g.x = (const uint16_t*)x; g.lhs = ws.lhs; g.lhs_div = 1; g.rows_per_batch = 1;
+  g.sorted_rhs = ws.srhs; g.offsets = ws.offsets; g.tiles = ws.tiles; g.n_tiles = ws.n_tiles;
+  g.P = P; g.E = (int)E;
+  g.w0 = (const uint32_t*)wg; g.s0 = (const uint16_t*)sg; g.b0 = (const uint16_t*)bg;
+  g.w1 = (const uint32_t*)wu; g.s1 = (const uint16_t*)su; g.b1 = (const uint16_t*)bu;
+  g.N = (int)I; g.K = (int)H; g.out = ws.h; g.bm = bm; g.tile_mode = tile_mode;
+  g.grid_tiles = tile_mode == MOEGQ_TILES_SCHEDULED ? tile_cap(P, E, bm) : (P + bm - 1) / bm;
+  e = launch_tiles(g, bits, group_size, true, s);
+  if (e != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  TileArgs d = g;
+  d.x = ws.h; d.lhs = nullptr; d.lhs_div = 1;
+  d.w0 = (const uint32_t*)wd; d.s0 = (const uint16_t*)sd; d.b0 = (const uint16_t*)bd;
+  d.w1 = nullptr; d.s1 = nullptr; d.b1 = nullptr;
+  d.N = (int)H; d.K = (int)I; d.out = (uint16_t*)y;
+  return status_of(launch_tiles(d, bits, group_size, false, s));
+}
+
+int moegq_moe_combine(const void* y, const int32_t* inv, const void* scores, const void* shared, int64_t T,
+                      int64_t top_k, int64_t H, void* out, void* stream) {
+  if (T < 0 || top_k <= 0 || H <= 0 || H % 8 != 0 || T > kMaxDim || H > kMaxDim) return MOEGQ_ERR_SHAPE;
+  if (T == 0) return MOEGQ_OK;
+  if (!y || !scores || !out) return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(y) || !aligned16(out) || (shared && !aligned16(shared))) return MOEGQ_ERR_ALIGN;
+  return status_of(launch_combine((const uint16_t*)y, inv, (const uint16_t*)scores, (const uint16_t*)shared, T,
+                                  (int)top_k, H, (uint16_t*)out, S(stream)));
+}
+
+int moegq_moe_combine_unfused(const void* y, const int32_t* inv, const void* scores, const void* shared,
+                              int64_t T, int64_t top_k, int64_t H, void* out, void* scratch,
+                              size_t scratch_bytes, void* stream) {
+  if (T < 0 || top_k <= 0 || H <= 0 || H % 8 != 0 || T > kMaxDim || H > kMaxDim) return MOEGQ_ERR_SHAPE;
+  if (T == 0) return MOEGQ_OK;
+  if (!y || !scores || !out) return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(y) || !aligned16(out) || (shared && !aligned16(shared))) return MOEGQ_ERR_ALIGN;
+  const size_t need = moegq_workspace_bytes(MOEGQ_OP_COMBINE_UNFUSED, T * top_k, 0, H, 0);
+  if (!scratch || scratch_bytes < need || !aligned16(scratch)) return MOEGQ_ERR_WORKSPACE;
+  return status_of(launch_combine_unfused((const uint16_t*)y, inv, (const uint16_t*)scores,
+                                          (const uint16_t*)shared, T, (int)top_k, H, (uint16_t*)out,
+                                          (uint16_t*)scratch, S(stream)));
+}
+
+int moegq_sort_pairs(const void* idx, int idx_dtype, int64_t T, int64_t top_k, int64_t E, int32_t* order,
+                     int32_t* lhs, int32_t* sorted_rhs, int32_t* inv, int32_t* counts, int32_t* offsets,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  int st;
+  if ((st = check_idx_dtype(idx_dtype))) return st;
+  if (T < 0 || top_k <= 0 || E <= 0 || T > kMaxDim || top_k > 64) return MOEGQ_ERR_SHAPE;
+  if (E > kMaxExperts) return MOEGQ_ERR_UNSUPPORTED;
+  if (!idx || !inv || !counts || !offsets) return MOEGQ_ERR_NULL_ARG;
+  SortArgs sa{};
+  sa.idx = (const int32_t*)idx; sa.P = T * top_k; sa.top_k = (int)top_k; sa.E = (int)E;
+  sa.order = order; sa.lhs = lhs; sa.sorted_rhs = sorted_rhs; sa.inv = inv;
+  sa.counts = counts; sa.offsets = offsets; sa.tiles = nullptr; sa.n_tiles = nullptr; sa.bm = 0;
+  return status_of(launch_sort(sa, S(stream)));
+}
+
+int moegq_schedule_tiles(const int32_t* offsets, int64_t E, int64_t P_max, int bm, int tile_mode,
+                         int32_t* tiles, int64_t cap, int32_t* n_tiles, void* stream) {
+  if (E <= 0 || P_max < 0 || !(bm == 16 || bm == 32 || bm == 64 || bm == 128)) return MOEGQ_ERR_SHAPE;
+  if (!(tile_mode == MOEGQ_TILES_SCHEDULED || tile_mode == MOEGQ_TILES_NAIVE)) return MOEGQ_ERR_SHAPE;
+  if (E > kMaxExperts) return MOEGQ_ERR_UNSUPPORTED;
+  if (!offsets || !tiles || !n_tiles) return MOEGQ_ERR_NULL_ARG;
+  if (cap < tile_cap(P_max, E, bm)) return MOEGQ_ERR_WORKSPACE;
+  return status_of(launch_schedule(offsets, (int)E, bm, tile_mode, tiles, n_tiles, S(stream)));
+}
+
+int moegq_rms_norm(const void* x, const void* w, int64_t M, int64_t K, float eps, void* out, void* stream) {
+  if (M < 0 || K <= 0) return MOEGQ_ERR_SHAPE;
+  if (M == 0) return MOEGQ_OK;
+  if (!x || !w || !out) return MOEGQ_ERR_NULL_ARG;
+  return status_of(launch_rms_norm((const uint16_t*)x, (const uint16_t*)w, M, K, eps, (uint16_t*)out, S(stream)));
+}
+
+int moegq_sigmoid_gate(const void* s, const void* z, int64_t z_stride, int64_t T, int64_t H, void* out,
+                       void* stream) {
+  if (T < 0 || H <= 0 || H % 8 != 0 || z_stride < 1) return MOEGQ_ERR_SHAPE;
+  if (T == 0) return MOEGQ_OK;
+  if (!s || !z || !out) return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(s) || !aligned16(out)) return MOEGQ_ERR_ALIGN;
+  return status_of(launch_sigmoid_gate((const uint16_t*)s, (const uint16_t*)z, z_stride, T, H, (uint16_t*)out,
+                                       S(stream)));
+}
+
+int moegq_kv_feed(const void* q, const void* k, const void* v, int64_t M, int64_t Nq, int64_t Nk, int64_t Nv,
+                  void* out, void* stream) {
+  if (M < 0 || Nq <= 0 || Nk <= 0 || Nv <= 0) return MOEGQ_ERR_SHAPE;
+  if (M == 0) return MOEGQ_OK;
+  if (!q || !k || !v || !out) return MOEGQ_ERR_NULL_ARG;
+  return status_of(launch_kv_feed((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, M, Nq, Nk, Nv,
+                                  (uint16_t*)out, S(stream)));
+}
+
+int moegq_selfcheck(void* workspace, size_t workspace_bytes, void* stream) {
+  const int64_t T = 128, K = 8, H = 2048, P = T * K;
+  if (!workspace || workspace_bytes < moegq_workspace_bytes(MOEGQ_OP_SELFCHECK, 0, 0, 0, 0) ||
+      !aligned16(workspace))
+    return MOEGQ_ERR_WORKSPACE;
+  char* b = (char*)workspace;
+  size_t off = 0;
+  auto take = [&](size_t n) { char* p = b + off; off += align256(n); return p; };
+  uint16_t* y = (uint16_t*)take(2 * P * H);
+  int32_t* inv = (int32_t*)take(4 * P);
+  uint16_t* scores = (uint16_t*)take(2 * P);
+  uint16_t* shared = (uint16_t*)take(2 * T * H);
+  uint16_t* o1 = (uint16_t*)take(2 * T * H);
+  uint16_t* o2 = (uint16_t*)take(2 * T * H);
+  uint16_t* scratch = (uint16_t*)take(2 * 3 * P * H);
+  hipStream_t s = S(stream);
+  if (launch_fill_selfcheck(y, inv, scores, shared, T, (int)K, H, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (launch_combine(y, inv, scores, shared, T, (int)K, H, o1, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (launch_combine_unfused(y, inv, scores, shared, T, (int)K, H, o2, scratch, s) != hipSuccess)
+    return MOEGQ_ERR_LAUNCH;
+  static uint16_t h1[128 * 2048], h2[128 * 2048];
+  if (hipMemcpyAsync(h1, o1, sizeof(h1), hipMemcpyDeviceToHost, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (hipMemcpyAsync(h2, o2, sizeof(h2), hipMemcpyDeviceToHost, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  const char* force = getenv("MOEGQ_FORCE_SELFCHECK_FAIL");
+  if (force && force[0] == '1') return MOEGQ_ERR_SELFCHECK;
+  return memcmp(h1, h2, sizeof(h1)) == 0 ? MOEGQ_OK : MOEGQ_ERR_SELFCHECK;
+}
+
+int moegq_validate_indices(const int32_t* idx, int64_t n, int64_t E, int sorted, int32_t* workspace,
+                           void* stream) {
+  if (n < 0 || E <= 0) return MOEGQ_ERR_SHAPE;
+  if (!workspace || (n > 0 && !idx)) return MOEGQ_ERR_NULL_ARG;
+  hipStream_t s = S(stream);
+  if (launch_validate(idx, n, E, sorted, workspace, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  int32_t flag = 0;
+  if (hipMemcpyAsync(&flag, workspace, 4, hipMemcpyDeviceToHost, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  return flag ? MOEGQ_ERR_INDEX : MOEGQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,291 @@
+// MoE combine tail and small glue kernels.  Built with -ffp-contract=off:
+// every bf16 op below is an fp32 operation followed by one round-to-nearest-
+// even, in a fixed order, so the fused and unfused tails are bit-identical.
+//
+// Combine (MTPLX PR 558, Summary/Motivation): unsort the expert-sorted rows,
+// multiply by the routing scores, sum over top_k and add the gated shared
+// expert; the stock tail materializes a bf16 tensor after each step, the fused
+// kernel does all four in one pass over HBM.
+#include "common.h"
+#include "launch.h"
+
+namespace moegq {
+
+// ---------------------------------------------------------------- fused combine
+// One thread owns 8 consecutive hidden elements (one 16-byte vector) of one
+// token and walks the token's top_k slots in order.
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ inv,
+                                                      const uint16_t* __restrict__ scores,
+                                                      const uint16_t* __restrict__ shared,
+                                                      int64_t T, int top_k, int64_t H,
+                                                      uint16_t* __restrict__ out) {
+  const int64_t cpr = H / 8;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= T * cpr) return;
+  const int64_t t = c / cpr, h8 = (c % cpr) * 8;
+  float acc[8];
+  for (int k = 0; k < top_k; ++k) {
+    const int64_t pair = t * top_k + k;
+    const int64_t row = inv ? (int64_t)inv[pair] : pair;
+    const float sc = bf16_to_f32(scores[pair]);
+    const uint4 v = *reinterpret_cast<const uint4*>(y + row * H + h8);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = bf16_to_f32(f32_to_bf16(bf16_lo(d[i]) * sc));
+      const float p1 = bf16_to_f32(f32_to_bf16(bf16_hi(d[i]) * sc));
+      if (k == 0) { acc[2 * i] = p0; acc[2 * i + 1] = p1; }
+      else { acc[2 * i] = acc[2 * i] + p0; acc[2 * i + 1] = acc[2 * i + 1] + p1; }
+    }
+  }
+  uint32_t o[4];
+  if (shared) {
+    const uint4 s = *reinterpret_cast<const uint4*>(shared + t * H + h8);
+    const uint32_t sd[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a0 = bf16_to_f32(f32_to_bf16(acc[2 * i])) + bf16_lo(sd[i]);
+      const float a1 = bf16_to_f32(f32_to_bf16(acc[2 * i + 1])) + bf16_hi(sd[i]);
+      o[i] = pack_bf16x2(a0, a1);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+  }
+  *reinterpret_cast<uint4*>(out + t * H + h8) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const uint16_t* scores,
+                          const uint16_t* shared, int64_t T, int top_k, int64_t H, uint16_t* out,
+                          hipStream_t st) {
+  const int64_t n = T * (H / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, y, inv,
+                     scores, shared, T, top_k, H, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- unfused tail
+// (1) unsort: u[t, k, :] = y[inv[t*top_k + k], :]
+__global__ __launch_bounds__(256) void unsort_kernel(const uint16_t* __restrict__ y,
+                                                     const int32_t* __restrict__ inv, int64_t P,
+                                                     int64_t H, uint16_t* __restrict__ u) {
+  const int64_t cpr = H / 8;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= P * cpr) return;
+  const int64_t pair = c / cpr, h8 = (c % cpr) * 8;
+  const int64_t row = inv ? (int64_t)inv[pair] : pair;
+  *reinterpret_cast<uint4*>(u + pair * H + h8) = *reinterpret_cast<const uint4*>(y + row * H + h8);
+}
+// (2) weight: w[t, k, :] = bf16(u[t, k, :] * score[t, k])
+__global__ __launch_bounds__(256) void weight_kernel(const uint16_t* __restrict__ u,
+                                                     const uint16_t* __restrict__ scores, int64_t P,
+                                                     int64_t H, uint16_t* __restrict__ w) {
+  const int64_t cpr = H / 8;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= P * cpr) return;
+  const int64_t pair = c / cpr, h8 = (c % cpr) * 8;
+  const float sc = bf16_to_f32(scores[pair]);
+  const uint4 v = *reinterpret_cast<const uint4*>(u + pair * H + h8);
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(bf16_lo(d[i]) * sc, bf16_hi(d[i]) * sc);
+  *reinterpret_cast<uint4*>(w + pair * H + h8) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+// (3) sum over top_k: s[t, :] = bf16(w[t, 0, :] + w[t, 1, :] + ...) in fp32, slot order
+__global__ __launch_bounds__(256) void topk_sum_kernel(const uint16_t* __restrict__ w, int64_t T,
+                                                       int top_k, int64_t H,
+                                                       uint16_t* __restrict__ s) {
+  const int64_t cpr = H / 8;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= T * cpr) return;
+  const int64_t t = c / cpr, h8 = (c % cpr) * 8;
+  float acc[8];
+  for (int k = 0; k < top_k; ++k) {
+    const uint4 v = *reinterpret_cast<const uint4*>(w + (t * top_k + k) * H + h8);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (k == 0) { acc[2 * i] = bf16_lo(d[i]); acc[2 * i + 1] = bf16_hi(d[i]); }
+      else { acc[2 * i] = acc[2 * i] + bf16_lo(d[i]); acc[2 * i + 1] = acc[2 * i + 1] + bf16_hi(d[i]); }
+    }
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+  *reinterpret_cast<uint4*>(s + t * H + h8) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+// (4) add: out[t, :] = bf16(s[t, :] + shared[t, :])  (copy when shared is null)
+__global__ __launch_bounds__(256) void add_kernel(const uint16_t* __restrict__ a,
+                                                  const uint16_t* __restrict__ b, int64_t n8,
+                                                  uint16_t* __restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= n8) return;
+  const uint4 va = reinterpret_cast<const uint4*>(a)[c];
+  if (!b) { reinterpret_cast<uint4*>(out)[c] = va; return; }
+  const uint4 vb = reinterpret_cast<const uint4*>(b)[c];
+  const uint32_t da[4] = {va.x, va.y, va.z, va.w}, db[4] = {vb.x, vb.y, vb.z, vb.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = pack_bf16x2(bf16_lo(da[i]) + bf16_lo(db[i]), bf16_hi(da[i]) + bf16_hi(db[i]));
+  reinterpret_cast<uint4*>(out)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_combine_unfused(const uint16_t* y, const int32_t* inv, const uint16_t* scores,
+                                  const uint16_t* shared, int64_t T, int top_k, int64_t H,
+                                  uint16_t* out, uint16_t* scratch, hipStream_t st) {
+  const int64_t P = T * top_k;
+  if (P == 0) return hipSuccess;
+  uint16_t* u = scratch;
+  uint16_t* w = scratch + P * H;
+  uint16_t* s = scratch + 2 * P * H;
+  const unsigned gp = (unsigned)((P * (H / 8) + 255) / 256);
+  const unsigned gt = (unsigned)((T * (H / 8) + 255) / 256);
+  hipLaunchKernelGGL(unsort_kernel, dim3(gp), dim3(256), 0, st, y, inv, P, H, u);
+  hipLaunchKernelGGL(weight_kernel, dim3(gp), dim3(256), 0, st, u, scores, P, H, w);
+  hipLaunchKernelGGL(topk_sum_kernel, dim3(gt), dim3(256), 0, st, w, T, top_k, H, s);
+  hipLaunchKernelGGL(add_kernel, dim3(gt), dim3(256), 0, st, s, shared, T * (H / 8), out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- glue
+// rms_norm: one workgroup per row; fp32 sum of squares, then x * r * w
+__global__ __launch_bounds__(256) void rms_norm_kernel(const uint16_t* __restrict__ x,
+                                                       const uint16_t* __restrict__ w, int64_t K,
+                                                       float eps, uint16_t* __restrict__ out) {
+  __shared__ float part[4];
+  const int64_t m = blockIdx.x;
+  const uint16_t* xr = x + m * K;
+  float ss = 0.f;
+  for (int64_t k = threadIdx.x; k < K; k += 256) {
+    const float v = bf16_to_f32(xr[k]);
+    ss = fmaf(v, v, ss);
+  }
+  for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor(ss, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float r = 1.0f / sqrtf(tot / (float)K + eps);
+  for (int64_t k = threadIdx.x; k < K; k += 256)
+    out[m * K + k] = f32_to_bf16(bf16_to_f32(xr[k]) * r * bf16_to_f32(w[k]));
+}
+
+hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t K, float eps,
+                           uint16_t* out, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(rms_norm_kernel, dim3((unsigned)M), dim3(256), 0, st, x, w, K, eps, out);
+  return hipGetLastError();
+}
+
+// shared expert gate: out[t, :] = bf16(sigmoid(z[t]) * s[t, :])
+__global__ __launch_bounds__(256) void sigmoid_gate_kernel(const uint16_t* __restrict__ s,
+                                                           const uint16_t* __restrict__ z, int64_t zs,
+                                                           int64_t T, int64_t H,
+                                                           uint16_t* __restrict__ out) {
+  const int64_t cpr = H / 8;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= T * cpr) return;
+  const int64_t t = c / cpr;
+  const float zf = bf16_to_f32(z[t * zs]);
+  const float gate = 1.0f / (1.0f + __expf(-zf));
+  const uint4 v = reinterpret_cast<const uint4*>(s)[c];
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(gate * bf16_lo(d[i]), gate * bf16_hi(d[i]));
+  reinterpret_cast<uint4*>(out)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_sigmoid_gate(const uint16_t* s, const uint16_t* z, int64_t zs, int64_t T, int64_t H,
+                               uint16_t* out, hipStream_t st) {
+  const int64_t n = T * (H / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(sigmoid_gate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s, z,
+                     zs, T, H, out);
+  return hipGetLastError();
+}
+
+// decoder chain feed: out[m, n] = bf16(q[m, n] + bf16(k[m, 0] + v[m, 0]))
+__global__ __launch_bounds__(256) void kv_feed_kernel(const uint16_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ k,
+                                                      const uint16_t* __restrict__ v, int64_t M,
+                                                      int64_t Nq, int64_t Nk, int64_t Nv,
+                                                      uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * Nq) return;
+  const int64_t m = i / Nq;
+  const float kv = bf16_to_f32(f32_to_bf16(bf16_to_f32(k[m * Nk]) + bf16_to_f32(v[m * Nv])));
+  out[i] = f32_to_bf16(bf16_to_f32(q[i]) + kv);
+}
+
+hipError_t launch_kv_feed(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t M,
+                          int64_t Nq, int64_t Nk, int64_t Nv, uint16_t* out, hipStream_t st) {
+  const int64_t n = M * Nq;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_feed_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, q, k, v, M,
+                     Nq, Nk, Nv, out);
+  return hipGetLastError();
+}
+
+__global__ void iota_kernel(int32_t* dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = (int32_t)i;
+}
+hipError_t launch_iota(int32_t* dst, int64_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(iota_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, n);
+  return hipGetLastError();
+}
+
+// index validation (debug path): flag[0] |= 1 for any bad index
+__global__ void zero_flag_kernel(int32_t* flag) { *flag = 0; }
+__global__ void validate_kernel(const int32_t* idx, int64_t n, int64_t E, int sorted, int32_t* flag) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int32_t v = idx[i];
+  bool bad = v < 0 || v >= E;
+  if (sorted && i + 1 < n && idx[i + 1] < v) bad = true;
+  if (bad) atomicOr(flag, 1);
+}
+hipError_t launch_validate(const int32_t* idx, int64_t n, int64_t E, int sorted, int32_t* flag,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(zero_flag_kernel, dim3(1), dim3(1), 0, st, flag);
+  if (n > 0)
+    hipLaunchKernelGGL(validate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, idx, n,
+                       E, sorted, flag);
+  return hipGetLastError();
+}
+
+// self-check inputs: a fixed hash of the element index (no host data needed)
+MOEGQ_DEV uint32_t mix(uint32_t v) {
+  v ^= v >> 16; v *= 0x7feb352dU; v ^= v >> 15; v *= 0x846ca68bU; v ^= v >> 16;
+  return v;
+}
+MOEGQ_DEV uint16_t hash_bf16(uint32_t i, uint32_t salt, float scale) {
+  const float u = (float)(mix(i * 2654435761U + salt) >> 8) * (1.0f / 16777216.0f);  // [0, 1)
+  return f32_to_bf16((u * 2.0f - 1.0f) * scale);
+}
+__global__ void fill_selfcheck_kernel(uint16_t* y, int32_t* inv, uint16_t* scores, uint16_t* shared,
+                                      int64_t T, int top_k, int64_t H) {
+  const int64_t P = T * top_k;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < P * H) y[i] = hash_bf16((uint32_t)i, 1u, 4.0f);
+  if (i < T * H) shared[i] = hash_bf16((uint32_t)i, 2u, 2.0f);
+  if (i < P) {
+    // i -> (i * 1021 + 7) mod P is a bijection for P a power of two (1021 is odd)
+    inv[i] = (int32_t)((i * 1021 + 7) % P);
+    scores[i] = f32_to_bf16((float)(mix((uint32_t)i + 3u) >> 8) * (1.0f / 16777216.0f));
+  }
+}
+hipError_t launch_fill_selfcheck(uint16_t* y, int32_t* inv, uint16_t* scores, uint16_t* shared,
+                                 int64_t T, int top_k, int64_t H, hipStream_t st) {
+  const int64_t n = T * top_k * H;
+  hipLaunchKernelGGL(fill_selfcheck_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, y,
+                     inv, scores, shared, T, top_k, H);
+  return hipGetLastError();
+}
+
+}  // namespace moegq

@@ -1,0 +1,83 @@
+// Device helpers shared by the gfx950 kernels: bf16 encode/decode, packed
+// pair construction for 4-bit codes, wave reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOEGQ_DEV __device__ __forceinline__
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+namespace moegq {
+
+// bf16 (as the upper half of an fp32) -> fp32
+MOEGQ_DEV float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+MOEGQ_DEV float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+MOEGQ_DEV float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN -> quiet NaN 0x7FC0.
+MOEGQ_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+MOEGQ_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+MOEGQ_DEV float fdot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Four bf16 pairs holding 128 + q for the eight 4-bit codes of a word w:
+// pair j = (128 + q_j, 128 + q_{j+4}).  0x4300 is bf16 128.0 and codes < 16
+// land in its low mantissa bits, so each lane is exactly 128 + q.
+MOEGQ_DEV void nib_pairs(uint32_t w, uint32_t p[4]) {
+  const uint32_t m = 0x000F000Fu, magic = 0x43004300u;
+  p[0] = (w & m) | magic;
+  p[1] = ((w >> 4) & m) | magic;
+  p[2] = ((w >> 8) & m) | magic;
+  p[3] = ((w >> 12) & m) | magic;
+}
+
+// Reorder eight consecutive bf16 values (four pairs d[0..3] = (x0,x1),
+// (x2,x3), (x4,x5), (x6,x7)) into the nib_pairs order (x0,x4), (x1,x5),
+// (x2,x6), (x3,x7).
+MOEGQ_DEV void perm_pairs(const uint32_t d[4], uint32_t o[4]) {
+  // __builtin_amdgcn_perm(hi_src, lo_src, sel): byte i of the result is
+  // byte sel_i of the 8-byte value {hi_src:lo_src}.
+  o[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);  // (lo of d0, lo of d2)
+  o[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);  // (hi of d0, hi of d2)
+  o[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
+}
+
+MOEGQ_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }
+MOEGQ_DEV float round_bf16(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+// SwitchGLU's middle step on the two projections of one output: the gate and
+// up results are bf16 tensors in the page's chain (MLX issue 4509, moe():
+// g, u = gather_qmm(...), then g * sigmoid(g) * u), so both are rounded to
+// bf16 before silu(g) * u, which is then rounded once by the caller.
+MOEGQ_DEV float glu(float g, float u) {
+  const float gr = round_bf16(g);
+  return silu(gr) * round_bf16(u);
+}
+
+MOEGQ_DEV float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+template <typename T>
+MOEGQ_DEV T ldg(const T* p) { return *p; }
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// 128-bit streaming load (non-temporal hint: weights are read once)
+MOEGQ_DEV uint4 ld_nt(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+}  // namespace moegq

@@ -1,0 +1,88 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moegq {
+
+// gathered matrix-vector (decode): one activation row per pair
+struct QmvArgs {
+  const uint16_t* x;        // activation rows [*, K] bf16
+  const int32_t* lhs;       // row of x per pair, or null -> p / lhs_div
+  int64_t lhs_div;
+  const int32_t* rhs;       // expert per pair, or null -> 0
+  const uint32_t* w0; const uint16_t* s0; const uint16_t* b0;   // [E, N, Kw], [E, N, G]
+  const uint32_t* w1; const uint16_t* s1; const uint16_t* b1;   // GLU: up projection
+  int N, K;
+  uint16_t* out;            // [P, N]
+  const uint16_t* residual; // null or [P, N]
+};
+hipError_t launch_qmv(const QmvArgs& a, int bits, int gs, bool glu, int64_t P, hipStream_t st);
+
+// few-row MFMA (2..16 rows per pair)
+struct SkinnyArgs {
+  const uint16_t* x;        // [X, M, K]
+  const int32_t* lhs; int64_t lhs_div;
+  const int32_t* rhs;
+  const uint32_t* w0; const uint16_t* s0; const uint16_t* b0;
+  const uint32_t* w1; const uint16_t* s1; const uint16_t* b1;
+  int M, N, K;
+  uint16_t* out;            // [P, M, N]
+  const uint16_t* residual; // null or [P, M, N]
+};
+hipError_t launch_skinny(const SkinnyArgs& a, int bits, int gs, bool glu, int64_t P, hipStream_t st);
+
+// expert sort + tile table (single workgroup)
+struct SortArgs {
+  const int32_t* idx; int64_t P; int top_k; int E;
+  int32_t* order; int32_t* lhs; int32_t* sorted_rhs; int32_t* inv;
+  int32_t* counts; int32_t* offsets;
+  int32_t* tiles; int32_t* n_tiles; int bm; int tile_mode;   // tiles may be null
+};
+hipError_t launch_sort(const SortArgs& a, hipStream_t st);
+hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int tile_mode, int32_t* tiles,
+                           int32_t* n_tiles, hipStream_t st);
+
+// prefill tile GEMM over expert-sorted rows
+struct TileArgs {
+  const uint16_t* x;        // activation rows [*, K]
+  const int32_t* lhs;       // virtual row r -> x row (lhs ? lhs[r / rpb] : (r / rpb) / lhs_div) * rpb + r % rpb
+  int64_t lhs_div;
+  int64_t rows_per_batch;   // rpb
+  const int32_t* sorted_rhs;// expert per sorted row (naive mode)
+  const int32_t* offsets;   // [E+1] (naive mode)
+  const int32_t* tiles;     // [cap, 3] scheduled tiles
+  const int32_t* n_tiles;   // device count
+  int64_t P;                // sorted rows
+  int E;
+  const uint32_t* w0; const uint16_t* s0; const uint16_t* b0;
+  const uint32_t* w1; const uint16_t* s1; const uint16_t* b1;
+  int N, K;
+  uint16_t* out;            // [P, N]
+  int bm; int tile_mode;    // 0 scheduled table, 1 naive (loop over experts), 2 dense (expert 0)
+  int64_t grid_tiles;       // upper bound of the tile count (grid size)
+};
+hipError_t launch_tiles(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st);
+
+// combine tail
+hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const uint16_t* scores,
+                          const uint16_t* shared, int64_t T, int top_k, int64_t H, uint16_t* out,
+                          hipStream_t st);
+hipError_t launch_combine_unfused(const uint16_t* y, const int32_t* inv, const uint16_t* scores,
+                                  const uint16_t* shared, int64_t T, int top_k, int64_t H,
+                                  uint16_t* out, uint16_t* scratch, hipStream_t st);
+
+// glue
+hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t K, float eps,
+                           uint16_t* out, hipStream_t st);
+hipError_t launch_sigmoid_gate(const uint16_t* s, const uint16_t* z, int64_t zs, int64_t T, int64_t H,
+                               uint16_t* out, hipStream_t st);
+hipError_t launch_kv_feed(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t M,
+                          int64_t Nq, int64_t Nk, int64_t Nv, uint16_t* out, hipStream_t st);
+hipError_t launch_iota(int32_t* dst, int64_t n, hipStream_t st);
+hipError_t launch_validate(const int32_t* idx, int64_t n, int64_t E, int sorted, int32_t* flag,
+                           hipStream_t st);
+hipError_t launch_fill_selfcheck(uint16_t* y, int32_t* inv, uint16_t* scores, uint16_t* shared,
+                                 int64_t T, int top_k, int64_t H, hipStream_t st);
+
+}  // namespace moegq

@@ -1,0 +1,157 @@
+// Few-row quantized matmul (2..16 activation rows per weight matrix) on MFMA.
+//
+// MLX PR 4787: at 3-16 rows the weights should feed the matrix units rather
+// than a per-row vector loop (the pages' qmv_mma).  On gfx950 a wave computes
+// a 16 (rows, zero-padded) x 16 (outputs) block with v_mfma_f32_16x16x32_bf16.
+//
+// The contraction order over K inside an MFMA is free as long as both
+// operands use the same order, so each lane loads 128-bit runs of its output
+// row (lane (n, j) takes words [4j, 4j+4) of every 16-word chunk) and the
+// activation operand is read at the matching K offsets.  Codes are
+// dequantized exactly in fp32 (q * s + b; nuvec "composed") and rounded to
+// bf16 for the MFMA; all 32 codes of a lane share one group.
+// The four waves of a workgroup take interleaved 128-code chunks of K for the
+// same 16 outputs and are summed through LDS at the end.
+#include "common.h"
+#include "launch.h"
+
+namespace moegq {
+
+template <int BITS, int GS, bool GLU>
+__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs A) {
+  constexpr int NM = GLU ? 2 : 1;
+  constexpr int BV = BITS / 4;          // uint4 per lane per chunk (32 codes)
+  __shared__ f32x4_t red[3][NM][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nrb = (A.N + 15) / 16;
+  const int64_t p = blockIdx.x / nrb;
+  const int n0 = (blockIdx.x % nrb) * 16;
+  const int K = A.K, N = A.N, M = A.M;
+  const int Kw = K * BITS / 32, G = K / GS;
+  const int64_t xb = A.lhs ? (int64_t)A.lhs[p] : p / A.lhs_div;
+  const int64_t e = A.rhs ? (int64_t)A.rhs[p] : 0;
+  const int li = lane % 16, lj = lane / 16;
+  const int n = min(n0 + li, N - 1);
+  const bool m_ok = li < M;
+  const uint16_t* xrow = A.x + (xb * M + (m_ok ? li : 0)) * (int64_t)K;
+
+  const uint32_t* wr[NM];
+  const uint16_t* sr[NM];
+  const uint16_t* br[NM];
+  wr[0] = A.w0 + (e * N + n) * (int64_t)Kw;
+  sr[0] = A.s0 + (e * N + n) * (int64_t)G;
+  br[0] = A.b0 + (e * N + n) * (int64_t)G;
+  if (GLU) {
+    wr[NM - 1] = A.w1 + (e * N + n) * (int64_t)Kw;
+    sr[NM - 1] = A.s1 + (e * N + n) * (int64_t)G;
+    br[NM - 1] = A.b1 + (e * N + n) * (int64_t)G;
+  }
+  f32x4_t acc[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nchunk = (K + 127) / 128;
+  for (int c = wave; c < nchunk; c += 4) {
+    const int kl = c * 128 + 32 * lj;          // first of this lane's 32 codes
+    const bool ok = kl < K;
+    uint4 cw[NM][BV];
+    float s[NM], b[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+#pragma unroll
+      for (int v = 0; v < BV; ++v)
+        cw[m][v] = ok ? ld_nt(reinterpret_cast<const uint4*>(wr[m] + kl * BITS / 32 + 4 * v))
+                      : make_uint4(0, 0, 0, 0);
+      s[m] = ok ? bf16_to_f32(sr[m][kl / GS]) : 0.f;
+      b[m] = ok ? bf16_to_f32(br[m][kl / GS]) : 0.f;
+    }
+    // activation operand for the four MFMA steps: step st covers codes
+    // [kl + 8 st, kl + 8 st + 8) of lane group lj
+    bf16x8_t xa[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint4 v = (ok && m_ok) ? *reinterpret_cast<const uint4*>(xrow + kl + 8 * st) : make_uint4(0, 0, 0, 0);
+      xa[st] = __builtin_bit_cast(bf16x8_t, v);
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        uint32_t o[4];
+        if (BITS == 4) {
+          const uint32_t w = (&cw[m][0].x)[st];
+          const uint32_t t0 = w & 0x0F0F0F0Fu, t1 = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bf16x2_t pr = {(__bf16)fmaf((float)((t0 >> (8 * j)) & 0xFFu), s[m], b[m]),
+                           (__bf16)fmaf((float)((t1 >> (8 * j)) & 0xFFu), s[m], b[m])};
+            o[j] = __builtin_bit_cast(uint32_t, pr);
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t w = (&cw[m][0].x)[2 * st + h];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              bf16x2_t pr = {(__bf16)fmaf((float)((w >> (16 * j)) & 0xFFu), s[m], b[m]),
+                             (__bf16)fmaf((float)((w >> (16 * j + 8)) & 0xFFu), s[m], b[m])};
+              o[2 * h + j] = __builtin_bit_cast(uint32_t, pr);
+            }
+          }
+        }
+        const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[st], bw, acc[m], 0, 0, 0);
+      }
+    }
+  }
+  // sum the four waves' partial blocks
+  if (wave > 0) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) red[wave - 1][m][lane] = acc[m];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int w = 0; w < 3; ++w) acc[m] += red[w][m][lane];
+  // C[row = 4*lj + q][col = li]
+  const int col = n0 + li;
+  if (col >= N) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 4 * lj + q;
+    if (row < M) {
+      const int64_t o = (p * M + row) * (int64_t)N + col;
+      float v = GLU ? glu(acc[0][q], acc[NM - 1][q]) : acc[0][q];
+      if (!GLU && A.residual) v = bf16_to_f32(f32_to_bf16(v)) + bf16_to_f32(A.residual[o]);
+      A.out[o] = f32_to_bf16(v);
+    }
+  }
+}
+
+template <int BITS, int GS, bool GLU>
+static hipError_t launch_sk(const SkinnyArgs& a, int64_t P, hipStream_t st) {
+  const int64_t nrb = (a.N + 15) / 16;
+  hipLaunchKernelGGL((skinny_kernel<BITS, GS, GLU>), dim3((unsigned)(nrb * P)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int BITS, bool GLU>
+static hipError_t launch_sk_gs(const SkinnyArgs& a, int gs, int64_t P, hipStream_t st) {
+  switch (gs) {
+    case 32: return launch_sk<BITS, 32, GLU>(a, P, st);
+    case 64: return launch_sk<BITS, 64, GLU>(a, P, st);
+    case 128: return launch_sk<BITS, 128, GLU>(a, P, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_skinny(const SkinnyArgs& a, int bits, int gs, bool glu, int64_t P, hipStream_t st) {
+  if (P <= 0 || a.N <= 0) return hipSuccess;
+  if (bits == 4) return glu ? launch_sk_gs<4, true>(a, gs, P, st) : launch_sk_gs<4, false>(a, gs, P, st);
+  if (bits == 8) return glu ? launch_sk_gs<8, true>(a, gs, P, st) : launch_sk_gs<8, false>(a, gs, P, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moegq

@@ -1,0 +1,122 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before any HIP call
+(the format's error catalogue: nuvec-core "invalid_arguments_are_rejected",
+"gather_qmm_selects_batches")."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moegq.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import moe_expert_gathered_amd as m
+    if not os.path.exists(m.library_path):
+        pytest.fail("libmoegq.so not built (run `python -m moe_expert_gathered_amd.build`)")
+    return m.lib()
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moegq_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    syms = header_symbols()
+    assert len(syms) >= 15
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_status_strings_and_version(L):
+    assert L.moegq_version().startswith(b"moegq")
+    for code in range(0, -12, -1):
+        assert L.moegq_status_string(code) != b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x100000)       # never dereferenced: every call below fails validation
+
+
+def gq(L, **kw):
+    a = dict(x=FAKE, x_dtype=0, X=4, M=1, K=256, w=FAKE, w_dtype=5, s=FAKE, b=FAKE, E=8, N=64,
+             lhs=None, lhs_div=1, rhs=FAKE, idx_dtype=4, P=4, sorted=0, transpose=1, gs=64, bits=4,
+             out=FAKE, ws=None, wsb=0)
+    a.update(kw)
+    return L.moegq_gather_qmm(a["x"], a["x_dtype"], a["X"], a["M"], a["K"], a["w"], a["w_dtype"], a["s"], a["b"],
+                              a["E"], a["N"], a["lhs"], a["lhs_div"], a["rhs"], a["idx_dtype"], a["P"], a["sorted"],
+                              a["transpose"], a["gs"], a["bits"], a["out"], a["ws"], a["wsb"], None)
+
+
+def test_gather_qmm_error_catalogue(L):
+    import moe_expert_gathered_amd as m
+    assert gq(L, gs=48) == -3                       # group size 48
+    assert gq(L, bits=7) == -2                      # bits 7
+    assert gq(L, bits=3) == -6                      # valid width, not built here
+    assert gq(L, K=96) == -4                        # K not divisible by the group size
+    assert gq(L, x_dtype=m.I32) == -5               # integer activations
+    assert gq(L, x_dtype=m.F64) == -5               # f64 activations
+    assert gq(L, x_dtype=m.F32) == -6               # f32: valid, not built
+    assert gq(L, w_dtype=m.F32) == -5               # packed weights must be u32
+    assert gq(L, idx_dtype=m.F32) == -5             # float indices
+    assert gq(L, transpose=0) == -6                 # transpose=False not built
+    assert gq(L, rhs=None) == -1
+    assert gq(L, x=ctypes.c_void_p(0x100008)) == -11
+    assert gq(L, lhs_div=0) == -4
+    assert gq(L, lhs_div=1, X=2) == -4              # pair rows past x's batch
+    assert gq(L, M=40) == -7                        # tile route needs a workspace
+    assert gq(L, sorted=1, P=128, X=128) == -7      # grouped route needs a workspace
+    # empty products launch nothing and succeed, even with null pointers
+    assert gq(L, P=0, x=None, w=None, out=None, rhs=None) == 0
+    assert gq(L, M=0, x=None, out=None) == 0
+
+
+def test_other_entry_points_validate(L):
+    p = FAKE
+    # affine_qmm: inner-size / group checks
+    assert L.moegq_affine_qmm(p, 0, 3, 63, p, 5, p, p, 16, 1, 64, 4, None, p, None) == -4
+    assert L.moegq_affine_qmm(p, 3, 3, 64, p, 5, p, p, 16, 1, 64, 4, None, p, None) == -5
+    assert L.moegq_affine_qmm(None, 0, 0, 64, None, 5, None, None, 16, 1, 64, 4, None, None, None) == 0
+    # switch_glu
+    args = [p, 4, 256, 128, 8, p, 2] + [p] * 9
+    assert L.moegq_switch_glu(*args, 64, 4, 1, 0, 0, p, None, None, 0, None) == -7   # no workspace
+    assert L.moegq_switch_glu(*args, 64, 4, 2, 0, 0, p, None, None, 0, None) == -1   # sorted needs inv
+    assert L.moegq_switch_glu(*args, 64, 4, 1, 0, 48, p, None, None, 0, None) == -4  # bm
+    assert L.moegq_switch_glu(*args, 64, 4, 7, 0, 0, p, None, None, 0, None) == -4   # mode
+    assert L.moegq_switch_glu(p, 0, 256, 128, 8, p, 2, *[p] * 9, 64, 4, 1, 0, 0, p, None, None, 0, None) == 0
+    # combine
+    assert L.moegq_moe_combine(p, None, p, None, 4, 8, 12, p, None) == -4           # H % 8
+    assert L.moegq_moe_combine(None, None, None, None, 0, 8, 16, None, None) == 0
+    assert L.moegq_moe_combine_unfused(p, None, p, None, 4, 8, 16, p, None, 0, None) == -7
+    # sort / schedule
+    assert L.moegq_sort_pairs(p, 2, 4, 8, 16, None, None, None, p, p, p, None, 0, None) == -5  # float idx
+    assert L.moegq_sort_pairs(p, 4, 4, 8, 2000, None, None, None, p, p, p, None, 0, None) == -6
+    assert L.moegq_schedule_tiles(p, 4, 33, 16, 0, p, 3, p, None) == -7            # capacity
+    assert L.moegq_schedule_tiles(p, 4, 33, 24, 0, p, 100, p, None) == -4          # bm
+    assert L.moegq_selfcheck(None, 0, None) == -7
+
+
+def test_workspace_sizes(L):
+    import moe_expert_gathered_amd as m
+    assert m.workspace_bytes(m.OP_SWITCH_GLU_DECODE, 8, 288, 2048) >= 8 * 2048 * 2
+    big = m.workspace_bytes(m.OP_SWITCH_GLU_SORTED, 16384, 256, 512, 16)
+    assert big >= 16384 * 512 * 2 + 3 * 16384 * 4
+    assert m.workspace_bytes(m.OP_SWITCH_GLU_SORTED, 16384, 256, 512, 0) == big
+    assert m.workspace_bytes(99, 1, 1, 1, 0) == 0
+    assert m.switch_glu_mode(1, 8, 288) == m.MODE_DECODE
+    assert m.switch_glu_mode(2048, 8, 256) == m.MODE_SORTED
+
+
+def test_no_cpu_fallback(tmp_path, monkeypatch):
+    """The binding refuses to run without the library (no silent fallback)."""
+    import importlib
+    import moe_expert_gathered_amd as m
+    monkeypatch.setattr(m, "library_path", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(m, "_LIB", None)
+    with pytest.raises(ImportError):
+        m.lib()
+    importlib.reload(m)

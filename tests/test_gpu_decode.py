@@ -1,0 +1,137 @@
+"""GPU parity: decode path (gathered qmv, SwitchGLU DECODE) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_parity, bf, host_bf, i32, triple, words
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import moe_expert_gathered_amd as m
+    m.lib()
+    return m
+
+
+def _experts(ex):
+    return [triple(m) for m in ex]
+
+
+def test_tiny_switch_glu_decode_and_sorted(mg):
+    """Tiny SwitchGLU: E=8, top-2, hidden 256, inter 128, 4-bit GS 64, M=4."""
+    sh = synth.TINY
+    ex = synth.expert_set(0, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode="drawn")
+    x = synth.activations(0, 4, sh.H)
+    idx = synth.sorted_topk(0, 4, sh.E, sh.top_k)
+    want = oracle.switch_glu(x, idx, *ex, gs=sh.gs, bits=sh.bits).reshape(-1, sh.H)
+    g = _experts(ex)
+    y, inv, mode = mg.switch_glu(bf(x), i32(idx), *g, group_size=sh.gs, bits=sh.bits, mode=mg.MODE_DECODE)
+    assert mode == mg.MODE_DECODE
+    assert_parity(host_bf(y), want, name="decode")
+    y2, inv2, _ = mg.switch_glu(bf(x), i32(idx), *g, group_size=sh.gs, bits=sh.bits, mode=mg.MODE_SORTED)
+    order = oracle.sort_pairs(idx, sh.E)[0]
+    assert_parity(host_bf(y2), want[order], name="sorted")
+    assert np.array_equal(inv2.cpu().numpy(), oracle.sort_pairs(idx, sh.E)[3])
+
+
+@pytest.mark.parametrize("E,N,K,bits,gs,P", [
+    (8, 64, 512, 4, 64, 6), (8, 36, 192, 4, 32, 5), (8, 13, 96, 8, 32, 3), (4, 40, 128, 8, 128, 4),
+    (3, 300, 4096, 4, 128, 5), (2, 257, 2560, 8, 64, 3), (5, 64, 9728, 4, 64, 2), (1, 8, 32, 4, 32, 1)])
+def test_gather_qmv_shapes(mg, E, N, K, bits, gs, P):
+    """M=1 rows per pair, ragged N, K off the 256-word slice, every group size."""
+    g = np.random.default_rng(E * 1000 + N + K + bits)
+    W = [synth.drawn_matrix(g, N, K, gs, bits) for _ in range(E)]
+    w, s, b = (np.stack([m[i] for m in W]) for i in range(3))
+    X = P + 2
+    x = synth.to_bf16(g.standard_normal((X, 1, K)))
+    lhs = g.integers(0, X, P)
+    rhs = (np.arange(P) * 7 + 3) % E
+    want = oracle.gather_qmm(x, w, s, b, lhs=lhs, rhs=rhs, gs=gs, bits=bits)
+    out = mg.gather_qmm(bf(x), words(w), bf(s), bf(b), rhs_indices=i32(rhs), lhs_indices=i32(lhs),
+                        group_size=gs, bits=bits)
+    assert out.shape == (P, 1, N)
+    assert_parity(host_bf(out), want, name=f"qmv {E},{N},{K},{bits},{gs}")
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 64), (4, 32), (8, 128), (8, 32)])
+@pytest.mark.parametrize("M", [1, 3, 16, 40])
+def test_integer_exact_bitwise(mg, bits, gs, M):
+    """Exact scales/biases and small-integer activations: every product and
+    partial sum is exact, so GPU and oracle agree bit for bit on every route
+    (M=1 qmv, 2..16 MFMA few-row, >16 MFMA tiles)."""
+    g = np.random.default_rng(100 + M + bits + gs)
+    N, K = 80, 512
+    w, s, b = synth.integer_exact(g, N, K, gs, bits)
+    x = synth.integer_x(g, M, K)
+    want = oracle.quantized_matmul(x, w, s, b, True, gs, bits)
+    got = host_bf(mg.affine_qmm(bf(x), words(w), bf(s), bf(b), group_size=gs, bits=bits))
+    assert np.array_equal(got, want)
+
+
+def test_expert_routing_bitwise(mg):
+    """Expert e has scale 0, bias e+1: y = (e+1) * sum(x) exactly; a wrong
+    expert or a wrong activation row shows bitwise."""
+    E, N, K, gs = 6, 24, 256, 64
+    w = np.zeros((E, N, K // 8), np.uint32)
+    s = np.zeros((E, N, K // gs), np.uint16)
+    b = np.broadcast_to(synth.to_bf16(np.arange(1, E + 1, dtype=np.float32))[:, None, None], (E, N, K // gs)).copy()
+    g = np.random.default_rng(7)
+    x = synth.integer_x(g, 5, K)[:, None, :]
+    lhs = np.array([4, 0, 2, 2, 1, 3, 3])
+    rhs = np.array([5, 0, 2, 3, 1, 4, 0])
+    want = oracle.gather_qmm(x, w, s, b, lhs=lhs, rhs=rhs, gs=gs, bits=4)
+    got = mg.gather_qmm(bf(x), words(w), bf(s), bf(b), rhs_indices=i32(rhs), lhs_indices=i32(lhs), group_size=gs)
+    assert np.array_equal(host_bf(got), want)
+
+
+@pytest.mark.parametrize("M,mode", [(1, "minmax"), (4, "drawn")])
+def test_decode_full_shape(mg, M, mode):
+    """MoE decode at hidden 4096, inter 2048, E=288, top-8, 4-bit GS 64; the
+    selected experts are drawn (min-max of N(0,1), or drawn codes), the
+    others stay zero on both sides."""
+    sh = synth.DECODE
+    idx = synth.sorted_topk(1, M, sh.E, sh.top_k)
+    sel = np.unique(idx)
+    x = synth.activations(1, M, sh.H)
+    ex = synth.expert_set(1, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode=mode, experts=sel)
+    want = oracle.switch_glu(x, idx, *ex, gs=sh.gs, bits=sh.bits).reshape(-1, sh.H)
+    y, _, _ = mg.switch_glu(bf(x), i32(idx), *_experts(ex), group_size=sh.gs, bits=sh.bits, mode=mg.MODE_DECODE)
+    assert_parity(host_bf(y), want, name=f"decode M={M}")
+
+
+def test_empty_inputs(mg):
+    sh = synth.TINY
+    ex = _experts(synth.expert_set(0, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode="drawn"))
+    x = torch.zeros((0, sh.H), dtype=torch.bfloat16, device="cuda")
+    idx = torch.zeros((0, 2), dtype=torch.int32, device="cuda")
+    y, _, _ = mg.switch_glu(x, idx, *ex, group_size=sh.gs, bits=sh.bits, mode=mg.MODE_DECODE)
+    assert y.shape == (0, sh.H)
+    w0, s0, b0 = ex[2][0][0], ex[2][1][0], ex[2][2][0]        # down of expert 0: [H, I/8]
+    out = mg.affine_qmm(torch.zeros((0, sh.I), dtype=torch.bfloat16, device="cuda"), w0, s0, b0, group_size=sh.gs)
+    assert out.shape == (0, sh.H)
+
+
+@pytest.mark.parametrize("M", [1, 3, 20])
+def test_gather_qmm_glu(mg, M):
+    """SwitchGLU's gate/up half over gathered experts (decode layout x[T, K],
+    pair p on token p // top_k) against the oracle's SwitchGLU intermediate."""
+    g = np.random.default_rng(90 + M)
+    E, N, K, top_k, T = 6, 96, 512, 2, 5
+    gate = [synth.drawn_matrix(g, N, K, 64, 4) for _ in range(E)]
+    up = [synth.drawn_matrix(g, N, K, 64, 4) for _ in range(E)]
+    G = synth.stack_experts(gate)
+    U = synth.stack_experts(up)
+    x = synth.to_bf16(g.standard_normal((T, M, K)))
+    rhs = g.integers(0, E, T * top_k)
+    gg = oracle.gather_qmm(x, *G, lhs=np.arange(T * top_k) // top_k, rhs=rhs, gs=64, bits=4)
+    uu = oracle.gather_qmm(x, *U, lhs=np.arange(T * top_k) // top_k, rhs=rhs, gs=64, bits=4)
+    want = oracle.f64_to_bf16(oracle.silu(oracle.bf16_to_f64(gg)) * oracle.bf16_to_f64(uu))
+    xd = bf(x) if M > 1 else bf(x[:, 0, :])
+    got = mg.gather_qmm_glu(xd, triple(G), triple(U), i32(rhs), lhs_div=top_k, group_size=64, bits=4)
+    assert_parity(host_bf(got), want, name=f"glu M={M}")

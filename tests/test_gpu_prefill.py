@@ -1,0 +1,153 @@
+"""GPU parity: expert sort, tile schedules, sorted SwitchGLU (prefill) and the
+whole MoE layer with combine, against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_parity, bf, host_bf, host_i32, i32, triple
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import moe_expert_gathered_amd as m
+    m.lib()
+    return m
+
+
+SORT_CASES = [(1, 8, 288), (4, 8, 288), (7, 2, 8), (128, 8, 256), (331, 8, 256), (2048, 8, 256),
+              (4123, 8, 288), (3, 4, 1024), (5000, 1, 3), (1, 1, 1)]
+
+
+@pytest.mark.parametrize("T,top_k,E", SORT_CASES)
+def test_sort_pairs_bitwise(mg, T, top_k, E):
+    if T >= 128:
+        idx, _ = synth.zipf_routing(3, T, E, top_k, sub=T)
+    else:
+        idx = synth.sorted_topk(5, T, E, top_k, sub=T)
+    got = mg.sort_pairs(i32(idx), E)
+    want = oracle.sort_pairs(idx, E)
+    for name, g, w in zip(("order", "lhs", "sorted_rhs", "inv", "counts", "offsets"), got, want):
+        assert np.array_equal(host_i32(g), w), name
+
+
+def test_sort_pairs_unsorted_slots_and_duplicates(mg):
+    # slots not in ascending order and repeated experts inside a token: stability by pair index
+    g = np.random.default_rng(3)
+    idx = g.integers(0, 5, size=(300, 6)).astype(np.int32)
+    got = mg.sort_pairs(i32(idx), 5)
+    want = oracle.sort_pairs(idx, 5)
+    for a, b in zip(got, want):
+        assert np.array_equal(host_i32(a), b)
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_schedule_tiles_bitwise(mg, bm, mode):
+    g = np.random.default_rng(bm + mode)
+    for trial in range(4):
+        E = int(g.integers(1, 300))
+        counts = (g.integers(0, 200, E) * (g.random(E) < 0.6)).astype(np.int64)
+        if trial == 0:
+            E, counts = 4, np.array([13, 8, 2, 10])   # MLX PR 4567 example
+        offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        P = int(offsets[-1])
+        tiles, n = mg.schedule_tiles(i32(offsets), E, P, bm, mode)
+        n = int(n.item())
+        if mode == 0:
+            want = oracle.schedule_tiles(offsets, bm)
+            assert n == len(want)
+            assert np.array_equal(host_i32(tiles[:n]), want)
+        else:
+            want, _ = oracle.naive_tiles(offsets, bm)
+            assert n == len(want)
+            t = host_i32(tiles[:n])
+            assert np.array_equal(t[:, [0, 2]], want) and (t[:, 1] == -1).all()
+
+
+def _prefill_case(T, cfg=3, shape=synth.PREFILL, mode="drawn", sub=0):
+    sh = shape
+    idx, scores = synth.zipf_routing(cfg, T, sh.E, sh.top_k, sub=sub)
+    x = synth.activations(cfg, T, sh.H, sub=sub)
+    ex = synth.expert_set(cfg, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode=mode, experts=np.unique(idx))
+    return sh, idx, scores, x, ex
+
+
+@pytest.mark.parametrize("T", [128, 331])
+@pytest.mark.parametrize("tile_mode,bm", [(0, 16), (0, 32), (0, 64), (0, 128), (1, 16), (1, 64)])
+def test_sorted_switch_glu(mg, T, tile_mode, bm):
+    """MoE prefill shape (hidden 2048, E=256, top-8, inter 512, 4-bit GS 64):
+    expert-sorted gate/up + SiLU and down over scheduled or naive tiles."""
+    sh, idx, scores, x, ex = _prefill_case(T)
+    want_tok = oracle.switch_glu(x, idx, *ex, gs=sh.gs, bits=sh.bits).reshape(-1, sh.H)
+    order, *_, inv_w, _, _ = oracle.sort_pairs(idx, sh.E)
+    y, inv, mode = mg.switch_glu(bf(x), i32(idx), *[triple(m) for m in ex], group_size=sh.gs, bits=sh.bits,
+                                 mode=mg.MODE_SORTED, tile_mode=tile_mode, bm=bm)
+    assert np.array_equal(host_i32(inv), inv_w)
+    assert_parity(host_bf(y), want_tok[order], name=f"sorted T={T} bm={bm} mode={tile_mode}")
+
+
+@pytest.mark.parametrize("T", [128, 331])
+def test_moe_layer_with_combine(mg, T):
+    """Whole layer: sorted SwitchGLU, gated shared expert, fused combine."""
+    sh, idx, scores, x, ex = _prefill_case(T, sub=1)
+    shp = synth.shared_params(3, sh.H, sh.shared_I, sh.gs, sh.bits)
+    want, inter = oracle.moe_prefill_layer(x, idx, scores, ex, shp, gs=sh.gs, bits=sh.bits)
+    xd = bf(x)
+    y, inv, _ = mg.switch_glu(xd, i32(idx), *[triple(m) for m in ex], group_size=sh.gs, bits=sh.bits,
+                              mode=mg.MODE_SORTED)
+    g_, u_, d_, r_ = (triple(m) for m in shp)
+    h = mg.affine_qmm_glu(xd, g_, u_, group_size=sh.gs, bits=sh.bits)
+    s_ = mg.affine_qmm(h, *d_, group_size=sh.gs, bits=sh.bits)
+    z = mg.affine_qmm(xd, *r_, group_size=sh.gs, bits=sh.bits)
+    shared = mg.sigmoid_gate(s_, z)
+    assert_parity(host_bf(shared), inter["shared"], name="shared expert")
+    out = mg.moe_combine(y, inv, bf(scores), shared)
+    assert_parity(host_bf(out), want, name=f"layer T={T}")
+    # the fused combine equals the unfused tail bit for bit, and the oracle's
+    # combine on the GPU's own expert outputs
+    out2 = mg.moe_combine_unfused(y, inv, bf(scores), shared)
+    assert np.array_equal(host_bf(out), host_bf(out2))
+    assert np.array_equal(host_bf(out), oracle.combine(host_bf(y), host_i32(inv), scores, host_bf(shared)))
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 64), (8, 128)])
+def test_large_prefill_sampled(mg, bits, gs):
+    """Large MoE prefill (hidden 4096, E=288, top-8, inter 2048) at 713 rows:
+    the GPU runs the whole problem; sampled experts are checked against the
+    oracle row by row (all their sorted rows, every column)."""
+    sh = synth.LARGE4 if bits == 4 else synth.LARGE8
+    T = 713
+    idx, _ = synth.zipf_routing(4, T, sh.E, sh.top_k)
+    x = synth.activations(4, T, sh.H)
+    ex = synth.expert_set(4 + bits, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode="words")
+    for tile_mode, bm in ((0, 32), (1, 16)):
+        y, inv, _ = mg.switch_glu(bf(x), i32(idx), *[triple(m) for m in ex], group_size=sh.gs, bits=sh.bits,
+                                  mode=mg.MODE_SORTED, tile_mode=tile_mode, bm=bm)
+        yh = host_bf(y)
+        order, lhs, srhs, inv_w, counts, offsets = oracle.sort_pairs(idx, sh.E)
+        assert np.array_equal(host_i32(inv), inv_w)
+        hot = int(np.argmax(counts))
+        rare = int(np.flatnonzero(counts == counts[counts > 0].min())[0])
+        for e in (hot, rare):
+            rows = np.arange(offsets[e], offsets[e + 1])
+            toks = lhs[rows]
+            sub_idx = np.full((len(rows), 1), e, np.int32)
+            want = oracle.switch_glu(x[toks], sub_idx, *ex, gs=sh.gs, bits=sh.bits)[:, 0]
+            assert_parity(yh[rows], want, name=f"expert {e} bits {bits} mode {tile_mode}")
+
+
+def test_auto_mode_and_identity_inv(mg):
+    sh = synth.TINY
+    ex = [triple(m) for m in synth.expert_set(0, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode="drawn")]
+    x = synth.activations(0, 4, sh.H)
+    idx = synth.sorted_topk(0, 4, sh.E, sh.top_k)
+    inv = torch.full((8,), -1, dtype=torch.int32, device="cuda")
+    y, inv, mode = mg.switch_glu(bf(x), i32(idx), *ex, group_size=sh.gs, bits=sh.bits, inv=inv)
+    assert mode == mg.MODE_DECODE
+    assert host_i32(inv).tolist() == list(range(8))

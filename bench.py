@@ -1,0 +1,399 @@
+"""Benchmark of the gathered affine-quantized MoE path on one MI355X.
+
+Headline (``value``): MoE decode at hidden 4096, inter 2048, 288 experts,
+top-8, 4-bit weights with group size 64, one token: effective weight GB/s
+(tokens * top_k * bytes per expert / time, duplicates counted) over a chain of
+42 distinct index sets cycled step after step, so the experts come from HBM.
+A step is one MoE decode layer: gate/up gather + SiLU (one kernel), down
+gather, and the combine over top_k.
+
+Further legs reported in the same JSON line (not ``value``): the same decode
+at 4 tokens and isolated (one index set, L2/MALL-resident), the MoE-layer
+prefill at 2048 rows (hidden 2048, 256 experts, inter 512, gated shared
+expert, combine), the expert-aware vs naive tile schedules on the large
+prefill (hidden 4096, 288 experts, inter 2048) and the dense few-row chain
+(36 decoder layers, 8 weight sets).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs a,b,...]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=42 * 4)
+    ap.add_argument("--warmup", type=int, default=42)
+    ap.add_argument("--legs", default="decode,prefill,large,dense,cpu")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream the kernels run on)."""
+
+    def __init__(self, torch):
+        self.t = torch
+        self.ev = []
+
+    def mark(self, tag):
+        e = self.t.cuda.Event(enable_timing=True)
+        e.record()
+        self.ev.append((tag, e))
+
+    def spans(self):
+        self.t.cuda.synchronize()
+        out = {}
+        for (tag, a), (_, b) in zip(self.ev[:-1], self.ev[1:]):
+            if tag is None:
+                continue
+            out.setdefault(tag, []).append(a.elapsed_time(b) * 1e3)   # us
+        return out
+
+
+# ----------------------------------------------------------------------------- decode
+def graph_time_us(torch, fn, n, reps=3, check=None):
+    """Capture fn(0..n-1) into one HIP graph, verify replays against an eager
+    run (check() -> tensor), and return the average microseconds per call over
+    `reps` replays, timed with HIP events on the capturing stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    if check is not None:
+        for i in range(n):
+            fn(i)
+        ref = check().clone()
+        for _ in range(3):
+            check().zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(check(), ref):
+                raise RuntimeError("graph replay differs from eager execution")
+    g.replay()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * n)
+
+
+def decode_leg(torch, m, synth, M, steps, warmup, n_sets=42, isolated=False, cfg=1):
+    """One MoE decode layer per step: gather gate/up + SiLU, then gather down
+    fused with the combine (scores 1/8, no shared expert)."""
+    sh = synth.DECODE
+    dev = torch.device("cuda")
+    gate, up, down = synth.device_expert_set(dev, cfg, sh.E, sh.H, sh.I, sh.gs, sh.bits)
+    idx_sets = [torch.from_numpy(synth.sorted_topk(cfg, M, sh.E, sh.top_k, sub=i)).to(dev) for i in range(n_sets)]
+    x = torch.from_numpy(synth.activations(cfg, M, sh.H).view(np.int16)).view(torch.bfloat16).to(dev)
+    scores = torch.full((M, sh.top_k), 0.125, dtype=torch.bfloat16, device=dev)
+    P = M * sh.top_k
+    h = torch.empty((P, sh.I), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((M, sh.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(m.workspace_bytes(m.OP_MOE_DECODE, P, sh.E, sh.I), dtype=torch.uint8, device=dev)
+
+    def idx_of(i):
+        return idx_sets[0 if isolated else i % n_sets]
+
+    def step(i):
+        m.moe_decode(x, idx_of(i), scores, gate, up, down, group_size=sh.gs, bits=sh.bits, out=out, workspace=ws)
+
+    def k1(i):
+        m.gather_qmm_glu(x, gate, up, idx_of(i).view(-1), lhs_div=sh.top_k, group_size=sh.gs, bits=sh.bits, out=h)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    el_eager = time.perf_counter() - t0
+    # headline timing: HIP graph of the whole 42-layer chain, replayed
+    layer_us = graph_time_us(torch, step, n_sets, reps=max(1, steps // n_sets), check=lambda: out)
+    k1_us = graph_time_us(torch, k1, n_sets, reps=max(1, steps // n_sets), check=lambda: h)
+    bpe = 3 * (sh.I * sh.H * sh.bits // 8 + 2 * sh.I * (sh.H // sh.gs) * 2)
+    eff = M * sh.top_k * bpe
+    k1_bytes = P * 2 * sh.I * (sh.H * sh.bits // 8 + 2 * (sh.H // sh.gs) * 2) + M * sh.H * 2 + P * sh.I * 2
+    res = {
+        "tokens": M, "isolated": isolated, "ms_per_layer": layer_us * 1e-3,
+        "effective_gbs": eff / (layer_us * 1e-6) / 1e9, "timing": "hip graph of the 42-layer chain",
+        "eager_ms_per_layer": el_eager / steps * 1e3, "eager_effective_gbs": eff * steps / el_eager / 1e9,
+        "gate_up_us": k1_us, "down_combine_us_approx": layer_us - k1_us,
+        "gate_up_bytes": k1_bytes, "gate_up_gbs": k1_bytes / (k1_us * 1e-6) / 1e9, "bytes_per_expert": bpe,
+    }
+    del gate, up, down
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- prefill
+def prefill_leg(torch, m, synth, T=2048, steps=20, warmup=5, cfg=3):
+    sh = synth.PREFILL
+    dev = torch.device("cuda")
+    gate, up, down = synth.device_expert_set(dev, cfg, sh.E, sh.H, sh.I, sh.gs, sh.bits)
+    sg, su, sd = synth.device_expert_set(dev, cfg + 100, 1, sh.H, sh.shared_I, sh.gs, sh.bits)
+    sg, su, sd = [tuple(t[0] for t in trip) for trip in (sg, su, sd)]
+    grow = tuple(t[0] for t in synth.device_drawn_words(dev, (cfg, 3, 3), (1, 1), sh.H, sh.gs, sh.bits))
+    idx_np, scores_np = synth.zipf_routing(cfg, T, sh.E, sh.top_k)
+    idx = torch.from_numpy(idx_np).to(dev)
+    scores = torch.from_numpy(scores_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    x = torch.from_numpy(synth.activations(cfg, T, sh.H).view(np.int16)).view(torch.bfloat16).to(dev)
+    P = T * sh.top_k
+    y = torch.empty((P, sh.H), dtype=torch.bfloat16, device=dev)
+    inv = torch.empty(P, dtype=torch.int32, device=dev)
+    hs = torch.empty((T, sh.shared_I), dtype=torch.bfloat16, device=dev)
+    s_ = torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev)
+    z = torch.empty((T, 1), dtype=torch.bfloat16, device=dev)
+    shared = torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev)
+    counts = np.bincount(idx_np.reshape(-1), minlength=sh.E)
+    active = int((counts > 0).sum())
+    bm = 0
+    tm = Timer(torch)
+
+    def step(timed):
+        if timed:
+            tm.mark("routed_experts")
+        m.switch_glu(x, idx, gate, up, down, group_size=sh.gs, bits=sh.bits, mode=m.MODE_SORTED, bm=bm, y=y,
+                     inv=inv)
+        if timed:
+            tm.mark("shared_expert")
+        m.affine_qmm_glu(x, sg, su, group_size=sh.gs, bits=sh.bits, out=hs)
+        m.affine_qmm(hs, *sd, group_size=sh.gs, bits=sh.bits, out=s_)
+        m.affine_qmm(x, *grow, group_size=sh.gs, bits=sh.bits, out=z)
+        m.sigmoid_gate(s_, z, out=shared)
+        if timed:
+            tm.mark("combine")
+        m.moe_combine(y, inv, scores, shared, out=out)
+        if timed:
+            tm.mark(None)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(False)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    for _ in range(steps):
+        step(True)
+    spans = tm.spans()
+    H, I, SI = sh.H, sh.I, sh.shared_I
+    flops = P * 6 * H * I + T * 6 * H * SI + T * 2 * H
+    B = lambda n, k: n * (k * sh.bits // 8 + 2 * (k // sh.gs) * 2)
+    wbytes = active * (2 * B(I, H) + B(H, I)) + 2 * B(SI, H) + B(H, SI) + B(1, H)
+    act = (T * H * 2 + P * I * 2 * 2 + P * H * 2          # x, h_sorted write+read, y_sorted write
+           + T * SI * 2 * 2 + T * H * 2 * 3               # shared path
+           + P * H * 2 + T * H * 2 * 2)                   # combine: y read, shared read, out write
+    res = {"rows": T, "active_experts": active, "max_load": int(counts.max()), "mean_load": float(P / active),
+           "ms_per_layer": el * 1e3, "gflop": flops / 1e9, "bytes": wbytes + act,
+           "mfma_util": flops / el / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+           "hbm_frac": (wbytes + act) / el / (HBM_PEAK_GBS * 1e9),
+           "kernel_us": {k: float(np.mean(v)) for k, v in spans.items()}}
+    res["roofline_frac"] = max(res["mfma_util"], res["hbm_frac"])
+    del gate, up, down
+    torch.cuda.empty_cache()
+    return res
+
+
+def large_leg(torch, m, synth, T=4123, steps=5, warmup=2, bits=4, cfg=4):
+    sh = synth.LARGE4 if bits == 4 else synth.LARGE8
+    dev = torch.device("cuda")
+    gate, up, down = synth.device_expert_set(dev, cfg, sh.E, sh.H, sh.I, sh.gs, sh.bits)
+    idx_np, _ = synth.zipf_routing(cfg, T, sh.E, sh.top_k)
+    idx = torch.from_numpy(idx_np).to(dev)
+    x = torch.from_numpy(synth.activations(cfg, T, sh.H).view(np.int16)).view(torch.bfloat16).to(dev)
+    P = T * sh.top_k
+    y = torch.empty((P, sh.H), dtype=torch.bfloat16, device=dev)
+    inv = torch.empty(P, dtype=torch.int32, device=dev)
+    counts = np.bincount(idx_np.reshape(-1), minlength=sh.E)
+    res = {"rows": T, "bits": bits, "active_experts": int((counts > 0).sum())}
+    for name, tmode, bm in (("scheduled_bm16", 0, 16), ("naive_bm16", 1, 16), ("scheduled_bm64", 0, 64)):
+        for _ in range(warmup):
+            m.switch_glu(x, idx, gate, up, down, group_size=sh.gs, bits=sh.bits, mode=m.MODE_SORTED,
+                         tile_mode=tmode, bm=bm, y=y, inv=inv)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            m.switch_glu(x, idx, gate, up, down, group_size=sh.gs, bits=sh.bits, mode=m.MODE_SORTED,
+                         tile_mode=tmode, bm=bm, y=y, inv=inv)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        offs = np.concatenate([[0], np.cumsum(counts)])
+        if tmode == 0:
+            tiles = int(sum(-(-int(c) // bm) for c in counts))
+            passes = tiles
+        else:
+            tiles = -(-P // bm)
+            passes = 0
+            for r0 in range(0, P, bm):
+                r1 = min(P, r0 + bm)
+                passes += int(((offs[1:] > r0) & (offs[:-1] < r1) & (counts > 0)).sum())
+        flops = P * 6 * sh.H * sh.I
+        res[name] = {"ms": ms, "tiles": tiles, "k_passes": passes, "mfma_util": flops / (ms * 1e-3) / 2.5e15}
+    del gate, up, down
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- dense chain
+def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=5, warmup=2, cfg=2):
+    dev = torch.device("cuda")
+    d = synth.DENSE
+    sets = synth.device_dense_sets(dev, cfg, gs, bits, d)
+    nw = torch.ones(d["hidden"], dtype=torch.bfloat16, device=dev)
+    per_fwd = 0
+    for name, (N, K) in synth.dense_dims(d).items():
+        per_fwd += N * (K * bits // 8 + 2 * (K // gs) * 2)
+    per_fwd *= d["layers"]
+    res = {"bits": bits, "group_size": gs, "forward_weight_bytes": per_fwd}
+    for M in rows:
+        h0 = torch.randn((M, d["hidden"]), device=dev).to(torch.bfloat16)
+
+        def fwd():
+            h = h0.clone()
+            for li in range(d["layers"]):
+                L = sets[li % d["sets"]]
+                x = m.rms_norm(h, nw)
+                q = m.affine_qmm(x, *L["q"], group_size=gs, bits=bits)
+                k = m.affine_qmm(x, *L["k"], group_size=gs, bits=bits)
+                v = m.affine_qmm(x, *L["v"], group_size=gs, bits=bits)
+                h = m.affine_qmm(m.kv_feed(q, k, v), *L["o"], group_size=gs, bits=bits, residual=h)
+                x = m.rms_norm(h, nw)
+                a = m.affine_qmm_glu(x, L["g"], L["u"], group_size=gs, bits=bits)
+                h = m.affine_qmm(a, *L["dn"], group_size=gs, bits=bits, residual=h)
+            return h
+
+        for _ in range(warmup):
+            fwd()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fwd()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        med = float(np.median(ts))
+        res[f"rows{M}"] = {"ms_per_forward": med * 1e3, "gbs": per_fwd / med / 1e9}
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(torch, synth, n_layers=2, cfg=1):
+    """The oracle (numpy) on a bounded sample of the headline workload: n_layers
+    MoE decode layers at one token, dequantizing only the selected experts,
+    on the same device-drawn weights (copied back for the selected experts)."""
+    import oracle
+    sh = synth.DECODE
+    dev = torch.device("cuda")
+    gate, up, down = synth.device_expert_set(dev, cfg, sh.E, sh.H, sh.I, sh.gs, sh.bits)
+    x = synth.activations(cfg, 1, sh.H)
+    tot = 0.0
+    host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16) if t.dtype == torch.bfloat16 \
+        else t.contiguous().cpu().numpy().view(np.uint32)
+    for i in range(n_layers):
+        idx = synth.sorted_topk(cfg, 1, sh.E, sh.top_k, sub=i)
+        sel = np.unique(idx)
+        pos = {int(e): j for j, e in enumerate(sel)}
+        rid = np.vectorize(lambda e: pos[int(e)])(idx)
+        sub = [tuple(host(t[torch.from_numpy(sel).to(dev)]) for t in trip) for trip in (gate, up, down)]
+        t0 = time.perf_counter()
+        oracle.switch_glu(x, rid, *sub, gs=sh.gs, bits=sh.bits)
+        tot += time.perf_counter() - t0
+    bpe = 3 * (sh.I * sh.H * sh.bits // 8 + 2 * sh.I * (sh.H // sh.gs) * 2)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    del gate, up, down
+    torch.cuda.empty_cache()
+    return {"value": n_layers * sh.top_k * bpe / tot / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_layers} MoE decode layers (1 token, top-8 of 288 experts, hidden 4096, inter 2048, "
+                      f"4-bit GS 64), {tot:.1f} s of CPU time", "seconds": tot}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus N > 1 is not supported "
+                                   "(the multi-GPU design is documented, not built)"}))
+        sys.exit(2)
+    import torch
+    import moe_expert_gathered_amd as m
+    import synth
+    m.lib()
+    legs = set(a.legs.split(","))
+    torch.cuda.set_device(0)
+    log("decode M=1 chained")
+    head = decode_leg(torch, m, synth, 1, a.steps, a.warmup)
+    extra = {"decode_m1_chained": head}
+    if "decode" in legs:
+        log("decode M=1 isolated, M=4 chained")
+        extra["decode_m1_isolated"] = decode_leg(torch, m, synth, 1, a.steps, a.warmup, isolated=True)
+        extra["decode_m4_chained"] = decode_leg(torch, m, synth, 4, a.steps, a.warmup)
+    if "prefill" in legs:
+        log("prefill 2048 rows")
+        extra["prefill_2048"] = prefill_leg(torch, m, synth)
+    if "large" in legs:
+        log("large prefill 4123 rows")
+        extra["large_prefill_4123"] = large_leg(torch, m, synth)
+    if "dense" in legs:
+        log("dense chain")
+        extra["dense_chain"] = dense_leg(torch, m, synth)
+    cpu = None
+    if "cpu" in legs:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(torch, synth)
+    k1_us = head["gate_up_us"]
+    ach = head["gate_up_bytes"] / (k1_us * 1e-6) / 1e9
+    line = {
+        "metric": "effective weight GB/s (M=1/4 MoE decode) + MoE-layer ms at 2048-row prefill",
+        "value": round(head["effective_gbs"], 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(head["ms_per_layer"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "moe_decode_h4096_i2048_e288_top8_w4g64_m1_chain42", "hidden": 4096,
+                   "inter": 2048, "experts": 288, "top_k": 8, "bits": 4, "group_size": 64, "tokens": 1,
+                   "index_sets": 42},
+        "roofline": {"bound": "hbm", "kernel": "qmv_kernel<4,64,glu,2,2> (gathered gate+up, SiLU)", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": head["gate_up_bytes"], "avg_launch_us": round(k1_us, 3)},
+        "cpu_baseline": cpu,
+        "legs": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -66,7 +66,8 @@ enum { MOEGQ_MODE_AUTO = 0, MOEGQ_MODE_DECODE = 1, MOEGQ_MODE_SORTED = 2 };
 enum { MOEGQ_TILES_SCHEDULED = 0, MOEGQ_TILES_NAIVE = 1 };
 /* operations whose workspace can be queried */
 enum { MOEGQ_OP_GATHER_QMM = 0, MOEGQ_OP_SWITCH_GLU_DECODE = 1, MOEGQ_OP_SWITCH_GLU_SORTED = 2,
-       MOEGQ_OP_COMBINE_UNFUSED = 3, MOEGQ_OP_SELFCHECK = 4, MOEGQ_OP_SORT_PAIRS = 5 };
+       MOEGQ_OP_COMBINE_UNFUSED = 3, MOEGQ_OP_SELFCHECK = 4, MOEGQ_OP_SORT_PAIRS = 5,
+       MOEGQ_OP_MOE_DECODE = 6 };
 
 const char* moegq_status_string(int status);
 const char* moegq_version(void);
@@ -75,7 +76,7 @@ const char* moegq_version(void);
  * ignored: GATHER_QMM(P, E, N=M rows per batch, bm ignored),
  * SWITCH_GLU_DECODE(P pairs, E, N = I, bm), SWITCH_GLU_SORTED(P, E, N = I, bm; bm 0 = auto),
  * COMBINE_UNFUSED(P = T*top_k, E ignored, N = H), SELFCHECK(all ignored),
- * SORT_PAIRS(P, E).  Returns 0 for an unknown op. */
+ * SORT_PAIRS(P, E), MOE_DECODE(P = T*top_k, E, N = I).  Returns 0 for an unknown op. */
 size_t moegq_workspace_bytes(int op, int64_t P, int64_t E, int64_t N, int bm);
 
 /*
@@ -175,6 +176,30 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
 
 /* The mode AUTO resolves to for T*top_k pairs over E experts (DECODE or SORTED). */
 int moegq_switch_glu_mode(int64_t T, int64_t top_k, int64_t E);
+
+/*
+ * moe_decode: the routed half of a MoE decode layer in two kernels.  Kernel 1
+ * is the gathered gate/up with silu(gate)*up (MLX issue 4509, moe()); kernel 2
+ * is the gathered down projection fused with the combine tail (MTPLX PR 558:
+ * unsort, x score, sum over top_k, + shared expert), so y never round-trips
+ * through HBM:
+ *   out[t] = bf16( bf16( sum_k bf16(y[t,k] * score[t,k]) ) + shared[t] ),
+ *   y[t,k] = bf16( h[t,k] . dequant(Wd[idx[t,k]])^T ),
+ *   h[t,k] = bf16( silu(bf16(g)) * bf16(u) ),  g/u = x[t] . dequant(Wg/Wu[idx[t,k]])^T.
+ * Bit-identical to moegq_switch_glu (DECODE) followed by moegq_moe_combine.
+ * x [T, H] bf16; idx [T, top_k] int32; scores [T, top_k] bf16; shared [T, H]
+ * bf16 or NULL; weights as moegq_switch_glu; out [T, H] bf16; y [T*top_k, H]
+ * bf16 or NULL (receives the expert outputs when given).
+ * workspace: moegq_workspace_bytes(MOEGQ_OP_MOE_DECODE, T*top_k, E, I, 0)
+ * bytes (for top_k > 8 the two steps run unfused and y must be given).
+ */
+int moegq_moe_decode(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
+                     const int32_t* idx, int64_t top_k, const void* scores, const void* shared,
+                     const void* wg, const void* sg, const void* bg,
+                     const void* wu, const void* su, const void* bu,
+                     const void* wd, const void* sd, const void* bd,
+                     int group_size, int bits, void* out, void* y,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * moe_combine (fused, one pass): MTPLX PR 558 Summary/Motivation -- unsort,

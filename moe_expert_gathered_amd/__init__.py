@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
-           "switch_glu", "switch_glu_mode", "moe_combine", "moe_combine_unfused", "sort_pairs",
+           "switch_glu", "switch_glu_mode", "moe_decode", "moe_combine", "moe_combine_unfused", "sort_pairs",
            "schedule_tiles", "rms_norm", "sigmoid_gate", "kv_feed", "selfcheck",
            "validate_indices", "workspace_bytes", "MODE_AUTO", "MODE_DECODE", "MODE_SORTED",
            "TILES_SCHEDULED", "TILES_NAIVE"]
@@ -29,7 +29,8 @@ OK = 0
 BF16, F16, F32, F64, I32, U32, I64 = range(7)
 MODE_AUTO, MODE_DECODE, MODE_SORTED = 0, 1, 2
 TILES_SCHEDULED, TILES_NAIVE = 0, 1
-OP_GATHER_QMM, OP_SWITCH_GLU_DECODE, OP_SWITCH_GLU_SORTED, OP_COMBINE_UNFUSED, OP_SELFCHECK, OP_SORT_PAIRS = range(6)
+OP_GATHER_QMM, OP_SWITCH_GLU_DECODE, OP_SWITCH_GLU_SORTED, OP_COMBINE_UNFUSED, OP_SELFCHECK, OP_SORT_PAIRS, \
+    OP_MOE_DECODE = range(7)
 
 _DTYPE = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.float64: F64,
           torch.int32: I32, torch.int64: I64}
@@ -59,6 +60,8 @@ _SIGS = {
     "moegq_switch_glu": ([_p, _i64, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _int, _int,
                           _int, _int, _int, _p, _p, _p, _sz, _p], _int),
     "moegq_switch_glu_mode": ([_i64, _i64, _i64], _int),
+    "moegq_moe_decode": ([_p, _i64, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _int,
+                          _int, _p, _p, _p, _sz, _p], _int),
     "moegq_moe_combine": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _p], _int),
     "moegq_moe_combine_unfused": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _sz, _p], _int),
     "moegq_sort_pairs": ([_p, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _sz, _p], _int),
@@ -121,6 +124,13 @@ def workspace_bytes(op: int, P: int, E: int, N: int, bm: int = 0) -> int:
     return int(lib().moegq_workspace_bytes(op, P, E, N, bm))
 
 
+def _gather_ws(P, E, M, sorted_indices):
+    # only the grouped (sorted, one row per pair) and the many-row routes use a workspace
+    if (M == 1 and not sorted_indices) or 2 <= M <= 16:
+        return 0
+    return workspace_bytes(OP_GATHER_QMM, P, E, M, 0)
+
+
 def _workspace(nbytes: int, device):
     if nbytes == 0:
         return None, 0
@@ -178,7 +188,7 @@ def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, transpo
         raise ValueError("lhs and rhs indices must share a dtype")
     if out is None:
         out = torch.empty(shape + (M, N), dtype=torch.bfloat16, device=x.device)
-    ws, wsb = _workspace(workspace_bytes(OP_GATHER_QMM, P, E, M, 0), x.device)
+    ws, wsb = _workspace(_gather_ws(P, E, M, sorted_indices), x.device)
     st = lib().moegq_gather_qmm(_ptr(x), _dt(x), X, M, K, _ptr(w), _wdt(w), _ptr(scales), _ptr(biases), E, N,
                                 _ptr(li), lhs_div, _ptr(ri), idx_dt, P, int(bool(sorted_indices)),
                                 int(bool(transpose)), group_size, bits, _ptr(out), _ptr(ws), wsb, _stream())
@@ -201,7 +211,7 @@ def gather_qmm_glu(x, gate, up, rhs_indices, lhs_indices=None, lhs_div=1, group_
     P = rhs_indices.numel()
     if out is None:
         out = torch.empty((P, M, N), dtype=torch.bfloat16, device=x.device)
-    ws, wsb = _workspace(workspace_bytes(OP_GATHER_QMM, P, E, M, 0), x.device)
+    ws, wsb = _workspace(_gather_ws(P, E, M, sorted_indices), x.device)
     st = lib().moegq_gather_qmm_glu(_ptr(x), _dt(x), X, M, K, *[_ptr(t) for t in gate], *[_ptr(t) for t in up], E,
                                     N, _ptr(lhs_indices), lhs_div, _ptr(rhs_indices), _dt(rhs_indices), P,
                                     int(bool(sorted_indices)), group_size, bits, _ptr(out), _ptr(ws), wsb,
@@ -262,6 +272,27 @@ def switch_glu(x, idx, gate, up, down, group_size=64, bits=4, mode=MODE_AUTO, ti
                                 tile_mode, bm, _ptr(y), _ptr(inv), _ptr(ws), wsb, _stream())
     _check(st, "switch_glu")
     return y, inv, mode
+
+
+def moe_decode(x, idx, scores, gate, up, down, shared=None, group_size=64, bits=4, out=None, y=None,
+               workspace=None):
+    """Routed MoE decode layer in two kernels: gate/up + SiLU, then down fused
+    with the combine tail.  Returns out [T, H] (y [T*top_k, H] filled if given)."""
+    _dev(x, idx, scores, shared, *gate, *up, *down, y)
+    T, H = x.shape
+    top_k = idx.shape[1]
+    E, I = gate[0].shape[0], gate[0].shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        ws, wsb = _workspace(workspace_bytes(OP_MOE_DECODE, T * top_k, E, I, 0), x.device)
+    else:
+        ws, wsb = workspace, workspace.numel()
+    st = lib().moegq_moe_decode(_ptr(x), T, H, I, E, _ptr(idx), top_k, _ptr(scores), _ptr(shared),
+                                *[_ptr(t) for t in gate], *[_ptr(t) for t in up], *[_ptr(t) for t in down],
+                                group_size, bits, _ptr(out), _ptr(y), _ptr(ws), wsb, _stream())
+    _check(st, "moe_decode")
+    return out
 
 
 def moe_combine(y, inv, scores, shared=None, out=None):

@@ -154,6 +154,11 @@ size_t moegq_workspace_bytes(int op, int64_t P, int64_t E, int64_t N, int bm) {
              align256(2 * 3 * T * K * H) + 256;
     }
     case MOEGQ_OP_SORT_PAIRS: return 0;
+    case MOEGQ_OP_MOE_DECODE: {
+      // N = I; h [P, I], plus y [P, H] for top_k > 8 when the caller passes none (H unknown here:
+      // callers with top_k > 8 pass y or size it with moegq_moe_decode_workspace)
+      return align256(2 * P * N);
+    }
   }
   return 0;
 }
@@ -416,6 +421,49 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
   d.w1 = nullptr; d.s1 = nullptr; d.b1 = nullptr;
   d.N = (int)H; d.K = (int)I; d.out = (uint16_t*)y;
   return status_of(launch_tiles(d, bits, group_size, false, s));
+}
+
+int moegq_moe_decode(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, const int32_t* idx,
+                     int64_t top_k, const void* scores, const void* shared, const void* wg, const void* sg,
+                     const void* bg, const void* wu, const void* su, const void* bu, const void* wd,
+                     const void* sd, const void* bd, int group_size, int bits, void* out, void* y,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int st;
+  if ((st = check_quant(H, group_size, bits))) return st;
+  if ((st = check_quant(I, group_size, bits))) return st;
+  if (T < 0 || top_k <= 0 || E <= 0 || T > kMaxDim || top_k > 64 || H % 8 != 0) return MOEGQ_ERR_SHAPE;
+  if (H > kMaxQmvK || I > kMaxQmvK) return MOEGQ_ERR_UNSUPPORTED;
+  if (T == 0) return MOEGQ_OK;
+  if (!x || !idx || !scores || !wg || !sg || !bg || !wu || !su || !bu || !wd || !sd || !bd || !out)
+    return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(x) || !aligned16(wg) || !aligned16(wu) || !aligned16(wd) || !aligned16(out) ||
+      (y && !aligned16(y)) || (shared && !aligned16(shared)))
+    return MOEGQ_ERR_ALIGN;
+  const int64_t P = T * top_k;
+  const size_t need = moegq_workspace_bytes(MOEGQ_OP_MOE_DECODE, P, E, I, 0) ;
+  if (!workspace || workspace_bytes < need) return MOEGQ_ERR_WORKSPACE;
+  hipStream_t s = S(stream);
+  uint16_t* h = (uint16_t*)workspace;
+  QmvArgs a{};
+  a.x = (const uint16_t*)x; a.lhs = nullptr; a.lhs_div = top_k; a.rhs = idx;
+  a.w0 = (const uint32_t*)wg; a.s0 = (const uint16_t*)sg; a.b0 = (const uint16_t*)bg;
+  a.w1 = (const uint32_t*)wu; a.s1 = (const uint16_t*)su; a.b1 = (const uint16_t*)bu;
+  a.N = (int)I; a.K = (int)H; a.out = h;
+  if (launch_qmv(a, bits, group_size, true, P, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  QmvArgs d{};
+  d.x = h; d.lhs = nullptr; d.lhs_div = 1; d.rhs = idx;
+  d.w0 = (const uint32_t*)wd; d.s0 = (const uint16_t*)sd; d.b0 = (const uint16_t*)bd;
+  d.N = (int)H; d.K = (int)I; d.out = (uint16_t*)y;
+  if (top_k <= 8)
+    return status_of(launch_qmv_combine(d, bits, group_size, (const uint16_t*)scores, (const uint16_t*)shared, T,
+                                        (int)top_k, (uint16_t*)out, s));
+  // wider top_k: separate down projection and combine, through the caller's y
+  if (!y) return MOEGQ_ERR_NULL_ARG;
+  uint16_t* yw = (uint16_t*)y;
+  d.out = yw;
+  if (launch_qmv(d, bits, group_size, false, P, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  return status_of(launch_combine(yw, nullptr, (const uint16_t*)scores, (const uint16_t*)shared, T, (int)top_k, H,
+                                  (uint16_t*)out, s));
 }
 
 int moegq_moe_combine(const void* y, const int32_t* inv, const void* scores, const void* shared, int64_t T,

@@ -74,6 +74,19 @@ template <typename T>
 MOEGQ_DEV T ldg(const T* p) { return *p; }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over `bytes` bytes at `base`: loads outside the range
+// return zero (the hardware bounds check), offsets are 32-bit.
+MOEGQ_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+MOEGQ_DEV uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+MOEGQ_DEV uint16_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
 // 128-bit streaming load (non-temporal hint: weights are read once)
 MOEGQ_DEV uint4 ld_nt(const uint4* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));

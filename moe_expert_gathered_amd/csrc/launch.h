@@ -10,6 +10,7 @@ struct QmvArgs {
   const uint16_t* x;        // activation rows [*, K] bf16
   const int32_t* lhs;       // row of x per pair, or null -> p / lhs_div
   int64_t lhs_div;
+  int lhs_shift;            // log2(lhs_div) when it is a power of two, else -1 (set by launch_qmv)
   const int32_t* rhs;       // expert per pair, or null -> 0
   const uint32_t* w0; const uint16_t* s0; const uint16_t* b0;   // [E, N, Kw], [E, N, G]
   const uint32_t* w1; const uint16_t* s1; const uint16_t* b1;   // GLU: up projection
@@ -18,6 +19,10 @@ struct QmvArgs {
   const uint16_t* residual; // null or [P, N]
 };
 hipError_t launch_qmv(const QmvArgs& a, int bits, int gs, bool glu, int64_t P, hipStream_t st);
+// decode down projection + combine: out[t] from pairs t*top_k .. t*top_k + top_k - 1
+// (a.out, if not null, also receives y [T*top_k, N]); top_k <= 8
+hipError_t launch_qmv_combine(const QmvArgs& a, int bits, int gs, const uint16_t* scores, const uint16_t* shared,
+                              int64_t T, int top_k, uint16_t* out, hipStream_t st);
 
 // few-row MFMA (2..16 rows per pair)
 struct SkinnyArgs {

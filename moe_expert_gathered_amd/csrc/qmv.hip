@@ -6,10 +6,11 @@
 // projections of SwitchGLU (same page, moe(): up, gate, silu(gate)*up).
 //
 // Mapping on gfx950: a workgroup owns one pair and 4 waves x RPW output rows.
-// The pair's activation row is staged once in LDS (already in the lane order
-// the dot products use).  Each wave streams RPW rows (two matrices in the GLU
-// variant) with 128-bit coalesced loads: lane l reads words [4l, 4l+4) of every
-// 256-word slice of a row, so one load instruction covers 1 KiB of one row.
+// Each wave streams RPW rows (two matrices in the GLU variant) with 128-bit
+// coalesced loads: lane l reads words [4l, 4l+4) of every 256-word slice of a
+// row, so one load instruction covers 1 KiB of one row.  The activations are
+// read straight from global memory (L2-resident: every wave of a pair reads
+// the same row) and reordered in registers.
 //
 // Arithmetic (4-bit): per lane and group g the partial sum of x_k (q_k s + b)
 // is s * D + (b - 128 s) * Sx with D = sum x_k (128 + q_k) and Sx = sum x_k,
@@ -24,148 +25,144 @@
 
 namespace moegq {
 
-template <int V>
-MOEGQ_DEV void butterfly(float (&a)[V], int lane) {
-  // After the halving steps lane l holds value v(l) = sum over steps of
-  // (l & (32 >> s)) ? V >> (s+1) : 0, partially reduced; the remaining
-  // offsets finish the sum.  Value v ends in lane v * (64 / V).
-#pragma unroll
-  for (int s = 0; (V >> s) > 1; ++s) {
-    const int half = V >> (s + 1);
-    const int off = 32 >> s;
-    const bool upper = (lane & off) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      float send = upper ? a[i] : a[i + half];
-      float keep = upper ? a[i + half] : a[i];
-      a[i] = keep + shfl_xor(send, off);
-    }
-  }
-  constexpr int lg = (V >= 64) ? 6 : (V >= 32) ? 5 : (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : (V >= 2) ? 1 : 0;
-#pragma unroll
-  for (int off = 32 >> lg; off >= 1; off >>= 1) a[0] += shfl_xor(a[0], off);
+// Sum of one float over the 16 lanes of each row (DPP row rotations).
+MOEGQ_DEV float row_sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));  // row_ror:2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));  // row_ror:1
+  return v;
 }
 
-template <int BITS, int GS, bool GLU, int RPW>
-__global__ __launch_bounds__(256) void qmv_kernel(QmvArgs A) {
-  extern __shared__ uint4 xs[];  // activation row, K bf16 (4-bit: pair-permuted)
-  constexpr int NM = GLU ? 2 : 1;
-  constexpr int V = RPW * NM;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // 1-D grid: consecutive blocks walk the row blocks of one pair, so one
-  // expert matrix is streamed front to back by neighbouring workgroups
-  const int nrb = (A.N + 4 * RPW - 1) / (4 * RPW);
-  const int64_t p = blockIdx.x / nrb;
-  const int rb = blockIdx.x % nrb;
-  const int K = A.K, N = A.N;
-  const int64_t xrow = A.lhs ? (int64_t)A.lhs[p] : p / A.lhs_div;
-  const int64_t e = A.rhs ? (int64_t)A.rhs[p] : 0;
-
-  // stage the activation row
-  const uint4* xg = reinterpret_cast<const uint4*>(A.x + xrow * (int64_t)K);
-  for (int c = tid; c < K / 8; c += 256) {
-    uint4 v = xg[c];
-    if (BITS == 4) {
-      uint32_t d[4] = {v.x, v.y, v.z, v.w}, o[4];
-      perm_pairs(d, o);
-      v = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-    xs[c] = v;
+// Reduce V per-lane partial sums over the wave.  Two swap steps halve the
+// live values without any select: v_permlane32_swap exchanges the upper half
+// of one register with the lower half of another, so X + Y afterwards is the
+// pairwise total of value i in lanes 0-31 and of value i + V/2 in lanes 32-63
+// (v_permlane16_swap does the same between odd and even 16-lane rows).  The
+// V/4 values left are then summed inside each 16-lane row.  On return every
+// lane of row r = 2*bit5 + bit4 holds a[j] = total of value
+// bit5*(V/2) + bit4*(V/4) + j, j < V/4.
+template <int V>
+MOEGQ_DEV void reduce_wave(float (&a)[V]) {
+  static_assert(V >= 4 && (V & (V - 1)) == 0, "V must be a power of two >= 4");
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[i]), __float_as_uint(a[i + V / 2]), false, false);
+    a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < V / 4; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[i + V / 4]), false, false);
+    a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < V / 4; ++i) a[i] = row_sum16(a[i]);
+}
 
+// One workgroup is one wave; it owns RPW output rows (two matrices in the GLU
+// variant) of one pair.  Every operand is read through a raw buffer
+// descriptor (one per matrix of the pair's expert, one for the activation
+// row): a lane's offset inside a 256-word slice is a single 32-bit VGPR shared
+// by all rows, the row offsets are scalars, and reads past the matrix or the
+// row return zero.  K is walked in chunks of NS slices; all loads of a chunk
+// (codes, scales, biases, activations) are issued before any arithmetic.
+template <int BITS, int GS, bool GLU, int RPW, int NS, int V = RPW * (GLU ? 2 : 1)>
+MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, float (&acc)[V]) {
+  constexpr int NM = GLU ? 2 : 1;
+  constexpr int XV = BITS == 4 ? 4 : 2;   // uint4 of activations per lane per slice
+  const int K = A.K, N = A.N;
+  const int64_t xrow = A.lhs ? (int64_t)A.lhs[p] : (A.lhs_shift >= 0 ? p >> A.lhs_shift : p / A.lhs_div);
+  const int64_t e = A.rhs ? (int64_t)A.rhs[p] : 0;
   const int Kw = K * BITS / 32;      // words per row
   const int G = K / GS;              // groups per row
-  const int n0 = rb * (4 * RPW) + wave * RPW;
-  const uint32_t* wm[NM];
-  const uint16_t* sm[NM];
-  const uint16_t* bm[NM];
-  wm[0] = A.w0 + e * (int64_t)N * Kw;
-  sm[0] = A.s0 + e * (int64_t)N * G;
-  bm[0] = A.b0 + e * (int64_t)N * G;
-  if (GLU) {
-    wm[NM - 1] = A.w1 + e * (int64_t)N * Kw;
-    sm[NM - 1] = A.s1 + e * (int64_t)N * G;
-    bm[NM - 1] = A.b1 + e * (int64_t)N * G;
-  }
-  int rown[RPW];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) rown[r] = min(n0 + r, N - 1);  // clamp: rows past N are computed and dropped
 
-  float acc[V];
+  __amdgpu_buffer_rsrc_t rw[NM], rs[NM], rb[NM];
+  rw[0] = make_rsrc(A.w0 + e * N * (int64_t)Kw, (uint32_t)N * Kw * 4);
+  rs[0] = make_rsrc(A.s0 + e * N * (int64_t)G, (uint32_t)N * G * 2);
+  rb[0] = make_rsrc(A.b0 + e * N * (int64_t)G, (uint32_t)N * G * 2);
+  if (GLU) {
+    rw[NM - 1] = make_rsrc(A.w1 + e * N * (int64_t)Kw, (uint32_t)N * Kw * 4);
+    rs[NM - 1] = make_rsrc(A.s1 + e * N * (int64_t)G, (uint32_t)N * G * 2);
+    rb[NM - 1] = make_rsrc(A.b1 + e * N * (int64_t)G, (uint32_t)N * G * 2);
+  }
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(A.x + xrow * (int64_t)K, (uint32_t)K * 2);
+
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  // 4-bit pair building: bytes of (w & 0x0F0F0F0F) are the even codes, of
+  // ((w >> 4) & 0x0F0F0F0F) the odd ones; v_perm places two of them under the
+  // bf16 exponent byte 0x43, giving (128 + q_a, 128 + q_b) per dword.
+  const uint32_t C43 = 0x43434343u;
 
   const int n_it = (Kw + 255) / 256;
-  uint4 cur[V];
-  auto load = [&](int it, uint4 (&dst)[V]) {
-    const int wb = it * 256 + lane * 4;
-    const bool ok = wb < Kw;
+  for (int it0 = 0; it0 < n_it; it0 += NS) {
+    uint4 c[NS][V], xv[NS][XV];
+    uint16_t sv[NS][V], bv[NS][V];
+    bool ok[NS];
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const uint4* src = reinterpret_cast<const uint4*>(wm[m] + (int64_t)rown[r] * Kw + wb);
-        dst[m * RPW + r] = ok ? ld_nt(src) : make_uint4(0, 0, 0, 0);
-      }
-  };
-  load(0, cur);
-  for (int it = 0; it < n_it; ++it) {
-    uint4 nxt[V];
-    if (it + 1 < n_it) load(it + 1, nxt);
-    const int wb = it * 256 + lane * 4;
-    const bool ok = wb < Kw;
-    const int k0 = wb * (32 / BITS);
-    const int g = min(k0 / GS, G - 1);
-    if (BITS == 4) {
-      // 32 codes per lane: x chunks k0/8 .. k0/8+3, each 8 bf16 in pair order
-      uint32_t xp[16];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint4 v = ok ? xs[k0 / 8 + j] : make_uint4(0, 0, 0, 0);
-        xp[4 * j + 0] = v.x; xp[4 * j + 1] = v.y; xp[4 * j + 2] = v.z; xp[4 * j + 3] = v.w;
-      }
-      float sx = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sx = fdot2_bf16(xp[i], 0x3F803F80u, sx);
+    for (int t = 0; t < NS; ++t) {
+      const int wb = (it0 + t) * 256 + lane * 4;     // first word of the lane's 16 bytes
+      ok[t] = wb < Kw;                               // lanes past the row end add nothing
+      const int k0 = wb * (32 / BITS);
+      const uint32_t g2 = (uint32_t)(k0 / GS) * 2;
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-          const uint4 c = cur[m * RPW + r];
-          const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+          const uint32_t row = (uint32_t)(n0 + r);
+          c[t][m * RPW + r] = buf_load16(rw[m], (uint32_t)wb * 4, row * Kw * 4);
+          sv[t][m * RPW + r] = buf_load2(rs[m], g2, row * G * 2);
+          bv[t][m * RPW + r] = buf_load2(rb[m], g2, row * G * 2);
+        }
+#pragma unroll
+      for (int j = 0; j < XV; ++j) xv[t][j] = buf_load16(rx, (uint32_t)(k0 + 8 * j) * 2, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      if (BITS == 4) {
+        // activations in the pair order (x0,x2) (x4,x6) (x1,x3) (x5,x7) per 8
+        uint32_t xp[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 v = xv[t][j];
+          xp[4 * j + 0] = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);
+          xp[4 * j + 1] = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
+          xp[4 * j + 2] = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
+          xp[4 * j + 3] = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
+        }
+        float sx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sx = fdot2_bf16(xp[i], 0x3F803F80u, sx);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const uint32_t cw[4] = {c[t][i].x, c[t][i].y, c[t][i].z, c[t][i].w};
           float d = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            uint32_t pr[4];
-            nib_pairs(cw[j], pr);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) d = fdot2_bf16(pr[q], xp[4 * j + q], d);
+            const uint32_t lo = cw[j] & 0x0F0F0F0Fu, hi = (cw[j] >> 4) & 0x0F0F0F0Fu;
+            d = fdot2_bf16(__builtin_amdgcn_perm(C43, lo, 0x04010400u), xp[4 * j + 0], d);
+            d = fdot2_bf16(__builtin_amdgcn_perm(C43, lo, 0x04030402u), xp[4 * j + 1], d);
+            d = fdot2_bf16(__builtin_amdgcn_perm(C43, hi, 0x04010400u), xp[4 * j + 2], d);
+            d = fdot2_bf16(__builtin_amdgcn_perm(C43, hi, 0x04030402u), xp[4 * j + 3], d);
           }
-          const int64_t gi = (int64_t)rown[r] * G + g;
-          const float s = ok ? bf16_to_f32(sm[m][gi]) : 0.f;
-          const float b = ok ? bf16_to_f32(bm[m][gi]) : 0.f;
-          acc[m * RPW + r] += s * d + (b - 128.f * s) * sx;
+          const float s = ok[t] ? bf16_to_f32(sv[t][i]) : 0.f;
+          const float b = ok[t] ? bf16_to_f32(bv[t][i]) : 0.f;
+          acc[i] = fmaf(s, d, fmaf(fmaf(-128.f, s, b), sx, acc[i]));
         }
-    } else {
-      // 16 codes per lane: x chunks k0/8, k0/8+1 in natural order
-      float xf[16];
+      } else {
+        float xf[16];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint4 v = ok ? xs[k0 / 8 + j] : make_uint4(0, 0, 0, 0);
-        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t d4[4] = {xv[t][j].x, xv[t][j].y, xv[t][j].z, xv[t][j].w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) { xf[8 * j + 2 * q] = bf16_lo(d[q]); xf[8 * j + 2 * q + 1] = bf16_hi(d[q]); }
-      }
-      float sx = 0.f;
+          for (int q = 0; q < 4; ++q) { xf[8 * j + 2 * q] = bf16_lo(d4[q]); xf[8 * j + 2 * q + 1] = bf16_hi(d4[q]); }
+        }
+        float sx = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sx += xf[i];
+        for (int i = 0; i < 16; ++i) sx += xf[i];
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-          const uint4 c = cur[m * RPW + r];
-          const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+        for (int i = 0; i < V; ++i) {
+          const uint32_t cw[4] = {c[t][i].x, c[t][i].y, c[t][i].z, c[t][i].w};
           float d = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -174,52 +171,154 @@ __global__ __launch_bounds__(256) void qmv_kernel(QmvArgs A) {
             d = fmaf((float)((cw[j] >> 16) & 0xFFu), xf[4 * j + 2], d);
             d = fmaf((float)((cw[j] >> 24) & 0xFFu), xf[4 * j + 3], d);
           }
-          const int64_t gi = (int64_t)rown[r] * G + g;
-          const float s = ok ? bf16_to_f32(sm[m][gi]) : 0.f;
-          const float b = ok ? bf16_to_f32(bm[m][gi]) : 0.f;
-          acc[m * RPW + r] += s * d + b * sx;
+          const float s = ok[t] ? bf16_to_f32(sv[t][i]) : 0.f;
+          const float b = ok[t] ? bf16_to_f32(bv[t][i]) : 0.f;
+          acc[i] = fmaf(s, d, fmaf(b, sx, acc[i]));
         }
-    }
-    if (it + 1 < n_it) {
-#pragma unroll
-      for (int i = 0; i < V; ++i) cur[i] = nxt[i];
+      }
     }
   }
 
-  butterfly<V>(acc, lane);
-  constexpr int STRIDE = 64 / V;
+  reduce_wave<V>(acc);
+}
+
+template <int BITS, int GS, bool GLU, int RPW, int NS>
+__global__ __launch_bounds__(64) void qmv_kernel(QmvArgs A, int64_t p_base) {
+  constexpr int V = RPW * (GLU ? 2 : 1);
+  const int lane = threadIdx.x;
+  const int n0 = blockIdx.x * RPW;
+  const int64_t p = p_base + blockIdx.y;
+  const int N = A.N;
+  float acc[V];
+  qmv_rows<BITS, GS, GLU, RPW, NS>(A, p, n0, lane, acc);
+  // lane 16*r (r = 2*bit5 + bit4) holds values r*V/4 .. r*V/4 + V/4 - 1
+  const int rowg = lane >> 4;
   if (GLU) {
-    const float u = __shfl_xor(acc[0], 32, 64);   // up of row r sits 32 lanes above its gate
-    const int r = lane / STRIDE;
-    if ((lane % STRIDE) == 0 && r < RPW) {
-      const int n = n0 + r;
-      if (n < N) {
-        float h = glu(acc[0], u);
-        A.out[p * (int64_t)N + n] = f32_to_bf16(h);
+    // gate values 0..RPW-1 sit in rows 0-1, up values RPW..2*RPW-1 in rows 2-3
+    float u[V / 4];
+#pragma unroll
+    for (int j = 0; j < V / 4; ++j) u[j] = __shfl_xor(acc[j], 32, 64);
+    if ((lane & 15) == 0 && rowg < 2) {
+#pragma unroll
+      for (int j = 0; j < V / 4; ++j) {
+        const int n = n0 + rowg * (V / 4) + j;
+        if (n < N) A.out[p * (int64_t)N + n] = f32_to_bf16(glu(acc[j], u[j]));
       }
     }
   } else {
-    const int r = lane / STRIDE;
-    if ((lane % STRIDE) == 0 && r < RPW) {
-      const int n = n0 + r;
-      if (n < N) {
-        float y = acc[0];
-        if (A.residual) {
-          y = bf16_to_f32(f32_to_bf16(y)) + bf16_to_f32(A.residual[p * (int64_t)N + n]);
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int j = 0; j < V / 4; ++j) {
+        const int n = n0 + rowg * (V / 4) + j;
+        if (n < N) {
+          float y = acc[j];
+          if (A.residual) y = bf16_to_f32(f32_to_bf16(y)) + bf16_to_f32(A.residual[p * (int64_t)N + n]);
+          A.out[p * (int64_t)N + n] = f32_to_bf16(y);
         }
-        A.out[p * (int64_t)N + n] = f32_to_bf16(y);
       }
     }
   }
 }
 
+// Decode down projection fused with the combine tail (MTPLX PR 558: unsort,
+// multiply by the routing scores, sum over top_k and add the shared expert in
+// one pass).  A workgroup is one token: wave k computes y for pair
+// t*top_k + k over RPW output rows (the same rows for every slot), rounds it
+// to bf16 as the materialized tensor would be, and the first RPW threads then
+// run the combine arithmetic of combine_kernel on those values in slot order:
+// out = bf16( bf16( sum_k bf16(y_k * score_k) ) + shared ).
+template <int BITS, int GS, int RPW, int NS>
+__global__ __launch_bounds__(512) void qmv_combine_kernel(QmvArgs A, const uint16_t* __restrict__ scores,
+                                                           const uint16_t* __restrict__ shared, int top_k,
+                                                           uint16_t* __restrict__ out) {
+  __shared__ float ys[8][RPW];
+  const int lane = threadIdx.x & 63;
+  const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t t = blockIdx.y;
+  const int n0 = blockIdx.x * RPW;
+  const int N = A.N;
+  const int64_t p = t * top_k + k;
+  float acc[RPW];
+  qmv_rows<BITS, GS, false, RPW, NS>(A, p, n0, lane, acc);
+  if ((lane & 15) == 0) {
+    const int rowg = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < RPW / 4; ++j) {
+      const int r = rowg * (RPW / 4) + j;
+      const uint16_t yb = f32_to_bf16(acc[j]);
+      ys[k][r] = bf16_to_f32(yb);
+      if (A.out && n0 + r < N) A.out[p * (int64_t)N + n0 + r] = yb;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < RPW && n0 + (int)threadIdx.x < N) {
+    const int r = threadIdx.x;
+    float s = 0.f;
+    for (int kk = 0; kk < top_k; ++kk) {
+      const float pk = bf16_to_f32(f32_to_bf16(ys[kk][r] * bf16_to_f32(scores[t * top_k + kk])));
+      s = (kk == 0) ? pk : s + pk;
+    }
+    float o = s;
+    if (shared) o = bf16_to_f32(f32_to_bf16(s)) + bf16_to_f32(shared[t * (int64_t)N + n0 + r]);
+    out[t * (int64_t)N + n0 + r] = f32_to_bf16(o);
+  }
+}
+
+template <int BITS, int GS>
+static hipError_t launch_qmv_combine_t(const QmvArgs& a, const uint16_t* scores, const uint16_t* shared, int64_t T,
+                                      int top_k, uint16_t* out, hipStream_t st) {
+  constexpr int RPW = 8;
+  const unsigned nrb = (unsigned)((a.N + RPW - 1) / RPW);
+  const int Kw = a.K * BITS / 32;
+  for (int64_t t0 = 0; t0 < T; t0 += 65535) {
+    QmvArgs b = a;
+    const int64_t nt = T - t0 < 65535 ? T - t0 : 65535;
+    // shift the token base into the pointers so blockIdx.y is the local token
+    b.rhs = a.rhs + t0 * top_k;
+    b.lhs = a.lhs ? a.lhs + t0 * top_k : nullptr;
+    b.x = a.lhs ? a.x : a.x + (t0 * top_k / a.lhs_div) * (int64_t)a.K;
+    b.out = a.out ? a.out + t0 * top_k * (int64_t)a.N : nullptr;
+    const uint16_t* sc = scores + t0 * top_k;
+    const uint16_t* sh = shared ? shared + t0 * (int64_t)a.N : nullptr;
+    uint16_t* o = out + t0 * (int64_t)a.N;
+    dim3 grid(nrb, (unsigned)nt);
+    if (Kw > 256 && Kw <= 512 && BITS == 4)
+      hipLaunchKernelGGL((qmv_combine_kernel<BITS, GS, RPW, 2>), grid, dim3(64 * top_k), 0, st, b, sc, sh, top_k, o);
+    else
+      hipLaunchKernelGGL((qmv_combine_kernel<BITS, GS, RPW, 1>), grid, dim3(64 * top_k), 0, st, b, sc, sh, top_k, o);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_qmv_combine(const QmvArgs& a_in, int bits, int gs, const uint16_t* scores, const uint16_t* shared,
+                              int64_t T, int top_k, uint16_t* out, hipStream_t st) {
+  if (T <= 0 || a_in.N <= 0) return hipSuccess;
+  QmvArgs a = a_in;
+  a.lhs_shift = -1;
+  if (a.lhs_div > 0 && (a.lhs_div & (a.lhs_div - 1)) == 0) {
+    a.lhs_shift = 0;
+    while ((int64_t(1) << a.lhs_shift) < a.lhs_div) ++a.lhs_shift;
+  }
+#define MOEGQ_QC(B, G) if (bits == B && gs == G) return launch_qmv_combine_t<B, G>(a, scores, shared, T, top_k, out, st);
+  MOEGQ_QC(4, 32) MOEGQ_QC(4, 64) MOEGQ_QC(4, 128) MOEGQ_QC(8, 32) MOEGQ_QC(8, 64) MOEGQ_QC(8, 128)
+#undef MOEGQ_QC
+  return hipErrorInvalidValue;
+}
+
 template <int BITS, int GS, bool GLU>
 static hipError_t launch_qmv_t(const QmvArgs& a, int64_t P, hipStream_t st) {
-  constexpr int RPW = GLU ? 4 : 8;
-  const int64_t nrb = (a.N + 4 * RPW - 1) / (4 * RPW);
-  dim3 grid((unsigned)(nrb * P));
-  size_t lds = (size_t)a.K * 2;
-  hipLaunchKernelGGL((qmv_kernel<BITS, GS, GLU, RPW>), grid, dim3(256), lds, st, a);
+  // rows per wave: 2 (GLU: 4 row streams) or 8; slices per chunk: the whole
+  // row up to 512 words (the decode gate/up), else 1
+  constexpr int RPW = GLU ? 2 : 8;
+  const int Kw = a.K * BITS / 32;
+  const unsigned nrb = (unsigned)((a.N + RPW - 1) / RPW);
+  for (int64_t p0 = 0; p0 < P; p0 += 65535) {
+    dim3 grid(nrb, (unsigned)(P - p0 < 65535 ? P - p0 : 65535));
+    if (Kw > 256 && Kw <= 512 && (GLU || BITS == 4))
+      hipLaunchKernelGGL((qmv_kernel<BITS, GS, GLU, RPW, 2>), grid, dim3(64), 0, st, a, p0);
+    else
+      hipLaunchKernelGGL((qmv_kernel<BITS, GS, GLU, RPW, 1>), grid, dim3(64), 0, st, a, p0);
+  }
   return hipGetLastError();
 }
 
@@ -233,8 +332,14 @@ static hipError_t launch_qmv_gs(const QmvArgs& a, int gs, int64_t P, hipStream_t
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_qmv(const QmvArgs& a, int bits, int gs, bool glu, int64_t P, hipStream_t st) {
-  if (P <= 0 || a.N <= 0) return hipSuccess;
+hipError_t launch_qmv(const QmvArgs& a_in, int bits, int gs, bool glu, int64_t P, hipStream_t st) {
+  if (P <= 0 || a_in.N <= 0) return hipSuccess;
+  QmvArgs a = a_in;
+  a.lhs_shift = -1;
+  if (a.lhs_div > 0 && (a.lhs_div & (a.lhs_div - 1)) == 0) {
+    a.lhs_shift = 0;
+    while ((int64_t(1) << a.lhs_shift) < a.lhs_div) ++a.lhs_shift;
+  }
   if (bits == 4) return glu ? launch_qmv_gs<4, true>(a, gs, P, st) : launch_qmv_gs<4, false>(a, gs, P, st);
   if (bits == 8) return glu ? launch_qmv_gs<8, true>(a, gs, P, st) : launch_qmv_gs<8, false>(a, gs, P, st);
   return hipErrorInvalidValue;

@@ -242,3 +242,53 @@ def integer_exact(g: np.random.Generator, N: int, K: int, gs: int, bits: int, j:
 
 def integer_x(g: np.random.Generator, M: int, K: int, amp: int = 8) -> np.ndarray:
     return to_bf16(g.integers(-amp, amp + 1, size=(M, K)).astype(np.float32))
+
+
+# ----------------------------------------------------------------------------
+# device-side draws for benchmark-sized weights (GBs); same distributions as
+# drawn_words / dense_sets(mode="words"), drawn with a seeded torch generator
+# ----------------------------------------------------------------------------
+def device_generator(device, *key):
+    import torch
+    seed = int(np.random.SeedSequence(list(key)).generate_state(1, dtype=np.uint64)[0] & 0x7FFFFFFFFFFFFFFF)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def device_drawn_words(device, key, shape_rows, K: int, gs: int, bits: int, scale0=None):
+    """(words int32 [*rows, K*bits/32], scales bf16 [*rows, K/gs], biases bf16)
+    on the device.  scale0 None: scales U(0.005, 0.02) * 16 / 2^bits and biases
+    -2^(bits-1) * s + N(0, 0.001); else scales U(0.5, 1.5) * scale0, biases
+    -2^(bits-1) * s."""
+    import torch
+    g = device_generator(device, *key)
+    levels = 1 << bits
+    rows = tuple(shape_rows)
+    w = torch.randint(-(1 << 31), (1 << 31) - 1, rows + (K * bits // 32,), dtype=torch.int32, device=device,
+                      generator=g)
+    u = torch.rand(rows + (K // gs,), device=device, generator=g, dtype=torch.float32)
+    if scale0 is None:
+        s = ((0.005 + 0.015 * u) * (16.0 / levels)).to(torch.bfloat16)
+        n = torch.randn(rows + (K // gs,), device=device, generator=g, dtype=torch.float32) * 0.001
+        b = (-(levels // 2) * s.float() + n).to(torch.bfloat16)
+    else:
+        s = ((0.5 + u) * scale0).to(torch.bfloat16)
+        b = (-(levels // 2) * s.float()).to(torch.bfloat16)
+    return w, s, b
+
+
+def device_expert_set(device, cfg: int, E: int, H: int, I: int, gs: int, bits: int):
+    return tuple(device_drawn_words(device, (cfg, 0, j), (E, N), K, gs, bits)
+                 for j, (N, K) in ((GATE, (I, H)), (UP, (I, H)), (DOWN, (H, I))))
+
+
+def device_dense_sets(device, cfg: int, gs: int, bits: int, d=DENSE, n_sets=None):
+    out = []
+    for si in range(n_sets or d["sets"]):
+        L = {}
+        for j, (name, (N, K)) in enumerate(dense_dims(d).items()):
+            L[name] = device_drawn_words(device, (cfg, 0, si, j), (N,), K, gs, bits,
+                                         scale0=float(np.sqrt(12.0) / ((1 << bits) * np.sqrt(K))))
+        out.append(L)
+    return out

@@ -42,7 +42,8 @@ def test_tiny_switch_glu_decode_and_sorted(mg):
 
 @pytest.mark.parametrize("E,N,K,bits,gs,P", [
     (8, 64, 512, 4, 64, 6), (8, 36, 192, 4, 32, 5), (8, 13, 96, 8, 32, 3), (4, 40, 128, 8, 128, 4),
-    (3, 300, 4096, 4, 128, 5), (2, 257, 2560, 8, 64, 3), (5, 64, 9728, 4, 64, 2), (1, 8, 32, 4, 32, 1)])
+    (3, 300, 4096, 4, 128, 5), (2, 257, 2560, 8, 64, 3), (5, 64, 9728, 4, 64, 2), (1, 8, 32, 4, 32, 1),
+    (4, 50, 2560, 4, 32, 3), (3, 33, 2048, 8, 128, 4), (2, 24, 6144, 4, 64, 2)])
 def test_gather_qmv_shapes(mg, E, N, K, bits, gs, P):
     """M=1 rows per pair, ragged N, K off the 256-word slice, every group size."""
     g = np.random.default_rng(E * 1000 + N + K + bits)
@@ -117,12 +118,12 @@ def test_empty_inputs(mg):
     assert out.shape == (0, sh.H)
 
 
-@pytest.mark.parametrize("M", [1, 3, 20])
-def test_gather_qmm_glu(mg, M):
+@pytest.mark.parametrize("M,K", [(1, 512), (3, 512), (20, 512), (1, 2560), (1, 4096), (1, 6144)])
+def test_gather_qmm_glu(mg, M, K):
     """SwitchGLU's gate/up half over gathered experts (decode layout x[T, K],
     pair p on token p // top_k) against the oracle's SwitchGLU intermediate."""
     g = np.random.default_rng(90 + M)
-    E, N, K, top_k, T = 6, 96, 512, 2, 5
+    E, N, top_k, T = 6, 96, 2, 5
     gate = [synth.drawn_matrix(g, N, K, 64, 4) for _ in range(E)]
     up = [synth.drawn_matrix(g, N, K, 64, 4) for _ in range(E)]
     G = synth.stack_experts(gate)
@@ -135,3 +136,31 @@ def test_gather_qmm_glu(mg, M):
     xd = bf(x) if M > 1 else bf(x[:, 0, :])
     got = mg.gather_qmm_glu(xd, triple(G), triple(U), i32(rhs), lhs_div=top_k, group_size=64, bits=4)
     assert_parity(host_bf(got), want, name=f"glu M={M}")
+
+
+@pytest.mark.parametrize("M,H,I,E,top_k,bits,gs", [(1, 4096, 2048, 288, 8, 4, 64), (4, 4096, 2048, 288, 8, 4, 64),
+                                                   (3, 256, 128, 8, 2, 4, 64), (2, 512, 384, 16, 4, 8, 128),
+                                                   (5, 1024, 2560, 12, 8, 4, 32), (2, 256, 256, 20, 12, 4, 64)])
+def test_moe_decode_fused_tail(mg, M, H, I, E, top_k, bits, gs):
+    """Two-kernel decode layer (gate/up, then down fused with the combine) equals
+    switch_glu DECODE followed by the separate combine, bit for bit, and the
+    oracle within tolerance."""
+    idx = synth.sorted_topk(11, M, E, top_k, sub=H + I)
+    ex = synth.expert_set(11, E, H, I, gs, bits, mode="drawn", experts=np.unique(idx))
+    x = synth.activations(11, M, H)
+    g = np.random.default_rng(M + H)
+    scores = synth.to_bf16(g.random((M, top_k)).astype(np.float32))
+    shared = synth.to_bf16(g.standard_normal((M, H)).astype(np.float32))
+    dev = [triple(m) for m in ex]
+    xd, idd, scd, shd = bf(x), i32(idx), bf(scores), bf(shared)
+    y = torch.empty((M * top_k, H), dtype=torch.bfloat16, device="cuda")
+    out = mg.moe_decode(xd, idd, scd, *dev, shared=shd, group_size=gs, bits=bits, y=y)
+    y_ref, _, _ = mg.switch_glu(xd, idd, *dev, group_size=gs, bits=bits, mode=mg.MODE_DECODE)
+    out_ref = mg.moe_combine(y_ref, None, scd, shd)
+    assert np.array_equal(host_bf(y), host_bf(y_ref))
+    assert np.array_equal(host_bf(out), host_bf(out_ref))
+    want_y = oracle.switch_glu(x, idx, *ex, gs=gs, bits=bits).reshape(-1, H)
+    want = oracle.combine(want_y, np.arange(M * top_k, dtype=np.int32), scores, shared)
+    assert_parity(host_bf(out), want, name="decode layer")
+    out2 = mg.moe_decode(xd, idd, scd, *dev, shared=None, group_size=gs, bits=bits, y=y)
+    assert np.array_equal(host_bf(out2), host_bf(mg.moe_combine(y_ref, None, scd, None)))

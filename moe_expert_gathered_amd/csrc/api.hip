@@ -57,10 +57,20 @@ int auto_bm(int64_t P, int64_t E) {
 
 int64_t tile_cap(int64_t P, int64_t E, int bm) { return (P + bm - 1) / bm + (P < E ? P : E); }
 
+// hybrid schedule: experts with >= kSmallMax rows get kBigM-row tiles, the
+// others one tile each for the few-row kernel
+constexpr int kBigM = 128;
+constexpr int kSmallMax = 32;
+int64_t big_cap(int64_t P, int64_t E) {
+  const int64_t nbig = P / kSmallMax < E ? P / kSmallMax : E;    // experts that can reach kSmallMax rows
+  return (P + kBigM - 1) / kBigM + nbig;
+}
+int64_t small_cap(int64_t P, int64_t E) { return P < E ? P : E; }
+
 // sorted-route workspace layout
 struct SortedWs {
   int32_t* order; int32_t* lhs; int32_t* srhs; int32_t* counts; int32_t* offsets;
-  int32_t* tiles; int32_t* n_tiles; uint16_t* h;
+  int32_t* tiles; int32_t* small_tiles; int32_t* n_tiles; uint16_t* h;
   size_t bytes;
 };
 SortedWs sorted_layout(char* base, int64_t P, int64_t E, int64_t I, int bm) {
@@ -72,8 +82,10 @@ SortedWs sorted_layout(char* base, int64_t P, int64_t E, int64_t I, int bm) {
   w.srhs = (int32_t*)take(4 * P);
   w.counts = (int32_t*)take(4 * E);
   w.offsets = (int32_t*)take(4 * (E + 1));
-  w.tiles = (int32_t*)take(12 * tile_cap(P, E, bm));
-  w.n_tiles = (int32_t*)take(4);
+  const int64_t cap = bm > 0 ? tile_cap(P, E, bm) : big_cap(P, E);
+  w.tiles = (int32_t*)take(12 * cap);
+  w.small_tiles = (int32_t*)take(12 * small_cap(P, E));
+  w.n_tiles = (int32_t*)take(8);
   w.h = (uint16_t*)take(2 * P * I);
   w.bytes = off;
   return w;
@@ -141,8 +153,9 @@ size_t moegq_workspace_bytes(int op, int64_t P, int64_t E, int64_t N, int bm) {
     }
     case MOEGQ_OP_SWITCH_GLU_DECODE: return align256(2 * P * N);
     case MOEGQ_OP_SWITCH_GLU_SORTED: {
-      const int b = bm > 0 ? bm : 16;   // the smallest tile has the largest table
-      return sorted_layout(nullptr, P, E, N, b).bytes;
+      const size_t a = sorted_layout(nullptr, P, E, N, bm).bytes;
+      const size_t b = sorted_layout(nullptr, P, E, N, 16).bytes;   // covers every explicit bm
+      return bm > 0 ? a : (a > b ? a : b);
     }
     case MOEGQ_OP_COMBINE_UNFUSED: {
       // N = H, P = T*top_k; T*H <= P*H
@@ -289,8 +302,17 @@ int moegq_affine_qmm(const void* x, int x_dtype, int64_t M, int64_t K, const voi
     return status_of(launch_skinny(a, bits, group_size, false, 1, s));
   }
   if (residual) return MOEGQ_ERR_UNSUPPORTED;
+  if (M >= kBigM) {
+    TileArgs a{};
+    a.x = (const uint16_t*)x; a.lhs = nullptr; a.lhs_div = 1; a.rows_per_batch = 1;
+    a.P = M; a.E = 1; a.tile_mode = 2;
+    a.w0 = (const uint32_t*)w; a.s0 = (const uint16_t*)scales; a.b0 = (const uint16_t*)biases;
+    a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out; a.bm = kBigM;
+    a.grid_tiles = (M + kBigM - 1) / kBigM;
+    return status_of(launch_tiles_big(a, bits, group_size, false, s));
+  }
   // many rows: one "expert", tiles over M on the device-free path
-  const int bm = M >= 1024 ? 64 : 32;
+  const int bm = 32;
   static_assert(sizeof(int32_t) == 4, "");
   TileArgs a{};
   a.x = (const uint16_t*)x; a.lhs = nullptr; a.lhs_div = 1; a.rows_per_batch = 1;
@@ -328,7 +350,17 @@ int moegq_affine_qmm_glu(const void* x, int64_t M, int64_t K, const void* wg, co
     a.M = (int)M; a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out;
     return status_of(launch_skinny(a, bits, group_size, true, 1, s));
   }
-  const int bm = M >= 1024 ? 64 : 32;
+  if (M >= kBigM) {
+    TileArgs a{};
+    a.x = (const uint16_t*)x; a.lhs_div = 1; a.rows_per_batch = 1;
+    a.P = M; a.E = 1; a.tile_mode = 2;
+    a.w0 = (const uint32_t*)wg; a.s0 = (const uint16_t*)sg; a.b0 = (const uint16_t*)bg;
+    a.w1 = (const uint32_t*)wu; a.s1 = (const uint16_t*)su; a.b1 = (const uint16_t*)bu;
+    a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out; a.bm = kBigM;
+    a.grid_tiles = (M + kBigM - 1) / kBigM;
+    return status_of(launch_tiles_big(a, bits, group_size, true, s));
+  }
+  const int bm = 32;
   TileArgs a{};
   a.x = (const uint16_t*)x; a.lhs_div = 1; a.rows_per_batch = 1;
   a.P = M; a.E = 1; a.tile_mode = 2;
@@ -395,14 +427,18 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
     return status_of(e);
   }
   // sorted route
-  if (bm == 0) bm = auto_bm(P, E);
+  const bool hybrid = (bm == 0 && tile_mode == MOEGQ_TILES_SCHEDULED);
+  const bool big = hybrid || (bm == kBigM && tile_mode == MOEGQ_TILES_SCHEDULED);
+  if (bm == 0) bm = tile_mode == MOEGQ_TILES_NAIVE ? auto_bm(P, E) : 0;
   const SortedWs ws = sorted_layout((char*)workspace, P, E, I, bm);
   if (!workspace || workspace_bytes < ws.bytes) return MOEGQ_ERR_WORKSPACE;
   SortArgs sa{};
   sa.idx = idx; sa.P = P; sa.top_k = (int)top_k; sa.E = (int)E;
   sa.order = ws.order; sa.lhs = ws.lhs; sa.sorted_rhs = ws.srhs; sa.inv = inv;
   sa.counts = ws.counts; sa.offsets = ws.offsets;
-  sa.tiles = ws.tiles; sa.n_tiles = ws.n_tiles; sa.bm = bm; sa.tile_mode = tile_mode;
+  sa.tiles = ws.tiles; sa.n_tiles = ws.n_tiles;
+  sa.bm = hybrid ? kBigM : bm; sa.tile_mode = hybrid ? 3 : tile_mode;
+  sa.small_tiles = ws.small_tiles; sa.small_max = kSmallMax;
   hipError_t e = launch_sort(sa, s);
   if (e != hipSuccess) return MOEGQ_ERR_LAUNCH;
   TileArgs g{};
@@ -411,16 +447,30 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
   g.P = P; g.E = (int)E;
   g.w0 = (const uint32_t*)wg; g.s0 = (const uint16_t*)sg; g.b0 = (const uint16_t*)bg;
   g.w1 = (const uint32_t*)wu; g.s1 = (const uint16_t*)su; g.b1 = (const uint16_t*)bu;
-  g.N = (int)I; g.K = (int)H; g.out = ws.h; g.bm = bm; g.tile_mode = tile_mode;
-  g.grid_tiles = tile_mode == MOEGQ_TILES_SCHEDULED ? tile_cap(P, E, bm) : (P + bm - 1) / bm;
-  e = launch_tiles(g, bits, group_size, true, s);
-  if (e != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  g.N = (int)I; g.K = (int)H; g.out = ws.h; g.bm = big ? kBigM : bm; g.tile_mode = tile_mode;
+  g.grid_tiles = hybrid ? big_cap(P, E) : (tile_mode == MOEGQ_TILES_SCHEDULED ? tile_cap(P, E, bm) : (P + bm - 1) / bm);
   TileArgs d = g;
   d.x = ws.h; d.lhs = nullptr; d.lhs_div = 1;
   d.w0 = (const uint32_t*)wd; d.s0 = (const uint16_t*)sd; d.b0 = (const uint16_t*)bd;
   d.w1 = nullptr; d.s1 = nullptr; d.b1 = nullptr;
   d.N = (int)H; d.K = (int)I; d.out = (uint16_t*)y;
-  return status_of(launch_tiles(d, bits, group_size, false, s));
+  if (!big) {
+    if (launch_tiles(g, bits, group_size, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    return status_of(launch_tiles(d, bits, group_size, false, s));
+  }
+  // 128-row tiles (all experts, or the experts with >= kSmallMax rows), then
+  // the few-row tiles of the remaining experts
+  TileArgs gs_ = g, ds_ = d;
+  gs_.tiles = ws.small_tiles; gs_.n_tiles = ws.n_tiles + 1; gs_.bm = kSmallMax; gs_.tile_mode = 0;
+  gs_.grid_tiles = small_cap(P, E);
+  ds_.tiles = ws.small_tiles; ds_.n_tiles = ws.n_tiles + 1; ds_.bm = kSmallMax; ds_.tile_mode = 0;
+  ds_.grid_tiles = small_cap(P, E);
+  g.tile_mode = 0; d.tile_mode = 0;
+  if (launch_tiles_big(g, bits, group_size, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (hybrid && launch_tiles_small(gs_, bits, group_size, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (launch_tiles_big(d, bits, group_size, false, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (hybrid && launch_tiles_small(ds_, bits, group_size, false, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  return MOEGQ_OK;
 }
 
 int moegq_moe_decode(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, const int32_t* idx,

@@ -9,6 +9,8 @@
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 namespace moegq {
@@ -55,6 +57,52 @@ MOEGQ_DEV void perm_pairs(const uint32_t d[4], uint32_t o[4]) {
   o[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);  // (hi of d0, hi of d2)
   o[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
   o[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
+}
+
+// ---- fp16 operands for the matrix cores ------------------------------------
+// The MFMA paths dequantize to fp16 (11-bit significand): w = q * s + b is
+// formed with one fused multiply-add and one rounding, and bf16 activations
+// convert to fp16 exactly inside fp16's normal range.
+//
+// Codes enter fp16 through the exponent trick: 0x64XX is fp16 1024 + XX for
+// XX < 1024, so v_perm placing a code byte under the byte 0x64 gives 1024 + q;
+// subtracting 1024 is exact, then fma(q, s, b) rounds once.
+
+MOEGQ_DEV f16x2_t f16_splat(float v) {
+  const _Float16 h = (_Float16)v;
+  return f16x2_t{h, h};
+}
+MOEGQ_DEV uint32_t deq_pair(uint32_t codes, uint32_t sel, f16x2_t s2, f16x2_t b2) {
+  const f16x2_t q = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, codes, sel)) -
+                    f16x2_t{(_Float16)1024.0f, (_Float16)1024.0f};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
+}
+// eight 4-bit codes of one word -> four fp16 pairs in the order
+// (q0,q2) (q4,q6) (q1,q3) (q5,q7)
+MOEGQ_DEV void deq4_f16(uint32_t w, f16x2_t s2, f16x2_t b2, uint32_t o[4]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  o[0] = deq_pair(lo, 0x04010400u, s2, b2);
+  o[1] = deq_pair(lo, 0x04030402u, s2, b2);
+  o[2] = deq_pair(hi, 0x04010400u, s2, b2);
+  o[3] = deq_pair(hi, 0x04030402u, s2, b2);
+}
+// four 8-bit codes of one word -> two fp16 pairs in natural order (q0,q1) (q2,q3)
+MOEGQ_DEV void deq8_f16(uint32_t w, f16x2_t s2, f16x2_t b2, uint32_t o[2]) {
+  o[0] = deq_pair(w, 0x04010400u, s2, b2);
+  o[1] = deq_pair(w, 0x04030402u, s2, b2);
+}
+MOEGQ_DEV uint32_t cvt_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+// eight consecutive bf16 activations (four dwords) -> four fp16 pairs in the
+// 4-bit code order (x0,x2) (x4,x6) (x1,x3) (x5,x7), or in natural order
+template <int BITS>
+MOEGQ_DEV uint4 act_f16(uint4 v) {
+  if (BITS == 4)
+    return make_uint4(cvt_f16x2(bf16_lo(v.x), bf16_lo(v.y)), cvt_f16x2(bf16_lo(v.z), bf16_lo(v.w)),
+                      cvt_f16x2(bf16_hi(v.x), bf16_hi(v.y)), cvt_f16x2(bf16_hi(v.z), bf16_hi(v.w)));
+  return make_uint4(cvt_f16x2(bf16_lo(v.x), bf16_hi(v.x)), cvt_f16x2(bf16_lo(v.y), bf16_hi(v.y)),
+                    cvt_f16x2(bf16_lo(v.z), bf16_hi(v.z)), cvt_f16x2(bf16_lo(v.w), bf16_hi(v.w)));
 }
 
 MOEGQ_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }

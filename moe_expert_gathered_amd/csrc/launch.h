@@ -43,6 +43,9 @@ struct SortArgs {
   int32_t* order; int32_t* lhs; int32_t* sorted_rhs; int32_t* inv;
   int32_t* counts; int32_t* offsets;
   int32_t* tiles; int32_t* n_tiles; int bm; int tile_mode;   // tiles may be null
+  // hybrid schedule (tile_mode 3): experts with >= small_max rows get bm-row
+  // tiles in `tiles`, the others one tile each in `small_tiles`; n_tiles[0..1]
+  int32_t* small_tiles; int small_max;
 };
 hipError_t launch_sort(const SortArgs& a, hipStream_t st);
 hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int tile_mode, int32_t* tiles,
@@ -68,6 +71,10 @@ struct TileArgs {
   int64_t grid_tiles;       // upper bound of the tile count (grid size)
 };
 hipError_t launch_tiles(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st);
+// 128-row tiles (tile_mode 0: table, 2: dense rows); grid_tiles = table capacity or row tiles
+hipError_t launch_tiles_big(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st);
+// tiles of at most 16 (bm <= 16) or 32 rows from a table (tile_mode 0); rows gathered through lhs
+hipError_t launch_tiles_small(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st);
 
 // combine tail
 hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const uint16_t* scores,

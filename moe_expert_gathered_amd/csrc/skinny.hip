@@ -2,14 +2,15 @@
 //
 // MLX PR 4787: at 3-16 rows the weights should feed the matrix units rather
 // than a per-row vector loop (the pages' qmv_mma).  On gfx950 a wave computes
-// a 16 (rows, zero-padded) x 16 (outputs) block with v_mfma_f32_16x16x32_bf16.
+// a 16 (rows, zero-padded) x 16 (outputs) block with v_mfma_f32_16x16x32_f16.
 //
 // The contraction order over K inside an MFMA is free as long as both
 // operands use the same order, so each lane loads 128-bit runs of its output
 // row (lane (n, j) takes words [4j, 4j+4) of every 16-word chunk) and the
 // activation operand is read at the matching K offsets.  Codes are
-// dequantized exactly in fp32 (q * s + b; nuvec "composed") and rounded to
-// bf16 for the MFMA; all 32 codes of a lane share one group.
+// dequantized to fp16 (q * s + b with one rounding; nuvec "composed") and the
+// activations converted to fp16 for v_mfma_f32_16x16x32_f16; all 32 codes of
+// a lane share one group.
 // The four waves of a workgroup take interleaved 128-code chunks of K for the
 // same 16 outputs and are summed through LDS at the end.
 #include "common.h"
@@ -67,40 +68,26 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs A) {
     }
     // activation operand for the four MFMA steps: step st covers codes
     // [kl + 8 st, kl + 8 st + 8) of lane group lj
-    bf16x8_t xa[4];
+    f16x8_t xa[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       uint4 v = (ok && m_ok) ? *reinterpret_cast<const uint4*>(xrow + kl + 8 * st) : make_uint4(0, 0, 0, 0);
-      xa[st] = __builtin_bit_cast(bf16x8_t, v);
+      xa[st] = __builtin_bit_cast(f16x8_t, act_f16<BITS>(v));
     }
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         uint32_t o[4];
+        const f16x2_t s2 = f16_splat(s[m]), b2 = f16_splat(b[m]);
         if (BITS == 4) {
-          const uint32_t w = (&cw[m][0].x)[st];
-          const uint32_t t0 = w & 0x0F0F0F0Fu, t1 = (w >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            bf16x2_t pr = {(__bf16)fmaf((float)((t0 >> (8 * j)) & 0xFFu), s[m], b[m]),
-                           (__bf16)fmaf((float)((t1 >> (8 * j)) & 0xFFu), s[m], b[m])};
-            o[j] = __builtin_bit_cast(uint32_t, pr);
-          }
+          deq4_f16((&cw[m][0].x)[st], s2, b2, o);
         } else {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint32_t w = (&cw[m][0].x)[2 * st + h];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              bf16x2_t pr = {(__bf16)fmaf((float)((w >> (16 * j)) & 0xFFu), s[m], b[m]),
-                             (__bf16)fmaf((float)((w >> (16 * j + 8)) & 0xFFu), s[m], b[m])};
-              o[2 * h + j] = __builtin_bit_cast(uint32_t, pr);
-            }
-          }
+          deq8_f16((&cw[m][0].x)[2 * st], s2, b2, &o[0]);
+          deq8_f16((&cw[m][0].x)[2 * st + 1], s2, b2, &o[2]);
         }
-        const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[st], bw, acc[m], 0, 0, 0);
+        const f16x8_t bw = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[st], bw, acc[m], 0, 0, 0);
       }
     }
   }
@@ -128,6 +115,146 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs A) {
       A.out[o] = f32_to_bf16(v);
     }
   }
+}
+
+// Expert tiles with few rows (the long tail of a skewed routing): tile t of
+// the small-tile list is (row_start, expert, valid <= 16 * MB); the rows are
+// sorted rows whose activations are gathered through lhs.  Each workgroup
+// streams 16 features of the expert once for all of the tile's rows (MB
+// 16-row MFMA blocks share every dequantized weight operand).
+template <int BITS, int GS, bool GLU, int MB>
+__global__ __launch_bounds__(256) void skinny_tiles_kernel(TileArgs A) {
+  constexpr int NM = GLU ? 2 : 1;
+  constexpr int BV = BITS / 4;
+  __shared__ f32x4_t red[3][NM][MB][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nrb = (A.N + 15) / 16;
+  const int64_t tile = blockIdx.x / nrb;
+  if (tile >= *A.n_tiles) return;
+  const int n0 = (blockIdx.x % nrb) * 16;
+  const int K = A.K, N = A.N;
+  const int Kw = K * BITS / 32, G = K / GS;
+  const int32_t* tl = A.tiles + 3 * tile;
+  const int64_t r0 = tl[0];
+  const int e = tl[1];
+  const int valid = tl[2];
+  const int li = lane % 16, lj = lane / 16;
+  const int n = min(n0 + li, N - 1);
+  const uint16_t* xrow[MB];
+  bool m_ok[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = mb * 16 + li;
+    m_ok[mb] = m < valid;
+    const int64_t r = r0 + (m_ok[mb] ? m : 0);
+    const int64_t xr = A.lhs ? (int64_t)A.lhs[r] : r;
+    xrow[mb] = A.x + xr * (int64_t)K;
+  }
+  const uint32_t* wr[NM];
+  const uint16_t* sr[NM];
+  const uint16_t* br[NM];
+  wr[0] = A.w0 + ((int64_t)e * N + n) * Kw;
+  sr[0] = A.s0 + ((int64_t)e * N + n) * G;
+  br[0] = A.b0 + ((int64_t)e * N + n) * G;
+  if (GLU) {
+    wr[NM - 1] = A.w1 + ((int64_t)e * N + n) * Kw;
+    sr[NM - 1] = A.s1 + ((int64_t)e * N + n) * G;
+    br[NM - 1] = A.b1 + ((int64_t)e * N + n) * G;
+  }
+  f32x4_t acc[NM][MB];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[m][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nchunk = (K + 127) / 128;
+  for (int c = wave; c < nchunk; c += 4) {
+    const int kl = c * 128 + 32 * lj;
+    const bool ok = kl < K;
+    uint4 cw[NM][BV];
+    float s[NM], b[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+#pragma unroll
+      for (int v = 0; v < BV; ++v)
+        cw[m][v] = ok ? ld_nt(reinterpret_cast<const uint4*>(wr[m] + kl * BITS / 32 + 4 * v)) : make_uint4(0, 0, 0, 0);
+      s[m] = ok ? bf16_to_f32(sr[m][kl / GS]) : 0.f;
+      b[m] = ok ? bf16_to_f32(br[m][kl / GS]) : 0.f;
+    }
+    f16x8_t xa[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        uint4 v = (ok && m_ok[mb]) ? *reinterpret_cast<const uint4*>(xrow[mb] + kl + 8 * st) : make_uint4(0, 0, 0, 0);
+        xa[mb][st] = __builtin_bit_cast(f16x8_t, act_f16<BITS>(v));
+      }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        uint32_t o[4];
+        const f16x2_t s2 = f16_splat(s[m]), b2 = f16_splat(b[m]);
+        if (BITS == 4) {
+          deq4_f16((&cw[m][0].x)[st], s2, b2, o);
+        } else {
+          deq8_f16((&cw[m][0].x)[2 * st], s2, b2, &o[0]);
+          deq8_f16((&cw[m][0].x)[2 * st + 1], s2, b2, &o[2]);
+        }
+        const f16x8_t bw = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[m][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[mb][st], bw, acc[m][mb], 0, 0, 0);
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) red[wave - 1][m][mb][lane] = acc[m][mb];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int w = 0; w < 3; ++w) acc[m][mb] += red[w][m][mb][lane];
+  const int col = n0 + li;
+  if (col >= N) return;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = mb * 16 + 4 * lj + q;
+      if (row < valid) {
+        const float v = GLU ? glu(acc[0][mb][q], acc[NM - 1][mb][q]) : acc[0][mb][q];
+        A.out[(r0 + row) * (int64_t)N + col] = f32_to_bf16(v);
+      }
+    }
+}
+
+template <int BITS, int GS, bool GLU>
+static hipError_t launch_skt(const TileArgs& a, hipStream_t st) {
+  const int64_t nrb = (a.N + 15) / 16;
+  const int64_t nblk = a.grid_tiles * nrb;
+  if (nblk <= 0) return hipSuccess;
+  if (a.bm <= 16)
+    hipLaunchKernelGGL((skinny_tiles_kernel<BITS, GS, GLU, 1>), dim3((unsigned)nblk), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((skinny_tiles_kernel<BITS, GS, GLU, 2>), dim3((unsigned)nblk), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tiles_small(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st) {
+#define MOEGQ_SKT(B, G)                                                                   \
+  if (bits == B && gs == G) return glu ? launch_skt<B, G, true>(a, st) : launch_skt<B, G, false>(a, st);
+  MOEGQ_SKT(4, 32) MOEGQ_SKT(4, 64) MOEGQ_SKT(4, 128) MOEGQ_SKT(8, 32) MOEGQ_SKT(8, 64) MOEGQ_SKT(8, 128)
+#undef MOEGQ_SKT
+  return hipErrorInvalidValue;
 }
 
 template <int BITS, int GS, bool GLU>

@@ -67,29 +67,53 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_kernel(SortArgs A) {
     for (int w = 0; w < SORT_WAVES; ++w) tab[w][e] = 0;
   }
   __syncthreads();
-  // 1. histogram (ids outside [0, E) break the precondition; clamp to stay in bounds)
-  for (int64_t p = tid; p < P; p += SORT_THREADS) {
-    const int e = min(max(A.idx[p], 0), E - 1);
-    atomicAdd(&cnt[e], 1);
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // 1. histogram (ids outside [0, E) break the precondition; clamp to stay in
+  //    bounds).  Lanes with equal ids are matched with one ballot per id bit and
+  //    only the first of them adds the group's count: no atomic contention on
+  //    popular experts.
+  for (int64_t base = 0; base < P; base += SORT_THREADS) {
+    const int64_t p = base + tid;
+    const bool valid = p < P;
+    const int e = valid ? min(max(A.idx[p], 0), E - 1) : 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      match &= bit ? bb : ~bb;
+    }
+    if (valid && __popcll(match & lt_mask) == 0) atomicAdd(&cnt[e], (int)__popcll(match));
   }
   __syncthreads();
   // 2. scans (E <= SORT_MAXE == SORT_THREADS: one expert per thread)
   const int c = tid < E ? cnt[tid] : 0;
   int off;
   block_excl_scan(c, wtot, off);
-  const int ntile = (A.bm > 0) ? (c + A.bm - 1) / A.bm : 0;
+  const bool hybrid = A.tile_mode == 3;
+  const bool is_big = !hybrid || c >= A.small_max;
+  const int ntile = (A.bm > 0 && is_big) ? (c + A.bm - 1) / A.bm : 0;
   int toff;
   const int total_tiles = block_excl_scan(ntile, wtot, toff);
+  const int nsmall = (hybrid && c > 0 && !is_big) ? 1 : 0;
+  int soff;
+  const int total_small = block_excl_scan(nsmall, wtot, soff);
   if (tid < E) {
     A.counts[tid] = c;
     A.offsets[tid] = off;
     cursor[tid] = off;
-    if (A.tiles && A.tile_mode == 0) write_tiles(tid, c, off, toff, A.bm, A.tiles);
+    if (A.tiles && (A.tile_mode == 0 || (hybrid && is_big))) write_tiles(tid, c, off, toff, A.bm, A.tiles);
+    if (A.small_tiles && nsmall) {
+      int32_t* t = A.small_tiles + 3 * soff;
+      t[0] = off; t[1] = tid; t[2] = c;
+    }
   }
   if (tid == 0) {
     A.offsets[E] = (int32_t)P;
     if (A.n_tiles) {
-      *A.n_tiles = (A.tile_mode == 0) ? total_tiles : (int32_t)((P + A.bm - 1) / A.bm);
+      A.n_tiles[0] = (A.tile_mode == 0 || hybrid) ? total_tiles : (int32_t)((P + A.bm - 1) / A.bm);
+      if (hybrid) A.n_tiles[1] = total_small;
     }
   }
   if (A.tiles && A.tile_mode == 1) {
@@ -102,9 +126,6 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_kernel(SortArgs A) {
   }
   __syncthreads();
   // 3. stable scatter
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t base = 0; base < P; base += SORT_THREADS) {
     const int64_t p = base + tid;
     const bool valid = p < P;

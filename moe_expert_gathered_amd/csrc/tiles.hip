@@ -12,10 +12,11 @@
 //
 // Per K step (BK = 128) a 256-thread workgroup
 //   * gathers BM activation rows (bf16) into LDS,
-//   * loads BN x BK packed codes per matrix, dequantizes them exactly in fp32
-//     (q * s + b, nuvec "composed") and stores them as bf16 into LDS,
-//   * runs v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the 4 waves split
-//     the BM x BN tile 2 x 2.
+//   * loads BN x BK packed codes per matrix, dequantizes them to fp16
+//     (q * s + b with one rounding, nuvec "composed") into LDS next to the
+//     activations converted to fp16,
+//   * runs v_mfma_f32_16x16x32_f16 with fp32 accumulation; the 4 waves split
+//     the BM x BN tile.
 // The next step's global loads are issued before the current step's MFMAs.
 // GLU: gate and up share the activation tile; the epilogue writes
 // bf16(silu(g) * u) (MLX issue 4509, moe()).
@@ -148,36 +149,18 @@ __global__ __launch_bounds__(256) void tile_kernel(TileArgs A) {
       __syncthreads();   // previous step's MFMAs are done with the LDS tiles
 #pragma unroll
       for (int i = 0; i < AV; ++i)
-        if (a_row0 + 16 * i < BM) *reinterpret_cast<uint4*>(As + (a_row0 + 16 * i) * TLD + a_chunk * 8) = ra[i];
+        if (a_row0 + 16 * i < BM)
+          *reinterpret_cast<uint4*>(As + (a_row0 + 16 * i) * TLD + a_chunk * 8) = act_f16<BITS>(ra[i]);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         uint32_t o[16];
-        const float s = rs[m], b = rbias[m];
+        const f16x2_t s2 = f16_splat(rs[m]), b2 = f16_splat(rbias[m]);
         if (BITS == 4) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const uint32_t w = (&rb[m][0].x)[v];
-            const uint32_t t0 = w & 0x0F0F0F0Fu, t1 = (w >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float lo = fmaf((float)((t0 >> (8 * j)) & 0xFFu), s, b);
-              const float hi = fmaf((float)((t1 >> (8 * j)) & 0xFFu), s, b);
-              bf16x2_t pr = {(__bf16)lo, (__bf16)hi};
-              o[4 * v + j] = __builtin_bit_cast(uint32_t, pr);
-            }
-          }
+          for (int v = 0; v < 4; ++v) deq4_f16((&rb[m][0].x)[v], s2, b2, &o[4 * v]);
         } else {
 #pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            const uint32_t w = (&rb[m][0].x)[v];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const float lo = fmaf((float)((w >> (16 * j)) & 0xFFu), s, b);
-              const float hi = fmaf((float)((w >> (16 * j + 8)) & 0xFFu), s, b);
-              bf16x2_t pr = {(__bf16)lo, (__bf16)hi};
-              o[2 * v + j] = __builtin_bit_cast(uint32_t, pr);
-            }
-          }
+          for (int v = 0; v < 8; ++v) deq8_f16((&rb[m][0].x)[v], s2, b2, &o[2 * v]);
         }
         uint4* dst = reinterpret_cast<uint4*>(Bs + (m * TBN + b_n) * TLD + 32 * b_q);
 #pragma unroll
@@ -188,19 +171,19 @@ __global__ __launch_bounds__(256) void tile_kernel(TileArgs A) {
 #pragma unroll
       for (int k32 = 0; k32 < TBK / 32; ++k32) {
         const int kof = k32 * 32 + 8 * (lane / 16);
-        bf16x8_t af[MI];
+        f16x8_t af[MI];
 #pragma unroll
         for (int i = 0; i < MI; ++i)
-          af[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * WM + i * 16 + (lane % 16)) * TLD + kof);
+          af[i] = *reinterpret_cast<const f16x8_t*>(As + (wm * WM + i * 16 + (lane % 16)) * TLD + kof);
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
           for (int j = 0; j < NI; ++j) {
-            const bf16x8_t bfr =
-                *reinterpret_cast<const bf16x8_t*>(Bs + (m * TBN + wn * WN + j * 16 + (lane % 16)) * TLD + kof);
+            const f16x8_t bfr =
+                *reinterpret_cast<const f16x8_t*>(Bs + (m * TBN + wn * WN + j * 16 + (lane % 16)) * TLD + kof);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-              acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr, acc[m][i][j], 0, 0, 0);
+              acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bfr, acc[m][i][j], 0, 0, 0);
           }
       }
     }

@@ -55,7 +55,7 @@ def test_validate_indices(mg):
     assert mg.validate_indices(i32(np.array([0, 8])), 8) == -10
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 6, 8, 12, 16, 33])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 6, 8, 12, 16, 33, 200])
 @pytest.mark.parametrize("bits,gs", [(4, 32), (4, 64), (4, 128), (8, 32), (8, 64), (8, 128)])
 def test_affine_qmm_rows(mg, M, bits, gs):
     g = np.random.default_rng(M * 7 + bits * 3 + gs)
@@ -86,7 +86,7 @@ def test_affine_qmm_full_shape_sampled(mg, M):
         assert_parity(got[:, cols], want, name=f"sampled {N}x{K} M={M}")
 
 
-@pytest.mark.parametrize("M", [1, 5, 16, 40])
+@pytest.mark.parametrize("M", [1, 5, 16, 40, 300])
 def test_affine_qmm_glu(mg, M):
     g = np.random.default_rng(50 + M)
     N, K = 96, 512

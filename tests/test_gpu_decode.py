@@ -61,7 +61,7 @@ def test_gather_qmv_shapes(mg, E, N, K, bits, gs, P):
 
 
 @pytest.mark.parametrize("bits,gs", [(4, 64), (4, 32), (8, 128), (8, 32)])
-@pytest.mark.parametrize("M", [1, 3, 16, 40])
+@pytest.mark.parametrize("M", [1, 3, 16, 40, 160])
 def test_integer_exact_bitwise(mg, bits, gs, M):
     """Exact scales/biases and small-integer activations: every product and
     partial sum is exact, so GPU and oracle agree bit for bit on every route

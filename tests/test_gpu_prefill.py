@@ -79,7 +79,7 @@ def _prefill_case(T, cfg=3, shape=synth.PREFILL, mode="drawn", sub=0):
 
 
 @pytest.mark.parametrize("T", [128, 331])
-@pytest.mark.parametrize("tile_mode,bm", [(0, 16), (0, 32), (0, 64), (0, 128), (1, 16), (1, 64)])
+@pytest.mark.parametrize("tile_mode,bm", [(0, 0), (0, 16), (0, 32), (0, 64), (0, 128), (1, 16), (1, 64), (1, 128)])
 def test_sorted_switch_glu(mg, T, tile_mode, bm):
     """MoE prefill shape (hidden 2048, E=256, top-8, inter 512, 4-bit GS 64):
     expert-sorted gate/up + SiLU and down over scheduled or naive tiles."""
@@ -126,7 +126,7 @@ def test_large_prefill_sampled(mg, bits, gs):
     idx, _ = synth.zipf_routing(4, T, sh.E, sh.top_k)
     x = synth.activations(4, T, sh.H)
     ex = synth.expert_set(4 + bits, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode="words")
-    for tile_mode, bm in ((0, 32), (1, 16)):
+    for tile_mode, bm in ((0, 0), (0, 32), (1, 16)):
         y, inv, _ = mg.switch_glu(bf(x), i32(idx), *[triple(m) for m in ex], group_size=sh.gs, bits=sh.bits,
                                   mode=mg.MODE_SORTED, tile_mode=tile_mode, bm=bm)
         yh = host_bf(y)

@@ -156,6 +156,9 @@ def decode_leg(torch, m, synth, M, steps, warmup, n_sets=42, isolated=False, cfg
 
 # ----------------------------------------------------------------------------- prefill
 def prefill_leg(torch, m, synth, T=2048, steps=20, warmup=5, cfg=3):
+    """The MoE layer at 2048 rows (hidden 2048, 256 experts, top-8, inter 512,
+    4-bit GS 64, gated shared expert): one moe_prefill call per step (sort,
+    routed + shared experts, gated combine)."""
     sh = synth.PREFILL
     dev = torch.device("cuda")
     gate, up, down = synth.device_expert_set(dev, cfg, sh.E, sh.H, sh.I, sh.gs, sh.bits)
@@ -167,58 +170,38 @@ def prefill_leg(torch, m, synth, T=2048, steps=20, warmup=5, cfg=3):
     scores = torch.from_numpy(scores_np.view(np.int16)).view(torch.bfloat16).to(dev)
     x = torch.from_numpy(synth.activations(cfg, T, sh.H).view(np.int16)).view(torch.bfloat16).to(dev)
     P = T * sh.top_k
-    y = torch.empty((P, sh.H), dtype=torch.bfloat16, device=dev)
-    inv = torch.empty(P, dtype=torch.int32, device=dev)
-    hs = torch.empty((T, sh.shared_I), dtype=torch.bfloat16, device=dev)
-    s_ = torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev)
-    z = torch.empty((T, 1), dtype=torch.bfloat16, device=dev)
-    shared = torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(m.moe_prefill_workspace_bytes(T, sh.top_k, sh.E, sh.H, sh.I, True), dtype=torch.uint8,
+                     device=dev)
     counts = np.bincount(idx_np.reshape(-1), minlength=sh.E)
     active = int((counts > 0).sum())
-    bm = 0
-    tm = Timer(torch)
 
-    def step(timed):
-        if timed:
-            tm.mark("routed_experts")
-        m.switch_glu(x, idx, gate, up, down, group_size=sh.gs, bits=sh.bits, mode=m.MODE_SORTED, bm=bm, y=y,
-                     inv=inv)
-        if timed:
-            tm.mark("shared_expert")
-        m.affine_qmm_glu(x, sg, su, group_size=sh.gs, bits=sh.bits, out=hs)
-        m.affine_qmm(hs, *sd, group_size=sh.gs, bits=sh.bits, out=s_)
-        m.affine_qmm(x, *grow, group_size=sh.gs, bits=sh.bits, out=z)
-        m.sigmoid_gate(s_, z, out=shared)
-        if timed:
-            tm.mark("combine")
-        m.moe_combine(y, inv, scores, shared, out=out)
-        if timed:
-            tm.mark(None)
+    def step(i=0):
+        m.moe_prefill(x, idx, scores, gate, up, down, shared=(sg, su, sd, grow), group_size=sh.gs, bits=sh.bits,
+                      out=out, workspace=ws)
 
     for _ in range(warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step(False)
+        step()
     torch.cuda.synchronize()
-    el = (time.perf_counter() - t0) / steps
-    for _ in range(steps):
-        step(True)
-    spans = tm.spans()
+    el_eager = (time.perf_counter() - t0) / steps
+    layer_us = graph_time_us(torch, step, 10, reps=max(1, steps // 10), check=lambda: out)
+    el = layer_us * 1e-6
     H, I, SI = sh.H, sh.I, sh.shared_I
     flops = P * 6 * H * I + T * 6 * H * SI + T * 2 * H
     B = lambda n, k: n * (k * sh.bits // 8 + 2 * (k // sh.gs) * 2)
     wbytes = active * (2 * B(I, H) + B(H, I)) + 2 * B(SI, H) + B(H, SI) + B(1, H)
     act = (T * H * 2 + P * I * 2 * 2 + P * H * 2          # x, h_sorted write+read, y_sorted write
-           + T * SI * 2 * 2 + T * H * 2 * 3               # shared path
+           + T * SI * 2 * 2 + T * H * 2                   # shared h write+read, shared y write
            + P * H * 2 + T * H * 2 * 2)                   # combine: y read, shared read, out write
     res = {"rows": T, "active_experts": active, "max_load": int(counts.max()), "mean_load": float(P / active),
-           "ms_per_layer": el * 1e3, "gflop": flops / 1e9, "bytes": wbytes + act,
+           "ms_per_layer": el * 1e3, "eager_ms_per_layer": el_eager * 1e3, "timing": "hip graph of 10 layers",
+           "gflop": flops / 1e9, "bytes": wbytes + act,
            "mfma_util": flops / el / (MFMA_BF16_PEAK_TFLOPS * 1e12),
-           "hbm_frac": (wbytes + act) / el / (HBM_PEAK_GBS * 1e9),
-           "kernel_us": {k: float(np.mean(v)) for k, v in spans.items()}}
+           "hbm_frac": (wbytes + act) / el / (HBM_PEAK_GBS * 1e9)}
     res["roofline_frac"] = max(res["mfma_util"], res["hbm_frac"])
     del gate, up, down
     torch.cuda.empty_cache()
@@ -237,7 +220,8 @@ def large_leg(torch, m, synth, T=4123, steps=5, warmup=2, bits=4, cfg=4):
     inv = torch.empty(P, dtype=torch.int32, device=dev)
     counts = np.bincount(idx_np.reshape(-1), minlength=sh.E)
     res = {"rows": T, "bits": bits, "active_experts": int((counts > 0).sum())}
-    for name, tmode, bm in (("scheduled_bm16", 0, 16), ("naive_bm16", 1, 16), ("scheduled_bm64", 0, 64)):
+    for name, tmode, bm in (("scheduled_bm16", 0, 16), ("naive_bm16", 1, 16), ("scheduled_bm64", 0, 64),
+                            ("scheduled_hybrid", 0, 0)):
         for _ in range(warmup):
             m.switch_glu(x, idx, gate, up, down, group_size=sh.gs, bits=sh.bits, mode=m.MODE_SORTED,
                          tile_mode=tmode, bm=bm, y=y, inv=inv)
@@ -249,7 +233,11 @@ def large_leg(torch, m, synth, T=4123, steps=5, warmup=2, bits=4, cfg=4):
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) / steps * 1e3
         offs = np.concatenate([[0], np.cumsum(counts)])
-        if tmode == 0:
+        if tmode == 0 and bm == 0:
+            # hybrid: 128-row tiles for experts with >= 32 rows, one few-row tile for the others
+            tiles = int(sum(-(-int(c) // 128) if c >= 32 else 1 for c in counts if c > 0))
+            passes = tiles
+        elif tmode == 0:
             tiles = int(sum(-(-int(c) // bm) for c in counts))
             passes = tiles
         else:

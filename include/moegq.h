@@ -178,6 +178,40 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
 int moegq_switch_glu_mode(int64_t T, int64_t top_k, int64_t E);
 
 /*
+ * moe_prefill: one whole MoE layer on the expert-sorted route (MTPLX PR 558
+ * Summary and Change: sorted gather, gated shared expert, one-pass combine;
+ * MLX PR 4567 Proposed changes: per-expert offsets and row tiles of one
+ * expert each; MLX issue 4509 moe(): gate, up, silu(gate) * up, down):
+ *   out[t] = bf16( bf16( sum_k bf16(y[t,k] * score[t,k]) ) + shared[t] ),
+ *   shared[t] = bf16( sigmoid(z[t]) * s[t] ), z[t] = bf16(x[t] . dequant(w_gate)^T),
+ *   s[t] = SwiGLU of the shared expert (gate/up [I, H], down [H, I]), y as in
+ *   moegq_switch_glu.
+ * The shared expert rides in the routed launches as one more expert whose
+ * rows are the T tokens.  Float parity with the composition moegq_switch_glu
+ * (SORTED) + moegq_affine_qmm_glu / moegq_affine_qmm / moegq_sigmoid_gate +
+ * moegq_moe_combine (the combine is bit-identical given the same y, s, z).
+ * x [T, H] bf16; idx [T, top_k] int32; scores [T, top_k] bf16; routed weights
+ * as moegq_switch_glu; shared matrices with the routed matrices' shapes minus
+ * the expert axis (the shared intermediate size must equal I), gate row
+ * [1, H*bits/32] words + [1, H/gs] scales/biases.  shg_w == NULL: no shared
+ * expert (every shared pointer ignored).  H and I must be multiples of 128.
+ * out [T, H] bf16.  workspace: moegq_moe_prefill_workspace_bytes(...) bytes.
+ */
+int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
+                      const int32_t* idx, int64_t top_k, const void* scores,
+                      const void* wg, const void* sg, const void* bg,
+                      const void* wu, const void* su, const void* bu,
+                      const void* wd, const void* sd, const void* bd,
+                      const void* shg_w, const void* shg_s, const void* shg_b,
+                      const void* shu_w, const void* shu_s, const void* shu_b,
+                      const void* shd_w, const void* shd_s, const void* shd_b,
+                      const void* gate_w, const void* gate_s, const void* gate_b,
+                      int group_size, int bits, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+size_t moegq_moe_prefill_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t H, int64_t I,
+                                         int has_shared);
+
+/*
  * moe_decode: the routed half of a MoE decode layer in two kernels.  Kernel 1
  * is the gathered gate/up with silu(gate)*up (MLX issue 4509, moe()); kernel 2
  * is the gathered down projection fused with the combine tail (MTPLX PR 558:
@@ -216,6 +250,17 @@ int moegq_moe_combine(const void* y, const int32_t* inv, const void* scores, con
                       int64_t T, int64_t top_k, int64_t H, void* out, void* stream);
 
 /*
+ * moe_combine_gated: moegq_moe_combine with the shared expert's sigmoid gate
+ * applied in the same pass: shared[t] is the ungated shared expert output and
+ * z [T] bf16 its gate logit; the added term is bf16(sigmoid(z[t]) * shared[t]),
+ * the arithmetic of moegq_sigmoid_gate (MTPLX PR 558 Summary: the combine
+ * takes the gated shared expert).  Bit-identical to moegq_sigmoid_gate
+ * followed by moegq_moe_combine.
+ */
+int moegq_moe_combine_gated(const void* y, const int32_t* inv, const void* scores, const void* shared,
+                            const void* z, int64_t T, int64_t top_k, int64_t H, void* out, void* stream);
+
+/*
  * moe_combine_unfused: the same arithmetic as four kernels that each write a
  * bf16 tensor (unsort -> [T, top_k, H], x score -> [T, top_k, H], sum -> [T, H],
  * + shared -> out), as the stock tail does (MTPLX PR 558 Motivation).
@@ -233,7 +278,8 @@ int moegq_moe_combine_unfused(const void* y, const int32_t* inv, const void* sco
  * lhs [P] = order / top_k, sorted_rhs [P], inv [P] (pair -> sorted row),
  * counts [E], offsets [E+1] (exclusive prefix of counts).  Any output except
  * inv, counts and offsets may be NULL.  E <= 1024.
- * workspace: moegq_workspace_bytes(MOEGQ_OP_SORT_PAIRS, P, E, 0, 0) (0 today).
+ * workspace: moegq_workspace_bytes(MOEGQ_OP_SORT_PAIRS, P, E, 0, 0) bytes (per-block
+ * expert counts of the multi-workgroup sort).
  */
 int moegq_sort_pairs(const void* idx, int idx_dtype, int64_t T, int64_t top_k, int64_t E,
                      int32_t* order, int32_t* lhs, int32_t* sorted_rhs, int32_t* inv,

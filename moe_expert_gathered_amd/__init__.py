@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
-           "switch_glu", "switch_glu_mode", "moe_decode", "moe_combine", "moe_combine_unfused", "sort_pairs",
+           "switch_glu", "switch_glu_mode", "moe_decode", "moe_prefill", "moe_prefill_workspace_bytes", "moe_combine", "moe_combine_gated", "moe_combine_unfused", "sort_pairs",
            "schedule_tiles", "rms_norm", "sigmoid_gate", "kv_feed", "selfcheck",
            "validate_indices", "workspace_bytes", "MODE_AUTO", "MODE_DECODE", "MODE_SORTED",
            "TILES_SCHEDULED", "TILES_NAIVE"]
@@ -62,7 +62,11 @@ _SIGS = {
     "moegq_switch_glu_mode": ([_i64, _i64, _i64], _int),
     "moegq_moe_decode": ([_p, _i64, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _int,
                           _int, _p, _p, _p, _sz, _p], _int),
+    "moegq_moe_prefill": ([_p, _i64, _i64, _i64, _i64, _p, _i64, _p] + [_p] * 21 + [_int, _int, _p, _p, _sz, _p],
+                          _int),
+    "moegq_moe_prefill_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64, _int], _sz),
     "moegq_moe_combine": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _p], _int),
+    "moegq_moe_combine_gated": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p], _int),
     "moegq_moe_combine_unfused": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _sz, _p], _int),
     "moegq_sort_pairs": ([_p, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _sz, _p], _int),
     "moegq_schedule_tiles": ([_p, _i64, _i64, _int, _int, _p, _i64, _p, _p], _int),
@@ -295,6 +299,36 @@ def moe_decode(x, idx, scores, gate, up, down, shared=None, group_size=64, bits=
     return out
 
 
+def moe_prefill_workspace_bytes(T: int, top_k: int, E: int, H: int, I: int, has_shared: bool = True) -> int:
+    return int(lib().moegq_moe_prefill_workspace_bytes(T, top_k, E, H, I, int(has_shared)))
+
+
+def moe_prefill(x, idx, scores, gate, up, down, shared=None, group_size=64, bits=4, out=None, workspace=None):
+    """One MoE layer on the expert-sorted route: sort, routed SwitchGLU with the
+    gated shared expert riding along, one-pass combine.  shared: None or
+    (gate, up, down, gate_row), each a (words, scales, biases) triple.
+    Returns out [T, H]."""
+    _dev(x, idx, scores, *gate, *up, *down)
+    T, H = x.shape
+    top_k = idx.shape[1]
+    E, I = gate[0].shape[0], gate[0].shape[1]
+    sh = [None] * 12
+    if shared is not None:
+        sh = [t for trip in shared for t in trip]
+        _dev(*sh)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        ws, wsb = _workspace(moe_prefill_workspace_bytes(T, top_k, E, H, I, shared is not None), x.device)
+    else:
+        ws, wsb = workspace, workspace.numel()
+    st = lib().moegq_moe_prefill(_ptr(x), T, H, I, E, _ptr(idx), top_k, _ptr(scores),
+                                 *[_ptr(t) for t in gate], *[_ptr(t) for t in up], *[_ptr(t) for t in down],
+                                 *[_ptr(t) for t in sh], group_size, bits, _ptr(out), _ptr(ws), wsb, _stream())
+    _check(st, "moe_prefill")
+    return out
+
+
 def moe_combine(y, inv, scores, shared=None, out=None):
     """Fused unsort * score, sum over top_k, + shared (one pass)."""
     _dev(y, inv, scores, shared)
@@ -305,6 +339,19 @@ def moe_combine(y, inv, scores, shared=None, out=None):
     st = lib().moegq_moe_combine(_ptr(y), _ptr(inv), _ptr(scores), _ptr(shared), T, top_k, H, _ptr(out),
                                  _stream())
     _check(st, "moe_combine")
+    return out
+
+
+def moe_combine_gated(y, inv, scores, shared, z, out=None):
+    """moe_combine with the shared expert's sigmoid gate applied in the same pass."""
+    _dev(y, inv, scores, shared, z)
+    T, top_k = scores.shape
+    H = y.shape[-1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    st = lib().moegq_moe_combine_gated(_ptr(y), _ptr(inv), _ptr(scores), _ptr(shared), _ptr(z), T, top_k, H,
+                                       _ptr(out), _stream())
+    _check(st, "moe_combine_gated")
     return out
 
 
@@ -329,8 +376,9 @@ def sort_pairs(idx, E: int):
     P = T * top_k
     mk = lambda n: torch.empty(n, dtype=torch.int32, device=idx.device)
     order, lhs, srhs, inv, counts, offsets = mk(P), mk(P), mk(P), mk(P), mk(E), mk(E + 1)
+    ws, wsb = _workspace(workspace_bytes(OP_SORT_PAIRS, P, E, 0, 0), idx.device)
     st = lib().moegq_sort_pairs(_ptr(idx), _dt(idx), T, top_k, E, _ptr(order), _ptr(lhs), _ptr(srhs), _ptr(inv),
-                                _ptr(counts), _ptr(offsets), None, 0, _stream())
+                                _ptr(counts), _ptr(offsets), _ptr(ws), wsb, _stream())
     _check(st, "sort_pairs")
     return order, lhs, srhs, inv, counts, offsets
 

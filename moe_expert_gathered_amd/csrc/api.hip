@@ -67,26 +67,36 @@ int64_t big_cap(int64_t P, int64_t E) {
 }
 int64_t small_cap(int64_t P, int64_t E) { return P < E ? P : E; }
 
-// sorted-route workspace layout
+// sorted-route workspace layout.  extra: rows of the extra (shared) expert
+// appended after the P sorted rows; layer: also the fp16 activations [T, H],
+// the expert outputs [P + extra, H] and the shared gate logits [T].
 struct SortedWs {
   int32_t* order; int32_t* lhs; int32_t* srhs; int32_t* counts; int32_t* offsets;
-  int32_t* tiles; int32_t* small_tiles; int32_t* n_tiles; uint16_t* h;
+  int32_t* tiles; int32_t* small_tiles; int32_t* n_tiles; int32_t* bc; uint16_t* h;
+  uint16_t* x16; uint16_t* y; uint16_t* z;
   size_t bytes;
 };
-SortedWs sorted_layout(char* base, int64_t P, int64_t E, int64_t I, int bm) {
+SortedWs sorted_layout(char* base, int64_t P, int64_t E, int64_t I, int bm, int64_t extra = 0,
+                       int64_t T = 0, int64_t H = 0, bool layer = false) {
   SortedWs w{};
   size_t off = 0;
   auto take = [&](size_t b) { char* p = base ? base + off : nullptr; off += align256(b); return p; };
   w.order = (int32_t*)take(4 * P);
-  w.lhs = (int32_t*)take(4 * P);
+  w.lhs = (int32_t*)take(4 * (P + extra));
   w.srhs = (int32_t*)take(4 * P);
   w.counts = (int32_t*)take(4 * E);
   w.offsets = (int32_t*)take(4 * (E + 1));
-  const int64_t cap = bm > 0 ? tile_cap(P, E, bm) : big_cap(P, E);
+  const int64_t cap = (bm > 0 ? tile_cap(P, E, bm) : big_cap(P, E)) + (extra + kBigM - 1) / kBigM;
   w.tiles = (int32_t*)take(12 * cap);
   w.small_tiles = (int32_t*)take(12 * small_cap(P, E));
   w.n_tiles = (int32_t*)take(8);
-  w.h = (uint16_t*)take(2 * P * I);
+  w.bc = (int32_t*)take(4 * sort_blocks(P) * E);
+  w.h = (uint16_t*)take(2 * (P + extra) * I);
+  if (layer) {
+    w.x16 = (uint16_t*)take(2 * T * H);
+    w.y = (uint16_t*)take(2 * (P + extra) * H);
+    w.z = (uint16_t*)take(2 * T);
+  }
   w.bytes = off;
   return w;
 }
@@ -166,7 +176,7 @@ size_t moegq_workspace_bytes(int op, int64_t P, int64_t E, int64_t N, int bm) {
       return align256(2 * T * K * H) + align256(4 * T * K) + align256(2 * T * K) + align256(2 * T * H) * 3 +
              align256(2 * 3 * T * K * H) + 256;
     }
-    case MOEGQ_OP_SORT_PAIRS: return 0;
+    case MOEGQ_OP_SORT_PAIRS: return align256(4 * sort_blocks(P) * E);
     case MOEGQ_OP_MOE_DECODE: {
       // N = I; h [P, I], plus y [P, H] for top_k > 8 when the caller passes none (H unknown here:
       // callers with top_k > 8 pass y or size it with moegq_moe_decode_workspace)
@@ -439,6 +449,7 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
   sa.tiles = ws.tiles; sa.n_tiles = ws.n_tiles;
   sa.bm = hybrid ? kBigM : bm; sa.tile_mode = hybrid ? 3 : tile_mode;
   sa.small_tiles = ws.small_tiles; sa.small_max = kSmallMax;
+  sa.block_counts = ws.bc;
   hipError_t e = launch_sort(sa, s);
   if (e != hipSuccess) return MOEGQ_ERR_LAUNCH;
   TileArgs g{};
@@ -466,11 +477,106 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
   ds_.tiles = ws.small_tiles; ds_.n_tiles = ws.n_tiles + 1; ds_.bm = kSmallMax; ds_.tile_mode = 0;
   ds_.grid_tiles = small_cap(P, E);
   g.tile_mode = 0; d.tile_mode = 0;
+  if (tiles_mma_supported(H, I, T) && tiles_mma_supported(I, H, P)) {
+    // fp16 copy of x for the matrix cores, parked in y (y is written only by the down pass);
+    // h is written and read in the same fp16 chunk order
+    if (launch_to_f16((const uint16_t*)x, T * H, bits, (uint16_t*)y, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    g.x = gs_.x = (const uint16_t*)y;
+    if (launch_tiles_mma(g, bits, group_size, true, true, 128, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    if (hybrid && launch_tiles_mma(gs_, bits, group_size, true, true, 32, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    if (launch_tiles_mma(d, bits, group_size, false, false, 128, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    if (hybrid && launch_tiles_mma(ds_, bits, group_size, false, false, 32, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    return MOEGQ_OK;
+  }
   if (launch_tiles_big(g, bits, group_size, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   if (hybrid && launch_tiles_small(gs_, bits, group_size, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   if (launch_tiles_big(d, bits, group_size, false, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   if (hybrid && launch_tiles_small(ds_, bits, group_size, false, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   return MOEGQ_OK;
+}
+
+size_t moegq_moe_prefill_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t H, int64_t I,
+                                         int has_shared) {
+  if (T < 0 || top_k <= 0 || E <= 0 || H <= 0 || I <= 0) return 0;
+  const int64_t P = T * top_k;
+  return sorted_layout(nullptr, P, E, I, 0, has_shared ? T : 0, T, H, true).bytes;
+}
+
+int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, const int32_t* idx,
+                      int64_t top_k, const void* scores, const void* wg, const void* sg, const void* bg,
+                      const void* wu, const void* su, const void* bu, const void* wd, const void* sd,
+                      const void* bd, const void* shg_w, const void* shg_s, const void* shg_b,
+                      const void* shu_w, const void* shu_s, const void* shu_b, const void* shd_w,
+                      const void* shd_s, const void* shd_b, const void* gate_w, const void* gate_s,
+                      const void* gate_b, int group_size, int bits, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st;
+  if ((st = check_quant(H, group_size, bits))) return st;
+  if ((st = check_quant(I, group_size, bits))) return st;
+  if (T < 0 || top_k <= 0 || E <= 0 || T > kMaxDim || top_k > 64 || H % 8 != 0) return MOEGQ_ERR_SHAPE;
+  if (E > kMaxExperts) return MOEGQ_ERR_UNSUPPORTED;
+  if (T == 0) return MOEGQ_OK;
+  if (!x || !idx || !scores || !wg || !sg || !bg || !wu || !su || !bu || !wd || !sd || !bd || !out)
+    return MOEGQ_ERR_NULL_ARG;
+  const bool shared = shg_w != nullptr;
+  if (shared && (!shg_s || !shg_b || !shu_w || !shu_s || !shu_b || !shd_w || !shd_s || !shd_b || !gate_w ||
+                 !gate_s || !gate_b))
+    return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(x) || !aligned16(wg) || !aligned16(wu) || !aligned16(wd) || !aligned16(out) ||
+      (shared && (!aligned16(shg_w) || !aligned16(shu_w) || !aligned16(shd_w) || !aligned16(gate_w))))
+    return MOEGQ_ERR_ALIGN;
+  const int64_t P = T * top_k;
+  const int64_t extra = shared ? T : 0;
+  if (!tiles_mma_supported(H, I, T) || !tiles_mma_supported(I, H, P + extra)) return MOEGQ_ERR_UNSUPPORTED;
+  const SortedWs ws = sorted_layout((char*)workspace, P, E, I, 0, extra, T, H, true);
+  if (!workspace || workspace_bytes < ws.bytes) return MOEGQ_ERR_WORKSPACE;
+  hipStream_t s = S(stream);
+  SortArgs sa{};
+  sa.idx = idx; sa.P = P; sa.top_k = (int)top_k; sa.E = (int)E;
+  int32_t* inv = ws.order;           // the layer keeps the inverse permutation, not the order
+  sa.order = nullptr; sa.lhs = ws.lhs; sa.sorted_rhs = ws.srhs; sa.inv = inv;
+  sa.counts = ws.counts; sa.offsets = ws.offsets;
+  sa.tiles = ws.tiles; sa.n_tiles = ws.n_tiles; sa.bm = kBigM; sa.tile_mode = 3;
+  sa.small_tiles = ws.small_tiles; sa.small_max = kSmallMax;
+  sa.extra_rows = extra; sa.block_counts = ws.bc;
+  if (launch_sort(sa, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (launch_to_f16((const uint16_t*)x, T * H, bits, ws.x16, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (shared) {
+    // shared expert's sigmoid gate logit z[t] = x[t] . w_gate (one output row)
+    QmvArgs zq{};
+    zq.x = (const uint16_t*)x; zq.lhs_div = 1;
+    zq.w0 = (const uint32_t*)gate_w; zq.s0 = (const uint16_t*)gate_s; zq.b0 = (const uint16_t*)gate_b;
+    zq.N = 1; zq.K = (int)H; zq.out = ws.z;
+    if (launch_qmv(zq, bits, group_size, false, T, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  }
+  TileArgs g{};
+  g.x = ws.x16; g.lhs = ws.lhs; g.lhs_div = 1; g.rows_per_batch = 1;
+  g.tiles = ws.tiles; g.n_tiles = ws.n_tiles; g.P = P; g.E = (int)E;
+  g.w0 = (const uint32_t*)wg; g.s0 = (const uint16_t*)sg; g.b0 = (const uint16_t*)bg;
+  g.w1 = (const uint32_t*)wu; g.s1 = (const uint16_t*)su; g.b1 = (const uint16_t*)bu;
+  g.xw0 = (const uint32_t*)shg_w; g.xs0 = (const uint16_t*)shg_s; g.xb0 = (const uint16_t*)shg_b;
+  g.xw1 = (const uint32_t*)shu_w; g.xs1 = (const uint16_t*)shu_s; g.xb1 = (const uint16_t*)shu_b;
+  g.N = (int)I; g.K = (int)H; g.out = ws.h; g.bm = kBigM; g.tile_mode = 0;
+  g.grid_tiles = big_cap(P, E) + (extra + kBigM - 1) / kBigM;
+  TileArgs d = g;
+  d.x = ws.h; d.lhs = nullptr;
+  d.w0 = (const uint32_t*)wd; d.s0 = (const uint16_t*)sd; d.b0 = (const uint16_t*)bd;
+  d.w1 = nullptr; d.s1 = nullptr; d.b1 = nullptr;
+  d.xw0 = (const uint32_t*)shd_w; d.xs0 = (const uint16_t*)shd_s; d.xb0 = (const uint16_t*)shd_b;
+  d.xw1 = nullptr; d.xs1 = nullptr; d.xb1 = nullptr;
+  d.N = (int)H; d.K = (int)I; d.out = ws.y;
+  TileArgs gs_ = g, ds_ = d;
+  gs_.tiles = ds_.tiles = ws.small_tiles;
+  gs_.n_tiles = ds_.n_tiles = ws.n_tiles + 1;
+  gs_.bm = ds_.bm = kSmallMax;
+  gs_.grid_tiles = ds_.grid_tiles = small_cap(P, E);
+  if (launch_tiles_mma(g, bits, group_size, true, true, 128, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (launch_tiles_mma(gs_, bits, group_size, true, true, 32, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (launch_tiles_mma(d, bits, group_size, false, false, 128, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (launch_tiles_mma(ds_, bits, group_size, false, false, 32, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  // out[t] = bf16(bf16(sum_k bf16(y[inv] * score)) + bf16(sigmoid(z[t]) * y[P + t]))
+  return status_of(launch_combine(ws.y, inv, (const uint16_t*)scores, shared ? ws.y + P * H : nullptr,
+                                  shared ? ws.z : nullptr, T, (int)top_k, H, (uint16_t*)out, s));
 }
 
 int moegq_moe_decode(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, const int32_t* idx,
@@ -512,8 +618,8 @@ int moegq_moe_decode(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
   uint16_t* yw = (uint16_t*)y;
   d.out = yw;
   if (launch_qmv(d, bits, group_size, false, P, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-  return status_of(launch_combine(yw, nullptr, (const uint16_t*)scores, (const uint16_t*)shared, T, (int)top_k, H,
-                                  (uint16_t*)out, s));
+  return status_of(launch_combine(yw, nullptr, (const uint16_t*)scores, (const uint16_t*)shared, nullptr, T,
+                                  (int)top_k, H, (uint16_t*)out, s));
 }
 
 int moegq_moe_combine(const void* y, const int32_t* inv, const void* scores, const void* shared, int64_t T,
@@ -522,8 +628,18 @@ int moegq_moe_combine(const void* y, const int32_t* inv, const void* scores, con
   if (T == 0) return MOEGQ_OK;
   if (!y || !scores || !out) return MOEGQ_ERR_NULL_ARG;
   if (!aligned16(y) || !aligned16(out) || (shared && !aligned16(shared))) return MOEGQ_ERR_ALIGN;
-  return status_of(launch_combine((const uint16_t*)y, inv, (const uint16_t*)scores, (const uint16_t*)shared, T,
-                                  (int)top_k, H, (uint16_t*)out, S(stream)));
+  return status_of(launch_combine((const uint16_t*)y, inv, (const uint16_t*)scores, (const uint16_t*)shared,
+                                  nullptr, T, (int)top_k, H, (uint16_t*)out, S(stream)));
+}
+
+int moegq_moe_combine_gated(const void* y, const int32_t* inv, const void* scores, const void* shared,
+                            const void* z, int64_t T, int64_t top_k, int64_t H, void* out, void* stream) {
+  if (T < 0 || top_k <= 0 || H <= 0 || H % 8 != 0 || T > kMaxDim || H > kMaxDim) return MOEGQ_ERR_SHAPE;
+  if (T == 0) return MOEGQ_OK;
+  if (!y || !scores || !shared || !z || !out) return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(y) || !aligned16(out) || !aligned16(shared)) return MOEGQ_ERR_ALIGN;
+  return status_of(launch_combine((const uint16_t*)y, inv, (const uint16_t*)scores, (const uint16_t*)shared,
+                                  (const uint16_t*)z, T, (int)top_k, H, (uint16_t*)out, S(stream)));
 }
 
 int moegq_moe_combine_unfused(const void* y, const int32_t* inv, const void* scores, const void* shared,
@@ -543,13 +659,15 @@ int moegq_moe_combine_unfused(const void* y, const int32_t* inv, const void* sco
 int moegq_sort_pairs(const void* idx, int idx_dtype, int64_t T, int64_t top_k, int64_t E, int32_t* order,
                      int32_t* lhs, int32_t* sorted_rhs, int32_t* inv, int32_t* counts, int32_t* offsets,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace; (void)workspace_bytes;
   int st;
   if ((st = check_idx_dtype(idx_dtype))) return st;
   if (T < 0 || top_k <= 0 || E <= 0 || T > kMaxDim || top_k > 64) return MOEGQ_ERR_SHAPE;
   if (E > kMaxExperts) return MOEGQ_ERR_UNSUPPORTED;
   if (!idx || !inv || !counts || !offsets) return MOEGQ_ERR_NULL_ARG;
+  const size_t need = moegq_workspace_bytes(MOEGQ_OP_SORT_PAIRS, T * top_k, E, 0, 0);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOEGQ_ERR_WORKSPACE;
   SortArgs sa{};
+  sa.block_counts = (int32_t*)workspace;
   sa.idx = (const int32_t*)idx; sa.P = T * top_k; sa.top_k = (int)top_k; sa.E = (int)E;
   sa.order = order; sa.lhs = lhs; sa.sorted_rhs = sorted_rhs; sa.inv = inv;
   sa.counts = counts; sa.offsets = offsets; sa.tiles = nullptr; sa.n_tiles = nullptr; sa.bm = 0;
@@ -609,7 +727,7 @@ int moegq_selfcheck(void* workspace, size_t workspace_bytes, void* stream) {
   uint16_t* scratch = (uint16_t*)take(2 * 3 * P * H);
   hipStream_t s = S(stream);
   if (launch_fill_selfcheck(y, inv, scores, shared, T, (int)K, H, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-  if (launch_combine(y, inv, scores, shared, T, (int)K, H, o1, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (launch_combine(y, inv, scores, shared, nullptr, T, (int)K, H, o1, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   if (launch_combine_unfused(y, inv, scores, shared, T, (int)K, H, o2, scratch, s) != hipSuccess)
     return MOEGQ_ERR_LAUNCH;
   static uint16_t h1[128 * 2048], h2[128 * 2048];

@@ -11,6 +11,10 @@
 
 namespace moegq {
 
+// shared expert's sigmoid gate: the fp32 gate of a bf16 logit, and one gated
+// element bf16(gate * s) (one rounding)
+MOEGQ_DEV float sigmoid_gate_of(uint16_t z) { return 1.0f / (1.0f + __expf(-bf16_to_f32(z))); }
+
 // ---------------------------------------------------------------- fused combine
 // One thread owns 8 consecutive hidden elements (one 16-byte vector) of one
 // token and walks the token's top_k slots in order.
@@ -18,6 +22,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                                                       const int32_t* __restrict__ inv,
                                                       const uint16_t* __restrict__ scores,
                                                       const uint16_t* __restrict__ shared,
+                                                      const uint16_t* __restrict__ z,
                                                       int64_t T, int top_k, int64_t H,
                                                       uint16_t* __restrict__ out) {
   const int64_t cpr = H / 8;
@@ -42,7 +47,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   uint32_t o[4];
   if (shared) {
     const uint4 s = *reinterpret_cast<const uint4*>(shared + t * H + h8);
-    const uint32_t sd[4] = {s.x, s.y, s.z, s.w};
+    uint32_t sd[4] = {s.x, s.y, s.z, s.w};
+    if (z) {
+      const float gate = sigmoid_gate_of(z[t]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sd[i] = pack_bf16x2(gate * bf16_lo(sd[i]), gate * bf16_hi(sd[i]));
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float a0 = bf16_to_f32(f32_to_bf16(acc[2 * i])) + bf16_lo(sd[i]);
@@ -57,12 +67,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 }
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const uint16_t* scores,
-                          const uint16_t* shared, int64_t T, int top_k, int64_t H, uint16_t* out,
+                          const uint16_t* shared, const uint16_t* z, int64_t T, int top_k, int64_t H, uint16_t* out,
                           hipStream_t st) {
   const int64_t n = T * (H / 8);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, y, inv,
-                     scores, shared, T, top_k, H, out);
+                     scores, shared, z, T, top_k, H, out);
   return hipGetLastError();
 }
 
@@ -189,8 +199,7 @@ __global__ __launch_bounds__(256) void sigmoid_gate_kernel(const uint16_t* __res
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= T * cpr) return;
   const int64_t t = c / cpr;
-  const float zf = bf16_to_f32(z[t * zs]);
-  const float gate = 1.0f / (1.0f + __expf(-zf));
+  const float gate = sigmoid_gate_of(z[t * zs]);
   const uint4 v = reinterpret_cast<const uint4*>(s)[c];
   const uint32_t d[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[4];

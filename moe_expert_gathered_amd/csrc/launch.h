@@ -46,7 +46,12 @@ struct SortArgs {
   // hybrid schedule (tile_mode 3): experts with >= small_max rows get bm-row
   // tiles in `tiles`, the others one tile each in `small_tiles`; n_tiles[0..1]
   int32_t* small_tiles; int small_max;
+  // extra expert E over rows [P, P + extra_rows) (the shared expert, row t = token t):
+  // bm-row tiles appended to `tiles`, lhs[P + t] = t
+  int64_t extra_rows;
+  int32_t* block_counts;    // workspace: [sort_blocks(P), E] int32
 };
+int64_t sort_blocks(int64_t P);
 hipError_t launch_sort(const SortArgs& a, hipStream_t st);
 hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int tile_mode, int32_t* tiles,
                            int32_t* n_tiles, hipStream_t st);
@@ -65,6 +70,9 @@ struct TileArgs {
   int E;
   const uint32_t* w0; const uint16_t* s0; const uint16_t* b0;
   const uint32_t* w1; const uint16_t* s1; const uint16_t* b1;
+  // extra expert (index E in the tile table; tiles_mma only): the shared expert's matrices
+  const uint32_t* xw0; const uint16_t* xs0; const uint16_t* xb0;
+  const uint32_t* xw1; const uint16_t* xs1; const uint16_t* xb1;
   int N, K;
   uint16_t* out;            // [P, N]
   int bm; int tile_mode;    // 0 scheduled table, 1 naive (loop over experts), 2 dense (expert 0)
@@ -75,11 +83,21 @@ hipError_t launch_tiles(const TileArgs& a, int bits, int gs, bool glu, hipStream
 hipError_t launch_tiles_big(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st);
 // tiles of at most 16 (bm <= 16) or 32 rows from a table (tile_mode 0); rows gathered through lhs
 hipError_t launch_tiles_small(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st);
+// 128-row tiles with register-dequantized weights (tile_mode 0: table, 2: dense rows).  a.x holds
+// fp16 rows in the dequantizer's chunk order (launch_to_f16), gathered through a.lhs (or row r);
+// out16: the GLU output is written the same way (fp16, chunk order) for a following down pass
+bool tiles_mma_supported(int64_t K, int64_t N, int64_t src_rows);
+// rows: 128 (tile table of up to 128-row tiles, or dense rows) or 32 (tiles of at most 32 rows)
+hipError_t launch_tiles_mma(const TileArgs& a, int bits, int gs, bool glu, bool out16, int rows,
+                            hipStream_t st);
+hipError_t launch_to_f16(const uint16_t* x, int64_t elems, int bits, uint16_t* out, hipStream_t st);
 
 // combine tail
+// shared (nullable) rows [T, H] are added as they are, or, with z (nullable, [T] bf16), gated first:
+// bf16(sigmoid(z[t]) * shared[t]) with the arithmetic of launch_sigmoid_gate
 hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const uint16_t* scores,
-                          const uint16_t* shared, int64_t T, int top_k, int64_t H, uint16_t* out,
-                          hipStream_t st);
+                          const uint16_t* shared, const uint16_t* z, int64_t T, int top_k, int64_t H,
+                          uint16_t* out, hipStream_t st);
 hipError_t launch_combine_unfused(const uint16_t* y, const int32_t* inv, const uint16_t* scores,
                                   const uint16_t* shared, int64_t T, int top_k, int64_t H,
                                   uint16_t* out, uint16_t* scratch, hipStream_t st);

@@ -5,15 +5,17 @@
 // changes): per-expert offsets precomputed from the expert ids feed a row-tile
 // scheduler whose tiles carry (row to start from, expert, valid rows).
 //
-// One workgroup of 1024 threads (the pair lists here are <= a few 10^5):
-//  1. histogram of expert ids with LDS atomics (counts are order-free);
-//  2. exclusive scan -> offsets, and per-expert tile counts -> tile offsets;
-//  3. stable scatter in chunks of 1024 pairs.  Inside a wave, the lanes with
-//     the same expert id are found from one ballot per key bit (no loop over
-//     distinct keys); a lane's rank among them is a popcount of the lower
-//     lanes.  Per-wave counts go to a small LDS table so each wave adds the
-//     counts of the waves before it; a running cursor per expert carries the
-//     chunks.  Every position is a function of the input only: deterministic.
+// Three launches, each pair list split in blocks of 1024 pairs:
+//  1. count: a per-block histogram of expert ids.  Lanes of a wave holding
+//     the same id are matched with one ballot per id bit, and only the first
+//     of them adds the group's count (one LDS atomic per distinct id per wave).
+//  2. scan (one workgroup, one expert per thread): counts, exclusive offsets,
+//     the base row of every (block, expert) for the stable scatter, and the
+//     tile tables.
+//  3. scatter: each pair's rank among the equal ids of its block is the
+//     popcount of the matched lower lanes plus the counts of the lower waves
+//     (per-wave LDS table); its row is the (block, expert) base plus that rank.
+//     Rows depend on the input only: the sort is stable and deterministic.
 #include "common.h"
 #include "launch.h"
 
@@ -22,6 +24,8 @@ namespace moegq {
 constexpr int SORT_THREADS = 1024;
 constexpr int SORT_WAVES = SORT_THREADS / 64;
 constexpr int SORT_MAXE = 1024;
+
+int64_t sort_blocks(int64_t P) { return (P + SORT_THREADS - 1) / SORT_THREADS; }
 
 // exclusive scan of one int per thread over the workgroup; returns the total
 MOEGQ_DEV int block_excl_scan(int v, int* wtot, int& excl) {
@@ -54,43 +58,60 @@ MOEGQ_DEV void write_tiles(int e, int cnt, int off, int toff, int bm, int32_t* t
   }
 }
 
-__global__ __launch_bounds__(SORT_THREADS) void sort_kernel(SortArgs A) {
-  __shared__ int cnt[SORT_MAXE];
-  __shared__ int cursor[SORT_MAXE];
-  __shared__ uint8_t tab[SORT_WAVES][SORT_MAXE];
-  __shared__ int wtot[SORT_WAVES];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = A.E;
-  const int64_t P = A.P;
-  for (int e = tid; e < SORT_MAXE; e += SORT_THREADS) {
-    cnt[e] = 0;
-    for (int w = 0; w < SORT_WAVES; ++w) tab[w][e] = 0;
+// Lanes of this wave whose key equals this lane's key (keys < 2^nbits; invalid
+// lanes are excluded).
+MOEGQ_DEV uint64_t match_key(int key, bool valid, int nbits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
   }
-  __syncthreads();
+  return m;
+}
+
+MOEGQ_DEV int key_bits(int E) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // 1. histogram (ids outside [0, E) break the precondition; clamp to stay in
-  //    bounds).  Lanes with equal ids are matched with one ballot per id bit and
-  //    only the first of them adds the group's count: no atomic contention on
-  //    popular experts.
-  for (int64_t base = 0; base < P; base += SORT_THREADS) {
-    const int64_t p = base + tid;
-    const bool valid = p < P;
-    const int e = valid ? min(max(A.idx[p], 0), E - 1) : 0;
-    uint64_t match = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bb = __ballot(bit);
-      match &= bit ? bb : ~bb;
-    }
-    if (valid && __popcll(match & lt_mask) == 0) atomicAdd(&cnt[e], (int)__popcll(match));
-  }
+  return nbits;
+}
+
+__global__ __launch_bounds__(SORT_THREADS) void sort_count_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
+                                                                  int32_t* __restrict__ bc) {
+  __shared__ int cnt[SORT_MAXE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int e = tid; e < E; e += SORT_THREADS) cnt[e] = 0;
   __syncthreads();
-  // 2. scans (E <= SORT_MAXE == SORT_THREADS: one expert per thread)
-  const int c = tid < E ? cnt[tid] : 0;
+  const int64_t p = (int64_t)blockIdx.x * SORT_THREADS + tid;
+  const bool valid = p < P;
+  // ids outside [0, E) break the precondition; clamp to stay in bounds
+  const int e = valid ? min(max(idx[p], 0), E - 1) : 0;
+  const uint64_t m = match_key(e, valid, key_bits(E));
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (valid && __popcll(m & lt) == 0) atomicAdd(&cnt[e], (int)__popcll(m));
+  __syncthreads();
+  for (int ee = tid; ee < E; ee += SORT_THREADS) bc[(int64_t)blockIdx.x * E + ee] = cnt[ee];
+}
+
+__global__ __launch_bounds__(SORT_THREADS) void sort_scan_kernel(SortArgs A, int nblk) {
+  __shared__ int wtot[SORT_WAVES];
+  const int tid = threadIdx.x;
+  const int E = A.E;
+  const int64_t P = A.P;
+  // counts, and per-block bases relative to the expert's first row
+  int c = 0;
+  if (tid < E) {
+    for (int b = 0; b < nblk; ++b) {
+      int32_t* q = A.block_counts + (int64_t)b * E + tid;
+      const int v = *q;
+      *q = c;
+      c += v;
+    }
+  }
   int off;
   block_excl_scan(c, wtot, off);
+  if (tid < E)
+    for (int b = 0; b < nblk; ++b) A.block_counts[(int64_t)b * E + tid] += off;
   const bool hybrid = A.tile_mode == 3;
   const bool is_big = !hybrid || c >= A.small_max;
   const int ntile = (A.bm > 0 && is_big) ? (c + A.bm - 1) / A.bm : 0;
@@ -102,17 +123,26 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_kernel(SortArgs A) {
   if (tid < E) {
     A.counts[tid] = c;
     A.offsets[tid] = off;
-    cursor[tid] = off;
     if (A.tiles && (A.tile_mode == 0 || (hybrid && is_big))) write_tiles(tid, c, off, toff, A.bm, A.tiles);
     if (A.small_tiles && nsmall) {
       int32_t* t = A.small_tiles + 3 * soff;
       t[0] = off; t[1] = tid; t[2] = c;
     }
   }
+  // the extra expert's tiles follow the routed ones
+  const int extra_tiles = (A.extra_rows > 0 && A.tiles && A.bm > 0) ? (int)((A.extra_rows + A.bm - 1) / A.bm) : 0;
+  for (int j = tid; j < extra_tiles; j += SORT_THREADS) {
+    int32_t* t = A.tiles + 3 * (int64_t)(total_tiles + j);
+    t[0] = (int32_t)(P + (int64_t)j * A.bm);
+    t[1] = E;
+    t[2] = (int32_t)min((int64_t)A.bm, A.extra_rows - (int64_t)j * A.bm);
+  }
+  if (A.lhs)
+    for (int64_t t = tid; t < A.extra_rows; t += SORT_THREADS) A.lhs[P + t] = (int32_t)t;
   if (tid == 0) {
     A.offsets[E] = (int32_t)P;
     if (A.n_tiles) {
-      A.n_tiles[0] = (A.tile_mode == 0 || hybrid) ? total_tiles : (int32_t)((P + A.bm - 1) / A.bm);
+      A.n_tiles[0] = (A.tile_mode == 0 || hybrid) ? total_tiles + extra_tiles : (int32_t)((P + A.bm - 1) / A.bm);
       if (hybrid) A.n_tiles[1] = total_small;
     }
   }
@@ -124,41 +154,40 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_kernel(SortArgs A) {
       A.tiles[3 * t + 2] = (int32_t)min((int64_t)A.bm, P - t * A.bm);
     }
   }
+}
+
+__global__ __launch_bounds__(SORT_THREADS) void sort_scatter_kernel(SortArgs A) {
+  __shared__ __attribute__((aligned(16))) uint8_t tab[SORT_WAVES][SORT_MAXE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = A.E;
+  reinterpret_cast<uint4*>(&tab[0][0])[tid] = make_uint4(0, 0, 0, 0);   // 16 KiB = 1024 x 16 B
   __syncthreads();
-  // 3. stable scatter
-  for (int64_t base = 0; base < P; base += SORT_THREADS) {
-    const int64_t p = base + tid;
-    const bool valid = p < P;
-    const int e = valid ? min(max(A.idx[p], 0), E - 1) : 0;
-    uint64_t match = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bb = __ballot(bit);
-      match &= bit ? bb : ~bb;
-    }
-    const int rank = __popcll(match & lt_mask);
-    if (valid && rank == 0) tab[wave][e] = (uint8_t)__popcll(match);
-    __syncthreads();
-    if (valid) {
-      int pos = cursor[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += tab[w][e];
-      if (A.order) A.order[pos] = (int32_t)p;
-      if (A.lhs) A.lhs[pos] = (int32_t)(p / A.top_k);
-      if (A.sorted_rhs) A.sorted_rhs[pos] = e;
-      A.inv[p] = pos;
-    }
-    __syncthreads();
-    for (int ee = tid; ee < E; ee += SORT_THREADS) {
-      int s = 0;
-      for (int w = 0; w < SORT_WAVES; ++w) { s += tab[w][ee]; tab[w][ee] = 0; }
-      cursor[ee] += s;
-    }
-    __syncthreads();
-  }
+  const int64_t p = (int64_t)blockIdx.x * SORT_THREADS + tid;
+  const bool valid = p < A.P;
+  const int e = valid ? min(max(A.idx[p], 0), E - 1) : 0;
+  const uint64_t m = match_key(e, valid, key_bits(E));
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(m & lt);
+  if (valid && rank == 0) tab[wave][e] = (uint8_t)__popcll(m);
+  __syncthreads();
+  if (!valid) return;
+  int pos = A.block_counts[(int64_t)blockIdx.x * E + e] + rank;
+  for (int w = 0; w < wave; ++w) pos += tab[w][e];
+  if (A.order) A.order[pos] = (int32_t)p;
+  if (A.lhs) A.lhs[pos] = (int32_t)(p / A.top_k);
+  if (A.sorted_rhs) A.sorted_rhs[pos] = e;
+  A.inv[p] = pos;
 }
 
 hipError_t launch_sort(const SortArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(SORT_THREADS), 0, st, a);
+  if (a.E <= 0 || a.E > SORT_MAXE || (!a.block_counts && a.P > 0)) return hipErrorInvalidValue;
+  const int64_t nb = sort_blocks(a.P);
+  if (nb > 0) {
+    hipLaunchKernelGGL(sort_count_kernel, dim3((unsigned)nb), dim3(SORT_THREADS), 0, st, a.idx, a.P, a.E,
+                       a.block_counts);
+  }
+  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(SORT_THREADS), 0, st, a, (int)nb);
+  if (nb > 0) hipLaunchKernelGGL(sort_scatter_kernel, dim3((unsigned)nb), dim3(SORT_THREADS), 0, st, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,297 @@
+// Row tiles of 16 * MI sorted rows x 256 MFMA columns (MI = 8: experts that
+// receive many rows, and dense many-row products; MI = 2: one tile per expert
+// with fewer than 32 rows), weights dequantized straight into matrix-core
+// registers.
+//
+// MLX PR 4567 (Proposed changes): each tile carries a row start, one expert
+// and a valid-row count, so it makes exactly one K pass over one expert.
+// MTPLX PR 558 (Change): the rows are the expert-sorted (token, slot) pairs;
+// the gate/up pass gathers activation rows through lhs, the down pass reads
+// the sorted intermediate rows in order.
+//
+// gfx950 mapping (v_mfma_f32_16x16x32_f16, fp32 accumulation):
+//  * 4 waves; each wave owns all 16 * MI rows and 64 MFMA columns (MI x 4
+//    blocks; 128 fp32 accumulators at MI = 8).  A column's codes are read by exactly one wave,
+//    so each code is dequantized once per tile, in registers, in the layout
+//    the MFMA B operand wants: lane (g = lane / 16, c = lane % 16) holds for
+//    column c the 32 consecutive k of lane group g (k0 + 32 g ..), which it
+//    loads as one (4-bit) or two (8-bit) 128-bit buffer loads.  Inside a K
+//    step of 128, MFMA sub-step s contracts k0 + 32 g + 8 s + (0..7) in lane
+//    group g; both operands use that same assignment, so the sum is the full
+//    dot product over K.
+//  * The activation rows are fp16 (converted once, before the tile pass) in
+//    the element order the dequantizer produces inside each 8-element chunk
+//    (4-bit: q0 q2 q4 q6 q1 q3 q5 q7; 8-bit: natural).  They travel from HBM
+//    to LDS with buffer loads that write LDS directly (no register staging),
+//    into a double buffer (2 x 4 KiB per 16 rows).  Row r's 16-byte chunk c sits in slot
+//    c ^ (r % 16) of the row, so the 16 rows a ds_read_b128 touches fall in
+//    distinct banks.
+//  * GLU: a wave's 4 column blocks are (gate f, up f, gate f+16, up f+16), so
+//    silu(g) * u is applied in registers in the epilogue.
+//  * One barrier per K step: the next step's activations and codes are in
+//    flight during the current step's MFMAs.
+//  * Workgroups are dealt to the 8 XCDs round-robin by the hardware; the
+//    block index is remapped so that each XCD works on a contiguous range of
+//    (tile, column block) pairs: the column blocks of one row tile, and the
+//    consecutive tiles of one expert, then share that XCD's L2.
+//  * An optional extra expert (index E, its own weight pointers) carries the
+//    shared expert through the same launch.
+#include "common.h"
+#include "launch.h"
+
+namespace moegq {
+
+constexpr int TM_C = 256;   // MFMA columns per tile
+constexpr int TM_K = 128;   // K per step
+
+// position of element k (0..7) of a chunk in the dequantizer's order
+template <int BITS>
+MOEGQ_DEV int chunk_pos(int k) { return BITS == 4 ? ((k >> 1) | ((k & 1) << 2)) : k; }
+
+// eight codes (one 4-bit word, or two 8-bit words) -> one fp16 MFMA operand
+template <int BITS>
+MOEGQ_DEV f16x8_t deq_operand(uint32_t w0, uint32_t w1, f16x2_t s2, f16x2_t b2) {
+  uint32_t o[4];
+  if (BITS == 4) {
+    deq4_f16(w0, s2, b2, o);
+  } else {
+    deq8_f16(w0, s2, b2, o);
+    deq8_f16(w1, s2, b2, o + 2);
+  }
+  return __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// register budget: 2 workgroups per CU (128 accumulators per lane at MI = 8;
+// the 32-row variant needs far fewer registers and fits more)
+template <int BITS, int GS, bool GLU, bool OUT16, int MI>
+__global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
+  constexpr int NF = GLU ? TM_C / 2 : TM_C;      // output features per tile
+  constexpr int CB = 4 * BITS;                    // code bytes per lane per K step (32 codes)
+  constexpr int TM_M = 16 * MI;                   // rows per tile
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][16 * MI * TM_K];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c16 = lane & 15;
+  const int N = A.N, K = A.K;
+  const int NB = (N + NF - 1) / NF;
+  const int total = A.tile_mode == 2 ? (int)gridDim.x : *A.n_tiles * NB;
+  int bid = blockIdx.x;
+  if (bid >= total) return;
+  {
+    const int q = total / 8;           // XCD-contiguous ranges over the first 8 q blocks
+    if (bid < 8 * q) bid = (bid % 8) * q + bid / 8;
+  }
+  const int tile = bid / NB;
+  const int n0 = (bid % NB) * NF;
+  const int Kw = K * BITS / 32, G = K / GS;
+
+  int r0, r1, e;
+  if (A.tile_mode == 2) {            // dense rows, one weight matrix
+    r0 = tile * TM_M;
+    if (r0 >= A.P) return;
+    r1 = (int)min(A.P, (int64_t)r0 + TM_M);
+    e = 0;
+  } else {
+    const int32_t* t = A.tiles + 3 * tile;
+    r0 = t[0]; e = t[1]; r1 = r0 + t[2];
+  }
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  r1 = __builtin_amdgcn_readfirstlane(r1);
+  e = __builtin_amdgcn_readfirstlane(e);
+
+  // ---- activation loads: wave w, load v covers rows 4 (MI w + v) .. + 3; lane
+  //      (g, c16) fetches chunk c16 ^ (row % 16) of row 4 (MI w + v) + g
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A.x, 0xFFFFFFFFu);
+  uint32_t a_off[8];                          // MI <= 8 entries used
+#pragma unroll
+  for (int v = 0; v < MI; ++v) {
+    const int r = 4 * (MI * wave + v) + g;
+    const int rr = min(r0 + r, r1 - 1);          // rows past the tile repeat a valid row (never stored)
+    const int src = A.lhs ? A.lhs[rr] : rr;
+    const int chunk = c16 ^ (r & 15);
+    a_off[v] = (uint32_t)src * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
+  }
+  auto load_a = [&](int ks, int buf) {
+    const uint32_t soff = (uint32_t)ks * TM_K * 2u;
+#pragma unroll
+    for (int v = 0; v < MI; ++v) {
+      uint16_t* dst = &As[buf][4 * (MI * wave + v) * TM_K];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, a_off[v], soff,
+                                               0, 0);
+    }
+  };
+
+  // ---- code / scale loads: column block j of this wave
+  const size_t wstride = (size_t)N * Kw, sstride = (size_t)N * G;
+  const bool ex = e >= A.E;          // the extra (shared) expert
+  const size_t eo = ex ? 0 : (size_t)e;
+  const __amdgpu_buffer_rsrc_t rw0 = make_rsrc((ex ? A.xw0 : A.w0) + eo * wstride, (uint32_t)(wstride * 4));
+  const __amdgpu_buffer_rsrc_t rs0 = make_rsrc((ex ? A.xs0 : A.s0) + eo * sstride, (uint32_t)(sstride * 2));
+  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc((ex ? A.xb0 : A.b0) + eo * sstride, (uint32_t)(sstride * 2));
+  __amdgpu_buffer_rsrc_t rw1 = rw0, rs1 = rs0, rb1 = rb0;
+  if (GLU) {
+    rw1 = make_rsrc((ex ? A.xw1 : A.w1) + eo * wstride, (uint32_t)(wstride * 4));
+    rs1 = make_rsrc((ex ? A.xs1 : A.s1) + eo * sstride, (uint32_t)(sstride * 2));
+    rb1 = make_rsrc((ex ? A.xb1 : A.b1) + eo * sstride, (uint32_t)(sstride * 2));
+  }
+  uint32_t w_off[4], s_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = GLU ? n0 + 32 * wave + 16 * (j >> 1) + c16 : n0 + 64 * wave + 16 * j + c16;
+    const int fr = min(col, N - 1);               // columns past N repeat a valid one (never stored)
+    w_off[j] = (uint32_t)fr * (uint32_t)Kw * 4u + (uint32_t)(g * CB);
+    s_off[j] = ((uint32_t)fr * (uint32_t)G + (uint32_t)((32 * g) / GS)) * 2u;
+  }
+  auto ld_codes = [&](int j, uint32_t soff) -> uint4 {
+    return buf_load16((GLU && (j & 1)) ? rw1 : rw0, w_off[j], soff);
+  };
+  uint4 cw[4][BITS / 4], nw[4][BITS / 4];
+  uint16_t cs[4], cb[4], ns[4], nb[4];
+  auto load_b = [&](int ks, uint4 (&dw)[4][BITS / 4], uint16_t (&ds)[4], uint16_t (&db)[4]) {
+    const uint32_t k0 = (uint32_t)ks * TM_K;
+    const uint32_t soff = k0 * BITS / 8, goff = (k0 / GS) * 2u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int h = 0; h < BITS / 4; ++h) dw[j][h] = ld_codes(j, soff + 16 * h);
+      const bool up = GLU && (j & 1);
+      ds[j] = buf_load2(up ? rs1 : rs0, s_off[j], goff);
+      db[j] = buf_load2(up ? rb1 : rb0, s_off[j], goff);
+    }
+  };
+
+  f32x4_t acc[MI][4];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nK = K / TM_K;
+  load_a(0, 0);
+  load_b(0, cw, cs, cb);
+  for (int ks = 0; ks < nK; ++ks) {
+    const int buf = ks & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's activation rows and codes have landed
+    __syncthreads();                      // ... and every wave's; the other buffer is free
+    if (ks + 1 < nK) {
+      load_a(ks + 1, buf ^ 1);
+      load_b(ks + 1, nw, ns, nb);
+    }
+    f16x2_t s2[4], b2[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s2[j] = f16_splat(bf16_to_f32(cs[j]));
+      b2[j] = f16_splat(bf16_to_f32(cb[j]));
+    }
+    const uint16_t* base = &As[buf][c16 * TM_K];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      f16x8_t bq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t* wv = &cw[j][0].x;
+        bq[j] = BITS == 4 ? deq_operand<4>(wv[s], 0, s2[j], b2[j])
+                          : deq_operand<8>(wv[2 * s], wv[2 * s + 1], s2[j], b2[j]);
+      }
+      const int slot = (4 * g + s) ^ c16;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(base + i * 16 * TM_K + slot * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (ks + 1 < nK) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int h = 0; h < BITS / 4; ++h) cw[j][h] = nw[j][h];
+        cs[j] = ns[j]; cb[j] = nb[j];
+      }
+    }
+  }
+
+  // epilogue: acc[i][j][q] = C[row 16 i + 4 g + q][wave column 16 j + c16]
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = r0 + 16 * i + 4 * g + q;
+      if (r >= r1) continue;
+      uint16_t* orow = A.out + (size_t)r * N;
+      if (GLU) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int f = n0 + 32 * wave + 16 * jj + c16;
+          if (f >= N) continue;
+          const float hv = round_bf16(glu(acc[i][2 * jj][q], acc[i][2 * jj + 1][q]));
+          if (OUT16)
+            orow[(f & ~7) + chunk_pos<BITS>(f & 7)] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+          else
+            orow[f] = f32_to_bf16(hv);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int f = n0 + 64 * wave + 16 * j + c16;
+          if (f < N) orow[f] = f32_to_bf16(acc[i][j][q]);
+        }
+      }
+    }
+}
+
+// bf16 rows -> fp16 rows in the dequantizer's element order (8-element chunks)
+template <int BITS>
+__global__ __launch_bounds__(256) void to_f16_kernel(const uint4* __restrict__ x, int64_t chunks,
+                                                     uint4* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < chunks) out[i] = act_f16<BITS>(x[i]);
+}
+
+template <int BITS, int GS, bool GLU, bool OUT16, int MI>
+static hipError_t launch_mma_t(const TileArgs& a, hipStream_t st) {
+  constexpr int NF = GLU ? TM_C / 2 : TM_C;
+  const int64_t NB = (a.N + NF - 1) / NF;
+  const int64_t nblk = a.grid_tiles * NB;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((tile_mma_kernel<BITS, GS, GLU, OUT16, MI>), dim3((unsigned)nblk), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int BITS, int GS, int MI>
+static hipError_t launch_mma_m(const TileArgs& a, bool glu, bool out16, hipStream_t st) {
+  if (glu) return out16 ? launch_mma_t<BITS, GS, true, true, MI>(a, st) : launch_mma_t<BITS, GS, true, false, MI>(a, st);
+  return launch_mma_t<BITS, GS, false, false, MI>(a, st);
+}
+
+bool tiles_mma_supported(int64_t K, int64_t N, int64_t src_rows) {
+  return K % TM_K == 0 && N > 0 && src_rows * K * 2 < ((int64_t)1 << 32) && N * K < ((int64_t)1 << 31);
+}
+
+hipError_t launch_tiles_mma(const TileArgs& a, int bits, int gs, bool glu, bool out16, int rows,
+                            hipStream_t st) {
+#define MOEGQ_TM(B, G)                                                                              \
+  if (bits == B && gs == G) {                                                                       \
+    if (rows == 128) return launch_mma_m<B, G, 8>(a, glu, out16, st);                               \
+    if (rows == 32) return launch_mma_m<B, G, 2>(a, glu, out16, st);                                \
+    return hipErrorInvalidValue;                                                                    \
+  }
+  MOEGQ_TM(4, 32) MOEGQ_TM(4, 64) MOEGQ_TM(4, 128) MOEGQ_TM(8, 32) MOEGQ_TM(8, 64) MOEGQ_TM(8, 128)
+#undef MOEGQ_TM
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_to_f16(const uint16_t* x, int64_t elems, int bits, uint16_t* out, hipStream_t st) {
+  const int64_t chunks = elems / 8;
+  if (chunks <= 0) return hipSuccess;
+  const unsigned nb = (unsigned)((chunks + 255) / 256);
+  if (bits == 4)
+    hipLaunchKernelGGL(to_f16_kernel<4>, dim3(nb), dim3(256), 0, st, (const uint4*)x, chunks, (uint4*)out);
+  else
+    hipLaunchKernelGGL(to_f16_kernel<8>, dim3(nb), dim3(256), 0, st, (const uint4*)x, chunks, (uint4*)out);
+  return hipGetLastError();
+}
+
+}  // namespace moegq

@@ -95,9 +95,19 @@ def test_other_entry_points_validate(L):
     # sort / schedule
     assert L.moegq_sort_pairs(p, 2, 4, 8, 16, None, None, None, p, p, p, None, 0, None) == -5  # float idx
     assert L.moegq_sort_pairs(p, 4, 4, 8, 2000, None, None, None, p, p, p, None, 0, None) == -6
+    assert L.moegq_sort_pairs(p, 4, 4, 8, 16, None, None, None, p, p, p, None, 0, None) == -7  # no workspace
+    assert L.moegq_sort_pairs(None, 4, 0, 8, 16, None, None, None, p, p, p, None, 0, None) == -1
     assert L.moegq_schedule_tiles(p, 4, 33, 16, 0, p, 3, p, None) == -7            # capacity
     assert L.moegq_schedule_tiles(p, 4, 33, 24, 0, p, 100, p, None) == -4          # bm
     assert L.moegq_selfcheck(None, 0, None) == -7
+    # whole prefill layer
+    lay = lambda T, H, I, ws, wsb, sh=p: L.moegq_moe_prefill(p, T, H, I, 8, p, 2, p, *[p] * 9, sh, *[p] * 11,
+                                                               64, 4, p, ws, wsb, None)
+    assert lay(64, 256, 128, None, 0) == -7                                         # no workspace
+    assert lay(64, 256, 96, None, 0) == -4                                          # I % 64
+    assert lay(64, 320, 128, p, 1 << 30) == -6                                      # H % 128
+    assert lay(0, 256, 128, None, 0) == 0
+    assert L.moegq_moe_combine_gated(p, None, p, None, p, 4, 8, 16, p, None) == -1  # shared required
 
 
 def test_workspace_sizes(L):
@@ -107,6 +117,11 @@ def test_workspace_sizes(L):
     assert big >= 16384 * 512 * 2 + 3 * 16384 * 4
     assert m.workspace_bytes(m.OP_SWITCH_GLU_SORTED, 16384, 256, 512, 0) == big
     assert m.workspace_bytes(99, 1, 1, 1, 0) == 0
+    assert m.workspace_bytes(m.OP_SORT_PAIRS, 16384, 256, 0, 0) >= 16 * 256 * 4
+    lay = m.moe_prefill_workspace_bytes(2048, 8, 256, 2048, 512, True)
+    # h and y for the routed and shared rows, the fp16 activations
+    assert lay >= (16384 + 2048) * (512 + 2048) * 2 + 2048 * 2048 * 2
+    assert m.moe_prefill_workspace_bytes(2048, 8, 256, 2048, 512, False) < lay
     assert m.switch_glu_mode(1, 8, 288) == m.MODE_DECODE
     assert m.switch_glu_mode(2048, 8, 256) == m.MODE_SORTED
 

@@ -151,3 +151,49 @@ def test_auto_mode_and_identity_inv(mg):
     y, inv, mode = mg.switch_glu(bf(x), i32(idx), *ex, group_size=sh.gs, bits=sh.bits, inv=inv)
     assert mode == mg.MODE_DECODE
     assert host_i32(inv).tolist() == list(range(8))
+
+
+@pytest.mark.parametrize("T", [128, 331])
+@pytest.mark.parametrize("with_shared", [True, False])
+def test_moe_prefill_layer(mg, T, with_shared):
+    """Whole layer in one entry point (sort, routed and shared experts in the
+    same tile launches, gated one-pass combine) against the oracle's layer."""
+    sh, idx, scores, x, ex = _prefill_case(T, sub=2)
+    shp = synth.shared_params(3, sh.H, sh.shared_I, sh.gs, sh.bits) if with_shared else None
+    want, _ = oracle.moe_prefill_layer(x, idx, scores, ex, shp, gs=sh.gs, bits=sh.bits)
+    got = mg.moe_prefill(bf(x), i32(idx), bf(scores), *[triple(m) for m in ex],
+                         shared=None if shp is None else tuple(triple(m) for m in shp),
+                         group_size=sh.gs, bits=sh.bits)
+    assert_parity(host_bf(got), want, name=f"layer T={T} shared={with_shared}")
+
+
+def test_moe_prefill_layer_2048_sampled(mg):
+    """The 2048-row layer (hidden 2048, 256 experts, top-8, inter 512, shared
+    expert) on the GPU; the oracle recomputes 48 sampled tokens (a token's
+    output depends only on its own row, experts and scores)."""
+    sh = synth.PREFILL
+    T = 2048
+    idx, scores = synth.zipf_routing(3, T, sh.E, sh.top_k)
+    x = synth.activations(3, T, sh.H)
+    ex = synth.expert_set(3, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode="words", experts=np.unique(idx))
+    shp = synth.shared_params(3, sh.H, sh.shared_I, sh.gs, sh.bits)
+    got = host_bf(mg.moe_prefill(bf(x), i32(idx), bf(scores), *[triple(m) for m in ex],
+                                 shared=tuple(triple(m) for m in shp), group_size=sh.gs, bits=sh.bits))
+    sub = np.sort(np.random.default_rng(11).choice(T, 48, replace=False))
+    want, _ = oracle.moe_prefill_layer(x[sub], idx[sub], scores[sub], ex, shp, gs=sh.gs, bits=sh.bits)
+    assert_parity(got[sub], want, name="layer 2048 sampled")
+
+
+def test_combine_gated_bitwise(mg):
+    """The gate inside the combine equals sigmoid_gate + combine bit for bit."""
+    g = np.random.default_rng(12)
+    T, top_k, H = 331, 8, 2048
+    P = T * top_k
+    y = synth.to_bf16(g.standard_normal((P, H)) * 3)
+    inv = g.permutation(P).astype(np.int32)
+    sc = synth.to_bf16(g.random((T, top_k)))
+    s = synth.to_bf16(g.standard_normal((T, H)))
+    z = synth.to_bf16(g.standard_normal(T) * 3)
+    ref = mg.moe_combine(bf(y), i32(inv), bf(sc), mg.sigmoid_gate(bf(s), bf(z)))
+    got = mg.moe_combine_gated(bf(y), i32(inv), bf(sc), bf(s), bf(z))
+    assert np.array_equal(host_bf(got), host_bf(ref))

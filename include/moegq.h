@@ -194,7 +194,8 @@ int moegq_switch_glu_mode(int64_t T, int64_t top_k, int64_t E);
  * as moegq_switch_glu; shared matrices with the routed matrices' shapes minus
  * the expert axis (the shared intermediate size must equal I), gate row
  * [1, H*bits/32] words + [1, H/gs] scales/biases.  shg_w == NULL: no shared
- * expert (every shared pointer ignored).  H and I must be multiples of 128.
+ * expert (every shared pointer ignored).  H and I must be multiples of 128
+ * and of 8 * group_size (else MOEGQ_ERR_UNSUPPORTED).
  * out [T, H] bf16.  workspace: moegq_moe_prefill_workspace_bytes(...) bytes.
  */
 int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,

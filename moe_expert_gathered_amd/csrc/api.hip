@@ -477,7 +477,7 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
   ds_.tiles = ws.small_tiles; ds_.n_tiles = ws.n_tiles + 1; ds_.bm = kSmallMax; ds_.tile_mode = 0;
   ds_.grid_tiles = small_cap(P, E);
   g.tile_mode = 0; d.tile_mode = 0;
-  if (tiles_mma_supported(H, I, T) && tiles_mma_supported(I, H, P)) {
+  if (tiles_mma_supported(H, I, T, group_size) && tiles_mma_supported(I, H, P, group_size)) {
     // fp16 copy of x for the matrix cores, parked in y (y is written only by the down pass);
     // h is written and read in the same fp16 chunk order
     if (launch_to_f16((const uint16_t*)x, T * H, bits, (uint16_t*)y, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
@@ -527,7 +527,8 @@ int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
     return MOEGQ_ERR_ALIGN;
   const int64_t P = T * top_k;
   const int64_t extra = shared ? T : 0;
-  if (!tiles_mma_supported(H, I, T) || !tiles_mma_supported(I, H, P + extra)) return MOEGQ_ERR_UNSUPPORTED;
+  if (!tiles_mma_supported(H, I, T, group_size) || !tiles_mma_supported(I, H, P + extra, group_size))
+    return MOEGQ_ERR_UNSUPPORTED;
   const SortedWs ws = sorted_layout((char*)workspace, P, E, I, 0, extra, T, H, true);
   if (!workspace || workspace_bytes < ws.bytes) return MOEGQ_ERR_WORKSPACE;
   hipStream_t s = S(stream);

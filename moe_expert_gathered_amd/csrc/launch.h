@@ -86,7 +86,7 @@ hipError_t launch_tiles_small(const TileArgs& a, int bits, int gs, bool glu, hip
 // 128-row tiles with register-dequantized weights (tile_mode 0: table, 2: dense rows).  a.x holds
 // fp16 rows in the dequantizer's chunk order (launch_to_f16), gathered through a.lhs (or row r);
 // out16: the GLU output is written the same way (fp16, chunk order) for a following down pass
-bool tiles_mma_supported(int64_t K, int64_t N, int64_t src_rows);
+bool tiles_mma_supported(int64_t K, int64_t N, int64_t src_rows, int gs);
 // rows: 128 (tile table of up to 128-row tiles, or dense rows) or 32 (tiles of at most 32 rows)
 hipError_t launch_tiles_mma(const TileArgs& a, int bits, int gs, bool glu, bool out16, int rows,
                             hipStream_t st);

@@ -23,9 +23,8 @@
 //    the element order the dequantizer produces inside each 8-element chunk
 //    (4-bit: q0 q2 q4 q6 q1 q3 q5 q7; 8-bit: natural).  They travel from HBM
 //    to LDS with buffer loads that write LDS directly (no register staging),
-//    into a double buffer (2 x 4 KiB per 16 rows).  Row r's 16-byte chunk c sits in slot
-//    c ^ (r % 16) of the row, so the 16 rows a ds_read_b128 touches fall in
-//    distinct banks.
+//    into a double buffer (2 x 4 KiB per 16 rows), each row's 16-byte chunks
+//    permuted (lds_swz) so that operand reads are free of bank conflicts.
 //  * GLU: a wave's 4 column blocks are (gate f, up f, gate f+16, up f+16), so
 //    silu(g) * u is applied in registers in the epilogue.
 //  * One barrier per K step: the next step's activations and codes are in
@@ -43,6 +42,12 @@ namespace moegq {
 
 constexpr int TM_C = 256;   // MFMA columns per tile
 constexpr int TM_K = 128;   // K per step
+
+// LDS slot permutation of a 256-byte activation row: row r keeps its 16-byte
+// chunk c in slot c ^ lds_swz(r).  The 16 rows that one ds_read_b128 of an
+// MFMA operand touches then spread over all banks (measured conflict-free on
+// gfx950; a plain c ^ r still collides across lane groups).
+MOEGQ_DEV int lds_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 // position of element k (0..7) of a chunk in the dequantizer's order
 template <int BITS>
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
     const int r = 4 * (MI * wave + v) + g;
     const int rr = min(r0 + r, r1 - 1);          // rows past the tile repeat a valid row (never stored)
     const int src = A.lhs ? A.lhs[rr] : rr;
-    const int chunk = c16 ^ (r & 15);
+    const int chunk = c16 ^ lds_swz(r);
     a_off[v] = (uint32_t)src * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
   }
   auto load_a = [&](int ks, int buf) {
@@ -135,30 +140,55 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
     rs1 = make_rsrc((ex ? A.xs1 : A.s1) + eo * sstride, (uint32_t)(sstride * 2));
     rb1 = make_rsrc((ex ? A.xb1 : A.b1) + eo * sstride, (uint32_t)(sstride * 2));
   }
-  uint32_t w_off[4], s_off[4];
+  uint32_t w_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int col = GLU ? n0 + 32 * wave + 16 * (j >> 1) + c16 : n0 + 64 * wave + 16 * j + c16;
     const int fr = min(col, N - 1);               // columns past N repeat a valid one (never stored)
     w_off[j] = (uint32_t)fr * (uint32_t)Kw * 4u + (uint32_t)(g * CB);
-    s_off[j] = ((uint32_t)fr * (uint32_t)G + (uint32_t)((32 * g) / GS)) * 2u;
   }
+  // Scales and biases come in windows of 8 groups: lane l of the wave fetches
+  // the window of the wave's column block l / 16, column l % 16, with one
+  // 16-byte load per array (instead of one 2-byte load per column block, array
+  // and K step); each step's lanes then pick their group with ds_bpermute.
+  // Window w covers groups 8 w .. 8 w + 7, i.e. K steps GS / 16 * w ..
+  constexpr int WSTEPS = GS / 16;
+  const int lj = lane >> 4;
+  const int lcol = GLU ? n0 + 32 * wave + 16 * (lj >> 1) + c16 : n0 + 64 * wave + 16 * lj + c16;
+  const uint32_t sw_off = (uint32_t)min(lcol, N - 1) * (uint32_t)G * 2u;
+  const bool lup = GLU && (lj & 1);
+  auto load_win = [&](int w, uint4& ws, uint4& wb) {
+    const uint32_t soff = (uint32_t)w * 16u;
+    ws = buf_load16(rs0, sw_off, soff);
+    wb = buf_load16(rb0, sw_off, soff);
+    if (GLU) {
+      const uint4 us = buf_load16(rs1, sw_off, soff), ub = buf_load16(rb1, sw_off, soff);
+      if (lup) { ws = us; wb = ub; }
+    }
+  };
+  // group of (lane group g, step ks) inside its window: e = (8 ks / WSTEPS + 32 g / GS) % 8;
+  // the dword holding it is the same for every lane except at GS = 32
+  auto sel4 = [](const uint4& v, int d) -> uint32_t {
+    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+  };
+  auto pick = [&](const uint4& win, int ks, int j) -> float {
+    const int src = (16 * j + c16) << 2;
+    if (GS == 32) {          // e = 4 (ks % 2) + g: dword 2 (ks % 2) + g / 2, half g % 2
+      const int d0 = 2 * (ks & 1);
+      const uint32_t lo = __builtin_amdgcn_ds_bpermute(src, (int)sel4(win, d0));
+      const uint32_t hi = __builtin_amdgcn_ds_bpermute(src, (int)sel4(win, d0 + 1));
+      const uint32_t d = (g & 2) ? hi : lo;
+      return (g & 1) ? bf16_hi(d) : bf16_lo(d);
+    } else if (GS == 64) {   // e = 2 (ks % 4) + g / 2: dword ks % 4, half g / 2
+      const uint32_t d = __builtin_amdgcn_ds_bpermute(src, (int)sel4(win, ks & 3));
+      return (g & 2) ? bf16_hi(d) : bf16_lo(d);
+    } else {                 // e = ks % 8: dword (ks % 8) / 2, half ks % 2
+      const uint32_t d = __builtin_amdgcn_ds_bpermute(src, (int)sel4(win, (ks >> 1) & 3));
+      return (ks & 1) ? bf16_hi(d) : bf16_lo(d);
+    }
+  };
   auto ld_codes = [&](int j, uint32_t soff) -> uint4 {
     return buf_load16((GLU && (j & 1)) ? rw1 : rw0, w_off[j], soff);
-  };
-  uint4 cw[4][BITS / 4], nw[4][BITS / 4];
-  uint16_t cs[4], cb[4], ns[4], nb[4];
-  auto load_b = [&](int ks, uint4 (&dw)[4][BITS / 4], uint16_t (&ds)[4], uint16_t (&db)[4]) {
-    const uint32_t k0 = (uint32_t)ks * TM_K;
-    const uint32_t soff = k0 * BITS / 8, goff = (k0 / GS) * 2u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int h = 0; h < BITS / 4; ++h) dw[j][h] = ld_codes(j, soff + 16 * h);
-      const bool up = GLU && (j & 1);
-      ds[j] = buf_load2(up ? rs1 : rs0, s_off[j], goff);
-      db[j] = buf_load2(up ? rb1 : rb0, s_off[j], goff);
-    }
   };
 
   f32x4_t acc[MI][4];
@@ -168,25 +198,47 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nK = K / TM_K;
+  uint4 cw[4][BITS / 4], nw[4][BITS / 4];
+  uint4 win_s, win_b, nwin_s, nwin_b;
   load_a(0, 0);
-  load_b(0, cw, cs, cb);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int h = 0; h < BITS / 4; ++h) cw[j][h] = ld_codes(j, 16 * h);
+  load_win(0, win_s, win_b);
+  nwin_s = win_s; nwin_b = win_b;
   for (int ks = 0; ks < nK; ++ks) {
     const int buf = ks & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's activation rows and codes have landed
+    const bool more = ks + 1 < nK;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's activation rows, codes and scales have landed
     __syncthreads();                      // ... and every wave's; the other buffer is free
-    if (ks + 1 < nK) {
-      load_a(ks + 1, buf ^ 1);
-      load_b(ks + 1, nw, ns, nb);
+    if (ks % WSTEPS == 0) {
+      win_s = nwin_s; win_b = nwin_b;
+      if ((ks + WSTEPS) < nK) load_win(ks / WSTEPS + 1, nwin_s, nwin_b);
     }
     f16x2_t s2[4], b2[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      s2[j] = f16_splat(bf16_to_f32(cs[j]));
-      b2[j] = f16_splat(bf16_to_f32(cb[j]));
+      s2[j] = f16_splat(pick(win_s, ks, j));
+      b2[j] = f16_splat(pick(win_b, ks, j));
     }
     const uint16_t* base = &As[buf][c16 * TM_K];
+    const uint32_t soff_next = (uint32_t)(ks + 1) * TM_K * BITS / 8;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      // this sub-step's share of the next step's loads (spread so that the
+      // address unit never holds up a whole step's MFMAs)
+      if (more) {
+        constexpr int AV = (MI + 3) / 4;
+#pragma unroll
+        for (int v = s * AV; v < (s + 1) * AV && v < MI; ++v) {
+          uint16_t* dst = &As[buf ^ 1][4 * (MI * wave + v) * TM_K];
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, a_off[v],
+                                                   (uint32_t)(ks + 1) * TM_K * 2u, 0, 0);
+        }
+#pragma unroll
+        for (int h = 0; h < BITS / 4; ++h) nw[s][h] = ld_codes(s, soff_next + 16 * h);
+      }
       f16x8_t bq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -194,21 +246,20 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
         bq[j] = BITS == 4 ? deq_operand<4>(wv[s], 0, s2[j], b2[j])
                           : deq_operand<8>(wv[2 * s], wv[2 * s + 1], s2[j], b2[j]);
       }
-      const int slot = (4 * g + s) ^ c16;
+      const int slot = (4 * g + s) ^ lds_swz(c16);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const f16x8_t a = *reinterpret_cast<const f16x8_t*>(base + i * 16 * TM_K + slot * 8);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[j], acc[i][j], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (ks + 1 < nK) {
+    if (more) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int h = 0; h < BITS / 4; ++h) cw[j][h] = nw[j][h];
-        cs[j] = ns[j]; cb[j] = nb[j];
-      }
     }
   }
 
@@ -266,8 +317,9 @@ static hipError_t launch_mma_m(const TileArgs& a, bool glu, bool out16, hipStrea
   return launch_mma_t<BITS, GS, false, false, MI>(a, st);
 }
 
-bool tiles_mma_supported(int64_t K, int64_t N, int64_t src_rows) {
-  return K % TM_K == 0 && N > 0 && src_rows * K * 2 < ((int64_t)1 << 32) && N * K < ((int64_t)1 << 31);
+bool tiles_mma_supported(int64_t K, int64_t N, int64_t src_rows, int gs) {
+  return K % TM_K == 0 && K % (8 * gs) == 0 && N > 0 && src_rows * K * 2 < ((int64_t)1 << 32) &&
+         N * K < ((int64_t)1 << 31);
 }
 
 hipError_t launch_tiles_mma(const TileArgs& a, int bits, int gs, bool glu, bool out16, int rows,

@@ -103,9 +103,10 @@ def test_other_entry_points_validate(L):
     # whole prefill layer
     lay = lambda T, H, I, ws, wsb, sh=p: L.moegq_moe_prefill(p, T, H, I, 8, p, 2, p, *[p] * 9, sh, *[p] * 11,
                                                                64, 4, p, ws, wsb, None)
-    assert lay(64, 256, 128, None, 0) == -7                                         # no workspace
+    assert lay(64, 1024, 512, None, 0) == -7                                        # no workspace
     assert lay(64, 256, 96, None, 0) == -4                                          # I % 64
-    assert lay(64, 320, 128, p, 1 << 30) == -6                                      # H % 128
+    assert lay(64, 320, 512, p, 1 << 30) == -6                                      # H % 128
+    assert lay(64, 1024, 128, p, 1 << 30) == -6                                     # I % (8 * 64)
     assert lay(0, 256, 128, None, 0) == 0
     assert L.moegq_moe_combine_gated(p, None, p, None, p, 4, 8, 16, p, None) == -1  # shared required
 

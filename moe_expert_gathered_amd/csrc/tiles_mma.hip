@@ -27,6 +27,9 @@
 //    permuted (lds_swz) so that operand reads are free of bank conflicts.
 //  * GLU: a wave's 4 column blocks are (gate f, up f, gate f+16, up f+16), so
 //    silu(g) * u is applied in registers in the epilogue.
+//  * The weights are the MFMA's first operand: each lane ends with four
+//    consecutive output features of one row and writes them as one 8-byte
+//    store.
 //  * One barrier per K step: the next step's activations and codes are in
 //    flight during the current step's MFMAs.
 //  * Workgroups are dealt to the 8 XCDs round-robin by the hardware; the
@@ -35,6 +38,8 @@
 //    consecutive tiles of one expert, then share that XCD's L2.
 //  * An optional extra expert (index E, its own weight pointers) carries the
 //    shared expert through the same launch.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -48,10 +53,6 @@ constexpr int TM_K = 128;   // K per step
 // MFMA operand touches then spread over all banks (measured conflict-free on
 // gfx950; a plain c ^ r still collides across lane groups).
 MOEGQ_DEV int lds_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
-// position of element k (0..7) of a chunk in the dequantizer's order
-template <int BITS>
-MOEGQ_DEV int chunk_pos(int k) { return BITS == 4 ? ((k >> 1) | ((k & 1) << 2)) : k; }
 
 // eight codes (one 4-bit word, or two 8-bit words) -> one fp16 MFMA operand
 template <int BITS>
@@ -73,7 +74,9 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
   constexpr int NF = GLU ? TM_C / 2 : TM_C;      // output features per tile
   constexpr int CB = 4 * BITS;                    // code bytes per lane per K step (32 codes)
   constexpr int TM_M = 16 * MI;                   // rows per tile
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][16 * MI * TM_K];
+  constexpr int PD = MI >= 8 ? 1 : 3;             // K steps of prefetch (activations and codes)
+  constexpr int RING = PD + 1;                     // LDS and register ring stages
+  __shared__ __attribute__((aligned(16))) uint16_t As[RING][16 * MI * TM_K];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -117,16 +120,6 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
     const int chunk = c16 ^ lds_swz(r);
     a_off[v] = (uint32_t)src * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
   }
-  auto load_a = [&](int ks, int buf) {
-    const uint32_t soff = (uint32_t)ks * TM_K * 2u;
-#pragma unroll
-    for (int v = 0; v < MI; ++v) {
-      uint16_t* dst = &As[buf][4 * (MI * wave + v) * TM_K];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, a_off[v], soff,
-                                               0, 0);
-    }
-  };
-
   // ---- code / scale loads: column block j of this wave
   const size_t wstride = (size_t)N * Kw, sstride = (size_t)N * G;
   const bool ex = e >= A.E;          // the extra (shared) expert
@@ -140,10 +133,18 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
     rs1 = make_rsrc((ex ? A.xs1 : A.s1) + eo * sstride, (uint32_t)(sstride * 2));
     rb1 = make_rsrc((ex ? A.xb1 : A.b1) + eo * sstride, (uint32_t)(sstride * 2));
   }
+  // MFMA column n of block j is output feature block_base(j) + col_perm(n).
+  // The MFMA runs with the weights as the first operand, so lane (g, c16) ends
+  // up with outputs n = 4 g .. 4 g + 3 of activation row c16; col_perm makes
+  // those four land next to each other in memory (one 8-byte store): the
+  // identity, except for the fp16 intermediate of 4-bit codes, whose chunk
+  // order (q0 q2 q4 q6 q1 q3 q5 q7) is undone by taking features 0 2 4 6 1 3 5 7.
+  auto block_base = [&](int j) { return GLU ? n0 + 32 * wave + 16 * (j >> 1) : n0 + 64 * wave + 16 * j; };
+  auto col_perm = [](int n) { return (OUT16 && BITS == 4) ? 8 * (n >> 3) + 2 * (n & 3) + ((n >> 2) & 1) : n; };
   uint32_t w_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int col = GLU ? n0 + 32 * wave + 16 * (j >> 1) + c16 : n0 + 64 * wave + 16 * j + c16;
+    const int col = block_base(j) + col_perm(c16);
     const int fr = min(col, N - 1);               // columns past N repeat a valid one (never stored)
     w_off[j] = (uint32_t)fr * (uint32_t)Kw * 4u + (uint32_t)(g * CB);
   }
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
   // Window w covers groups 8 w .. 8 w + 7, i.e. K steps GS / 16 * w ..
   constexpr int WSTEPS = GS / 16;
   const int lj = lane >> 4;
-  const int lcol = GLU ? n0 + 32 * wave + 16 * (lj >> 1) + c16 : n0 + 64 * wave + 16 * lj + c16;
+  const int lcol = block_base(lj) + col_perm(c16);
   const uint32_t sw_off = (uint32_t)min(lcol, N - 1) * (uint32_t)G * 2u;
   const bool lup = GLU && (lj & 1);
   auto load_win = [&](int w, uint4& ws, uint4& wb) {
@@ -198,20 +199,31 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nK = K / TM_K;
-  uint4 cw[4][BITS / 4], nw[4][BITS / 4];
+  // ring of code registers: stage t % RING holds step t's codes (fixed extents:
+  // the unused stages and halves are never touched and cost no registers)
+  uint4 cw[4][4][2];
   uint4 win_s, win_b, nwin_s, nwin_b;
-  load_a(0, 0);
+  constexpr int LPS = MI + 4 * (BITS / 4);        // loads per step: activations + codes
+  auto issue = [&](int t, int stg, int part) {    // part p of step t's loads (p = 0..3), into stage stg
+    if (t >= nK) return;
+    constexpr int AV = (MI + 3) / 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int v = part * AV; v < (part + 1) * AV && v < MI; ++v) {
+      uint16_t* dst = &As[stg][4 * (MI * wave + v) * TM_K];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, a_off[v],
+                                               (uint32_t)t * TM_K * 2u, 0, 0);
+    }
+    const uint32_t soff = (uint32_t)t * TM_K * BITS / 8;
 #pragma unroll
-    for (int h = 0; h < BITS / 4; ++h) cw[j][h] = ld_codes(j, 16 * h);
-  load_win(0, win_s, win_b);
-  nwin_s = win_s; nwin_b = win_b;
-  for (int ks = 0; ks < nK; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < nK;
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's activation rows, codes and scales have landed
-    __syncthreads();                      // ... and every wave's; the other buffer is free
+    for (int h = 0; h < BITS / 4; ++h) cw[stg][part][h] = ld_codes(part, soff + 16 * h);
+  };
+  auto step = [&](int ks, auto stage) {
+    constexpr int sl = decltype(stage)::value;
+    constexpr int fut = (sl + PD) % RING;
+    // step ks's loads were issued PD steps ago; at most the later PD - 1 steps' loads may still fly
+    constexpr int VM = (PD - 1) * LPS;
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (VM & 15) | ((VM >> 4) << 14));
+    __syncthreads();                      // every wave's rows landed; stage fut (step ks - 1) is free
     if (ks % WSTEPS == 0) {
       win_s = nwin_s; win_b = nwin_b;
       if ((ks + WSTEPS) < nK) load_win(ks / WSTEPS + 1, nwin_s, nwin_b);
@@ -222,27 +234,14 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
       s2[j] = f16_splat(pick(win_s, ks, j));
       b2[j] = f16_splat(pick(win_b, ks, j));
     }
-    const uint16_t* base = &As[buf][c16 * TM_K];
-    const uint32_t soff_next = (uint32_t)(ks + 1) * TM_K * BITS / 8;
+    const uint16_t* base = &As[sl][c16 * TM_K];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      // this sub-step's share of the next step's loads (spread so that the
-      // address unit never holds up a whole step's MFMAs)
-      if (more) {
-        constexpr int AV = (MI + 3) / 4;
-#pragma unroll
-        for (int v = s * AV; v < (s + 1) * AV && v < MI; ++v) {
-          uint16_t* dst = &As[buf ^ 1][4 * (MI * wave + v) * TM_K];
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, a_off[v],
-                                                   (uint32_t)(ks + 1) * TM_K * 2u, 0, 0);
-        }
-#pragma unroll
-        for (int h = 0; h < BITS / 4; ++h) nw[s][h] = ld_codes(s, soff_next + 16 * h);
-      }
+      issue(ks + PD, fut, s);             // a quarter of a later step's loads per sub-step
       f16x8_t bq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t* wv = &cw[j][0].x;
+        const uint32_t* wv = &cw[sl][j][0].x;
         bq[j] = BITS == 4 ? deq_operand<4>(wv[s], 0, s2[j], b2[j])
                           : deq_operand<8>(wv[2 * s], wv[2 * s + 1], s2[j], b2[j]);
       }
@@ -251,45 +250,53 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
       for (int i = 0; i < MI; ++i) {
         const f16x8_t a = *reinterpret_cast<const f16x8_t*>(base + i * 16 * TM_K + slot * 8);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bq[j], a, acc[i][j], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
+  };
+  load_win(0, win_s, win_b);
+  nwin_s = win_s; nwin_b = win_b;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+  for (int t = 0; t < PD; ++t)
 #pragma unroll
-        for (int h = 0; h < BITS / 4; ++h) cw[j][h] = nw[j][h];
-    }
+    for (int part = 0; part < 4; ++part) issue(t, t, part);
+  for (int ks = 0; ks < nK; ks += RING) {
+    step(ks, std::integral_constant<int, 0>{});
+    if (ks + 1 < nK) step(ks + 1, std::integral_constant<int, 1 % RING>{});
+    if (RING > 2 && ks + 2 < nK) step(ks + 2, std::integral_constant<int, 2 % RING>{});
+    if (RING > 3 && ks + 3 < nK) step(ks + 3, std::integral_constant<int, 3 % RING>{});
   }
 
-  // epilogue: acc[i][j][q] = C[row 16 i + 4 g + q][wave column 16 j + c16]
+  // epilogue: acc[i][j][q] = output (row 16 i + c16, memory column block_base(j) + 4 g + q)
+  const bool vec = (N & 3) == 0;
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < MI; ++i) {
+    const int r = r0 + 16 * i + c16;
+    if (r >= r1) continue;
+    uint16_t* orow = A.out + (size_t)r * N;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = r0 + 16 * i + 4 * g + q;
-      if (r >= r1) continue;
-      uint16_t* orow = A.out + (size_t)r * N;
-      if (GLU) {
+    for (int j = 0; j < (GLU ? 2 : 4); ++j) {
+      const int f = (GLU ? block_base(2 * j) : block_base(j)) + 4 * g;
+      uint16_t o[4];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int f = n0 + 32 * wave + 16 * jj + c16;
-          if (f >= N) continue;
-          const float hv = round_bf16(glu(acc[i][2 * jj][q], acc[i][2 * jj + 1][q]));
-          if (OUT16)
-            orow[(f & ~7) + chunk_pos<BITS>(f & 7)] = __builtin_bit_cast(uint16_t, (_Float16)hv);
-          else
-            orow[f] = f32_to_bf16(hv);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int f = n0 + 64 * wave + 16 * j + c16;
-          if (f < N) orow[f] = f32_to_bf16(acc[i][j][q]);
+      for (int q = 0; q < 4; ++q) {
+        if (GLU) {
+          const float hv = round_bf16(glu(acc[i][2 * j][q], acc[i][2 * j + 1][q]));
+          o[q] = OUT16 ? __builtin_bit_cast(uint16_t, (_Float16)hv) : f32_to_bf16(hv);
+        } else {
+          o[q] = f32_to_bf16(acc[i][j][q]);
         }
       }
+      if (vec && f + 3 < N) {
+        *reinterpret_cast<uint2*>(orow + f) = make_uint2(o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16));
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (f + q < N) orow[f + q] = o[q];
+      }
     }
+  }
 }
 
 // bf16 rows -> fp16 rows in the dequantizer's element order (8-element chunks)

@@ -297,6 +297,55 @@ def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=5, warmup=2,
     return res
 
 
+# ----------------------------------------------------------------------------- counter calibration
+CALIB_BYTES = 256 << 20
+
+
+def calib_leg(torch, reps=3):
+    """A plain device copy of CALIB_BYTES (fp32 tensors): its FETCH_SIZE and
+    WRITE_SIZE counter readings against the known bytes give the scale that
+    turns those counters into HBM bytes."""
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes": CALIB_BYTES, "reps": reps}
+
+
+# counter-derived HBM traffic of the headline kernel, measured on the source
+# files listed in the summary; reported only while those files are unchanged
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "qmv_glu_decode_m1_chain42_traffic.txt")
+
+
+def source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic():
+    """Bytes per launch from the committed counter summary, or None when it is
+    missing or the kernel's sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        files = kv["sources"].split()
+        if source_digest(files) != kv["sources_sha256"]:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError, OSError):
+        return None
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(torch, synth, n_layers=2, cfg=1):
     """The oracle (numpy) on a bounded sample of the headline workload: n_layers
@@ -360,6 +409,9 @@ def main():
     if "dense" in legs:
         log("dense chain")
         extra["dense_chain"] = dense_leg(torch, m, synth)
+    if "calib" in legs:
+        log("counter calibration copy")
+        extra["calib"] = calib_leg(torch)
     cpu = None
     if "cpu" in legs:
         log("cpu baseline (oracle)")
@@ -375,7 +427,7 @@ def main():
                    "inter": 2048, "experts": 288, "top_k": 8, "bits": 4, "group_size": 64, "tokens": 1,
                    "index_sets": 42},
         "roofline": {"bound": "hbm", "kernel": "qmv_kernel<4,64,glu,2,2> (gathered gate+up, SiLU)", "achieved": round(ach, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": counted_traffic(),
                      "bytes_per_launch": head["gate_up_bytes"], "avg_launch_us": round(k1_us, 3)},
         "cpu_baseline": cpu,
         "legs": extra,

@@ -482,11 +482,14 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
     // h is written and read in the same fp16 chunk order
     if (launch_to_f16((const uint16_t*)x, T * H, bits, (uint16_t*)y, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
     g.x = gs_.x = (const uint16_t*)y;
+    if (hybrid) {
+      g.tiles2 = d.tiles2 = ws.small_tiles; g.n_tiles2 = d.n_tiles2 = ws.n_tiles + 1;
+      g.grid_tiles2 = d.grid_tiles2 = small_cap(P, E);
+      if (launch_tiles_mma_dual(g, bits, group_size, true, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+      return status_of(launch_tiles_mma_dual(d, bits, group_size, false, false, s));
+    }
     if (launch_tiles_mma(g, bits, group_size, true, true, 128, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-    if (hybrid && launch_tiles_mma(gs_, bits, group_size, true, true, 32, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-    if (launch_tiles_mma(d, bits, group_size, false, false, 128, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-    if (hybrid && launch_tiles_mma(ds_, bits, group_size, false, false, 32, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-    return MOEGQ_OK;
+    return status_of(launch_tiles_mma(d, bits, group_size, false, false, 128, s));
   }
   if (launch_tiles_big(g, bits, group_size, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   if (hybrid && launch_tiles_small(gs_, bits, group_size, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
@@ -566,15 +569,11 @@ int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
   d.xw0 = (const uint32_t*)shd_w; d.xs0 = (const uint16_t*)shd_s; d.xb0 = (const uint16_t*)shd_b;
   d.xw1 = nullptr; d.xs1 = nullptr; d.xb1 = nullptr;
   d.N = (int)H; d.K = (int)I; d.out = ws.y;
-  TileArgs gs_ = g, ds_ = d;
-  gs_.tiles = ds_.tiles = ws.small_tiles;
-  gs_.n_tiles = ds_.n_tiles = ws.n_tiles + 1;
-  gs_.bm = ds_.bm = kSmallMax;
-  gs_.grid_tiles = ds_.grid_tiles = small_cap(P, E);
-  if (launch_tiles_mma(g, bits, group_size, true, true, 128, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-  if (launch_tiles_mma(gs_, bits, group_size, true, true, 32, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-  if (launch_tiles_mma(d, bits, group_size, false, false, 128, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-  if (launch_tiles_mma(ds_, bits, group_size, false, false, 32, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  // 128-row tiles (hot experts, shared expert) and 32-row tiles (tail experts) in one launch per pass
+  g.tiles2 = d.tiles2 = ws.small_tiles; g.n_tiles2 = d.n_tiles2 = ws.n_tiles + 1;
+  g.grid_tiles2 = d.grid_tiles2 = small_cap(P, E);
+  if (launch_tiles_mma_dual(g, bits, group_size, true, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (launch_tiles_mma_dual(d, bits, group_size, false, false, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   // out[t] = bf16(bf16(sum_k bf16(y[inv] * score)) + bf16(sigmoid(z[t]) * y[P + t]))
   return status_of(launch_combine(ws.y, inv, (const uint16_t*)scores, shared ? ws.y + P * H : nullptr,
                                   shared ? ws.z : nullptr, T, (int)top_k, H, (uint16_t*)out, s));

@@ -77,6 +77,8 @@ struct TileArgs {
   uint16_t* out;            // [P, N]
   int bm; int tile_mode;    // 0 scheduled table, 1 naive (loop over experts), 2 dense (expert 0)
   int64_t grid_tiles;       // upper bound of the tile count (grid size)
+  // second tile table (tiles_mma dual launch: tiles of at most 32 rows)
+  const int32_t* tiles2; const int32_t* n_tiles2; int64_t grid_tiles2;
 };
 hipError_t launch_tiles(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st);
 // 128-row tiles (tile_mode 0: table, 2: dense rows); grid_tiles = table capacity or row tiles
@@ -90,6 +92,8 @@ bool tiles_mma_supported(int64_t K, int64_t N, int64_t src_rows, int gs);
 // rows: 128 (tile table of up to 128-row tiles, or dense rows) or 32 (tiles of at most 32 rows)
 hipError_t launch_tiles_mma(const TileArgs& a, int bits, int gs, bool glu, bool out16, int rows,
                             hipStream_t st);
+// both tables in one launch: `tiles` (up to 128 rows, n_tiles) and `tiles2` (up to 32 rows, n_tiles2)
+hipError_t launch_tiles_mma_dual(const TileArgs& a, int bits, int gs, bool glu, bool out16, hipStream_t st);
 hipError_t launch_to_f16(const uint16_t* x, int64_t elems, int bits, uint16_t* out, hipStream_t st);
 
 // combine tail

@@ -67,43 +67,25 @@ MOEGQ_DEV f16x8_t deq_operand(uint32_t w0, uint32_t w1, f16x2_t s2, f16x2_t b2) 
   return __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-// register budget: 2 workgroups per CU (128 accumulators per lane at MI = 8;
-// the 32-row variant needs far fewer registers and fits more)
-template <int BITS, int GS, bool GLU, bool OUT16, int MI>
-__global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
-  constexpr int NF = GLU ? TM_C / 2 : TM_C;      // output features per tile
-  constexpr int CB = 4 * BITS;                    // code bytes per lane per K step (32 codes)
-  constexpr int TM_M = 16 * MI;                   // rows per tile
-  constexpr int PD = MI >= 8 ? 1 : 3;             // K steps of prefetch (activations and codes)
-  constexpr int RING = PD + 1;                     // LDS and register ring stages
-  __shared__ __attribute__((aligned(16))) uint16_t As[RING][16 * MI * TM_K];
+// One tile: rows r0 .. r1 - 1 of expert e, MFMA columns n0 .. n0 + 255.  lds
+// holds the activation ring: RING stages of 16 * MI rows x TM_K fp16.
+template <int MI> struct MmaRing {
+  static constexpr int PD = MI >= 8 ? 1 : 3;     // K steps of prefetch (activations and codes)
+  static constexpr int RING = PD + 1;             // LDS and register ring stages
+  static constexpr int HALFS = RING * 16 * MI * TM_K;
+};
 
+template <int BITS, int GS, bool GLU, bool OUT16, int MI>
+MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e, int n0) {
+  constexpr int CB = 4 * BITS;                    // code bytes per lane per K step (32 codes)
+  constexpr int PD = MmaRing<MI>::PD;
+  constexpr int RING = MmaRing<MI>::RING;
+  constexpr int STAGE = 16 * MI * TM_K;           // halfs per ring stage
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int N = A.N, K = A.K;
-  const int NB = (N + NF - 1) / NF;
-  const int total = A.tile_mode == 2 ? (int)gridDim.x : *A.n_tiles * NB;
-  int bid = blockIdx.x;
-  if (bid >= total) return;
-  {
-    const int q = total / 8;           // XCD-contiguous ranges over the first 8 q blocks
-    if (bid < 8 * q) bid = (bid % 8) * q + bid / 8;
-  }
-  const int tile = bid / NB;
-  const int n0 = (bid % NB) * NF;
   const int Kw = K * BITS / 32, G = K / GS;
-
-  int r0, r1, e;
-  if (A.tile_mode == 2) {            // dense rows, one weight matrix
-    r0 = tile * TM_M;
-    if (r0 >= A.P) return;
-    r1 = (int)min(A.P, (int64_t)r0 + TM_M);
-    e = 0;
-  } else {
-    const int32_t* t = A.tiles + 3 * tile;
-    r0 = t[0]; e = t[1]; r1 = r0 + t[2];
-  }
   r0 = __builtin_amdgcn_readfirstlane(r0);
   r1 = __builtin_amdgcn_readfirstlane(r1);
   e = __builtin_amdgcn_readfirstlane(e);
@@ -209,7 +191,7 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
     constexpr int AV = (MI + 3) / 4;
 #pragma unroll
     for (int v = part * AV; v < (part + 1) * AV && v < MI; ++v) {
-      uint16_t* dst = &As[stg][4 * (MI * wave + v) * TM_K];
+      uint16_t* dst = lds + stg * STAGE + 4 * (MI * wave + v) * TM_K;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, a_off[v],
                                                (uint32_t)t * TM_K * 2u, 0, 0);
     }
@@ -234,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
       s2[j] = f16_splat(pick(win_s, ks, j));
       b2[j] = f16_splat(pick(win_b, ks, j));
     }
-    const uint16_t* base = &As[sl][c16 * TM_K];
+    const uint16_t* base = lds + sl * STAGE + c16 * TM_K;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       issue(ks + PD, fut, s);             // a quarter of a later step's loads per sub-step
@@ -299,6 +281,62 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
   }
 }
 
+// XCD-contiguous ranges: the hardware deals workgroups to the 8 XCDs round
+// robin; block b of a range of `total` goes to XCD b % 8, so logical id
+// (b % 8) * q + b / 8 keeps neighbours (column blocks of one tile, tiles of
+// one expert) on one XCD's L2.  The last total % 8 blocks keep their index.
+MOEGQ_DEV int xcd_remap(int b, int total) {
+  const int q = total / 8;
+  return b < 8 * q ? (b % 8) * q + b / 8 : b;
+}
+
+// register budget: 2 workgroups per CU (128 accumulators per lane at MI = 8;
+// the 32-row variant needs far fewer registers)
+template <int BITS, int GS, bool GLU, bool OUT16, int MI>
+__global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
+  constexpr int NF = GLU ? TM_C / 2 : TM_C;      // output features per tile
+  __shared__ __attribute__((aligned(16))) uint16_t As[MmaRing<MI>::HALFS];
+  const int NB = (A.N + NF - 1) / NF;
+  const int total = A.tile_mode == 2 ? (int)gridDim.x : *A.n_tiles * NB;
+  if ((int)blockIdx.x >= total) return;
+  const int bid = xcd_remap(blockIdx.x, total);
+  const int tile = bid / NB, n0 = (bid % NB) * NF;
+  int r0, r1, e;
+  if (A.tile_mode == 2) {            // dense rows, one weight matrix
+    r0 = tile * 16 * MI;
+    if (r0 >= A.P) return;
+    r1 = (int)min(A.P, (int64_t)r0 + 16 * MI);
+    e = 0;
+  } else {
+    const int32_t* t = A.tiles + 3 * tile;
+    r0 = t[0]; e = t[1]; r1 = r0 + t[2];
+  }
+  tile_body<BITS, GS, GLU, OUT16, MI>(A, As, r0, r1, e, n0);
+}
+
+// Both tile tables in one launch: blocks [0, n_big * NB) take the 128-row
+// tiles of `tiles`, the next n_small * NB blocks the 32-row tiles of `tiles2`.
+// The few-row tiles stream their experts' weights from HBM while the last
+// round of 128-row tiles keeps only part of the machine busy.
+template <int BITS, int GS, bool GLU, bool OUT16>
+__global__ __launch_bounds__(256, 2) void tile_mma_dual_kernel(TileArgs A) {
+  constexpr int NF = GLU ? TM_C / 2 : TM_C;
+  constexpr int HALFS = MmaRing<8>::HALFS > MmaRing<2>::HALFS ? MmaRing<8>::HALFS : MmaRing<2>::HALFS;
+  __shared__ __attribute__((aligned(16))) uint16_t As[HALFS];
+  const int NB = (A.N + NF - 1) / NF;
+  const int nbig = *A.n_tiles * NB, nsmall = *A.n_tiles2 * NB;
+  const int b = blockIdx.x;
+  if (b < nbig) {
+    const int bid = xcd_remap(b, nbig);
+    const int32_t* t = A.tiles + 3 * (bid / NB);
+    tile_body<BITS, GS, GLU, OUT16, 8>(A, As, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
+  } else if (b < nbig + nsmall) {
+    const int bid = b - nbig;
+    const int32_t* t = A.tiles2 + 3 * (bid / NB);
+    tile_body<BITS, GS, GLU, OUT16, 2>(A, As, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
+  }
+}
+
 // bf16 rows -> fp16 rows in the dequantizer's element order (8-element chunks)
 template <int BITS>
 __global__ __launch_bounds__(256) void to_f16_kernel(const uint4* __restrict__ x, int64_t chunks,
@@ -322,6 +360,28 @@ template <int BITS, int GS, int MI>
 static hipError_t launch_mma_m(const TileArgs& a, bool glu, bool out16, hipStream_t st) {
   if (glu) return out16 ? launch_mma_t<BITS, GS, true, true, MI>(a, st) : launch_mma_t<BITS, GS, true, false, MI>(a, st);
   return launch_mma_t<BITS, GS, false, false, MI>(a, st);
+}
+
+template <int BITS, int GS, bool GLU, bool OUT16>
+static hipError_t launch_dual_t(const TileArgs& a, hipStream_t st) {
+  constexpr int NF = GLU ? TM_C / 2 : TM_C;
+  const int64_t NB = (a.N + NF - 1) / NF;
+  const int64_t nblk = (a.grid_tiles + a.grid_tiles2) * NB;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((tile_mma_dual_kernel<BITS, GS, GLU, OUT16>), dim3((unsigned)nblk), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tiles_mma_dual(const TileArgs& a, int bits, int gs, bool glu, bool out16, hipStream_t st) {
+#define MOEGQ_TD(B, G)                                                                              \
+  if (bits == B && gs == G) {                                                                       \
+    if (glu) return out16 ? launch_dual_t<B, G, true, true>(a, st) : launch_dual_t<B, G, true, false>(a, st); \
+    return launch_dual_t<B, G, false, false>(a, st);                                                \
+  }
+  MOEGQ_TD(4, 32) MOEGQ_TD(4, 64) MOEGQ_TD(4, 128) MOEGQ_TD(8, 32) MOEGQ_TD(8, 64) MOEGQ_TD(8, 128)
+#undef MOEGQ_TD
+  return hipErrorInvalidValue;
 }
 
 bool tiles_mma_supported(int64_t K, int64_t N, int64_t src_rows, int gs) {

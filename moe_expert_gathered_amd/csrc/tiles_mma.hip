@@ -68,18 +68,20 @@ MOEGQ_DEV f16x8_t deq_operand(uint32_t w0, uint32_t w1, f16x2_t s2, f16x2_t b2) 
 }
 
 // One tile: rows r0 .. r1 - 1 of expert e, MFMA columns n0 .. n0 + 255.  lds
-// holds the activation ring: RING stages of 16 * MI rows x TM_K fp16.
-template <int MI> struct MmaRing {
-  static constexpr int PD = MI >= 8 ? 1 : 3;     // K steps of prefetch (activations and codes)
-  static constexpr int RING = PD + 1;             // LDS and register ring stages
-  static constexpr int HALFS = RING * 16 * MI * TM_K;
+// holds the activation ring: RA stages of 16 * MI rows x TM_K fp16.
+template <int MI, int BITS = 4> struct MmaRing {
+  static constexpr int PDA = MI >= 8 ? 1 : 3;                   // K steps of activation prefetch
+  static constexpr int PDB = MI >= 8 ? 1 : 3;                   // K steps of code prefetch (registers)
+  static constexpr int RA = PDA + 1, RB = PDB + 1;              // LDS and register ring stages
+  static constexpr int U = (RA % RB == 0) ? RA : (RB % RA == 0) ? RB : RA * RB;   // steps per unrolled loop
+  static constexpr int HALFS = RA * 16 * MI * TM_K;
 };
 
 template <int BITS, int GS, bool GLU, bool OUT16, int MI>
 MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e, int n0) {
   constexpr int CB = 4 * BITS;                    // code bytes per lane per K step (32 codes)
-  constexpr int PD = MmaRing<MI>::PD;
-  constexpr int RING = MmaRing<MI>::RING;
+  using Ring = MmaRing<MI, BITS>;
+  constexpr int PDA = Ring::PDA, PDB = Ring::PDB, RA = Ring::RA, RB = Ring::RB, U = Ring::U;
   constexpr int STAGE = 16 * MI * TM_K;           // halfs per ring stage
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -181,31 +183,38 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nK = K / TM_K;
-  // ring of code registers: stage t % RING holds step t's codes (fixed extents:
+  // ring of code registers: stage t % RB holds step t's codes (fixed extents:
   // the unused stages and halves are never touched and cost no registers)
   uint4 cw[4][4][2];
   uint4 win_s, win_b, nwin_s, nwin_b;
   constexpr int LPS = MI + 4 * (BITS / 4);        // loads per step: activations + codes
-  auto issue = [&](int t, int stg, int part) {    // part p of step t's loads (p = 0..3), into stage stg
+  // part p (0..3) of step t's loads: activation rows into LDS stage sa, codes of block p into register stage sb
+  auto issue_a = [&](int t, int sa, int part) {
     if (t >= nK) return;
     constexpr int AV = (MI + 3) / 4;
 #pragma unroll
     for (int v = part * AV; v < (part + 1) * AV && v < MI; ++v) {
-      uint16_t* dst = lds + stg * STAGE + 4 * (MI * wave + v) * TM_K;
+      uint16_t* dst = lds + sa * STAGE + 4 * (MI * wave + v) * TM_K;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, a_off[v],
                                                (uint32_t)t * TM_K * 2u, 0, 0);
     }
+  };
+  auto issue_b = [&](int t, int sb, int part) {
+    if (t >= nK) return;
     const uint32_t soff = (uint32_t)t * TM_K * BITS / 8;
 #pragma unroll
-    for (int h = 0; h < BITS / 4; ++h) cw[stg][part][h] = ld_codes(part, soff + 16 * h);
+    for (int h = 0; h < BITS / 4; ++h) cw[sb][part][h] = ld_codes(part, soff + 16 * h);
   };
-  auto step = [&](int ks, auto stage) {
-    constexpr int sl = decltype(stage)::value;
-    constexpr int fut = (sl + PD) % RING;
-    // step ks's loads were issued PD steps ago; at most the later PD - 1 steps' loads may still fly
-    constexpr int VM = (PD - 1) * LPS;
+  auto step = [&](int ks, auto phase) {
+    constexpr int sa = decltype(phase)::value % RA, sb = decltype(phase)::value % RB;
+    constexpr int fa = (sa + PDA) % RA, fb = (sb + PDB) % RB;
+    // step ks's activation rows were issued PDA steps ago; at least the PDA - 1 later steps'
+    // loads were issued after them (the compiler may reorder loads inside a sub-step, never
+    // across the sub-step barriers; extra window loads only lengthen the wait)
+    constexpr int VM = (PDA - 1) * LPS;
+    static_assert(VM < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt(0x0F70 | (VM & 15) | ((VM >> 4) << 14));
-    __syncthreads();                      // every wave's rows landed; stage fut (step ks - 1) is free
+    __syncthreads();                      // every wave's rows landed; the stage of step ks - 1 is free
     if (ks % WSTEPS == 0) {
       win_s = nwin_s; win_b = nwin_b;
       if ((ks + WSTEPS) < nK) load_win(ks / WSTEPS + 1, nwin_s, nwin_b);
@@ -216,14 +225,15 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
       s2[j] = f16_splat(pick(win_s, ks, j));
       b2[j] = f16_splat(pick(win_b, ks, j));
     }
-    const uint16_t* base = lds + sl * STAGE + c16 * TM_K;
+    const uint16_t* base = lds + sa * STAGE + c16 * TM_K;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      issue(ks + PD, fut, s);             // a quarter of a later step's loads per sub-step
+      issue_a(ks + PDA, fa, s);           // a quarter of later steps' loads per sub-step
+      issue_b(ks + PDB, fb, s);
       f16x8_t bq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t* wv = &cw[sl][j][0].x;
+        const uint32_t* wv = &cw[sb][j][0].x;
         bq[j] = BITS == 4 ? deq_operand<4>(wv[s], 0, s2[j], b2[j])
                           : deq_operand<8>(wv[2 * s], wv[2 * s + 1], s2[j], b2[j]);
       }
@@ -239,16 +249,24 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
   };
   load_win(0, win_s, win_b);
   nwin_s = win_s; nwin_b = win_b;
+  // prologue: activations of steps 0 .. PDA - 1, codes of steps 0 .. PDB - 1, in step order
 #pragma unroll
-  for (int t = 0; t < PD; ++t)
+  for (int t = 0; t < (PDA > PDB ? PDA : PDB); ++t)
 #pragma unroll
-    for (int part = 0; part < 4; ++part) issue(t, t, part);
-  for (int ks = 0; ks < nK; ks += RING) {
-    step(ks, std::integral_constant<int, 0>{});
-    if (ks + 1 < nK) step(ks + 1, std::integral_constant<int, 1 % RING>{});
-    if (RING > 2 && ks + 2 < nK) step(ks + 2, std::integral_constant<int, 2 % RING>{});
-    if (RING > 3 && ks + 3 < nK) step(ks + 3, std::integral_constant<int, 3 % RING>{});
+    for (int part = 0; part < 4; ++part) {
+      if (t < PDA) issue_a(t, t % RA, part);
+      if (t < PDB) issue_b(t, t % RB, part);
+    }
+  using std::integral_constant;
+  for (int ks = 0; ks < nK; ks += U) {
+    step(ks, integral_constant<int, 0>{});
+    if (U > 1 && ks + 1 < nK) step(ks + 1, integral_constant<int, 1 % U>{});
+    if (U > 2 && ks + 2 < nK) step(ks + 2, integral_constant<int, 2 % U>{});
+    if (U > 3 && ks + 3 < nK) step(ks + 3, integral_constant<int, 3 % U>{});
+    if (U > 4 && ks + 4 < nK) step(ks + 4, integral_constant<int, 4 % U>{});
+    if (U > 5 && ks + 5 < nK) step(ks + 5, integral_constant<int, 5 % U>{});
   }
+  static_assert(U <= 6, "unroll");
 
   // epilogue: acc[i][j][q] = output (row 16 i + c16, memory column block_base(j) + 4 g + q)
   const bool vec = (N & 3) == 0;
@@ -295,7 +313,7 @@ MOEGQ_DEV int xcd_remap(int b, int total) {
 template <int BITS, int GS, bool GLU, bool OUT16, int MI>
 __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
   constexpr int NF = GLU ? TM_C / 2 : TM_C;      // output features per tile
-  __shared__ __attribute__((aligned(16))) uint16_t As[MmaRing<MI>::HALFS];
+  __shared__ __attribute__((aligned(16))) uint16_t As[MmaRing<MI, BITS>::HALFS];
   const int NB = (A.N + NF - 1) / NF;
   const int total = A.tile_mode == 2 ? (int)gridDim.x : *A.n_tiles * NB;
   if ((int)blockIdx.x >= total) return;
@@ -321,7 +339,7 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
 template <int BITS, int GS, bool GLU, bool OUT16>
 __global__ __launch_bounds__(256, 2) void tile_mma_dual_kernel(TileArgs A) {
   constexpr int NF = GLU ? TM_C / 2 : TM_C;
-  constexpr int HALFS = MmaRing<8>::HALFS > MmaRing<2>::HALFS ? MmaRing<8>::HALFS : MmaRing<2>::HALFS;
+  constexpr int HALFS = MmaRing<8, BITS>::HALFS > MmaRing<2, BITS>::HALFS ? MmaRing<8, BITS>::HALFS : MmaRing<2, BITS>::HALFS;
   __shared__ __attribute__((aligned(16))) uint16_t As[HALFS];
   const int NB = (A.N + NF - 1) / NF;
   const int nbig = *A.n_tiles * NB, nsmall = *A.n_tiles2 * NB;

@@ -197,3 +197,19 @@ def test_combine_gated_bitwise(mg):
     ref = mg.moe_combine(bf(y), i32(inv), bf(sc), mg.sigmoid_gate(bf(s), bf(z)))
     got = mg.moe_combine_gated(bf(y), i32(inv), bf(sc), bf(s), bf(z))
     assert np.array_equal(host_bf(got), host_bf(ref))
+
+
+def test_moe_prefill_repeatable(mg):
+    """Five calls of the 512-row layer give the same bits (no race in the
+    asynchronous loads into LDS, the tile schedule or the combine)."""
+    sh = synth.PREFILL
+    T = 512
+    idx, scores = synth.zipf_routing(3, T, sh.E, sh.top_k, sub=5)
+    x = synth.activations(3, T, sh.H, sub=5)
+    ex = [triple(m) for m in synth.expert_set(3, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode="words",
+                                              experts=np.unique(idx))]
+    shp = tuple(triple(m) for m in synth.shared_params(3, sh.H, sh.shared_I, sh.gs, sh.bits))
+    outs = [host_bf(mg.moe_prefill(bf(x), i32(idx), bf(scores), *ex, shared=shp, group_size=sh.gs, bits=sh.bits))
+            for _ in range(5)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])

@@ -480,7 +480,9 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
   if (tiles_mma_supported(H, I, T, group_size) && tiles_mma_supported(I, H, P, group_size)) {
     // fp16 copy of x for the matrix cores, parked in y (y is written only by the down pass);
     // h is written and read in the same fp16 chunk order
-    if (launch_to_f16((const uint16_t*)x, T * H, bits, (uint16_t*)y, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    if (launch_prep((const uint16_t*)x, T, (int)H, bits, group_size, (uint16_t*)y, nullptr, nullptr, nullptr, nullptr,
+                    s) != hipSuccess)
+      return MOEGQ_ERR_LAUNCH;
     g.x = gs_.x = (const uint16_t*)y;
     if (hybrid) {
       g.tiles2 = d.tiles2 = ws.small_tiles; g.n_tiles2 = d.n_tiles2 = ws.n_tiles + 1;
@@ -544,15 +546,10 @@ int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
   sa.small_tiles = ws.small_tiles; sa.small_max = kSmallMax;
   sa.extra_rows = extra; sa.block_counts = ws.bc;
   if (launch_sort(sa, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-  if (launch_to_f16((const uint16_t*)x, T * H, bits, ws.x16, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-  if (shared) {
-    // shared expert's sigmoid gate logit z[t] = x[t] . w_gate (one output row)
-    QmvArgs zq{};
-    zq.x = (const uint16_t*)x; zq.lhs_div = 1;
-    zq.w0 = (const uint32_t*)gate_w; zq.s0 = (const uint16_t*)gate_s; zq.b0 = (const uint16_t*)gate_b;
-    zq.N = 1; zq.K = (int)H; zq.out = ws.z;
-    if (launch_qmv(zq, bits, group_size, false, T, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-  }
+  // fp16 activations and the shared expert's sigmoid gate logit in one pass over x
+  if (launch_prep((const uint16_t*)x, T, (int)H, bits, group_size, ws.x16, shared ? (const uint32_t*)gate_w : nullptr,
+                  (const uint16_t*)gate_s, (const uint16_t*)gate_b, ws.z, s) != hipSuccess)
+    return MOEGQ_ERR_LAUNCH;
   TileArgs g{};
   g.x = ws.x16; g.lhs = ws.lhs; g.lhs_div = 1; g.rows_per_batch = 1;
   g.tiles = ws.tiles; g.n_tiles = ws.n_tiles; g.P = P; g.E = (int)E;

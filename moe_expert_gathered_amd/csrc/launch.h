@@ -86,7 +86,7 @@ hipError_t launch_tiles_big(const TileArgs& a, int bits, int gs, bool glu, hipSt
 // tiles of at most 16 (bm <= 16) or 32 rows from a table (tile_mode 0); rows gathered through lhs
 hipError_t launch_tiles_small(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st);
 // 128-row tiles with register-dequantized weights (tile_mode 0: table, 2: dense rows).  a.x holds
-// fp16 rows in the dequantizer's chunk order (launch_to_f16), gathered through a.lhs (or row r);
+// fp16 rows in the dequantizer's chunk order (launch_prep), gathered through a.lhs (or row r);
 // out16: the GLU output is written the same way (fp16, chunk order) for a following down pass
 bool tiles_mma_supported(int64_t K, int64_t N, int64_t src_rows, int gs);
 // rows: 128 (tile table of up to 128-row tiles, or dense rows) or 32 (tiles of at most 32 rows)
@@ -94,7 +94,9 @@ hipError_t launch_tiles_mma(const TileArgs& a, int bits, int gs, bool glu, bool 
                             hipStream_t st);
 // both tables in one launch: `tiles` (up to 128 rows, n_tiles) and `tiles2` (up to 32 rows, n_tiles2)
 hipError_t launch_tiles_mma_dual(const TileArgs& a, int bits, int gs, bool glu, bool out16, hipStream_t st);
-hipError_t launch_to_f16(const uint16_t* x, int64_t elems, int bits, uint16_t* out, hipStream_t st);
+// x [T, H] bf16 -> x16 (fp16, chunk order); with gw (a [1, H] quantized row) also z[t] = bf16(x[t] . w)
+hipError_t launch_prep(const uint16_t* x, int64_t T, int H, int bits, int gs, uint16_t* x16, const uint32_t* gw,
+                       const uint16_t* gsc, const uint16_t* gbi, uint16_t* z, hipStream_t st);
 
 // combine tail
 // shared (nullable) rows [T, H] are added as they are, or, with z (nullable, [T] bf16), gated first:

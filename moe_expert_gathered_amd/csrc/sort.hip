@@ -98,20 +98,33 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_scan_kernel(SortArgs A, int
   const int tid = threadIdx.x;
   const int E = A.E;
   const int64_t P = A.P;
-  // counts, and per-block bases relative to the expert's first row
+  // counts (16 independent loads in flight per batch)
   int c = 0;
   if (tid < E) {
-    for (int b = 0; b < nblk; ++b) {
-      int32_t* q = A.block_counts + (int64_t)b * E + tid;
-      const int v = *q;
-      *q = c;
-      c += v;
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = b0 + j < nblk ? A.block_counts[(int64_t)(b0 + j) * E + tid] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) c += v[j];
     }
   }
   int off;
   block_excl_scan(c, wtot, off);
-  if (tid < E)
-    for (int b = 0; b < nblk; ++b) A.block_counts[(int64_t)b * E + tid] += off;
+  // per-block bases: the expert's first row plus the counts of the blocks before
+  if (tid < E) {
+    int run = off;
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = b0 + j < nblk ? A.block_counts[(int64_t)(b0 + j) * E + tid] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (b0 + j < nblk) A.block_counts[(int64_t)(b0 + j) * E + tid] = run;
+        run += v[j];
+      }
+    }
+  }
   const bool hybrid = A.tile_mode == 3;
   const bool is_big = !hybrid || c >= A.small_max;
   const int ntile = (A.bm > 0 && is_big) ? (c + A.bm - 1) / A.bm : 0;

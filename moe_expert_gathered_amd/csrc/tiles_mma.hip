@@ -355,12 +355,43 @@ __global__ __launch_bounds__(256, 2) void tile_mma_dual_kernel(TileArgs A) {
   }
 }
 
-// bf16 rows -> fp16 rows in the dequantizer's element order (8-element chunks)
-template <int BITS>
-__global__ __launch_bounds__(256) void to_f16_kernel(const uint4* __restrict__ x, int64_t chunks,
-                                                     uint4* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < chunks) out[i] = act_f16<BITS>(x[i]);
+// One pass over the activation rows before the tile passes: bf16 -> fp16 in
+// the dequantizer's element order (8-element chunks), and, given the shared
+// expert's one-row sigmoid gate, its logit z[t] = bf16(x[t] . dequant(w)^T)
+// (fp32 dequant and accumulation; MTPLX PR 558 Summary: the gated shared
+// expert).  One workgroup per row.
+template <int BITS, int GS>
+__global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ x, int H, uint16_t* __restrict__ x16,
+                                                   const uint32_t* __restrict__ gw, const uint16_t* __restrict__ gs_,
+                                                   const uint16_t* __restrict__ gb, uint16_t* __restrict__ z) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + t * (int64_t)H);
+  uint4* xo = reinterpret_cast<uint4*>(x16 + t * (int64_t)H);
+  float part = 0.f;
+  for (int c = tid; c < H / 8; c += 256) {
+    const uint4 v = xr[c];
+    xo[c] = act_f16<BITS>(v);
+    if (gw) {
+      const int k0 = 8 * c;
+      const float s = bf16_to_f32(gs_[k0 / GS]), b = bf16_to_f32(gb[k0 / GS]);
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+      uint32_t w0 = gw[k0 * BITS / 32], w1 = BITS == 8 ? gw[k0 * BITS / 32 + 1] : 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t q = BITS == 4 ? (w0 >> (4 * j)) & 0xFu : ((j < 4 ? w0 : w1) >> (8 * (j & 3))) & 0xFFu;
+        const float xv = (j & 1) ? bf16_hi(d[j >> 1]) : bf16_lo(d[j >> 1]);
+        part = fmaf(xv, fmaf((float)q, s, b), part);
+      }
+    }
+  }
+  if (!gw) return;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = part;
+  __syncthreads();
+  if (tid == 0) z[t] = f32_to_bf16(red[0] + red[1] + red[2] + red[3]);
 }
 
 template <int BITS, int GS, bool GLU, bool OUT16, int MI>
@@ -420,15 +451,18 @@ hipError_t launch_tiles_mma(const TileArgs& a, int bits, int gs, bool glu, bool 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_to_f16(const uint16_t* x, int64_t elems, int bits, uint16_t* out, hipStream_t st) {
-  const int64_t chunks = elems / 8;
-  if (chunks <= 0) return hipSuccess;
-  const unsigned nb = (unsigned)((chunks + 255) / 256);
-  if (bits == 4)
-    hipLaunchKernelGGL(to_f16_kernel<4>, dim3(nb), dim3(256), 0, st, (const uint4*)x, chunks, (uint4*)out);
-  else
-    hipLaunchKernelGGL(to_f16_kernel<8>, dim3(nb), dim3(256), 0, st, (const uint4*)x, chunks, (uint4*)out);
-  return hipGetLastError();
+hipError_t launch_prep(const uint16_t* x, int64_t T, int H, int bits, int gs, uint16_t* x16, const uint32_t* gw,
+                       const uint16_t* gsc, const uint16_t* gbi, uint16_t* z, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (T >= ((int64_t)1 << 31) || H % 8 != 0) return hipErrorInvalidValue;
+#define MOEGQ_PREP(B, G)                                                                                     \
+  if (bits == B && gs == G) {                                                                                \
+    hipLaunchKernelGGL((prep_kernel<B, G>), dim3((unsigned)T), dim3(256), 0, st, x, H, x16, gw, gsc, gbi, z); \
+    return hipGetLastError();                                                                                \
+  }
+  MOEGQ_PREP(4, 32) MOEGQ_PREP(4, 64) MOEGQ_PREP(4, 128) MOEGQ_PREP(8, 32) MOEGQ_PREP(8, 64) MOEGQ_PREP(8, 128)
+#undef MOEGQ_PREP
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moegq

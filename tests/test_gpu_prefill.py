@@ -213,3 +213,31 @@ def test_moe_prefill_repeatable(mg):
             for _ in range(5)]
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("T", [1, 4, 37])
+def test_moe_prefill_few_tokens(mg, T):
+    """The whole-layer entry point with fewer tokens than one tile (every
+    routed expert a few-row tile, the shared expert one partial 128-row tile)."""
+    sh, idx, scores, x, ex = _prefill_case(T, sub=7)
+    shp = synth.shared_params(3, sh.H, sh.shared_I, sh.gs, sh.bits)
+    want, _ = oracle.moe_prefill_layer(x, idx, scores, ex, shp, gs=sh.gs, bits=sh.bits)
+    got = mg.moe_prefill(bf(x), i32(idx), bf(scores), *[triple(m) for m in ex],
+                         shared=tuple(triple(m) for m in shp), group_size=sh.gs, bits=sh.bits)
+    assert_parity(host_bf(got), want, name=f"layer T={T}")
+
+
+def test_moe_prefill_8bit_large_sampled(mg):
+    """Whole layer at the large shape with 8-bit GS 128 codes (hidden 4096,
+    288 experts, inter 2048), no shared expert: 713 rows on the GPU, 3
+    sampled tokens (up to 24 experts) through the oracle."""
+    sh = synth.LARGE8
+    T = 713
+    idx, scores = synth.zipf_routing(4, T, sh.E, sh.top_k, sub=3)
+    x = synth.activations(4, T, sh.H, sub=3)
+    ex = synth.expert_set(12, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode="words", experts=np.unique(idx))
+    got = host_bf(mg.moe_prefill(bf(x), i32(idx), bf(scores), *[triple(m) for m in ex], shared=None,
+                                 group_size=sh.gs, bits=sh.bits))
+    sub = np.sort(np.random.default_rng(13).choice(T, 3, replace=False))
+    want, _ = oracle.moe_prefill_layer(x[sub], idx[sub], scores[sub], ex, None, gs=sh.gs, bits=sh.bits)
+    assert_parity(got[sub], want, name="layer 8-bit sampled")

@@ -155,101 +155,142 @@ def decode_leg(torch, m, synth, M, steps, warmup, n_sets=42, isolated=False, cfg
 
 
 # ----------------------------------------------------------------------------- prefill
-def prefill_leg(torch, m, synth, T=2048, steps=20, warmup=5, cfg=3):
-    """The MoE layer at 2048 rows (hidden 2048, 256 experts, top-8, inter 512,
-    4-bit GS 64, gated shared expert): one moe_prefill call per step (sort,
-    routed + shared experts, gated combine)."""
+def layer_bytes_flops(sh, T, counts, shared):
+    """Algorithmic flops and bytes of one MoE prefill layer (weights of the
+    active experts once, activations once per materialized tensor)."""
+    P = T * sh.top_k
+    active = int((counts > 0).sum())
+    H, I = sh.H, sh.I
+    SI = sh.shared_I if shared else 0
+    flops = P * 6 * H * I + (T * 6 * H * SI + T * 2 * H if shared else 0)
+    B = lambda n, k: n * (k * sh.bits // 8 + 2 * (k // sh.gs) * 2)
+    wbytes = active * (2 * B(I, H) + B(H, I)) + ((2 * B(SI, H) + B(H, SI) + B(1, H)) if shared else 0)
+    act = (T * H * 2 + P * I * 2 * 2 + P * H * 2          # x, h_sorted write+read, y_sorted write
+           + (T * SI * 2 * 2 + T * H * 2 if shared else 0)   # shared h write+read, shared y write
+           + P * H * 2 + (T * H * 2 if shared else 0) + T * H * 2)   # combine: y, shared, out
+    return flops, wbytes + act
+
+
+def prefill_leg(torch, m, synth, rows=(2048, 128, 512, 4096), steps=20, warmup=5, cfg=3):
+    """The MoE layer of hidden 2048, 256 experts, top-8, inter 512, 4-bit GS 64
+    with a gated shared expert: one moe_prefill call per step (sort, routed +
+    shared experts, gated combine), timed as HIP-graph replays of 10 layers."""
     sh = synth.PREFILL
     dev = torch.device("cuda")
     gate, up, down = synth.device_expert_set(dev, cfg, sh.E, sh.H, sh.I, sh.gs, sh.bits)
     sg, su, sd = synth.device_expert_set(dev, cfg + 100, 1, sh.H, sh.shared_I, sh.gs, sh.bits)
     sg, su, sd = [tuple(t[0] for t in trip) for trip in (sg, su, sd)]
     grow = tuple(t[0] for t in synth.device_drawn_words(dev, (cfg, 3, 3), (1, 1), sh.H, sh.gs, sh.bits))
-    idx_np, scores_np = synth.zipf_routing(cfg, T, sh.E, sh.top_k)
-    idx = torch.from_numpy(idx_np).to(dev)
-    scores = torch.from_numpy(scores_np.view(np.int16)).view(torch.bfloat16).to(dev)
-    x = torch.from_numpy(synth.activations(cfg, T, sh.H).view(np.int16)).view(torch.bfloat16).to(dev)
-    P = T * sh.top_k
-    out = torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(m.moe_prefill_workspace_bytes(T, sh.top_k, sh.E, sh.H, sh.I, True), dtype=torch.uint8,
-                     device=dev)
-    counts = np.bincount(idx_np.reshape(-1), minlength=sh.E)
-    active = int((counts > 0).sum())
+    res = {}
+    for T in rows:
+        idx_np, scores_np = synth.zipf_routing(cfg, T, sh.E, sh.top_k)
+        idx = torch.from_numpy(idx_np).to(dev)
+        scores = torch.from_numpy(scores_np.view(np.int16)).view(torch.bfloat16).to(dev)
+        x = torch.from_numpy(synth.activations(cfg, T, sh.H).view(np.int16)).view(torch.bfloat16).to(dev)
+        out = torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(m.moe_prefill_workspace_bytes(T, sh.top_k, sh.E, sh.H, sh.I, True), dtype=torch.uint8,
+                         device=dev)
+        counts = np.bincount(idx_np.reshape(-1), minlength=sh.E)
 
-    def step(i=0):
-        m.moe_prefill(x, idx, scores, gate, up, down, shared=(sg, su, sd, grow), group_size=sh.gs, bits=sh.bits,
-                      out=out, workspace=ws)
+        def step(i=0):
+            m.moe_prefill(x, idx, scores, gate, up, down, shared=(sg, su, sd, grow), group_size=sh.gs,
+                          bits=sh.bits, out=out, workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    el_eager = (time.perf_counter() - t0) / steps
-    layer_us = graph_time_us(torch, step, 10, reps=max(1, steps // 10), check=lambda: out)
-    el = layer_us * 1e-6
-    H, I, SI = sh.H, sh.I, sh.shared_I
-    flops = P * 6 * H * I + T * 6 * H * SI + T * 2 * H
-    B = lambda n, k: n * (k * sh.bits // 8 + 2 * (k // sh.gs) * 2)
-    wbytes = active * (2 * B(I, H) + B(H, I)) + 2 * B(SI, H) + B(H, SI) + B(1, H)
-    act = (T * H * 2 + P * I * 2 * 2 + P * H * 2          # x, h_sorted write+read, y_sorted write
-           + T * SI * 2 * 2 + T * H * 2                   # shared h write+read, shared y write
-           + P * H * 2 + T * H * 2 * 2)                   # combine: y read, shared read, out write
-    res = {"rows": T, "active_experts": active, "max_load": int(counts.max()), "mean_load": float(P / active),
-           "ms_per_layer": el * 1e3, "eager_ms_per_layer": el_eager * 1e3, "timing": "hip graph of 10 layers",
-           "gflop": flops / 1e9, "bytes": wbytes + act,
-           "mfma_util": flops / el / (MFMA_BF16_PEAK_TFLOPS * 1e12),
-           "hbm_frac": (wbytes + act) / el / (HBM_PEAK_GBS * 1e9)}
-    res["roofline_frac"] = max(res["mfma_util"], res["hbm_frac"])
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        el_eager = (time.perf_counter() - t0) / steps
+        el = graph_time_us(torch, step, 10, reps=max(1, steps // 10), check=lambda: out) * 1e-6
+        flops, nbytes = layer_bytes_flops(sh, T, counts, True)
+        r = {"rows": T, "active_experts": int((counts > 0).sum()), "max_load": int(counts.max()),
+             "ms_per_layer": el * 1e3, "eager_ms_per_layer": el_eager * 1e3, "timing": "hip graph of 10 layers",
+             "gflop": flops / 1e9, "bytes": nbytes,
+             "mfma_util": flops / el / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+             "hbm_frac": nbytes / el / (HBM_PEAK_GBS * 1e9)}
+        r["roofline_frac"] = max(r["mfma_util"], r["hbm_frac"])
+        res[f"rows{T}"] = r
+        del ws
     del gate, up, down
     torch.cuda.empty_cache()
     return res
 
 
-def large_leg(torch, m, synth, T=4123, steps=5, warmup=2, bits=4, cfg=4):
-    sh = synth.LARGE4 if bits == 4 else synth.LARGE8
-    dev = torch.device("cuda")
-    gate, up, down = synth.device_expert_set(dev, cfg, sh.E, sh.H, sh.I, sh.gs, sh.bits)
-    idx_np, _ = synth.zipf_routing(cfg, T, sh.E, sh.top_k)
-    idx = torch.from_numpy(idx_np).to(dev)
-    x = torch.from_numpy(synth.activations(cfg, T, sh.H).view(np.int16)).view(torch.bfloat16).to(dev)
-    P = T * sh.top_k
-    y = torch.empty((P, sh.H), dtype=torch.bfloat16, device=dev)
-    inv = torch.empty(P, dtype=torch.int32, device=dev)
-    counts = np.bincount(idx_np.reshape(-1), minlength=sh.E)
-    res = {"rows": T, "bits": bits, "active_experts": int((counts > 0).sum())}
-    for name, tmode, bm in (("scheduled_bm16", 0, 16), ("naive_bm16", 1, 16), ("scheduled_bm64", 0, 64),
-                            ("scheduled_hybrid", 0, 0)):
-        for _ in range(warmup):
-            m.switch_glu(x, idx, gate, up, down, group_size=sh.gs, bits=sh.bits, mode=m.MODE_SORTED,
-                         tile_mode=tmode, bm=bm, y=y, inv=inv)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            m.switch_glu(x, idx, gate, up, down, group_size=sh.gs, bits=sh.bits, mode=m.MODE_SORTED,
-                         tile_mode=tmode, bm=bm, y=y, inv=inv)
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) / steps * 1e3
-        offs = np.concatenate([[0], np.cumsum(counts)])
-        if tmode == 0 and bm == 0:
-            # hybrid: 128-row tiles for experts with >= 32 rows, one few-row tile for the others
-            tiles = int(sum(-(-int(c) // 128) if c >= 32 else 1 for c in counts if c > 0))
-            passes = tiles
-        elif tmode == 0:
-            tiles = int(sum(-(-int(c) // bm) for c in counts))
-            passes = tiles
-        else:
-            tiles = -(-P // bm)
-            passes = 0
-            for r0 in range(0, P, bm):
-                r1 = min(P, r0 + bm)
-                passes += int(((offs[1:] > r0) & (offs[:-1] < r1) & (counts > 0)).sum())
-        flops = P * 6 * sh.H * sh.I
-        res[name] = {"ms": ms, "tiles": tiles, "k_passes": passes, "mfma_util": flops / (ms * 1e-3) / 2.5e15}
-    del gate, up, down
-    torch.cuda.empty_cache()
+def large_leg(torch, m, synth, rows=(713, 4123, 8192, 16384), steps=4, warmup=2, cfg=4):
+    """Large MoE prefill (hidden 4096, 288 experts, top-8, inter 2048): the
+    expert-aware schedule against naive BM 16 row tiling at 4123 rows (tile and
+    K-pass counts, switch_glu time), and the whole layer (moe_prefill, no shared
+    expert) at each size, 4-bit GS 64 and, at 4123 rows, 8-bit GS 128."""
+    res = {}
+    for bits in (4, 8):
+        sh = synth.LARGE4 if bits == 4 else synth.LARGE8
+        dev = torch.device("cuda")
+        gate, up, down = synth.device_expert_set(dev, cfg, sh.E, sh.H, sh.I, sh.gs, sh.bits)
+        for T in (rows if bits == 4 else (4123,)):
+            idx_np, scores_np = synth.zipf_routing(cfg, T, sh.E, sh.top_k)
+            idx = torch.from_numpy(idx_np).to(dev)
+            scores = torch.from_numpy(scores_np.view(np.int16)).view(torch.bfloat16).to(dev)
+            x = torch.from_numpy(synth.activations(cfg, T, sh.H).view(np.int16)).view(torch.bfloat16).to(dev)
+            P = T * sh.top_k
+            counts = np.bincount(idx_np.reshape(-1), minlength=sh.E)
+            r = {"rows": T, "bits": bits, "active_experts": int((counts > 0).sum())}
+            if bits == 4 and T == 4123:
+                y = torch.empty((P, sh.H), dtype=torch.bfloat16, device=dev)
+                inv = torch.empty(P, dtype=torch.int32, device=dev)
+                offs = np.concatenate([[0], np.cumsum(counts)])
+                for name, tmode, bm in (("scheduled_bm16", 0, 16), ("naive_bm16", 1, 16), ("scheduled_bm64", 0, 64),
+                                        ("scheduled_hybrid", 0, 0)):
+                    run = lambda: m.switch_glu(x, idx, gate, up, down, group_size=sh.gs, bits=sh.bits,
+                                               mode=m.MODE_SORTED, tile_mode=tmode, bm=bm, y=y, inv=inv)
+                    for _ in range(warmup):
+                        run()
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    for _ in range(steps):
+                        run()
+                    torch.cuda.synchronize()
+                    ms = (time.perf_counter() - t0) / steps * 1e3
+                    if tmode == 0 and bm == 0:
+                        # hybrid: 128-row tiles for experts with >= 32 rows, one few-row tile for the others
+                        tiles = int(sum(-(-int(c) // 128) if c >= 32 else 1 for c in counts if c > 0))
+                        passes = tiles
+                    elif tmode == 0:
+                        tiles = int(sum(-(-int(c) // bm) for c in counts))
+                        passes = tiles
+                    else:
+                        tiles = -(-P // bm)
+                        passes = 0
+                        for r0 in range(0, P, bm):
+                            r1 = min(P, r0 + bm)
+                            passes += int(((offs[1:] > r0) & (offs[:-1] < r1) & (counts > 0)).sum())
+                    flops = P * 6 * sh.H * sh.I
+                    r[name] = {"ms": ms, "tiles": tiles, "k_passes": passes,
+                               "mfma_util": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)}
+                del y, inv
+            out = torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(m.moe_prefill_workspace_bytes(T, sh.top_k, sh.E, sh.H, sh.I, False),
+                             dtype=torch.uint8, device=dev)
+            layer = lambda: m.moe_prefill(x, idx, scores, gate, up, down, shared=None, group_size=sh.gs,
+                                          bits=sh.bits, out=out, workspace=ws)
+            for _ in range(warmup):
+                layer()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                layer()
+            torch.cuda.synchronize()
+            el = (time.perf_counter() - t0) / steps
+            flops, nbytes = layer_bytes_flops(sh, T, counts, False)
+            r["layer"] = {"ms": el * 1e3, "gflop": flops / 1e9, "bytes": nbytes,
+                          "mfma_util": flops / el / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                          "hbm_frac": nbytes / el / (HBM_PEAK_GBS * 1e9)}
+            res[f"rows{T}_bits{bits}"] = r
+            del ws, out
+        del gate, up, down
+        torch.cuda.empty_cache()
     return res
 
 
@@ -401,11 +442,11 @@ def main():
         extra["decode_m1_isolated"] = decode_leg(torch, m, synth, 1, a.steps, a.warmup, isolated=True)
         extra["decode_m4_chained"] = decode_leg(torch, m, synth, 4, a.steps, a.warmup)
     if "prefill" in legs:
-        log("prefill 2048 rows")
-        extra["prefill_2048"] = prefill_leg(torch, m, synth)
+        log("prefill 2048 rows (and 128, 512, 4096)")
+        extra["prefill"] = prefill_leg(torch, m, synth)
     if "large" in legs:
-        log("large prefill 4123 rows")
-        extra["large_prefill_4123"] = large_leg(torch, m, synth)
+        log("large prefill 713 / 4123 / 8192 / 16384 rows")
+        extra["large_prefill"] = large_leg(torch, m, synth)
     if "dense" in legs:
         log("dense chain")
         extra["dense_chain"] = dense_leg(torch, m, synth)

@@ -219,6 +219,18 @@ def prefill_leg(torch, m, synth, rows=(2048, 128, 512, 4096), steps=20, warmup=5
     return res
 
 
+def hybrid_tile_count(counts, inter, small_max=32, big=128, slots=512):
+    """Tiles of the library's hybrid schedule for these per-expert counts (a
+    host-side restatement for the report): 128-row tiles for experts with at
+    least 32 rows and 32-row tiles for the others, or 32-row tiles for every
+    expert when the 128-row tiles would give the gate/up pass at most
+    slots / 8 work items."""
+    nbig = sum(-(-int(c) // big) for c in counts if c >= small_max)
+    if nbig * -(-inter // 128) <= slots // 8:
+        return int(sum(-(-int(c) // small_max) for c in counts if c > 0))
+    return int(nbig + sum(1 for c in counts if 0 < c < small_max))
+
+
 def large_leg(torch, m, synth, rows=(713, 4123, 8192, 16384), steps=4, warmup=2, cfg=4):
     """Large MoE prefill (hidden 4096, 288 experts, top-8, inter 2048): the
     expert-aware schedule against naive BM 16 row tiling at 4123 rows (tile and
@@ -254,9 +266,7 @@ def large_leg(torch, m, synth, rows=(713, 4123, 8192, 16384), steps=4, warmup=2,
                     torch.cuda.synchronize()
                     ms = (time.perf_counter() - t0) / steps * 1e3
                     if tmode == 0 and bm == 0:
-                        # hybrid: 128-row tiles for experts with >= 32 rows, one few-row tile for the others
-                        tiles = int(sum(-(-int(c) // 128) if c >= 32 else 1 for c in counts if c > 0))
-                        passes = tiles
+                        tiles = passes = hybrid_tile_count(counts, sh.I)
                     elif tmode == 0:
                         tiles = int(sum(-(-int(c) // bm) for c in counts))
                         passes = tiles
@@ -273,18 +283,13 @@ def large_leg(torch, m, synth, rows=(713, 4123, 8192, 16384), steps=4, warmup=2,
             out = torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev)
             ws = torch.empty(m.moe_prefill_workspace_bytes(T, sh.top_k, sh.E, sh.H, sh.I, False),
                              dtype=torch.uint8, device=dev)
-            layer = lambda: m.moe_prefill(x, idx, scores, gate, up, down, shared=None, group_size=sh.gs,
-                                          bits=sh.bits, out=out, workspace=ws)
+            layer = lambda i=0: m.moe_prefill(x, idx, scores, gate, up, down, shared=None, group_size=sh.gs,
+                                              bits=sh.bits, out=out, workspace=ws)
             for _ in range(warmup):
                 layer()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(steps):
-                layer()
-            torch.cuda.synchronize()
-            el = (time.perf_counter() - t0) / steps
+            el = graph_time_us(torch, layer, 3, reps=max(1, steps // 2), check=lambda: out) * 1e-6
             flops, nbytes = layer_bytes_flops(sh, T, counts, False)
-            r["layer"] = {"ms": el * 1e3, "gflop": flops / 1e9, "bytes": nbytes,
+            r["layer"] = {"ms": el * 1e3, "timing": "hip graph of 3 layers", "gflop": flops / 1e9, "bytes": nbytes,
                           "mfma_util": flops / el / (MFMA_BF16_PEAK_TFLOPS * 1e12),
                           "hbm_frac": nbytes / el / (HBM_PEAK_GBS * 1e9)}
             res[f"rows{T}_bits{bits}"] = r

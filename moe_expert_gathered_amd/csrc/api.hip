@@ -65,7 +65,29 @@ int64_t big_cap(int64_t P, int64_t E) {
   const int64_t nbig = P / kSmallMax < E ? P / kSmallMax : E;    // experts that can reach kSmallMax rows
   return (P + kBigM - 1) / kBigM + nbig;
 }
-int64_t small_cap(int64_t P, int64_t E) { return P < E ? P : E; }
+// small tiles: at most ceil(c / kSmallMax) per expert, and as many for the extra rows
+int64_t small_cap(int64_t P, int64_t E, int64_t extra = 0) {
+  return P / kSmallMax + (P < E ? P : E) + (extra + kSmallMax - 1) / kSmallMax;
+}
+
+// Hybrid schedule parameters: two tile workgroups fit on each compute unit;
+// the first pass (gate/up) has I / 128 column blocks per row tile.
+int device_slots() {
+  static int slots[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (slots[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    slots[dev] = 2 * cus;
+  }
+  return slots[dev];
+}
+void set_hybrid_model(SortArgs& sa, int64_t I) {
+  sa.small_max = kSmallMax;
+  sa.cost_slots = device_slots();
+  sa.cost_nb = (int)((I + 127) / 128);
+}
 
 // sorted-route workspace layout.  extra: rows of the extra (shared) expert
 // appended after the P sorted rows; layer: also the fp16 activations [T, H],
@@ -88,7 +110,7 @@ SortedWs sorted_layout(char* base, int64_t P, int64_t E, int64_t I, int bm, int6
   w.offsets = (int32_t*)take(4 * (E + 1));
   const int64_t cap = (bm > 0 ? tile_cap(P, E, bm) : big_cap(P, E)) + (extra + kBigM - 1) / kBigM;
   w.tiles = (int32_t*)take(12 * cap);
-  w.small_tiles = (int32_t*)take(12 * small_cap(P, E));
+  w.small_tiles = (int32_t*)take(12 * small_cap(P, E, extra));
   w.n_tiles = (int32_t*)take(8);
   w.bc = (int32_t*)take(4 * sort_blocks(P) * E);
   w.h = (uint16_t*)take(2 * (P + extra) * I);
@@ -448,7 +470,8 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
   sa.counts = ws.counts; sa.offsets = ws.offsets;
   sa.tiles = ws.tiles; sa.n_tiles = ws.n_tiles;
   sa.bm = hybrid ? kBigM : bm; sa.tile_mode = hybrid ? 3 : tile_mode;
-  sa.small_tiles = ws.small_tiles; sa.small_max = kSmallMax;
+  sa.small_tiles = ws.small_tiles;
+  if (hybrid) set_hybrid_model(sa, I);
   sa.block_counts = ws.bc;
   hipError_t e = launch_sort(sa, s);
   if (e != hipSuccess) return MOEGQ_ERR_LAUNCH;
@@ -543,12 +566,14 @@ int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
   sa.order = nullptr; sa.lhs = ws.lhs; sa.sorted_rhs = ws.srhs; sa.inv = inv;
   sa.counts = ws.counts; sa.offsets = ws.offsets;
   sa.tiles = ws.tiles; sa.n_tiles = ws.n_tiles; sa.bm = kBigM; sa.tile_mode = 3;
-  sa.small_tiles = ws.small_tiles; sa.small_max = kSmallMax;
+  sa.small_tiles = ws.small_tiles;
+  set_hybrid_model(sa, I);
   sa.extra_rows = extra; sa.block_counts = ws.bc;
-  if (launch_sort(sa, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-  // fp16 activations and the shared expert's sigmoid gate logit in one pass over x
-  if (launch_prep((const uint16_t*)x, T, (int)H, bits, group_size, ws.x16, shared ? (const uint32_t*)gate_w : nullptr,
-                  (const uint16_t*)gate_s, (const uint16_t*)gate_b, ws.z, s) != hipSuccess)
+  // the sort, and the fp16 activations with the shared expert's sigmoid gate
+  // logit (one pass over x), in one launch when the pairs allow
+  if (launch_front(sa, (const uint16_t*)x, T, (int)H, bits, group_size, ws.x16,
+                   shared ? (const uint32_t*)gate_w : nullptr, (const uint16_t*)gate_s, (const uint16_t*)gate_b, ws.z,
+                   s) != hipSuccess)
     return MOEGQ_ERR_LAUNCH;
   TileArgs g{};
   g.x = ws.x16; g.lhs = ws.lhs; g.lhs_div = 1; g.rows_per_batch = 1;
@@ -568,7 +593,7 @@ int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
   d.N = (int)H; d.K = (int)I; d.out = ws.y;
   // 128-row tiles (hot experts, shared expert) and 32-row tiles (tail experts) in one launch per pass
   g.tiles2 = d.tiles2 = ws.small_tiles; g.n_tiles2 = d.n_tiles2 = ws.n_tiles + 1;
-  g.grid_tiles2 = d.grid_tiles2 = small_cap(P, E);
+  g.grid_tiles2 = d.grid_tiles2 = small_cap(P, E, extra);
   if (launch_tiles_mma_dual(g, bits, group_size, true, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   if (launch_tiles_mma_dual(d, bits, group_size, false, false, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   // out[t] = bf16(bf16(sum_k bf16(y[inv] * score)) + bf16(sigmoid(z[t]) * y[P + t]))

@@ -43,9 +43,13 @@ struct SortArgs {
   int32_t* order; int32_t* lhs; int32_t* sorted_rhs; int32_t* inv;
   int32_t* counts; int32_t* offsets;
   int32_t* tiles; int32_t* n_tiles; int bm; int tile_mode;   // tiles may be null
-  // hybrid schedule (tile_mode 3): experts with >= small_max rows get bm-row
-  // tiles in `tiles`, the others one tile each in `small_tiles`; n_tiles[0..1]
+  // hybrid schedule (tile_mode 3): bm-row tiles in `tiles` for experts with
+  // at least small_max rows, small_max-row tiles in `small_tiles` for the
+  // others (counts in n_tiles[0..1]); when cost_slots > 0 and those bm-row
+  // tiles times cost_nb column blocks come to at most cost_slots / 8 work
+  // items, every expert gets small_max-row tiles instead.
   int32_t* small_tiles; int small_max;
+  int cost_slots; int cost_nb;
   // extra expert E over rows [P, P + extra_rows) (the shared expert, row t = token t):
   // bm-row tiles appended to `tiles`, lhs[P + t] = t
   int64_t extra_rows;
@@ -53,6 +57,8 @@ struct SortArgs {
 };
 int64_t sort_blocks(int64_t P);
 hipError_t launch_sort(const SortArgs& a, hipStream_t st);
+// the scan and scatter launches of the block sort, once a.block_counts holds the block histograms
+hipError_t launch_sort_rest(const SortArgs& a, hipStream_t st);
 hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int tile_mode, int32_t* tiles,
                            int32_t* n_tiles, hipStream_t st);
 
@@ -97,6 +103,10 @@ hipError_t launch_tiles_mma_dual(const TileArgs& a, int bits, int gs, bool glu, 
 // x [T, H] bf16 -> x16 (fp16, chunk order); with gw (a [1, H] quantized row) also z[t] = bf16(x[t] . w)
 hipError_t launch_prep(const uint16_t* x, int64_t T, int H, int bits, int gs, uint16_t* x16, const uint32_t* gw,
                        const uint16_t* gsc, const uint16_t* gbi, uint16_t* z, hipStream_t st);
+// sort (SortArgs) and prep: one launch when the pairs fit one workgroup's
+// sort, else the block sort with prep riding in its count launch
+hipError_t launch_front(const SortArgs& sa, const uint16_t* x, int64_t T, int H, int bits, int gs, uint16_t* x16,
+                        const uint32_t* gw, const uint16_t* gsc, const uint16_t* gbi, uint16_t* z, hipStream_t st);
 
 // combine tail
 // shared (nullable) rows [T, H] are added as they are, or, with z (nullable, [T] bf16), gated first:

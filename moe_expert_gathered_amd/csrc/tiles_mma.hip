@@ -42,6 +42,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "sort_dev.h"
 
 namespace moegq {
 
@@ -359,30 +360,30 @@ __global__ __launch_bounds__(256, 2) void tile_mma_dual_kernel(TileArgs A) {
 // the dequantizer's element order (8-element chunks), and, given the shared
 // expert's one-row sigmoid gate, its logit z[t] = bf16(x[t] . dequant(w)^T)
 // (fp32 dequant and accumulation; MTPLX PR 558 Summary: the gated shared
-// expert).  One workgroup per row.
+// expert).  256 threads per row (tid 0..255); red holds 4 floats; every
+// thread of the block calls this.
 template <int BITS, int GS>
-__global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ x, int H, uint16_t* __restrict__ x16,
-                                                   const uint32_t* __restrict__ gw, const uint16_t* __restrict__ gs_,
-                                                   const uint16_t* __restrict__ gb, uint16_t* __restrict__ z) {
-  __shared__ float red[4];
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + t * (int64_t)H);
-  uint4* xo = reinterpret_cast<uint4*>(x16 + t * (int64_t)H);
+MOEGQ_DEV void prep_row(const uint16_t* __restrict__ x, int64_t T, int H, uint16_t* __restrict__ x16,
+                        const uint32_t* __restrict__ gw, const uint16_t* __restrict__ gs_,
+                        const uint16_t* __restrict__ gb, uint16_t* __restrict__ z, int64_t t, int tid, float* red) {
   float part = 0.f;
-  for (int c = tid; c < H / 8; c += 256) {
-    const uint4 v = xr[c];
-    xo[c] = act_f16<BITS>(v);
-    if (gw) {
-      const int k0 = 8 * c;
-      const float s = bf16_to_f32(gs_[k0 / GS]), b = bf16_to_f32(gb[k0 / GS]);
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-      uint32_t w0 = gw[k0 * BITS / 32], w1 = BITS == 8 ? gw[k0 * BITS / 32 + 1] : 0u;
+  if (t < T) {
+    const uint4* xr = reinterpret_cast<const uint4*>(x + t * (int64_t)H);
+    uint4* xo = reinterpret_cast<uint4*>(x16 + t * (int64_t)H);
+    for (int c = tid; c < H / 8; c += 256) {
+      const uint4 v = xr[c];
+      xo[c] = act_f16<BITS>(v);
+      if (gw) {
+        const int k0 = 8 * c;
+        const float s = bf16_to_f32(gs_[k0 / GS]), b = bf16_to_f32(gb[k0 / GS]);
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        uint32_t w0 = gw[k0 * BITS / 32], w1 = BITS == 8 ? gw[k0 * BITS / 32 + 1] : 0u;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t q = BITS == 4 ? (w0 >> (4 * j)) & 0xFu : ((j < 4 ? w0 : w1) >> (8 * (j & 3))) & 0xFFu;
-        const float xv = (j & 1) ? bf16_hi(d[j >> 1]) : bf16_lo(d[j >> 1]);
-        part = fmaf(xv, fmaf((float)q, s, b), part);
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t q = BITS == 4 ? (w0 >> (4 * j)) & 0xFu : ((j < 4 ? w0 : w1) >> (8 * (j & 3))) & 0xFFu;
+          const float xv = (j & 1) ? bf16_hi(d[j >> 1]) : bf16_lo(d[j >> 1]);
+          part = fmaf(xv, fmaf((float)q, s, b), part);
+        }
       }
     }
   }
@@ -391,7 +392,54 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
   if ((tid & 63) == 0) red[tid >> 6] = part;
   __syncthreads();
-  if (tid == 0) z[t] = f32_to_bf16(red[0] + red[1] + red[2] + red[3]);
+  if (tid == 0 && t < T) z[t] = f32_to_bf16(red[0] + red[1] + red[2] + red[3]);
+}
+
+template <int BITS, int GS>
+__global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ x, int64_t T, int H,
+                                                   uint16_t* __restrict__ x16, const uint32_t* __restrict__ gw,
+                                                   const uint16_t* __restrict__ gs_, const uint16_t* __restrict__ gb,
+                                                   uint16_t* __restrict__ z) {
+  __shared__ float red[4];
+  prep_row<BITS, GS>(x, T, H, x16, gw, gs_, gb, z, blockIdx.x, threadIdx.x, red);
+}
+
+// The front of a prefill layer in one launch (at most SORT_ONE_MAX_P pairs):
+// block 0 sorts the pairs and writes the tile tables, blocks 1 .. prepare four
+// activation rows each.  The two parts touch disjoint memory.
+template <int BITS, int GS>
+__global__ __launch_bounds__(SORT_THREADS) void front_kernel(SortArgs S, const uint16_t* __restrict__ x, int64_t T,
+                                                             int H, uint16_t* __restrict__ x16,
+                                                             const uint32_t* __restrict__ gw,
+                                                             const uint16_t* __restrict__ gs_,
+                                                             const uint16_t* __restrict__ gb, uint16_t* __restrict__ z) {
+  __shared__ float red[16];
+  if (blockIdx.x == 0) {
+    sort_one_block(S);
+    return;
+  }
+  const int sub = threadIdx.x >> 8;
+  prep_row<BITS, GS>(x, T, H, x16, gw, gs_, gb, z, (int64_t)(blockIdx.x - 1) * 4 + sub, threadIdx.x & 255,
+                     red + 4 * sub);
+}
+
+// Above SORT_ONE_MAX_P pairs: blocks 0 .. nb - 1 count the block sort's
+// blocks of pairs, blocks nb .. prepare four activation rows each.
+template <int BITS, int GS>
+__global__ __launch_bounds__(SORT_THREADS) void count_prep_kernel(SortArgs S, int64_t nb, const uint16_t* __restrict__ x,
+                                                                  int64_t T, int H, uint16_t* __restrict__ x16,
+                                                                  const uint32_t* __restrict__ gw,
+                                                                  const uint16_t* __restrict__ gs_,
+                                                                  const uint16_t* __restrict__ gb,
+                                                                  uint16_t* __restrict__ z) {
+  __shared__ float red[16];
+  if ((int64_t)blockIdx.x < nb) {
+    sort_count_block(S.idx, S.P, S.E, S.block_counts, blockIdx.x);
+    return;
+  }
+  const int sub = threadIdx.x >> 8;
+  prep_row<BITS, GS>(x, T, H, x16, gw, gs_, gb, z, ((int64_t)blockIdx.x - nb) * 4 + sub, threadIdx.x & 255,
+                     red + 4 * sub);
 }
 
 template <int BITS, int GS, bool GLU, bool OUT16, int MI>
@@ -457,11 +505,39 @@ hipError_t launch_prep(const uint16_t* x, int64_t T, int H, int bits, int gs, ui
   if (T >= ((int64_t)1 << 31) || H % 8 != 0) return hipErrorInvalidValue;
 #define MOEGQ_PREP(B, G)                                                                                     \
   if (bits == B && gs == G) {                                                                                \
-    hipLaunchKernelGGL((prep_kernel<B, G>), dim3((unsigned)T), dim3(256), 0, st, x, H, x16, gw, gsc, gbi, z); \
+    hipLaunchKernelGGL((prep_kernel<B, G>), dim3((unsigned)T), dim3(256), 0, st, x, T, H, x16, gw, gsc, gbi, z); \
     return hipGetLastError();                                                                                \
   }
   MOEGQ_PREP(4, 32) MOEGQ_PREP(4, 64) MOEGQ_PREP(4, 128) MOEGQ_PREP(8, 32) MOEGQ_PREP(8, 64) MOEGQ_PREP(8, 128)
 #undef MOEGQ_PREP
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_front(const SortArgs& sa, const uint16_t* x, int64_t T, int H, int bits, int gs, uint16_t* x16,
+                        const uint32_t* gw, const uint16_t* gsc, const uint16_t* gbi, uint16_t* z, hipStream_t st) {
+  if (T <= 0 || sa.E <= 0 || sa.E > SORT_MAXE || (!sa.block_counts && sa.P > SORT_ONE_MAX_P)) {
+    const hipError_t e = launch_sort(sa, st);
+    if (e != hipSuccess) return e;
+    return launch_prep(x, T, H, bits, gs, x16, gw, gsc, gbi, z, st);
+  }
+  if (H % 8 != 0 || T >= ((int64_t)1 << 30)) return hipErrorInvalidValue;
+  const bool one = sa.P <= SORT_ONE_MAX_P;
+  const int64_t nb = one ? 1 : sort_blocks(sa.P);
+  const unsigned grid = (unsigned)(nb + (T + 3) / 4);
+#define MOEGQ_FRONT(B, G)                                                                                      \
+  if (bits == B && gs == G) {                                                                                  \
+    if (one)                                                                                                   \
+      hipLaunchKernelGGL((front_kernel<B, G>), dim3(grid), dim3(SORT_THREADS), 0, st, sa, x, T, H, x16, gw, gsc, \
+                         gbi, z);                                                                              \
+    else                                                                                                       \
+      hipLaunchKernelGGL((count_prep_kernel<B, G>), dim3(grid), dim3(SORT_THREADS), 0, st, sa, nb, x, T, H, x16, \
+                         gw, gsc, gbi, z);                                                                     \
+    const hipError_t e = hipGetLastError();                                                                    \
+    if (e != hipSuccess || one) return e;                                                                      \
+    return launch_sort_rest(sa, st);                                                                           \
+  }
+  MOEGQ_FRONT(4, 32) MOEGQ_FRONT(4, 64) MOEGQ_FRONT(4, 128) MOEGQ_FRONT(8, 32) MOEGQ_FRONT(8, 64) MOEGQ_FRONT(8, 128)
+#undef MOEGQ_FRONT
   return hipErrorInvalidValue;
 }
 

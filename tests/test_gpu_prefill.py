@@ -20,8 +20,11 @@ def mg():
     return m
 
 
-SORT_CASES = [(1, 8, 288), (4, 8, 288), (7, 2, 8), (128, 8, 256), (331, 8, 256), (2048, 8, 256),
-              (4123, 8, 288), (3, 4, 1024), (5000, 1, 3), (1, 1, 1)]
+# up to 4096 pairs one workgroup sorts; (512, 8) is that limit, (513, 8) and
+# more take the three-launch block sort
+SORT_CASES = [(1, 8, 288), (4, 8, 288), (7, 2, 8), (128, 8, 256), (331, 8, 256), (512, 8, 256),
+              (513, 8, 256), (2048, 8, 256), (4096, 8, 256), (4123, 8, 288), (3, 4, 1024), (4096, 1, 3),
+              (5000, 1, 3), (1, 1, 1)]
 
 
 @pytest.mark.parametrize("T,top_k,E", SORT_CASES)
@@ -167,12 +170,14 @@ def test_moe_prefill_layer(mg, T, with_shared):
     assert_parity(host_bf(got), want, name=f"layer T={T} shared={with_shared}")
 
 
-def test_moe_prefill_layer_2048_sampled(mg):
-    """The 2048-row layer (hidden 2048, 256 experts, top-8, inter 512, shared
-    expert) on the GPU; the oracle recomputes 48 sampled tokens (a token's
-    output depends only on its own row, experts and scores)."""
+@pytest.mark.parametrize("T", [1024, 2048, 4096])
+def test_moe_prefill_layer_2048_sampled(mg, T):
+    """The 1024-, 2048- and 4096-row layers (hidden 2048, 256 experts, top-8,
+    inter 512, shared expert) on the GPU; the oracle recomputes 48 sampled
+    tokens (a token's output depends only on its own row, experts and scores).
+    Above 512 rows the activation prep rides in the block sort's count
+    launch."""
     sh = synth.PREFILL
-    T = 2048
     idx, scores = synth.zipf_routing(3, T, sh.E, sh.top_k)
     x = synth.activations(3, T, sh.H)
     ex = synth.expert_set(3, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode="words", experts=np.unique(idx))
@@ -181,7 +186,7 @@ def test_moe_prefill_layer_2048_sampled(mg):
                                  shared=tuple(triple(m) for m in shp), group_size=sh.gs, bits=sh.bits))
     sub = np.sort(np.random.default_rng(11).choice(T, 48, replace=False))
     want, _ = oracle.moe_prefill_layer(x[sub], idx[sub], scores[sub], ex, shp, gs=sh.gs, bits=sh.bits)
-    assert_parity(got[sub], want, name="layer 2048 sampled")
+    assert_parity(got[sub], want, name=f"layer {T} sampled")
 
 
 def test_combine_gated_bitwise(mg):
@@ -218,7 +223,7 @@ def test_moe_prefill_repeatable(mg):
 @pytest.mark.parametrize("T", [1, 4, 37])
 def test_moe_prefill_few_tokens(mg, T):
     """The whole-layer entry point with fewer tokens than one tile (every
-    routed expert a few-row tile, the shared expert one partial 128-row tile)."""
+    routed expert and the shared expert in 32-row tiles)."""
     sh, idx, scores, x, ex = _prefill_case(T, sub=7)
     shp = synth.shared_params(3, sh.H, sh.shared_I, sh.gs, sh.bits)
     want, _ = oracle.moe_prefill_layer(x, idx, scores, ex, shp, gs=sh.gs, bits=sh.bits)

@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=42 * 4)
     ap.add_argument("--warmup", type=int, default=42)
     ap.add_argument("--legs", default="decode,prefill,large,dense,cpu")
+    ap.add_argument("--prefill-rows", default="2048,128,512,4096", help="row counts of the prefill leg")
+    ap.add_argument("--large-rows", default="713,4123,8192,16384", help="row counts of the large-prefill leg")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -337,7 +339,12 @@ def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=5, warmup=2,
             torch.cuda.synchronize()
             ts.append(time.perf_counter() - t0)
         med = float(np.median(ts))
-        res[f"rows{M}"] = {"ms_per_forward": med * 1e3, "gbs": per_fwd / med / 1e9}
+        # the same forward captured once as a HIP graph: kernel time without the
+        # per-call host work of ~300 launches from Python
+        g_s = graph_time_us(torch, lambda i: fwd(), 1, reps=reps) * 1e-6
+        res[f"rows{M}"] = {"ms_per_forward": g_s * 1e3, "gbs": per_fwd / g_s / 1e9,
+                           "hbm_frac": per_fwd / g_s / (HBM_PEAK_GBS * 1e9), "timing": "hip graph of one forward",
+                           "eager_ms_per_forward": med * 1e3, "eager_gbs": per_fwd / med / 1e9}
     del sets
     torch.cuda.empty_cache()
     return res
@@ -447,11 +454,13 @@ def main():
         extra["decode_m1_isolated"] = decode_leg(torch, m, synth, 1, a.steps, a.warmup, isolated=True)
         extra["decode_m4_chained"] = decode_leg(torch, m, synth, 4, a.steps, a.warmup)
     if "prefill" in legs:
-        log("prefill 2048 rows (and 128, 512, 4096)")
-        extra["prefill"] = prefill_leg(torch, m, synth)
+        rows = tuple(int(v) for v in a.prefill_rows.split(","))
+        log(f"prefill rows {rows}")
+        extra["prefill"] = prefill_leg(torch, m, synth, rows=rows)
     if "large" in legs:
-        log("large prefill 713 / 4123 / 8192 / 16384 rows")
-        extra["large_prefill"] = large_leg(torch, m, synth)
+        rows = tuple(int(v) for v in a.large_rows.split(","))
+        log(f"large prefill rows {rows}")
+        extra["large_prefill"] = large_leg(torch, m, synth, rows=rows)
     if "dense" in legs:
         log("dense chain")
         extra["dense_chain"] = dense_leg(torch, m, synth)

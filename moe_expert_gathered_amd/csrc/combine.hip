@@ -183,10 +183,68 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const uint16_t* __restric
     out[m * K + k] = f32_to_bf16(bf16_to_f32(xr[k]) * r * bf16_to_f32(w[k]));
 }
 
+// The same arithmetic with 16-byte accesses, the row held in registers
+// between the two passes (K a multiple of 8, K <= 8 * 256 * RV, rows and w
+// 16-byte aligned).  The per-thread sums of squares follow the element order
+// of the scalar kernel's loop only up to regrouping; the block sum is formed
+// the same way.
+template <int RV>
+__global__ __launch_bounds__(256) void rms_norm_vec_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ w, int64_t K, float eps,
+                                                           uint16_t* __restrict__ out) {
+  __shared__ float part[4];
+  const int64_t m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nc = (int)(K / 8);
+  const uint4* xr = reinterpret_cast<const uint4*>(x + m * K);
+  uint4 v[RV];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < RV; ++j) {
+    const int c = tid + 256 * j;
+    v[j] = c < nc ? xr[c] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < RV; ++j) {
+    const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ss = fmaf(bf16_lo(d[i]), bf16_lo(d[i]), ss);
+      ss = fmaf(bf16_hi(d[i]), bf16_hi(d[i]), ss);
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor(ss, off);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float r = 1.0f / sqrtf(tot / (float)K + eps);
+  const uint4* wr = reinterpret_cast<const uint4*>(w);
+  uint4* orow = reinterpret_cast<uint4*>(out + m * K);
+#pragma unroll
+  for (int j = 0; j < RV; ++j) {
+    const int c = tid + 256 * j;
+    if (c >= nc) break;
+    const uint4 wv = wr[c];
+    const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w}, g[4] = {wv.x, wv.y, wv.z, wv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = pack_bf16x2(bf16_lo(d[i]) * r * bf16_lo(g[i]), bf16_hi(d[i]) * r * bf16_hi(g[i]));
+    orow[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t K, float eps,
                            uint16_t* out, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(rms_norm_kernel, dim3((unsigned)M), dim3(256), 0, st, x, w, K, eps, out);
+  const bool vec = K % 8 == 0 && K <= 8 * 256 * 4 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)w & 15) == 0 &&
+                   ((uintptr_t)out & 15) == 0;
+  if (vec && K <= 8 * 256)
+    hipLaunchKernelGGL((rms_norm_vec_kernel<1>), dim3((unsigned)M), dim3(256), 0, st, x, w, K, eps, out);
+  else if (vec)
+    hipLaunchKernelGGL((rms_norm_vec_kernel<4>), dim3((unsigned)M), dim3(256), 0, st, x, w, K, eps, out);
+  else
+    hipLaunchKernelGGL(rms_norm_kernel, dim3((unsigned)M), dim3(256), 0, st, x, w, K, eps, out);
   return hipGetLastError();
 }
 

@@ -59,15 +59,18 @@ MOEGQ_DEV void reduce_wave(float (&a)[V]) {
   for (int i = 0; i < V / 4; ++i) a[i] = row_sum16(a[i]);
 }
 
-// One workgroup is one wave; it owns RPW output rows (two matrices in the GLU
-// variant) of one pair.  Every operand is read through a raw buffer
-// descriptor (one per matrix of the pair's expert, one for the activation
-// row): a lane's offset inside a 256-word slice is a single 32-bit VGPR shared
-// by all rows, the row offsets are scalars, and reads past the matrix or the
-// row return zero.  K is walked in chunks of NS slices; all loads of a chunk
-// (codes, scales, biases, activations) are issued before any arithmetic.
+// One wave owns RPW output rows (two matrices in the GLU variant) of one
+// pair, over the 256-word slices it0, it0 + 1, .. (chunks of NS slices, one
+// chunk every `step` slices from `first`).  Every operand is read through a
+// raw buffer descriptor (one per matrix of the pair's expert, one for the
+// activation row): a lane's offset inside a slice is a single 32-bit VGPR
+// shared by all rows, the row offsets are scalars.  Lanes past the end of a
+// row load with an offset beyond every descriptor's range, so the hardware
+// returns zero without fetching.  All loads of a chunk (codes, scales,
+// biases, activations) are issued before any arithmetic.  acc holds the
+// wave's per-lane partial sums (reduce_wave completes them).
 template <int BITS, int GS, bool GLU, int RPW, int NS, int V = RPW * (GLU ? 2 : 1)>
-MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, float (&acc)[V]) {
+MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first, int step, float (&acc)[V]) {
   constexpr int NM = GLU ? 2 : 1;
   constexpr int XV = BITS == 4 ? 4 : 2;   // uint4 of activations per lane per slice
   const int K = A.K, N = A.N;
@@ -95,7 +98,8 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, float (&a
   const uint32_t C43 = 0x43434343u;
 
   const int n_it = (Kw + 255) / 256;
-  for (int it0 = 0; it0 < n_it; it0 += NS) {
+  constexpr uint32_t kNoFetch = 0x7FFFFFF0u;   // past every descriptor's range
+  for (int it0 = first; it0 < n_it; it0 += step) {
     uint4 c[NS][V], xv[NS][XV];
     uint16_t sv[NS][V], bv[NS][V];
     bool ok[NS];
@@ -110,9 +114,9 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, float (&a
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
           const uint32_t row = (uint32_t)(n0 + r);
-          c[t][m * RPW + r] = buf_load16(rw[m], (uint32_t)wb * 4, row * Kw * 4);
-          sv[t][m * RPW + r] = buf_load2(rs[m], g2, row * G * 2);
-          bv[t][m * RPW + r] = buf_load2(rb[m], g2, row * G * 2);
+          c[t][m * RPW + r] = buf_load16(rw[m], ok[t] ? (uint32_t)wb * 4 : kNoFetch, row * Kw * 4);
+          sv[t][m * RPW + r] = buf_load2(rs[m], ok[t] ? g2 : kNoFetch, row * G * 2);
+          bv[t][m * RPW + r] = buf_load2(rb[m], ok[t] ? g2 : kNoFetch, row * G * 2);
         }
 #pragma unroll
       for (int j = 0; j < XV; ++j) xv[t][j] = buf_load16(rx, (uint32_t)(k0 + 8 * j) * 2, 0);
@@ -178,19 +182,43 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, float (&a
       }
     }
   }
-
-  reduce_wave<V>(acc);
 }
 
-template <int BITS, int GS, bool GLU, int RPW, int NS>
-__global__ __launch_bounds__(64) void qmv_kernel(QmvArgs A, int64_t p_base) {
+// Sum the partial sums of the S waves of the workgroup into wave 0 (S > 1;
+// the other waves return false), then reduce across wave 0's lanes.
+template <int S, int V>
+MOEGQ_DEV bool reduce_waves(float (&acc)[V], int lane, int wave) {
+  if (S > 1) {
+    __shared__ float part[S > 1 ? S - 1 : 1][V][64];
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) part[wave - 1][i][lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave != 0) return false;
+#pragma unroll
+    for (int w = 0; w < S - 1; ++w)
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += part[w][i][lane];
+  }
+  reduce_wave<V>(acc);
+  return true;
+}
+
+// A workgroup of S waves owns RPW output rows of one pair; wave w takes the
+// chunks w, w + S, .. of K (S > 1 when the grid alone would not keep enough
+// loads in flight: few pairs, few rows).
+template <int BITS, int GS, bool GLU, int RPW, int NS, int S>
+__global__ __launch_bounds__(64 * S) void qmv_kernel(QmvArgs A, int64_t p_base) {
   constexpr int V = RPW * (GLU ? 2 : 1);
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * RPW;
   const int64_t p = p_base + blockIdx.y;
   const int N = A.N;
   float acc[V];
-  qmv_rows<BITS, GS, GLU, RPW, NS>(A, p, n0, lane, acc);
+  qmv_rows<BITS, GS, GLU, RPW, NS>(A, p, n0, lane, wave * NS, S * NS, acc);
+  if (!reduce_waves<S>(acc, lane, wave)) return;
   // lane 16*r (r = 2*bit5 + bit4) holds values r*V/4 .. r*V/4 + V/4 - 1
   const int rowg = lane >> 4;
   if (GLU) {
@@ -239,7 +267,8 @@ __global__ __launch_bounds__(512) void qmv_combine_kernel(QmvArgs A, const uint1
   const int N = A.N;
   const int64_t p = t * top_k + k;
   float acc[RPW];
-  qmv_rows<BITS, GS, false, RPW, NS>(A, p, n0, lane, acc);
+  qmv_rows<BITS, GS, false, RPW, NS>(A, p, n0, lane, 0, NS, acc);
+  reduce_wave<RPW>(acc);
   if ((lane & 15) == 0) {
     const int rowg = lane >> 4;
 #pragma unroll
@@ -305,20 +334,43 @@ hipError_t launch_qmv_combine(const QmvArgs& a_in, int bits, int gs, const uint1
   return hipErrorInvalidValue;
 }
 
-template <int BITS, int GS, bool GLU>
-static hipError_t launch_qmv_t(const QmvArgs& a, int64_t P, hipStream_t st) {
-  // rows per wave: 2 (GLU: 4 row streams) or 8; slices per chunk: the whole
-  // row up to 512 words (the decode gate/up), else 1
-  constexpr int RPW = GLU ? 2 : 8;
-  const int Kw = a.K * BITS / 32;
+template <int BITS, int GS, bool GLU, int RPW, int NS, int S>
+static void launch_qmv_cfg(const QmvArgs& a, int64_t P, hipStream_t st) {
   const unsigned nrb = (unsigned)((a.N + RPW - 1) / RPW);
   for (int64_t p0 = 0; p0 < P; p0 += 65535) {
     dim3 grid(nrb, (unsigned)(P - p0 < 65535 ? P - p0 : 65535));
-    if (Kw > 256 && Kw <= 512 && (GLU || BITS == 4))
-      hipLaunchKernelGGL((qmv_kernel<BITS, GS, GLU, RPW, 2>), grid, dim3(64), 0, st, a, p0);
-    else
-      hipLaunchKernelGGL((qmv_kernel<BITS, GS, GLU, RPW, 1>), grid, dim3(64), 0, st, a, p0);
+    hipLaunchKernelGGL((qmv_kernel<BITS, GS, GLU, RPW, NS, S>), grid, dim3(64 * S), 0, st, a, p0);
   }
+}
+
+// Waves in flight wanted for the whole launch: with fewer, each wave's loads
+// are too few to cover the memory latency.
+constexpr int64_t kQmvWaves = 4096;
+
+template <int BITS, int GS, bool GLU>
+static hipError_t launch_qmv_t(const QmvArgs& a, int64_t P, hipStream_t st) {
+  const int Kw = a.K * BITS / 32;
+  const int n_it = (Kw + 255) / 256;
+  const bool two = Kw > 256 && Kw <= 512 && (GLU || BITS == 4);   // the whole row in one chunk of 2 slices
+  if (GLU) {
+    // 2 rows x 2 matrices per wave
+    if (two) launch_qmv_cfg<BITS, GS, true, 2, 2, 1>(a, P, st);
+    else launch_qmv_cfg<BITS, GS, true, 2, 1, 1>(a, P, st);
+    return hipGetLastError();
+  }
+  if ((int64_t)((a.N + 7) / 8) * P >= kQmvWaves) {      // many pairs: 8 rows per wave
+    if (two) launch_qmv_cfg<BITS, GS, false, 8, 2, 1>(a, P, st);
+    else launch_qmv_cfg<BITS, GS, false, 8, 1, 1>(a, P, st);
+    return hipGetLastError();
+  }
+  // few pairs (a dense product): 4 rows per wave, and K split over up to 4
+  // waves of a workgroup
+  const int64_t w4 = (int64_t)((a.N + 3) / 4) * P;
+  int S = 1;
+  while (S < 4 && 2 * S <= n_it && w4 * S < kQmvWaves) S *= 2;
+  if (S == 4) launch_qmv_cfg<BITS, GS, false, 4, 1, 4>(a, P, st);
+  else if (S == 2) launch_qmv_cfg<BITS, GS, false, 4, 1, 2>(a, P, st);
+  else launch_qmv_cfg<BITS, GS, false, 4, 1, 1>(a, P, st);
   return hipGetLastError();
 }
 

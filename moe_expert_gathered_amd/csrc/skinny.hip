@@ -11,19 +11,25 @@
 // dequantized to fp16 (q * s + b with one rounding; nuvec "composed") and the
 // activations converted to fp16 for v_mfma_f32_16x16x32_f16; all 32 codes of
 // a lane share one group.
-// The four waves of a workgroup take interleaved 128-code chunks of K for the
-// same 16 outputs and are summed through LDS at the end.
+// The 4 to 16 waves of a workgroup take interleaved 128-code chunks of K for
+// the same 16 outputs (each with the next chunk's loads in flight) and are
+// summed through LDS at the end.
 #include "common.h"
 #include "launch.h"
 
 namespace moegq {
 
-template <int BITS, int GS, bool GLU>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs A) {
+template <int BITS, int GS, bool GLU, int SK, int CL>
+__global__ __launch_bounds__(64 * SK) void skinny_kernel(SkinnyArgs A) {
+  // CL codes per lane and chunk (32 or 64): a chunk is 4 * CL codes of K
   constexpr int NM = GLU ? 2 : 1;
-  constexpr int BV = BITS / 4;          // uint4 per lane per chunk (32 codes)
-  __shared__ f32x4_t red[3][NM][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int BV = BITS * CL / 128;   // uint4 per lane per chunk
+  constexpr int NG = CL / 32 > 1 && GS < CL ? CL / GS : 1;   // groups per lane and chunk
+  constexpr int ST = CL / 8;            // MFMA steps per chunk
+  constexpr int CK = 4 * CL;            // codes per chunk
+  __shared__ f32x4_t red[SK - 1][NM][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nrb = (A.N + 15) / 16;
   const int64_t p = blockIdx.x / nrb;
   const int n0 = (blockIdx.x % nrb) * 16;
@@ -51,47 +57,65 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs A) {
 #pragma unroll
   for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nchunk = (K + 127) / 128;
-  for (int c = wave; c < nchunk; c += 4) {
-    const int kl = c * 128 + 32 * lj;          // first of this lane's 32 codes
-    const bool ok = kl < K;
+  // one chunk's operands: CL codes per lane and matrix, their groups' scales
+  // and biases, and the matching activations (8-element runs)
+  struct Chunk {
     uint4 cw[NM][BV];
-    float s[NM], b[NM];
+    uint16_t s[NM][NG], b[NM][NG];
+    uint4 xv[ST];
+  };
+  const int nchunk = (K + CK - 1) / CK;
+  auto load = [&](int c, Chunk& d) {
+    const int kl = c * CK + CL * lj;           // first of this lane's CL codes
+    const bool ok = c < nchunk && kl < K;
+    // K is a multiple of 32: each run of 32 codes is all in or all out
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
 #pragma unroll
       for (int v = 0; v < BV; ++v)
-        cw[m][v] = ok ? ld_nt(reinterpret_cast<const uint4*>(wr[m] + kl * BITS / 32 + 4 * v))
-                      : make_uint4(0, 0, 0, 0);
-      s[m] = ok ? bf16_to_f32(sr[m][kl / GS]) : 0.f;
-      b[m] = ok ? bf16_to_f32(br[m][kl / GS]) : 0.f;
-    }
-    // activation operand for the four MFMA steps: step st covers codes
-    // [kl + 8 st, kl + 8 st + 8) of lane group lj
-    f16x8_t xa[4];
+        d.cw[m][v] = (ok && kl + v * (128 / BITS) < K)
+                         ? ldg(reinterpret_cast<const uint4*>(wr[m] + kl * BITS / 32 + 4 * v)) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      uint4 v = (ok && m_ok) ? *reinterpret_cast<const uint4*>(xrow + kl + 8 * st) : make_uint4(0, 0, 0, 0);
-      xa[st] = __builtin_bit_cast(f16x8_t, act_f16<BITS>(v));
-    }
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        uint32_t o[4];
-        const f16x2_t s2 = f16_splat(s[m]), b2 = f16_splat(b[m]);
-        if (BITS == 4) {
-          deq4_f16((&cw[m][0].x)[st], s2, b2, o);
-        } else {
-          deq8_f16((&cw[m][0].x)[2 * st], s2, b2, &o[0]);
-          deq8_f16((&cw[m][0].x)[2 * st + 1], s2, b2, &o[2]);
-        }
-        const f16x8_t bw = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[st], bw, acc[m], 0, 0, 0);
+      for (int gi = 0; gi < NG; ++gi) {
+        d.s[m][gi] = (ok && kl + gi * GS < K) ? sr[m][kl / GS + gi] : (uint16_t)0;
+        d.b[m][gi] = (ok && kl + gi * GS < K) ? br[m][kl / GS + gi] : (uint16_t)0;
       }
     }
+#pragma unroll
+    for (int st = 0; st < ST; ++st)
+      d.xv[st] = (ok && m_ok && kl + 8 * st < K) ? *reinterpret_cast<const uint4*>(xrow + kl + 8 * st)
+                                                 : make_uint4(0, 0, 0, 0);
+  };
+  auto compute = [&](const Chunk& d) {
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      const f16x8_t xa = __builtin_bit_cast(f16x8_t, act_f16<BITS>(d.xv[st]));   // shared by both matrices
+      const int gi = NG > 1 ? (8 * st) / GS : 0;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const f16x2_t s2 = f16_splat(bf16_to_f32(d.s[m][gi])), b2 = f16_splat(bf16_to_f32(d.b[m][gi]));
+        uint32_t o[4];
+        if (BITS == 4) {
+          deq4_f16((&d.cw[m][0].x)[st], s2, b2, o);
+        } else {
+          deq8_f16((&d.cw[m][0].x)[2 * st], s2, b2, &o[0]);
+          deq8_f16((&d.cw[m][0].x)[2 * st + 1], s2, b2, &o[2]);
+        }
+        const f16x8_t bw = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bw, acc[m], 0, 0, 0);
+      }
+    }
+  };
+  // chunk c belongs to wave c % SK; the next chunk's loads are in flight
+  // while the current one is computed
+  Chunk cur, nxt;
+  load(wave, cur);
+  for (int c = wave; c < nchunk; c += SK) {
+    load(c + SK, nxt);
+    compute(cur);
+    cur = nxt;
   }
-  // sum the four waves' partial blocks
+  // sum the waves' partial blocks
   if (wave > 0) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) red[wave - 1][m][lane] = acc[m];
@@ -101,7 +125,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs A) {
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int w = 0; w < 3; ++w) acc[m] += red[w][m][lane];
+    for (int w = 0; w < SK - 1; ++w) acc[m] += red[w][m][lane];
   // C[row = 4*lj + q][col = li]
   const int col = n0 + li;
   if (col >= N) return;
@@ -257,10 +281,25 @@ hipError_t launch_tiles_small(const TileArgs& a, int bits, int gs, bool glu, hip
   return hipErrorInvalidValue;
 }
 
+// Waves per workgroup: 4, or up to 16 when the grid alone would not keep
+// enough loads in flight (a dense product: one pair, few column blocks).
+constexpr int64_t kSkinnyWaves = 4096;
+
 template <int BITS, int GS, bool GLU>
 static hipError_t launch_sk(const SkinnyArgs& a, int64_t P, hipStream_t st) {
+  constexpr int CL = 32;   // 64 codes per lane measured slower at 4 and 16 rows
   const int64_t nrb = (a.N + 15) / 16;
-  hipLaunchKernelGGL((skinny_kernel<BITS, GS, GLU>), dim3((unsigned)(nrb * P)), dim3(256), 0, st, a);
+  const int64_t nblk = nrb * P;
+  if (nblk >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int nchunk = (a.K + 4 * CL - 1) / (4 * CL);
+  int SK = 4;
+  while (SK < 16 && 2 * SK <= nchunk && nblk * SK < kSkinnyWaves) SK *= 2;
+  if (SK == 16)
+    hipLaunchKernelGGL((skinny_kernel<BITS, GS, GLU, 16, CL>), dim3((unsigned)nblk), dim3(1024), 0, st, a);
+  else if (SK == 8)
+    hipLaunchKernelGGL((skinny_kernel<BITS, GS, GLU, 8, CL>), dim3((unsigned)nblk), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((skinny_kernel<BITS, GS, GLU, 4, CL>), dim3((unsigned)nblk), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

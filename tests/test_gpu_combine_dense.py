@@ -100,6 +100,18 @@ def test_affine_qmm_glu(mg, M):
     assert_parity(host_bf(got), want, name=f"glu M={M}")
 
 
+@pytest.mark.parametrize("M,K", [(1, 2560), (4, 4096), (16, 9728), (3, 100), (2, 2048), (5, 8192)])
+def test_rms_norm_paths(mg, M, K):
+    """RMSNorm on the GPU (16-byte path with the row in registers for K a
+    multiple of 8 up to 8192, element path otherwise) against the oracle."""
+    g = np.random.default_rng(70 + K)
+    x = synth.to_bf16(g.standard_normal((M, K)) * 2)
+    w = synth.to_bf16(1 + 0.1 * g.standard_normal(K))
+    want = oracle.rms_norm(x, w, 1e-6)
+    got = host_bf(mg.rms_norm(bf(x), bf(w)))
+    assert_parity(got, want, name=f"rms_norm M={M} K={K}")
+
+
 def test_dense_chain_small(mg):
     """Two layers of the decoder chain (rms_norm, q/k/v, kv feed, o + residual,
     rms_norm, SwiGLU, down + residual) at reduced width, 2 weight sets."""

@@ -132,6 +132,13 @@ MOEGQ_DEV uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t sof
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// the same with the non-temporal cache hint (policy bit 1 on gfx950): for
+// weight streams read once per launch, which then do not push reused lines
+// out of the caches
+MOEGQ_DEV uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 MOEGQ_DEV uint16_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }

@@ -66,7 +66,8 @@ MOEGQ_DEV void reduce_wave(float (&a)[V]) {
 // activation row): a lane's offset inside a slice is a single 32-bit VGPR
 // shared by all rows, the row offsets are scalars.  Lanes past the end of a
 // row load with an offset beyond every descriptor's range, so the hardware
-// returns zero without fetching.  All loads of a chunk (codes, scales,
+// returns zero without fetching.  Codes are loaded with the non-temporal
+// hint: each is read once per launch.  All loads of a chunk (codes, scales,
 // biases, activations) are issued before any arithmetic.  acc holds the
 // wave's per-lane partial sums (reduce_wave completes them).
 template <int BITS, int GS, bool GLU, int RPW, int NS, int V = RPW * (GLU ? 2 : 1)>
@@ -114,7 +115,7 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
           const uint32_t row = (uint32_t)(n0 + r);
-          c[t][m * RPW + r] = buf_load16(rw[m], ok[t] ? (uint32_t)wb * 4 : kNoFetch, row * Kw * 4);
+          c[t][m * RPW + r] = buf_load16_nt(rw[m], ok[t] ? (uint32_t)wb * 4 : kNoFetch, row * Kw * 4);
           sv[t][m * RPW + r] = buf_load2(rs[m], ok[t] ? g2 : kNoFetch, row * G * 2);
           bv[t][m * RPW + r] = buf_load2(rb[m], ok[t] ? g2 : kNoFetch, row * G * 2);
         }

@@ -14,6 +14,8 @@ listed with its justification in the design notes of the repository.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 __all__ = [
@@ -22,7 +24,7 @@ __all__ = [
     "unpack", "dequant", "quantized_matmul", "gather_qmm", "broadcast_gather_indices",
     "silu", "switch_glu", "sort_pairs", "schedule_tiles", "naive_tiles",
     "combine", "unsort", "shared_expert", "rms_norm", "moe_prefill_layer",
-    "dense_forward", "validate_quant_args",
+    "dense_forward", "validate_quant_args", "route",
 ]
 
 # [nuvec] "round_trip_error_is_about_half_a_step": bit widths 1..6 and 8, group
@@ -460,3 +462,35 @@ def dense_forward(h0, sets, layers: int, norm_w, gs: int = 64, bits: int = 4) ->
         d = quantized_matmul(a, *L["dn"], True, gs, bits)
         h = f64_to_bf16(bf16_to_f64(h) + bf16_to_f64(d))
     return h
+
+
+# ----------------------------------------------------------------------------
+# router
+# ----------------------------------------------------------------------------
+def route(logits, top_k: int):
+    """The MoE block's routing from its router logits [T, E] (fp32).
+
+    [MTPLX#558] Change: the fused block computes the routing exactly as the
+    stock block does before the sorted experts and the combine run; the pages
+    do not spell the routing out.
+    READING: the top_k experts with the largest logits (ties to the lower id),
+    stored in ascending expert id; the score of a chosen expert is its softmax
+    probability over all E logits, evaluated in float64 (max-subtracted), not
+    renormalised over the chosen ones, rounded to fp32 and then to bf16.
+    Returns (idx int32 [T, top_k], scores bf16 bits [T, top_k])."""
+    lg = np.asarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    if not 0 < top_k <= E:
+        raise ValueError("top_k must be in 1..E")
+    idx = np.zeros((T, top_k), np.int32)
+    scores = np.zeros((T, top_k), np.uint16)
+    for t in range(T):
+        row = [float(v) for v in lg[t]]
+        chosen = sorted(sorted(range(E), key=lambda e: (-row[e], e))[:top_k])
+        m = max(row)
+        ex = [math.exp(v - m) for v in row]
+        total = math.fsum(ex)
+        for j, e in enumerate(chosen):
+            idx[t, j] = e
+            scores[t, j] = f64_to_bf16(np.float32(ex[e] / total))
+    return idx, scores

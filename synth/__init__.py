@@ -147,16 +147,21 @@ def sorted_topk(cfg: int, M: int, E: int, top_k: int, sub: int = 0) -> np.ndarra
     return np.stack([np.sort(g.choice(E, size=top_k, replace=False)) for _ in range(M)]).astype(np.int32)
 
 
-def zipf_routing(cfg: int, T: int, E: int, top_k: int, zipf: float = 1.1, sub: int = 0):
-    """Router: logits fp32 = N(0,1) + bias_e with bias_e = -zipf * ln(r_e), r a
-    seeded permutation of the ranks 1..E (so expert popularity ~ r^-zipf).
-    Top-k by logit (ties to the lower id); scores = softmax over all E logits
-    (float64) taken at the chosen experts, not renormalised, rounded to bf16.
-    Each token's slots are stored in ascending expert id."""
+def zipf_logits(cfg: int, T: int, E: int, zipf: float = 1.1, sub: int = 0) -> np.ndarray:
+    """Router logits fp32 [T, E] = N(0,1) + bias_e with bias_e = -zipf * ln(r_e),
+    r a seeded permutation of the ranks 1..E (so expert popularity ~ r^-zipf)."""
     g = rng(cfg, 2, sub)
     ranks = g.permutation(E) + 1
     bias = (-zipf * np.log(ranks.astype(np.float64))).astype(np.float32)
-    logits = (g.standard_normal((T, E), dtype=np.float32) + bias[None, :]).astype(np.float32)
+    return (g.standard_normal((T, E), dtype=np.float32) + bias[None, :]).astype(np.float32)
+
+
+def zipf_routing(cfg: int, T: int, E: int, top_k: int, zipf: float = 1.1, sub: int = 0):
+    """Routing inputs from zipf_logits: top-k by logit (ties to the lower id);
+    scores = softmax over all E logits (float64) taken at the chosen experts,
+    not renormalised, rounded to fp32 and then bf16.  Each token's slots are
+    stored in ascending expert id."""
+    logits = zipf_logits(cfg, T, E, zipf, sub)
     order = np.lexsort((np.broadcast_to(np.arange(E), (T, E)), -logits.astype(np.float64)), axis=-1)
     idx = np.sort(order[:, :top_k], axis=-1).astype(np.int32)
     l64 = logits.astype(np.float64)

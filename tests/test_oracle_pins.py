@@ -462,3 +462,58 @@ def test_dense_forward_constant_weights_closed_form():
         a = r(gg / (1 + math.exp(-gg)) * uu)
         dn = r(0.25 * a * 96)
         assert np.array_equal(got[m], oracle.f64_to_bf16(h1 + dn))
+
+
+# ----------------------------------------------------------------------------- router
+def test_route_selection_brute_force():
+    """On tiny inputs the chosen set is the unique size-k subset whose every
+    member beats every non-member (larger logit, or equal logit and lower id),
+    found by enumerating all subsets."""
+    import itertools
+    g = np.random.default_rng(81)
+    for E, k in ((5, 2), (6, 3), (7, 1), (4, 4)):
+        for _ in range(20):
+            lg = g.integers(-3, 4, size=(1, E)).astype(np.float32) * 0.5   # many equal logits
+            beats = lambda a, b: lg[0, a] > lg[0, b] or (lg[0, a] == lg[0, b] and a < b)
+            good = [S for S in itertools.combinations(range(E), k)
+                    if all(beats(a, b) for a in S for b in range(E) if b not in S)]
+            assert len(good) == 1
+            idx, _ = oracle.route(lg, k)
+            assert idx[0].tolist() == list(good[0])
+
+
+def test_route_equal_logits_and_two_expert_closed_form():
+    """All logits equal: the first k ids, each scored 1/E.  Two experts, k = 1:
+    the larger one, scored 1 / (1 + e^-d) with d the logit gap (the logistic
+    function), rounded to fp32 then bf16."""
+    idx, sc = oracle.route(np.full((3, 10), 0.75, np.float32), 4)
+    assert (idx == np.arange(4)).all()
+    assert (sc == bf16_torch(np.float32(0.1))).all()
+    for a, b in ((0.0, 1.0), (2.5, -1.25), (-3.0, -3.5), (7.0, 0.0)):
+        idx, sc = oracle.route(np.array([[a, b]], np.float32), 1)
+        d = abs(np.float64(np.float32(a)) - np.float64(np.float32(b)))
+        assert idx[0, 0] == (0 if a >= b else 1)
+        assert sc[0, 0] == bf16_torch(np.float32(1.0 / (1.0 + math.exp(-d))))[()]
+
+
+def test_route_full_softmax_sums_to_one_and_matches_torch():
+    """k = E: every score is the softmax probability; against torch's float64
+    softmax (library route) after the same fp32 and bf16 roundings, and the
+    unrounded probabilities sum to 1."""
+    g = np.random.default_rng(82)
+    lg = (g.standard_normal((6, 16)) * 3).astype(np.float32)
+    idx, sc = oracle.route(lg, 16)
+    assert (idx == np.arange(16)).all()
+    p = torch.softmax(torch.from_numpy(lg.astype(np.float64)), dim=-1).numpy()
+    assert np.array_equal(sc, bf16_torch(p.astype(np.float32)))
+    assert np.allclose(p.sum(-1), 1.0, atol=1e-12)
+
+
+def test_route_matches_the_input_recipe():
+    """The routing recipe of the synthetic workloads (vectorised numpy) and the
+    oracle's router (per-token loops, exactly summed softmax) agree bit for
+    bit on the prefill shape."""
+    for cfg, T, E, k in ((3, 96, 256, 8), (4, 40, 288, 8)):
+        i1, s1 = synth.zipf_routing(cfg, T, E, k)
+        i2, s2 = oracle.route(synth.zipf_logits(cfg, T, E), k)
+        assert np.array_equal(i1, i2) and np.array_equal(s1, s2)

@@ -207,9 +207,23 @@ def prefill_leg(torch, m, synth, rows=(2048, 128, 512, 4096), steps=20, warmup=5
         torch.cuda.synchronize()
         el_eager = (time.perf_counter() - t0) / steps
         el = graph_time_us(torch, step, 10, reps=max(1, steps // 10), check=lambda: out) * 1e-6
+        # the router on the GPU (fp32 logits of the same routing), alone and in front of the layer
+        logits = torch.from_numpy(synth.zipf_logits(cfg, T, sh.E)).to(dev)
+        ridx = torch.empty((T, sh.top_k), dtype=torch.int32, device=dev)
+        rsc = torch.empty((T, sh.top_k), dtype=torch.bfloat16, device=dev)
+        route = lambda i=0: m.route(logits, sh.top_k, idx=ridx, scores=rsc)
+        route_us = graph_time_us(torch, route, 10, reps=max(1, steps // 10), check=lambda: ridx)
+
+        def step_logits(i=0):
+            route()
+            m.moe_prefill(x, ridx, rsc, gate, up, down, shared=(sg, su, sd, grow), group_size=sh.gs,
+                          bits=sh.bits, out=out, workspace=ws)
+
+        el_logits = graph_time_us(torch, step_logits, 10, reps=max(1, steps // 10), check=lambda: out) * 1e-6
         flops, nbytes = layer_bytes_flops(sh, T, counts, True)
         r = {"rows": T, "active_experts": int((counts > 0).sum()), "max_load": int(counts.max()),
              "ms_per_layer": el * 1e3, "eager_ms_per_layer": el_eager * 1e3, "timing": "hip graph of 10 layers",
+             "router_us": route_us, "ms_per_layer_from_logits": el_logits * 1e3,
              "gflop": flops / 1e9, "bytes": nbytes,
              "mfma_util": flops / el / (MFMA_BF16_PEAK_TFLOPS * 1e12),
              "hbm_frac": nbytes / el / (HBM_PEAK_GBS * 1e9)}

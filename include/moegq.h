@@ -304,6 +304,20 @@ int moegq_schedule_tiles(const int32_t* offsets, int64_t E, int64_t P_max, int b
 int moegq_rms_norm(const void* x, const void* w, int64_t M, int64_t K, float eps, void* out,
                    void* stream);
 
+/*
+ * route: the MoE block's routing from its router logits, which produces the
+ * idx and scores the expert path takes (MTPLX PR 558 Change: the block
+ * computes the routing as the stock block does before the sorted experts and
+ * the combine).  logits [T, E] fp32 row-major (finite).  idx [T, top_k] int32:
+ * the top_k experts by logit, ties to the lower id, stored in ascending expert
+ * id.  scores [T, top_k] bf16: each chosen expert's softmax probability over
+ * all E logits, evaluated in float64 with the largest logit subtracted, not
+ * renormalised, rounded to fp32 and then to bf16.  1 <= E <= 1024 and
+ * 1 <= top_k <= min(E, 64) (else MOEGQ_ERR_SHAPE); T = 0 launches nothing.
+ */
+int moegq_route(const void* logits, int64_t T, int64_t E, int64_t top_k, int32_t* idx, void* scores,
+                void* stream);
+
 /* sigmoid_gate: out = bf16( sigmoid(z[t]) * s[t, :] ), z [T] (stride z_stride) bf16,
  * s [T, H] bf16: the shared expert's sigmoid gate (MTPLX PR 558 Summary). */
 int moegq_sigmoid_gate(const void* s, const void* z, int64_t z_stride, int64_t T, int64_t H,

@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
            "switch_glu", "switch_glu_mode", "moe_decode", "moe_prefill", "moe_prefill_workspace_bytes", "moe_combine", "moe_combine_gated", "moe_combine_unfused", "sort_pairs",
-           "schedule_tiles", "rms_norm", "sigmoid_gate", "kv_feed", "selfcheck",
+           "schedule_tiles", "rms_norm", "sigmoid_gate", "route", "kv_feed", "selfcheck",
            "validate_indices", "workspace_bytes", "MODE_AUTO", "MODE_DECODE", "MODE_SORTED",
            "TILES_SCHEDULED", "TILES_NAIVE"]
 
@@ -72,6 +72,7 @@ _SIGS = {
     "moegq_schedule_tiles": ([_p, _i64, _i64, _int, _int, _p, _i64, _p, _p], _int),
     "moegq_rms_norm": ([_p, _p, _i64, _i64, ctypes.c_float, _p, _p], _int),
     "moegq_sigmoid_gate": ([_p, _p, _i64, _i64, _i64, _p, _p], _int),
+    "moegq_route": ([_p, _i64, _i64, _i64, _p, _p, _p], _int),
     "moegq_kv_feed": ([_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p], _int),
     "moegq_selfcheck": ([_p, _sz, _p], _int),
     "moegq_validate_indices": ([_p, _i64, _i64, _int, _p, _p], _int),
@@ -392,6 +393,22 @@ def schedule_tiles(offsets, E: int, P_max: int, bm: int, tile_mode=TILES_SCHEDUL
     st = lib().moegq_schedule_tiles(_ptr(offsets), E, P_max, bm, tile_mode, _ptr(tiles), cap, _ptr(n), _stream())
     _check(st, "schedule_tiles")
     return tiles, n
+
+
+def route(logits, top_k, idx=None, scores=None):
+    """Router: fp32 logits [T, E] -> (idx int32 [T, top_k], scores bf16 [T, top_k]);
+    top_k by logit (ties to the lower id) in ascending id, float64 softmax scores."""
+    _dev(logits)
+    if logits.dtype != torch.float32:
+        raise MoegqError(-5, "route: logits must be float32")
+    T, E = logits.shape
+    logits = logits.contiguous()
+    if idx is None:
+        idx = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    if scores is None:
+        scores = torch.empty((T, top_k), dtype=torch.bfloat16, device=logits.device)
+    _check(lib().moegq_route(_ptr(logits), T, E, top_k, _ptr(idx), _ptr(scores), _stream()), "route")
+    return idx, scores
 
 
 def rms_norm(x, w, eps=1e-6, out=None):

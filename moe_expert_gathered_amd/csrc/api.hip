@@ -713,6 +713,14 @@ int moegq_rms_norm(const void* x, const void* w, int64_t M, int64_t K, float eps
   return status_of(launch_rms_norm((const uint16_t*)x, (const uint16_t*)w, M, K, eps, (uint16_t*)out, S(stream)));
 }
 
+int moegq_route(const void* logits, int64_t T, int64_t E, int64_t top_k, int32_t* idx, void* scores,
+                void* stream) {
+  if (T < 0 || T > kMaxDim || E < 1 || E > 1024 || top_k < 1 || top_k > E || top_k > 64) return MOEGQ_ERR_SHAPE;
+  if (T == 0) return MOEGQ_OK;
+  if (!logits || !idx || !scores) return MOEGQ_ERR_NULL_ARG;
+  return status_of(launch_route((const float*)logits, T, (int)E, (int)top_k, idx, (uint16_t*)scores, S(stream)));
+}
+
 int moegq_sigmoid_gate(const void* s, const void* z, int64_t z_stride, int64_t T, int64_t H, void* out,
                        void* stream) {
   if (T < 0 || H <= 0 || H % 8 != 0 || z_stride < 1) return MOEGQ_ERR_SHAPE;

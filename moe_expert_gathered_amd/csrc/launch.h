@@ -121,6 +121,9 @@ hipError_t launch_combine_unfused(const uint16_t* y, const int32_t* inv, const u
 // glue
 hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t K, float eps,
                            uint16_t* out, hipStream_t st);
+// router: idx [T, top_k] and bf16 scores from fp32 logits [T, E] (E <= 1024, top_k <= min(E, 64))
+hipError_t launch_route(const float* logits, int64_t T, int E, int top_k, int32_t* idx, uint16_t* scores,
+                        hipStream_t st);
 hipError_t launch_sigmoid_gate(const uint16_t* s, const uint16_t* z, int64_t zs, int64_t T, int64_t H,
                                uint16_t* out, hipStream_t st);
 hipError_t launch_kv_feed(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t M,

@@ -109,6 +109,13 @@ def test_other_entry_points_validate(L):
     assert lay(64, 1024, 128, p, 1 << 30) == -6                                     # I % (8 * 64)
     assert lay(0, 256, 128, None, 0) == 0
     assert L.moegq_moe_combine_gated(p, None, p, None, p, 4, 8, 16, p, None) == -1  # shared required
+    # router
+    assert L.moegq_route(p, 4, 2000, 8, p, p, None) == -4                           # E > 1024
+    assert L.moegq_route(p, 4, 16, 17, p, p, None) == -4                            # top_k > E
+    assert L.moegq_route(p, 4, 256, 65, p, p, None) == -4                           # top_k > 64
+    assert L.moegq_route(p, 4, 256, 0, p, p, None) == -4
+    assert L.moegq_route(None, 4, 256, 8, p, p, None) == -1
+    assert L.moegq_route(None, 0, 256, 8, None, None, None) == 0
 
 
 def test_workspace_sizes(L):

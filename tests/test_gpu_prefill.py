@@ -170,9 +170,9 @@ def test_moe_prefill_layer(mg, T, with_shared):
     assert_parity(host_bf(got), want, name=f"layer T={T} shared={with_shared}")
 
 
-@pytest.mark.parametrize("T", [1024, 2048, 4096])
+@pytest.mark.parametrize("T", [512, 1024, 2048, 4096])
 def test_moe_prefill_layer_2048_sampled(mg, T):
-    """The 1024-, 2048- and 4096-row layers (hidden 2048, 256 experts, top-8,
+    """The 512-, 1024-, 2048- and 4096-row layers (hidden 2048, 256 experts, top-8,
     inter 512, shared expert) on the GPU; the oracle recomputes 48 sampled
     tokens (a token's output depends only on its own row, experts and scores).
     Above 512 rows the activation prep rides in the block sort's count
@@ -246,3 +246,35 @@ def test_moe_prefill_8bit_large_sampled(mg):
     sub = np.sort(np.random.default_rng(13).choice(T, 3, replace=False))
     want, _ = oracle.moe_prefill_layer(x[sub], idx[sub], scores[sub], ex, None, gs=sh.gs, bits=sh.bits)
     assert_parity(got[sub], want, name="layer 8-bit sampled")
+
+
+def _host_experts(trips, uniq):
+    """Host copies (uint32 words, bf16 bits) of the experts `uniq` of device weight triples."""
+    out = []
+    for w, sc, bi in trips:
+        u = torch.from_numpy(uniq.astype(np.int64)).to(w.device)
+        out.append((w.index_select(0, u).cpu().numpy().view(np.uint32),
+                    host_bf(sc.index_select(0, u)), host_bf(bi.index_select(0, u))))
+    return out
+
+
+@pytest.mark.parametrize("T,bits,nsub", [(4123, 4, 3), (8192, 4, 2), (16384, 4, 2), (4123, 8, 2)])
+def test_large_layer_timed_sizes_sampled(mg, T, bits, nsub):
+    """The large layer (hidden 4096, 288 experts, top-8, inter 2048, no shared
+    expert) at the sizes the benchmark times, with the benchmark's weights
+    (drawn on the device): the GPU runs all T rows; the oracle recomputes a few
+    sampled tokens from host copies of the experts they use."""
+    sh = synth.LARGE4 if bits == 4 else synth.LARGE8
+    dev = torch.device("cuda")
+    ex = synth.device_expert_set(dev, 4, sh.E, sh.H, sh.I, sh.gs, sh.bits)
+    idx, scores = synth.zipf_routing(4, T, sh.E, sh.top_k)
+    x = synth.activations(4, T, sh.H)
+    got = host_bf(mg.moe_prefill(bf(x), i32(idx), bf(scores), *ex, shared=None, group_size=sh.gs, bits=sh.bits))
+    sub = np.sort(np.random.default_rng(T + bits).choice(T, nsub, replace=False))
+    uniq = np.unique(idx[sub])
+    local = np.searchsorted(uniq, idx[sub]).astype(np.int32)       # ascending ids stay ascending
+    want, _ = oracle.moe_prefill_layer(x[sub], local, scores[sub], _host_experts(ex, uniq), None,
+                                       gs=sh.gs, bits=sh.bits)
+    del ex
+    torch.cuda.empty_cache()
+    assert_parity(got[sub], want, name=f"large layer T={T} bits={bits}")

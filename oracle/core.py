@@ -24,7 +24,7 @@ __all__ = [
     "unpack", "dequant", "quantized_matmul", "gather_qmm", "broadcast_gather_indices",
     "silu", "switch_glu", "sort_pairs", "schedule_tiles", "naive_tiles",
     "combine", "unsort", "shared_expert", "rms_norm", "moe_prefill_layer",
-    "dense_forward", "validate_quant_args", "route",
+    "dense_forward", "validate_quant_args", "route", "gather_mm", "switch_glu_mm",
 ]
 
 # [nuvec] "round_trip_error_is_about_half_a_step": bit widths 1..6 and 8, group
@@ -494,3 +494,52 @@ def route(logits, top_k: int):
             idx[t, j] = e
             scores[t, j] = f64_to_bf16(np.float32(ex[e] / total))
     return idx, scores
+
+
+# ----------------------------------------------------------------------------
+# unquantized gather_mm
+# ----------------------------------------------------------------------------
+def gather_mm(x, w, lhs=None, rhs=None) -> np.ndarray:
+    """out[j] = bf16( x[lhs[j]] . w[rhs[j]]^T ), float64 accumulation, for every
+    j of the broadcast index shape; output shape = index shape + [M, N].
+
+    [MLX#4567] (title, Proposed changes): gather_mm, the matrix product of the
+    selected activation batch and the selected expert matrix, is the operation
+    the expert-aware tile schedule speeds up.
+    READING: the expert matrices are stored as a linear layer's weights, w [E, N, K]
+    bf16 (the product takes their transpose), the layout of the quantized path.
+    x [X, M, K] bf16; indices as in gather_qmm."""
+    x = np.asarray(x, dtype=np.uint16)
+    w = np.asarray(w, dtype=np.uint16)
+    li, ri, shape = broadcast_gather_indices(x.shape[:-2], w.shape[:-2], lhs, rhs)
+    M, N = x.shape[-2], w.shape[-2]
+    xf = bf16_to_f64(x.reshape((-1,) + x.shape[-2:]))
+    wf = w.reshape((-1,) + w.shape[-2:])
+    out = np.zeros((len(li), M, N), dtype=np.uint16)
+    cache = {}
+    for j, (l, r) in enumerate(zip(li, ri)):
+        if r not in cache:
+            cache = {r: bf16_to_f64(wf[r])}
+        out[j] = f64_to_bf16(xf[l] @ cache[r].T)
+    return out.reshape(tuple(shape) + (M, N))
+
+
+def switch_glu_mm(x, idx, gate, up, down) -> np.ndarray:
+    """SwitchGLU on unquantized bf16 experts [E, N, K]: for every (token, slot)
+    u = bf16(x w_up^T), g = bf16(x w_gate^T), h = bf16(silu(g) u),
+    y = bf16(h w_down^T); returns y [T, top_k, H].
+    [MLX#4509] SwitchGLU order (up, gate, silu(gate) * up, down)."""
+    idx = np.asarray(idx)
+    T, top_k = idx.shape
+    x = np.asarray(x, dtype=np.uint16)
+    H = np.asarray(down).shape[1]
+    y = np.zeros((T, top_k, H), dtype=np.uint16)
+    for e in np.unique(idx):
+        toks, slots = np.nonzero(idx == e)
+        xe = bf16_to_f64(x[toks])
+        g = f64_to_bf16(xe @ bf16_to_f64(np.asarray(gate)[e]).T)
+        u = f64_to_bf16(xe @ bf16_to_f64(np.asarray(up)[e]).T)
+        gf = bf16_to_f64(g)
+        h = f64_to_bf16(silu(gf) * bf16_to_f64(u))
+        y[toks, slots] = f64_to_bf16(bf16_to_f64(h) @ bf16_to_f64(np.asarray(down)[e]).T)
+    return y

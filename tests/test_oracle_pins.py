@@ -517,3 +517,61 @@ def test_route_matches_the_input_recipe():
         i1, s1 = synth.zipf_routing(cfg, T, E, k)
         i2, s2 = oracle.route(synth.zipf_logits(cfg, T, E), k)
         assert np.array_equal(i1, i2) and np.array_equal(s1, s2)
+
+
+# ----------------------------------------------------------------------------- unquantized gather_mm
+def test_gather_mm_brute_force_exact():
+    """Tiny gather_mm against exact rational sums (Python loops, Fractions) of
+    bf16 inputs, rounded once: every selected pair, every broadcast form."""
+    g = np.random.default_rng(83)
+    x = synth.to_bf16(g.standard_normal((3, 2, 5)).astype(np.float32))
+    w = synth.to_bf16(g.standard_normal((4, 3, 5)).astype(np.float32))
+    lhs = np.array([0, 2, 2, 1]); rhs = np.array([3, 0, 1, 3])
+    got = oracle.gather_mm(x, w, lhs=lhs, rhs=rhs)
+    xv, wv = oracle.bf16_to_f64(x), oracle.bf16_to_f64(w)
+    for j in range(4):
+        for m in range(2):
+            for n in range(3):
+                exact = sum(Fraction(float(xv[lhs[j], m, k])) * Fraction(float(wv[rhs[j], n, k])) for k in range(5))
+                assert got[j, m, n] == oracle.f64_to_bf16(float(exact))
+    # defaults: batch j of x against expert j when the batch shapes agree
+    assert np.array_equal(oracle.gather_mm(x[:1], w[3:4])[0], got[0])
+
+
+def test_gather_mm_rank_one_closed_form():
+    """w_e = u_e v_e^T with small integers: out = (x . v_e) u_e, formed as a
+    dot product first and a scaling second (all exact)."""
+    g = np.random.default_rng(84)
+    E, N, K, M = 3, 6, 16, 4
+    u = g.integers(-3, 4, size=(E, N)).astype(np.float64)
+    v = g.integers(-3, 4, size=(E, K)).astype(np.float64)
+    w = oracle.f64_to_bf16(u[:, :, None] * v[:, None, :])
+    x = oracle.f64_to_bf16(g.integers(-4, 5, size=(2, M, K)).astype(np.float64))
+    rhs = np.array([2, 0, 1, 2, 1]); lhs = np.array([0, 1, 1, 0, 0])
+    got = oracle.gather_mm(x, w, lhs=lhs, rhs=rhs)
+    xv = oracle.bf16_to_f64(x)
+    for j in range(len(rhs)):
+        d = xv[lhs[j]] @ v[rhs[j]]
+        want = oracle.f64_to_bf16(d[:, None] * u[rhs[j]][None, :])
+        assert np.array_equal(oracle.bf16_to_f64(got[j]), oracle.bf16_to_f64(want))   # -0 == +0
+
+
+def test_switch_glu_mm_matches_torch():
+    """Unquantized SwitchGLU against torch's float64 matmul and SiLU (library
+    route), with the same bf16 rounding points."""
+    g = np.random.default_rng(85)
+    E, H, I, T, k = 5, 32, 16, 6, 2
+    mk = lambda *s: synth.to_bf16((g.standard_normal(s) * 0.3).astype(np.float32))
+    gate, up, down = mk(E, I, H), mk(E, I, H), mk(E, H, I)
+    x = mk(T, H)
+    idx = np.stack([np.sort(g.choice(E, k, replace=False)) for _ in range(T)])
+    got = oracle.switch_glu_mm(x, idx, gate, up, down)
+    tb = lambda a: torch.from_numpy(oracle.bf16_to_f64(a))
+    for t in range(T):
+        for s_ in range(k):
+            e = idx[t, s_]
+            gg = tb(oracle.f64_to_bf16((tb(x[t]) @ tb(gate[e]).T).numpy()))
+            uu = tb(oracle.f64_to_bf16((tb(x[t]) @ tb(up[e]).T).numpy()))
+            hh = tb(oracle.f64_to_bf16((torch.nn.functional.silu(gg) * uu).numpy()))
+            yy = oracle.f64_to_bf16((hh @ tb(down[e]).T).numpy())
+            assert np.array_equal(got[t, s_], yy)

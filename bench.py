@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=42 * 4)
     ap.add_argument("--warmup", type=int, default=42)
-    ap.add_argument("--legs", default="decode,prefill,large,dense,cpu")
+    ap.add_argument("--legs", default="decode,prefill,large,gather_mm,dense,cpu")
     ap.add_argument("--prefill-rows", default="2048,128,512,4096", help="row counts of the prefill leg")
     ap.add_argument("--large-rows", default="713,4123,8192,16384", help="row counts of the large-prefill leg")
     ap.add_argument("--quiet", action="store_true")
@@ -315,6 +315,51 @@ def large_leg(torch, m, synth, rows=(713, 4123, 8192, 16384), steps=4, warmup=2,
     return res
 
 
+# ----------------------------------------------------------------------------- unquantized gather_mm
+def gather_mm_leg(torch, m, synth, steps=20):
+    """Unquantized bf16 gather_mm on the expert-sorted route (the operation
+    the expert-aware schedule was designed for): 2048 tokens, top-8 of 256
+    experts, N 512, K 2048 (the prefill shape's gate projection), pairs sorted
+    by expert, 64-row scheduled tiles on the matrix cores; and one decode token
+    (8 pairs, N 2048, K 4096) on the one-row path.  HIP-graph replays."""
+    dev = torch.device("cuda")
+    res = {}
+    T, E, N, K, top_k = 2048, 256, 512, 2048, 8
+    g = synth.device_generator(dev, 6, 0)
+    w = (torch.randn((E, N, K), device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    idx_np, _ = synth.zipf_routing(3, T, E, top_k)
+    flat = idx_np.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    srhs = torch.from_numpy(flat[order].astype(np.int32)).to(dev)
+    lhs = torch.from_numpy((order // top_k).astype(np.int32)).to(dev)
+    x = torch.randn((T, K), device=dev, generator=g).to(torch.bfloat16)
+    P = T * top_k
+    out = torch.empty((P, N), dtype=torch.bfloat16, device=dev)
+    fn = lambda i=0: m.gather_mm(x, w, srhs, lhs_indices=lhs, sorted_indices=True, out=out)
+    us = graph_time_us(torch, fn, 10, reps=max(1, steps // 10), check=lambda: out)
+    active = int(np.unique(flat).size)
+    flops = 2.0 * P * N * K
+    nbytes = active * N * K * 2 + T * K * 2 + P * N * 2
+    res["sorted_2048x8_e256_n512_k2048"] = {
+        "us": us, "tflops": flops / us / 1e6, "mfma_util": flops / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+        "hbm_frac": nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), "active_experts": active, "pairs": P}
+    del w
+    # one decode token: 8 pairs over [288, 2048, 4096] bf16 experts
+    E2, N2, K2 = 288, 2048, 4096
+    w2 = (torch.randn((E2, N2, K2), device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    sets = [torch.from_numpy(synth.sorted_topk(1, 1, E2, 8, sub=i).reshape(-1)).to(dev) for i in range(42)]
+    x2 = torch.randn((1, K2), device=dev, generator=g).to(torch.bfloat16)
+    out2 = torch.empty((8, N2), dtype=torch.bfloat16, device=dev)
+    fn2 = lambda i=0: m.gather_mm(x2, w2, sets[i % 42], lhs_div=8, out=out2)
+    us2 = graph_time_us(torch, fn2, 42, reps=max(1, steps // 10), check=lambda: out2)
+    b2 = 8 * N2 * K2 * 2
+    res["decode_1tok_8pairs_n2048_k4096"] = {"us": us2, "gbs": b2 / us2 / 1e3,
+                                             "hbm_frac": b2 / (us2 * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+    del w2
+    torch.cuda.empty_cache()
+    return res
+
+
 # ----------------------------------------------------------------------------- dense chain
 def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=5, warmup=2, cfg=2):
     dev = torch.device("cuda")
@@ -475,6 +520,9 @@ def main():
         rows = tuple(int(v) for v in a.large_rows.split(","))
         log(f"large prefill rows {rows}")
         extra["large_prefill"] = large_leg(torch, m, synth, rows=rows)
+    if "gather_mm" in legs:
+        log("unquantized gather_mm")
+        extra["gather_mm"] = gather_mm_leg(torch, m, synth)
     if "dense" in legs:
         log("dense chain")
         extra["dense_chain"] = dense_leg(torch, m, synth)

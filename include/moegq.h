@@ -67,7 +67,7 @@ enum { MOEGQ_TILES_SCHEDULED = 0, MOEGQ_TILES_NAIVE = 1 };
 /* operations whose workspace can be queried */
 enum { MOEGQ_OP_GATHER_QMM = 0, MOEGQ_OP_SWITCH_GLU_DECODE = 1, MOEGQ_OP_SWITCH_GLU_SORTED = 2,
        MOEGQ_OP_COMBINE_UNFUSED = 3, MOEGQ_OP_SELFCHECK = 4, MOEGQ_OP_SORT_PAIRS = 5,
-       MOEGQ_OP_MOE_DECODE = 6 };
+       MOEGQ_OP_MOE_DECODE = 6, MOEGQ_OP_GATHER_MM = 7 };
 
 const char* moegq_status_string(int status);
 const char* moegq_version(void);
@@ -303,6 +303,25 @@ int moegq_schedule_tiles(const int32_t* offsets, int64_t E, int64_t P_max, int b
  * (MLX PR 4787 benchmark script, mx.fast.rms_norm). */
 int moegq_rms_norm(const void* x, const void* w, int64_t M, int64_t K, float eps, void* out,
                    void* stream);
+
+/*
+ * gather_mm: out[j] = bf16( x[lhs[j]] . w[rhs[j]]^T ) with unquantized bf16
+ * expert matrices (MLX PR 4567, "[Metal] Gather mm improvement": the
+ * expert-aware row-tile schedule is built for this operation).  x [X, M, K]
+ * bf16; w [E, N, K] bf16 (a linear layer's weights; the product takes their
+ * transpose); lhs_indices [P] int32 or NULL (then the x batch of pair j is
+ * j / lhs_div); rhs_indices [P] int32 expert ids; out [P, M, N] bf16 in pair
+ * order.  sorted_indices = 1 promises rhs ascending: with M = 1, P >= 64 and
+ * K a multiple of 128 the pairs run as per-expert 64-row tiles on the matrix
+ * cores (one K pass per tile).  M = 1 otherwise: one pass per pair over its
+ * expert's rows.  M > 1: per-pair tiles on the matrix cores (K a multiple of
+ * 128, else MOEGQ_ERR_UNSUPPORTED).  K must be a multiple of 8; N * K and
+ * X * M * K below 2^31.  workspace: moegq_workspace_bytes(MOEGQ_OP_GATHER_MM,
+ * P, E, M, 0) bytes.
+ */
+int moegq_gather_mm(const void* x, int64_t X, int64_t M, int64_t K, const void* w, int64_t E, int64_t N,
+                    const int32_t* lhs_indices, int64_t lhs_div, const int32_t* rhs_indices, int64_t P,
+                    int sorted_indices, void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * route: the MoE block's routing from its router logits, which produces the

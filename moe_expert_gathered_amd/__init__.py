@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
            "switch_glu", "switch_glu_mode", "moe_decode", "moe_prefill", "moe_prefill_workspace_bytes", "moe_combine", "moe_combine_gated", "moe_combine_unfused", "sort_pairs",
-           "schedule_tiles", "rms_norm", "sigmoid_gate", "route", "kv_feed", "selfcheck",
+           "schedule_tiles", "rms_norm", "sigmoid_gate", "route", "gather_mm", "kv_feed", "selfcheck",
            "validate_indices", "workspace_bytes", "MODE_AUTO", "MODE_DECODE", "MODE_SORTED",
            "TILES_SCHEDULED", "TILES_NAIVE"]
 
@@ -30,7 +30,7 @@ BF16, F16, F32, F64, I32, U32, I64 = range(7)
 MODE_AUTO, MODE_DECODE, MODE_SORTED = 0, 1, 2
 TILES_SCHEDULED, TILES_NAIVE = 0, 1
 OP_GATHER_QMM, OP_SWITCH_GLU_DECODE, OP_SWITCH_GLU_SORTED, OP_COMBINE_UNFUSED, OP_SELFCHECK, OP_SORT_PAIRS, \
-    OP_MOE_DECODE = range(7)
+    OP_MOE_DECODE, OP_GATHER_MM = range(8)
 
 _DTYPE = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.float64: F64,
           torch.int32: I32, torch.int64: I64}
@@ -73,6 +73,7 @@ _SIGS = {
     "moegq_rms_norm": ([_p, _p, _i64, _i64, ctypes.c_float, _p, _p], _int),
     "moegq_sigmoid_gate": ([_p, _p, _i64, _i64, _i64, _p, _p], _int),
     "moegq_route": ([_p, _i64, _i64, _i64, _p, _p, _p], _int),
+    "moegq_gather_mm": ([_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _p, _sz, _p], _int),
     "moegq_kv_feed": ([_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p], _int),
     "moegq_selfcheck": ([_p, _sz, _p], _int),
     "moegq_validate_indices": ([_p, _i64, _i64, _int, _p, _p], _int),
@@ -198,6 +199,25 @@ def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, transpo
                                 _ptr(li), lhs_div, _ptr(ri), idx_dt, P, int(bool(sorted_indices)),
                                 int(bool(transpose)), group_size, bits, _ptr(out), _ptr(ws), wsb, _stream())
     _check(st, "gather_qmm")
+    return out
+
+
+def gather_mm(x, w, rhs_indices, lhs_indices=None, lhs_div=1, sorted_indices=False, out=None):
+    """out[p] = x[row(p)] . w[rhs[p]]^T with unquantized bf16 experts.
+    x: [X, M, K] (or [X, K] for M = 1) bf16; w: [E, N, K] bf16; rhs_indices [P]
+    int32; the x batch of pair p is lhs_indices[p], or p // lhs_div.
+    Returns [P, M, N] (M = 1: [P, N])."""
+    _dev(x, w, rhs_indices, lhs_indices)
+    squeeze = x.dim() == 2
+    X, M, K = (x.shape[0], 1, x.shape[1]) if squeeze else tuple(x.shape)
+    E, N = w.shape[0], w.shape[1]
+    P = int(rhs_indices.numel())
+    if out is None:
+        out = torch.empty((P, N) if squeeze else (P, M, N), dtype=torch.bfloat16, device=x.device)
+    ws, wsb = _workspace(workspace_bytes(OP_GATHER_MM, P, E, M, 0), x.device)
+    st = lib().moegq_gather_mm(_ptr(x), X, M, K, _ptr(w), E, N, _ptr(lhs_indices), lhs_div, _ptr(rhs_indices), P,
+                               int(bool(sorted_indices)), _ptr(out), _ptr(ws), wsb, _stream())
+    _check(st, "gather_mm")
     return out
 
 

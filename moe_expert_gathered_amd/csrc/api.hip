@@ -183,6 +183,12 @@ size_t moegq_workspace_bytes(int op, int64_t P, int64_t E, int64_t N, int bm) {
       if (M == 1) return align256(4 * (E + 1)) + align256(12 * tile_cap(P, E, 16)) + 256;
       return 0;
     }
+    case MOEGQ_OP_GATHER_MM: {
+      // N carries M: M == 1 sorted: offsets + tiles; M > 1: the per-pair tile table
+      const int64_t M = N;
+      if (M > 1) return align256(12 * (P * ((M + 63) / 64))) + 256;
+      return align256(4 * (E + 1)) + align256(12 * tile_cap(P, E, 16)) + 256;
+    }
     case MOEGQ_OP_SWITCH_GLU_DECODE: return align256(2 * P * N);
     case MOEGQ_OP_SWITCH_GLU_SORTED: {
       const size_t a = sorted_layout(nullptr, P, E, N, bm).bytes;
@@ -711,6 +717,57 @@ int moegq_rms_norm(const void* x, const void* w, int64_t M, int64_t K, float eps
   if (M == 0) return MOEGQ_OK;
   if (!x || !w || !out) return MOEGQ_ERR_NULL_ARG;
   return status_of(launch_rms_norm((const uint16_t*)x, (const uint16_t*)w, M, K, eps, (uint16_t*)out, S(stream)));
+}
+
+int moegq_gather_mm(const void* x, int64_t X, int64_t M, int64_t K, const void* w, int64_t E, int64_t N,
+                    const int32_t* lhs_indices, int64_t lhs_div, const int32_t* rhs_indices, int64_t P,
+                    int sorted_indices, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (X < 0 || M < 0 || K <= 0 || E <= 0 || N < 0 || P < 0 || X > kMaxDim || N > kMaxDim || P > kMaxDim ||
+      K > kMaxDim || K % 8 != 0)
+    return MOEGQ_ERR_SHAPE;
+  if (!lhs_indices && lhs_div < 1) return MOEGQ_ERR_SHAPE;
+  if (P == 0 || M == 0 || N == 0) return MOEGQ_OK;
+  if (!x || !w || !rhs_indices || !out) return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return MOEGQ_ERR_ALIGN;
+  if (!lhs_indices && (P - 1) / lhs_div >= X) return MOEGQ_ERR_SHAPE;
+  if (N * K >= ((int64_t)1 << 31) || X * M * K >= ((int64_t)1 << 31)) return MOEGQ_ERR_UNSUPPORTED;
+  hipStream_t s = S(stream);
+  const size_t need = moegq_workspace_bytes(MOEGQ_OP_GATHER_MM, P, E, M, 0);
+  TileArgs a{};
+  a.x = (const uint16_t*)x; a.lhs = lhs_indices; a.lhs_div = lhs_div; a.rows_per_batch = 1;
+  a.E = (int)E; a.w0 = (const uint32_t*)w; a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out;
+  a.tile_mode = 0;
+  if (M == 1 && sorted_indices && P >= 64 && E <= kMaxExperts && K % 128 == 0) {
+    // pairs already sorted by expert: per-expert offsets, the expert-aware schedule at
+    // BM 64, one K pass per tile on the matrix cores
+    if (!workspace || workspace_bytes < need) return MOEGQ_ERR_WORKSPACE;
+    char* base = (char*)workspace;
+    int32_t* offsets = (int32_t*)base;
+    int32_t* tiles = (int32_t*)(base + align256(4 * (E + 1)));
+    int32_t* n_tiles = (int32_t*)(base + align256(4 * (E + 1)) + align256(12 * tile_cap(P, E, 16)));
+    hipLaunchKernelGGL(offsets_from_sorted_kernel, dim3((unsigned)((E + 1 + 255) / 256)), dim3(256), 0, s,
+                       rhs_indices, P, (int)E, offsets);
+    if (launch_schedule(offsets, (int)E, 64, 0, tiles, n_tiles, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    a.tiles = tiles; a.n_tiles = n_tiles; a.P = P; a.bm = 64; a.grid_tiles = tile_cap(P, E, 64);
+    return status_of(launch_tiles_mma_w16(a, false, 64, s));
+  }
+  if (M == 1) {
+    QmvArgs q{};
+    q.x = (const uint16_t*)x; q.lhs = lhs_indices; q.lhs_div = lhs_div; q.rhs = rhs_indices;
+    q.w0 = (const uint32_t*)w; q.N = (int)N; q.K = (int)K; q.out = (uint16_t*)out;
+    return status_of(launch_mv16(q, P, s));
+  }
+  // M > 1: per-pair tiles of up to 64 virtual rows (pair-major)
+  if (K % 128 != 0) return MOEGQ_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < need) return MOEGQ_ERR_WORKSPACE;
+  const int bm = 64;
+  const int64_t nt = P * ((M + bm - 1) / bm);
+  int32_t* tiles = (int32_t*)workspace;
+  int32_t* n_tiles = (int32_t*)((char*)workspace + align256(12 * nt));
+  hipLaunchKernelGGL(pair_tiles_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, rhs_indices, P, (int)M,
+                     bm, tiles, n_tiles);
+  a.rows_per_batch = M; a.tiles = tiles; a.n_tiles = n_tiles; a.P = P * M; a.bm = bm; a.grid_tiles = nt;
+  return status_of(launch_tiles_mma_w16(a, false, 64, s));
 }
 
 int moegq_route(const void* logits, int64_t T, int64_t E, int64_t top_k, int32_t* idx, void* scores,

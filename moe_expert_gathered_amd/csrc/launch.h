@@ -19,6 +19,8 @@ struct QmvArgs {
   const uint16_t* residual; // null or [P, N]
 };
 hipError_t launch_qmv(const QmvArgs& a, int bits, int gs, bool glu, int64_t P, hipStream_t st);
+// unquantized bf16 expert rows [E, N, K] (a.w0), one activation row per pair; K % 8 == 0
+hipError_t launch_mv16(const QmvArgs& a, int64_t P, hipStream_t st);
 // decode down projection + combine: out[t] from pairs t*top_k .. t*top_k + top_k - 1
 // (a.out, if not null, also receives y [T*top_k, N]); top_k <= 8
 hipError_t launch_qmv_combine(const QmvArgs& a, int bits, int gs, const uint16_t* scores, const uint16_t* shared,
@@ -99,6 +101,8 @@ bool tiles_mma_supported(int64_t K, int64_t N, int64_t src_rows, int gs);
 hipError_t launch_tiles_mma(const TileArgs& a, int bits, int gs, bool glu, bool out16, int rows,
                             hipStream_t st);
 // both tables in one launch: `tiles` (up to 128 rows, n_tiles) and `tiles2` (up to 32 rows, n_tiles2)
+// bf16 expert matrices as the first MFMA operand (no dequantization): rows 64 or 32 (one table), 0 (both)
+hipError_t launch_tiles_mma_w16(const TileArgs& a, bool glu, int rows, hipStream_t st);
 hipError_t launch_tiles_mma_dual(const TileArgs& a, int bits, int gs, bool glu, bool out16, hipStream_t st);
 // x [T, H] bf16 -> x16 (fp16, chunk order); with gw (a [1, H] quantized row) also z[t] = bf16(x[t] . w)
 hipError_t launch_prep(const uint16_t* x, int64_t T, int H, int bits, int gs, uint16_t* x16, const uint32_t* gw,

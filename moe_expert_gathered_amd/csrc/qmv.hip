@@ -249,6 +249,63 @@ __global__ __launch_bounds__(64 * S) void qmv_kernel(QmvArgs A, int64_t p_base) 
   }
 }
 
+// Unquantized bf16 expert rows (gather_mm with one activation row per pair):
+// a wave owns 4 output rows of one pair and walks K in chunks of 512 (a lane
+// takes 8 consecutive elements: one 16-byte load per row and one of x),
+// accumulating with v_dot2_f32_bf16; then reduce_wave.  Rows past N repeat
+// the last row (never stored); lanes past K load nothing.
+__global__ __launch_bounds__(64) void mv16_kernel(QmvArgs A, int64_t p_base) {
+  constexpr int RPW = 4;
+  const int lane = threadIdx.x;
+  const int n0 = blockIdx.x * RPW;
+  const int64_t p = p_base + blockIdx.y;
+  const int K = A.K, N = A.N;
+  const int64_t xrow = A.lhs ? (int64_t)A.lhs[p] : p / A.lhs_div;
+  const int64_t e = A.rhs ? (int64_t)A.rhs[p] : 0;
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(A.w0) + e * (int64_t)N * K;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (uint32_t)N * (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(A.x + xrow * (int64_t)K, (uint32_t)K * 2u);
+  constexpr uint32_t kNoFetch = 0x7FFFFFF0u;
+  uint32_t soff[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) soff[r] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K * 2u;
+  float acc[RPW] = {0.f, 0.f, 0.f, 0.f};
+  const int nchunk = (K + 511) / 512;
+#pragma unroll 2
+  for (int c = 0; c < nchunk; ++c) {
+    const int k = c * 512 + lane * 8;
+    const uint32_t vo = k < K ? (uint32_t)k * 2u : kNoFetch;
+    const uint4 xv = buf_load16(rx, vo, 0);
+    uint4 wv[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) wv[r] = buf_load16_nt(rw, vo, soff[r]);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      acc[r] = fdot2_bf16(wv[r].x, xv.x, acc[r]);
+      acc[r] = fdot2_bf16(wv[r].y, xv.y, acc[r]);
+      acc[r] = fdot2_bf16(wv[r].z, xv.z, acc[r]);
+      acc[r] = fdot2_bf16(wv[r].w, xv.w, acc[r]);
+    }
+  }
+  reduce_wave<RPW>(acc);
+  // lane 16 r holds row r's total
+  if ((lane & 15) == 0) {
+    const int n = n0 + (lane >> 4);
+    if (n < N) A.out[p * (int64_t)N + n] = f32_to_bf16(acc[0]);
+  }
+}
+
+hipError_t launch_mv16(const QmvArgs& a, int64_t P, hipStream_t st) {
+  if (P <= 0 || a.N <= 0) return hipSuccess;
+  if (a.K % 8 != 0) return hipErrorInvalidValue;
+  const unsigned nrb = (unsigned)((a.N + 3) / 4);
+  for (int64_t p0 = 0; p0 < P; p0 += 65535) {
+    dim3 grid(nrb, (unsigned)(P - p0 < 65535 ? P - p0 : 65535));
+    hipLaunchKernelGGL(mv16_kernel, grid, dim3(64), 0, st, a, p0);
+  }
+  return hipGetLastError();
+}
+
 // Decode down projection fused with the combine tail (MTPLX PR 558: unsort,
 // multiply by the routing scores, sum over top_k and add the shared expert in
 // one pass).  A workgroup is one token: wave k computes y for pair

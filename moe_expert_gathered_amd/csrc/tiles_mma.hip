@@ -71,15 +71,21 @@ MOEGQ_DEV f16x8_t deq_operand(uint32_t w0, uint32_t w1, f16x2_t s2, f16x2_t b2) 
 // One tile: rows r0 .. r1 - 1 of expert e, MFMA columns n0 .. n0 + 255.  lds
 // holds the activation ring: RA stages of 16 * MI rows x TM_K fp16.
 template <int MI, int BITS = 4> struct MmaRing {
-  static constexpr int PDA = MI >= 8 ? 1 : 3;                   // K steps of activation prefetch
-  static constexpr int PDB = MI >= 8 ? 1 : 3;                   // K steps of code prefetch (registers)
+  // K steps of activation (LDS) and code (register) prefetch: one for 128-row
+  // tiles and for bf16 weights (register-bound), three for the shorter tiles
+  static constexpr int PDA = (MI >= 8 || BITS == 16) ? 1 : 3;
+  static constexpr int PDB = PDA;
   static constexpr int RA = PDA + 1, RB = PDB + 1;              // LDS and register ring stages
   static constexpr int U = (RA % RB == 0) ? RA : (RB % RA == 0) ? RB : RA * RB;   // steps per unrolled loop
   static constexpr int HALFS = RA * 16 * MI * TM_K;
 };
 
+// BITS = 16: the expert matrices are plain bf16 (no scales or biases); their
+// words go to v_mfma_f32_16x16x32_bf16 as loaded, with the bf16 activations
+// in natural order.
 template <int BITS, int GS, bool GLU, bool OUT16, int MI>
 MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e, int n0) {
+  constexpr bool W16 = BITS == 16;
   constexpr int CB = 4 * BITS;                    // code bytes per lane per K step (32 codes)
   using Ring = MmaRing<MI, BITS>;
   constexpr int PDA = Ring::PDA, PDB = Ring::PDB, RA = Ring::RA, RB = Ring::RB, U = Ring::U;
@@ -101,7 +107,15 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
   for (int v = 0; v < MI; ++v) {
     const int r = 4 * (MI * wave + v) + g;
     const int rr = min(r0 + r, r1 - 1);          // rows past the tile repeat a valid row (never stored)
-    const int src = A.lhs ? A.lhs[rr] : rr;
+    // virtual row rr = batch rr / rpb, row rr % rpb of it; the batch's x rows start at
+    // (lhs ? lhs[batch] : batch / lhs_div) * rpb (rpb and lhs_div of 0 mean 1)
+    int src;
+    if (A.rows_per_batch > 1) {
+      const int rpb = (int)A.rows_per_batch, bt = rr / rpb;
+      src = (A.lhs ? A.lhs[bt] : (A.lhs_div > 1 ? bt / (int)A.lhs_div : bt)) * rpb + rr % rpb;
+    } else {
+      src = A.lhs ? A.lhs[rr] : (A.lhs_div > 1 ? rr / (int)A.lhs_div : rr);
+    }
     const int chunk = c16 ^ lds_swz(r);
     a_off[v] = (uint32_t)src * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
   }
@@ -110,13 +124,17 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
   const bool ex = e >= A.E;          // the extra (shared) expert
   const size_t eo = ex ? 0 : (size_t)e;
   const __amdgpu_buffer_rsrc_t rw0 = make_rsrc((ex ? A.xw0 : A.w0) + eo * wstride, (uint32_t)(wstride * 4));
-  const __amdgpu_buffer_rsrc_t rs0 = make_rsrc((ex ? A.xs0 : A.s0) + eo * sstride, (uint32_t)(sstride * 2));
-  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc((ex ? A.xb0 : A.b0) + eo * sstride, (uint32_t)(sstride * 2));
+  const uint16_t* s0p = W16 ? A.s0 : (ex ? A.xs0 : A.s0) + eo * sstride;   // unused for bf16 weights
+  const uint16_t* b0p = W16 ? A.b0 : (ex ? A.xb0 : A.b0) + eo * sstride;
+  const __amdgpu_buffer_rsrc_t rs0 = make_rsrc(s0p, W16 ? 0u : (uint32_t)(sstride * 2));
+  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(b0p, W16 ? 0u : (uint32_t)(sstride * 2));
   __amdgpu_buffer_rsrc_t rw1 = rw0, rs1 = rs0, rb1 = rb0;
   if (GLU) {
     rw1 = make_rsrc((ex ? A.xw1 : A.w1) + eo * wstride, (uint32_t)(wstride * 4));
-    rs1 = make_rsrc((ex ? A.xs1 : A.s1) + eo * sstride, (uint32_t)(sstride * 2));
-    rb1 = make_rsrc((ex ? A.xb1 : A.b1) + eo * sstride, (uint32_t)(sstride * 2));
+    if (!W16) {
+      rs1 = make_rsrc((ex ? A.xs1 : A.s1) + eo * sstride, (uint32_t)(sstride * 2));
+      rb1 = make_rsrc((ex ? A.xb1 : A.b1) + eo * sstride, (uint32_t)(sstride * 2));
+    }
   }
   // MFMA column n of block j is output feature block_base(j) + col_perm(n).
   // The MFMA runs with the weights as the first operand, so lane (g, c16) ends
@@ -186,7 +204,7 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
   const int nK = K / TM_K;
   // ring of code registers: stage t % RB holds step t's codes (fixed extents:
   // the unused stages and halves are never touched and cost no registers)
-  uint4 cw[4][4][2];
+  uint4 cw[4][4][W16 ? 4 : 2];
   uint4 win_s, win_b, nwin_s, nwin_b;
   constexpr int LPS = MI + 4 * (BITS / 4);        // loads per step: activations + codes
   // part p (0..3) of step t's loads: activation rows into LDS stage sa, codes of block p into register stage sb
@@ -216,15 +234,17 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
     static_assert(VM < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt(0x0F70 | (VM & 15) | ((VM >> 4) << 14));
     __syncthreads();                      // every wave's rows landed; the stage of step ks - 1 is free
-    if (ks % WSTEPS == 0) {
-      win_s = nwin_s; win_b = nwin_b;
-      if ((ks + WSTEPS) < nK) load_win(ks / WSTEPS + 1, nwin_s, nwin_b);
-    }
     f16x2_t s2[4], b2[4];
+    if constexpr (!W16) {
+      if (ks % WSTEPS == 0) {
+        win_s = nwin_s; win_b = nwin_b;
+        if ((ks + WSTEPS) < nK) load_win(ks / WSTEPS + 1, nwin_s, nwin_b);
+      }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s2[j] = f16_splat(pick(win_s, ks, j));
-      b2[j] = f16_splat(pick(win_b, ks, j));
+      for (int j = 0; j < 4; ++j) {
+        s2[j] = f16_splat(pick(win_s, ks, j));
+        b2[j] = f16_splat(pick(win_b, ks, j));
+      }
     }
     const uint16_t* base = lds + sa * STAGE + c16 * TM_K;
 #pragma unroll
@@ -235,21 +255,30 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t* wv = &cw[sb][j][0].x;
-        bq[j] = BITS == 4 ? deq_operand<4>(wv[s], 0, s2[j], b2[j])
-                          : deq_operand<8>(wv[2 * s], wv[2 * s + 1], s2[j], b2[j]);
+        if constexpr (W16) bq[j] = __builtin_bit_cast(f16x8_t, cw[sb][j][s]);   // k 32 g + 8 s .. + 7
+        else if constexpr (BITS == 4) bq[j] = deq_operand<4>(wv[s], 0, s2[j], b2[j]);
+        else bq[j] = deq_operand<8>(wv[2 * s], wv[2 * s + 1], s2[j], b2[j]);
       }
       const int slot = (4 * g + s) ^ lds_swz(c16);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const f16x8_t a = *reinterpret_cast<const f16x8_t*>(base + i * 16 * TM_K + slot * 8);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bq[j], a, acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (W16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bq[j]),
+                                                                __builtin_bit_cast(bf16x8_t, a), acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bq[j], a, acc[i][j], 0, 0, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  load_win(0, win_s, win_b);
-  nwin_s = win_s; nwin_b = win_b;
+  if constexpr (!W16) {
+    load_win(0, win_s, win_b);
+    nwin_s = win_s; nwin_b = win_b;
+  }
   // prologue: activations of steps 0 .. PDA - 1, codes of steps 0 .. PDB - 1, in step order
 #pragma unroll
   for (int t = 0; t < (PDA > PDB ? PDA : PDB); ++t)
@@ -334,13 +363,16 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
 }
 
 // Both tile tables in one launch: blocks [0, n_big * NB) take the 128-row
-// tiles of `tiles`, the next n_small * NB blocks the 32-row tiles of `tiles2`.
+// (bf16 weights: 64-row) tiles of `tiles`, the next n_small * NB blocks the
+// 32-row tiles of `tiles2`.
 // The few-row tiles stream their experts' weights from HBM while the last
 // round of 128-row tiles keeps only part of the machine busy.
 template <int BITS, int GS, bool GLU, bool OUT16>
 __global__ __launch_bounds__(256, 2) void tile_mma_dual_kernel(TileArgs A) {
   constexpr int NF = GLU ? TM_C / 2 : TM_C;
-  constexpr int HALFS = MmaRing<8, BITS>::HALFS > MmaRing<2, BITS>::HALFS ? MmaRing<8, BITS>::HALFS : MmaRing<2, BITS>::HALFS;
+  constexpr int MIB = BITS == 16 ? 4 : 8;   // bf16 weights: 64-row big tiles (register budget)
+  constexpr int HALFS = MmaRing<MIB, BITS>::HALFS > MmaRing<2, BITS>::HALFS ? MmaRing<MIB, BITS>::HALFS
+                                                                           : MmaRing<2, BITS>::HALFS;
   __shared__ __attribute__((aligned(16))) uint16_t As[HALFS];
   const int NB = (A.N + NF - 1) / NF;
   const int nbig = *A.n_tiles * NB, nsmall = *A.n_tiles2 * NB;
@@ -348,7 +380,7 @@ __global__ __launch_bounds__(256, 2) void tile_mma_dual_kernel(TileArgs A) {
   if (b < nbig) {
     const int bid = xcd_remap(b, nbig);
     const int32_t* t = A.tiles + 3 * (bid / NB);
-    tile_body<BITS, GS, GLU, OUT16, 8>(A, As, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
+    tile_body<BITS, GS, GLU, OUT16, MIB>(A, As, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
   } else if (b < nbig + nsmall) {
     const int bid = b - nbig;
     const int32_t* t = A.tiles2 + 3 * (bid / NB);
@@ -478,6 +510,14 @@ hipError_t launch_tiles_mma_dual(const TileArgs& a, int bits, int gs, bool glu, 
   }
   MOEGQ_TD(4, 32) MOEGQ_TD(4, 64) MOEGQ_TD(4, 128) MOEGQ_TD(8, 32) MOEGQ_TD(8, 64) MOEGQ_TD(8, 128)
 #undef MOEGQ_TD
+  return hipErrorInvalidValue;
+}
+
+// bf16 expert matrices (gather_mm): 64-row tiles (rows 64), 32-row tiles, or both tables (rows 0)
+hipError_t launch_tiles_mma_w16(const TileArgs& a, bool glu, int rows, hipStream_t st) {
+  if (rows == 64) return glu ? launch_mma_t<16, 64, true, false, 4>(a, st) : launch_mma_t<16, 64, false, false, 4>(a, st);
+  if (rows == 32) return glu ? launch_mma_t<16, 64, true, false, 2>(a, st) : launch_mma_t<16, 64, false, false, 2>(a, st);
+  if (rows == 0) return glu ? launch_dual_t<16, 64, true, false>(a, st) : launch_dual_t<16, 64, false, false>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -109,6 +109,13 @@ def test_other_entry_points_validate(L):
     assert lay(64, 1024, 128, p, 1 << 30) == -6                                     # I % (8 * 64)
     assert lay(0, 256, 128, None, 0) == 0
     assert L.moegq_moe_combine_gated(p, None, p, None, p, 4, 8, 16, p, None) == -1  # shared required
+    # unquantized gather_mm
+    assert L.moegq_gather_mm(p, 4, 1, 100, p, 8, 16, None, 1, p, 4, 0, p, None, 0, None) == -4      # K % 8
+    assert L.moegq_gather_mm(p, 4, 1, 128, p, 8, 16, None, 1, None, 4, 0, p, None, 0, None) == -1   # no rhs
+    assert L.moegq_gather_mm(p, 4, 1, 128, p, 8, 16, None, 0, p, 4, 0, p, None, 0, None) == -4      # lhs_div
+    assert L.moegq_gather_mm(p, 2, 1, 128, p, 8, 16, None, 1, p, 4, 0, p, None, 0, None) == -4      # x rows
+    assert L.moegq_gather_mm(p, 4, 3, 96, p, 8, 16, None, 1, p, 4, 0, p, p, 1 << 20, None) == -6    # M > 1, K % 128
+    assert L.moegq_gather_mm(None, 4, 1, 128, None, 8, 16, None, 1, None, 0, 0, None, None, 0, None) == 0
     # router
     assert L.moegq_route(p, 4, 2000, 8, p, p, None) == -4                           # E > 1024
     assert L.moegq_route(p, 4, 16, 17, p, p, None) == -4                            # top_k > E
@@ -130,6 +137,8 @@ def test_workspace_sizes(L):
     # h and y for the routed and shared rows, the fp16 activations
     assert lay >= (16384 + 2048) * (512 + 2048) * 2 + 2048 * 2048 * 2
     assert m.moe_prefill_workspace_bytes(2048, 8, 256, 2048, 512, False) < lay
+    assert m.workspace_bytes(m.OP_GATHER_MM, 100, 8, 3, 0) >= 12 * 100       # per-pair tiles
+    assert m.workspace_bytes(m.OP_GATHER_MM, 4096, 64, 1, 0) >= 4 * 65 + 12 * (4096 // 64)
     assert m.switch_glu_mode(1, 8, 288) == m.MODE_DECODE
     assert m.switch_glu_mode(2048, 8, 256) == m.MODE_SORTED
 

@@ -21,6 +21,7 @@ import numpy as np
 __all__ = [
     "SUPPORTED_BITS", "SUPPORTED_GROUPS",
     "bf16_to_f64", "bf16_to_f32", "f64_to_bf16",
+    "activations_f64", "promoted_type", "round_to",
     "unpack", "dequant", "quantized_matmul", "gather_qmm", "broadcast_gather_indices",
     "silu", "switch_glu", "sort_pairs", "schedule_tiles", "naive_tiles",
     "combine", "unsort", "shared_expert", "rms_norm", "moe_prefill_layer",
@@ -140,6 +141,38 @@ def dequant(words, scales, biases, gs: int, bits: int, length: int) -> np.ndarra
 # ----------------------------------------------------------------------------
 # quantized_matmul and gather_qmm
 # ----------------------------------------------------------------------------
+def activations_f64(x):
+    """Activation values in float64 and their type: bf16 bit patterns
+    (``numpy.uint16``), or ``numpy.float16`` / ``numpy.float32`` arrays.  Each
+    conversion is exact."""
+    a = np.asarray(x)
+    if a.dtype == np.uint16:
+        return bf16_to_f64(a), "bf16"
+    if a.dtype == np.float16:
+        return a.astype(np.float64), "f16"
+    if a.dtype == np.float32:
+        return a.astype(np.float64), "f32"
+    raise ValueError("activations must be bf16 bit patterns, float16 or float32")
+
+
+def promoted_type(x_type: str) -> str:
+    """Result type of a product of activations of ``x_type`` with bf16 scales.
+
+    [nuvec] "reference": the product is computed in the type that the
+    activation and scale types promote to; the batched case there checks that
+    half precision promotes.  bf16 with bf16 stays bf16; float16 with bf16 has
+    no common 16-bit type and becomes float32; float32 stays float32.
+    """
+    if x_type not in ("bf16", "f16", "f32"):
+        raise ValueError(x_type)
+    return "bf16" if x_type == "bf16" else "f32"
+
+
+def round_to(y, t: str) -> np.ndarray:
+    """Round float64 results once to type ``t`` (bf16 bit patterns or float32)."""
+    return f64_to_bf16(y) if t == "bf16" else np.asarray(y, dtype=np.float64).astype(np.float32)
+
+
 def quantized_matmul(x, words, scales, biases, transpose: bool = True, gs: int = 64,
                      bits: int = 4) -> np.ndarray:
     """out = x . dequant(W)^T  (transpose=True, W is [N, K*bits/32], groups run
@@ -148,9 +181,10 @@ def quantized_matmul(x, words, scales, biases, transpose: bool = True, gs: int =
 
     [nuvec] "reference" and "quantized_matmul_equals_the_dequantized_product":
     the product of x with the dequantized weights.  The sum over K is formed in
-    float64 and rounded to bf16 once.
+    float64 and rounded once to the promoted type (``promoted_type``): bf16 bit
+    patterns for bf16 activations, float32 for float16 and float32 ones.
     """
-    xf = bf16_to_f64(x)
+    xf, xt = activations_f64(x)
     w = np.asarray(words)
     if transpose:
         K = xf.shape[-1]
@@ -162,7 +196,7 @@ def quantized_matmul(x, words, scales, biases, transpose: bool = True, gs: int =
         if W.shape[-2] != xf.shape[-1]:
             raise ValueError("inner sizes differ")
         y = np.matmul(xf, W)
-    return f64_to_bf16(y)
+    return round_to(y, promoted_type(xt))
 
 
 def broadcast_gather_indices(x_batch: tuple, w_batch: tuple, lhs=None, rhs=None):
@@ -200,7 +234,8 @@ def gather_qmm(x, words, scales, biases, lhs=None, rhs=None, transpose: bool = T
     group_size, bits).  [nuvec] "gather_qmm_selects_batches": each output batch
     equals quantized_matmul of the selected x batch and weight batch.
     """
-    x = np.asarray(x, dtype=np.uint16)
+    x = np.asarray(x)
+    _, xt = activations_f64(x[..., :0])
     w = np.asarray(words, dtype=np.uint32)
     s = np.asarray(scales, dtype=np.uint16)
     b = np.asarray(biases, dtype=np.uint16)
@@ -215,7 +250,7 @@ def gather_qmm(x, words, scales, biases, lhs=None, rhs=None, transpose: bool = T
         N = w.shape[-2]
     else:
         N = w.shape[-1] * 32 // bits
-    out = np.zeros((len(li), M, N), dtype=np.uint16)
+    out = np.zeros((len(li), M, N), dtype=np.uint16 if promoted_type(xt) == "bf16" else np.float32)
     for j, (l, r) in enumerate(zip(li, ri)):
         out[j] = quantized_matmul(xf[l], wf[r], sf[r], bf[r], transpose, gs, bits)
     return out.reshape(tuple(shape) + (M, N))

@@ -109,8 +109,13 @@ def test_straddling_widths_unpack():
 
 # ----------------------------------------------------------------------------- quantized matmul
 def _brute_qmm(x_u16, words, s_u16, b_u16, gs, bits, transpose=True):
-    """Triple loop in exact rational arithmetic, codes read off the bit string."""
-    xv = [[Fraction(float(v)) for v in row] for row in oracle.bf16_to_f64(x_u16)]
+    """Triple loop in exact rational arithmetic, codes read off the bit string.
+    Activations are bf16 bit patterns (result bf16) or float16/float32 values
+    (result float32)."""
+    xa = np.asarray(x_u16)
+    half_or_single = xa.dtype in (np.float16, np.float32)
+    xvals = xa.astype(np.float64) if half_or_single else oracle.bf16_to_f64(xa)
+    xv = [[Fraction(float(v)) for v in row] for row in xvals]
     sv = oracle.bf16_to_f64(s_u16)
     bv = oracle.bf16_to_f64(b_u16)
     rows = []
@@ -128,6 +133,8 @@ def _brute_qmm(x_u16, words, s_u16, b_u16, gs, bits, transpose=True):
         W = [[Fraction(int(rows[k][n * bits:(n + 1) * bits][::-1], 2)) * Fraction(float(sv[k][n // gs]))
               + Fraction(float(bv[k][n // gs])) for n in range(N)] for k in range(K)]
         out = [[float(sum(xv[m][k] * W[k][n] for k in range(K))) for n in range(N)] for m in range(len(xv))]
+    if half_or_single:
+        return np.array(out, dtype=np.float64).astype(np.float32)
     return oracle.f64_to_bf16(np.array(out))
 
 
@@ -145,6 +152,52 @@ def test_qmm_brute_force(bits, gs, M, N, K):
     got2 = oracle.quantized_matmul(x2, w2, s2, b2, False, 32, bits)
     assert got2.shape == (M, 64)
     assert np.array_equal(got2, _brute_qmm(x2, w2, s2, b2, 32, bits, transpose=False))
+
+
+@pytest.mark.parametrize("xdt", [np.float16, np.float32])
+@pytest.mark.parametrize("bits,gs", [(4, 32), (8, 64), (4, 128)])
+def test_qmm_half_and_single_activations_brute_force(xdt, bits, gs):
+    # float16 / float32 activations keep every bit (values off the bf16 grid:
+    # a conversion to bf16 would change them) and the result is float32
+    g = np.random.default_rng(bits * 7 + gs)
+    M, N, K = 2, 3, 2 * gs
+    x = (g.standard_normal((M, K)) * (1 + 2.0 ** -9)).astype(xdt)
+    assert not np.array_equal(synth.from_bf16(synth.to_bf16(x.astype(np.float32))), x.astype(np.float32))
+    w, s, b = synth.drawn_matrix(g, N, K, gs, bits)
+    got = oracle.quantized_matmul(x, w, s, b, True, gs, bits)
+    assert got.dtype == np.float32 and got.shape == (M, N)
+    assert np.array_equal(got, _brute_qmm(x, w, s, b, gs, bits))
+    w2, s2, b2 = synth.drawn_matrix(g, 24, gs, gs, bits)       # [K'=24, N'=gs], groups along N
+    x2 = (g.standard_normal((M, 24)) * (1 + 2.0 ** -9)).astype(xdt)
+    got2 = oracle.quantized_matmul(x2, w2, s2, b2, False, gs, bits)
+    assert got2.dtype == np.float32 and got2.shape == (M, gs)
+    assert np.array_equal(got2, _brute_qmm(x2, w2, s2, b2, gs, bits, transpose=False))
+
+
+def test_promoted_type_matches_torch():
+    # the result type is the promotion of the activation type with bf16 scales
+    torch = pytest.importorskip("torch")
+    names = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}
+    for t, n in names.items():
+        want = torch.promote_types(t, torch.bfloat16)
+        assert oracle.promoted_type(n) == names[want]
+    with pytest.raises(ValueError):
+        oracle.activations_f64(np.zeros(3, dtype=np.int32))
+
+
+def test_gather_qmm_batched_weights_promote_page_shape():
+    # [nuvec] "quantized_matmul_equals_the_dequantized_product": weights with
+    # batch [2, 1] (16 x 64, group 32, 4 bits) against float32 activations with
+    # batch [3] (5 x 64) give a float32 result of shape [2, 3, 5, 16]
+    g = np.random.default_rng(11)
+    w, s, b = synth.drawn_matrix(g, 2 * 16, 64, 32, 4)
+    w, s, b = w.reshape(2, 1, 16, 8), s.reshape(2, 1, 16, 2), b.reshape(2, 1, 16, 2)
+    x = g.standard_normal((3, 5, 64)).astype(np.float32)
+    got = oracle.gather_qmm(x, w, s, b, transpose=True, gs=32, bits=4)
+    assert got.shape == (2, 3, 5, 16) and got.dtype == np.float32
+    for i in range(2):
+        for j in range(3):
+            assert np.array_equal(got[i, j], _brute_qmm(x[j], w[i, 0], s[i, 0], b[i, 0], 32, 4))
 
 
 def test_qmm_group_factored_identity():

@@ -44,8 +44,9 @@ typedef enum {
   MOEGQ_ERR_SHAPE = -4,        /* K % group_size, packed width, inner size, counts */
   MOEGQ_ERR_DTYPE = -5,        /* integer activations, non-u32 packed words,
                                   float indices                                    */
-  MOEGQ_ERR_UNSUPPORTED = -6,  /* valid for the format but not built here
-                                  (transpose=0, f16/f32/f64 activations)           */
+  MOEGQ_ERR_UNSUPPORTED = -6,  /* valid for the format but not built here (bit
+                                  widths other than 4 and 8, 64-bit indices, and
+                                  the entry points whose comment says so)          */
   MOEGQ_ERR_WORKSPACE = -7,    /* workspace NULL or smaller than required          */
   MOEGQ_ERR_LAUNCH = -8,       /* a kernel launch failed (hipGetLastError)         */
   MOEGQ_ERR_SELFCHECK = -9,    /* fused combine differs from the unfused tail      */
@@ -85,18 +86,28 @@ size_t moegq_workspace_bytes(int op, int64_t P, int64_t E, int64_t N, int bm);
  *   transpose, group_size, bits, sorted_indices); nuvec "gather_qmm_selects_batches"
  *   adds lhs_indices (each output batch = quantized_matmul of the selected x
  *   batch and weight batch).
- * x        [X, M, K] activations (x_dtype; bf16 only here).
- * w        [E, N, K*bits/32] uint32 (w_dtype must be MOEGQ_U32);
- * scales, biases [E, N, K/group_size] bf16.
+ * x        [X, M, K] activations, x_dtype BF16, F16 or F32 (F64 and integers ->
+ *          MOEGQ_ERR_DTYPE).
+ * transpose=1: w [E, N, K*bits/32] uint32 (w_dtype must be MOEGQ_U32),
+ *          scales, biases [E, N, K/group_size] bf16 (groups along K).
+ * transpose=0: w [E, K, N*bits/32], scales, biases [E, K, N/group_size] bf16
+ *          (groups along N; nuvec "quantized_matmul_equals_the_dequantized_product"
+ *          runs this layout with K as the weight rows): out = x . dequant(W).
  * lhs_indices [P] (idx_dtype I32 or U32) or NULL -> lhs(p) = p / lhs_div
  *          (lhs_div >= 1; P1's x[M,1,1,K] with idx[M,top_k] is lhs_div = top_k).
  * rhs_indices [P] expert per pair (same idx_dtype), required.
  * sorted_indices  hint that rhs is non-decreasing; with M == 1 it selects the
  *          expert-grouped MFMA route (needs workspace).
- * transpose must be 1 (0 -> MOEGQ_ERR_UNSUPPORTED).
- * out      [P, M, N] bf16.
- * workspace/workspace_bytes: moegq_workspace_bytes(MOEGQ_OP_GATHER_QMM, P, E, M, 0)
- *          bytes (0 when the route needs none; then NULL is accepted).
+ * out      [P, M, N] in the promoted type (nuvec "reference": activation type
+ *          promoted with the bf16 scale type): bf16 for BF16 activations,
+ *          float32 for F16 and F32 ones.
+ * Routes: bf16 activations with transpose=1 use the matrix-vector, few-row
+ *          MFMA and tile kernels; transpose=0 or F16/F32 activations use the
+ *          vector-unit kernels, whose K split keeps fp32 partial sums in the
+ *          workspace (one matrix must be below 2 GiB, else UNSUPPORTED).
+ * workspace/workspace_bytes: moegq_gather_qmm_workspace_bytes(...) bytes (0 when
+ *          the route needs none; then NULL is accepted).  Not shared between
+ *          calls that overlap on one stream or on several streams.
  */
 int moegq_gather_qmm(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K,
                      const void* w, int w_dtype, const void* scales, const void* biases,
@@ -105,6 +116,12 @@ int moegq_gather_qmm(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K
                      int idx_dtype, int64_t P, int sorted_indices, int transpose,
                      int group_size, int bits, void* out,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that moegq_gather_qmm needs for these arguments (every
+ * route; sorted_indices as passed to the call).  0 for arguments the call
+ * rejects. */
+size_t moegq_gather_qmm_workspace_bytes(int64_t P, int64_t E, int64_t M, int64_t N, int64_t K, int x_dtype,
+                                        int transpose, int bits, int sorted_indices);
 
 /*
  * gather_qmm_glu: h[p] = bf16( silu(g) * u ) with g = x[lhs(p)] . dequant(wg[rhs[p]])^T
@@ -130,6 +147,10 @@ int moegq_gather_qmm_glu(const void* x, int x_dtype, int64_t X, int64_t M, int64
  * residual: NULL, or [M, N] bf16 added after rounding:
  *   out = bf16(residual + bf16(x . W^T)) (the decoder chain's residual add,
  *   MLX PR 4787 benchmark script).  out may alias residual.
+ * x_dtype must be BF16 and transpose 1 (else MOEGQ_ERR_UNSUPPORTED): the other
+ *   activation types and the layout without the transpose are served by
+ *   moegq_gather_qmm with one weight batch (E = 1, rhs all zero), which takes
+ *   a workspace for its K split.
  */
 int moegq_affine_qmm(const void* x, int x_dtype, int64_t M, int64_t K,
                      const void* w, int w_dtype, const void* scales, const void* biases,

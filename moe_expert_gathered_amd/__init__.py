@@ -16,7 +16,7 @@ import os
 
 import torch
 
-__all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
+__all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "quantized_matmul", "gather_qmm_workspace_bytes", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
            "switch_glu", "switch_glu_mode", "moe_decode", "moe_prefill", "moe_prefill_workspace_bytes", "moe_combine", "moe_combine_gated", "moe_combine_unfused", "sort_pairs",
            "schedule_tiles", "rms_norm", "sigmoid_gate", "route", "gather_mm", "kv_feed", "selfcheck",
            "validate_indices", "workspace_bytes", "MODE_AUTO", "MODE_DECODE", "MODE_SORTED",
@@ -51,6 +51,7 @@ _SIGS = {
     "moegq_status_string": ([_int], ctypes.c_char_p),
     "moegq_version": ([], ctypes.c_char_p),
     "moegq_workspace_bytes": ([_int, _i64, _i64, _i64, _int], _sz),
+    "moegq_gather_qmm_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64, _int, _int, _int, _int], _sz),
     "moegq_gather_qmm": ([_p, _int, _i64, _i64, _i64, _p, _int, _p, _p, _i64, _i64, _p, _i64, _p, _int, _i64,
                           _int, _int, _int, _int, _p, _p, _sz, _p], _int),
     "moegq_gather_qmm_glu": ([_p, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _int,
@@ -130,11 +131,9 @@ def workspace_bytes(op: int, P: int, E: int, N: int, bm: int = 0) -> int:
     return int(lib().moegq_workspace_bytes(op, P, E, N, bm))
 
 
-def _gather_ws(P, E, M, sorted_indices):
-    # only the grouped (sorted, one row per pair) and the many-row routes use a workspace
-    if (M == 1 and not sorted_indices) or 2 <= M <= 16:
-        return 0
-    return workspace_bytes(OP_GATHER_QMM, P, E, M, 0)
+def gather_qmm_workspace_bytes(P, E, M, N, K, x_dtype, transpose, bits, sorted_indices) -> int:
+    return int(lib().moegq_gather_qmm_workspace_bytes(P, E, M, N, K, x_dtype, int(bool(transpose)), bits,
+                                                      int(bool(sorted_indices))))
 
 
 def _workspace(nbytes: int, device):
@@ -193,13 +192,35 @@ def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, transpo
     if li is not None and li.dtype != ri.dtype:
         raise ValueError("lhs and rhs indices must share a dtype")
     if out is None:
-        out = torch.empty(shape + (M, N), dtype=torch.bfloat16, device=x.device)
-    ws, wsb = _workspace(_gather_ws(P, E, M, sorted_indices), x.device)
+        # the promoted type: bf16 activations stay bf16, float16 and float32 give float32
+        odt = torch.bfloat16 if x.dtype == torch.bfloat16 else torch.float32
+        out = torch.empty(shape + (M, N), dtype=odt, device=x.device)
+    ws, wsb = _workspace(gather_qmm_workspace_bytes(P, E, M, N, K, _dt(x), transpose, bits, sorted_indices),
+                         x.device)
     st = lib().moegq_gather_qmm(_ptr(x), _dt(x), X, M, K, _ptr(w), _wdt(w), _ptr(scales), _ptr(biases), E, N,
                                 _ptr(li), lhs_div, _ptr(ri), idx_dt, P, int(bool(sorted_indices)),
                                 int(bool(transpose)), group_size, bits, _ptr(out), _ptr(ws), wsb, _stream())
     _check(st, "gather_qmm")
     return out
+
+
+def quantized_matmul(x, w, scales, biases, transpose=True, group_size=64, bits=4, out=None):
+    """x . dequant(w)^T (or x . dequant(w) without the transpose) with the
+    leading batch axes of x [*bx, M, K] and w [*bw, rows, words] broadcast
+    together; the result type is bf16 for bf16 activations, float32 for
+    float16 and float32 ones.  Runs as gather_qmm over the broadcast batch
+    indices (marshalling only)."""
+    xb, wb = tuple(x.shape[:-2]), tuple(w.shape[:-2])
+    M = x.shape[-2]
+    N = w.shape[-2] if transpose else w.shape[-1] * 32 // bits
+    shape = tuple(torch.broadcast_shapes(xb, wb))
+    x3 = x if x.dim() >= 3 else x.reshape((1,) * (3 - x.dim()) + tuple(x.shape))
+    w3 = w if w.dim() >= 3 else w.reshape((1,) + tuple(w.shape))
+    s3 = scales if scales.dim() >= 3 else scales.reshape((1,) + tuple(scales.shape))
+    b3 = biases if biases.dim() >= 3 else biases.reshape((1,) + tuple(biases.shape))
+    res = gather_qmm(x3, w3, s3, b3, transpose=transpose, group_size=group_size, bits=bits,
+                     out=out)
+    return res.reshape(shape + (M, N))
 
 
 def gather_mm(x, w, rhs_indices, lhs_indices=None, lhs_div=1, sorted_indices=False, out=None):
@@ -236,7 +257,7 @@ def gather_qmm_glu(x, gate, up, rhs_indices, lhs_indices=None, lhs_div=1, group_
     P = rhs_indices.numel()
     if out is None:
         out = torch.empty((P, M, N), dtype=torch.bfloat16, device=x.device)
-    ws, wsb = _workspace(_gather_ws(P, E, M, sorted_indices), x.device)
+    ws, wsb = _workspace(gather_qmm_workspace_bytes(P, E, M, N, K, BF16, True, bits, sorted_indices), x.device)
     st = lib().moegq_gather_qmm_glu(_ptr(x), _dt(x), X, M, K, *[_ptr(t) for t in gate], *[_ptr(t) for t in up], E,
                                     N, _ptr(lhs_indices), lhs_div, _ptr(rhs_indices), _dt(rhs_indices), P,
                                     int(bool(sorted_indices)), group_size, bits, _ptr(out), _ptr(ws), wsb,

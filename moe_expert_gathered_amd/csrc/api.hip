@@ -39,6 +39,13 @@ int check_act_dtype(int d) {
   return MOEGQ_ERR_DTYPE;   // f64 and integer activations are rejected by the format
 }
 
+// activations accepted by gather_qmm: bf16 on every route, float16 and
+// float32 on the vector-unit route
+int check_any_act_dtype(int d) {
+  if (d == MOEGQ_BF16 || d == MOEGQ_F16 || d == MOEGQ_F32) return MOEGQ_OK;
+  return MOEGQ_ERR_DTYPE;
+}
+
 int check_idx_dtype(int d) {
   if (d == MOEGQ_I32 || d == MOEGQ_U32) return MOEGQ_OK;
   if (d == MOEGQ_I64) return MOEGQ_ERR_UNSUPPORTED;
@@ -214,6 +221,48 @@ size_t moegq_workspace_bytes(int op, int64_t P, int64_t E, int64_t N, int bm) {
   return 0;
 }
 
+size_t moegq_gather_qmm_workspace_bytes(int64_t P, int64_t E, int64_t M, int64_t N, int64_t K, int x_dtype,
+                                        int transpose, int bits, int sorted_indices) {
+  if (P <= 0 || M <= 0 || N <= 0 || K <= 0 || E <= 0) return 0;
+  if (!(bits == 4 || bits == 8)) return 0;
+  if (!transpose || x_dtype != MOEGQ_BF16) return vec_plan(P, M, N, K, bits, transpose).part_bytes;
+  if ((M == 1 && !sorted_indices) || (M >= 2 && M <= 16)) return 0;
+  return moegq_workspace_bytes(MOEGQ_OP_GATHER_QMM, P, E, M, 0);
+}
+
+// transpose = 0 (weights [E, K, N*bits/32], groups along N) or float16 /
+// float32 activations: the vector-unit kernels, fp32 partial sums of the K
+// split in the workspace
+static int gather_vec(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K, const void* w,
+                      const void* scales, const void* biases, int64_t E, int64_t N, const void* lhs_indices,
+                      int64_t lhs_div, const void* rhs_indices, int64_t P, int transpose, int group_size,
+                      int bits, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st;
+  // the quantized axis: K with the transpose, N without it
+  if ((st = check_quant(transpose ? K : N, group_size, bits))) return st;
+  if (K <= 0 || K > kMaxDim || M > kMaxDim) return MOEGQ_ERR_SHAPE;
+  // one expert matrix must fit a 2 GiB buffer range (32-bit offsets)
+  if (K * N * bits / 8 >= ((int64_t)1 << 31)) return MOEGQ_ERR_UNSUPPORTED;
+  if (!lhs_indices && lhs_div < 1) return MOEGQ_ERR_SHAPE;
+  if (P == 0 || M == 0 || N == 0) return MOEGQ_OK;
+  if (!x || !w || !scales || !biases || !rhs_indices || !out) return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return MOEGQ_ERR_ALIGN;
+  if (!lhs_indices && (P - 1) / lhs_div >= X) return MOEGQ_ERR_SHAPE;
+  const VecPlan pl = vec_plan(P, M, N, K, bits, transpose);
+  if (pl.part_bytes && (!workspace || workspace_bytes < pl.part_bytes)) return MOEGQ_ERR_WORKSPACE;
+  if (pl.part_bytes && !aligned16(workspace)) return MOEGQ_ERR_ALIGN;
+  VecArgs a{};
+  a.x = x; a.x_type = x_dtype == MOEGQ_BF16 ? 0 : (x_dtype == MOEGQ_F16 ? 1 : 2);
+  a.lhs = (const int32_t*)lhs_indices; a.lhs_div = lhs_div; a.rhs = (const int32_t*)rhs_indices;
+  a.P = P; a.M = (int)M; a.N = (int)N; a.K = (int)K; a.gs = group_size;
+  a.w = (const uint32_t*)w; a.s = (const uint16_t*)scales; a.b = (const uint16_t*)biases;
+  a.out = out; a.out_f32 = x_dtype != MOEGQ_BF16;
+  a.part = (float*)workspace;
+  a.MB = pl.MB; a.MBLK = pl.MBLK; a.WPL = pl.WPL; a.NC = pl.NC; a.KS = pl.KS; a.kchunk = pl.kchunk;
+  a.items = pl.items;
+  return status_of(launch_qmm_vec(a, bits, transpose, S(stream)));
+}
+
 static int gather_impl(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K, const void* w,
                        int w_dtype, const void* scales, const void* biases, const void* w1, const void* s1,
                        const void* b1, bool glu, int64_t E, int64_t N, const void* lhs_indices,
@@ -221,13 +270,17 @@ static int gather_impl(const void* x, int x_dtype, int64_t X, int64_t M, int64_t
                        int transpose, int group_size, int bits, void* out, void* workspace,
                        size_t workspace_bytes, void* stream) {
   int st;
-  if ((st = check_act_dtype(x_dtype))) return st;
+  if ((st = check_any_act_dtype(x_dtype))) return st;
   if (w_dtype != MOEGQ_U32) return MOEGQ_ERR_DTYPE;
   if ((st = check_idx_dtype(idx_dtype))) return st;
-  if ((st = check_quant(K, group_size, bits))) return st;
-  if (!transpose) return MOEGQ_ERR_UNSUPPORTED;
   if (X < 0 || M < 0 || E <= 0 || N < 0 || P < 0 || X > kMaxDim || N > kMaxDim || P > kMaxDim)
     return MOEGQ_ERR_SHAPE;
+  if (!transpose || x_dtype != MOEGQ_BF16) {
+    if (glu) return MOEGQ_ERR_UNSUPPORTED;
+    return gather_vec(x, x_dtype, X, M, K, w, scales, biases, E, N, lhs_indices, lhs_div, rhs_indices, P,
+                      transpose, group_size, bits, out, workspace, workspace_bytes, stream);
+  }
+  if ((st = check_quant(K, group_size, bits))) return st;
   if (!lhs_indices && lhs_div < 1) return MOEGQ_ERR_SHAPE;
   if (P == 0 || M == 0 || N == 0) return MOEGQ_OK;
   if (!x || !w || !scales || !biases || !rhs_indices || !out) return MOEGQ_ERR_NULL_ARG;

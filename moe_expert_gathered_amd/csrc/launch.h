@@ -132,6 +132,26 @@ hipError_t launch_sigmoid_gate(const uint16_t* s, const uint16_t* z, int64_t zs,
                                uint16_t* out, hipStream_t st);
 hipError_t launch_kv_feed(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t M,
                           int64_t Nq, int64_t Nk, int64_t Nv, uint16_t* out, hipStream_t st);
+// vector-unit products: weights without the transpose, float16/float32 activations
+constexpr int kQmtRows = 4;   // weight rows per wave with the transpose
+struct VecPlan {
+  int MB, MBLK, WPL, NC, KS, kchunk;   // rows per block, blocks, words per lane, column strips, splits, K per split
+  int64_t items;                       // waves
+  size_t part_bytes;                   // fp32 partial sums (workspace) when KS > 1
+};
+VecPlan vec_plan(int64_t P, int64_t M, int64_t N, int64_t K, int bits, int transpose);
+struct VecArgs {
+  const void* x; int x_type;           // [X, M, K]; 0 bf16, 1 float16, 2 float32
+  const int32_t* lhs; int64_t lhs_div; // x batch per pair (or p / lhs_div)
+  const int32_t* rhs;                  // weight batch per pair (or 0)
+  int64_t P; int M, N, K, gs;
+  const uint32_t* w; const uint16_t* s; const uint16_t* b;
+  void* out; int out_f32;              // [P, M, N] bf16 or float32
+  float* part;                         // [KS, P, M, N] when KS > 1
+  int MB, MBLK, WPL, NC, KS, kchunk;   // from vec_plan
+  int64_t items;
+};
+hipError_t launch_qmm_vec(const VecArgs& a, int bits, int transpose, hipStream_t st);
 hipError_t launch_iota(int32_t* dst, int64_t n, hipStream_t st);
 hipError_t launch_validate(const int32_t* idx, int64_t n, int64_t E, int sorted, int32_t* flag,
                            hipStream_t st);

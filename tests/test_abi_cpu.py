@@ -60,10 +60,14 @@ def test_gather_qmm_error_catalogue(L):
     assert gq(L, K=96) == -4                        # K not divisible by the group size
     assert gq(L, x_dtype=m.I32) == -5               # integer activations
     assert gq(L, x_dtype=m.F64) == -5               # f64 activations
-    assert gq(L, x_dtype=m.F32) == -6               # f32: valid, not built
+    assert gq(L, x_dtype=m.F32, K=96) == -4         # f32 activations take the same format checks
     assert gq(L, w_dtype=m.F32) == -5               # packed weights must be u32
     assert gq(L, idx_dtype=m.F32) == -5             # float indices
-    assert gq(L, transpose=0) == -6                 # transpose=False not built
+    assert gq(L, transpose=0, N=96) == -4           # without the transpose the groups run along N
+    assert gq(L, transpose=0, N=64, gs=128) == -4
+    # the vector-unit route's K split needs its workspace
+    assert gq(L, transpose=0, X=1, P=1, N=4096, K=4096) == -7
+    assert gq(L, x_dtype=m.F16, X=1, P=1, N=64, K=8192) == -7
     assert gq(L, rhs=None) == -1
     assert gq(L, x=ctypes.c_void_p(0x100008)) == -11
     assert gq(L, lhs_div=0) == -4
@@ -73,6 +77,27 @@ def test_gather_qmm_error_catalogue(L):
     # empty products launch nothing and succeed, even with null pointers
     assert gq(L, P=0, x=None, w=None, out=None, rhs=None) == 0
     assert gq(L, M=0, x=None, out=None) == 0
+
+
+def test_gather_qmm_workspace_query(L):
+    import moe_expert_gathered_amd as m
+    q = L.moegq_gather_qmm_workspace_bytes
+    # vector route: [splits, P, M, N] fp32 partial sums
+    # transpose=0, one pair, 4096 x 4096 4-bit: 2 column strips -> 256 splits of 16 rows
+    assert q(1, 1, 1, 4096, 4096, m.BF16, 0, 4, 0) == 256 * 4096 * 4
+    # float16, transposed, N = 64, K = 8192: 16 row blocks -> 8 splits of 128 words
+    assert q(1, 1, 1, 64, 8192, m.F16, 1, 4, 0) == 8 * 64 * 4
+    # enough work items: no split, no workspace
+    assert q(4096, 8, 1, 64, 256, m.F32, 1, 4, 0) == 0
+    # bf16 with the transpose: the existing routes
+    assert q(8, 8, 1, 64, 256, m.BF16, 1, 4, 0) == 0
+    assert q(8, 8, 4, 64, 256, m.BF16, 1, 4, 0) == 0
+    assert q(8, 8, 40, 64, 256, m.BF16, 1, 4, 0) == L.moegq_workspace_bytes(m.OP_GATHER_QMM, 8, 8, 40, 0)
+    assert q(0, 8, 1, 64, 256, m.BF16, 1, 4, 0) == 0
+    # the gate/up variant rejects the vector route
+    p = FAKE
+    assert L.moegq_gather_qmm_glu(p, m.F32, 4, 1, 256, p, p, p, p, p, p, 8, 64, None, 1, p, 4, 4, 0, 64, 4, p,
+                                  None, 0, None) == -6
 
 
 def test_other_entry_points_validate(L):

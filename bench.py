@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=42 * 4)
     ap.add_argument("--warmup", type=int, default=42)
-    ap.add_argument("--legs", default="decode,prefill,large,gather_mm,dense,cpu")
+    ap.add_argument("--legs", default="decode,prefill,large,gather_mm,vec,dense,cpu")
     ap.add_argument("--prefill-rows", default="2048,128,512,4096", help="row counts of the prefill leg")
     ap.add_argument("--large-rows", default="713,4123,8192,16384", help="row counts of the large-prefill leg")
     ap.add_argument("--quiet", action="store_true")
@@ -360,6 +360,47 @@ def gather_mm_leg(torch, m, synth, steps=20):
     return res
 
 
+def vec_leg(torch, m, synth, steps=42, cfg=1):
+    """The vector-unit route of gather_qmm at the decode shape (one token,
+    8 of 288 experts, 4-bit, group 64): the gate projection stored without
+    the transpose ([288, 4096, 2048/8] words, groups along N) with bf16
+    activations, and the transposed gate projection with float32 activations
+    (float32 result).  42 index sets chained in one HIP graph, as the decode
+    leg does, so that weights come from HBM."""
+    sh = synth.DECODE
+    dev = torch.device("cuda")
+    gate = synth.device_drawn_words(dev, (cfg, 0, synth.GATE), (sh.E, sh.I), sh.H, sh.gs, sh.bits)
+    E, H, I = sh.E, sh.H, sh.I
+    sets = [torch.from_numpy(synth.sorted_topk(cfg, 1, E, sh.top_k, sub=i).reshape(-1)).to(dev) for i in range(42)]
+    P = sh.top_k
+    per_pair = I * H * sh.bits // 8 + 2 * I * (H // sh.gs) * 2
+    res = {}
+    # without the transpose: the same bytes read as [E, K = H, N = I] with groups along N
+    w_nt = gate[0].view(E, H, I * sh.bits // 32)
+    s_nt = gate[1].view(E, H, I // sh.gs)
+    b_nt = gate[2].view(E, H, I // sh.gs)
+    for name, x, w, s, b, tr, N in (
+            ("no_transpose_bf16_1tok_8pairs_k4096_n2048",
+             torch.randn((1, 1, H), device=dev).to(torch.bfloat16), w_nt, s_nt, b_nt, False, I),
+            ("transpose_f32_act_1tok_8pairs_n2048_k4096",
+             torch.randn((1, 1, H), device=dev, dtype=torch.float32), *gate, True, I)):
+        odt = torch.bfloat16 if x.dtype == torch.bfloat16 else torch.float32
+        out = torch.empty((P, 1, N), dtype=odt, device=dev)
+        need = m.gather_qmm_workspace_bytes(P, E, 1, N, H, m._dt(x), tr, sh.bits, False)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        fn = lambda i, x=x, w=w, s=s, b=b, tr=tr, out=out, ws=ws: m.gather_qmm(
+            x, w, s, b, rhs_indices=sets[i % 42], transpose=tr, group_size=sh.gs, bits=sh.bits, out=out,
+            workspace=ws)
+        us = graph_time_us(torch, fn, 42, reps=max(1, steps // 42), check=lambda out=out: out)
+        nbytes = P * per_pair + H * x.element_size() + P * N * out.element_size()
+        plan_ks = m.gather_qmm_workspace_bytes(P, E, 1, N, H, m._dt(x), tr, sh.bits, False) // (P * N * 4)
+        res[name] = {"us": us, "gbs": nbytes / us / 1e3, "hbm_frac": nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+                     "bytes": nbytes, "k_splits": int(plan_ks) if plan_ks else 1}
+    del gate
+    torch.cuda.empty_cache()
+    return res
+
+
 # ----------------------------------------------------------------------------- dense chain
 def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=5, warmup=2, cfg=2):
     dev = torch.device("cuda")
@@ -523,6 +564,9 @@ def main():
     if "gather_mm" in legs:
         log("unquantized gather_mm")
         extra["gather_mm"] = gather_mm_leg(torch, m, synth)
+    if "vec" in legs:
+        log("== vec leg")
+        extra["vec"] = vec_leg(torch, m, synth)
     if "dense" in legs:
         log("dense chain")
         extra["dense_chain"] = dense_leg(torch, m, synth)

@@ -144,16 +144,19 @@ def _workspace(nbytes: int, device):
 
 # ----------------------------------------------------------------------------- ops
 def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, transpose=True,
-               group_size=64, bits=4, sorted_indices=False, out=None):
+               group_size=64, bits=4, sorted_indices=False, out=None, workspace=None):
     """out[j] = x[lhs[j]] . dequant(w[rhs[j]])^T over the broadcast index shape.
 
     x: [*bx, M, K]; w: [E, N, K*bits/32] (or [*bw, N, Kw], flattened to E).
     With x of shape [B, 1, 1, K] and rhs [B, top_k] (the MoE decode layout)
     the x row of pair (b, k) is b, passed as lhs_div = top_k without building
     an index array.  Otherwise indices are broadcast (marshalling only).
-    Output: index shape + [M, N].
+    Output: index shape + [M, N], bf16 for bf16 activations, float32 for
+    float16/float32 ones.  transpose=False takes w [E, K, N*bits/32] with
+    groups along N.  workspace: an optional uint8 device tensor of at least
+    gather_qmm_workspace_bytes(...) bytes (else one is allocated).
     """
-    _dev(x, w, scales, biases, rhs_indices, lhs_indices)
+    _dev(x, w, scales, biases, rhs_indices, lhs_indices, workspace)
     M, K = x.shape[-2], x.shape[-1]
     xb, wb = tuple(x.shape[:-2]), tuple(w.shape[:-2])
     X = 1
@@ -195,8 +198,11 @@ def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, transpo
         # the promoted type: bf16 activations stay bf16, float16 and float32 give float32
         odt = torch.bfloat16 if x.dtype == torch.bfloat16 else torch.float32
         out = torch.empty(shape + (M, N), dtype=odt, device=x.device)
-    ws, wsb = _workspace(gather_qmm_workspace_bytes(P, E, M, N, K, _dt(x), transpose, bits, sorted_indices),
-                         x.device)
+    need = gather_qmm_workspace_bytes(P, E, M, N, K, _dt(x), transpose, bits, sorted_indices)
+    if workspace is not None and workspace.numel() >= need:
+        ws, wsb = workspace, int(workspace.numel())
+    else:
+        ws, wsb = _workspace(need, x.device)
     st = lib().moegq_gather_qmm(_ptr(x), _dt(x), X, M, K, _ptr(w), _wdt(w), _ptr(scales), _ptr(biases), E, N,
                                 _ptr(li), lhs_div, _ptr(ri), idx_dt, P, int(bool(sorted_indices)),
                                 int(bool(transpose)), group_size, bits, _ptr(out), _ptr(ws), wsb, _stream())

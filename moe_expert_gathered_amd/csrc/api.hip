@@ -39,6 +39,15 @@ int check_act_dtype(int d) {
   return MOEGQ_ERR_DTYPE;   // f64 and integer activations are rejected by the format
 }
 
+// the format's checks for the vector-unit route, which takes every width of
+// the format (1-6 and 8 bits)
+int check_quant_any(int64_t L, int gs, int bits) {
+  if (!(bits >= 1 && bits <= 6) && bits != 8) return MOEGQ_ERR_BITS;
+  if (!(gs == 32 || gs == 64 || gs == 128)) return MOEGQ_ERR_GROUP_SIZE;
+  if (L <= 0 || L > kMaxDim || L % gs != 0) return MOEGQ_ERR_SHAPE;
+  return MOEGQ_OK;
+}
+
 // activations accepted by gather_qmm: bf16 on every route, float16 and
 // float32 on the vector-unit route
 int check_any_act_dtype(int d) {
@@ -224,8 +233,9 @@ size_t moegq_workspace_bytes(int op, int64_t P, int64_t E, int64_t N, int bm) {
 size_t moegq_gather_qmm_workspace_bytes(int64_t P, int64_t E, int64_t M, int64_t N, int64_t K, int x_dtype,
                                         int transpose, int bits, int sorted_indices) {
   if (P <= 0 || M <= 0 || N <= 0 || K <= 0 || E <= 0) return 0;
-  if (!(bits == 4 || bits == 8)) return 0;
-  if (!transpose || x_dtype != MOEGQ_BF16) return vec_plan(P, M, N, K, bits, transpose).part_bytes;
+  if (!(bits >= 1 && bits <= 6) && bits != 8) return 0;
+  if (!transpose || x_dtype != MOEGQ_BF16 || (bits != 4 && bits != 8))
+    return vec_plan(P, M, N, K, bits, transpose).part_bytes;
   if ((M == 1 && !sorted_indices) || (M >= 2 && M <= 16)) return 0;
   return moegq_workspace_bytes(MOEGQ_OP_GATHER_QMM, P, E, M, 0);
 }
@@ -239,7 +249,7 @@ static int gather_vec(const void* x, int x_dtype, int64_t X, int64_t M, int64_t 
                       int bits, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   int st;
   // the quantized axis: K with the transpose, N without it
-  if ((st = check_quant(transpose ? K : N, group_size, bits))) return st;
+  if ((st = check_quant_any(transpose ? K : N, group_size, bits))) return st;
   if (K <= 0 || K > kMaxDim || M > kMaxDim) return MOEGQ_ERR_SHAPE;
   // one expert matrix must fit a 2 GiB buffer range (32-bit offsets)
   if (K * N * bits / 8 >= ((int64_t)1 << 31)) return MOEGQ_ERR_UNSUPPORTED;
@@ -275,8 +285,8 @@ static int gather_impl(const void* x, int x_dtype, int64_t X, int64_t M, int64_t
   if ((st = check_idx_dtype(idx_dtype))) return st;
   if (X < 0 || M < 0 || E <= 0 || N < 0 || P < 0 || X > kMaxDim || N > kMaxDim || P > kMaxDim)
     return MOEGQ_ERR_SHAPE;
-  if (!transpose || x_dtype != MOEGQ_BF16) {
-    if (glu) return MOEGQ_ERR_UNSUPPORTED;
+  if (!transpose || x_dtype != MOEGQ_BF16 || (bits != 4 && bits != 8)) {
+    if (glu) return (bits >= 1 && bits <= 6) || bits == 8 ? MOEGQ_ERR_UNSUPPORTED : MOEGQ_ERR_BITS;
     return gather_vec(x, x_dtype, X, M, K, w, scales, biases, E, N, lhs_indices, lhs_div, rhs_indices, P,
                       transpose, group_size, bits, out, workspace, workspace_bytes, stream);
   }

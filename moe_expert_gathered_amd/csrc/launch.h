@@ -133,9 +133,8 @@ hipError_t launch_sigmoid_gate(const uint16_t* s, const uint16_t* z, int64_t zs,
 hipError_t launch_kv_feed(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t M,
                           int64_t Nq, int64_t Nk, int64_t Nv, uint16_t* out, hipStream_t st);
 // vector-unit products: weights without the transpose, float16/float32 activations
-constexpr int kQmtRows = 4;   // weight rows per wave with the transpose
 struct VecPlan {
-  int MB, MBLK, WPL, NC, KS, kchunk;   // rows per block, blocks, words per lane, column strips, splits, K per split
+  int MB, MBLK, WPL, NC, KS, kchunk;   // rows per block, blocks, codes per lane, column strips (row blocks), splits, K per split
   int64_t items;                       // waves
   size_t part_bytes;                   // fp32 partial sums (workspace) when KS > 1
 };

@@ -1,39 +1,42 @@
 // Vector-unit quantized products for the rest of the operation's surface:
-// weights without the transpose (W is [K, N] with its groups along N), and
-// float16 / float32 activations in either layout.
+// weights without the transpose (W is [K, N] with its groups along N),
+// float16 / float32 activations in either layout, and the bit widths 1, 2, 3,
+// 5 and 6 next to 4 and 8.
 //
 // nuvec "reference": the product is x . dequant(W)^T, or x . dequant(W)
 // without the transpose, in the type that the activation and scale types
 // promote to; "quantized_matmul_equals_the_dequantized_product" runs both
-// layouts (without the transpose, W's rows are the K axis) and lets half
-// precision promote.  With bf16 scales the result is bf16 for bf16
-// activations and float32 for float16 or float32 ones.  MLX issue 4509, gq():
+// layouts (without the transpose, W's rows are the K axis), the widths
+// 1-6 and 8, and lets half precision promote.  With bf16 scales the result is
+// bf16 for bf16 activations and float32 for float16 or float32 ones.  Code k
+// of a packed row occupies bits [k b, k b + b) of the row's little-endian word
+// stream, so 3-, 5- and 6-bit codes straddle words.  MLX issue 4509, gq():
 // gather_qmm over (lhs, rhs) index pairs; nuvec "gather_qmm_selects_batches".
 //
 // Arithmetic: fp32 throughout.  For one group g of a weight row,
 //   sum_k x_k (q_k s + b) = s * sum_k x_k q_k + b * sum_k x_k,
 // the group identity of the affine code (nuvec "composed": codes * s + b).
-// Codes become floats with v_cvt_f32_ubyte on masked bytes (exact).
+// Codes become floats exactly (byte or bit-field extraction, then a convert).
 //
-// gfx950 mapping.  Every wave is one independent work item: a pair, a block
-// of up to MB activation rows, a strip of output columns and a range of K.
-// Four waves share a workgroup and nothing else (no LDS, no barriers).
-//  * Without the transpose (qvm_kernel): lane l owns WPL consecutive packed
-//    words of each weight row k, i.e. 8 * WPL (4-bit) or 4 * WPL (8-bit)
-//    consecutive output columns, which lie in one quantization group (the
-//    group size is at least 32 and a lane's columns are aligned to their
-//    count).  A weight row is a contiguous run of words, so a wave's load of
-//    one row is one coalesced 256 B (WPL = 1) or 1 KiB (WPL = 4) access.
-//    The activations of 64 consecutive k are loaded one per lane and handed
-//    to the whole wave with v_readlane, one value per row step.
-//  * With the transpose (qmt_kernel): W is [N, K] with groups along K; lane
-//    l owns 2 packed words (16 or 8 codes, one group) of RPW consecutive
-//    weight rows and the matching activations; the wave walks K in slices
-//    of 128 words and finishes with a butterfly over its 64 lanes.
+// gfx950 mapping.  A lane owns a chunk of CH consecutive codes of a weight
+// row: CH * b / 32 whole words, all in one quantization group (CH divides 32
+// and the group size is at least 32).  CH is 32 for every width (b words), or
+// 8 (4-bit) / 4 (8-bit) for narrow rows.
+//  * Without the transpose (qvm_kernel): the chunk is CH output columns of
+//    weight row k.  One workgroup per work item (a pair, a block of up to MB
+//    activation rows, a strip of 64 CH columns, a range of K); its 4 waves take
+//    the rows k0 + w, k0 + w + 4, .. (the workgroup streams a contiguous run of
+//    rows), U rows in flight per wave with the activations of those rows (one
+//    per lane, handed to the wave with v_readlane), and add their sums through
+//    LDS at the end.
+//  * With the transpose (qmt_kernel): the chunk is 32 codes of K of RPW
+//    consecutive weight rows; each wave is a work item and walks K in slices
+//    of 64 chunks, loading the next slice before the current one's arithmetic,
+//    and ends with a butterfly over its lanes.
 //  * K is split over KS work items when the pairs, rows and columns alone
-//    give too few waves; each split writes fp32 partial sums to the
-//    workspace and vec_reduce_kernel adds the KS partials in split order and
-//    rounds once (to bf16 or float32), so results do not depend on timing.
+//    give too few; each split writes fp32 partial sums to the workspace and
+//    vec_reduce_kernel adds the KS partials in split order and rounds once
+//    (to bf16 or float32), so results do not depend on timing.
 #include "common.h"
 #include "launch.h"
 
@@ -41,50 +44,80 @@ namespace moegq {
 
 constexpr uint32_t kVecNoFetch = 0x7FFFFFF0u;   // beyond every descriptor's range: loads return 0
 
-// activation element i of a row (type XT: 0 bf16, 1 float16, 2 float32)
-template <int XT>
-MOEGQ_DEV float act_at(const void* x, int64_t i) {
-  if constexpr (XT == 0) return bf16_to_f32(static_cast<const uint16_t*>(x)[i]);
-  else if constexpr (XT == 1) return (float)static_cast<const _Float16*>(x)[i];
-  else return static_cast<const float*>(x)[i];
+// NW consecutive 32-bit words at byte offset voff + soff (4-byte aligned)
+template <int NW>
+MOEGQ_DEV void load_words(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t (&w)[NW]) {
+  int i = 0;
+#pragma unroll
+  for (; i + 4 <= NW; i += 4) {
+    const uint4 v = buf_load16(r, voff == kVecNoFetch ? voff : voff + 4 * i, soff);
+    w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+  }
+  if constexpr (NW % 4 >= 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff == kVecNoFetch ? voff : voff + 4 * (NW / 4) * 4,
+                                                        soff, 0);
+    w[(NW / 4) * 4] = v[0]; w[(NW / 4) * 4 + 1] = v[1];
+  }
+  if constexpr (NW % 2 == 1)
+    w[NW - 1] = __builtin_amdgcn_raw_buffer_load_b32(r, voff == kVecNoFetch ? voff : voff + 4 * (NW - 1), soff, 0);
 }
 
-// code j (0..32/BITS-1) of a packed word as a float; lo = w & 0x0F0F0F0F and
-// hi = (w >> 4) & 0x0F0F0F0F hold the even and odd 4-bit codes as bytes.  A
-// byte extraction followed by the conversion is one v_cvt_f32_ubyteN.
-template <int BITS>
-MOEGQ_DEV float code_f(uint32_t w, uint32_t lo, uint32_t hi, int j) {
+// The CH codes of a chunk as floats.  4-bit: w & 0x0F0F0F0F and
+// (w >> 4) & 0x0F0F0F0F hold the even and odd codes as bytes; 8-bit: the bytes;
+// other widths: a funnel shift across the word boundary, then a mask.  A byte
+// extraction followed by the conversion is one v_cvt_f32_ubyteN.
+template <int BITS, int CH>
+MOEGQ_DEV void codes_f(const uint32_t (&w)[CH * BITS / 32], float (&q)[CH]) {
   if constexpr (BITS == 4) {
-    const uint32_t src = (j & 1) ? hi : lo;
-    return (float)((src >> (8 * (j >> 1))) & 0xFFu);
+#pragma unroll
+    for (int i = 0; i < CH / 8; ++i) {
+      const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        q[8 * i + 2 * j] = (float)((lo >> (8 * j)) & 0xFFu);
+        q[8 * i + 2 * j + 1] = (float)((hi >> (8 * j)) & 0xFFu);
+      }
+    }
+  } else if constexpr (BITS == 8) {
+#pragma unroll
+    for (int i = 0; i < CH / 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q[4 * i + j] = (float)((w[i] >> (8 * j)) & 0xFFu);
   } else {
-    return (float)((w >> (8 * j)) & 0xFFu);
+    constexpr uint32_t mask = (1u << BITS) - 1u;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int o = j * BITS, wi = o >> 5, sh = o & 31;
+      uint32_t v;
+      if (sh + BITS <= 32) v = w[wi] >> sh;
+      else v = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], (uint32_t)sh);
+      q[j] = (float)(v & mask);
+    }
   }
 }
 
-// n (a multiple of 4) consecutive activations from element i (16-byte aligned
-// for the wider types) as floats
+// NV (a multiple of 8) consecutive activations at byte offset `off` of the
+// row descriptor r, as floats; an offset past the range gives zeros
 template <int XT, int NV>
-MOEGQ_DEV void load_acts(const void* x, int64_t i, float (&v)[NV]) {
-  static_assert(NV % 4 == 0, "");
+MOEGQ_DEV void load_acts(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&v)[NV]) {
+  static_assert(NV % 8 == 0, "");
   if constexpr (XT == 2) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + i);
 #pragma unroll
     for (int j = 0; j < NV / 4; ++j) {
-      const float4 t = p[j];
-      v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+      const uint4 t = buf_load16(r, off == kVecNoFetch ? off : off + 16 * j, 0);
+      v[4 * j] = __uint_as_float(t.x); v[4 * j + 1] = __uint_as_float(t.y);
+      v[4 * j + 2] = __uint_as_float(t.z); v[4 * j + 3] = __uint_as_float(t.w);
     }
   } else {
-    const uint2* p = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + i);
 #pragma unroll
-    for (int j = 0; j < NV / 4; ++j) {
-      const uint2 t = p[j];
-      const uint32_t d[2] = {t.x, t.y};
+    for (int j = 0; j < NV / 8; ++j) {
+      const uint4 t = buf_load16(r, off == kVecNoFetch ? off : off + 16 * j, 0);
+      const uint32_t d[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
+      for (int h = 0; h < 8; ++h) {
         const uint32_t half = (d[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
-        if constexpr (XT == 0) v[4 * j + h] = __uint_as_float(half << 16);
-        else v[4 * j + h] = (float)__builtin_bit_cast(_Float16, (uint16_t)half);
+        if constexpr (XT == 0) v[8 * j + h] = __uint_as_float(half << 16);
+        else v[8 * j + h] = (float)__builtin_bit_cast(_Float16, (uint16_t)half);
       }
     }
   }
@@ -95,121 +128,141 @@ MOEGQ_DEV void store_result(void* out, int out_f32, int64_t i, float v) {
   else static_cast<uint16_t*>(out)[i] = f32_to_bf16(v);
 }
 
-// work item of wave `item`: split ks fastest, then column strip / row block,
-// row block of the activations, pair
+// work item `item`: split ks, column strip (row block) cs, block mb of the
+// activation rows, pair p; `cs_fast` puts the strip first (neighbouring
+// waves then read the same activations), else the split
 struct VecItem { int64_t p; int mb, cs, ks; };
-MOEGQ_DEV VecItem vec_item(const VecArgs& A, int64_t item) {
+MOEGQ_DEV VecItem vec_item(const VecArgs& A, int64_t item, bool cs_fast) {
   VecItem it;
-  it.ks = (int)(item % A.KS); item /= A.KS;
-  it.cs = (int)(item % A.NC); item /= A.NC;
+  if (cs_fast) {
+    it.cs = (int)(item % A.NC); item /= A.NC;
+    it.ks = (int)(item % A.KS); item /= A.KS;
+  } else {
+    it.ks = (int)(item % A.KS); item /= A.KS;
+    it.cs = (int)(item % A.NC); item /= A.NC;
+  }
   it.mb = (int)(item % A.MBLK);
   it.p = item / A.MBLK;
   return it;
 }
 
 // ---------------------------------------------------------------- without the transpose
-template <int BITS, int XT, int MB, int WPL>
+template <int BITS, int XT, int MB, int CH, int U>
 __global__ __launch_bounds__(256) void qvm_kernel(VecArgs A) {
-  constexpr int CPW = 32 / BITS;        // codes per word
-  constexpr int CPL = CPW * WPL;        // output columns per lane
+  constexpr int NW = CH * BITS / 32;    // words per lane per row
+  __shared__ float red[3][CH][64];      // waves 1..3, one activation row at a time
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-  if (item >= A.items) return;                       // whole waves leave together
-  const VecItem it = vec_item(A, item);
+  const int64_t item = blockIdx.x;
+  if (item >= A.items) return;                       // the whole workgroup leaves
+  const VecItem it = vec_item(A, item, false);
   const int K = A.K, N = A.N, M = A.M;
-  const int Nw = N / CPW, G = N / A.gs;
+  const int Nw = N / 32 * BITS, G = N / A.gs;        // N is a multiple of 32
   const int64_t xb = A.lhs ? (int64_t)A.lhs[it.p] : it.p / A.lhs_div;
   const int64_t e = A.rhs ? (int64_t)A.rhs[it.p] : 0;
-  const int w0 = (it.cs * 64 + lane) * WPL;          // first word of the lane's columns
-  const bool act = w0 < Nw;
-  const int col0 = w0 * CPW;
+  const int col0 = (it.cs * 64 + lane) * CH;         // first of the lane's columns
+  const bool act = col0 < N;
   const uint32_t g2 = act ? (uint32_t)(col0 / A.gs) * 2 : kVecNoFetch;
-  const uint32_t wo = act ? (uint32_t)w0 * 4 : kVecNoFetch;
+  const uint32_t wo = act ? (uint32_t)(col0 * BITS / 32) * 4 : kVecNoFetch;   // CH * BITS is a multiple of 32
   const int k0 = it.ks * A.kchunk;
   const int k1 = min(K, k0 + A.kchunk);
   const int m0 = it.mb * MB;
   const int nm = min(MB, M - m0);
+  const int kw = k0 + wave;                          // the wave's first row; its rows step by 4
+  const int nr = k1 > kw ? (k1 - kw + 3) / 4 : 0;    // rows of this wave
 
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(A.w + e * (int64_t)K * Nw, (uint32_t)((int64_t)K * Nw * 4));
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(A.s + e * (int64_t)K * G, (uint32_t)((int64_t)K * G * 2));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(A.b + e * (int64_t)K * G, (uint32_t)((int64_t)K * G * 2));
   const int64_t xrow0 = (xb * M + m0) * (int64_t)K;
+  constexpr int XSZ = XT == 2 ? 4 : 2;
+  __amdgpu_buffer_rsrc_t rx[MB];                      // one descriptor per activation row (empty past M)
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+    rx[m] = make_rsrc(static_cast<const char*>(A.x) + (xrow0 + (int64_t)(m < nm ? m : 0) * K) * XSZ,
+                      m < nm ? (uint32_t)K * XSZ : 0u);
 
-  float acc[MB][CPL], bacc[MB];
+  float acc[MB][CH], bacc[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     bacc[m] = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[m][c] = 0.f;
+    for (int c = 0; c < CH; ++c) acc[m][c] = 0.f;
   }
-  constexpr int U = 4;   // weight rows in flight per step
-  for (int kb = k0; kb < k1; kb += 64) {
-    const int kn = min(64, k1 - kb);
+  for (int j = 0; j < nr; j += U) {
+    uint32_t cw[U][NW];
+    uint16_t sv[U], bv[U];
+    // lane u < U: the activations of the batch's row u
     float xl[MB];
+    {
+      const bool xok = lane < U && j + lane < nr;
+      const uint32_t xo = xok ? (uint32_t)(kw + 4 * (j + lane)) * XSZ : kVecNoFetch;
 #pragma unroll
-    for (int m = 0; m < MB; ++m)
-      xl[m] = (lane < kn && m < nm) ? act_at<XT>(A.x, xrow0 + (int64_t)m * K + kb + lane) : 0.f;
-    for (int j = 0; j < kn; j += U) {
-      uint32_t cw[U][WPL];
-      uint16_t sv[U], bv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool ok = j + u < kn;                   // uniform
-        const uint32_t row = (uint32_t)(kb + j + u);
-        const uint32_t off = ok ? wo : kVecNoFetch;
-        if constexpr (WPL == 4) {
-          const uint4 v = buf_load16(rw, off, ok ? row * Nw * 4 : 0);
-          cw[u][0] = v.x; cw[u][1] = v.y; cw[u][2] = v.z; cw[u][3] = v.w;
-        } else {
-          cw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rw, off, ok ? row * Nw * 4 : 0, 0);
-        }
-        sv[u] = buf_load2(rs, ok ? g2 : kVecNoFetch, ok ? row * G * 2 : 0);
-        bv[u] = buf_load2(rb, ok ? g2 : kVecNoFetch, ok ? row * G * 2 : 0);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (j + u >= kn) break;                       // uniform
-        const float s = bf16_to_f32(sv[u]), b = bf16_to_f32(bv[u]);
-        float xs[MB];
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          const float xm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xl[m]), j + u));
-          xs[m] = xm * s;
-          bacc[m] = fmaf(xm, b, bacc[m]);
-        }
-#pragma unroll
-        for (int wi = 0; wi < WPL; ++wi) {
-          const uint32_t w = cw[u][wi];
-          const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-          for (int jj = 0; jj < CPW; ++jj) {
-            const float q = code_f<BITS>(w, lo, hi, jj);
-#pragma unroll
-            for (int m = 0; m < MB; ++m) acc[m][wi * CPW + jj] = fmaf(xs[m], q, acc[m][wi * CPW + jj]);
-          }
+      for (int m = 0; m < MB; ++m) {
+        if constexpr (XT == 2) xl[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx[m], xo, 0, 0));
+        else {
+          const uint16_t h = buf_load2(rx[m], xo, 0);
+          xl[m] = XT == 0 ? bf16_to_f32(h) : (float)__builtin_bit_cast(_Float16, h);
         }
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = j + u < nr;                     // uniform
+      const uint32_t row = ok ? (uint32_t)(kw + 4 * (j + u)) : 0u;
+      load_words<NW>(rw, ok ? wo : kVecNoFetch, row * Nw * 4, cw[u]);
+      sv[u] = buf_load2(rs, ok ? g2 : kVecNoFetch, row * G * 2);
+      bv[u] = buf_load2(rb, ok ? g2 : kVecNoFetch, row * G * 2);
+    }
+    // rows past nr loaded zeros (codes, scale, bias) and their activation
+    // lanes hold zero: they add nothing, and no branch separates the loads
+    // above from the arithmetic below
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float s = bf16_to_f32(sv[u]), b = bf16_to_f32(bv[u]);
+      float xs[MB];
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const float xm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xl[m]), u));
+        xs[m] = xm * s;
+        bacc[m] = fmaf(xm, b, bacc[m]);
+      }
+      float q[CH];
+      codes_f<BITS, CH>(cw[u], q);
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[m][c] = fmaf(xs[m], q[c], acc[m][c]);
+    }
   }
-  if (!act) return;
+  // wave 0 adds the sums of waves 1, 2, 3 (in that order) and writes
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
-    if (m >= nm) break;
-    const int64_t orow = (it.p * M + m0 + m) * (int64_t)N + col0;   // a multiple of 4
-    float v[CPL];
+    if (m >= nm) break;                               // uniform over the workgroup
+    float v[CH];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) v[c] = acc[m][c] + bacc[m];
-    if (A.KS > 1 || A.out_f32) {
-      float* dst = A.KS > 1 ? A.part + (int64_t)it.ks * A.P * M * N + orow : static_cast<float*>(A.out) + orow;
+    for (int c = 0; c < CH; ++c) v[c] = acc[m][c] + bacc[m];
+    if (wave > 0) {
 #pragma unroll
-      for (int c = 0; c < CPL; c += 4) *reinterpret_cast<float4*>(dst + c) = make_float4(v[c], v[c + 1], v[c + 2], v[c + 3]);
-    } else {
-      uint16_t* dst = static_cast<uint16_t*>(A.out) + orow;
-#pragma unroll
-      for (int c = 0; c < CPL; c += 4)
-        *reinterpret_cast<uint2*>(dst + c) = make_uint2(pack_bf16x2(v[c], v[c + 1]), pack_bf16x2(v[c + 2], v[c + 3]));
+      for (int c = 0; c < CH; ++c) red[wave - 1][c][lane] = v[c];
     }
+    __syncthreads();
+    if (wave == 0 && act) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) v[c] = ((v[c] + red[0][c][lane]) + red[1][c][lane]) + red[2][c][lane];
+      const int64_t orow = (it.p * M + m0 + m) * (int64_t)N + col0;   // a multiple of 4
+      if (A.KS > 1 || A.out_f32) {
+        float* dst = A.KS > 1 ? A.part + (int64_t)it.ks * A.P * M * N + orow : static_cast<float*>(A.out) + orow;
+#pragma unroll
+        for (int c = 0; c < CH; c += 4) *reinterpret_cast<float4*>(dst + c) = make_float4(v[c], v[c + 1], v[c + 2], v[c + 3]);
+      } else {
+        uint16_t* dst = static_cast<uint16_t*>(A.out) + orow;
+#pragma unroll
+        for (int c = 0; c < CH; c += 4)
+          *reinterpret_cast<uint2*>(dst + c) = make_uint2(pack_bf16x2(v[c], v[c + 1]), pack_bf16x2(v[c + 2], v[c + 3]));
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -222,83 +275,94 @@ MOEGQ_DEV void wave_sum(float (&a)[V]) {
     for (int i = 0; i < V; ++i) a[i] += __shfl_xor(a[i], off, 64);
 }
 
+// one slice (64 chunks of 32 codes) of RPW weight rows and the activations
+template <int BITS, int MB, int RPW>
+struct QmtSlice {
+  uint32_t c[RPW][BITS];
+  uint16_t s[RPW], b[RPW];
+  float x[MB][32];
+};
+
 template <int BITS, int XT, int MB, int RPW>
 __global__ __launch_bounds__(256) void qmt_kernel(VecArgs A) {
-  constexpr int CPW = 32 / BITS;
-  constexpr int CPL = 2 * CPW;          // codes per lane per slice (two words)
+  using Slice = QmtSlice<BITS, MB, RPW>;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-  if (item >= A.items) return;
-  const VecItem it = vec_item(A, item);
+  if (item >= A.items) return;                       // whole waves leave together
+  const VecItem it = vec_item(A, item, true);
   const int K = A.K, N = A.N, M = A.M;
-  const int Kw = K / CPW, G = K / A.gs;
+  const int Kw = K / 32 * BITS, G = K / A.gs;        // K is a multiple of 32
   const int64_t xb = A.lhs ? (int64_t)A.lhs[it.p] : it.p / A.lhs_div;
   const int64_t e = A.rhs ? (int64_t)A.rhs[it.p] : 0;
   const int n0 = it.cs * RPW;
-  const int kw0 = it.ks * A.kchunk;                  // in words
-  const int kw1 = min(Kw, kw0 + A.kchunk);
+  const int kc0 = it.ks * A.kchunk;                  // in codes (a multiple of 2048)
+  const int kc1 = min(K, kc0 + A.kchunk);
   const int m0 = it.mb * MB;
   const int nm = min(MB, M - m0);
 
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(A.w + e * (int64_t)N * Kw, (uint32_t)((int64_t)N * Kw * 4));
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(A.s + e * (int64_t)N * G, (uint32_t)((int64_t)N * G * 2));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(A.b + e * (int64_t)N * G, (uint32_t)((int64_t)N * G * 2));
-  const int64_t xrow0 = (xb * M + m0) * (int64_t)K;
-
-  float acc[MB * RPW];
+  constexpr int XSZ = XT == 2 ? 4 : 2;
+  __amdgpu_buffer_rsrc_t rx[MB];                      // one descriptor per activation row (empty past M)
 #pragma unroll
-  for (int i = 0; i < MB * RPW; ++i) acc[i] = 0.f;
-  for (int sw = kw0; sw < kw1; sw += 128) {
-    const int wi = sw + 2 * lane;
-    const bool ok = wi < kw1;
-    const int kc = wi * CPW;                          // first code of the lane
+  for (int m = 0; m < MB; ++m)
+    rx[m] = make_rsrc(static_cast<const char*>(A.x) + ((xb * M + m0 + (m < nm ? m : 0)) * (int64_t)K) * XSZ,
+                      m < nm ? (uint32_t)K * XSZ : 0u);
+
+  auto load = [&](int sc, Slice& S) {
+    const int kc = sc + 32 * lane;                    // the lane's first code
+    const bool ok = kc < kc1;                         // kc1 is a multiple of 32
     const uint32_t g2 = ok ? (uint32_t)(kc / A.gs) * 2 : kVecNoFetch;
-    uint2 cw[RPW];
-    uint16_t sv[RPW], bv[RPW];
+    const uint32_t wo = ok ? (uint32_t)(kc / 32 * BITS) * 4 : kVecNoFetch;
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const bool rok = ok && n0 + r < N;
       const uint32_t row = (uint32_t)min(n0 + r, N - 1);
-      const uint32_t off = rok ? (uint32_t)wi * 4 : kVecNoFetch;
-      cw[r].x = __builtin_amdgcn_raw_buffer_load_b32(rw, off, row * Kw * 4, 0);
-      cw[r].y = __builtin_amdgcn_raw_buffer_load_b32(rw, rok ? off + 4 : kVecNoFetch, row * Kw * 4, 0);
-      sv[r] = buf_load2(rs, rok ? g2 : kVecNoFetch, row * G * 2);
-      bv[r] = buf_load2(rb, rok ? g2 : kVecNoFetch, row * G * 2);
+      load_words<BITS>(rw, rok ? wo : kVecNoFetch, row * Kw * 4, S.c[r]);
+      S.s[r] = buf_load2(rs, rok ? g2 : kVecNoFetch, row * G * 2);
+      S.b[r] = buf_load2(rb, rok ? g2 : kVecNoFetch, row * G * 2);
     }
-    float xv[MB][CPL], sx[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) load_acts<XT>(rx[m], ok ? (uint32_t)kc * XSZ : kVecNoFetch, S.x[m]);
+  };
+
+  float acc[MB * RPW];
+#pragma unroll
+  for (int i = 0; i < MB * RPW; ++i) acc[i] = 0.f;
+  auto compute = [&](const Slice& S) {
+    float sx[MB];
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      if (ok && m < nm) {
-        load_acts<XT>(A.x, xrow0 + (int64_t)m * K + kc, xv[m]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) xv[m][c] = 0.f;
-      }
       sx[m] = 0.f;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) sx[m] += xv[m][c];
+      for (int c = 0; c < 32; ++c) sx[m] += S.x[m][c];
     }
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
+      float q[32];
+      codes_f<BITS, 32>(S.c[r], q);
       float d[MB];
 #pragma unroll
       for (int m = 0; m < MB; ++m) d[m] = 0.f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t w = h ? cw[r].y : cw[r].x;
-        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+      for (int c = 0; c < 32; ++c)
 #pragma unroll
-        for (int jj = 0; jj < CPW; ++jj) {
-          const float q = code_f<BITS>(w, lo, hi, jj);
-#pragma unroll
-          for (int m = 0; m < MB; ++m) d[m] = fmaf(xv[m][h * CPW + jj], q, d[m]);
-        }
-      }
-      const float s = bf16_to_f32(sv[r]), b = bf16_to_f32(bv[r]);
+        for (int m = 0; m < MB; ++m) d[m] = fmaf(S.x[m][c], q[c], d[m]);
+      const float s = bf16_to_f32(S.s[r]), b = bf16_to_f32(S.b[r]);
 #pragma unroll
       for (int m = 0; m < MB; ++m) acc[m * RPW + r] = fmaf(s, d[m], fmaf(b, sx[m], acc[m * RPW + r]));
     }
+  };
+
+  // the slice after the last one loads zeros (offsets past kc1) without a branch
+  Slice cur, nxt;
+  load(kc0, cur);
+  for (int sc = kc0; sc < kc1; sc += 2048) {
+    load(sc + 2048, nxt);
+    compute(cur);
+    cur = nxt;
   }
   wave_sum(acc);
   if (lane != 0) return;
@@ -315,48 +379,62 @@ __global__ __launch_bounds__(256) void qmt_kernel(VecArgs A) {
   }
 }
 
-// out[i] = round(sum_{ks < KS} part[ks][i]), the splits added in order
-__global__ __launch_bounds__(256) void vec_reduce_kernel(const float* __restrict__ part, int KS, int64_t total,
-                                                         void* out, int out_f32) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
-    float v = part[i];
-    for (int k = 1; k < KS; ++k) v += part[(int64_t)k * total + i];
+// out[i] = round(sum_{ks < KS} part[ks][i]), the splits added in order.  KS is
+// at most kVecMaxSplits: every partial of an output is requested before the
+// first is added (one memory latency, not KS of them).  One wave per
+// workgroup, so that the requests spread over every CU.
+constexpr int kVecMaxSplits = 64;
+__global__ __launch_bounds__(64) void vec_reduce_kernel(const float* __restrict__ part, int KS, int64_t total,
+                                                        void* out, int out_f32) {
+  const int64_t stride = (int64_t)gridDim.x * 64;
+  for (int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x; i < total; i += stride) {
+    float t[kVecMaxSplits];
+#pragma unroll
+    for (int k = 0; k < kVecMaxSplits; ++k) t[k] = k < KS ? part[(int64_t)k * total + i] : -0.f;
+    float v = t[0];
+#pragma unroll
+    for (int k = 1; k < kVecMaxSplits; ++k) v += t[k];   // -0 past KS: the additive identity
     store_result(out, out_f32, i, v);
   }
 }
 
 // ---------------------------------------------------------------- host side
-constexpr int64_t kVecWaves = 4096;                 // waves the split aims for
+constexpr int64_t kVecWaves = 4096;                 // waves the split aims for (half that with the transpose)
 constexpr int64_t kVecPartMax = (int64_t)1 << 26;   // bytes of partial sums at most
+
+static int qmt_rows(int bits) { return bits <= 4 ? 8 : 4; }
 
 VecPlan vec_plan(int64_t P, int64_t M, int64_t N, int64_t K, int bits, int transpose) {
   VecPlan pl{};
-  const int cpw = 32 / bits;
-  pl.MB = M >= 3 ? 4 : (int)M;
-  pl.MBLK = (M + pl.MB - 1) / pl.MB;
-  int64_t steps;                 // units of K a split can take
+  int64_t items0, steps, target;
   if (!transpose) {
-    const int64_t Nw = N / cpw;
-    pl.WPL = Nw >= 256 ? 4 : 1;
-    pl.NC = (Nw + 64 * pl.WPL - 1) / (64 * pl.WPL);
-    steps = (K + 15) / 16;                           // at least 16 weight rows per split
+    // workgroup items; a split takes at least 64 weight rows (16 per wave)
+    pl.MB = M >= 3 ? 4 : (int)M;
+    // codes per lane: 32, or one word (4-bit, 8-bit) when the row is narrow
+    pl.WPL = ((bits == 4 || bits == 8) && N < 2048) ? 32 / bits : 32;
+    pl.NC = (N + 64 * pl.WPL - 1) / (64 * pl.WPL);
+    steps = (K + 63) / 64;
+    target = kVecWaves / 4;
   } else {
-    pl.WPL = 2;
-    pl.NC = (N + kQmtRows - 1) / kQmtRows;
-    steps = (K / cpw + 127) / 128;                   // 128-word slices
+    // wave items; a split takes whole slices of 2048 codes
+    pl.MB = M >= 2 ? 2 : 1;
+    pl.WPL = 32;
+    pl.NC = (N + qmt_rows(bits) - 1) / qmt_rows(bits);
+    steps = (K + 2047) / 2048;
+    target = kVecWaves / 2;
   }
-  const int64_t items0 = P * pl.MBLK * pl.NC;
-  int64_t ks = (kVecWaves + items0 - 1) / items0;
+  pl.MBLK = (M + pl.MB - 1) / pl.MB;
+  items0 = P * pl.MBLK * pl.NC;
+  int64_t ks = (target + items0 - 1) / items0;
   if (ks > steps) ks = steps;
   const int64_t out_elems = P * M * N;
   const int64_t ks_cap = kVecPartMax / (out_elems * 4);
   if (ks > ks_cap) ks = ks_cap;
+  if (ks > kVecMaxSplits) ks = kVecMaxSplits;
   if (ks < 1) ks = 1;
   const int64_t per = (steps + ks - 1) / ks;         // steps per split
-  pl.kchunk = (int)(transpose ? per * 128 : per * 16);
-  const int64_t kunits = transpose ? K / cpw : K;
-  pl.KS = (int)((kunits + pl.kchunk - 1) / pl.kchunk);
+  pl.kchunk = (int)(transpose ? per * 2048 : per * 64);
+  pl.KS = (int)((K + pl.kchunk - 1) / pl.kchunk);
   pl.items = items0 * pl.KS;
   pl.part_bytes = pl.KS > 1 ? (size_t)(pl.KS * out_elems * 4) : 0;
   return pl;
@@ -364,39 +442,54 @@ VecPlan vec_plan(int64_t P, int64_t M, int64_t N, int64_t K, int bits, int trans
 
 template <int BITS, int XT>
 static hipError_t launch_vec_t(const VecArgs& a, int transpose, hipStream_t st) {
-  const dim3 grid((unsigned)((a.items + 3) / 4)), block(256);
+  const dim3 block(256);
   if (!transpose) {
-#define MOEGQ_QVM(RB, WL) \
-  if (a.MB == RB && a.WPL == WL) { hipLaunchKernelGGL((qvm_kernel<BITS, XT, RB, WL>), grid, block, 0, st, a); return hipGetLastError(); }
-    MOEGQ_QVM(1, 1) MOEGQ_QVM(2, 1) MOEGQ_QVM(4, 1) MOEGQ_QVM(1, 4) MOEGQ_QVM(2, 4) MOEGQ_QVM(4, 4)
+    const dim3 grid((unsigned)a.items);                       // one workgroup per item
+#define MOEGQ_QVM(RB, CC, UU) \
+  if (a.MB == RB && a.WPL == CC) { hipLaunchKernelGGL((qvm_kernel<BITS, XT, RB, CC, UU>), grid, block, 0, st, a); return hipGetLastError(); }
+    MOEGQ_QVM(1, 32, 16) MOEGQ_QVM(2, 32, 8) MOEGQ_QVM(4, 32, 8)
+    if constexpr (BITS == 4 || BITS == 8) {
+      MOEGQ_QVM(1, 32 / BITS, 16) MOEGQ_QVM(2, 32 / BITS, 8) MOEGQ_QVM(4, 32 / BITS, 8)
+    }
 #undef MOEGQ_QVM
   } else {
+    const dim3 grid((unsigned)((a.items + 3) / 4));           // one wave per item
+    constexpr int R = BITS <= 4 ? 8 : 4;
 #define MOEGQ_QMT(RB) \
-  if (a.MB == RB) { hipLaunchKernelGGL((qmt_kernel<BITS, XT, RB, kQmtRows>), grid, block, 0, st, a); return hipGetLastError(); }
-    MOEGQ_QMT(1) MOEGQ_QMT(2) MOEGQ_QMT(4)
+  if (a.MB == RB) { hipLaunchKernelGGL((qmt_kernel<BITS, XT, RB, R>), grid, block, 0, st, a); return hipGetLastError(); }
+    MOEGQ_QMT(1) MOEGQ_QMT(2)
 #undef MOEGQ_QMT
   }
   return hipErrorInvalidValue;
 }
 
+template <int BITS>
+static hipError_t launch_vec_bits(const VecArgs& a, int transpose, hipStream_t st) {
+  if (a.x_type == 0) return launch_vec_t<BITS, 0>(a, transpose, st);
+  if (a.x_type == 1) return launch_vec_t<BITS, 1>(a, transpose, st);
+  if (a.x_type == 2) return launch_vec_t<BITS, 2>(a, transpose, st);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_qmm_vec(const VecArgs& a, int bits, int transpose, hipStream_t st) {
   if (a.items <= 0) return hipSuccess;
-  if ((a.items + 3) / 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (a.items >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   hipError_t e = hipErrorInvalidValue;
-  if (bits == 4) {
-    if (a.x_type == 0) e = launch_vec_t<4, 0>(a, transpose, st);
-    else if (a.x_type == 1) e = launch_vec_t<4, 1>(a, transpose, st);
-    else if (a.x_type == 2) e = launch_vec_t<4, 2>(a, transpose, st);
-  } else if (bits == 8) {
-    if (a.x_type == 0) e = launch_vec_t<8, 0>(a, transpose, st);
-    else if (a.x_type == 1) e = launch_vec_t<8, 1>(a, transpose, st);
-    else if (a.x_type == 2) e = launch_vec_t<8, 2>(a, transpose, st);
+  switch (bits) {
+    case 1: e = launch_vec_bits<1>(a, transpose, st); break;
+    case 2: e = launch_vec_bits<2>(a, transpose, st); break;
+    case 3: e = launch_vec_bits<3>(a, transpose, st); break;
+    case 4: e = launch_vec_bits<4>(a, transpose, st); break;
+    case 5: e = launch_vec_bits<5>(a, transpose, st); break;
+    case 6: e = launch_vec_bits<6>(a, transpose, st); break;
+    case 8: e = launch_vec_bits<8>(a, transpose, st); break;
+    default: break;
   }
   if (e != hipSuccess || a.KS <= 1) return e;
   const int64_t total = a.P * a.M * (int64_t)a.N;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(vec_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.part, a.KS, total, a.out,
+  int64_t blocks = (total + 63) / 64;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(vec_reduce_kernel, dim3((unsigned)blocks), dim3(64), 0, st, a.part, a.KS, total, a.out,
                      a.out_f32);
   return hipGetLastError();
 }

@@ -56,7 +56,9 @@ def test_gather_qmm_error_catalogue(L):
     import moe_expert_gathered_amd as m
     assert gq(L, gs=48) == -3                       # group size 48
     assert gq(L, bits=7) == -2                      # bits 7
-    assert gq(L, bits=3) == -6                      # valid width, not built here
+    assert gq(L, bits=3, K=96) == -4                # 3 bits: the format's checks (vector-unit route)
+    assert gq(L, bits=6, gs=48) == -3
+    assert gq(L, bits=0) == -2 and gq(L, bits=9) == -2
     assert gq(L, K=96) == -4                        # K not divisible by the group size
     assert gq(L, x_dtype=m.I32) == -5               # integer activations
     assert gq(L, x_dtype=m.F64) == -5               # f64 activations
@@ -83,10 +85,11 @@ def test_gather_qmm_workspace_query(L):
     import moe_expert_gathered_amd as m
     q = L.moegq_gather_qmm_workspace_bytes
     # vector route: [splits, P, M, N] fp32 partial sums
-    # transpose=0, one pair, 4096 x 4096 4-bit: 2 column strips -> 256 splits of 16 rows
-    assert q(1, 1, 1, 4096, 4096, m.BF16, 0, 4, 0) == 256 * 4096 * 4
-    # float16, transposed, N = 64, K = 8192: 16 row blocks -> 8 splits of 128 words
-    assert q(1, 1, 1, 64, 8192, m.F16, 1, 4, 0) == 8 * 64 * 4
+    # transpose=0, one pair, 4096 x 4096 4-bit: 2 column strips (workgroup items)
+    # -> 64 splits of 64 rows
+    assert q(1, 1, 1, 4096, 4096, m.BF16, 0, 4, 0) == 64 * 4096 * 4
+    # float16, transposed, N = 64, K = 8192: 16 row blocks (wave items) -> 4 splits of 256 words
+    assert q(1, 1, 1, 64, 8192, m.F16, 1, 4, 0) == 4 * 64 * 4
     # enough work items: no split, no workspace
     assert q(4096, 8, 1, 64, 256, m.F32, 1, 4, 0) == 0
     # bf16 with the transpose: the existing routes
@@ -94,6 +97,9 @@ def test_gather_qmm_workspace_query(L):
     assert q(8, 8, 4, 64, 256, m.BF16, 1, 4, 0) == 0
     assert q(8, 8, 40, 64, 256, m.BF16, 1, 4, 0) == L.moegq_workspace_bytes(m.OP_GATHER_QMM, 8, 8, 40, 0)
     assert q(0, 8, 1, 64, 256, m.BF16, 1, 4, 0) == 0
+    # every width of the format has a workspace size on the vector route
+    assert q(1, 1, 1, 4096, 4096, m.BF16, 1, 3, 0) > 0
+    assert q(1, 1, 1, 4096, 4096, m.BF16, 1, 7, 0) == 0
     # the gate/up variant rejects the vector route
     p = FAKE
     assert L.moegq_gather_qmm_glu(p, m.F32, 4, 1, 256, p, p, p, p, p, p, 8, 64, None, 1, p, 4, 4, 0, 64, 4, p,

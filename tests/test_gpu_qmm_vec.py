@@ -1,7 +1,8 @@
 """GPU parity of the vector-unit route of gather_qmm against the oracle:
-weights without the transpose ([E, K, N*bits/32], groups along N) and float16
-/ float32 activations (float32 result) in both layouts, with and without the
-split of K, ragged column strips, row blocks and K tails.
+weights without the transpose ([E, K, N*bits/32], groups along N), float16
+/ float32 activations (float32 result) in both layouts, and the bit widths
+1, 2, 3, 5 and 6 (codes straddling words) in both layouts, with and without
+the split of K, ragged column strips, row blocks and K tails.
 
 Tolerances: bf16 results use the fixed bar |gpu - oracle| <= 1e-2 max|oracle|.
 float32 results are held to the recursive-summation bound of the fp32
@@ -162,6 +163,32 @@ def test_half_single_with_transpose(mg, case):
     g = np.random.default_rng(zlib.crc32(repr(case).encode()))
     _run(mg, g, kind=kind, transpose=True, bits=bits, gs=gs, X=X, M=M, K=K, N=N, E=E, P=P, lhs_mode=lhs_mode,
          name=f"t {case}")
+
+
+# every width of the format (nuvec "round_trip_error_is_about_half_a_step":
+# 1-6 and 8 bits), both layouts, all three activation types
+W_CASES = [
+    # kind, transpose, bits, gs, X, M, K, N, E, P, lhs_mode
+    ("bf16", True, 3, 32, 1, 1, 4128, 37, 3, 2, "div"),     # 3 bits: two 2048-code slices and a tail
+    ("bf16", True, 5, 64, 2, 2, 320, 45, 4, 6, "idx"),
+    ("f32", True, 6, 128, 3, 3, 256, 9, 2, 3, "div"),
+    ("f16", True, 2, 64, 2, 1, 2112, 70, 3, 4, "idx"),
+    ("bf16", True, 1, 32, 1, 1, 96, 130, 2, 2, "div"),
+    ("bf16", False, 3, 32, 1, 1, 202, 2080, 3, 2, "div"),   # 65 chunks of 32 columns: a ragged strip
+    ("f32", False, 5, 64, 2, 2, 130, 192, 4, 6, "idx"),
+    ("f16", False, 6, 128, 3, 5, 64, 256, 2, 3, "div"),
+    ("bf16", False, 2, 32, 2, 16, 96, 96, 3, 4, "idx"),
+    ("f32", False, 1, 64, 1, 1, 300, 4096, 2, 2, "div"),
+]
+
+
+@pytest.mark.parametrize("case", W_CASES,
+                         ids=[f"{c[0]}-{'t' if c[1] else 'nt'}-{c[2]}b-gs{c[3]}-M{c[5]}-K{c[6]}-N{c[7]}" for c in W_CASES])
+def test_other_bit_widths(mg, case):
+    kind, tr, bits, gs, X, M, K, N, E, P, lhs_mode = case
+    g = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    _run(mg, g, kind=kind, transpose=tr, bits=bits, gs=gs, X=X, M=M, K=K, N=N, E=E, P=P, lhs_mode=lhs_mode,
+         name=f"w {case}")
 
 
 def test_split_and_unsplit_agree_with_oracle(mg):

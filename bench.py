@@ -365,7 +365,8 @@ def vec_leg(torch, m, synth, steps=42, cfg=1):
     8 of 288 experts, 4-bit, group 64): the gate projection stored without
     the transpose ([288, 4096, 2048/8] words, groups along N) with bf16
     activations, and the transposed gate projection with float32 activations
-    (float32 result).  42 index sets chained in one HIP graph, as the decode
+    (float32 result), and the transposed gate projection at 3 bits (codes
+    straddle words).  42 index sets chained in one HIP graph, as the decode
     leg does, so that weights come from HBM."""
     sh = synth.DECODE
     dev = torch.device("cuda")
@@ -373,30 +374,33 @@ def vec_leg(torch, m, synth, steps=42, cfg=1):
     E, H, I = sh.E, sh.H, sh.I
     sets = [torch.from_numpy(synth.sorted_topk(cfg, 1, E, sh.top_k, sub=i).reshape(-1)).to(dev) for i in range(42)]
     P = sh.top_k
-    per_pair = I * H * sh.bits // 8 + 2 * I * (H // sh.gs) * 2
     res = {}
     # without the transpose: the same bytes read as [E, K = H, N = I] with groups along N
     w_nt = gate[0].view(E, H, I * sh.bits // 32)
     s_nt = gate[1].view(E, H, I // sh.gs)
     b_nt = gate[2].view(E, H, I // sh.gs)
-    for name, x, w, s, b, tr, N in (
+    gate3 = synth.device_drawn_words(dev, (cfg, 0, synth.GATE, 3), (sh.E, sh.I), sh.H, sh.gs, 3)
+    for name, x, w, s, b, tr, N, bits in (
             ("no_transpose_bf16_1tok_8pairs_k4096_n2048",
-             torch.randn((1, 1, H), device=dev).to(torch.bfloat16), w_nt, s_nt, b_nt, False, I),
+             torch.randn((1, 1, H), device=dev).to(torch.bfloat16), w_nt, s_nt, b_nt, False, I, sh.bits),
             ("transpose_f32_act_1tok_8pairs_n2048_k4096",
-             torch.randn((1, 1, H), device=dev, dtype=torch.float32), *gate, True, I)):
+             torch.randn((1, 1, H), device=dev, dtype=torch.float32), *gate, True, I, sh.bits),
+            ("transpose_bf16_3bit_1tok_8pairs_n2048_k4096",
+             torch.randn((1, 1, H), device=dev).to(torch.bfloat16), *gate3, True, I, 3)):
+        per_pair = I * H * bits // 8 + 2 * I * (H // sh.gs) * 2
         odt = torch.bfloat16 if x.dtype == torch.bfloat16 else torch.float32
         out = torch.empty((P, 1, N), dtype=odt, device=dev)
-        need = m.gather_qmm_workspace_bytes(P, E, 1, N, H, m._dt(x), tr, sh.bits, False)
+        need = m.gather_qmm_workspace_bytes(P, E, 1, N, H, m._dt(x), tr, bits, False)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-        fn = lambda i, x=x, w=w, s=s, b=b, tr=tr, out=out, ws=ws: m.gather_qmm(
-            x, w, s, b, rhs_indices=sets[i % 42], transpose=tr, group_size=sh.gs, bits=sh.bits, out=out,
+        fn = lambda i, x=x, w=w, s=s, b=b, tr=tr, out=out, ws=ws, bits=bits: m.gather_qmm(
+            x, w, s, b, rhs_indices=sets[i % 42], transpose=tr, group_size=sh.gs, bits=bits, out=out,
             workspace=ws)
         us = graph_time_us(torch, fn, 42, reps=max(1, steps // 42), check=lambda out=out: out)
         nbytes = P * per_pair + H * x.element_size() + P * N * out.element_size()
-        plan_ks = m.gather_qmm_workspace_bytes(P, E, 1, N, H, m._dt(x), tr, sh.bits, False) // (P * N * 4)
+        plan_ks = need // (P * N * 4)
         res[name] = {"us": us, "gbs": nbytes / us / 1e3, "hbm_frac": nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
                      "bytes": nbytes, "k_splits": int(plan_ks) if plan_ks else 1}
-    del gate
+    del gate, gate3
     torch.cuda.empty_cache()
     return res
 

@@ -45,8 +45,9 @@ typedef enum {
   MOEGQ_ERR_DTYPE = -5,        /* integer activations, non-u32 packed words,
                                   float indices                                    */
   MOEGQ_ERR_UNSUPPORTED = -6,  /* valid for the format but not built here (bit
-                                  widths other than 4 and 8, 64-bit indices, and
-                                  the entry points whose comment says so)          */
+                                  widths other than 4 and 8 outside gather_qmm,
+                                  64-bit indices, and the entry points whose
+                                  comment says so)                                 */
   MOEGQ_ERR_WORKSPACE = -7,    /* workspace NULL or smaller than required          */
   MOEGQ_ERR_LAUNCH = -8,       /* a kernel launch failed (hipGetLastError)         */
   MOEGQ_ERR_SELFCHECK = -9,    /* fused combine differs from the unfused tail      */
@@ -101,10 +102,14 @@ size_t moegq_workspace_bytes(int op, int64_t P, int64_t E, int64_t N, int bm);
  * out      [P, M, N] in the promoted type (nuvec "reference": activation type
  *          promoted with the bf16 scale type): bf16 for BF16 activations,
  *          float32 for F16 and F32 ones.
- * Routes: bf16 activations with transpose=1 use the matrix-vector, few-row
- *          MFMA and tile kernels; transpose=0 or F16/F32 activations use the
- *          vector-unit kernels, whose K split keeps fp32 partial sums in the
- *          workspace (one matrix must be below 2 GiB, else UNSUPPORTED).
+ * bits     1, 2, 3, 4, 5, 6 or 8 (nuvec "round_trip_error_is_about_half_a_step":
+ *          the format's widths; code k of a row at bits [k*bits, (k+1)*bits) of
+ *          its little-endian word stream); group_size 32, 64 or 128.
+ * Routes: bf16 activations with transpose=1 and 4 or 8 bits use the
+ *          matrix-vector, few-row MFMA and tile kernels; transpose=0, F16/F32
+ *          activations or the other widths use the vector-unit kernels, whose
+ *          K split keeps fp32 partial sums in the workspace (one matrix must be
+ *          below 2 GiB, else UNSUPPORTED).
  * workspace/workspace_bytes: moegq_gather_qmm_workspace_bytes(...) bytes (0 when
  *          the route needs none; then NULL is accepted).  Not shared between
  *          calls that overlap on one stream or on several streams.

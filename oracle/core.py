@@ -22,6 +22,7 @@ __all__ = [
     "SUPPORTED_BITS", "SUPPORTED_GROUPS",
     "bf16_to_f64", "bf16_to_f32", "f64_to_bf16",
     "activations_f64", "promoted_type", "round_to",
+    "MX_MODES", "MX_BLOCK", "e2m1_to_f64", "e4m3_to_f64", "e8m0_to_f64", "mx_dequant", "mx_matmul", "gather_qmm_mx",
     "unpack", "dequant", "quantized_matmul", "gather_qmm", "broadcast_gather_indices",
     "silu", "switch_glu", "sort_pairs", "schedule_tiles", "naive_tiles",
     "combine", "unsort", "shared_expert", "rms_norm", "moe_prefill_layer",
@@ -197,6 +198,102 @@ def quantized_matmul(x, words, scales, biases, transpose: bool = True, gs: int =
             raise ValueError("inner sizes differ")
         y = np.matmul(xf, W)
     return round_to(y, promoted_type(xt))
+
+
+# ----------------------------------------------------------------------------
+# microscaling (mx) formats
+# ----------------------------------------------------------------------------
+# [MLX#4787] benchmark script: besides the affine modes, quantize() and
+# quantized_matmul() take mode="mxfp8" and mode="mxfp4", and those modes
+# return no biases.  READING: the pages name the modes but not their encoding;
+# the encoding taken is the OCP Microscaling (MX) one: blocks of 32 elements
+# along the packed axis share one E8M0 scale (a power of two, one byte), and
+# the elements are E4M3 (mxfp8) or E2M1 (mxfp4) floats, packed LSB-first into
+# 32-bit words like the affine codes (8 per word for mxfp4, 4 for mxfp8).
+MX_MODES = {"mxfp4": 4, "mxfp8": 8}     # element bits
+MX_BLOCK = 32
+
+
+def e2m1_to_f64(codes) -> np.ndarray:
+    """E2M1 element: sign bit 3, exponent bits 2-1 (bias 1), mantissa bit 0;
+    exponent 0 is subnormal (mantissa * 0.5).  No infinities or NaN."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, m * 0.5, np.ldexp(1.0 + m / 2.0, (e - 1).astype(np.int32)))
+    return sign * mag
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """E4M3 element: sign bit 7, exponent bits 6-3 (bias 7), mantissa bits
+    2-0; exponent 0 is subnormal (mantissa/8 * 2^-6); exponent and mantissa
+    all ones is NaN; no infinities."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32)))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e8m0_to_f64(e) -> np.ndarray:
+    """E8M0 scale: 2^(e - 127); e = 255 is NaN."""
+    e = np.asarray(e, dtype=np.int64)
+    return np.where(e == 255, np.nan, np.ldexp(1.0, (e - 127).astype(np.int32)))
+
+
+def mx_dequant(words, scales_u8, mode: str, length: int) -> np.ndarray:
+    """Elements times their block's scale along the packed (last) axis."""
+    if mode not in MX_MODES:
+        raise ValueError("mode must be mxfp4 or mxfp8")
+    if length % MX_BLOCK:
+        raise ValueError("length must be a multiple of 32")
+    bits = MX_MODES[mode]
+    q = unpack(words, length, bits)
+    v = e2m1_to_f64(q) if mode == "mxfp4" else e4m3_to_f64(q)
+    sc = e8m0_to_f64(np.asarray(scales_u8, dtype=np.uint8))
+    if sc.shape[-1] * MX_BLOCK != length:
+        raise ValueError("scales do not match the packed length")
+    return v * sc[..., np.arange(length) // MX_BLOCK]
+
+
+def mx_matmul(x, words, scales_u8, mode: str, transpose: bool = True) -> np.ndarray:
+    """x . dequant(W)^T (transpose=True, W [N, K*bits/32], blocks along K) or
+    x . dequant(W) (W [K, N*bits/32], blocks along N) for an mx mode; float64
+    sum rounded once to the promoted type (bf16 activations give bf16,
+    float16/float32 give float32, as for the affine modes)."""
+    xf, xt = activations_f64(x)
+    w = np.asarray(words)
+    if transpose:
+        W = mx_dequant(w, scales_u8, mode, xf.shape[-1])
+        y = np.matmul(xf, np.swapaxes(W, -1, -2))
+    else:
+        N = w.shape[-1] * 32 // MX_MODES[mode]
+        W = mx_dequant(w, scales_u8, mode, N)
+        if W.shape[-2] != xf.shape[-1]:
+            raise ValueError("inner sizes differ")
+        y = np.matmul(xf, W)
+    return round_to(y, promoted_type(xt))
+
+
+def gather_qmm_mx(x, words, scales_u8, lhs=None, rhs=None, transpose: bool = True, mode: str = "mxfp8"):
+    """gather_qmm for an mx mode: out[j] = x[lhs[j]] . dequant(W[rhs[j]])^T."""
+    x = np.asarray(x)
+    _, xt = activations_f64(x[..., :0])
+    w = np.asarray(words, dtype=np.uint32)
+    sc = np.asarray(scales_u8, dtype=np.uint8)
+    li, ri, shape = broadcast_gather_indices(x.shape[:-2], w.shape[:-2], lhs, rhs)
+    M = x.shape[-2]
+    xf = x.reshape((-1,) + x.shape[-2:])
+    wf = w.reshape((-1,) + w.shape[-2:])
+    sf = sc.reshape((-1,) + sc.shape[-2:])
+    N = w.shape[-2] if transpose else w.shape[-1] * 32 // MX_MODES[mode]
+    out = np.zeros((len(li), M, N), dtype=np.uint16 if promoted_type(xt) == "bf16" else np.float32)
+    for j, (l, r) in enumerate(zip(li, ri)):
+        out[j] = mx_matmul(xf[l], wf[r], sf[r], mode, transpose)
+    return out.reshape(tuple(shape) + (M, N))
 
 
 def broadcast_gather_indices(x_batch: tuple, w_batch: tuple, lhs=None, rhs=None):

@@ -628,3 +628,110 @@ def test_switch_glu_mm_matches_torch():
             hh = tb(oracle.f64_to_bf16((torch.nn.functional.silu(gg) * uu).numpy()))
             yy = oracle.f64_to_bf16((hh @ tb(down[e]).T).numpy())
             assert np.array_equal(got[t, s_], yy)
+
+
+# ----------------------------------------------------------------------------- mx formats
+def test_e4m3_and_e8m0_match_torch_decoders():
+    # every E4M3 element code and every E8M0 scale code against torch's own
+    # float8_e4m3fn / float8_e8m0fnu decoders
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256)
+    t = torch.arange(256, dtype=torch.uint8)
+    want4 = t.view(torch.float8_e4m3fn).double().numpy()
+    got4 = oracle.e4m3_to_f64(codes)
+    assert np.array_equal(np.isnan(got4), np.isnan(want4))
+    assert np.array_equal(got4[~np.isnan(got4)], want4[~np.isnan(want4)])
+    assert np.array_equal(np.signbit(got4[~np.isnan(got4)]), np.signbit(want4[~np.isnan(want4)]))
+    want8 = t.view(torch.float8_e8m0fnu).double().numpy()
+    got8 = oracle.e8m0_to_f64(codes)
+    assert np.array_equal(np.isnan(got8), np.isnan(want8))
+    assert np.array_equal(got8[:255], want8[:255])
+
+
+def test_e2m1_is_the_e4m3_subset():
+    # an E2M1 element (exponent bias 1, one mantissa bit) has the value of the
+    # E4M3 element with exponent e + 6 and mantissa 4 m (normal), or of the
+    # E4M3 subnormal-free code for 0.5 (e = 0, m = 1) and zero; checked through
+    # torch's E4M3 decoder
+    torch = pytest.importorskip("torch")
+    got = oracle.e2m1_to_f64(np.arange(16))
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        if e > 0:
+            e4 = (s << 7) | ((e + 6) << 3) | (m << 2)
+        else:
+            e4 = (s << 7) | (6 << 3) if m else (s << 7)
+        want = torch.tensor([e4], dtype=torch.uint8).view(torch.float8_e4m3fn).double().item()
+        assert got[c] == want and np.signbit(got[c]) == np.signbit(want), c
+    assert np.all(np.diff(got[:8]) > 0) and got[7] == 6.0
+
+
+def _brute_mx(x, words, scales, mode, transpose):
+    """Triple loop in exact rationals: element value (from the bit string) times
+    2^(scale - 127)."""
+    bits = oracle.MX_MODES[mode]
+    xa = np.asarray(x)
+    xvals = xa.astype(np.float64) if xa.dtype in (np.float16, np.float32) else oracle.bf16_to_f64(xa)
+    xv = [[Fraction(float(v)) for v in row] for row in xvals]
+
+    def elem(code):
+        if mode == "mxfp4":
+            s, e, m = code >> 3, (code >> 1) & 3, code & 1
+            mag = Fraction(m, 2) if e == 0 else Fraction(2) ** (e - 1) * (1 + Fraction(m, 2))
+        else:
+            s, e, m = code >> 7, (code >> 3) & 15, code & 7
+            mag = Fraction(m, 8) * Fraction(1, 64) if e == 0 else Fraction(2) ** (e - 7) * (1 + Fraction(m, 8))
+        return -mag if s else mag
+
+    rows = ["".join(format(int(v), "032b")[::-1] for v in wr) for wr in words]
+    L = len(rows[0]) // bits
+
+    def W(r, c):
+        code = int(rows[r][c * bits:(c + 1) * bits][::-1], 2)
+        return elem(code) * Fraction(2) ** (int(scales[r][c // 32]) - 127)
+
+    if transpose:
+        N, K = len(words), L
+        out = [[float(sum(xv[mm][k] * W(n, k) for k in range(K))) for n in range(N)] for mm in range(len(xv))]
+    else:
+        K, N = len(words), L
+        out = [[float(sum(xv[mm][k] * W(k, n) for k in range(K))) for n in range(N)] for mm in range(len(xv))]
+    if xa.dtype in (np.float16, np.float32):
+        return np.array(out).astype(np.float32)
+    return oracle.f64_to_bf16(np.array(out))
+
+
+@pytest.mark.parametrize("mode", ["mxfp4", "mxfp8"])
+def test_mx_matmul_brute_force(mode):
+    g = np.random.default_rng(21 if mode == "mxfp4" else 22)
+    bits = oracle.MX_MODES[mode]
+    M, N, K = 2, 3, 64
+    # codes away from E4M3's NaN pattern; scales around 2^0
+    codes = g.integers(0, 1 << bits, size=(N, K))
+    if bits == 8:
+        codes = np.where((codes & 0x7F) == 0x7F, 0x7E, codes)
+    w = synth.pack(codes, bits)
+    sc = g.integers(120, 134, size=(N, K // 32)).astype(np.uint8)
+    x = synth.to_bf16(g.standard_normal((M, K)))
+    got = oracle.mx_matmul(x, w, sc, mode, True)
+    assert np.array_equal(got, _brute_mx(x, w, sc, mode, True))
+    # without the transpose: [K'=5, N'=64] with blocks along N; float32 activations
+    codes2 = g.integers(0, 1 << bits, size=(5, 64))
+    if bits == 8:
+        codes2 = np.where((codes2 & 0x7F) == 0x7F, 0x01, codes2)
+    w2 = synth.pack(codes2, bits)
+    sc2 = g.integers(110, 140, size=(5, 2)).astype(np.uint8)
+    x2 = g.standard_normal((M, 5)).astype(np.float32)
+    got2 = oracle.mx_matmul(x2, w2, sc2, mode, False)
+    assert got2.dtype == np.float32
+    assert np.array_equal(got2, _brute_mx(x2, w2, sc2, mode, False))
+
+
+def test_mx_block_scale_applies_to_its_32_elements():
+    # one element code (1.0 in both element types) everywhere, block scales
+    # 2^0, 2^1, 2^-3: the dequantized row is 1, 2, 1/8 over the three blocks
+    for mode, one in (("mxfp4", 0b0010), ("mxfp8", 0x38)):
+        bits = oracle.MX_MODES[mode]
+        w = synth.pack(np.full((1, 96), one), bits)
+        d = oracle.mx_dequant(w, np.array([[127, 128, 124]], dtype=np.uint8), mode, 96)
+        assert d[0].tolist() == [1.0] * 32 + [2.0] * 32 + [0.125] * 32

@@ -128,6 +128,30 @@ int moegq_gather_qmm(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K
 size_t moegq_gather_qmm_workspace_bytes(int64_t P, int64_t E, int64_t M, int64_t N, int64_t K, int x_dtype,
                                         int transpose, int bits, int sorted_indices);
 
+/* mx modes of gather_qmm */
+enum { MOEGQ_MXFP4 = 1, MOEGQ_MXFP8 = 2 };
+
+/*
+ * gather_qmm_mx: gather_qmm for the microscaling modes.  MLX PR 4787's
+ * benchmark script runs quantized_matmul with mode "mxfp8" (and lists
+ * "mxfp4"), whose quantize() returns no biases.  Encoding (OCP Microscaling):
+ * elements E2M1 (MOEGQ_MXFP4, 8 per uint32 word) or E4M3 (MOEGQ_MXFP8, 4 per
+ * word), packed LSB-first like the affine codes; one E8M0 scale byte
+ * (2^(e-127), 255 = NaN) per 32 consecutive elements along the packed axis.
+ * transpose=1: w [E, N, K*bits/32] uint32, scales [E, N, K/32] uint8.
+ * transpose=0: w [E, K, N*bits/32], scales [E, K, N/32] uint8.
+ * The packed axis must be a multiple of 32 (else MOEGQ_ERR_SHAPE); mode
+ * other than the two -> MOEGQ_ERR_BITS.  Other arguments, the result type
+ * (bf16 for BF16 activations, float32 for F16/F32) and the workspace rules
+ * are those of moegq_gather_qmm; workspace bytes from
+ * moegq_gather_qmm_mx_workspace_bytes.
+ */
+int moegq_gather_qmm_mx(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K, const void* w,
+                        const void* scales, int64_t E, int64_t N, const void* lhs_indices, int64_t lhs_div,
+                        const void* rhs_indices, int idx_dtype, int64_t P, int transpose, int mode, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+size_t moegq_gather_qmm_mx_workspace_bytes(int64_t P, int64_t M, int64_t N, int64_t K, int transpose, int mode);
+
 /*
  * gather_qmm_glu: h[p] = bf16( silu(g) * u ) with g = x[lhs(p)] . dequant(wg[rhs[p]])^T
  * and u = x[lhs(p)] . dequant(wu[rhs[p]])^T, g and u rounded to bf16 first:

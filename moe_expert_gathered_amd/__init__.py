@@ -16,7 +16,8 @@ import os
 
 import torch
 
-__all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "quantized_matmul", "gather_qmm_workspace_bytes", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
+__all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "quantized_matmul", "gather_qmm_workspace_bytes",
+           "gather_qmm_mx", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
            "switch_glu", "switch_glu_mode", "moe_decode", "moe_prefill", "moe_prefill_workspace_bytes", "moe_combine", "moe_combine_gated", "moe_combine_unfused", "sort_pairs",
            "schedule_tiles", "rms_norm", "sigmoid_gate", "route", "gather_mm", "kv_feed", "selfcheck",
            "validate_indices", "workspace_bytes", "MODE_AUTO", "MODE_DECODE", "MODE_SORTED",
@@ -29,6 +30,7 @@ OK = 0
 BF16, F16, F32, F64, I32, U32, I64 = range(7)
 MODE_AUTO, MODE_DECODE, MODE_SORTED = 0, 1, 2
 TILES_SCHEDULED, TILES_NAIVE = 0, 1
+MX_MODES = {"mxfp4": (1, 4), "mxfp8": (2, 8)}     # mode code, element bits
 OP_GATHER_QMM, OP_SWITCH_GLU_DECODE, OP_SWITCH_GLU_SORTED, OP_COMBINE_UNFUSED, OP_SELFCHECK, OP_SORT_PAIRS, \
     OP_MOE_DECODE, OP_GATHER_MM = range(8)
 
@@ -52,6 +54,9 @@ _SIGS = {
     "moegq_version": ([], ctypes.c_char_p),
     "moegq_workspace_bytes": ([_int, _i64, _i64, _i64, _int], _sz),
     "moegq_gather_qmm_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64, _int, _int, _int, _int], _sz),
+    "moegq_gather_qmm_mx": ([_p, _int, _i64, _i64, _i64, _p, _p, _i64, _i64, _p, _i64, _p, _int, _i64, _int, _int,
+                             _p, _p, _sz, _p], _int),
+    "moegq_gather_qmm_mx_workspace_bytes": ([_i64, _i64, _i64, _i64, _int, _int], _sz),
     "moegq_gather_qmm": ([_p, _int, _i64, _i64, _i64, _p, _int, _p, _p, _i64, _i64, _p, _i64, _p, _int, _i64,
                           _int, _int, _int, _int, _p, _p, _sz, _p], _int),
     "moegq_gather_qmm_glu": ([_p, _int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _i64, _p, _i64, _p, _int,
@@ -142,22 +147,10 @@ def _workspace(nbytes: int, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
-# ----------------------------------------------------------------------------- ops
-def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, transpose=True,
-               group_size=64, bits=4, sorted_indices=False, out=None, workspace=None):
-    """out[j] = x[lhs[j]] . dequant(w[rhs[j]])^T over the broadcast index shape.
-
-    x: [*bx, M, K]; w: [E, N, K*bits/32] (or [*bw, N, Kw], flattened to E).
-    With x of shape [B, 1, 1, K] and rhs [B, top_k] (the MoE decode layout)
-    the x row of pair (b, k) is b, passed as lhs_div = top_k without building
-    an index array.  Otherwise indices are broadcast (marshalling only).
-    Output: index shape + [M, N], bf16 for bf16 activations, float32 for
-    float16/float32 ones.  transpose=False takes w [E, K, N*bits/32] with
-    groups along N.  workspace: an optional uint8 device tensor of at least
-    gather_qmm_workspace_bytes(...) bytes (else one is allocated).
-    """
-    _dev(x, w, scales, biases, rhs_indices, lhs_indices, workspace)
-    M, K = x.shape[-2], x.shape[-1]
+def _gather_indices(x, w, rhs_indices, lhs_indices):
+    """Flattened (lhs, rhs) pair indices over the broadcast index shape
+    (marshalling only).  With x's batch a prefix of the index shape, the x
+    batch of flat pair p is p // lhs_div and no lhs array is built."""
     xb, wb = tuple(x.shape[:-2]), tuple(w.shape[:-2])
     X = 1
     for d in xb:
@@ -165,7 +158,6 @@ def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, transpo
     E = 1
     for d in wb:
         E *= d
-    N = w.shape[-2] if transpose else w.shape[-1] * 32 // bits
     lhs_div = 1
     li = None
     if rhs_indices is None:
@@ -190,6 +182,27 @@ def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, transpo
         lb, rb = torch.broadcast_tensors(lhs_indices, rhs_indices)
         shape = tuple(lb.shape)
         li, ri = lb.reshape(-1).contiguous(), rb.reshape(-1).contiguous()
+    return X, E, li, ri, lhs_div, shape
+
+
+# ----------------------------------------------------------------------------- ops
+def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, transpose=True,
+               group_size=64, bits=4, sorted_indices=False, out=None, workspace=None):
+    """out[j] = x[lhs[j]] . dequant(w[rhs[j]])^T over the broadcast index shape.
+
+    x: [*bx, M, K]; w: [E, N, K*bits/32] (or [*bw, N, Kw], flattened to E).
+    With x of shape [B, 1, 1, K] and rhs [B, top_k] (the MoE decode layout)
+    the x row of pair (b, k) is b, passed as lhs_div = top_k without building
+    an index array.  Otherwise indices are broadcast (marshalling only).
+    Output: index shape + [M, N], bf16 for bf16 activations, float32 for
+    float16/float32 ones.  transpose=False takes w [E, K, N*bits/32] with
+    groups along N.  workspace: an optional uint8 device tensor of at least
+    gather_qmm_workspace_bytes(...) bytes (else one is allocated).
+    """
+    _dev(x, w, scales, biases, rhs_indices, lhs_indices, workspace)
+    M, K = x.shape[-2], x.shape[-1]
+    N = w.shape[-2] if transpose else w.shape[-1] * 32 // bits
+    X, E, li, ri, lhs_div, shape = _gather_indices(x, w, rhs_indices, lhs_indices)
     P = int(ri.numel())
     idx_dt = _dt(ri)
     if li is not None and li.dtype != ri.dtype:
@@ -210,19 +223,55 @@ def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, transpo
     return out
 
 
-def quantized_matmul(x, w, scales, biases, transpose=True, group_size=64, bits=4, out=None):
+def gather_qmm_mx(x, w, scales, rhs_indices=None, lhs_indices=None, transpose=True, mode="mxfp8", out=None,
+                  workspace=None):
+    """gather_qmm for the mx modes ("mxfp4": E2M1 elements, 8 per word;
+    "mxfp8": E4M3, 4 per word), one E8M0 scale byte per 32 elements along the
+    packed axis (scales: uint8 tensor), no biases.  Indices and result type
+    as gather_qmm."""
+    _dev(x, w, scales, rhs_indices, lhs_indices, workspace)
+    code, bits = MX_MODES[mode]
+    M, K = x.shape[-2], x.shape[-1]
+    N = w.shape[-2] if transpose else w.shape[-1] * 32 // bits
+    X, E, li, ri, lhs_div, shape = _gather_indices(x, w, rhs_indices, lhs_indices)
+    P = int(ri.numel())
+    if li is not None and li.dtype != ri.dtype:
+        raise ValueError("lhs and rhs indices must share a dtype")
+    if out is None:
+        odt = torch.bfloat16 if x.dtype == torch.bfloat16 else torch.float32
+        out = torch.empty(shape + (M, N), dtype=odt, device=x.device)
+    need = int(lib().moegq_gather_qmm_mx_workspace_bytes(P, M, N, K, int(bool(transpose)), code))
+    if workspace is not None and workspace.numel() >= need:
+        ws, wsb = workspace, int(workspace.numel())
+    else:
+        ws, wsb = _workspace(need, x.device)
+    st = lib().moegq_gather_qmm_mx(_ptr(x), _dt(x), X, M, K, _ptr(w), _ptr(scales), E, N, _ptr(li), lhs_div,
+                                   _ptr(ri), _dt(ri), P, int(bool(transpose)), code, _ptr(out), _ptr(ws), wsb,
+                                   _stream())
+    _check(st, "gather_qmm_mx")
+    return out
+
+
+def quantized_matmul(x, w, scales, biases=None, transpose=True, group_size=64, bits=4, mode="affine", out=None):
     """x . dequant(w)^T (or x . dequant(w) without the transpose) with the
     leading batch axes of x [*bx, M, K] and w [*bw, rows, words] broadcast
     together; the result type is bf16 for bf16 activations, float32 for
-    float16 and float32 ones.  Runs as gather_qmm over the broadcast batch
-    indices (marshalling only)."""
+    float16 and float32 ones.  mode "affine" (scales and biases, group_size,
+    bits) or "mxfp4" / "mxfp8" (E8M0 scale bytes, no biases).  Runs as
+    gather_qmm over the broadcast batch indices (marshalling only)."""
     xb, wb = tuple(x.shape[:-2]), tuple(w.shape[:-2])
     M = x.shape[-2]
-    N = w.shape[-2] if transpose else w.shape[-1] * 32 // bits
+    eb = bits if mode == "affine" else MX_MODES[mode][1]
+    N = w.shape[-2] if transpose else w.shape[-1] * 32 // eb
     shape = tuple(torch.broadcast_shapes(xb, wb))
     x3 = x if x.dim() >= 3 else x.reshape((1,) * (3 - x.dim()) + tuple(x.shape))
     w3 = w if w.dim() >= 3 else w.reshape((1,) + tuple(w.shape))
     s3 = scales if scales.dim() >= 3 else scales.reshape((1,) + tuple(scales.shape))
+    if mode != "affine":
+        if biases is not None:
+            raise ValueError("mx modes take no biases")
+        res = gather_qmm_mx(x3, w3, s3, transpose=transpose, mode=mode, out=out)
+        return res.reshape(shape + (M, N))
     b3 = biases if biases.dim() >= 3 else biases.reshape((1,) + tuple(biases.shape))
     res = gather_qmm(x3, w3, s3, b3, transpose=transpose, group_size=group_size, bits=bits,
                      out=out)

@@ -246,19 +246,24 @@ size_t moegq_gather_qmm_workspace_bytes(int64_t P, int64_t E, int64_t M, int64_t
 static int gather_vec(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K, const void* w,
                       const void* scales, const void* biases, int64_t E, int64_t N, const void* lhs_indices,
                       int64_t lhs_div, const void* rhs_indices, int64_t P, int transpose, int group_size,
-                      int bits, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                      int bits, void* out, void* workspace, size_t workspace_bytes, void* stream, int mode = 0) {
   int st;
-  // the quantized axis: K with the transpose, N without it
-  if ((st = check_quant_any(transpose ? K : N, group_size, bits))) return st;
+  // the quantized axis: K with the transpose, N without it (mx: blocks of 32)
+  if (mode) {
+    const int64_t L = transpose ? K : N;
+    if (L <= 0 || L > kMaxDim || L % 32 != 0) return MOEGQ_ERR_SHAPE;
+  } else if ((st = check_quant_any(transpose ? K : N, group_size, bits))) {
+    return st;
+  }
   if (K <= 0 || K > kMaxDim || M > kMaxDim) return MOEGQ_ERR_SHAPE;
   // one expert matrix must fit a 2 GiB buffer range (32-bit offsets)
   if (K * N * bits / 8 >= ((int64_t)1 << 31)) return MOEGQ_ERR_UNSUPPORTED;
   if (!lhs_indices && lhs_div < 1) return MOEGQ_ERR_SHAPE;
   if (P == 0 || M == 0 || N == 0) return MOEGQ_OK;
-  if (!x || !w || !scales || !biases || !rhs_indices || !out) return MOEGQ_ERR_NULL_ARG;
+  if (!x || !w || !scales || (!biases && !mode) || !rhs_indices || !out) return MOEGQ_ERR_NULL_ARG;
   if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return MOEGQ_ERR_ALIGN;
   if (!lhs_indices && (P - 1) / lhs_div >= X) return MOEGQ_ERR_SHAPE;
-  const VecPlan pl = vec_plan(P, M, N, K, bits, transpose);
+  const VecPlan pl = vec_plan(P, M, N, K, bits, transpose, mode);
   if (pl.part_bytes && (!workspace || workspace_bytes < pl.part_bytes)) return MOEGQ_ERR_WORKSPACE;
   if (pl.part_bytes && !aligned16(workspace)) return MOEGQ_ERR_ALIGN;
   VecArgs a{};
@@ -266,6 +271,7 @@ static int gather_vec(const void* x, int x_dtype, int64_t X, int64_t M, int64_t 
   a.lhs = (const int32_t*)lhs_indices; a.lhs_div = lhs_div; a.rhs = (const int32_t*)rhs_indices;
   a.P = P; a.M = (int)M; a.N = (int)N; a.K = (int)K; a.gs = group_size;
   a.w = (const uint32_t*)w; a.s = (const uint16_t*)scales; a.b = (const uint16_t*)biases;
+  a.mode = mode;
   a.out = out; a.out_f32 = x_dtype != MOEGQ_BF16;
   a.part = (float*)workspace;
   a.MB = pl.MB; a.MBLK = pl.MBLK; a.WPL = pl.WPL; a.NC = pl.NC; a.KS = pl.KS; a.kchunk = pl.kchunk;
@@ -363,6 +369,27 @@ int moegq_gather_qmm(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K
   return gather_impl(x, x_dtype, X, M, K, w, w_dtype, scales, biases, nullptr, nullptr, nullptr, false, E, N,
                      lhs_indices, lhs_div, rhs_indices, idx_dtype, P, sorted_indices, transpose, group_size,
                      bits, out, workspace, workspace_bytes, stream);
+}
+
+int moegq_gather_qmm_mx(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K, const void* w,
+                        const void* scales, int64_t E, int64_t N, const void* lhs_indices, int64_t lhs_div,
+                        const void* rhs_indices, int idx_dtype, int64_t P, int transpose, int mode, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  int st;
+  if ((st = check_any_act_dtype(x_dtype))) return st;
+  if ((st = check_idx_dtype(idx_dtype))) return st;
+  if (mode != MOEGQ_MXFP4 && mode != MOEGQ_MXFP8) return MOEGQ_ERR_BITS;
+  if (X < 0 || M < 0 || E <= 0 || N < 0 || P < 0 || X > kMaxDim || N > kMaxDim || P > kMaxDim)
+    return MOEGQ_ERR_SHAPE;
+  const int bits = mode == MOEGQ_MXFP4 ? 4 : 8;
+  return gather_vec(x, x_dtype, X, M, K, w, scales, nullptr, E, N, lhs_indices, lhs_div, rhs_indices, P,
+                    transpose, 32, bits, out, workspace, workspace_bytes, stream, mode);
+}
+
+size_t moegq_gather_qmm_mx_workspace_bytes(int64_t P, int64_t M, int64_t N, int64_t K, int transpose, int mode) {
+  if (P <= 0 || M <= 0 || N <= 0 || K <= 0) return 0;
+  if (mode != MOEGQ_MXFP4 && mode != MOEGQ_MXFP8) return 0;
+  return vec_plan(P, M, N, K, mode == MOEGQ_MXFP4 ? 4 : 8, transpose, mode).part_bytes;
 }
 
 int moegq_gather_qmm_glu(const void* x, int x_dtype, int64_t X, int64_t M, int64_t K, const void* wg,

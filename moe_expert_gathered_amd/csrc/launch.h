@@ -138,13 +138,15 @@ struct VecPlan {
   int64_t items;                       // waves
   size_t part_bytes;                   // fp32 partial sums (workspace) when KS > 1
 };
-VecPlan vec_plan(int64_t P, int64_t M, int64_t N, int64_t K, int bits, int transpose);
+// mode 0: affine codes (bits 1-6, 8); 1: mxfp4; 2: mxfp8
+VecPlan vec_plan(int64_t P, int64_t M, int64_t N, int64_t K, int bits, int transpose, int mode = 0);
 struct VecArgs {
   const void* x; int x_type;           // [X, M, K]; 0 bf16, 1 float16, 2 float32
   const int32_t* lhs; int64_t lhs_div; // x batch per pair (or p / lhs_div)
   const int32_t* rhs;                  // weight batch per pair (or 0)
   int64_t P; int M, N, K, gs;
-  const uint32_t* w; const uint16_t* s; const uint16_t* b;
+  const uint32_t* w; const uint16_t* s; const uint16_t* b;   // mx modes: s holds E8M0 bytes, b unused
+  int mode;                            // 0 affine, 1 mxfp4, 2 mxfp8
   void* out; int out_f32;              // [P, M, N] bf16 or float32
   float* part;                         // [KS, P, M, N] when KS > 1
   int MB, MBLK, WPL, NC, KS, kchunk;   // from vec_plan

@@ -13,6 +13,13 @@
 // stream, so 3-, 5- and 6-bit codes straddle words.  MLX issue 4509, gq():
 // gather_qmm over (lhs, rhs) index pairs; nuvec "gather_qmm_selects_batches".
 //
+// The mx modes (MLX PR 4787 benchmark script: mode "mxfp4" / "mxfp8", no
+// biases) read their elements as E2M1 / E4M3 floats, 32 per block along the
+// packed axis, each block scaled by an E8M0 power of two (the OCP
+// Microscaling encoding): the gfx950 conversions v_cvt_scalef32_pk_f32_fp4 /
+// _fp8 turn two elements into fp32 per instruction, and the block scale
+// multiplies the block's dot product.
+//
 // Arithmetic: fp32 throughout.  For one group g of a weight row,
 //   sum_k x_k (q_k s + b) = s * sum_k x_k q_k + b * sum_k x_k,
 // the group identity of the affine code (nuvec "composed": codes * s + b).
@@ -96,6 +103,53 @@ MOEGQ_DEV void codes_f(const uint32_t (&w)[CH * BITS / 32], float (&q)[CH]) {
   }
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// The CH elements of a chunk as floats, by mode: 0 the affine codes, 1 E2M1
+// (code k in the nibble at bit 4k, two per byte), 2 E4M3 (one per byte).
+template <int BITS, int CH, int MODE>
+MOEGQ_DEV void elems_f(const uint32_t (&w)[CH * BITS / 32], float (&q)[CH]) {
+  if constexpr (MODE == 0) {
+    codes_f<BITS, CH>(w, q);
+  } else if constexpr (MODE == 1) {
+#pragma unroll
+    for (int i = 0; i < CH / 8; ++i) {
+      const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 0);
+      const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 1);
+      const f32x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 2);
+      const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 3);
+      q[8 * i] = a.x; q[8 * i + 1] = a.y; q[8 * i + 2] = b.x; q[8 * i + 3] = b.y;
+      q[8 * i + 4] = c.x; q[8 * i + 5] = c.y; q[8 * i + 6] = d.x; q[8 * i + 7] = d.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CH / 4; ++i) {
+      const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[i], 1.0f, false);
+      const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[i], 1.0f, true);
+      q[4 * i] = a.x; q[4 * i + 1] = a.y; q[4 * i + 2] = b.x; q[4 * i + 3] = b.y;
+    }
+  }
+}
+
+// E8M0 block scale: 2^(e - 127) as an fp32 (e = 0 gives the subnormal 2^-127,
+// e = 255 NaN)
+MOEGQ_DEV float e8m0_f32(uint32_t e) {
+  if (e == 255u) return __uint_as_float(0x7FC00000u);
+  return e == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);
+}
+
+// scale (and bias) loads: bf16 per group, or one byte per mx block
+template <int MODE>
+MOEGQ_DEV uint16_t load_scale(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (MODE == 0) return buf_load2(r, voff, soff);
+  else return (uint16_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+template <int MODE>
+MOEGQ_DEV float scale_f(uint16_t v) {
+  if constexpr (MODE == 0) return bf16_to_f32(v);
+  else return e8m0_f32(v);
+}
+
 // NV (a multiple of 8) consecutive activations at byte offset `off` of the
 // row descriptor r, as floats; an offset past the range gives zeros
 template <int XT, int NV>
@@ -147,8 +201,10 @@ MOEGQ_DEV VecItem vec_item(const VecArgs& A, int64_t item, bool cs_fast) {
 }
 
 // ---------------------------------------------------------------- without the transpose
-template <int BITS, int XT, int MB, int CH, int U>
+template <int BITS, int XT, int MB, int CH, int U, int MODE>
 __global__ __launch_bounds__(256) void qvm_kernel(VecArgs A) {
+  constexpr bool MX = MODE != 0;        // mx block scales: one byte per 32 columns, no biases
+  constexpr int SSZ = MX ? 1 : 2;
   constexpr int NW = CH * BITS / 32;    // words per lane per row
   __shared__ float red[3][CH][64];      // waves 1..3, one activation row at a time
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -157,12 +213,12 @@ __global__ __launch_bounds__(256) void qvm_kernel(VecArgs A) {
   if (item >= A.items) return;                       // the whole workgroup leaves
   const VecItem it = vec_item(A, item, false);
   const int K = A.K, N = A.N, M = A.M;
-  const int Nw = N / 32 * BITS, G = N / A.gs;        // N is a multiple of 32
+  const int Nw = N / 32 * BITS, G = N / (MX ? 32 : A.gs);   // N is a multiple of 32
   const int64_t xb = A.lhs ? (int64_t)A.lhs[it.p] : it.p / A.lhs_div;
   const int64_t e = A.rhs ? (int64_t)A.rhs[it.p] : 0;
   const int col0 = (it.cs * 64 + lane) * CH;         // first of the lane's columns
   const bool act = col0 < N;
-  const uint32_t g2 = act ? (uint32_t)(col0 / A.gs) * 2 : kVecNoFetch;
+  const uint32_t g2 = act ? (uint32_t)(col0 / (MX ? 32 : A.gs)) * SSZ : kVecNoFetch;
   const uint32_t wo = act ? (uint32_t)(col0 * BITS / 32) * 4 : kVecNoFetch;   // CH * BITS is a multiple of 32
   const int k0 = it.ks * A.kchunk;
   const int k1 = min(K, k0 + A.kchunk);
@@ -172,8 +228,9 @@ __global__ __launch_bounds__(256) void qvm_kernel(VecArgs A) {
   const int nr = k1 > kw ? (k1 - kw + 3) / 4 : 0;    // rows of this wave
 
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(A.w + e * (int64_t)K * Nw, (uint32_t)((int64_t)K * Nw * 4));
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(A.s + e * (int64_t)K * G, (uint32_t)((int64_t)K * G * 2));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(A.b + e * (int64_t)K * G, (uint32_t)((int64_t)K * G * 2));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(A.s) + e * (int64_t)K * G * SSZ,
+                                              (uint32_t)((int64_t)K * G * SSZ));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(MX ? A.s : A.b + e * (int64_t)K * G, MX ? 0u : (uint32_t)((int64_t)K * G * 2));
   const int64_t xrow0 = (xb * M + m0) * (int64_t)K;
   constexpr int XSZ = XT == 2 ? 4 : 2;
   __amdgpu_buffer_rsrc_t rx[MB];                      // one descriptor per activation row (empty past M)
@@ -211,24 +268,25 @@ __global__ __launch_bounds__(256) void qvm_kernel(VecArgs A) {
       const bool ok = j + u < nr;                     // uniform
       const uint32_t row = ok ? (uint32_t)(kw + 4 * (j + u)) : 0u;
       load_words<NW>(rw, ok ? wo : kVecNoFetch, row * Nw * 4, cw[u]);
-      sv[u] = buf_load2(rs, ok ? g2 : kVecNoFetch, row * G * 2);
-      bv[u] = buf_load2(rb, ok ? g2 : kVecNoFetch, row * G * 2);
+      sv[u] = load_scale<MODE>(rs, ok ? g2 : kVecNoFetch, row * G * SSZ);
+      bv[u] = MX ? (uint16_t)0 : buf_load2(rb, ok ? g2 : kVecNoFetch, row * G * 2);
     }
     // rows past nr loaded zeros (codes, scale, bias) and their activation
     // lanes hold zero: they add nothing, and no branch separates the loads
     // above from the arithmetic below
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float s = bf16_to_f32(sv[u]), b = bf16_to_f32(bv[u]);
+      // rows past nr: scale byte 0 (2^-127) times zero elements and zero activations
+      const float s = scale_f<MODE>(sv[u]), b = bf16_to_f32(bv[u]);
       float xs[MB];
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         const float xm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xl[m]), u));
         xs[m] = xm * s;
-        bacc[m] = fmaf(xm, b, bacc[m]);
+        if constexpr (!MX) bacc[m] = fmaf(xm, b, bacc[m]);
       }
       float q[CH];
-      codes_f<BITS, CH>(cw[u], q);
+      elems_f<BITS, CH, MODE>(cw[u], q);
 #pragma unroll
       for (int c = 0; c < CH; ++c)
 #pragma unroll
@@ -283,16 +341,18 @@ struct QmtSlice {
   float x[MB][32];
 };
 
-template <int BITS, int XT, int MB, int RPW>
+template <int BITS, int XT, int MB, int RPW, int MODE>
 __global__ __launch_bounds__(256) void qmt_kernel(VecArgs A) {
   using Slice = QmtSlice<BITS, MB, RPW>;
+  constexpr bool MX = MODE != 0;        // mx block scales: one byte per 32 codes, no biases
+  constexpr int SSZ = MX ? 1 : 2;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + wave;
   if (item >= A.items) return;                       // whole waves leave together
   const VecItem it = vec_item(A, item, true);
   const int K = A.K, N = A.N, M = A.M;
-  const int Kw = K / 32 * BITS, G = K / A.gs;        // K is a multiple of 32
+  const int Kw = K / 32 * BITS, G = K / (MX ? 32 : A.gs);   // K is a multiple of 32
   const int64_t xb = A.lhs ? (int64_t)A.lhs[it.p] : it.p / A.lhs_div;
   const int64_t e = A.rhs ? (int64_t)A.rhs[it.p] : 0;
   const int n0 = it.cs * RPW;
@@ -302,8 +362,9 @@ __global__ __launch_bounds__(256) void qmt_kernel(VecArgs A) {
   const int nm = min(MB, M - m0);
 
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(A.w + e * (int64_t)N * Kw, (uint32_t)((int64_t)N * Kw * 4));
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(A.s + e * (int64_t)N * G, (uint32_t)((int64_t)N * G * 2));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(A.b + e * (int64_t)N * G, (uint32_t)((int64_t)N * G * 2));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(A.s) + e * (int64_t)N * G * SSZ,
+                                              (uint32_t)((int64_t)N * G * SSZ));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(MX ? A.s : A.b + e * (int64_t)N * G, MX ? 0u : (uint32_t)((int64_t)N * G * 2));
   constexpr int XSZ = XT == 2 ? 4 : 2;
   __amdgpu_buffer_rsrc_t rx[MB];                      // one descriptor per activation row (empty past M)
 #pragma unroll
@@ -314,15 +375,15 @@ __global__ __launch_bounds__(256) void qmt_kernel(VecArgs A) {
   auto load = [&](int sc, Slice& S) {
     const int kc = sc + 32 * lane;                    // the lane's first code
     const bool ok = kc < kc1;                         // kc1 is a multiple of 32
-    const uint32_t g2 = ok ? (uint32_t)(kc / A.gs) * 2 : kVecNoFetch;
+    const uint32_t g2 = ok ? (uint32_t)(kc / (MX ? 32 : A.gs)) * SSZ : kVecNoFetch;
     const uint32_t wo = ok ? (uint32_t)(kc / 32 * BITS) * 4 : kVecNoFetch;
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const bool rok = ok && n0 + r < N;
       const uint32_t row = (uint32_t)min(n0 + r, N - 1);
       load_words<BITS>(rw, rok ? wo : kVecNoFetch, row * Kw * 4, S.c[r]);
-      S.s[r] = buf_load2(rs, rok ? g2 : kVecNoFetch, row * G * 2);
-      S.b[r] = buf_load2(rb, rok ? g2 : kVecNoFetch, row * G * 2);
+      S.s[r] = load_scale<MODE>(rs, rok ? g2 : kVecNoFetch, row * G * SSZ);
+      S.b[r] = MX ? (uint16_t)0 : buf_load2(rb, rok ? g2 : kVecNoFetch, row * G * 2);
     }
 #pragma unroll
     for (int m = 0; m < MB; ++m) load_acts<XT>(rx[m], ok ? (uint32_t)kc * XSZ : kVecNoFetch, S.x[m]);
@@ -342,7 +403,7 @@ __global__ __launch_bounds__(256) void qmt_kernel(VecArgs A) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       float q[32];
-      codes_f<BITS, 32>(S.c[r], q);
+      elems_f<BITS, 32, MODE>(S.c[r], q);
       float d[MB];
 #pragma unroll
       for (int m = 0; m < MB; ++m) d[m] = 0.f;
@@ -350,9 +411,12 @@ __global__ __launch_bounds__(256) void qmt_kernel(VecArgs A) {
       for (int c = 0; c < 32; ++c)
 #pragma unroll
         for (int m = 0; m < MB; ++m) d[m] = fmaf(S.x[m][c], q[c], d[m]);
-      const float s = bf16_to_f32(S.s[r]), b = bf16_to_f32(S.b[r]);
+      const float s = scale_f<MODE>(S.s[r]), b = bf16_to_f32(S.b[r]);
 #pragma unroll
-      for (int m = 0; m < MB; ++m) acc[m * RPW + r] = fmaf(s, d[m], fmaf(b, sx[m], acc[m * RPW + r]));
+      for (int m = 0; m < MB; ++m) {
+        if constexpr (MX) acc[m * RPW + r] = fmaf(s, d[m], acc[m * RPW + r]);
+        else acc[m * RPW + r] = fmaf(s, d[m], fmaf(b, sx[m], acc[m * RPW + r]));
+      }
     }
   };
 
@@ -404,14 +468,14 @@ constexpr int64_t kVecPartMax = (int64_t)1 << 26;   // bytes of partial sums at 
 
 static int qmt_rows(int bits) { return bits <= 4 ? 8 : 4; }
 
-VecPlan vec_plan(int64_t P, int64_t M, int64_t N, int64_t K, int bits, int transpose) {
+VecPlan vec_plan(int64_t P, int64_t M, int64_t N, int64_t K, int bits, int transpose, int mode) {
   VecPlan pl{};
   int64_t items0, steps, target;
   if (!transpose) {
     // workgroup items; a split takes at least 64 weight rows (16 per wave)
     pl.MB = M >= 3 ? 4 : (int)M;
     // codes per lane: 32, or one word (4-bit, 8-bit) when the row is narrow
-    pl.WPL = ((bits == 4 || bits == 8) && N < 2048) ? 32 / bits : 32;
+    pl.WPL = (mode == 0 && (bits == 4 || bits == 8) && N < 2048) ? 32 / bits : 32;
     pl.NC = (N + 64 * pl.WPL - 1) / (64 * pl.WPL);
     steps = (K + 63) / 64;
     target = kVecWaves / 4;
@@ -440,15 +504,15 @@ VecPlan vec_plan(int64_t P, int64_t M, int64_t N, int64_t K, int bits, int trans
   return pl;
 }
 
-template <int BITS, int XT>
+template <int BITS, int XT, int MODE>
 static hipError_t launch_vec_t(const VecArgs& a, int transpose, hipStream_t st) {
   const dim3 block(256);
   if (!transpose) {
     const dim3 grid((unsigned)a.items);                       // one workgroup per item
 #define MOEGQ_QVM(RB, CC, UU) \
-  if (a.MB == RB && a.WPL == CC) { hipLaunchKernelGGL((qvm_kernel<BITS, XT, RB, CC, UU>), grid, block, 0, st, a); return hipGetLastError(); }
+  if (a.MB == RB && a.WPL == CC) { hipLaunchKernelGGL((qvm_kernel<BITS, XT, RB, CC, UU, MODE>), grid, block, 0, st, a); return hipGetLastError(); }
     MOEGQ_QVM(1, 32, 16) MOEGQ_QVM(2, 32, 8) MOEGQ_QVM(4, 32, 8)
-    if constexpr (BITS == 4 || BITS == 8) {
+    if constexpr (MODE == 0 && (BITS == 4 || BITS == 8)) {
       MOEGQ_QVM(1, 32 / BITS, 16) MOEGQ_QVM(2, 32 / BITS, 8) MOEGQ_QVM(4, 32 / BITS, 8)
     }
 #undef MOEGQ_QVM
@@ -456,18 +520,18 @@ static hipError_t launch_vec_t(const VecArgs& a, int transpose, hipStream_t st) 
     const dim3 grid((unsigned)((a.items + 3) / 4));           // one wave per item
     constexpr int R = BITS <= 4 ? 8 : 4;
 #define MOEGQ_QMT(RB) \
-  if (a.MB == RB) { hipLaunchKernelGGL((qmt_kernel<BITS, XT, RB, R>), grid, block, 0, st, a); return hipGetLastError(); }
+  if (a.MB == RB) { hipLaunchKernelGGL((qmt_kernel<BITS, XT, RB, R, MODE>), grid, block, 0, st, a); return hipGetLastError(); }
     MOEGQ_QMT(1) MOEGQ_QMT(2)
 #undef MOEGQ_QMT
   }
   return hipErrorInvalidValue;
 }
 
-template <int BITS>
+template <int BITS, int MODE = 0>
 static hipError_t launch_vec_bits(const VecArgs& a, int transpose, hipStream_t st) {
-  if (a.x_type == 0) return launch_vec_t<BITS, 0>(a, transpose, st);
-  if (a.x_type == 1) return launch_vec_t<BITS, 1>(a, transpose, st);
-  if (a.x_type == 2) return launch_vec_t<BITS, 2>(a, transpose, st);
+  if (a.x_type == 0) return launch_vec_t<BITS, 0, MODE>(a, transpose, st);
+  if (a.x_type == 1) return launch_vec_t<BITS, 1, MODE>(a, transpose, st);
+  if (a.x_type == 2) return launch_vec_t<BITS, 2, MODE>(a, transpose, st);
   return hipErrorInvalidValue;
 }
 
@@ -475,7 +539,9 @@ hipError_t launch_qmm_vec(const VecArgs& a, int bits, int transpose, hipStream_t
   if (a.items <= 0) return hipSuccess;
   if (a.items >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   hipError_t e = hipErrorInvalidValue;
-  switch (bits) {
+  if (a.mode == 1) e = bits == 4 ? launch_vec_bits<4, 1>(a, transpose, st) : hipErrorInvalidValue;
+  else if (a.mode == 2) e = bits == 8 ? launch_vec_bits<8, 2>(a, transpose, st) : hipErrorInvalidValue;
+  else switch (bits) {
     case 1: e = launch_vec_bits<1>(a, transpose, st); break;
     case 2: e = launch_vec_bits<2>(a, transpose, st); break;
     case 3: e = launch_vec_bits<3>(a, transpose, st); break;

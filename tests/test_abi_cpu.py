@@ -106,6 +106,25 @@ def test_gather_qmm_workspace_query(L):
                                   None, 0, None) == -6
 
 
+def test_gather_qmm_mx_validates(L):
+    import moe_expert_gathered_amd as m
+    p = FAKE
+    mx = lambda **kw: L.moegq_gather_qmm_mx(*[kw.get(k, v) for k, v in (
+        ("x", p), ("xd", 0), ("X", 4), ("M", 1), ("K", 256), ("w", p), ("s", p), ("E", 8), ("N", 64), ("lhs", None),
+        ("div", 1), ("rhs", p), ("idt", 4), ("P", 4), ("tr", 1), ("mode", 2), ("out", p), ("ws", None), ("wsb", 0),
+        ("st", None))])
+    assert mx(mode=0) == -2 and mx(mode=3) == -2     # only mxfp4 (1) and mxfp8 (2)
+    assert mx(K=200) == -4                            # blocks of 32 along the packed axis
+    assert mx(tr=0, N=48) == -4
+    assert mx(xd=m.F64) == -5 and mx(idt=m.F32) == -5
+    assert mx(rhs=None) == -1 and mx(s=None) == -1
+    assert mx(P=0, x=None, w=None, s=None, out=None, rhs=None) == 0
+    assert mx(X=1, P=1, N=4096, K=4096, tr=0) == -7  # the K split needs its workspace
+    q = L.moegq_gather_qmm_mx_workspace_bytes
+    assert q(1, 1, 4096, 4096, 0, 2) == 64 * 4096 * 4 and q(1, 1, 4096, 4096, 0, 5) == 0
+    assert q(4096, 1, 64, 256, 1, 1) == 0
+
+
 def test_other_entry_points_validate(L):
     p = FAKE
     # affine_qmm: inner-size / group checks

@@ -260,3 +260,125 @@ def test_empty_and_degenerate(mg):
     # zero activations give exactly zero
     z = _gather(mg, x, words(w), bf(s), bf(b), i32([1]), None, False, 32, 4)
     assert torch.count_nonzero(z).item() == 0
+
+
+# ----------------------------------------------------------------------------- mx modes
+def _mx_weights(g, E, rows, cols, mode, nan_free=True):
+    """E matrices [rows, cols] of mx elements packed along cols, E8M0 scales
+    around 2^0 (uint8 [E, rows, cols / 32])."""
+    bits = oracle.MX_MODES[mode]
+    codes = g.integers(0, 1 << bits, size=(E, rows, cols))
+    if bits == 8 and nan_free:
+        codes = np.where((codes & 0x7F) == 0x7F, 0x7E, codes)
+    w = synth.pack(codes, bits)
+    sc = g.integers(118, 136, size=(E, rows, cols // 32)).astype(np.uint8)
+    return w, sc
+
+
+def _mx_gather(mg, x, w, sc, rhs, lhs, transpose, mode, lhs_div=1):
+    import ctypes
+    X, M, K = x.shape
+    E = w.shape[0]
+    bits = oracle.MX_MODES[mode]
+    code = mg.MX_MODES[mode][0]
+    N = w.shape[1] if transpose else w.shape[2] * 32 // bits
+    P = rhs.numel()
+    odt = torch.bfloat16 if x.dtype == torch.bfloat16 else torch.float32
+    out = torch.empty((P, M, N), dtype=odt, device=x.device)
+    need = mg.lib().moegq_gather_qmm_mx_workspace_bytes(P, M, N, K, int(transpose), code)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = mg.lib().moegq_gather_qmm_mx(mg._ptr(x), mg._dt(x), X, M, K, mg._ptr(w), mg._ptr(sc), E, N, mg._ptr(lhs),
+                                      lhs_div, mg._ptr(rhs), mg.I32, P, int(transpose), code, mg._ptr(out),
+                                      ctypes.c_void_p(ws.data_ptr()), need, mg._stream())
+    assert st == 0, mg.lib().moegq_status_string(st)
+    torch.cuda.synchronize()
+    return out
+
+
+def _mx_check(got_t, want, x, w, sc, lhs, rhs, transpose, mode, name):
+    if want.dtype == np.uint16:
+        assert got_t.dtype == torch.bfloat16, name
+        assert_parity(host_bf(got_t), want, name=name)
+        return
+    got = got_t.cpu().numpy().astype(np.float64)
+    w64 = want.astype(np.float64)
+    xf, _ = oracle.activations_f64(x)
+    bits = oracle.MX_MODES[mode]
+    bound = []
+    for l, r in zip(lhs, rhs):
+        L = xf.shape[-1] if transpose else w.shape[-1] * 32 // bits
+        W = np.abs(oracle.mx_dequant(w[r], sc[r], mode, L))
+        bound.append(np.abs(xf[l]) @ (W.T if transpose else W))
+    K = x.shape[-1]
+    bound = (K + 8) * 2.0 ** -24 * np.stack(bound).reshape(w64.shape)
+    bound += np.spacing(np.abs(w64).astype(np.float32)).astype(np.float64)
+    err = np.abs(got - w64)
+    assert not (err > bound).any(), f"{name}: worst {err.max():.3g}"
+
+
+MX_CASES = [
+    # kind, transpose, mode, X, M, K, N, E, P, lhs_mode
+    ("bf16", True, "mxfp8", 1, 1, 4160, 37, 3, 2, "div"),
+    ("bf16", True, "mxfp4", 2, 2, 320, 45, 4, 6, "idx"),
+    ("f32", True, "mxfp4", 3, 3, 2080, 9, 2, 3, "div"),
+    ("f16", True, "mxfp8", 2, 1, 96, 70, 3, 4, "idx"),
+    ("bf16", False, "mxfp4", 1, 1, 202, 2080, 3, 2, "div"),
+    ("bf16", False, "mxfp8", 2, 5, 130, 192, 4, 6, "idx"),
+    ("f32", False, "mxfp8", 3, 2, 64, 256, 2, 3, "div"),
+    ("f16", False, "mxfp4", 2, 16, 96, 96, 3, 4, "idx"),
+]
+
+
+@pytest.mark.parametrize("case", MX_CASES,
+                         ids=[f"{c[0]}-{'t' if c[1] else 'nt'}-{c[2]}-M{c[4]}-K{c[5]}-N{c[6]}" for c in MX_CASES])
+def test_mx_modes(mg, case):
+    kind, tr, mode, X, M, K, N, E, P, lhs_mode = case
+    g = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    x = _acts(g, (X, M, K), kind)
+    rows, cols = (N, K) if tr else (K, N)
+    w, sc = _mx_weights(g, E, rows, cols, mode)
+    rhs = g.integers(0, E, size=P).astype(np.int32)
+    if lhs_mode == "div":
+        div = max(1, P // X)
+        lhs, lhs_t, kw = np.arange(P) // div, None, dict(lhs_div=div)
+    else:
+        lhs = g.integers(0, X, size=P)
+        lhs_t, kw = i32(lhs), {}
+    sc_t = torch.from_numpy(sc).cuda()
+    got = _mx_gather(mg, _dev_acts(x), words(w), sc_t, i32(rhs), lhs_t, tr, mode, **kw)
+    want = oracle.gather_qmm_mx(x, w, sc, lhs=lhs, rhs=rhs, transpose=tr, mode=mode)
+    _mx_check(got, want, x, w, sc, lhs, rhs, tr, mode, f"mx {case}")
+
+
+def test_mx_special_values(mg):
+    """E8M0 byte 255 (NaN) poisons its block's outputs, byte 0 (2^-127) and
+    E4M3 NaN elements follow the oracle; NaN positions must agree exactly."""
+    g = np.random.default_rng(41)
+    K, N = 128, 8
+    x = _acts(g, (1, 1, K), "f32")
+    codes = g.integers(0, 256, size=(1, N, K))
+    codes = np.where((codes & 0x7F) == 0x7F, 0x7E, codes)
+    codes[0, 5, 77] = 0xFF                            # one E4M3 NaN element in row 5
+    w = synth.pack(codes, 8)
+    sc = g.integers(118, 136, size=(1, N, K // 32)).astype(np.uint8)
+    sc[0, 1, 2] = 255                                 # NaN scale: row 1
+    sc[0, 2, 0] = 0                                   # 2^-127: row 2's first block vanishes
+    got = _mx_gather(mg, _dev_acts(x), words(w), torch.from_numpy(sc).cuda(), i32([0]), None, True, "mxfp8")
+    want = oracle.gather_qmm_mx(x, w, sc, lhs=[0], rhs=[0], transpose=True, mode="mxfp8")
+    gv = got.cpu().numpy()
+    assert np.array_equal(np.isnan(gv), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.allclose(gv[ok], want[ok], rtol=1e-5, atol=1e-30)
+
+
+def test_quantized_matmul_mx_binding(mg):
+    """The binding's quantized_matmul with mode="mxfp4": 2-D weights, bf16 rows."""
+    g = np.random.default_rng(42)
+    K, N = 256, 64
+    w, sc = _mx_weights(g, 1, N, K, "mxfp4")
+    x = _acts(g, (5, K), "bf16")
+    got = mg.quantized_matmul(_dev_acts(x), words(w[0]), torch.from_numpy(sc[0]).cuda(), transpose=True,
+                              mode="mxfp4")
+    assert tuple(got.shape) == (5, N)
+    want = oracle.mx_matmul(x, w[0], sc[0], "mxfp4", True)
+    assert_parity(host_bf(got), want, name="qmm mx")

@@ -365,8 +365,8 @@ def vec_leg(torch, m, synth, steps=42, cfg=1):
     8 of 288 experts, 4-bit, group 64): the gate projection stored without
     the transpose ([288, 4096, 2048/8] words, groups along N) with bf16
     activations, and the transposed gate projection with float32 activations
-    (float32 result), and the transposed gate projection at 3 bits (codes
-    straddle words).  42 index sets chained in one HIP graph, as the decode
+    (float32 result), the transposed gate projection at 3 bits (codes
+    straddle words), and in the mxfp8 and mxfp4 modes.  42 index sets chained in one HIP graph, as the decode
     leg does, so that weights come from HBM."""
     sh = synth.DECODE
     dev = torch.device("cuda")
@@ -401,6 +401,27 @@ def vec_leg(torch, m, synth, steps=42, cfg=1):
         res[name] = {"us": us, "gbs": nbytes / us / 1e3, "hbm_frac": nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
                      "bytes": nbytes, "k_splits": int(plan_ks) if plan_ks else 1}
     del gate, gate3
+    # mx modes, transposed gate projection, bf16 activations: E8M0 scale bytes
+    # around 2^0; E4M3 bytes with bit 3 cleared (no NaN pattern)
+    g = synth.device_generator(dev, cfg, 7)
+    x = torch.randn((1, 1, H), device=dev).to(torch.bfloat16)
+    for mode, bits in (("mxfp8", 8), ("mxfp4", 4)):
+        w = torch.randint(-(1 << 31), (1 << 31) - 1, (E, I, H * bits // 32), dtype=torch.int32, device=dev,
+                          generator=g)
+        if bits == 8:
+            w &= 0xF7F7F7F7 - (1 << 32)
+        sc = torch.randint(118, 136, (E, I, H // 32), dtype=torch.uint8, device=dev, generator=g)
+        out = torch.empty((P, 1, I), dtype=torch.bfloat16, device=dev)
+        need = int(m.lib().moegq_gather_qmm_mx_workspace_bytes(P, 1, I, H, 1, m.MX_MODES[mode][0]))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        fn = lambda i, w=w, sc=sc, out=out, ws=ws, mode=mode: m.gather_qmm_mx(
+            x, w, sc, rhs_indices=sets[i % 42], transpose=True, mode=mode, out=out, workspace=ws)
+        us = graph_time_us(torch, fn, 42, reps=max(1, steps // 42), check=lambda out=out: out)
+        nbytes = P * (I * H * bits // 8 + I * (H // 32)) + H * 2 + P * I * 2
+        res[f"{mode}_transpose_bf16_1tok_8pairs_n2048_k4096"] = {
+            "us": us, "gbs": nbytes / us / 1e3, "hbm_frac": nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+            "bytes": nbytes, "k_splits": need // (P * I * 4) if need else 1}
+        del w, sc
     torch.cuda.empty_cache()
     return res
 

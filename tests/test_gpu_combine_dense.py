@@ -86,6 +86,27 @@ def test_affine_qmm_full_shape_sampled(mg, M):
         assert_parity(got[:, cols], want, name=f"sampled {N}x{K} M={M}")
 
 
+@pytest.mark.parametrize("M,N", [(3, 8200), (16, 8200), (6, 2600), (16, 2600), (4, 1040)])
+def test_affine_qmm_wide_ragged(mg, M, N):
+    """Few-row products on wide matrices whose last 16-column block is ragged
+    (N 8200, 2600, 1040), with a K split over several waves; plain and gate/up."""
+    g = np.random.default_rng(60 + M + N)
+    K = 1024
+    w, s, b = synth.drawn_words(g, N, K, 64, 4)
+    x = synth.to_bf16(g.standard_normal((M, K)))
+    got = host_bf(mg.affine_qmm(bf(x), words(w), bf(s), bf(b), group_size=64, bits=4))
+    cols = np.unique(np.concatenate([g.choice(N, 96, replace=False), np.arange(N - 40, N)]))
+    want = oracle.quantized_matmul(x, w[cols], s[cols], b[cols], True, 64, 4)
+    assert_parity(got[:, cols], want, name=f"blocks M={M} N={N}")
+    w2, s2, b2 = synth.drawn_words(g, N, K, 64, 4)
+    got2 = host_bf(mg.affine_qmm_glu(bf(x), (words(w), bf(s), bf(b)), (words(w2), bf(s2), bf(b2)),
+                                     group_size=64, bits=4))
+    gg = oracle.quantized_matmul(x, w[cols], s[cols], b[cols], True, 64, 4)
+    uu = oracle.quantized_matmul(x, w2[cols], s2[cols], b2[cols], True, 64, 4)
+    want2 = oracle.f64_to_bf16(oracle.silu(oracle.bf16_to_f64(gg)) * oracle.bf16_to_f64(uu))
+    assert_parity(got2[:, cols], want2, name=f"blocks glu M={M} N={N}")
+
+
 @pytest.mark.parametrize("M", [1, 5, 16, 40, 300])
 def test_affine_qmm_glu(mg, M):
     g = np.random.default_rng(50 + M)

@@ -525,7 +525,7 @@ def counted_traffic():
 
 
 # ----------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(torch, synth, n_layers=2, cfg=1):
+def cpu_baseline(torch, synth, n_layers=5, cfg=1):
     """The oracle (numpy) on a bounded sample of the headline workload: n_layers
     MoE decode layers at one token, dequantizing only the selected experts,
     on the same device-drawn weights (copied back for the selected experts)."""

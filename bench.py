@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=42 * 4)
     ap.add_argument("--warmup", type=int, default=42)
-    ap.add_argument("--legs", default="decode,prefill,large,gather_mm,vec,dense,cpu")
+    ap.add_argument("--legs", default="decode,prefill,large,combine,gather_mm,vec,dense,cpu")
     ap.add_argument("--prefill-rows", default="2048,128,512,4096", help="row counts of the prefill leg")
     ap.add_argument("--large-rows", default="713,4123,8192,16384", help="row counts of the large-prefill leg")
     ap.add_argument("--quiet", action="store_true")
@@ -426,6 +426,42 @@ def vec_leg(torch, m, synth, steps=42, cfg=1):
     return res
 
 
+def combine_leg(torch, m, synth, reps=20, cfg=3):
+    """The layer's tail at the 2048-row prefill shape (top-8, hidden 2048,
+    shared expert): the fused combine (one pass) against the unfused tail
+    (unsort, x score, sum over top_k, + shared: four kernels, each writing a
+    bf16 tensor), HIP-graph replays of 10 calls each.  The two outputs are
+    checked bit for bit."""
+    dev = torch.device("cuda")
+    T, top_k, H = 2048, 8, 2048
+    P = T * top_k
+    g = synth.device_generator(dev, cfg, 8)
+    y = torch.randn((P, H), device=dev, generator=g).to(torch.bfloat16)
+    inv = torch.randperm(P, device=dev, generator=g).to(torch.int32)
+    scores = torch.rand((T, top_k), device=dev, generator=g).to(torch.bfloat16)
+    shared = torch.randn((T, H), device=dev, generator=g).to(torch.bfloat16)
+    out_f = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    out_u = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(m.workspace_bytes(m.OP_COMBINE_UNFUSED, P, 0, H, 0), dtype=torch.uint8, device=dev)
+    fused = lambda i: m.moe_combine(y, inv, scores, shared, out=out_f)
+    unfused = lambda i: m.moe_combine_unfused(y, inv, scores, shared, out=out_u, workspace=ws)
+    us_f = graph_time_us(torch, fused, 10, reps=max(1, reps // 10), check=lambda: out_f)
+    us_u = graph_time_us(torch, unfused, 10, reps=max(1, reps // 10), check=lambda: out_u)
+    torch.cuda.synchronize()
+    if not torch.equal(out_f.view(torch.int16), out_u.view(torch.int16)):
+        raise RuntimeError("fused combine differs from the unfused tail")
+    # bytes each form moves: fused reads y, inv, scores, shared and writes out;
+    # unfused writes and re-reads [T, top_k, H] twice, then [T, H]
+    b_f = P * H * 2 + P * 4 + P * 2 + T * H * 2 + T * H * 2
+    b_u = (P * H * 2 + P * 4 + P * H * 2) + (P * H * 2 + P * 2 + P * H * 2) + (P * H * 2 + T * H * 2) \
+        + (T * H * 2 * 3)
+    return {"rows": T, "top_k": top_k, "hidden": H,
+            "fused_us": us_f, "fused_bytes": b_f, "fused_hbm_frac": b_f / (us_f * 1e-6) / (HBM_PEAK_GBS * 1e9),
+            "unfused_us": us_u, "unfused_bytes": b_u,
+            "unfused_hbm_frac": b_u / (us_u * 1e-6) / (HBM_PEAK_GBS * 1e9),
+            "speedup": us_u / us_f, "bitwise_equal": True}
+
+
 # ----------------------------------------------------------------------------- dense chain
 def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=5, warmup=2, cfg=2):
     dev = torch.device("cuda")
@@ -589,6 +625,9 @@ def main():
     if "gather_mm" in legs:
         log("unquantized gather_mm")
         extra["gather_mm"] = gather_mm_leg(torch, m, synth)
+    if "combine" in legs:
+        log("== combine leg")
+        extra["combine"] = combine_leg(torch, m, synth)
     if "vec" in legs:
         log("== vec leg")
         extra["vec"] = vec_leg(torch, m, synth)

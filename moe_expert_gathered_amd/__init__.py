@@ -452,14 +452,19 @@ def moe_combine_gated(y, inv, scores, shared, z, out=None):
     return out
 
 
-def moe_combine_unfused(y, inv, scores, shared=None, out=None):
-    """The same tail as four kernels, each writing a bf16 tensor."""
-    _dev(y, inv, scores, shared)
+def moe_combine_unfused(y, inv, scores, shared=None, out=None, workspace=None):
+    """The same tail as four kernels, each writing a bf16 tensor.  workspace:
+    optional uint8 device tensor of workspace_bytes(OP_COMBINE_UNFUSED, ...) bytes."""
+    _dev(y, inv, scores, shared, workspace)
     T, top_k = scores.shape
     H = y.shape[-1]
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
-    ws, wsb = _workspace(workspace_bytes(OP_COMBINE_UNFUSED, T * top_k, 0, H, 0), y.device)
+    need = workspace_bytes(OP_COMBINE_UNFUSED, T * top_k, 0, H, 0)
+    if workspace is not None and workspace.numel() >= need:
+        ws, wsb = workspace, int(workspace.numel())
+    else:
+        ws, wsb = _workspace(need, y.device)
     st = lib().moegq_moe_combine_unfused(_ptr(y), _ptr(inv), _ptr(scores), _ptr(shared), T, top_k, H, _ptr(out),
                                          _ptr(ws), wsb, _stream())
     _check(st, "moe_combine_unfused")

@@ -23,7 +23,8 @@ def mg():
 
 
 @pytest.mark.parametrize("T,top_k,H", [(128, 8, 2048), (331, 8, 2048), (2048, 8, 2048), (4096, 8, 2048),
-                                       (3, 1, 16), (17, 2, 40), (5, 8, 4096)])
+                                       (3, 1, 16), (17, 2, 40), (5, 8, 4096), (11, 4, 32), (13, 6, 48),
+                                       (9, 3, 64), (7, 5, 24)])
 def test_combine_bitwise(mg, T, top_k, H):
     g = np.random.default_rng(T + top_k + H)
     P = T * top_k

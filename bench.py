@@ -467,6 +467,13 @@ def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=5, warmup=2,
     dev = torch.device("cuda")
     d = synth.DENSE
     sets = synth.device_dense_sets(dev, cfg, gs, bits, d)
+    # q, k and v read the same normalized rows: their weights are stacked into
+    # one [q_out + 2 kv_out, hidden] matrix (the same bytes) and run as one product
+    nq, nk = d["q_out"], d["kv_out"]
+    for L in sets:
+        L["qkv"] = tuple(torch.cat([L["q"][i], L["k"][i], L["v"][i]], 0).contiguous() for i in range(3))
+        del L["q"], L["k"], L["v"]
+    torch.cuda.empty_cache()
     nw = torch.ones(d["hidden"], dtype=torch.bfloat16, device=dev)
     per_fwd = 0
     for name, (N, K) in synth.dense_dims(d).items():
@@ -481,10 +488,8 @@ def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=5, warmup=2,
             for li in range(d["layers"]):
                 L = sets[li % d["sets"]]
                 x = m.rms_norm(h, nw)
-                q = m.affine_qmm(x, *L["q"], group_size=gs, bits=bits)
-                k = m.affine_qmm(x, *L["k"], group_size=gs, bits=bits)
-                v = m.affine_qmm(x, *L["v"], group_size=gs, bits=bits)
-                h = m.affine_qmm(m.kv_feed(q, k, v), *L["o"], group_size=gs, bits=bits, residual=h)
+                qkv = m.affine_qmm(x, *L["qkv"], group_size=gs, bits=bits)
+                h = m.affine_qmm(m.kv_feed_stacked(qkv, nq, nk, nk), *L["o"], group_size=gs, bits=bits, residual=h)
                 x = m.rms_norm(h, nw)
                 a = m.affine_qmm_glu(x, L["g"], L["u"], group_size=gs, bits=bits)
                 h = m.affine_qmm(a, *L["dn"], group_size=gs, bits=bits, residual=h)

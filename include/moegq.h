@@ -396,6 +396,12 @@ int moegq_sigmoid_gate(const void* s, const void* z, int64_t z_stride, int64_t T
  * (MLX PR 4787 benchmark script: o is applied to q + (k[:, :1] + v[:, :1])). */
 int moegq_kv_feed(const void* q, const void* k, const void* v, int64_t M, int64_t Nq,
                   int64_t Nk, int64_t Nv, void* out, void* stream);
+/* kv_feed with row strides (element counts): q row m at q + m*ldq (ldq >= Nq),
+ * k[m, 0] at k + m*ldk, v[m, 0] at v + m*ldv; out [M, Nq] bf16.  With one
+ * stacked product qkv [M, Nq + Nk + Nv]: q = qkv, k = qkv + Nq, v = qkv + Nq + Nk,
+ * every stride Nq + Nk + Nv. */
+int moegq_kv_feed_ld(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v, int64_t ldv,
+                     int64_t M, int64_t Nq, void* out, void* stream);
 
 /*
  * selfcheck: runs the fused and the unfused combine on seeded data of 128

@@ -19,7 +19,8 @@ import torch
 __all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "quantized_matmul", "gather_qmm_workspace_bytes",
            "gather_qmm_mx", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
            "switch_glu", "switch_glu_mode", "moe_decode", "moe_prefill", "moe_prefill_workspace_bytes", "moe_combine", "moe_combine_gated", "moe_combine_unfused", "sort_pairs",
-           "schedule_tiles", "rms_norm", "sigmoid_gate", "route", "gather_mm", "kv_feed", "selfcheck",
+           "schedule_tiles", "rms_norm", "sigmoid_gate", "route", "gather_mm", "kv_feed", "kv_feed_stacked",
+           "selfcheck",
            "validate_indices", "workspace_bytes", "MODE_AUTO", "MODE_DECODE", "MODE_SORTED",
            "TILES_SCHEDULED", "TILES_NAIVE"]
 
@@ -81,6 +82,7 @@ _SIGS = {
     "moegq_route": ([_p, _i64, _i64, _i64, _p, _p, _p], _int),
     "moegq_gather_mm": ([_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _p, _sz, _p], _int),
     "moegq_kv_feed": ([_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p], _int),
+    "moegq_kv_feed_ld": ([_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _p], _int),
     "moegq_selfcheck": ([_p, _sz, _p], _int),
     "moegq_validate_indices": ([_p, _i64, _i64, _int, _p, _p], _int),
 }
@@ -540,6 +542,23 @@ def kv_feed(q, k, v, out=None):
         out = torch.empty_like(q)
     _check(lib().moegq_kv_feed(_ptr(q), _ptr(k), _ptr(v), M, Nq, k.shape[1], v.shape[1], _ptr(out), _stream()),
            "kv_feed")
+    return out
+
+
+def kv_feed_stacked(qkv, nq, nk, nv, out=None):
+    """kv_feed on one stacked product qkv [M, nq + nk + nv] (q, k, v as its
+    column ranges): bf16(q + bf16(k[:, :1] + v[:, :1]))."""
+    _dev(qkv)
+    M, L = qkv.shape
+    if L != nq + nk + nv:
+        raise ValueError("stacked width must be nq + nk + nv")
+    if out is None:
+        out = torch.empty((M, nq), dtype=qkv.dtype, device=qkv.device)
+    base = qkv.data_ptr()
+    es = qkv.element_size()
+    _check(lib().moegq_kv_feed_ld(ctypes.c_void_p(base), L, ctypes.c_void_p(base + nq * es), L,
+                                  ctypes.c_void_p(base + (nq + nk) * es), L, M, nq, _ptr(out), _stream()),
+           "kv_feed_stacked")
     return out
 
 

@@ -880,10 +880,15 @@ int moegq_sigmoid_gate(const void* s, const void* z, int64_t z_stride, int64_t T
 
 int moegq_kv_feed(const void* q, const void* k, const void* v, int64_t M, int64_t Nq, int64_t Nk, int64_t Nv,
                   void* out, void* stream) {
-  if (M < 0 || Nq <= 0 || Nk <= 0 || Nv <= 0) return MOEGQ_ERR_SHAPE;
+  return moegq_kv_feed_ld(q, Nq, k, Nk, v, Nv, M, Nq, out, stream);
+}
+
+int moegq_kv_feed_ld(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v, int64_t ldv, int64_t M,
+                     int64_t Nq, void* out, void* stream) {
+  if (M < 0 || Nq <= 0 || ldq < Nq || ldk <= 0 || ldv <= 0) return MOEGQ_ERR_SHAPE;
   if (M == 0) return MOEGQ_OK;
   if (!q || !k || !v || !out) return MOEGQ_ERR_NULL_ARG;
-  return status_of(launch_kv_feed((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, M, Nq, Nk, Nv,
+  return status_of(launch_kv_feed((const uint16_t*)q, ldq, (const uint16_t*)k, ldk, (const uint16_t*)v, ldv, M, Nq,
                                   (uint16_t*)out, S(stream)));
 }
 

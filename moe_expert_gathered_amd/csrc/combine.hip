@@ -276,24 +276,26 @@ hipError_t launch_sigmoid_gate(const uint16_t* s, const uint16_t* z, int64_t zs,
 }
 
 // decoder chain feed: out[m, n] = bf16(q[m, n] + bf16(k[m, 0] + v[m, 0]))
-__global__ __launch_bounds__(256) void kv_feed_kernel(const uint16_t* __restrict__ q,
-                                                      const uint16_t* __restrict__ k,
-                                                      const uint16_t* __restrict__ v, int64_t M,
-                                                      int64_t Nq, int64_t Nk, int64_t Nv,
-                                                      uint16_t* __restrict__ out) {
+// out[m, j] = bf16( q[m, j] + bf16(k[m, 0] + v[m, 0]) ); q, k, v rows at the
+// given row strides (element counts), so q, k and v may be column ranges of
+// one stacked [M, Nq + Nk + Nv] product
+__global__ __launch_bounds__(256) void kv_feed_kernel(const uint16_t* __restrict__ q, int64_t ldq,
+                                                      const uint16_t* __restrict__ k, int64_t ldk,
+                                                      const uint16_t* __restrict__ v, int64_t ldv, int64_t M,
+                                                      int64_t Nq, uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= M * Nq) return;
-  const int64_t m = i / Nq;
-  const float kv = bf16_to_f32(f32_to_bf16(bf16_to_f32(k[m * Nk]) + bf16_to_f32(v[m * Nv])));
-  out[i] = f32_to_bf16(bf16_to_f32(q[i]) + kv);
+  const int64_t m = i / Nq, j = i - m * Nq;
+  const float kv = bf16_to_f32(f32_to_bf16(bf16_to_f32(k[m * ldk]) + bf16_to_f32(v[m * ldv])));
+  out[i] = f32_to_bf16(bf16_to_f32(q[m * ldq + j]) + kv);
 }
 
-hipError_t launch_kv_feed(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t M,
-                          int64_t Nq, int64_t Nk, int64_t Nv, uint16_t* out, hipStream_t st) {
+hipError_t launch_kv_feed(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk, const uint16_t* v,
+                          int64_t ldv, int64_t M, int64_t Nq, uint16_t* out, hipStream_t st) {
   const int64_t n = M * Nq;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(kv_feed_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, q, k, v, M,
-                     Nq, Nk, Nv, out);
+  hipLaunchKernelGGL(kv_feed_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, q, ldq, k, ldk, v, ldv,
+                     M, Nq, out);
   return hipGetLastError();
 }
 

@@ -130,8 +130,8 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int top_k, int32_
                         hipStream_t st);
 hipError_t launch_sigmoid_gate(const uint16_t* s, const uint16_t* z, int64_t zs, int64_t T, int64_t H,
                                uint16_t* out, hipStream_t st);
-hipError_t launch_kv_feed(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t M,
-                          int64_t Nq, int64_t Nk, int64_t Nv, uint16_t* out, hipStream_t st);
+hipError_t launch_kv_feed(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk, const uint16_t* v,
+                          int64_t ldv, int64_t M, int64_t Nq, uint16_t* out, hipStream_t st);
 // vector-unit products: weights without the transpose, float16/float32 activations
 struct VecPlan {
   int MB, MBLK, WPL, NC, KS, kchunk;   // rows per block, blocks, codes per lane, column strips (row blocks), splits, K per split

@@ -161,6 +161,35 @@ def test_dense_chain_small(mg):
         assert_parity(host_bf(h), want, name=f"chain M={M}")
 
 
+def test_dense_chain_stacked_qkv(mg):
+    """The chain with q, k and v as one stacked product [q_out + 2 kv_out,
+    hidden] and the kv feed reading its column ranges (the benchmark's form)."""
+    import torch
+    d = dict(hidden=256, q_out=512, kv_out=128, inter=768, layers=2, sets=2)
+    sets = synth.dense_sets(2, 64, 4, mode="minmax", d=d)
+    g = np.random.default_rng(61)
+    for M in (1, 4, 16):
+        h0 = synth.to_bf16(g.standard_normal((M, 256)))
+        nw = synth.to_bf16(np.ones(256, np.float32))
+        want = oracle.dense_forward(h0, sets, 2, nw, gs=64, bits=4)
+        dsets = []
+        for L in sets:
+            t = {k: triple(v) for k, v in L.items()}
+            t["qkv"] = tuple(torch.cat([t["q"][i], t["k"][i], t["v"][i]], 0).contiguous() for i in range(3))
+            dsets.append(t)
+        h = bf(h0)
+        nwd = bf(nw)
+        for li in range(2):
+            L = dsets[li % 2]
+            x = mg.rms_norm(h, nwd)
+            qkv = mg.affine_qmm(x, *L["qkv"], group_size=64)
+            h = mg.affine_qmm(mg.kv_feed_stacked(qkv, 512, 128, 128), *L["o"], group_size=64, residual=h)
+            x = mg.rms_norm(h, nwd)
+            a = mg.affine_qmm_glu(x, L["g"], L["u"], group_size=64)
+            h = mg.affine_qmm(a, *L["dn"], group_size=64, residual=h)
+        assert_parity(host_bf(h), want, name=f"stacked chain M={M}")
+
+
 def test_gather_qmm_page_cases(mg):
     """nuvec "gather_qmm_selects_batches" / gather kernels: explicit lhs/rhs,
     default indices, broadcast index shapes, rows M > 1, sorted grouped rows."""

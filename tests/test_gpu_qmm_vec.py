@@ -382,3 +382,60 @@ def test_quantized_matmul_mx_binding(mg):
     assert tuple(got.shape) == (5, N)
     want = oracle.mx_matmul(x, w[0], sc[0], "mxfp4", True)
     assert_parity(host_bf(got), want, name="qmm mx")
+
+
+# ----------------------------------------------------------------------------- bitwise pins
+EXACT_CASES = [
+    # kind, transpose, bits, gs, M, K, N, P
+    ("bf16", False, 4, 64, 1, 2048, 256, 1),     # split over K
+    ("f32", False, 8, 32, 3, 512, 96, 2),
+    ("f16", True, 4, 128, 2, 1024, 40, 3),
+    ("f32", True, 3, 32, 1, 4096, 24, 1),        # split over slices
+    ("bf16", False, 5, 64, 5, 320, 128, 2),
+    ("bf16", True, 6, 64, 1, 640, 33, 2),
+    ("bf16", True, 2, 32, 4, 256, 50, 2),
+    ("f16", False, 1, 32, 2, 96, 2048, 1),
+]
+
+
+@pytest.mark.parametrize("case", EXACT_CASES, ids=[f"{c[0]}-{'t' if c[1] else 'nt'}-{c[2]}b-M{c[4]}" for c in EXACT_CASES])
+def test_vector_route_integer_exact_bitwise(mg, case):
+    """Scales 2^-2, integer biases times 2^-2 and small-integer activations:
+    every product and partial sum (and the sum of the K split's partials) is
+    exact in fp32, so the GPU equals the oracle bit for bit."""
+    kind, tr, bits, gs, M, K, N, P = case
+    g = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    rows, cols = (N, K) if tr else (K, N)
+    ms = [synth.integer_exact(g, rows, cols, gs, bits) for _ in range(P)]
+    w, s, b = (np.stack([m[i] for m in ms]) for i in range(3))
+    xi = g.integers(-8, 9, size=(1, M, K)).astype(np.float32)
+    x = synth.to_bf16(xi) if kind == "bf16" else xi.astype(np.float16 if kind == "f16" else np.float32)
+    rhs = np.arange(P, dtype=np.int32)
+    got = _gather(mg, _dev_acts(x), words(w), bf(s), bf(b), i32(rhs), None, tr, gs, bits, lhs_div=P)
+    want = oracle.gather_qmm(x, w, s, b, lhs=np.zeros(P, np.int64), rhs=rhs, transpose=tr, gs=gs, bits=bits)
+    if want.dtype == np.uint16:
+        assert np.array_equal(host_bf(got), want)
+    else:
+        assert np.array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("mode,tr", [("mxfp8", True), ("mxfp4", False), ("mxfp8", False), ("mxfp4", True)])
+def test_mx_integer_exact_bitwise(mg, mode, tr):
+    """mx elements with exponents near 2^0 (E4M3: exponent field 6..8), block
+    scales 2^-1..2^1 and small-integer activations: exact in fp32, so bit for
+    bit."""
+    g = np.random.default_rng(zlib.crc32((mode + str(tr)).encode()))
+    bits = oracle.MX_MODES[mode]
+    M, K, N = 3, 1024, 64
+    rows, cols = (N, K) if tr else (K, N)
+    if bits == 8:
+        codes = (g.integers(0, 2, size=(1, rows, cols)) << 7) | (g.integers(6, 9, size=(1, rows, cols)) << 3) \
+            | g.integers(0, 8, size=(1, rows, cols))
+    else:
+        codes = g.integers(0, 16, size=(1, rows, cols))
+    w = synth.pack(codes, bits)
+    sc = g.integers(126, 129, size=(1, rows, cols // 32)).astype(np.uint8)
+    x = g.integers(-8, 9, size=(1, M, K)).astype(np.float32)
+    got = _mx_gather(mg, _dev_acts(x), words(w), torch.from_numpy(sc).cuda(), i32([0]), None, tr, mode)
+    want = oracle.gather_qmm_mx(x, w, sc, lhs=[0], rhs=[0], transpose=tr, mode=mode)
+    assert np.array_equal(got.cpu().numpy(), want)

@@ -2,6 +2,7 @@
 // catalogue, nuvec-core tests/quantized.rs "invalid_arguments_are_rejected" and
 // "gather_qmm_selects_batches"), workspace sizing and kernel dispatch.  No
 // allocation, no synchronization (except the two documented checks).
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 
@@ -88,16 +89,21 @@ int64_t small_cap(int64_t P, int64_t E, int64_t extra = 0) {
 
 // Hybrid schedule parameters: two tile workgroups fit on each compute unit;
 // the first pass (gate/up) has I / 128 column blocks per row tile.
+// workgroup slots of the current device (2 per compute unit), cached per
+// device; calls from several host threads may fill the cache concurrently
+// (they store the same value)
 int device_slots() {
-  static int slots[64];
+  static std::atomic<int> slots[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-  if (slots[dev] == 0) {
+  int v = slots[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    slots[dev] = 2 * cus;
+    v = 2 * cus;
+    slots[dev].store(v, std::memory_order_relaxed);
   }
-  return slots[dev];
+  return v;
 }
 void set_hybrid_model(SortArgs& sa, int64_t I) {
   sa.small_max = kSmallMax;

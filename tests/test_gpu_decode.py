@@ -164,3 +164,35 @@ def test_moe_decode_fused_tail(mg, M, H, I, E, top_k, bits, gs):
     assert_parity(host_bf(out), want, name="decode layer")
     out2 = mg.moe_decode(xd, idd, scd, *dev, shared=None, group_size=gs, bits=bits, y=y)
     assert np.array_equal(host_bf(out2), host_bf(mg.moe_combine(y_ref, None, scd, None)))
+
+
+def test_gather_qmv_past_grid_limit(mg):
+    """70,000 one-row pairs: the launch splits its pair axis into grids of
+    65,535; pairs around each split (and the last) checked against the oracle."""
+    g = np.random.default_rng(123)
+    E, N, K, P = 5, 32, 128, 70000
+    w, s, b = synth.stack_experts([synth.drawn_matrix(g, N, K, 64, 4) for _ in range(E)])
+    x = synth.to_bf16(g.standard_normal((P, 1, K)))
+    rhs = g.integers(0, E, P).astype(np.int32)
+    got = host_bf(mg.gather_qmm(bf(x), words(w), bf(s), bf(b), rhs_indices=i32(rhs), group_size=64, bits=4))
+    pick = np.array([0, 1, 65533, 65534, 65535, 65536, P - 2, P - 1])
+    want = oracle.gather_qmm(x[pick], w, s, b, lhs=np.arange(len(pick)), rhs=rhs[pick], gs=64, bits=4)
+    assert_parity(got[pick], want, name="past grid limit")
+
+
+def test_moe_decode_past_grid_limit(mg):
+    """65,600 tokens through the two-kernel decode layer (the fused down +
+    combine launches its token axis in grids of 65,535); sampled tokens
+    against the oracle's SwitchGLU and combine."""
+    T, H, I, E, top_k, gs = 65600, 64, 64, 4, 2, 32
+    g = np.random.default_rng(124)
+    idx = np.sort(np.stack([g.choice(E, top_k, replace=False) for _ in range(T)]), axis=1).astype(np.int32)
+    ex = synth.expert_set(12, E, H, I, gs, 4, mode="drawn")
+    x = synth.to_bf16(g.standard_normal((T, H)))
+    scores = synth.to_bf16(g.random((T, top_k)).astype(np.float32))
+    dev = [triple(m) for m in ex]
+    out = host_bf(mg.moe_decode(bf(x), i32(idx), bf(scores), *dev, group_size=gs, bits=4))
+    pick = np.array([0, 65534, 65535, 65536, T - 1])
+    want_y = oracle.switch_glu(x[pick], idx[pick], *ex, gs=gs, bits=4).reshape(-1, H)
+    want = oracle.combine(want_y, np.arange(len(pick) * top_k, dtype=np.int32), scores[pick])
+    assert_parity(out[pick], want, name="decode past grid limit")

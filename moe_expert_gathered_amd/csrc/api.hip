@@ -14,7 +14,7 @@ using namespace moegq;
 namespace {
 
 constexpr int kMaxExperts = 1024;     // single-workgroup sort
-constexpr int64_t kMaxQmvK = 32768;   // activation row staged in 64 KiB of LDS
+constexpr int64_t kMaxQmvK = 32768;   // longest row of the one-row kernels (the size the tests cover)
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 
 hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }

@@ -196,3 +196,19 @@ def test_moe_decode_past_grid_limit(mg):
     want_y = oracle.switch_glu(x[pick], idx[pick], *ex, gs=gs, bits=4).reshape(-1, H)
     want = oracle.combine(want_y, np.arange(len(pick) * top_k, dtype=np.int32), scores[pick])
     assert_parity(out[pick], want, name="decode past grid limit")
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 128), (8, 64)])
+def test_gather_qmv_longest_row(mg, bits, gs):
+    """One-row pairs at the longest row the one-row kernels take (K 32768)."""
+    g = np.random.default_rng(125 + bits)
+    E, N, K, P = 3, 24, 32768, 4
+    w, s, b = synth.stack_experts([synth.drawn_matrix(g, N, K, gs, bits) for _ in range(E)])
+    x = synth.to_bf16(g.standard_normal((P, 1, K)))
+    rhs = np.array([2, 0, 1, 2], np.int32)
+    got = host_bf(mg.gather_qmm(bf(x), words(w), bf(s), bf(b), rhs_indices=i32(rhs), group_size=gs, bits=bits))
+    want = oracle.gather_qmm(x, w, s, b, lhs=np.arange(P), rhs=rhs, gs=gs, bits=bits)
+    assert_parity(got, want, name=f"K=32768 {bits}-bit")
+    x1 = synth.to_bf16(g.standard_normal((1, K)))
+    got1 = host_bf(mg.affine_qmm(bf(x1), words(w[1]), bf(s[1]), bf(b[1]), group_size=gs, bits=bits))
+    assert_parity(got1, oracle.quantized_matmul(x1, w[1], s[1], b[1], True, gs, bits), name="dense K=32768")

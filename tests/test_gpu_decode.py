@@ -138,6 +138,29 @@ def test_gather_qmm_glu(mg, M, K):
     assert_parity(host_bf(got), want, name=f"glu M={M}")
 
 
+@pytest.mark.parametrize("N,K,bits,gs", [(97, 4096, 4, 64), (33, 512, 4, 32), (65, 2048, 8, 128), (1, 256, 8, 64),
+                                         (129, 2560, 4, 128)])
+def test_gather_qmm_glu_ragged(mg, N, K, bits, gs):
+    """One-row GLU pairs with an odd number of output rows: the last two-row
+    block of each expert has one row past N, whose loads must read zeros (the
+    last expert of the stack included) and whose result is not written.  K
+    covers rows of one and of two 256-word slices and a partial slice."""
+    g = np.random.default_rng(N * 7 + K + bits)
+    E, top_k, T = 4, 2, 5
+    G = synth.stack_experts([synth.drawn_matrix(g, N, K, gs, bits) for _ in range(E)])
+    U = synth.stack_experts([synth.drawn_matrix(g, N, K, gs, bits) for _ in range(E)])
+    x = synth.to_bf16(g.standard_normal((T, 1, K)))
+    rhs = (np.arange(T * top_k) * 3 + 1) % E
+    rhs[-1] = E - 1
+    lhs = np.arange(T * top_k) // top_k
+    gg = oracle.gather_qmm(x, *G, lhs=lhs, rhs=rhs, gs=gs, bits=bits)
+    uu = oracle.gather_qmm(x, *U, lhs=lhs, rhs=rhs, gs=gs, bits=bits)
+    want = oracle.f64_to_bf16(oracle.silu(oracle.bf16_to_f64(gg)) * oracle.bf16_to_f64(uu))
+    got = mg.gather_qmm_glu(bf(x[:, 0, :]), triple(G), triple(U), i32(rhs), lhs_div=top_k, group_size=gs, bits=bits)
+    assert got.shape[-1] == N
+    assert_parity(host_bf(got), want, name=f"glu ragged N={N} K={K} bits={bits}")
+
+
 @pytest.mark.parametrize("M,H,I,E,top_k,bits,gs", [(1, 4096, 2048, 288, 8, 4, 64), (4, 4096, 2048, 288, 8, 4, 64),
                                                    (3, 256, 128, 8, 2, 4, 64), (2, 512, 384, 16, 4, 8, 128),
                                                    (5, 1024, 2560, 12, 8, 4, 32), (2, 256, 256, 20, 12, 4, 64)])

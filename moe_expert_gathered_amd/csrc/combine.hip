@@ -185,9 +185,10 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const uint16_t* __restric
 
 // The same arithmetic with 16-byte accesses, the row held in registers
 // between the two passes (K a multiple of 8, K <= 8 * 256 * RV, rows and w
-// 16-byte aligned).  The per-thread sums of squares follow the element order
-// of the scalar kernel's loop only up to regrouping; the block sum is formed
-// the same way.
+// 16-byte aligned).  The norm weights are loaded with the row, so the kernel
+// waits for memory once.  The per-thread sums of squares follow the element
+// order of the scalar kernel's loop only up to regrouping; the block sum is
+// formed the same way.
 template <int RV>
 __global__ __launch_bounds__(256) void rms_norm_vec_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ w, int64_t K, float eps,
@@ -197,12 +198,14 @@ __global__ __launch_bounds__(256) void rms_norm_vec_kernel(const uint16_t* __res
   const int tid = threadIdx.x;
   const int nc = (int)(K / 8);
   const uint4* xr = reinterpret_cast<const uint4*>(x + m * K);
-  uint4 v[RV];
+  const uint4* wr = reinterpret_cast<const uint4*>(w);
+  uint4 v[RV], wv[RV];
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < RV; ++j) {
     const int c = tid + 256 * j;
     v[j] = c < nc ? xr[c] : make_uint4(0, 0, 0, 0);
+    wv[j] = c < nc ? wr[c] : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < RV; ++j) {
@@ -218,14 +221,12 @@ __global__ __launch_bounds__(256) void rms_norm_vec_kernel(const uint16_t* __res
   __syncthreads();
   const float tot = part[0] + part[1] + part[2] + part[3];
   const float r = 1.0f / sqrtf(tot / (float)K + eps);
-  const uint4* wr = reinterpret_cast<const uint4*>(w);
   uint4* orow = reinterpret_cast<uint4*>(out + m * K);
 #pragma unroll
   for (int j = 0; j < RV; ++j) {
     const int c = tid + 256 * j;
     if (c >= nc) break;
-    const uint4 wv = wr[c];
-    const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w}, g[4] = {wv.x, wv.y, wv.z, wv.w};
+    const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w}, g[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)

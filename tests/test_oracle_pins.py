@@ -273,6 +273,21 @@ def test_gather_qmm_selects_batches_and_broadcasts():
         oracle.gather_qmm(x, w, s, b, lhs=[3, 0, 2], rhs=[0, 1], gs=32, bits=4)
 
 
+def test_broadcast_gather_indices_cases():
+    # defaults: every batch of x and of the weights in order, broadcast together
+    li, ri, shape = oracle.broadcast_gather_indices((2, 1), (1, 3), None, None)
+    assert tuple(shape) == (2, 3)
+    assert li.tolist() == [0, 0, 0, 1, 1, 1] and ri.tolist() == [0, 1, 2, 0, 1, 2]
+    # given indices of shapes [2, 1] and [1, 3]
+    li, ri, shape = oracle.broadcast_gather_indices((4,), (3,), np.array([[3], [0]]), np.array([[2, 0, 1]]))
+    assert tuple(shape) == (2, 3)
+    assert li.tolist() == [3, 3, 3, 0, 0, 0] and ri.tolist() == [2, 0, 1, 2, 0, 1]
+    with pytest.raises(ValueError):
+        oracle.broadcast_gather_indices((4,), (3,), np.array([0.5]), None)
+    with pytest.raises(ValueError):
+        oracle.broadcast_gather_indices((4,), (3,), np.array([0, 1]), np.array([0, 1, 2]))
+
+
 def test_invalid_arguments():
     # nuvec "invalid_arguments_are_rejected"
     for kw in (dict(K=64, gs=48, bits=4), dict(K=64, gs=64, bits=7), dict(K=96, gs=64, bits=4),
@@ -335,6 +350,56 @@ def test_switch_glu_tiny_brute_force():
     idx = synth.sorted_topk(0, 4, sh.E, sh.top_k)
     got = oracle.switch_glu(x, idx, *ex, gs=sh.gs, bits=sh.bits)
     assert np.array_equal(got, _brute_switch_glu(x, idx, *ex, sh.gs, sh.bits))
+
+
+def test_unsort_inverts_a_stable_expert_sort():
+    """Rows put in expert order by an independent stable argsort come back to
+    token order through the inverse permutation."""
+    g = np.random.default_rng(31)
+    T, top_k, E, H = 7, 3, 5, 4
+    idx = np.sort(np.stack([g.choice(E, top_k, replace=False) for _ in range(T)]), axis=1)
+    y_tok = g.integers(0, 1 << 16, size=(T, top_k, H)).astype(np.uint16)
+    order = np.argsort(idx.reshape(-1), kind="stable")
+    inv = np.empty_like(order)
+    inv[order] = np.arange(order.size)
+    assert np.array_equal(oracle.unsort(y_tok.reshape(T * top_k, H)[order], inv, T, top_k), y_tok)
+
+
+def test_moe_prefill_layer_brute_force():
+    """The sorted-route layer against token-order scalar code: each slot's
+    brute-force SwitchGLU output times its score, summed in slot order in fp32
+    with a bf16 rounding after each product and after the sum, plus the
+    brute-force gated shared expert (sigmoid of its one-row gate logit), added
+    in fp32 and rounded once.  A wrong permutation, gather row or slot order in
+    the sort / unsort / combine composition changes the result."""
+    sh = synth.TINY
+    ex = synth.expert_set(0, sh.E, sh.H, sh.I, sh.gs, sh.bits, mode="drawn")
+    g = np.random.default_rng(33)
+    T = 5
+    x = synth.activations(0, T, sh.H)
+    idx = synth.sorted_topk(0, T, sh.E, sh.top_k)
+    scores = synth.to_bf16(g.uniform(0.05, 0.6, size=(T, sh.top_k)))
+    shp = (synth.drawn_matrix(g, sh.I, sh.H, sh.gs, sh.bits), synth.drawn_matrix(g, sh.I, sh.H, sh.gs, sh.bits),
+           synth.drawn_matrix(g, sh.H, sh.I, sh.gs, sh.bits), synth.drawn_matrix(g, 1, sh.H, sh.gs, sh.bits))
+    out, _ = oracle.moe_prefill_layer(x, idx, scores, ex, shp, gs=sh.gs, bits=sh.bits)
+    y = _brute_switch_glu(x, idx, *ex, sh.gs, sh.bits)
+    one = [tuple(a[None] for a in m) for m in shp[:3]]
+    sw = _brute_switch_glu(x, np.zeros((T, 1), np.int64), *one, sh.gs, sh.bits)[:, 0]
+    wz = oracle.dequant(*shp[3], sh.gs, sh.bits, sh.H)[0]
+    xf = oracle.bf16_to_f64(x)
+    f32 = np.float32
+    r16 = lambda v: f32(oracle.bf16_to_f64(oracle.f64_to_bf16(float(v))))
+    want = np.zeros((T, sh.H), np.uint16)
+    for t in range(T):
+        z = float(r16(math.fsum(xf[t] * wz)))
+        for h in range(sh.H):
+            acc = None
+            for k in range(sh.top_k):
+                p = r16(f32(oracle.bf16_to_f64(y[t, k, h])) * f32(oracle.bf16_to_f64(scores[t, k])))
+                acc = p if acc is None else f32(acc + p)
+            shared = r16(float(oracle.bf16_to_f64(sw[t, h])) / (1.0 + math.exp(-z)))
+            want[t, h] = oracle.f64_to_bf16(float(f32(r16(acc) + shared)))
+    assert np.array_equal(out, want)
 
 
 def test_switch_glu_special_cases():
@@ -725,6 +790,27 @@ def test_mx_matmul_brute_force(mode):
     got2 = oracle.mx_matmul(x2, w2, sc2, mode, False)
     assert got2.dtype == np.float32
     assert np.array_equal(got2, _brute_mx(x2, w2, sc2, mode, False))
+
+
+@pytest.mark.parametrize("mode", ["mxfp4", "mxfp8"])
+def test_gather_qmm_mx_selects_pairs(mode):
+    """gather_qmm_mx takes x[lhs] and expert rhs per pair over the broadcast
+    index shape; each pair equals the exact-rational product of that pair."""
+    g = np.random.default_rng(41 if mode == "mxfp4" else 42)
+    bits = oracle.MX_MODES[mode]
+    E, N, K, X, M = 3, 2, 64, 4, 1
+    codes = g.integers(0, 1 << bits, size=(E, N, K))
+    if bits == 8:
+        codes = np.where((codes & 0x7F) == 0x7F, 0x7E, codes)
+    w = np.stack([synth.pack(codes[e], bits) for e in range(E)])
+    sc = g.integers(120, 134, size=(E, N, K // 32)).astype(np.uint8)
+    x = synth.to_bf16(g.standard_normal((X, M, K)))
+    lhs, rhs = np.array([[3], [0]]), np.array([[2, 0, 1]])
+    got = oracle.gather_qmm_mx(x, w, sc, lhs=lhs, rhs=rhs, transpose=True, mode=mode)
+    assert got.shape == (2, 3, M, N)
+    for i in range(2):
+        for j in range(3):
+            assert np.array_equal(got[i, j], _brute_mx(x[lhs[i, 0]], w[rhs[0, j]], sc[rhs[0, j]], mode, True))
 
 
 def test_mx_block_scale_applies_to_its_32_elements():

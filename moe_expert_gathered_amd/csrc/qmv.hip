@@ -64,13 +64,20 @@ MOEGQ_DEV void reduce_wave(float (&a)[V]) {
 // chunk every `step` slices from `first`).  Every operand is read through a
 // raw buffer descriptor (one per matrix of the pair's expert, one for the
 // activation row): a lane's offset inside a slice is a single 32-bit VGPR
-// shared by all rows, the row offsets are scalars.  Lanes past the end of a
-// row load with an offset beyond every descriptor's range, so the hardware
+// shared by all rows, the row offsets are scalars (the range check covers the
+// scalar offset too, so rows past N read zero).  Lanes past the end of a row
+// load with an offset beyond every descriptor's range, so the hardware
 // returns zero without fetching.  Codes are loaded with the non-temporal
 // hint: each is read once per launch.  All loads of a chunk (codes, scales,
 // biases, activations) are issued before any arithmetic.  acc holds the
 // wave's per-lane partial sums (reduce_wave completes them).
-template <int BITS, int GS, bool GLU, int RPW, int NS, int V = RPW * (GLU ? 2 : 1)>
+// SEL: lanes past the row end also take zero scale and bias through a select.
+// Their loads already return zero, so no value changes; the select makes the
+// compiler wait for the whole chunk before the first arithmetic, which keeps
+// the gate/up and plain kernels at fewer registers and more waves per SIMD
+// (measured faster there).  The down+combine kernel runs faster without it:
+// its arithmetic then starts as each row's loads land.
+template <int BITS, int GS, bool GLU, int RPW, int NS, bool SEL = true, int V = RPW * (GLU ? 2 : 1)>
 MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first, int step, float (&acc)[V]) {
   constexpr int NM = GLU ? 2 : 1;
   constexpr int XV = BITS == 4 ? 4 : 2;   // uint4 of activations per lane per slice
@@ -150,8 +157,8 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
             d = fdot2_bf16(__builtin_amdgcn_perm(C43, hi, 0x04010400u), xp[4 * j + 2], d);
             d = fdot2_bf16(__builtin_amdgcn_perm(C43, hi, 0x04030402u), xp[4 * j + 3], d);
           }
-          const float s = ok[t] ? bf16_to_f32(sv[t][i]) : 0.f;
-          const float b = ok[t] ? bf16_to_f32(bv[t][i]) : 0.f;
+          const float s = (!SEL || ok[t]) ? bf16_to_f32(sv[t][i]) : 0.f;
+          const float b = (!SEL || ok[t]) ? bf16_to_f32(bv[t][i]) : 0.f;
           acc[i] = fmaf(s, d, fmaf(fmaf(-128.f, s, b), sx, acc[i]));
         }
       } else {
@@ -176,8 +183,8 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
             d = fmaf((float)((cw[j] >> 16) & 0xFFu), xf[4 * j + 2], d);
             d = fmaf((float)((cw[j] >> 24) & 0xFFu), xf[4 * j + 3], d);
           }
-          const float s = ok[t] ? bf16_to_f32(sv[t][i]) : 0.f;
-          const float b = ok[t] ? bf16_to_f32(bv[t][i]) : 0.f;
+          const float s = (!SEL || ok[t]) ? bf16_to_f32(sv[t][i]) : 0.f;
+          const float b = (!SEL || ok[t]) ? bf16_to_f32(bv[t][i]) : 0.f;
           acc[i] = fmaf(s, d, fmaf(b, sx, acc[i]));
         }
       }
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(512) void qmv_combine_kernel(QmvArgs A, const uint1
   const int N = A.N;
   const int64_t p = t * top_k + k;
   float acc[RPW];
-  qmv_rows<BITS, GS, false, RPW, NS>(A, p, n0, lane, 0, NS, acc);
+  qmv_rows<BITS, GS, false, RPW, NS, false>(A, p, n0, lane, 0, NS, acc);
   reduce_wave<RPW>(acc);
   if ((lane & 15) == 0) {
     const int rowg = lane >> 4;

@@ -176,7 +176,7 @@ def layer_bytes_flops(sh, T, counts, shared):
     return flops, wbytes + act
 
 
-def prefill_leg(torch, m, synth, rows=(2048, 128, 512, 4096), steps=20, warmup=5, cfg=3):
+def prefill_leg(torch, m, synth, rows=(2048, 128, 512, 4096), steps=100, warmup=5, cfg=3):
     """The MoE layer of hidden 2048, 256 experts, top-8, inter 512, 4-bit GS 64
     with a gated shared expert: one moe_prefill call per step (sort, routed +
     shared experts, gated combine), timed as HIP-graph replays of 10 layers."""

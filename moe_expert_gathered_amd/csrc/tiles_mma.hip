@@ -103,20 +103,29 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
   //      (g, c16) fetches chunk c16 ^ (row % 16) of row 4 (MI w + v) + g
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A.x, 0xFFFFFFFFu);
   uint32_t a_off[8];                          // MI <= 8 entries used
+  // virtual row rr = batch rr / rpb, row rr % rpb of it; the batch's x rows start at
+  // (lhs ? lhs[batch] : batch / lhs_div) * rpb (rpb and lhs_div of 0 mean 1).  The
+  // conditions are uniform and tested once, so the MI index loads are issued
+  // together and waited for once.
+  int rr[8], bt[8];
+  const bool batched = A.rows_per_batch > 1;
+  const int rpb = batched ? (int)A.rows_per_batch : 1;
 #pragma unroll
   for (int v = 0; v < MI; ++v) {
-    const int r = 4 * (MI * wave + v) + g;
-    const int rr = min(r0 + r, r1 - 1);          // rows past the tile repeat a valid row (never stored)
-    // virtual row rr = batch rr / rpb, row rr % rpb of it; the batch's x rows start at
-    // (lhs ? lhs[batch] : batch / lhs_div) * rpb (rpb and lhs_div of 0 mean 1)
-    int src;
-    if (A.rows_per_batch > 1) {
-      const int rpb = (int)A.rows_per_batch, bt = rr / rpb;
-      src = (A.lhs ? A.lhs[bt] : (A.lhs_div > 1 ? bt / (int)A.lhs_div : bt)) * rpb + rr % rpb;
-    } else {
-      src = A.lhs ? A.lhs[rr] : (A.lhs_div > 1 ? rr / (int)A.lhs_div : rr);
-    }
-    const int chunk = c16 ^ lds_swz(r);
+    rr[v] = min(r0 + 4 * (MI * wave + v) + g, r1 - 1);   // rows past the tile repeat a valid row (never stored)
+    bt[v] = batched ? rr[v] / rpb : rr[v];
+  }
+  if (A.lhs) {
+#pragma unroll
+    for (int v = 0; v < MI; ++v) bt[v] = A.lhs[bt[v]];
+  } else if (A.lhs_div > 1) {
+#pragma unroll
+    for (int v = 0; v < MI; ++v) bt[v] /= (int)A.lhs_div;
+  }
+#pragma unroll
+  for (int v = 0; v < MI; ++v) {
+    const int src = batched ? bt[v] * rpb + rr[v] % rpb : bt[v];
+    const int chunk = c16 ^ lds_swz(4 * (MI * wave + v) + g);
     a_off[v] = (uint32_t)src * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
   }
   // ---- code / scale loads: column block j of this wave

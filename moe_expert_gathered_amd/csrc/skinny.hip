@@ -56,6 +56,16 @@ __global__ __launch_bounds__(64 * SK) void skinny_kernel(SkinnyArgs A) {
   f32x4_t acc[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the residual of the lane's four outputs (wave 0 writes them) is requested
+  // before the K loop, so the epilogue waits for no memory
+  uint32_t res_in[4] = {0, 0, 0, 0};      // 32-bit: no packing step that would wait for the loads
+  if (!GLU && A.residual && wave == 0) {
+    // clamped to a valid element (the epilogue uses only valid ones): no
+    // per-lane branch, so no wait before the values are used
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      res_in[q] = A.residual[(p * M + min(4 * lj + q, M - 1)) * (int64_t)N + min(n0 + li, N - 1)];
+  }
 
   // one chunk's operands: CL codes per lane and matrix, their groups' scales
   // and biases, and the matching activations (8-element runs)
@@ -135,7 +145,7 @@ __global__ __launch_bounds__(64 * SK) void skinny_kernel(SkinnyArgs A) {
     if (row < M) {
       const int64_t o = (p * M + row) * (int64_t)N + col;
       float v = GLU ? glu(acc[0][q], acc[NM - 1][q]) : acc[0][q];
-      if (!GLU && A.residual) v = bf16_to_f32(f32_to_bf16(v)) + bf16_to_f32(A.residual[o]);
+      if (!GLU && A.residual) v = bf16_to_f32(f32_to_bf16(v)) + bf16_to_f32((uint16_t)res_in[q]);
       A.out[o] = f32_to_bf16(v);
     }
   }

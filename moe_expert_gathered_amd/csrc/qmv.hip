@@ -224,11 +224,21 @@ __global__ __launch_bounds__(64 * S) void qmv_kernel(QmvArgs A, int64_t p_base) 
   const int n0 = blockIdx.x * RPW;
   const int64_t p = p_base + blockIdx.y;
   const int N = A.N;
+  const int rowg = lane >> 4;
+  // the residual of the values this lane writes is requested before the
+  // weight stream (clamped addresses, 32-bit registers), so the epilogue
+  // waits for no memory
+  uint32_t res_in[V / 4];
+#pragma unroll
+  for (int j = 0; j < V / 4; ++j) res_in[j] = 0;
+  if (!GLU && A.residual && wave == 0) {
+#pragma unroll
+    for (int j = 0; j < V / 4; ++j) res_in[j] = A.residual[p * (int64_t)N + min(n0 + rowg * (V / 4) + j, N - 1)];
+  }
   float acc[V];
   qmv_rows<BITS, GS, GLU, RPW, NS>(A, p, n0, lane, wave * NS, S * NS, acc);
   if (!reduce_waves<S>(acc, lane, wave)) return;
   // lane 16*r (r = 2*bit5 + bit4) holds values r*V/4 .. r*V/4 + V/4 - 1
-  const int rowg = lane >> 4;
   if (GLU) {
     // gate values 0..RPW-1 sit in rows 0-1, up values RPW..2*RPW-1 in rows 2-3
     float u[V / 4];
@@ -248,7 +258,7 @@ __global__ __launch_bounds__(64 * S) void qmv_kernel(QmvArgs A, int64_t p_base) 
         const int n = n0 + rowg * (V / 4) + j;
         if (n < N) {
           float y = acc[j];
-          if (A.residual) y = bf16_to_f32(f32_to_bf16(y)) + bf16_to_f32(A.residual[p * (int64_t)N + n]);
+          if (A.residual) y = bf16_to_f32(f32_to_bf16(y)) + bf16_to_f32((uint16_t)res_in[j]);
           A.out[p * (int64_t)N + n] = f32_to_bf16(y);
         }
       }

@@ -75,18 +75,25 @@ __global__ __launch_bounds__(256) void tile_kernel(TileArgs A) {
   // per-thread roles in the global loads
   const int a_row0 = tid / 16, a_chunk = tid % 16;     // A: rows a_row0 + 16 i, 8 bf16 at chunk
   const int b_n = tid / 4, b_q = tid % 4;              // B: row b_n, codes [32 b_q, 32 b_q + 32)
-  int64_t a_src[AV];
+  // rows past the tile look up row r0 (always valid) and are marked -1 after,
+  // so the AV index loads are issued together and waited for once
+  int64_t a_src[AV], a_r[AV], a_bx[AV];
 #pragma unroll
   for (int i = 0; i < AV; ++i) {
     const int64_t r = r0 + a_row0 + 16 * i;
-    if (a_row0 + 16 * i < BM && r < r1) {
-      const int64_t bq = r / A.rows_per_batch;
-      const int64_t bx = A.lhs ? (int64_t)A.lhs[bq] : bq / A.lhs_div;
-      a_src[i] = bx * A.rows_per_batch + r % A.rows_per_batch;
-    } else {
-      a_src[i] = -1;
-    }
+    a_r[i] = (a_row0 + 16 * i < BM && r < r1) ? r : -1;
+    a_bx[i] = (a_r[i] >= 0 ? a_r[i] : r0) / A.rows_per_batch;
   }
+  if (A.lhs) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) a_bx[i] = A.lhs[a_bx[i]];
+  } else {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) a_bx[i] /= A.lhs_div;
+  }
+#pragma unroll
+  for (int i = 0; i < AV; ++i)
+    a_src[i] = a_r[i] >= 0 ? a_bx[i] * A.rows_per_batch + a_r[i] % A.rows_per_batch : -1;
   const int bn_g = min(n0 + b_n, N - 1);
 
   f32x4_t acc[NM][MI][NI];

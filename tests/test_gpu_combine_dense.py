@@ -71,6 +71,11 @@ def test_affine_qmm_rows(mg, M, bits, gs):
         got_r = mg.affine_qmm(bf(x), words(w), bf(s), bf(b), group_size=gs, bits=bits, residual=bf(r))
         want_r = oracle.f64_to_bf16(oracle.bf16_to_f64(want) + oracle.bf16_to_f64(r))
         assert_parity(host_bf(got_r), want_r, name="residual")
+        # in place (out is the residual buffer): each output's residual is read
+        # by the lane that writes it, so the result is the same bit for bit
+        rt = bf(r)
+        mg.affine_qmm(bf(x), words(w), bf(s), bf(b), group_size=gs, bits=bits, residual=rt, out=rt)
+        assert np.array_equal(host_bf(rt), host_bf(got_r))
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])

@@ -606,8 +606,8 @@ def cpu_baseline(torch, synth, n_layers=5, cfg=1):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus N > 1 is not supported "
-                                   "(the multi-GPU design is documented, not built)"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus N > 1 is not supported "
+                                   "(the library has no multi-GPU path)"}))
         sys.exit(2)
     import torch
     import moe_expert_gathered_amd as m

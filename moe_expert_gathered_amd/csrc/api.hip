@@ -182,7 +182,7 @@ const char* moegq_status_string(int s) {
     case MOEGQ_ERR_GROUP_SIZE: return "group size must be 32, 64 or 128";
     case MOEGQ_ERR_SHAPE: return "shape mismatch";
     case MOEGQ_ERR_DTYPE: return "invalid dtype";
-    case MOEGQ_ERR_UNSUPPORTED: return "valid but not supported by this build";
+    case MOEGQ_ERR_UNSUPPORTED: return "valid but not supported by this library";
     case MOEGQ_ERR_WORKSPACE: return "workspace missing or too small";
     case MOEGQ_ERR_LAUNCH: return "kernel launch failed";
     case MOEGQ_ERR_SELFCHECK: return "fused combine differs from the unfused tail";

@@ -34,7 +34,8 @@ def test_bf16_known_values():
 
 def test_bf16_rounding_matches_torch():
     g = np.random.default_rng(1)
-    x = (g.standard_normal(200000) * np.exp2(g.integers(-140, 128, 200000))).astype(np.float32)
+    with np.errstate(over="ignore"):          # values past float32's range become inf and are dropped below
+        x = (g.standard_normal(200000) * np.exp2(g.integers(-140, 128, 200000))).astype(np.float32)
     # exact ties, to exercise round-half-to-even
     ties = (np.arange(1, 20001, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
     x = np.concatenate([x, ties, -ties])

@@ -246,7 +246,10 @@ int moegq_switch_glu_mode(int64_t T, int64_t top_k, int64_t E);
  * [1, H*bits/32] words + [1, H/gs] scales/biases.  shg_w == NULL: no shared
  * expert (every shared pointer ignored).  H and I must be multiples of 128
  * and of 8 * group_size (else MOEGQ_ERR_UNSUPPORTED).
- * out [T, H] bf16.  workspace: moegq_moe_prefill_workspace_bytes(...) bytes.
+ * out [T, H] bf16.  workspace: moegq_moe_prefill_workspace_bytes(...) bytes;
+ * it includes room for the unfused tail, which the layer runs (sigmoid gate,
+ * unsort, score, sum, add: same bits) instead of the one-pass combine after a
+ * failed moegq_selfcheck on the current device.
  */
 int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
                       const int32_t* idx, int64_t top_k, const void* scores,
@@ -261,6 +264,32 @@ int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
                       size_t workspace_bytes, void* stream);
 size_t moegq_moe_prefill_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t H, int64_t I,
                                          int has_shared);
+
+/*
+ * moe_prefill_layout: where moegq_moe_prefill keeps its sort results and its
+ * two tile tables inside the caller's workspace, for inspection after a call
+ * (MLX PR 4567 Proposed changes: each tile is (row start, expert, valid
+ * rows); the whole-layer route writes one table of up-to-128-row tiles and
+ * one of up-to-32-row tiles).  Writes, for the same (T, top_k, E, H, I,
+ * has_shared) as the call:
+ *   offsets[9]: byte offsets from the workspace start of inv [P] int32,
+ *     lhs [P + extra] int32 (extra = T with a shared expert, else 0),
+ *     sorted_rhs [P], counts [E], expert offsets [E + 1], the 128-row table
+ *     [caps[0], 3], the 32-row table [caps[1], 3], the two tile counts
+ *     [2] int32, and the unfused tail's scratch [P + 2 T, H] bf16 (written
+ *     only after a failed self-check);
+ *   caps[2]: capacity (entries) of the two tables;
+ *   params[4]: the big tile height (128), the small tile height (32), the
+ *     workgroup slots and the first pass's column blocks (ceil(I / 128))
+ *     that decide, on the current device, whether any expert gets 128-row
+ *     tiles (every expert takes 32-row tiles when the 128-row tiles times the
+ *     column blocks come to at most slots / 8).
+ * Host-only (no launch, no device access); all pointers are host memory owned
+ * by the caller.  Errors: MOEGQ_ERR_SHAPE, MOEGQ_ERR_UNSUPPORTED (E > 1024),
+ * MOEGQ_ERR_NULL_ARG.
+ */
+int moegq_moe_prefill_layout(int64_t T, int64_t top_k, int64_t E, int64_t H, int64_t I, int has_shared,
+                             int64_t* offsets, int64_t* caps, int32_t* params);
 
 /*
  * moe_decode: the routed half of a MoE decode layer in two kernels.  Kernel 1
@@ -296,6 +325,8 @@ int moegq_moe_decode(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
  * y [T*top_k, H] bf16; inv [T*top_k] int32 or NULL (= identity, token order);
  * scores [T, top_k] bf16; shared [T, H] bf16 or NULL; out [T, H] bf16.
  * Bit-identical to moegq_moe_combine_unfused on the same inputs.
+ * After a failed moegq_selfcheck on the current device it launches nothing
+ * and returns MOEGQ_ERR_SELFCHECK (the caller runs moegq_moe_combine_unfused).
  */
 int moegq_moe_combine(const void* y, const int32_t* inv, const void* scores, const void* shared,
                       int64_t T, int64_t top_k, int64_t H, void* out, void* stream);
@@ -306,7 +337,8 @@ int moegq_moe_combine(const void* y, const int32_t* inv, const void* scores, con
  * z [T] bf16 its gate logit; the added term is bf16(sigmoid(z[t]) * shared[t]),
  * the arithmetic of moegq_sigmoid_gate (MTPLX PR 558 Summary: the combine
  * takes the gated shared expert).  Bit-identical to moegq_sigmoid_gate
- * followed by moegq_moe_combine.
+ * followed by moegq_moe_combine.  After a failed moegq_selfcheck on the
+ * current device it launches nothing and returns MOEGQ_ERR_SELFCHECK.
  */
 int moegq_moe_combine_gated(const void* y, const int32_t* inv, const void* scores, const void* shared,
                             const void* z, int64_t T, int64_t top_k, int64_t H, void* out, void* stream);
@@ -375,9 +407,9 @@ int moegq_gather_mm(const void* x, int64_t X, int64_t M, int64_t K, const void* 
 
 /*
  * route: the MoE block's routing from its router logits, which produces the
- * idx and scores the expert path takes (MTPLX PR 558 Change: the block
- * computes the routing as the stock block does before the sorted experts and
- * the combine).  logits [T, E] fp32 row-major (finite).  idx [T, top_k] int32:
+ * idx and scores the expert path takes (MTPLX PR 558 Change: the one-kernel
+ * block keeps the unfused block's routing ahead of the sorted experts and the
+ * combine).  logits [T, E] fp32 row-major (finite).  idx [T, top_k] int32:
  * the top_k experts by logit, ties to the lower id, stored in ascending expert
  * id.  scores [T, top_k] bf16: each chosen expert's softmax probability over
  * all E logits, evaluated in float64 with the largest logit subtracted, not
@@ -409,9 +441,33 @@ int moegq_kv_feed_ld(const void* q, int64_t ldq, const void* k, int64_t ldk, con
  * geometry) and compares them bit for bit.  Synchronizes.  Returns MOEGQ_OK or
  * MOEGQ_ERR_SELFCHECK.  workspace: moegq_workspace_bytes(MOEGQ_OP_SELFCHECK,...).
  * Setting the environment variable MOEGQ_FORCE_SELFCHECK_FAIL=1 makes it
- * report a failure (for testing the fallback).
+ * report a failure (for testing the fallback).  The result is kept per
+ * device: after a failure moegq_moe_prefill runs the unfused tail and
+ * moegq_moe_combine / moegq_moe_combine_gated return MOEGQ_ERR_SELFCHECK
+ * (MTPLX PR 558 Change and Tests: a failed check turns the one-kernel route
+ * off for the process); a later passing check turns it back on.
  */
 int moegq_selfcheck(void* workspace, size_t workspace_bytes, void* stream);
+/* selfcheck_state: the current device's last self-check result: 0 not run,
+ * 1 passed, 2 failed.  Host-only. */
+int moegq_selfcheck_state(void);
+
+/*
+ * Measured ceilings (diagnostics, not part of the MoE path): the two plain
+ * kernels that the path's results are stated against besides the published
+ * peaks.
+ * probe_stream_read: reads every byte of buf [bytes] (bytes a multiple of 16,
+ *   buf 16-byte aligned) once with 128-bit loads, blocks workgroups of 256
+ *   threads striding over the buffer; sink: 4 bytes of device memory that the
+ *   kernel only writes when the data XOR to a sentinel (keeps the loads live).
+ * probe_mfma_bf16: blocks workgroups of 4 waves; each wave runs iters rounds
+ *   of 8 independent v_mfma_f32_16x16x32_bf16 on registers, i.e.
+ *   blocks * 4 * iters * 8 * 16384 flops; out: 4 bytes of device memory,
+ *   written only on a sentinel value.
+ * Both asynchronous on `stream`; errors MOEGQ_ERR_SHAPE, _NULL_ARG, _ALIGN.
+ */
+int moegq_probe_stream_read(const void* buf, int64_t bytes, void* sink, int blocks, void* stream);
+int moegq_probe_mfma_bf16(int iters, int blocks, void* out, void* stream);
 
 /* validate_indices: synchronizing debug check that every idx[i] (i < n,
  * int32) lies in [0, E); if `sorted` also that idx is non-decreasing.

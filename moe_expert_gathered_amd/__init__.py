@@ -18,9 +18,10 @@ import torch
 
 __all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "quantized_matmul", "gather_qmm_workspace_bytes",
            "gather_qmm_mx", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
-           "switch_glu", "switch_glu_mode", "moe_decode", "moe_prefill", "moe_prefill_workspace_bytes", "moe_combine", "moe_combine_gated", "moe_combine_unfused", "sort_pairs",
+           "switch_glu", "switch_glu_mode", "moe_decode", "moe_prefill", "moe_prefill_workspace_bytes",
+           "moe_prefill_layout", "moe_prefill_tables", "moe_combine", "moe_combine_gated", "moe_combine_unfused", "sort_pairs",
            "schedule_tiles", "rms_norm", "sigmoid_gate", "route", "gather_mm", "kv_feed", "kv_feed_stacked",
-           "selfcheck",
+           "selfcheck", "selfcheck_state", "probe_stream_read", "probe_mfma_bf16",
            "validate_indices", "workspace_bytes", "MODE_AUTO", "MODE_DECODE", "MODE_SORTED",
            "TILES_SCHEDULED", "TILES_NAIVE"]
 
@@ -72,6 +73,7 @@ _SIGS = {
     "moegq_moe_prefill": ([_p, _i64, _i64, _i64, _i64, _p, _i64, _p] + [_p] * 21 + [_int, _int, _p, _p, _sz, _p],
                           _int),
     "moegq_moe_prefill_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64, _int], _sz),
+    "moegq_moe_prefill_layout": ([_i64, _i64, _i64, _i64, _i64, _int, _p, _p, _p], _int),
     "moegq_moe_combine": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _p], _int),
     "moegq_moe_combine_gated": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p], _int),
     "moegq_moe_combine_unfused": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _sz, _p], _int),
@@ -84,6 +86,9 @@ _SIGS = {
     "moegq_kv_feed": ([_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p], _int),
     "moegq_kv_feed_ld": ([_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _p], _int),
     "moegq_selfcheck": ([_p, _sz, _p], _int),
+    "moegq_selfcheck_state": ([], _int),
+    "moegq_probe_stream_read": ([_p, _i64, _p, _int, _p], _int),
+    "moegq_probe_mfma_bf16": ([_int, _int, _p, _p], _int),
     "moegq_validate_indices": ([_p, _i64, _i64, _int, _p, _p], _int),
 }
 
@@ -132,6 +137,54 @@ def _dev(*ts):
             raise ValueError("moegq ops take device tensors")
         if t is not None and not t.is_contiguous():
             raise ValueError("moegq ops take contiguous tensors")
+
+
+def _req(t, name, dtypes, shape=None):
+    """Argument check of the binding: dtype (one of ``dtypes``) and, where
+    given, the exact shape; a mismatch raises ValueError before anything is
+    launched (the C entry points take raw pointers and cannot see either)."""
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+_BF = (torch.bfloat16,)
+_IDX = (torch.int32,)
+_WORDS = tuple(d for d in (torch.int32, getattr(torch, "uint32", None)) if d is not None)
+
+
+def _req_matrix(trip, name, N, K, bits, gs, batch=()):
+    """(words, scales, biases) of quantized rows: words [*batch, N, K*bits/32]
+    int32/uint32, scales and biases [*batch, N, K/gs] bf16."""
+    w, sc, bi = trip
+    if K * bits % 32 or K % gs:
+        raise ValueError(f"{name}: K={K} is not a whole number of words and groups")
+    _req(w, name + " words", _WORDS, tuple(batch) + (N, K * bits // 32))
+    _req(sc, name + " scales", _BF, tuple(batch) + (N, K // gs))
+    _req(bi, name + " biases", _BF, tuple(batch) + (N, K // gs))
+
+
+def _req_combine(y, inv, scores, shared, out):
+    """Combine tail arguments: y [P, H] bf16 (P = T*top_k expert outputs),
+    inv [P] int32 or None, scores [T, top_k] bf16, shared/out [T, H] bf16."""
+    _req(scores, "scores", _BF)
+    T, top_k = scores.shape
+    _req(y, "y", _BF)
+    if y.dim() != 2 or y.shape[0] < T * top_k:
+        raise ValueError(f"y: shape {tuple(y.shape)}, expected [{T * top_k}, H]")
+    H = y.shape[-1]
+    _req(inv, "inv", _IDX, (T * top_k,))
+    _req(shared, "shared", _BF, (T, H))
+    _req(out, "out", _BF, (T, H))
+
+
+def _req_experts(gate, up, down, E, H, I, bits, gs):
+    _req_matrix(gate, "gate", I, H, bits, gs, (E,))
+    _req_matrix(up, "up", I, H, bits, gs, (E,))
+    _req_matrix(down, "down", H, I, bits, gs, (E,))
 
 
 def workspace_bytes(op: int, P: int, E: int, N: int, bm: int = 0) -> int:
@@ -201,6 +254,8 @@ def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, transpo
     groups along N.  workspace: an optional uint8 device tensor of at least
     gather_qmm_workspace_bytes(...) bytes (else one is allocated).
     """
+    _req(scales, "scales", _BF)
+    _req(biases, "biases", _BF)
     _dev(x, w, scales, biases, rhs_indices, lhs_indices, workspace)
     M, K = x.shape[-2], x.shape[-1]
     N = w.shape[-2] if transpose else w.shape[-1] * 32 // bits
@@ -231,6 +286,7 @@ def gather_qmm_mx(x, w, scales, rhs_indices=None, lhs_indices=None, transpose=Tr
     "mxfp8": E4M3, 4 per word), one E8M0 scale byte per 32 elements along the
     packed axis (scales: uint8 tensor), no biases.  Indices and result type
     as gather_qmm."""
+    _req(scales, "scales", (torch.uint8,))
     _dev(x, w, scales, rhs_indices, lhs_indices, workspace)
     code, bits = MX_MODES[mode]
     M, K = x.shape[-2], x.shape[-1]
@@ -285,6 +341,10 @@ def gather_mm(x, w, rhs_indices, lhs_indices=None, lhs_div=1, sorted_indices=Fal
     x: [X, M, K] (or [X, K] for M = 1) bf16; w: [E, N, K] bf16; rhs_indices [P]
     int32; the x batch of pair p is lhs_indices[p], or p // lhs_div.
     Returns [P, M, N] (M = 1: [P, N])."""
+    _req(x, "x", _BF)
+    _req(w, "w", _BF)
+    _req(rhs_indices, "rhs_indices", _IDX)
+    _req(lhs_indices, "lhs_indices", _IDX)
     _dev(x, w, rhs_indices, lhs_indices)
     squeeze = x.dim() == 2
     X, M, K = (x.shape[0], 1, x.shape[1]) if squeeze else tuple(x.shape)
@@ -304,13 +364,18 @@ def gather_qmm_glu(x, gate, up, rhs_indices, lhs_indices=None, lhs_div=1, group_
     """h[p] = bf16(silu(g) * u) over gathered experts, g/u = x[row(p)] . W[rhs[p]]^T.
     x: [X, M, K] (or [X, K] for M = 1); gate/up: (words [E, N, Kw], scales, biases);
     rhs_indices [P]; the x row of pair p is lhs_indices[p], or p // lhs_div."""
-    _dev(x, *gate, *up, rhs_indices, lhs_indices)
+    _req(x, "x", _BF)
+    _req(rhs_indices, "rhs_indices", _IDX)
+    _req(lhs_indices, "lhs_indices", _IDX)
     if x.dim() == 2:
         X, K = x.shape
         M = 1
     else:
         X, M, K = x.shape
     E, N = gate[0].shape[0], gate[0].shape[1]
+    _req_matrix(gate, "gate", N, K, bits, group_size, (E,))
+    _req_matrix(up, "up", N, K, bits, group_size, (E,))
+    _dev(x, *gate, *up, rhs_indices, lhs_indices)
     P = rhs_indices.numel()
     if out is None:
         out = torch.empty((P, M, N), dtype=torch.bfloat16, device=x.device)
@@ -325,9 +390,12 @@ def gather_qmm_glu(x, gate, up, rhs_indices, lhs_indices=None, lhs_div=1, group_
 
 def affine_qmm(x, w, scales, biases, group_size=64, bits=4, transpose=True, residual=None, out=None):
     """out = x . dequant(w)^T (+ residual after rounding).  x [M, K], w [N, Kw]."""
-    _dev(x, w, scales, biases, residual)
     M, K = x.shape
     N = w.shape[0]
+    _req(x, "x", _BF)
+    _req_matrix((w, scales, biases), "w", N, K, bits, group_size)
+    _req(residual, "residual", _BF, (M, N))
+    _dev(x, w, scales, biases, residual)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     st = lib().moegq_affine_qmm(_ptr(x), _dt(x), M, K, _ptr(w), _wdt(w), _ptr(scales), _ptr(biases), N,
@@ -338,9 +406,12 @@ def affine_qmm(x, w, scales, biases, group_size=64, bits=4, transpose=True, resi
 
 def affine_qmm_glu(x, gate, up, group_size=64, bits=4, out=None):
     """bf16(silu(x . Wg^T) * (x . Wu^T)); gate/up are (words, scales, biases)."""
-    _dev(x, *gate, *up)
     M, K = x.shape
     N = gate[0].shape[0]
+    _req(x, "x", _BF)
+    _req_matrix(gate, "gate", N, K, bits, group_size)
+    _req_matrix(up, "up", N, K, bits, group_size)
+    _dev(x, *gate, *up)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     st = lib().moegq_affine_qmm_glu(_ptr(x), M, K, *[_ptr(t) for t in gate], *[_ptr(t) for t in up], N,
@@ -357,10 +428,15 @@ def switch_glu(x, idx, gate, up, down, group_size=64, bits=4, mode=MODE_AUTO, ti
                bm=0, y=None, inv=None):
     """Routed SwitchGLU.  Returns (y [T*top_k, H], inv [T*top_k] or None, mode used).
     DECODE: y in token order; SORTED: y expert-sorted and inv the inverse permutation."""
-    _dev(x, idx, *gate, *up, *down)
     T, H = x.shape
     top_k = idx.shape[1]
     E, I = gate[0].shape[0], gate[0].shape[1]
+    _req(x, "x", _BF)
+    _req(idx, "idx", _IDX, (T, top_k))
+    _req_experts(gate, up, down, E, H, I, bits, group_size)
+    _req(y, "y", _BF, (T * top_k, H))
+    _req(inv, "inv", _IDX, (T * top_k,))
+    _dev(x, idx, *gate, *up, *down, y, inv)
     P = T * top_k
     if mode == MODE_AUTO:
         mode = switch_glu_mode(T, top_k, E)
@@ -381,10 +457,17 @@ def moe_decode(x, idx, scores, gate, up, down, shared=None, group_size=64, bits=
                workspace=None):
     """Routed MoE decode layer in two kernels: gate/up + SiLU, then down fused
     with the combine tail.  Returns out [T, H] (y [T*top_k, H] filled if given)."""
-    _dev(x, idx, scores, shared, *gate, *up, *down, y)
     T, H = x.shape
     top_k = idx.shape[1]
     E, I = gate[0].shape[0], gate[0].shape[1]
+    _req(x, "x", _BF)
+    _req(idx, "idx", _IDX, (T, top_k))
+    _req(scores, "scores", _BF, (T, top_k))
+    _req(shared, "shared", _BF, (T, H))
+    _req(y, "y", _BF, (T * top_k, H))
+    _req(out, "out", _BF, (T, H))
+    _req_experts(gate, up, down, E, H, I, bits, group_size)
+    _dev(x, idx, scores, shared, *gate, *up, *down, y, out, workspace)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
@@ -402,21 +485,107 @@ def moe_prefill_workspace_bytes(T: int, top_k: int, E: int, H: int, I: int, has_
     return int(lib().moegq_moe_prefill_workspace_bytes(T, top_k, E, H, I, int(has_shared)))
 
 
+ERR_SELFCHECK = -9
+_CHECKED_DEVICES = set()
+
+
+def _ensure_selfcheck(device):
+    """Run the fused-vs-unfused combine self-check once per device before the
+    first combine on it (it synchronizes, so never while a HIP graph is being
+    captured).  MOEGQ_SELFCHECK=0 in the environment skips it."""
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    if key in _CHECKED_DEVICES or os.environ.get("MOEGQ_SELFCHECK", "1") == "0":
+        return
+    if torch.cuda.is_current_stream_capturing():
+        return
+    _CHECKED_DEVICES.add(key)
+    with torch.cuda.device(key):
+        selfcheck(dev)
+
+
+def probe_stream_read(buf, blocks: int, sink=None):
+    """Diagnostic: one streaming read of every byte of the device tensor buf."""
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check(lib().moegq_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), blocks,
+                                         _stream()), "probe_stream_read")
+    return sink
+
+
+def probe_mfma_bf16(iters: int, blocks: int, out) -> int:
+    """Diagnostic: bf16 MFMA loop; returns the flops it performs."""
+    _check(lib().moegq_probe_mfma_bf16(iters, blocks, _ptr(out), _stream()), "probe_mfma_bf16")
+    return blocks * 4 * iters * 8 * 16384
+
+
+def selfcheck_state() -> int:
+    """The current device's last self-check result: 0 not run, 1 passed, 2 failed."""
+    return int(lib().moegq_selfcheck_state())
+
+
+def moe_prefill_layout(T: int, top_k: int, E: int, H: int, I: int, has_shared: bool = True) -> dict:
+    """Byte offsets of moe_prefill's sort results and tile tables inside its
+    workspace, the tables' capacities and the schedule parameters used on
+    the current device (host query, no launch)."""
+    off = (ctypes.c_int64 * 9)()
+    caps = (ctypes.c_int64 * 2)()
+    par = (ctypes.c_int32 * 4)()
+    _check(lib().moegq_moe_prefill_layout(T, top_k, E, H, I, int(bool(has_shared)), off, caps, par),
+           "moe_prefill_layout")
+    names = ("inv", "lhs", "sorted_rhs", "counts", "offsets", "tiles", "small_tiles", "n_tiles", "tail")
+    return dict(offsets=dict(zip(names, list(off))), caps=(caps[0], caps[1]), big=par[0], small=par[1],
+                slots=par[2], col_blocks=par[3])
+
+
+def moe_prefill_tables(workspace, T: int, top_k: int, E: int, H: int, I: int, has_shared: bool = True) -> dict:
+    """Views into a moe_prefill workspace (uint8 device tensor) after a call:
+    inv, lhs, sorted_rhs, counts, offsets, and the two tile tables cut to
+    their counts (each tile = (row start, expert, valid rows))."""
+    L = moe_prefill_layout(T, top_k, E, H, I, has_shared)
+    o = L["offsets"]
+    P = T * top_k
+    extra = T if has_shared else 0
+
+    def view(name, n):
+        return workspace[o[name]:o[name] + 4 * n].view(torch.int32)
+
+    n = view("n_tiles", 2).cpu()
+    big = view("tiles", 3 * L["caps"][0]).view(-1, 3)[:int(n[0])]
+    small = view("small_tiles", 3 * L["caps"][1]).view(-1, 3)[:int(n[1])]
+    return dict(inv=view("inv", P), lhs=view("lhs", P + extra), sorted_rhs=view("sorted_rhs", P),
+                counts=view("counts", E), offsets=view("offsets", E + 1), tiles=big, small_tiles=small,
+                layout=L)
+
+
 def moe_prefill(x, idx, scores, gate, up, down, shared=None, group_size=64, bits=4, out=None, workspace=None):
     """One MoE layer on the expert-sorted route: sort, routed SwitchGLU with the
     gated shared expert riding along, one-pass combine.  shared: None or
     (gate, up, down, gate_row), each a (words, scales, biases) triple.
     Returns out [T, H]."""
-    _dev(x, idx, scores, *gate, *up, *down)
     T, H = x.shape
     top_k = idx.shape[1]
     E, I = gate[0].shape[0], gate[0].shape[1]
+    _req(x, "x", _BF)
+    _req(idx, "idx", _IDX, (T, top_k))
+    _req(scores, "scores", _BF, (T, top_k))
+    _req(out, "out", _BF, (T, H))
+    _req_experts(gate, up, down, E, H, I, bits, group_size)
+    _dev(x, idx, scores, *gate, *up, *down, out, workspace)
     sh = [None] * 12
     if shared is not None:
+        if len(shared) != 4:
+            raise ValueError("shared: (gate, up, down, gate_row) triples")
+        Is = shared[0][0].shape[0]
+        _req_matrix(shared[0], "shared gate", Is, H, bits, group_size)
+        _req_matrix(shared[1], "shared up", Is, H, bits, group_size)
+        _req_matrix(shared[2], "shared down", H, Is, bits, group_size)
+        _req_matrix(shared[3], "shared gate row", 1, H, bits, group_size)
         sh = [t for trip in shared for t in trip]
         _dev(*sh)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _ensure_selfcheck(x.device)
     if workspace is None:
         ws, wsb = _workspace(moe_prefill_workspace_bytes(T, top_k, E, H, I, shared is not None), x.device)
     else:
@@ -430,26 +599,39 @@ def moe_prefill(x, idx, scores, gate, up, down, shared=None, group_size=64, bits
 
 def moe_combine(y, inv, scores, shared=None, out=None):
     """Fused unsort * score, sum over top_k, + shared (one pass)."""
-    _dev(y, inv, scores, shared)
     T, top_k = scores.shape
     H = y.shape[-1]
+    _req_combine(y, inv, scores, shared, out)
+    _dev(y, inv, scores, shared, out)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _ensure_selfcheck(y.device)
     st = lib().moegq_moe_combine(_ptr(y), _ptr(inv), _ptr(scores), _ptr(shared), T, top_k, H, _ptr(out),
                                  _stream())
+    if st == ERR_SELFCHECK:          # the one-pass combine is off on this device: the unfused tail
+        return moe_combine_unfused(y, inv, scores, shared, out=out)
     _check(st, "moe_combine")
     return out
 
 
 def moe_combine_gated(y, inv, scores, shared, z, out=None):
     """moe_combine with the shared expert's sigmoid gate applied in the same pass."""
-    _dev(y, inv, scores, shared, z)
     T, top_k = scores.shape
     H = y.shape[-1]
+    _req_combine(y, inv, scores, shared, out)
+    if shared is None or z is None:
+        raise ValueError("moe_combine_gated: shared and z are required")
+    _req(z, "z", _BF)
+    if z.numel() != T:
+        raise ValueError(f"z: {z.numel()} values, expected {T}")
+    _dev(y, inv, scores, shared, z, out)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _ensure_selfcheck(y.device)
     st = lib().moegq_moe_combine_gated(_ptr(y), _ptr(inv), _ptr(scores), _ptr(shared), _ptr(z), T, top_k, H,
                                        _ptr(out), _stream())
+    if st == ERR_SELFCHECK:          # the one-pass combine is off on this device: gate, then the unfused tail
+        return moe_combine_unfused(y, inv, scores, sigmoid_gate(shared, z), out=out)
     _check(st, "moe_combine_gated")
     return out
 
@@ -457,9 +639,10 @@ def moe_combine_gated(y, inv, scores, shared, z, out=None):
 def moe_combine_unfused(y, inv, scores, shared=None, out=None, workspace=None):
     """The same tail as four kernels, each writing a bf16 tensor.  workspace:
     optional uint8 device tensor of workspace_bytes(OP_COMBINE_UNFUSED, ...) bytes."""
-    _dev(y, inv, scores, shared, workspace)
     T, top_k = scores.shape
     H = y.shape[-1]
+    _req_combine(y, inv, scores, shared, out)
+    _dev(y, inv, scores, shared, workspace, out)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
     need = workspace_bytes(OP_COMBINE_UNFUSED, T * top_k, 0, H, 0)
@@ -475,6 +658,7 @@ def moe_combine_unfused(y, inv, scores, shared=None, out=None, workspace=None):
 
 def sort_pairs(idx, E: int):
     """(order, lhs, sorted_rhs, inv, counts, offsets), all int32 device tensors."""
+    _req(idx, "idx", _IDX)
     _dev(idx)
     T, top_k = idx.shape
     P = T * top_k
@@ -489,6 +673,7 @@ def sort_pairs(idx, E: int):
 
 def schedule_tiles(offsets, E: int, P_max: int, bm: int, tile_mode=TILES_SCHEDULED):
     """(tiles [cap, 3], n_tiles [1]) device int32."""
+    _req(offsets, "offsets", _IDX, (E + 1,))
     _dev(offsets)
     cap = (P_max + bm - 1) // bm + min(E, P_max)
     tiles = torch.full((max(cap, 1), 3), -7, dtype=torch.int32, device=offsets.device)
@@ -515,8 +700,11 @@ def route(logits, top_k, idx=None, scores=None):
 
 
 def rms_norm(x, w, eps=1e-6, out=None):
-    _dev(x, w)
     M, K = x.shape
+    _req(x, "x", _BF)
+    _req(w, "w", _BF, (K,))
+    _req(out, "out", _BF, (M, K))
+    _dev(x, w, out)
     if out is None:
         out = torch.empty_like(x)
     _check(lib().moegq_rms_norm(_ptr(x), _ptr(w), M, K, eps, _ptr(out), _stream()), "rms_norm")
@@ -525,8 +713,12 @@ def rms_norm(x, w, eps=1e-6, out=None):
 
 def sigmoid_gate(s, z, out=None):
     """bf16(sigmoid(z[t]) * s[t, :]); z [T, 1] or [T]."""
-    _dev(s, z)
     T, H = s.shape
+    _req(s, "s", _BF)
+    _req(z, "z", _BF)
+    if z.shape[0] != T:
+        raise ValueError(f"z: {z.shape[0]} rows, expected {T}")
+    _dev(s, out)
     zs = z.stride(0) if z.dim() >= 1 else 1
     if out is None:
         out = torch.empty_like(s)
@@ -536,8 +728,12 @@ def sigmoid_gate(s, z, out=None):
 
 def kv_feed(q, k, v, out=None):
     """bf16(q + bf16(k[:, :1] + v[:, :1]))."""
-    _dev(q, k, v)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _req(t, n, _BF)
     M, Nq = q.shape
+    if k.shape[0] != M or v.shape[0] != M:
+        raise ValueError("q, k and v must have the same rows")
+    _dev(q, k, v)
     if out is None:
         out = torch.empty_like(q)
     _check(lib().moegq_kv_feed(_ptr(q), _ptr(k), _ptr(v), M, Nq, k.shape[1], v.shape[1], _ptr(out), _stream()),
@@ -548,6 +744,7 @@ def kv_feed(q, k, v, out=None):
 def kv_feed_stacked(qkv, nq, nk, nv, out=None):
     """kv_feed on one stacked product qkv [M, nq + nk + nv] (q, k, v as its
     column ranges): bf16(q + bf16(k[:, :1] + v[:, :1]))."""
+    _req(qkv, "qkv", _BF)
     _dev(qkv)
     M, L = qkv.shape
     if L != nq + nk + nv:

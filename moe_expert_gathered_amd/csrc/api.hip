@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "../../include/moegq.h"
 #include "launch.h"
@@ -22,6 +23,12 @@ hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int status_of(hipError_t e) { return e == hipSuccess ? MOEGQ_OK : MOEGQ_ERR_LAUNCH; }
+
+// The one-row kernels address one expert matrix through a 32-bit buffer
+// range and park the lanes past a row's end at offset 0x7FFFFFF0, which must
+// lie beyond that range: one matrix of codes stays at most 0x7FFFFFF0 bytes.
+constexpr int64_t kNoFetchOffset = 0x7FFFFFF0;
+bool one_row_fits(int64_t N, int64_t K, int bits) { return N * K * bits / 8 <= kNoFetchOffset; }
 
 // bit width / group size / quantized length checks
 int check_quant(int64_t K, int gs, int bits) {
@@ -105,6 +112,24 @@ int device_slots() {
   }
   return v;
 }
+// Result of the last moegq_selfcheck per device: 0 not run, 1 passed,
+// 2 failed.  After a failure the entry points that would run the one-pass
+// combine run the unfused tail instead (moe_prefill) or refuse
+// (moe_combine, moe_combine_gated), for the rest of the process unless a
+// later self-check passes (MTPLX PR 558 Change and Tests: a failed check turns
+// the one-kernel route off).
+std::atomic<int> g_selfcheck[64];
+int selfcheck_state() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  return g_selfcheck[dev].load(std::memory_order_relaxed);
+}
+bool fused_tail_off() { return selfcheck_state() == 2; }
+void set_selfcheck_state(int v) {
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) g_selfcheck[dev].store(v, std::memory_order_relaxed);
+}
+
 void set_hybrid_model(SortArgs& sa, int64_t I) {
   sa.small_max = kSmallMax;
   sa.cost_slots = device_slots();
@@ -112,12 +137,15 @@ void set_hybrid_model(SortArgs& sa, int64_t I) {
 }
 
 // sorted-route workspace layout.  extra: rows of the extra (shared) expert
-// appended after the P sorted rows; layer: also the fp16 activations [T, H],
-// the expert outputs [P + extra, H] and the shared gate logits [T].
+// appended after the P sorted rows; xexp: the exponents of the gate/up pass's
+// fp16 activation rows (at most P rows); layer: also the fp16 activations
+// [T, H], the expert outputs [P + extra, H], the shared gate logits [T] and
+// the unfused tail's scratch.
 struct SortedWs {
   int32_t* order; int32_t* lhs; int32_t* srhs; int32_t* counts; int32_t* offsets;
-  int32_t* tiles; int32_t* small_tiles; int32_t* n_tiles; int32_t* bc; uint16_t* h;
+  int32_t* tiles; int32_t* small_tiles; int32_t* n_tiles; int32_t* bc; uint16_t* h; int32_t* xexp;
   uint16_t* x16; uint16_t* y; uint16_t* z;
+  uint16_t* tail;     // layer: scratch of the unfused tail after a failed self-check, [(P + 2 T), H]
   size_t bytes;
 };
 SortedWs sorted_layout(char* base, int64_t P, int64_t E, int64_t I, int bm, int64_t extra = 0,
@@ -136,10 +164,12 @@ SortedWs sorted_layout(char* base, int64_t P, int64_t E, int64_t I, int bm, int6
   w.n_tiles = (int32_t*)take(8);
   w.bc = (int32_t*)take(4 * sort_blocks(P) * E);
   w.h = (uint16_t*)take(2 * (P + extra) * I);
+  w.xexp = (int32_t*)take(4 * (layer ? T : P));
   if (layer) {
     w.x16 = (uint16_t*)take(2 * T * H);
     w.y = (uint16_t*)take(2 * (P + extra) * H);
     w.z = (uint16_t*)take(2 * T);
+    w.tail = (uint16_t*)take(2 * (P + 2 * T) * H);
   }
   w.bytes = off;
   return w;
@@ -334,7 +364,7 @@ static int gather_impl(const void* x, int x_dtype, int64_t X, int64_t M, int64_t
     return status_of(launch_tiles(a, bits, group_size, glu, s));
   }
   if (M == 1) {
-    if (K > kMaxQmvK) return MOEGQ_ERR_UNSUPPORTED;
+    if (K > kMaxQmvK || !one_row_fits(N, K, bits)) return MOEGQ_ERR_UNSUPPORTED;
     QmvArgs a{};
     a.x = (const uint16_t*)x; a.lhs = lhs; a.lhs_div = lhs_div; a.rhs = rhs;
     a.w0 = (const uint32_t*)w; a.s0 = (const uint16_t*)scales; a.b0 = (const uint16_t*)biases;
@@ -421,7 +451,7 @@ int moegq_affine_qmm(const void* x, int x_dtype, int64_t M, int64_t K, const voi
   if (!x || !w || !scales || !biases || !out) return MOEGQ_ERR_NULL_ARG;
   if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return MOEGQ_ERR_ALIGN;
   hipStream_t s = S(stream);
-  if (M == 1 && K <= kMaxQmvK) {
+  if (M == 1 && K <= kMaxQmvK && one_row_fits(N, K, bits)) {
     QmvArgs a{};
     a.x = (const uint16_t*)x; a.lhs_div = 1;
     a.w0 = (const uint32_t*)w; a.s0 = (const uint16_t*)scales; a.b0 = (const uint16_t*)biases;
@@ -468,7 +498,7 @@ int moegq_affine_qmm_glu(const void* x, int64_t M, int64_t K, const void* wg, co
   if (!x || !wg || !sg || !bg || !wu || !su || !bu || !out) return MOEGQ_ERR_NULL_ARG;
   if (!aligned16(x) || !aligned16(wg) || !aligned16(wu) || !aligned16(out)) return MOEGQ_ERR_ALIGN;
   hipStream_t s = S(stream);
-  if (M == 1 && K <= kMaxQmvK) {
+  if (M == 1 && K <= kMaxQmvK && one_row_fits(N, K, bits)) {
     QmvArgs a{};
     a.x = (const uint16_t*)x; a.lhs_div = 1;
     a.w0 = (const uint32_t*)wg; a.s0 = (const uint16_t*)sg; a.b0 = (const uint16_t*)bg;
@@ -540,7 +570,8 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
   if (mode == MOEGQ_MODE_SORTED && (E > kMaxExperts)) return MOEGQ_ERR_UNSUPPORTED;
   if (mode == MOEGQ_MODE_SORTED && !inv) return MOEGQ_ERR_NULL_ARG;
   if (mode == MOEGQ_MODE_DECODE) {
-    if (H > kMaxQmvK || I > kMaxQmvK) return MOEGQ_ERR_UNSUPPORTED;
+    if (H > kMaxQmvK || I > kMaxQmvK || !one_row_fits(I, H, bits) || !one_row_fits(H, I, bits))
+      return MOEGQ_ERR_UNSUPPORTED;
     const size_t need = moegq_workspace_bytes(MOEGQ_OP_SWITCH_GLU_DECODE, P, E, I, 0);
     if (!workspace || workspace_bytes < need) return MOEGQ_ERR_WORKSPACE;
     uint16_t* h = (uint16_t*)workspace;
@@ -603,20 +634,22 @@ int moegq_switch_glu(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
   ds_.grid_tiles = small_cap(P, E);
   g.tile_mode = 0; d.tile_mode = 0;
   if (tiles_mma_supported(H, I, T, group_size) && tiles_mma_supported(I, H, P, group_size)) {
-    // fp16 copy of x for the matrix cores, parked in y (y is written only by the down pass);
-    // h is written and read in the same fp16 chunk order
-    if (launch_prep((const uint16_t*)x, T, (int)H, bits, group_size, (uint16_t*)y, nullptr, nullptr, nullptr, nullptr,
-                    s) != hipSuccess)
+    // the gate/up pass reads x as scaled fp16 rows (their exponents in the
+    // workspace), parked in y, which only the down pass writes, after every
+    // reader of x; the down pass reads the bf16 intermediate as stored
+    if (launch_prep((const uint16_t*)x, T, (int)H, bits, group_size, (uint16_t*)y, ws.xexp, nullptr, nullptr,
+                    nullptr, nullptr, s) != hipSuccess)
       return MOEGQ_ERR_LAUNCH;
-    g.x = gs_.x = (const uint16_t*)y;
+    g.x = (const uint16_t*)y;
+    g.xexp = ws.xexp;
     if (hybrid) {
       g.tiles2 = d.tiles2 = ws.small_tiles; g.n_tiles2 = d.n_tiles2 = ws.n_tiles + 1;
       g.grid_tiles2 = d.grid_tiles2 = small_cap(P, E);
-      if (launch_tiles_mma_dual(g, bits, group_size, true, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-      return status_of(launch_tiles_mma_dual(d, bits, group_size, false, false, s));
+      if (launch_tiles_mma_dual(g, bits, group_size, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+      return status_of(launch_tiles_mma_dual(d, bits, group_size, false, s));
     }
-    if (launch_tiles_mma(g, bits, group_size, true, true, 128, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-    return status_of(launch_tiles_mma(d, bits, group_size, false, false, 128, s));
+    if (launch_tiles_mma(g, bits, group_size, true, 128, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    return status_of(launch_tiles_mma(d, bits, group_size, false, 128, s));
   }
   if (launch_tiles_big(g, bits, group_size, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   if (hybrid && launch_tiles_small(gs_, bits, group_size, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
@@ -630,6 +663,27 @@ size_t moegq_moe_prefill_workspace_bytes(int64_t T, int64_t top_k, int64_t E, in
   if (T < 0 || top_k <= 0 || E <= 0 || H <= 0 || I <= 0) return 0;
   const int64_t P = T * top_k;
   return sorted_layout(nullptr, P, E, I, 0, has_shared ? T : 0, T, H, true).bytes;
+}
+
+int moegq_moe_prefill_layout(int64_t T, int64_t top_k, int64_t E, int64_t H, int64_t I, int has_shared,
+                             int64_t* offsets, int64_t* caps, int32_t* params) {
+  if (T < 0 || top_k <= 0 || E <= 0 || H <= 0 || I <= 0 || T > kMaxDim || top_k > 64) return MOEGQ_ERR_SHAPE;
+  if (E > kMaxExperts) return MOEGQ_ERR_UNSUPPORTED;
+  if (!offsets || !caps || !params) return MOEGQ_ERR_NULL_ARG;
+  const int64_t P = T * top_k, extra = has_shared ? T : 0;
+  char* const base = (char*)(uintptr_t)4096;        // any aligned base: offsets are relative to it
+  const SortedWs w = sorted_layout(base, P, E, I, 0, extra, T, H, true);
+  const void* parts[9] = {w.order, w.lhs, w.srhs, w.counts, w.offsets, w.tiles, w.small_tiles, w.n_tiles, w.tail};
+  for (int i = 0; i < 9; ++i) offsets[i] = (int64_t)((const char*)parts[i] - base);
+  caps[0] = big_cap(P, E) + (extra + kBigM - 1) / kBigM;
+  caps[1] = small_cap(P, E, extra);
+  SortArgs sa{};
+  set_hybrid_model(sa, I);
+  params[0] = kBigM;
+  params[1] = sa.small_max;
+  params[2] = sa.cost_slots;
+  params[3] = sa.cost_nb;
+  return MOEGQ_OK;
 }
 
 int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, const int32_t* idx,
@@ -671,14 +725,14 @@ int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
   sa.small_tiles = ws.small_tiles;
   set_hybrid_model(sa, I);
   sa.extra_rows = extra; sa.block_counts = ws.bc;
-  // the sort, and the fp16 activations with the shared expert's sigmoid gate
-  // logit (one pass over x), in one launch when the pairs allow
-  if (launch_front(sa, (const uint16_t*)x, T, (int)H, bits, group_size, ws.x16,
+  // the sort, and the scaled fp16 activations with the shared expert's
+  // sigmoid-gate logit (one pass over x), in one launch when the pairs allow
+  if (launch_front(sa, (const uint16_t*)x, T, (int)H, bits, group_size, ws.x16, ws.xexp,
                    shared ? (const uint32_t*)gate_w : nullptr, (const uint16_t*)gate_s, (const uint16_t*)gate_b, ws.z,
                    s) != hipSuccess)
     return MOEGQ_ERR_LAUNCH;
   TileArgs g{};
-  g.x = ws.x16; g.lhs = ws.lhs; g.lhs_div = 1; g.rows_per_batch = 1;
+  g.x = ws.x16; g.xexp = ws.xexp; g.lhs = ws.lhs; g.lhs_div = 1; g.rows_per_batch = 1;
   g.tiles = ws.tiles; g.n_tiles = ws.n_tiles; g.P = P; g.E = (int)E;
   g.w0 = (const uint32_t*)wg; g.s0 = (const uint16_t*)sg; g.b0 = (const uint16_t*)bg;
   g.w1 = (const uint32_t*)wu; g.s1 = (const uint16_t*)su; g.b1 = (const uint16_t*)bu;
@@ -696,9 +750,20 @@ int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
   // 128-row tiles (hot experts, shared expert) and 32-row tiles (tail experts) in one launch per pass
   g.tiles2 = d.tiles2 = ws.small_tiles; g.n_tiles2 = d.n_tiles2 = ws.n_tiles + 1;
   g.grid_tiles2 = d.grid_tiles2 = small_cap(P, E, extra);
-  if (launch_tiles_mma_dual(g, bits, group_size, true, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-  if (launch_tiles_mma_dual(d, bits, group_size, false, false, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (launch_tiles_mma_dual(g, bits, group_size, true, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (launch_tiles_mma_dual(d, bits, group_size, false, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   // out[t] = bf16(bf16(sum_k bf16(y[inv] * score)) + bf16(sigmoid(z[t]) * y[P + t]))
+  if (fused_tail_off()) {
+    // the self-check failed on this device: the unfused tail, the gate first
+    // (its own kernel), then unsort, score, sum over top_k, add
+    uint16_t* gated = nullptr;
+    if (shared) {
+      gated = ws.tail + (P + T) * H;
+      if (launch_sigmoid_gate(ws.y + P * H, ws.z, 1, T, H, gated, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+    }
+    return status_of(launch_combine_unfused(ws.y, inv, (const uint16_t*)scores, gated, T, (int)top_k, H,
+                                            (uint16_t*)out, ws.tail, s, true));
+  }
   return status_of(launch_combine(ws.y, inv, (const uint16_t*)scores, shared ? ws.y + P * H : nullptr,
                                   shared ? ws.z : nullptr, T, (int)top_k, H, (uint16_t*)out, s));
 }
@@ -712,7 +777,8 @@ int moegq_moe_decode(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
   if ((st = check_quant(H, group_size, bits))) return st;
   if ((st = check_quant(I, group_size, bits))) return st;
   if (T < 0 || top_k <= 0 || E <= 0 || T > kMaxDim || top_k > 64 || H % 8 != 0) return MOEGQ_ERR_SHAPE;
-  if (H > kMaxQmvK || I > kMaxQmvK) return MOEGQ_ERR_UNSUPPORTED;
+  if (H > kMaxQmvK || I > kMaxQmvK || !one_row_fits(I, H, bits) || !one_row_fits(H, I, bits))
+    return MOEGQ_ERR_UNSUPPORTED;
   if (T == 0) return MOEGQ_OK;
   if (!x || !idx || !scores || !wg || !sg || !bg || !wu || !su || !bu || !wd || !sd || !bd || !out)
     return MOEGQ_ERR_NULL_ARG;
@@ -752,6 +818,7 @@ int moegq_moe_combine(const void* y, const int32_t* inv, const void* scores, con
   if (T == 0) return MOEGQ_OK;
   if (!y || !scores || !out) return MOEGQ_ERR_NULL_ARG;
   if (!aligned16(y) || !aligned16(out) || (shared && !aligned16(shared))) return MOEGQ_ERR_ALIGN;
+  if (fused_tail_off()) return MOEGQ_ERR_SELFCHECK;
   return status_of(launch_combine((const uint16_t*)y, inv, (const uint16_t*)scores, (const uint16_t*)shared,
                                   nullptr, T, (int)top_k, H, (uint16_t*)out, S(stream)));
 }
@@ -762,6 +829,7 @@ int moegq_moe_combine_gated(const void* y, const int32_t* inv, const void* score
   if (T == 0) return MOEGQ_OK;
   if (!y || !scores || !shared || !z || !out) return MOEGQ_ERR_NULL_ARG;
   if (!aligned16(y) || !aligned16(out) || !aligned16(shared)) return MOEGQ_ERR_ALIGN;
+  if (fused_tail_off()) return MOEGQ_ERR_SELFCHECK;
   return status_of(launch_combine((const uint16_t*)y, inv, (const uint16_t*)scores, (const uint16_t*)shared,
                                   (const uint16_t*)z, T, (int)top_k, H, (uint16_t*)out, S(stream)));
 }
@@ -826,7 +894,7 @@ int moegq_gather_mm(const void* x, int64_t X, int64_t M, int64_t K, const void* 
   if (!x || !w || !rhs_indices || !out) return MOEGQ_ERR_NULL_ARG;
   if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return MOEGQ_ERR_ALIGN;
   if (!lhs_indices && (P - 1) / lhs_div >= X) return MOEGQ_ERR_SHAPE;
-  if (N * K >= ((int64_t)1 << 31) || X * M * K >= ((int64_t)1 << 31)) return MOEGQ_ERR_UNSUPPORTED;
+  if (N * K * 2 > kNoFetchOffset || X * M * K >= ((int64_t)1 << 31)) return MOEGQ_ERR_UNSUPPORTED;
   hipStream_t s = S(stream);
   const size_t need = moegq_workspace_bytes(MOEGQ_OP_GATHER_MM, P, E, M, 0);
   TileArgs a{};
@@ -918,13 +986,30 @@ int moegq_selfcheck(void* workspace, size_t workspace_bytes, void* stream) {
   if (launch_combine(y, inv, scores, shared, nullptr, T, (int)K, H, o1, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   if (launch_combine_unfused(y, inv, scores, shared, T, (int)K, H, o2, scratch, s) != hipSuccess)
     return MOEGQ_ERR_LAUNCH;
-  static uint16_t h1[128 * 2048], h2[128 * 2048];
-  if (hipMemcpyAsync(h1, o1, sizeof(h1), hipMemcpyDeviceToHost, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
-  if (hipMemcpyAsync(h2, o2, sizeof(h2), hipMemcpyDeviceToHost, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  std::vector<uint16_t> h1(T * H), h2(T * H);      // host copies (calls from several threads stay apart)
+  const size_t nb = h1.size() * sizeof(uint16_t);
+  if (hipMemcpyAsync(h1.data(), o1, nb, hipMemcpyDeviceToHost, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
+  if (hipMemcpyAsync(h2.data(), o2, nb, hipMemcpyDeviceToHost, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   if (hipStreamSynchronize(s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   const char* force = getenv("MOEGQ_FORCE_SELFCHECK_FAIL");
-  if (force && force[0] == '1') return MOEGQ_ERR_SELFCHECK;
-  return memcmp(h1, h2, sizeof(h1)) == 0 ? MOEGQ_OK : MOEGQ_ERR_SELFCHECK;
+  const bool same = memcmp(h1.data(), h2.data(), nb) == 0 && !(force && force[0] == '1');
+  set_selfcheck_state(same ? 1 : 2);
+  return same ? MOEGQ_OK : MOEGQ_ERR_SELFCHECK;
+}
+
+int moegq_selfcheck_state(void) { return selfcheck_state(); }
+
+int moegq_probe_stream_read(const void* buf, int64_t bytes, void* sink, int blocks, void* stream) {
+  if (bytes < 16 || bytes % 16 != 0 || blocks <= 0) return MOEGQ_ERR_SHAPE;
+  if (!buf || !sink) return MOEGQ_ERR_NULL_ARG;
+  if (!aligned16(buf)) return MOEGQ_ERR_ALIGN;
+  return status_of(launch_stream_read(buf, bytes, (uint32_t*)sink, blocks, S(stream)));
+}
+
+int moegq_probe_mfma_bf16(int iters, int blocks, void* out, void* stream) {
+  if (iters <= 0 || blocks <= 0) return MOEGQ_ERR_SHAPE;
+  if (!out) return MOEGQ_ERR_NULL_ARG;
+  return status_of(launch_mfma_loop(iters, blocks, (float*)out, S(stream)));
 }
 
 int moegq_validate_indices(const int32_t* idx, int64_t n, int64_t E, int sorted, int32_t* workspace,

@@ -89,9 +89,10 @@ __global__ __launch_bounds__(256) void unsort_kernel(const uint16_t* __restrict_
   *reinterpret_cast<uint4*>(u + pair * H + h8) = *reinterpret_cast<const uint4*>(y + row * H + h8);
 }
 // (2) weight: w[t, k, :] = bf16(u[t, k, :] * score[t, k])
-__global__ __launch_bounds__(256) void weight_kernel(const uint16_t* __restrict__ u,
-                                                     const uint16_t* __restrict__ scores, int64_t P,
-                                                     int64_t H, uint16_t* __restrict__ w) {
+// u and w may be the same buffer (each thread reads its 8 elements, then
+// writes them), so neither is declared restrict
+__global__ __launch_bounds__(256) void weight_kernel(const uint16_t* u, const uint16_t* __restrict__ scores,
+                                                     int64_t P, int64_t H, uint16_t* w) {
   const int64_t cpr = H / 8;
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= P * cpr) return;
@@ -146,12 +147,12 @@ __global__ __launch_bounds__(256) void add_kernel(const uint16_t* __restrict__ a
 
 hipError_t launch_combine_unfused(const uint16_t* y, const int32_t* inv, const uint16_t* scores,
                                   const uint16_t* shared, int64_t T, int top_k, int64_t H,
-                                  uint16_t* out, uint16_t* scratch, hipStream_t st) {
+                                  uint16_t* out, uint16_t* scratch, hipStream_t st, bool compact) {
   const int64_t P = T * top_k;
   if (P == 0) return hipSuccess;
   uint16_t* u = scratch;
-  uint16_t* w = scratch + P * H;
-  uint16_t* s = scratch + 2 * P * H;
+  uint16_t* w = compact ? u : scratch + P * H;      // compact: the weighting writes over the unsorted copy
+  uint16_t* s = compact ? scratch + P * H : scratch + 2 * P * H;
   const unsigned gp = (unsigned)((P * (H / 8) + 255) / 256);
   const unsigned gt = (unsigned)((T * (H / 8) + 255) / 256);
   hipLaunchKernelGGL(unsort_kernel, dim3(gp), dim3(256), 0, st, y, inv, P, H, u);

@@ -91,8 +91,9 @@ MOEGQ_DEV void deq8_f16(uint32_t w, f16x2_t s2, f16x2_t b2, uint32_t o[2]) {
   o[0] = deq_pair(w, 0x04010400u, s2, b2);
   o[1] = deq_pair(w, 0x04030402u, s2, b2);
 }
+// fp32 pair -> fp16 pair, round to nearest even
 MOEGQ_DEV uint32_t cvt_f16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+  return __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)a, (_Float16)b});
 }
 // eight consecutive bf16 activations (four dwords) -> four fp16 pairs in the
 // 4-bit code order (x0,x2) (x4,x6) (x1,x3) (x5,x7), or in natural order
@@ -104,6 +105,59 @@ MOEGQ_DEV uint4 act_f16(uint4 v) {
   return make_uint4(cvt_f16x2(bf16_lo(v.x), bf16_hi(v.x)), cvt_f16x2(bf16_lo(v.y), bf16_hi(v.y)),
                     cvt_f16x2(bf16_lo(v.z), bf16_hi(v.z)), cvt_f16x2(bf16_lo(v.w), bf16_hi(v.w)));
 }
+// the same with every value multiplied by 2^e (exact: the bf16 values keep
+// their 8 significant bits in fp16 down to 2^-14; smaller ones round to
+// fp16's subnormal spacing, 2^-24)
+template <int BITS>
+MOEGQ_DEV uint4 act_f16_ldexp(uint4 v, int e) {
+  auto lo = [&](uint32_t d) { return __builtin_ldexpf(bf16_lo(d), e); };
+  auto hi = [&](uint32_t d) { return __builtin_ldexpf(bf16_hi(d), e); };
+  if (BITS == 4)
+    return make_uint4(cvt_f16x2(lo(v.x), lo(v.y)), cvt_f16x2(lo(v.z), lo(v.w)), cvt_f16x2(hi(v.x), hi(v.y)),
+                      cvt_f16x2(hi(v.z), hi(v.w)));
+  return make_uint4(cvt_f16x2(lo(v.x), hi(v.x)), cvt_f16x2(lo(v.y), hi(v.y)), cvt_f16x2(lo(v.z), hi(v.z)),
+                    cvt_f16x2(lo(v.w), hi(v.w)));
+}
+
+// ---- bf16 operands for the matrix cores ------------------------------------
+// The tile kernels dequantize to bf16 for v_mfma_f32_16x16x32_bf16, so the
+// activations and intermediates enter the matrix cores as stored (bf16's
+// whole range, no conversion).  A code enters fp16 exactly as 1024 + q (its
+// byte under the exponent byte 0x64, one v_perm per two codes);
+// v_fma_mix_f32 evaluates (1024 + q) * s + c in fp32, with c = b - 1024 s
+// formed once per group, so w = q * s + b up to two fp32 roundings (far
+// below bf16's); v_cvt_pk_bf16_f32 rounds two weights to bf16 (nearest
+// even).  Limit: |s| < 2^117 (1024 s stays finite).
+MOEGQ_DEV float bias1024(float s, float b) { return __builtin_fmaf(-1024.0f, s, b); }
+MOEGQ_DEV uint32_t pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
+}
+MOEGQ_DEV f16x2_t magic_pair(uint32_t codes, uint32_t sel) {
+  return __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, codes, sel));
+}
+// eight 4-bit codes of one word -> four bf16 pairs in natural order (q0,q1) .. (q6,q7)
+MOEGQ_DEV void deq4_bf16(uint32_t w, float s, float c, uint32_t o[4]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;   // bytes: q0 q2 q4 q6 / q1 q3 q5 q7
+  const f16x2_t a0 = magic_pair(lo, 0x04010400u), a1 = magic_pair(lo, 0x04030402u);
+  const f16x2_t b0 = magic_pair(hi, 0x04010400u), b1 = magic_pair(hi, 0x04030402u);
+  o[0] = pk_bf16(__builtin_fmaf((float)a0[0], s, c), __builtin_fmaf((float)b0[0], s, c));
+  o[1] = pk_bf16(__builtin_fmaf((float)a0[1], s, c), __builtin_fmaf((float)b0[1], s, c));
+  o[2] = pk_bf16(__builtin_fmaf((float)a1[0], s, c), __builtin_fmaf((float)b1[0], s, c));
+  o[3] = pk_bf16(__builtin_fmaf((float)a1[1], s, c), __builtin_fmaf((float)b1[1], s, c));
+}
+// four 8-bit codes of one word -> two bf16 pairs in natural order (q0,q1) (q2,q3)
+MOEGQ_DEV void deq8_bf16(uint32_t w, float s, float c, uint32_t o[2]) {
+  const f16x2_t a = magic_pair(w, 0x04010400u), b = magic_pair(w, 0x04030402u);
+  o[0] = pk_bf16(__builtin_fmaf((float)a[0], s, c), __builtin_fmaf((float)a[1], s, c));
+  o[1] = pk_bf16(__builtin_fmaf((float)b[0], s, c), __builtin_fmaf((float)b[1], s, c));
+}
+
+// Exponent that brings a magnitude m > 0 into [2^13, 2^14) when divided out:
+// m * 2^-e is in that range for e = frexp_exp(m) - 14 (exact for subnormal
+// m too); 0 for m == 0.  Scaling fp16 operands this way keeps them normal
+// and finite whatever the bf16 magnitudes, and undoing it on the fp32 result
+// is exact.
+MOEGQ_DEV int f16_exponent(float m) { return m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 14 : 0; }
 
 MOEGQ_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }
 MOEGQ_DEV float round_bf16(float v) { return bf16_to_f32(f32_to_bf16(v)); }

@@ -87,30 +87,32 @@ struct TileArgs {
   int64_t grid_tiles;       // upper bound of the tile count (grid size)
   // second tile table (tiles_mma dual launch: tiles of at most 32 rows)
   const int32_t* tiles2; const int32_t* n_tiles2; int64_t grid_tiles2;
+  const int32_t* xexp;      // tiles_mma gate/up: exponent of each fp16 activation row (indexed like x)
 };
 hipError_t launch_tiles(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st);
 // 128-row tiles (tile_mode 0: table, 2: dense rows); grid_tiles = table capacity or row tiles
 hipError_t launch_tiles_big(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st);
 // tiles of at most 16 (bm <= 16) or 32 rows from a table (tile_mode 0); rows gathered through lhs
 hipError_t launch_tiles_small(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st);
-// 128-row tiles with register-dequantized weights (tile_mode 0: table, 2: dense rows).  a.x holds
-// fp16 rows in the dequantizer's chunk order (launch_prep), gathered through a.lhs (or row r);
-// out16: the GLU output is written the same way (fp16, chunk order) for a following down pass
+// tiles with register-dequantized weights on the matrix cores (tile_mode 0: table, 2: dense rows).
+// GLU (gate/up): a.x holds the fp16 rows of launch_prep and a.xexp their exponents, gathered
+// through a.lhs (or row r); otherwise a.x holds bf16 rows
 bool tiles_mma_supported(int64_t K, int64_t N, int64_t src_rows, int gs);
 // rows: 128 (tile table of up to 128-row tiles, or dense rows) or 32 (tiles of at most 32 rows)
-hipError_t launch_tiles_mma(const TileArgs& a, int bits, int gs, bool glu, bool out16, int rows,
-                            hipStream_t st);
+hipError_t launch_tiles_mma(const TileArgs& a, int bits, int gs, bool glu, int rows, hipStream_t st);
 // both tables in one launch: `tiles` (up to 128 rows, n_tiles) and `tiles2` (up to 32 rows, n_tiles2)
 // bf16 expert matrices as the first MFMA operand (no dequantization): rows 64 or 32 (one table), 0 (both)
 hipError_t launch_tiles_mma_w16(const TileArgs& a, bool glu, int rows, hipStream_t st);
-hipError_t launch_tiles_mma_dual(const TileArgs& a, int bits, int gs, bool glu, bool out16, hipStream_t st);
-// x [T, H] bf16 -> x16 (fp16, chunk order); with gw (a [1, H] quantized row) also z[t] = bf16(x[t] . w)
-hipError_t launch_prep(const uint16_t* x, int64_t T, int H, int bits, int gs, uint16_t* x16, const uint32_t* gw,
-                       const uint16_t* gsc, const uint16_t* gbi, uint16_t* z, hipStream_t st);
+hipError_t launch_tiles_mma_dual(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st);
+// x [T, H] bf16 -> xexp[t] (row exponent) and x16 = fp16(x * 2^-xexp) in the dequantizer's chunk
+// order, the input of the gate/up pass; with gw (a [1, H] quantized row) also z[t] = bf16(x[t] . w)
+hipError_t launch_prep(const uint16_t* x, int64_t T, int H, int bits, int gs, uint16_t* x16, int32_t* xexp,
+                       const uint32_t* gw, const uint16_t* gsc, const uint16_t* gbi, uint16_t* z, hipStream_t st);
 // sort (SortArgs) and prep: one launch when the pairs fit one workgroup's
 // sort, else the block sort with prep riding in its count launch
 hipError_t launch_front(const SortArgs& sa, const uint16_t* x, int64_t T, int H, int bits, int gs, uint16_t* x16,
-                        const uint32_t* gw, const uint16_t* gsc, const uint16_t* gbi, uint16_t* z, hipStream_t st);
+                        int32_t* xexp, const uint32_t* gw, const uint16_t* gsc, const uint16_t* gbi, uint16_t* z,
+                        hipStream_t st);
 
 // combine tail
 // shared (nullable) rows [T, H] are added as they are, or, with z (nullable, [T] bf16), gated first:
@@ -118,9 +120,11 @@ hipError_t launch_front(const SortArgs& sa, const uint16_t* x, int64_t T, int H,
 hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const uint16_t* scores,
                           const uint16_t* shared, const uint16_t* z, int64_t T, int top_k, int64_t H,
                           uint16_t* out, hipStream_t st);
+// scratch: 2 P H + T H elements (unsorted, weighted, summed), or with compact
+// (P + T) H (the weighting writes over the unsorted copy, element by element)
 hipError_t launch_combine_unfused(const uint16_t* y, const int32_t* inv, const uint16_t* scores,
                                   const uint16_t* shared, int64_t T, int top_k, int64_t H,
-                                  uint16_t* out, uint16_t* scratch, hipStream_t st);
+                                  uint16_t* out, uint16_t* scratch, hipStream_t st, bool compact = false);
 
 // glue
 hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t K, float eps,
@@ -154,6 +158,9 @@ struct VecArgs {
 };
 hipError_t launch_qmm_vec(const VecArgs& a, int bits, int transpose, hipStream_t st);
 hipError_t launch_iota(int32_t* dst, int64_t n, hipStream_t st);
+// measured ceilings (diagnostics): a streaming read of `bytes` and a bf16 MFMA loop
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int blocks, hipStream_t st);
+hipError_t launch_mfma_loop(int iters, int blocks, float* out, hipStream_t st);
 hipError_t launch_validate(const int32_t* idx, int64_t n, int64_t E, int sorted, int32_t* flag,
                            hipStream_t st);
 hipError_t launch_fill_selfcheck(uint16_t* y, int32_t* inv, uint16_t* scores, uint16_t* shared,

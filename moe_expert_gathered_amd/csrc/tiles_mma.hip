@@ -9,21 +9,22 @@
 // the gate/up pass gathers activation rows through lhs, the down pass reads
 // the sorted intermediate rows in order.
 //
-// gfx950 mapping (v_mfma_f32_16x16x32_f16, fp32 accumulation):
+// gfx950 mapping (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
 //  * 4 waves; each wave owns all 16 * MI rows and 64 MFMA columns (MI x 4
 //    blocks; 128 fp32 accumulators at MI = 8).  A column's codes are read by exactly one wave,
 //    so each code is dequantized once per tile, in registers, in the layout
-//    the MFMA B operand wants: lane (g = lane / 16, c = lane % 16) holds for
+//    the MFMA operand wants: lane (g = lane / 16, c = lane % 16) holds for
 //    column c the 32 consecutive k of lane group g (k0 + 32 g ..), which it
 //    loads as one (4-bit) or two (8-bit) 128-bit buffer loads.  Inside a K
 //    step of 128, MFMA sub-step s contracts k0 + 32 g + 8 s + (0..7) in lane
 //    group g; both operands use that same assignment, so the sum is the full
-//    dot product over K.
-//  * The activation rows are fp16 (converted once, before the tile pass) in
-//    the element order the dequantizer produces inside each 8-element chunk
-//    (4-bit: q0 q2 q4 q6 q1 q3 q5 q7; 8-bit: natural).  They travel from HBM
-//    to LDS with buffer loads that write LDS directly (no register staging),
-//    into a double buffer (2 x 4 KiB per 16 rows), each row's 16-byte chunks
+//    dot product over K.  Weights are dequantized to bf16 in natural k order
+//    (deq4_bf16 / deq8_bf16).
+//  * The activation rows are the caller's bf16 rows (gate/up: x gathered
+//    through lhs; down: the bf16 intermediate), used as stored: no
+//    conversion pass, and bf16's whole range.  They travel from HBM to LDS
+//    with buffer loads that write LDS directly (no register staging), into a
+//    ring of stages (4 KiB per 16 rows each), each row's 16-byte chunks
 //    permuted (lds_swz) so that operand reads are free of bank conflicts.
 //  * GLU: a wave's 4 column blocks are (gate f, up f, gate f+16, up f+16), so
 //    silu(g) * u is applied in registers in the epilogue.
@@ -56,8 +57,9 @@ constexpr int TM_K = 128;   // K per step
 MOEGQ_DEV int lds_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 // eight codes (one 4-bit word, or two 8-bit words) -> one fp16 MFMA operand
+// (4-bit: in the order q0 q2 q4 q6 q1 q3 q5 q7; 8-bit: natural)
 template <int BITS>
-MOEGQ_DEV f16x8_t deq_operand(uint32_t w0, uint32_t w1, f16x2_t s2, f16x2_t b2) {
+MOEGQ_DEV f16x8_t deq_operand_f16(uint32_t w0, uint32_t w1, f16x2_t s2, f16x2_t b2) {
   uint32_t o[4];
   if (BITS == 4) {
     deq4_f16(w0, s2, b2, o);
@@ -67,9 +69,21 @@ MOEGQ_DEV f16x8_t deq_operand(uint32_t w0, uint32_t w1, f16x2_t s2, f16x2_t b2) 
   }
   return __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
+// the same as one bf16 operand in natural k order; s the group's scale, c = b - 1024 s
+template <int BITS>
+MOEGQ_DEV bf16x8_t deq_operand_bf16(uint32_t w0, uint32_t w1, float s, float c) {
+  uint32_t o[4];
+  if (BITS == 4) {
+    deq4_bf16(w0, s, c, o);
+  } else {
+    deq8_bf16(w0, s, c, o);
+    deq8_bf16(w1, s, c, o + 2);
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
 
 // One tile: rows r0 .. r1 - 1 of expert e, MFMA columns n0 .. n0 + 255.  lds
-// holds the activation ring: RA stages of 16 * MI rows x TM_K fp16.
+// holds the activation ring: RA stages of 16 * MI rows x TM_K 16-bit values.
 template <int MI, int BITS = 4> struct MmaRing {
   // K steps of activation (LDS) and code (register) prefetch: one for 128-row
   // tiles and for bf16 weights (register-bound), three for the shorter tiles
@@ -80,12 +94,24 @@ template <int MI, int BITS = 4> struct MmaRing {
   static constexpr int HALFS = RA * 16 * MI * TM_K;
 };
 
-// BITS = 16: the expert matrices are plain bf16 (no scales or biases); their
-// words go to v_mfma_f32_16x16x32_bf16 as loaded, with the bf16 activations
-// in natural order.
-template <int BITS, int GS, bool GLU, bool OUT16, int MI>
-MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e, int n0) {
+// Operand precision per pass:
+//  * gate/up (GLU, quantized weights): fp16 operands.  The activation rows
+//    arrive as fp16 copies scaled by 2^-xexp[row] (launch_front / launch_prep:
+//    the row's largest magnitude lands in [2^13, 2^14)), and each weight
+//    column is scaled by 2^-ec, ec taken at the tile's start from the
+//    column's largest |s| * qmax + |b| over all its groups; the epilogue
+//    multiplies the fp32 result by 2^(xexp + ec).  The scalings are exact, so
+//    the products keep fp16's 11-bit weights (the precision silu(g) * u
+//    needs: it rounds g and u to bf16 first) over bf16's whole range.
+//  * down (and any pass without GLU): bf16 operands, the intermediate as
+//    stored, weights dequantized to bf16.
+//  * BITS = 16: the expert matrices are plain bf16 (no scales or biases);
+//    their words go to the MFMA as loaded.
+// xe_s: LDS for 16 * MI row exponents (gate/up pass).
+template <int BITS, int GS, bool GLU, int MI>
+MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, int r1, int e, int n0) {
   constexpr bool W16 = BITS == 16;
+  constexpr bool F16 = GLU && !W16;
   constexpr int CB = 4 * BITS;                    // code bytes per lane per K step (32 codes)
   using Ring = MmaRing<MI, BITS>;
   constexpr int PDA = Ring::PDA, PDB = Ring::PDB, RA = Ring::RA, RB = Ring::RB, U = Ring::U;
@@ -127,6 +153,9 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
     const int src = batched ? bt[v] * rpb + rr[v] % rpb : bt[v];
     const int chunk = c16 ^ lds_swz(4 * (MI * wave + v) + g);
     a_off[v] = (uint32_t)src * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
+    // the row exponents of the fp16 activations, for the epilogue (row-major
+    // position in the tile; one lane per row writes)
+    if (F16 && c16 == 0) xe_s[4 * (MI * wave + v) + g] = A.xexp[src];
   }
   // ---- code / scale loads: column block j of this wave
   const size_t wstride = (size_t)N * Kw, sstride = (size_t)N * G;
@@ -145,18 +174,15 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
       rb1 = make_rsrc((ex ? A.xb1 : A.b1) + eo * sstride, (uint32_t)(sstride * 2));
     }
   }
-  // MFMA column n of block j is output feature block_base(j) + col_perm(n).
-  // The MFMA runs with the weights as the first operand, so lane (g, c16) ends
-  // up with outputs n = 4 g .. 4 g + 3 of activation row c16; col_perm makes
-  // those four land next to each other in memory (one 8-byte store): the
-  // identity, except for the fp16 intermediate of 4-bit codes, whose chunk
-  // order (q0 q2 q4 q6 q1 q3 q5 q7) is undone by taking features 0 2 4 6 1 3 5 7.
+  // MFMA column n of block j is output feature block_base(j) + n.  The MFMA
+  // runs with the weights as the first operand, so lane (g, c16) ends up with
+  // outputs n = 4 g .. 4 g + 3 of activation row c16, next to each other in
+  // memory (one 8-byte store).
   auto block_base = [&](int j) { return GLU ? n0 + 32 * wave + 16 * (j >> 1) : n0 + 64 * wave + 16 * j; };
-  auto col_perm = [](int n) { return (OUT16 && BITS == 4) ? 8 * (n >> 3) + 2 * (n & 3) + ((n >> 2) & 1) : n; };
   uint32_t w_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int col = block_base(j) + col_perm(c16);
+    const int col = block_base(j) + c16;
     const int fr = min(col, N - 1);               // columns past N repeat a valid one (never stored)
     w_off[j] = (uint32_t)fr * (uint32_t)Kw * 4u + (uint32_t)(g * CB);
   }
@@ -167,7 +193,7 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
   // Window w covers groups 8 w .. 8 w + 7, i.e. K steps GS / 16 * w ..
   constexpr int WSTEPS = GS / 16;
   const int lj = lane >> 4;
-  const int lcol = block_base(lj) + col_perm(c16);
+  const int lcol = block_base(lj) + c16;
   const uint32_t sw_off = (uint32_t)min(lcol, N - 1) * (uint32_t)G * 2u;
   const bool lup = GLU && (lj & 1);
   auto load_win = [&](int w, uint4& ws, uint4& wb) {
@@ -179,6 +205,32 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
       if (lup) { ws = us; wb = ub; }
     }
   };
+  // fp16 weight columns: the owner lane of column (block lj, c16) finds the
+  // column's exponent from all its groups' scales and biases; ecj[j] is the
+  // exponent of this lane's column in block j (the picks), taken from its owner
+  int ecol = 0, ecj[4] = {0, 0, 0, 0};
+  if constexpr (F16) {
+    constexpr float QMAX = (float)((1 << BITS) - 1);
+    const int nwin = G / 8;
+    float mx = 0.f;
+    for (int w0 = 0; w0 < nwin; w0 += 4) {        // four windows' loads in flight at a time
+      uint4 ws[4], wb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_win(min(w0 + i, nwin - 1), ws[i], wb[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t ds[4] = {ws[i].x, ws[i].y, ws[i].z, ws[i].w}, db[4] = {wb[i].x, wb[i].y, wb[i].z, wb[i].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          mx = fmaxf(mx, __builtin_fmaf(fabsf(bf16_lo(ds[d])), QMAX, fabsf(bf16_lo(db[d]))));
+          mx = fmaxf(mx, __builtin_fmaf(fabsf(bf16_hi(ds[d])), QMAX, fabsf(bf16_hi(db[d]))));
+        }
+      }
+    }
+    ecol = f16_exponent(mx);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ecj[j] = __shfl(ecol, 16 * j + c16, 64);
+  }
   // group of (lane group g, step ks) inside its window: e = (8 ks / WSTEPS + 32 g / GS) % 8;
   // the dword holding it is the same for every lane except at GS = 32
   auto sel4 = [](const uint4& v, int d) -> uint32_t {
@@ -244,6 +296,7 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
     __builtin_amdgcn_s_waitcnt(0x0F70 | (VM & 15) | ((VM >> 4) << 14));
     __syncthreads();                      // every wave's rows landed; the stage of step ks - 1 is free
     f16x2_t s2[4], b2[4];
+    float sj[4], cj[4];
     if constexpr (!W16) {
       if (ks % WSTEPS == 0) {
         win_s = nwin_s; win_b = nwin_b;
@@ -251,8 +304,13 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        s2[j] = f16_splat(pick(win_s, ks, j));
-        b2[j] = f16_splat(pick(win_b, ks, j));
+        if constexpr (F16) {
+          s2[j] = f16_splat(__builtin_ldexpf(pick(win_s, ks, j), -ecj[j]));
+          b2[j] = f16_splat(__builtin_ldexpf(pick(win_b, ks, j), -ecj[j]));
+        } else {
+          sj[j] = pick(win_s, ks, j);
+          cj[j] = bias1024(sj[j], pick(win_b, ks, j));
+        }
       }
     }
     const uint16_t* base = lds + sa * STAGE + c16 * TM_K;
@@ -260,25 +318,28 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
     for (int s = 0; s < 4; ++s) {
       issue_a(ks + PDA, fa, s);           // a quarter of later steps' loads per sub-step
       issue_b(ks + PDB, fb, s);
-      f16x8_t bq[4];
+      uint4 bq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t* wv = &cw[sb][j][0].x;
-        if constexpr (W16) bq[j] = __builtin_bit_cast(f16x8_t, cw[sb][j][s]);   // k 32 g + 8 s .. + 7
-        else if constexpr (BITS == 4) bq[j] = deq_operand<4>(wv[s], 0, s2[j], b2[j]);
-        else bq[j] = deq_operand<8>(wv[2 * s], wv[2 * s + 1], s2[j], b2[j]);
+        if constexpr (W16) bq[j] = cw[sb][j][s];   // k 32 g + 8 s .. + 7
+        else if constexpr (F16 && BITS == 4) bq[j] = __builtin_bit_cast(uint4, deq_operand_f16<4>(wv[s], 0, s2[j], b2[j]));
+        else if constexpr (F16) bq[j] = __builtin_bit_cast(uint4, deq_operand_f16<8>(wv[2 * s], wv[2 * s + 1], s2[j], b2[j]));
+        else if constexpr (BITS == 4) bq[j] = __builtin_bit_cast(uint4, deq_operand_bf16<4>(wv[s], 0, sj[j], cj[j]));
+        else bq[j] = __builtin_bit_cast(uint4, deq_operand_bf16<8>(wv[2 * s], wv[2 * s + 1], sj[j], cj[j]));
       }
       const int slot = (4 * g + s) ^ lds_swz(c16);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(base + i * 16 * TM_K + slot * 8);
+        const uint4 a = *reinterpret_cast<const uint4*>(base + i * 16 * TM_K + slot * 8);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if constexpr (W16)
+          if constexpr (F16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, bq[j]),
+                                                               __builtin_bit_cast(f16x8_t, a), acc[i][j], 0, 0, 0);
+          else
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bq[j]),
                                                                 __builtin_bit_cast(bf16x8_t, a), acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bq[j], a, acc[i][j], 0, 0, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -307,12 +368,21 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
   }
   static_assert(U <= 6, "unroll");
 
-  // epilogue: acc[i][j][q] = output (row 16 i + c16, memory column block_base(j) + 4 g + q)
+  // epilogue: acc[i][j][q] = output (row 16 i + c16, memory column block_base(j) + 4 g + q);
+  // the fp16 pass undoes its scalings: column (j, 4 g + q) is owned by lane 16 j + 4 g + q
+  int eo_col[4][4];
+  if constexpr (F16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) eo_col[j][q] = __shfl(ecol, 16 * j + 4 * g + q, 64);
+  }
   const bool vec = (N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int r = r0 + 16 * i + c16;
     if (r >= r1) continue;
+    const int xe = F16 ? xe_s[16 * i + c16] : 0;
     uint16_t* orow = A.out + (size_t)r * N;
 #pragma unroll
     for (int j = 0; j < (GLU ? 2 : 4); ++j) {
@@ -321,8 +391,12 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int r0, int r1, int e
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (GLU) {
-          const float hv = round_bf16(glu(acc[i][2 * j][q], acc[i][2 * j + 1][q]));
-          o[q] = OUT16 ? __builtin_bit_cast(uint16_t, (_Float16)hv) : f32_to_bf16(hv);
+          float gv = acc[i][2 * j][q], uv = acc[i][2 * j + 1][q];
+          if (F16) {
+            gv = __builtin_ldexpf(gv, xe + eo_col[2 * j][q]);
+            uv = __builtin_ldexpf(uv, xe + eo_col[2 * j + 1][q]);
+          }
+          o[q] = f32_to_bf16(glu(gv, uv));
         } else {
           o[q] = f32_to_bf16(acc[i][j][q]);
         }
@@ -349,10 +423,11 @@ MOEGQ_DEV int xcd_remap(int b, int total) {
 
 // register budget: 2 workgroups per CU (128 accumulators per lane at MI = 8;
 // the 32-row variant needs far fewer registers)
-template <int BITS, int GS, bool GLU, bool OUT16, int MI>
+template <int BITS, int GS, bool GLU, int MI>
 __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
   constexpr int NF = GLU ? TM_C / 2 : TM_C;      // output features per tile
   __shared__ __attribute__((aligned(16))) uint16_t As[MmaRing<MI, BITS>::HALFS];
+  __shared__ int xe_s[16 * MI];
   const int NB = (A.N + NF - 1) / NF;
   const int total = A.tile_mode == 2 ? (int)gridDim.x : *A.n_tiles * NB;
   if ((int)blockIdx.x >= total) return;
@@ -368,7 +443,7 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
     const int32_t* t = A.tiles + 3 * tile;
     r0 = t[0]; e = t[1]; r1 = r0 + t[2];
   }
-  tile_body<BITS, GS, GLU, OUT16, MI>(A, As, r0, r1, e, n0);
+  tile_body<BITS, GS, GLU, MI>(A, As, xe_s, r0, r1, e, n0);
 }
 
 // Both tile tables in one launch: blocks [0, n_big * NB) take the 128-row
@@ -376,48 +451,52 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
 // 32-row tiles of `tiles2`.
 // The few-row tiles stream their experts' weights from HBM while the last
 // round of 128-row tiles keeps only part of the machine busy.
-template <int BITS, int GS, bool GLU, bool OUT16>
+template <int BITS, int GS, bool GLU>
 __global__ __launch_bounds__(256, 2) void tile_mma_dual_kernel(TileArgs A) {
   constexpr int NF = GLU ? TM_C / 2 : TM_C;
   constexpr int MIB = BITS == 16 ? 4 : 8;   // bf16 weights: 64-row big tiles (register budget)
   constexpr int HALFS = MmaRing<MIB, BITS>::HALFS > MmaRing<2, BITS>::HALFS ? MmaRing<MIB, BITS>::HALFS
                                                                            : MmaRing<2, BITS>::HALFS;
   __shared__ __attribute__((aligned(16))) uint16_t As[HALFS];
+  __shared__ int xe_s[16 * MIB];
   const int NB = (A.N + NF - 1) / NF;
   const int nbig = *A.n_tiles * NB, nsmall = *A.n_tiles2 * NB;
   const int b = blockIdx.x;
   if (b < nbig) {
     const int bid = xcd_remap(b, nbig);
     const int32_t* t = A.tiles + 3 * (bid / NB);
-    tile_body<BITS, GS, GLU, OUT16, MIB>(A, As, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
+    tile_body<BITS, GS, GLU, MIB>(A, As, xe_s, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
   } else if (b < nbig + nsmall) {
     const int bid = b - nbig;
     const int32_t* t = A.tiles2 + 3 * (bid / NB);
-    tile_body<BITS, GS, GLU, OUT16, 2>(A, As, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
+    tile_body<BITS, GS, GLU, 2>(A, As, xe_s, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
   }
 }
 
-// One pass over the activation rows before the tile passes: bf16 -> fp16 in
-// the dequantizer's element order (8-element chunks), and, given the shared
-// expert's one-row sigmoid gate, its logit z[t] = bf16(x[t] . dequant(w)^T)
-// (fp32 dequant and accumulation; MTPLX PR 558 Summary: the gated shared
-// expert).  256 threads per row (tid 0..255); red holds 4 floats; every
-// thread of the block calls this.
+// One activation row before the gate/up pass (256 threads, tid 0..255, per
+// row): its exponent xexp[t] (the row's largest |x| lands in [2^13, 2^14)
+// when scaled by 2^-xexp), the fp16 copy x16[t] = x[t] * 2^-xexp[t] in the
+// dequantizer's element order (4-bit: x0 x2 x4 x6 x1 x3 x5 x7 per 8), and,
+// given the shared expert's one-row sigmoid gate gw, its logit
+// z[t] = bf16(x[t] . dequant(w)^T) with fp32 dequant and accumulation (MTPLX
+// PR 558 Summary: the gated shared expert).  red holds 8 floats; every thread
+// of the block calls this (it synchronises the block once).
 template <int BITS, int GS>
 MOEGQ_DEV void prep_row(const uint16_t* __restrict__ x, int64_t T, int H, uint16_t* __restrict__ x16,
-                        const uint32_t* __restrict__ gw, const uint16_t* __restrict__ gs_,
-                        const uint16_t* __restrict__ gb, uint16_t* __restrict__ z, int64_t t, int tid, float* red) {
-  float part = 0.f;
+                        int32_t* __restrict__ xexp, const uint32_t* __restrict__ gw,
+                        const uint16_t* __restrict__ gs_, const uint16_t* __restrict__ gb,
+                        uint16_t* __restrict__ z, int64_t t, int tid, float* red) {
+  float part = 0.f, mx = 0.f;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (t < T ? t : 0) * (int64_t)H);
   if (t < T) {
-    const uint4* xr = reinterpret_cast<const uint4*>(x + t * (int64_t)H);
-    uint4* xo = reinterpret_cast<uint4*>(x16 + t * (int64_t)H);
     for (int c = tid; c < H / 8; c += 256) {
       const uint4 v = xr[c];
-      xo[c] = act_f16<BITS>(v);
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(d[i])), fabsf(bf16_hi(d[i]))));
       if (gw) {
         const int k0 = 8 * c;
         const float s = bf16_to_f32(gs_[k0 / GS]), b = bf16_to_f32(gb[k0 / GS]);
-        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
         uint32_t w0 = gw[k0 * BITS / 32], w1 = BITS == 8 ? gw[k0 * BITS / 32 + 1] : 0u;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -428,21 +507,33 @@ MOEGQ_DEV void prep_row(const uint16_t* __restrict__ x, int64_t T, int H, uint16
       }
     }
   }
-  if (!gw) return;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
-  if ((tid & 63) == 0) red[tid >> 6] = part;
+  for (int m = 32; m >= 1; m >>= 1) {
+    part += __shfl_xor(part, m, 64);
+    mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  }
+  if ((tid & 63) == 0) {
+    red[tid >> 6] = part;
+    red[4 + (tid >> 6)] = mx;
+  }
   __syncthreads();
-  if (tid == 0 && t < T) z[t] = f32_to_bf16(red[0] + red[1] + red[2] + red[3]);
+  if (t >= T) return;
+  const int ex = f16_exponent(fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
+  if (tid == 0) {
+    xexp[t] = ex;
+    if (gw) z[t] = f32_to_bf16(red[0] + red[1] + red[2] + red[3]);
+  }
+  uint4* xo = reinterpret_cast<uint4*>(x16 + t * (int64_t)H);
+  for (int c = tid; c < H / 8; c += 256) xo[c] = act_f16_ldexp<BITS>(xr[c], -ex);
 }
 
 template <int BITS, int GS>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ x, int64_t T, int H,
-                                                   uint16_t* __restrict__ x16, const uint32_t* __restrict__ gw,
-                                                   const uint16_t* __restrict__ gs_, const uint16_t* __restrict__ gb,
-                                                   uint16_t* __restrict__ z) {
-  __shared__ float red[4];
-  prep_row<BITS, GS>(x, T, H, x16, gw, gs_, gb, z, blockIdx.x, threadIdx.x, red);
+                                                   uint16_t* __restrict__ x16, int32_t* __restrict__ xexp,
+                                                   const uint32_t* __restrict__ gw, const uint16_t* __restrict__ gs_,
+                                                   const uint16_t* __restrict__ gb, uint16_t* __restrict__ z) {
+  __shared__ float red[8];
+  prep_row<BITS, GS>(x, T, H, x16, xexp, gw, gs_, gb, z, blockIdx.x, threadIdx.x, red);
 }
 
 // The front of a prefill layer in one launch (at most SORT_ONE_MAX_P pairs):
@@ -451,17 +542,18 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 template <int BITS, int GS>
 __global__ __launch_bounds__(SORT_THREADS) void front_kernel(SortArgs S, const uint16_t* __restrict__ x, int64_t T,
                                                              int H, uint16_t* __restrict__ x16,
+                                                             int32_t* __restrict__ xexp,
                                                              const uint32_t* __restrict__ gw,
                                                              const uint16_t* __restrict__ gs_,
                                                              const uint16_t* __restrict__ gb, uint16_t* __restrict__ z) {
-  __shared__ float red[16];
+  __shared__ float red[32];
   if (blockIdx.x == 0) {
     sort_one_block(S);
     return;
   }
   const int sub = threadIdx.x >> 8;
-  prep_row<BITS, GS>(x, T, H, x16, gw, gs_, gb, z, (int64_t)(blockIdx.x - 1) * 4 + sub, threadIdx.x & 255,
-                     red + 4 * sub);
+  prep_row<BITS, GS>(x, T, H, x16, xexp, gw, gs_, gb, z, (int64_t)(blockIdx.x - 1) * 4 + sub, threadIdx.x & 255,
+                     red + 8 * sub);
 }
 
 // Above SORT_ONE_MAX_P pairs: blocks 0 .. nb - 1 count the block sort's
@@ -469,54 +561,51 @@ __global__ __launch_bounds__(SORT_THREADS) void front_kernel(SortArgs S, const u
 template <int BITS, int GS>
 __global__ __launch_bounds__(SORT_THREADS) void count_prep_kernel(SortArgs S, int64_t nb, const uint16_t* __restrict__ x,
                                                                   int64_t T, int H, uint16_t* __restrict__ x16,
+                                                                  int32_t* __restrict__ xexp,
                                                                   const uint32_t* __restrict__ gw,
                                                                   const uint16_t* __restrict__ gs_,
                                                                   const uint16_t* __restrict__ gb,
                                                                   uint16_t* __restrict__ z) {
-  __shared__ float red[16];
+  __shared__ float red[32];
   if ((int64_t)blockIdx.x < nb) {
     sort_count_block(S.idx, S.P, S.E, S.block_counts, blockIdx.x);
     return;
   }
   const int sub = threadIdx.x >> 8;
-  prep_row<BITS, GS>(x, T, H, x16, gw, gs_, gb, z, ((int64_t)blockIdx.x - nb) * 4 + sub, threadIdx.x & 255,
-                     red + 4 * sub);
+  prep_row<BITS, GS>(x, T, H, x16, xexp, gw, gs_, gb, z, ((int64_t)blockIdx.x - nb) * 4 + sub, threadIdx.x & 255,
+                     red + 8 * sub);
 }
 
-template <int BITS, int GS, bool GLU, bool OUT16, int MI>
+template <int BITS, int GS, bool GLU, int MI>
 static hipError_t launch_mma_t(const TileArgs& a, hipStream_t st) {
   constexpr int NF = GLU ? TM_C / 2 : TM_C;
   const int64_t NB = (a.N + NF - 1) / NF;
   const int64_t nblk = a.grid_tiles * NB;
   if (nblk <= 0) return hipSuccess;
   if (nblk >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((tile_mma_kernel<BITS, GS, GLU, OUT16, MI>), dim3((unsigned)nblk), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((tile_mma_kernel<BITS, GS, GLU, MI>), dim3((unsigned)nblk), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 template <int BITS, int GS, int MI>
-static hipError_t launch_mma_m(const TileArgs& a, bool glu, bool out16, hipStream_t st) {
-  if (glu) return out16 ? launch_mma_t<BITS, GS, true, true, MI>(a, st) : launch_mma_t<BITS, GS, true, false, MI>(a, st);
-  return launch_mma_t<BITS, GS, false, false, MI>(a, st);
+static hipError_t launch_mma_m(const TileArgs& a, bool glu, hipStream_t st) {
+  return glu ? launch_mma_t<BITS, GS, true, MI>(a, st) : launch_mma_t<BITS, GS, false, MI>(a, st);
 }
 
-template <int BITS, int GS, bool GLU, bool OUT16>
+template <int BITS, int GS, bool GLU>
 static hipError_t launch_dual_t(const TileArgs& a, hipStream_t st) {
   constexpr int NF = GLU ? TM_C / 2 : TM_C;
   const int64_t NB = (a.N + NF - 1) / NF;
   const int64_t nblk = (a.grid_tiles + a.grid_tiles2) * NB;
   if (nblk <= 0) return hipSuccess;
   if (nblk >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((tile_mma_dual_kernel<BITS, GS, GLU, OUT16>), dim3((unsigned)nblk), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((tile_mma_dual_kernel<BITS, GS, GLU>), dim3((unsigned)nblk), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_tiles_mma_dual(const TileArgs& a, int bits, int gs, bool glu, bool out16, hipStream_t st) {
-#define MOEGQ_TD(B, G)                                                                              \
-  if (bits == B && gs == G) {                                                                       \
-    if (glu) return out16 ? launch_dual_t<B, G, true, true>(a, st) : launch_dual_t<B, G, true, false>(a, st); \
-    return launch_dual_t<B, G, false, false>(a, st);                                                \
-  }
+hipError_t launch_tiles_mma_dual(const TileArgs& a, int bits, int gs, bool glu, hipStream_t st) {
+#define MOEGQ_TD(B, G) \
+  if (bits == B && gs == G) return glu ? launch_dual_t<B, G, true>(a, st) : launch_dual_t<B, G, false>(a, st);
   MOEGQ_TD(4, 32) MOEGQ_TD(4, 64) MOEGQ_TD(4, 128) MOEGQ_TD(8, 32) MOEGQ_TD(8, 64) MOEGQ_TD(8, 128)
 #undef MOEGQ_TD
   return hipErrorInvalidValue;
@@ -524,9 +613,9 @@ hipError_t launch_tiles_mma_dual(const TileArgs& a, int bits, int gs, bool glu, 
 
 // bf16 expert matrices (gather_mm): 64-row tiles (rows 64), 32-row tiles, or both tables (rows 0)
 hipError_t launch_tiles_mma_w16(const TileArgs& a, bool glu, int rows, hipStream_t st) {
-  if (rows == 64) return glu ? launch_mma_t<16, 64, true, false, 4>(a, st) : launch_mma_t<16, 64, false, false, 4>(a, st);
-  if (rows == 32) return glu ? launch_mma_t<16, 64, true, false, 2>(a, st) : launch_mma_t<16, 64, false, false, 2>(a, st);
-  if (rows == 0) return glu ? launch_dual_t<16, 64, true, false>(a, st) : launch_dual_t<16, 64, false, false>(a, st);
+  if (rows == 64) return glu ? launch_mma_t<16, 64, true, 4>(a, st) : launch_mma_t<16, 64, false, 4>(a, st);
+  if (rows == 32) return glu ? launch_mma_t<16, 64, true, 2>(a, st) : launch_mma_t<16, 64, false, 2>(a, st);
+  if (rows == 0) return glu ? launch_dual_t<16, 64, true>(a, st) : launch_dual_t<16, 64, false>(a, st);
   return hipErrorInvalidValue;
 }
 
@@ -535,27 +624,26 @@ bool tiles_mma_supported(int64_t K, int64_t N, int64_t src_rows, int gs) {
          N * K < ((int64_t)1 << 31);
 }
 
-hipError_t launch_tiles_mma(const TileArgs& a, int bits, int gs, bool glu, bool out16, int rows,
-                            hipStream_t st) {
-#define MOEGQ_TM(B, G)                                                                              \
-  if (bits == B && gs == G) {                                                                       \
-    if (rows == 128) return launch_mma_m<B, G, 8>(a, glu, out16, st);                               \
-    if (rows == 32) return launch_mma_m<B, G, 2>(a, glu, out16, st);                                \
-    return hipErrorInvalidValue;                                                                    \
+hipError_t launch_tiles_mma(const TileArgs& a, int bits, int gs, bool glu, int rows, hipStream_t st) {
+#define MOEGQ_TM(B, G)                                              \
+  if (bits == B && gs == G) {                                       \
+    if (rows == 128) return launch_mma_m<B, G, 8>(a, glu, st);      \
+    if (rows == 32) return launch_mma_m<B, G, 2>(a, glu, st);       \
+    return hipErrorInvalidValue;                                    \
   }
   MOEGQ_TM(4, 32) MOEGQ_TM(4, 64) MOEGQ_TM(4, 128) MOEGQ_TM(8, 32) MOEGQ_TM(8, 64) MOEGQ_TM(8, 128)
 #undef MOEGQ_TM
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prep(const uint16_t* x, int64_t T, int H, int bits, int gs, uint16_t* x16, const uint32_t* gw,
-                       const uint16_t* gsc, const uint16_t* gbi, uint16_t* z, hipStream_t st) {
+hipError_t launch_prep(const uint16_t* x, int64_t T, int H, int bits, int gs, uint16_t* x16, int32_t* xexp,
+                       const uint32_t* gw, const uint16_t* gsc, const uint16_t* gbi, uint16_t* z, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if (T >= ((int64_t)1 << 31) || H % 8 != 0) return hipErrorInvalidValue;
-#define MOEGQ_PREP(B, G)                                                                                     \
-  if (bits == B && gs == G) {                                                                                \
-    hipLaunchKernelGGL((prep_kernel<B, G>), dim3((unsigned)T), dim3(256), 0, st, x, T, H, x16, gw, gsc, gbi, z); \
-    return hipGetLastError();                                                                                \
+#define MOEGQ_PREP(B, G)                                                                                           \
+  if (bits == B && gs == G) {                                                                                      \
+    hipLaunchKernelGGL((prep_kernel<B, G>), dim3((unsigned)T), dim3(256), 0, st, x, T, H, x16, xexp, gw, gsc, gbi, z); \
+    return hipGetLastError();                                                                                      \
   }
   MOEGQ_PREP(4, 32) MOEGQ_PREP(4, 64) MOEGQ_PREP(4, 128) MOEGQ_PREP(8, 32) MOEGQ_PREP(8, 64) MOEGQ_PREP(8, 128)
 #undef MOEGQ_PREP
@@ -563,24 +651,21 @@ hipError_t launch_prep(const uint16_t* x, int64_t T, int H, int bits, int gs, ui
 }
 
 hipError_t launch_front(const SortArgs& sa, const uint16_t* x, int64_t T, int H, int bits, int gs, uint16_t* x16,
-                        const uint32_t* gw, const uint16_t* gsc, const uint16_t* gbi, uint16_t* z, hipStream_t st) {
-  if (T <= 0 || sa.E <= 0 || sa.E > SORT_MAXE || (!sa.block_counts && sa.P > SORT_ONE_MAX_P)) {
-    const hipError_t e = launch_sort(sa, st);
-    if (e != hipSuccess) return e;
-    return launch_prep(x, T, H, bits, gs, x16, gw, gsc, gbi, z, st);
-  }
-  if (H % 8 != 0 || T >= ((int64_t)1 << 30)) return hipErrorInvalidValue;
+                        int32_t* xexp, const uint32_t* gw, const uint16_t* gsc, const uint16_t* gbi, uint16_t* z,
+                        hipStream_t st) {
+  if (T >= ((int64_t)1 << 30) || H % 8 != 0) return hipErrorInvalidValue;
   const bool one = sa.P <= SORT_ONE_MAX_P;
+  if (sa.E <= 0 || sa.E > SORT_MAXE || (!one && !sa.block_counts)) return hipErrorInvalidValue;
   const int64_t nb = one ? 1 : sort_blocks(sa.P);
   const unsigned grid = (unsigned)(nb + (T + 3) / 4);
 #define MOEGQ_FRONT(B, G)                                                                                      \
   if (bits == B && gs == G) {                                                                                  \
     if (one)                                                                                                   \
-      hipLaunchKernelGGL((front_kernel<B, G>), dim3(grid), dim3(SORT_THREADS), 0, st, sa, x, T, H, x16, gw, gsc, \
-                         gbi, z);                                                                              \
+      hipLaunchKernelGGL((front_kernel<B, G>), dim3(grid), dim3(SORT_THREADS), 0, st, sa, x, T, H, x16, xexp,   \
+                         gw, gsc, gbi, z);                                                                     \
     else                                                                                                       \
       hipLaunchKernelGGL((count_prep_kernel<B, G>), dim3(grid), dim3(SORT_THREADS), 0, st, sa, nb, x, T, H, x16, \
-                         gw, gsc, gbi, z);                                                                     \
+                         xexp, gw, gsc, gbi, z);                                                               \
     const hipError_t e = hipGetLastError();                                                                    \
     if (e != hipSuccess || one) return e;                                                                      \
     return launch_sort_rest(sa, st);                                                                           \

@@ -24,7 +24,7 @@ __all__ = [
     "activations_f64", "promoted_type", "round_to",
     "MX_MODES", "MX_BLOCK", "e2m1_to_f64", "e4m3_to_f64", "e8m0_to_f64", "mx_dequant", "mx_matmul", "gather_qmm_mx",
     "unpack", "dequant", "quantized_matmul", "gather_qmm", "broadcast_gather_indices",
-    "silu", "switch_glu", "sort_pairs", "schedule_tiles", "naive_tiles",
+    "silu", "switch_glu", "sort_pairs", "schedule_tiles", "naive_tiles", "hybrid_tiles",
     "combine", "unsort", "shared_expert", "rms_norm", "moe_prefill_layer",
     "dense_forward", "validate_quant_args", "route", "gather_mm", "switch_glu_mm",
 ]
@@ -475,6 +475,49 @@ def naive_tiles(offsets, bm: int):
     return np.array(tiles, dtype=np.int32).reshape(-1, 2), np.array(passes, dtype=np.int32)
 
 
+def hybrid_tiles(offsets, extra_rows: int = 0, big: int = 128, small: int = 32,
+                 slots: int = 512, col_blocks: int = 4):
+    """The two-size expert-aware schedule the whole-layer route runs.
+
+    [MLX#4567] Proposed changes: a tile is (row to start from, expert, valid
+    rows) and never spans two experts.  This library's rule for the tile
+    height (its own design, stated here so that the GPU's tables can be
+    checked entry by entry):
+      * an expert with at least ``small`` rows gets ceil(c / big) tiles of
+        ``big`` rows in the first table; an expert with fewer rows gets
+        ceil(c / small) tiles of ``small`` rows in the second table;
+      * except when the first table would hold so few tiles that, times the
+        ``col_blocks`` column blocks of the first pass, they make at most
+        slots // 8 work items: then every expert takes ``small``-row tiles;
+      * an extra expert (index E, the shared expert) owns the rows
+        [P, P + extra_rows) and is split by the same rule; its tiles follow
+        the routed experts' tiles in each table.
+    Each table lists its tiles expert-major, then by row start.
+    Returns (big_table [n1, 3], small_table [n2, 3]) int32.
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E = len(offsets) - 1
+    P = int(offsets[-1])
+    counts = [int(offsets[e + 1] - offsets[e]) for e in range(E)]
+    firsts = [int(offsets[e]) for e in range(E)]
+    if extra_rows > 0:
+        counts.append(int(extra_rows))
+        firsts.append(P)
+    n_big = sum(-(-c // big) for c in counts if c >= small)
+    threshold = small if n_big * col_blocks > slots // 8 else None   # None: no expert is big
+    big_t, small_t = [], []
+    for e, (c, r0) in enumerate(zip(counts, firsts)):
+        if c == 0:
+            continue
+        if threshold is not None and c >= threshold:
+            table, height = big_t, big
+        else:
+            table, height = small_t, small
+        for j in range(0, c, height):
+            table.append((r0 + j, e, min(height, c - j)))
+    return (np.array(big_t, dtype=np.int32).reshape(-1, 3), np.array(small_t, dtype=np.int32).reshape(-1, 3))
+
+
 # ----------------------------------------------------------------------------
 # Combine tail
 # ----------------------------------------------------------------------------
@@ -602,9 +645,9 @@ def dense_forward(h0, sets, layers: int, norm_w, gs: int = 64, bits: int = 4) ->
 def route(logits, top_k: int):
     """The MoE block's routing from its router logits [T, E] (fp32).
 
-    [MTPLX#558] Change: the fused block computes the routing exactly as the
-    stock block does before the sorted experts and the combine run; the pages
-    do not spell the routing out.
+    [MTPLX#558] Change: the one-kernel block routes tokens the same way as
+    the unfused block it replaces, ahead of the sorted experts and the
+    combine; the page does not define the routing itself.
     READING: the top_k experts with the largest logits (ties to the lower id),
     stored in ascending expert id; the score of a chosen expert is its softmax
     probability over all E logits, evaluated in float64 (max-subtracted), not

@@ -249,6 +249,71 @@ def integer_x(g: np.random.Generator, M: int, K: int, amp: int = 8) -> np.ndarra
     return to_bf16(g.integers(-amp, amp + 1, size=(M, K)).astype(np.float32))
 
 
+# ---- integer-exact SwitchGLU chain: every product and partial sum of gate,
+#      up and down is exact in fp32, and the gate output is a power of two
+#      >= 32 (so silu(g) rounds to g in fp32 and g * u is a bf16 value).
+def group_unit_x(g: np.random.Generator, T: int, K: int, gs: int) -> np.ndarray:
+    """Integer activations whose every group of gs consecutive elements sums
+    to 1: entries uniform on {-1, 0, 1}, the last entry of each group set to
+    make the sum."""
+    x = g.integers(-1, 2, size=(T, K // gs, gs)).astype(np.float32)
+    x[:, :, -1] = 1.0 - x[:, :, :-1].sum(axis=-1)
+    return to_bf16(x.reshape(T, K))
+
+
+def pow2_gate(g: np.random.Generator, N: int, K: int, gs: int, bits: int, targets=(32, 64)):
+    """A gate matrix with random codes, zero scales and integer biases whose
+    sum along each row is a value drawn from ``targets`` (powers of two)."""
+    G = K // gs
+    codes = g.integers(0, 1 << bits, size=(N, K), dtype=np.uint32)
+    s = to_bf16(np.zeros((N, G), np.float32))
+    b = g.integers(-4, 5, size=(N, G)).astype(np.float32)
+    b[:, -1] = np.asarray(targets, np.float32)[g.integers(0, len(targets), size=N)] - b[:, :-1].sum(axis=1)
+    return pack(codes, bits), s, to_bf16(b)
+
+
+def dyadic_matrix(g: np.random.Generator, N: int, K: int, gs: int, bits: int, js=(4, 5), bias_den: int = 5):
+    """Random codes, scales 2^-j (j drawn from js per group) and biases that
+    are small integers times 2^-bias_den."""
+    G = K // gs
+    codes = g.integers(0, 1 << bits, size=(N, K), dtype=np.uint32)
+    s = np.float32(2.0) ** -np.asarray(js, np.float32)[g.integers(0, len(js), size=(N, G))]
+    b = g.integers(-8, 1, size=(N, G)).astype(np.float32) * np.float32(2.0 ** -bias_den)
+    return pack(codes, bits), to_bf16(s), to_bf16(b)
+
+
+def exact_glu_experts(cfg: int, E: int, H: int, I: int, gs: int, bits: int, experts=None):
+    """Per-expert (gate, up, down) with the recipes above; experts outside
+    ``experts`` (when given) get all-zero words and scales."""
+    want = set(range(E)) if experts is None else set(int(e) for e in experts)
+    mats = []
+    for m, (N, K) in enumerate(((I, H), (I, H), (H, I))):
+        ws = np.zeros((E, N, K * bits // 32), np.uint32)
+        ss = np.zeros((E, N, K // gs), np.uint16)
+        bs = np.zeros((E, N, K // gs), np.uint16)
+        for e in sorted(want):
+            gg = rng(cfg, 4, 100 + e, m)
+            if m == 0:
+                w, sc, bi = pow2_gate(gg, N, K, gs, bits)
+            elif m == 1:
+                w, sc, bi = dyadic_matrix(gg, N, K, gs, bits, js=(4, 5) if bits == 4 else (8, 9))
+            else:
+                w, sc, bi = dyadic_matrix(gg, N, K, gs, bits, js=(5, 6) if bits == 4 else (9, 10), bias_den=6)
+            ws[e], ss[e], bs[e] = w, sc, bi
+        mats.append((ws, ss, bs))
+    return tuple(mats)
+
+
+def exact_shared(cfg: int, H: int, I: int, gs: int, bits: int):
+    """Shared expert (gate, up, down, gate_row) with the same recipes; the
+    gate row's biases sum to 64, so its logit on group_unit_x rows is 64."""
+    gate = pow2_gate(rng(cfg, 4, 7, 0), I, H, gs, bits)
+    up = dyadic_matrix(rng(cfg, 4, 7, 1), I, H, gs, bits, js=(4, 5) if bits == 4 else (8, 9))
+    down = dyadic_matrix(rng(cfg, 4, 7, 2), H, I, gs, bits, js=(5, 6) if bits == 4 else (9, 10), bias_den=6)
+    grow = pow2_gate(rng(cfg, 4, 7, 3), 1, H, gs, bits, targets=(64,))
+    return gate, up, down, grow
+
+
 # ----------------------------------------------------------------------------
 # device-side draws for benchmark-sized weights (GBs); same distributions as
 # drawn_words / dense_sets(mode="words"), drawn with a seeded torch generator

@@ -202,3 +202,76 @@ def test_no_cpu_fallback(tmp_path, monkeypatch):
     with pytest.raises(ImportError):
         m.lib()
     importlib.reload(m)
+
+
+def _mat(E, N, K, bits=4, gs=64, wdt=None):
+    import torch
+    lead = (E,) if E else ()
+    return (torch.zeros(lead + (N, K * bits // 32), dtype=wdt or torch.int32),
+            torch.zeros(lead + (N, K // gs), dtype=torch.bfloat16),
+            torch.zeros(lead + (N, K // gs), dtype=torch.bfloat16))
+
+
+def test_binding_rejects_wrong_dtypes_and_shapes():
+    """The layer wrappers check dtypes and shapes before any launch (the C
+    entry points take raw pointers): int64 indices (as torch.topk returns),
+    float32 scores or activations, mismatched index and score shapes, and
+    weights of the wrong size raise ValueError, here on host tensors."""
+    import torch
+    import moe_expert_gathered_amd as m
+    T, H, I, E, k = 4, 256, 128, 8, 2
+    x = torch.zeros((T, H), dtype=torch.bfloat16)
+    idx = torch.zeros((T, k), dtype=torch.int32)
+    sc = torch.zeros((T, k), dtype=torch.bfloat16)
+    ex = (_mat(E, I, H), _mat(E, I, H), _mat(E, H, I))
+
+    def raises(fn, *a, **kw):
+        with pytest.raises(ValueError):
+            fn(*a, **kw)
+
+    for fn in (m.moe_decode, m.moe_prefill):
+        raises(fn, x, idx.long(), sc, *ex)                           # int64 indices
+        raises(fn, x, idx, sc.float(), *ex)                          # fp32 scores
+        raises(fn, x.float(), idx, sc, *ex)                          # fp32 activations
+        raises(fn, x, idx, sc[:, :1], *ex)                           # scores shape
+        raises(fn, x, idx, sc, _mat(E, I, H + 64), *ex[1:])          # gate K mismatch
+        raises(fn, x, idx, sc, ex[0], ex[1], _mat(E, H, I, bits=8))  # down packed for 8 bits, called with 4
+        # the right arguments pass every check and stop only at the device check
+        with pytest.raises(ValueError, match="device tensors"):
+            fn(x, idx, sc, *ex)
+    raises(m.moe_decode, x, idx, sc, *ex, shared=torch.zeros((T, H + 8), dtype=torch.bfloat16))
+    raises(m.switch_glu, x, idx.long(), *ex)
+    raises(m.switch_glu, x, idx, *ex, y=torch.zeros((T * k, H), dtype=torch.float32))
+    y = torch.zeros((T * k, H), dtype=torch.bfloat16)
+    raises(m.moe_combine, y, idx.reshape(-1).long(), sc)             # int64 inverse permutation
+    raises(m.moe_combine, y, None, sc.float())
+    raises(m.moe_combine, y[: T * k - 1], None, sc)                  # too few expert rows
+    raises(m.moe_combine_unfused, y, None, sc, torch.zeros((T, H), dtype=torch.float32))
+    raises(m.moe_combine_gated, y, None, sc, torch.zeros((T, H), dtype=torch.bfloat16),
+           torch.zeros(T + 1, dtype=torch.bfloat16))
+    raises(m.sort_pairs, idx.long(), E)
+    raises(m.affine_qmm, x, *_mat(0, I, H, gs=32))                   # scales for group size 32, called with 64
+    raises(m.affine_qmm, x, *_mat(0, I, H), residual=torch.zeros((T, I), dtype=torch.float32))
+    raises(m.gather_qmm_glu, x, _mat(E, I, H), _mat(E, I, H), torch.zeros(T * k, dtype=torch.int64))
+    raises(m.rms_norm, x, torch.zeros(H + 1, dtype=torch.bfloat16))
+    raises(m.gather_mm, x.float(), torch.zeros((E, I, H), dtype=torch.bfloat16), idx.reshape(-1))
+
+
+def test_prefill_layout_query(L):
+    """The host-side layout query of the whole-layer workspace: pieces in
+    order, 256-byte aligned, inside the workspace size, with the schedule
+    parameters (128/32-row tiles, 4 column blocks at inter 512)."""
+    import moe_expert_gathered_amd as m
+    for T, shared in ((1, True), (2048, True), (4123, False)):
+        lay = m.moe_prefill_layout(T, 8, 256, 2048, 512, shared)
+        o = list(lay["offsets"].values())
+        assert o == sorted(o) and all(v % 256 == 0 for v in o)
+        assert o[-1] + 2 * (8 * T + 2 * T) * 2048 <= m.moe_prefill_workspace_bytes(T, 8, 256, 2048, 512, shared)
+        assert (lay["big"], lay["small"], lay["col_blocks"]) == (128, 32, 4)
+        assert lay["slots"] > 0 and min(lay["caps"]) > 0
+    off = (ctypes.c_int64 * 9)()
+    caps = (ctypes.c_int64 * 2)()
+    par = (ctypes.c_int32 * 4)()
+    assert L.moegq_moe_prefill_layout(4, 8, 2000, 2048, 512, 1, off, caps, par) == -6
+    assert L.moegq_moe_prefill_layout(4, 8, 256, 2048, 512, 1, None, caps, par) == -1
+    assert L.moegq_moe_prefill_layout(-1, 8, 256, 2048, 512, 1, off, caps, par) == -4

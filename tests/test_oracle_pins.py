@@ -475,6 +475,75 @@ def test_schedule_random_invariants():
         assert len(sched) <= P // bm + int((counts > 0).sum())
 
 
+def test_hybrid_tiles_worked_example():
+    """The two-size schedule on loads 200, 31, 0, 32, 5 (offsets 0 200 231 231
+    263 268), 128- and 32-row tiles, 4 column blocks, worked by hand."""
+    off = np.array([0, 200, 231, 231, 263, 268])
+    # 8 slots: experts 0 and 3 reach 32 rows -> ceil(200/128) + ceil(32/128) = 3
+    # tiles, x 4 column blocks = 12 items > 8 // 8 = 1, so two tile sizes
+    big, small = oracle.hybrid_tiles(off, 0, 128, 32, 8, 4)
+    assert big.tolist() == [[0, 0, 128], [128, 0, 72], [231, 3, 32]]
+    assert small.tolist() == [[200, 1, 31], [263, 4, 5]]
+    # 512 slots: 12 <= 512 // 8 = 64 items, so every expert takes 32-row tiles
+    big, small = oracle.hybrid_tiles(off, 0, 128, 32, 512, 4)
+    assert big.size == 0
+    assert small.tolist() == [[0, 0, 32], [32, 0, 32], [64, 0, 32], [96, 0, 32], [128, 0, 32], [160, 0, 32],
+                              [192, 0, 8], [200, 1, 31], [231, 3, 32], [263, 4, 5]]
+    # an extra expert (index 5) of 40 rows at rows 268..307 joins each table last
+    big, small = oracle.hybrid_tiles(off, 40, 128, 32, 8, 4)
+    assert big.tolist() == [[0, 0, 128], [128, 0, 72], [231, 3, 32], [268, 5, 40]]
+    assert small.tolist() == [[200, 1, 31], [263, 4, 5]]
+    big, small = oracle.hybrid_tiles(off, 40, 128, 32, 512, 4)
+    assert big.size == 0 and small.tolist()[-2:] == [[268, 5, 32], [300, 5, 8]]
+
+
+def test_hybrid_tiles_reduce_to_one_size():
+    """With every load at 32 rows or more and the fill rule off, the first
+    table is the plain 128-row schedule; with the fill rule on, the second is
+    the plain 32-row schedule."""
+    g = np.random.default_rng(21)
+    for _ in range(20):
+        E = int(g.integers(1, 60))
+        counts = g.integers(32, 700, E)
+        off = np.concatenate([[0], np.cumsum(counts)])
+        big, small = oracle.hybrid_tiles(off, 0, 128, 32, 0, 4)
+        assert small.size == 0 and np.array_equal(big, oracle.schedule_tiles(off, 128))
+        counts = g.integers(0, 700, E) * (g.random(E) < 0.7)
+        off = np.concatenate([[0], np.cumsum(counts)])
+        big, small = oracle.hybrid_tiles(off, 0, 128, 32, 1 << 40, 4)
+        assert big.size == 0 and np.array_equal(small, oracle.schedule_tiles(off, 32))
+
+
+def test_hybrid_tiles_random_invariants():
+    """Random loads, both sides of the fill rule, with and without extra rows:
+    every row of [0, P + extra) lies in exactly one tile; a tile stays inside
+    its expert's rows and within its table's height; each table is
+    expert-major with ascending row starts; with two sizes an expert's tiles
+    sit in the first table exactly when it has at least 32 rows."""
+    g = np.random.default_rng(22)
+    for trial in range(60):
+        E = int(g.integers(1, 300))
+        counts = g.integers(0, 400, E) * (g.random(E) < 0.5)
+        off = np.concatenate([[0], np.cumsum(counts)])
+        P = int(off[-1])
+        extra = int(g.integers(0, 300)) if trial % 2 else 0
+        slots = int(g.choice([0, 512, 1 << 20]))
+        big, small = oracle.hybrid_tiles(off, extra, 128, 32, slots, int(g.integers(1, 17)))
+        ends = np.concatenate([off, [P + extra]])
+        seen = np.zeros(P + extra, np.int64)
+        for table, height in ((big, 128), (small, 32)):
+            for r0, e, v in table:
+                assert 0 < v <= height and ends[e] <= r0 and r0 + v <= ends[e + 1]
+                seen[r0:r0 + v] += 1
+            keys = [(int(e), int(r0)) for r0, e, _ in table]
+            assert keys == sorted(keys)
+        assert (seen == 1).all()
+        if len(big):
+            loads = np.concatenate([counts, [extra]])
+            in_big = set(big[:, 1].tolist())
+            assert in_big == {e for e in range(len(loads)) if loads[e] >= 32}
+
+
 # ----------------------------------------------------------------------------- combine
 def _torch_combine(y_sorted, inv, scores, shared):
     """Library route: torch bf16 arithmetic on the CPU (each op computes in fp32

@@ -316,6 +316,28 @@ int moegq_moe_decode(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_decode_static: moegq_moe_decode for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, kernels and results, without the
+ * workspace; the gate/up intermediate [T * top_k, I] bf16 lives in a static
+ * device array of the library, one per GPU, of moegq_static_scratch_bytes()
+ * bytes (8 MiB: T * top_k * I <= 4 Mi, e.g. 256 tokens at top-8 and inter
+ * 2048), held until the process ends.  Larger sizes return
+ * MOEGQ_ERR_WORKSPACE with nothing launched; no memory is allocated or freed.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (several streams or host threads) race and must be serialized by the
+ * caller.  The array keeps the last call's contents; nothing in it needs to
+ * start at zero (each call writes the intermediate before reading it).
+ */
+int moegq_moe_decode_static(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
+                            const int32_t* idx, int64_t top_k, const void* scores, const void* shared,
+                            const void* wg, const void* sg, const void* bg,
+                            const void* wu, const void* su, const void* bu,
+                            const void* wd, const void* sd, const void* bd,
+                            int group_size, int bits, void* out, void* y, void* stream);
+size_t moegq_static_scratch_bytes(void);
+
+/*
  * moe_combine (fused, one pass): MTPLX PR 558 Summary/Motivation -- unsort,
  * multiply by the routing scores, sum over top_k and add the gated shared
  * expert in one pass, with the rounding of the unfused tail:

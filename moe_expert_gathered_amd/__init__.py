@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "quantized_matmul", "gather_qmm_workspace_bytes",
            "gather_qmm_mx", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
-           "switch_glu", "switch_glu_mode", "moe_decode", "moe_prefill", "moe_prefill_workspace_bytes",
+           "switch_glu", "switch_glu_mode", "moe_decode", "moe_decode_static", "static_scratch_bytes", "moe_prefill", "moe_prefill_workspace_bytes",
            "moe_prefill_layout", "moe_prefill_tables", "moe_combine", "moe_combine_gated", "moe_combine_unfused", "sort_pairs",
            "schedule_tiles", "rms_norm", "sigmoid_gate", "route", "gather_mm", "kv_feed", "kv_feed_stacked",
            "selfcheck", "selfcheck_state", "probe_stream_read", "probe_mfma_bf16",
@@ -70,6 +70,9 @@ _SIGS = {
     "moegq_switch_glu_mode": ([_i64, _i64, _i64], _int),
     "moegq_moe_decode": ([_p, _i64, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _int,
                           _int, _p, _p, _p, _sz, _p], _int),
+    "moegq_moe_decode_static": ([_p, _i64, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                 _int, _int, _p, _p, _p], _int),
+    "moegq_static_scratch_bytes": ([], _sz),
     "moegq_moe_prefill": ([_p, _i64, _i64, _i64, _i64, _p, _i64, _p] + [_p] * 21 + [_int, _int, _p, _p, _sz, _p],
                           _int),
     "moegq_moe_prefill_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64, _int], _sz),
@@ -479,6 +482,34 @@ def moe_decode(x, idx, scores, gate, up, down, shared=None, group_size=64, bits=
                                 group_size, bits, _ptr(out), _ptr(y), _ptr(ws), wsb, _stream())
     _check(st, "moe_decode")
     return out
+
+
+def moe_decode_static(x, idx, scores, gate, up, down, shared=None, group_size=64, bits=4, out=None, y=None):
+    """moe_decode without a workspace: the intermediate lives in the library's
+    static per-GPU scratch (moegq_static_scratch_bytes() bytes); calls that
+    overlap on one GPU race.  Returns out [T, H]."""
+    T, H = x.shape
+    top_k = idx.shape[1]
+    E, I = gate[0].shape[0], gate[0].shape[1]
+    _req(x, "x", _BF)
+    _req(idx, "idx", _IDX, (T, top_k))
+    _req(scores, "scores", _BF, (T, top_k))
+    _req(shared, "shared", _BF, (T, H))
+    _req(y, "y", _BF, (T * top_k, H))
+    _req(out, "out", _BF, (T, H))
+    _req_experts(gate, up, down, E, H, I, bits, group_size)
+    _dev(x, idx, scores, shared, *gate, *up, *down, y, out)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    st = lib().moegq_moe_decode_static(_ptr(x), T, H, I, E, _ptr(idx), top_k, _ptr(scores), _ptr(shared),
+                                       *[_ptr(t) for t in gate], *[_ptr(t) for t in up], *[_ptr(t) for t in down],
+                                       group_size, bits, _ptr(out), _ptr(y), _stream())
+    _check(st, "moe_decode_static")
+    return out
+
+
+def static_scratch_bytes() -> int:
+    return int(lib().moegq_static_scratch_bytes())
 
 
 def moe_prefill_workspace_bytes(T: int, top_k: int, E: int, H: int, I: int, has_shared: bool = True) -> int:

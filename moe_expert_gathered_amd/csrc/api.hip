@@ -768,11 +768,13 @@ int moegq_moe_prefill(const void* x, int64_t T, int64_t H, int64_t I, int64_t E,
                                   shared ? ws.z : nullptr, T, (int)top_k, H, (uint16_t*)out, s));
 }
 
-int moegq_moe_decode(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, const int32_t* idx,
-                     int64_t top_k, const void* scores, const void* shared, const void* wg, const void* sg,
-                     const void* bg, const void* wu, const void* su, const void* bu, const void* wd,
-                     const void* sd, const void* bd, int group_size, int bits, void* out, void* y,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+// The decode layer given the intermediate h [T * top_k, I] bf16 (workspace of
+// the caller or the static scratch below): argument checks, then the two launches.
+static int decode_layer(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, const int32_t* idx,
+                        int64_t top_k, const void* scores, const void* shared, const void* wg, const void* sg,
+                        const void* bg, const void* wu, const void* su, const void* bu, const void* wd,
+                        const void* sd, const void* bd, int group_size, int bits, void* out, void* y,
+                        uint16_t* h, size_t h_bytes, hipStream_t s) {
   int st;
   if ((st = check_quant(H, group_size, bits))) return st;
   if ((st = check_quant(I, group_size, bits))) return st;
@@ -786,10 +788,9 @@ int moegq_moe_decode(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
       (y && !aligned16(y)) || (shared && !aligned16(shared)))
     return MOEGQ_ERR_ALIGN;
   const int64_t P = T * top_k;
-  const size_t need = moegq_workspace_bytes(MOEGQ_OP_MOE_DECODE, P, E, I, 0) ;
-  if (!workspace || workspace_bytes < need) return MOEGQ_ERR_WORKSPACE;
-  hipStream_t s = S(stream);
-  uint16_t* h = (uint16_t*)workspace;
+  const size_t need = moegq_workspace_bytes(MOEGQ_OP_MOE_DECODE, P, E, I, 0);
+  if (!h || h_bytes < need) return MOEGQ_ERR_WORKSPACE;
+  if (top_k > 8 && !y) return MOEGQ_ERR_NULL_ARG;
   QmvArgs a{};
   a.x = (const uint16_t*)x; a.lhs = nullptr; a.lhs_div = top_k; a.rhs = idx;
   a.w0 = (const uint32_t*)wg; a.s0 = (const uint16_t*)sg; a.b0 = (const uint16_t*)bg;
@@ -804,12 +805,73 @@ int moegq_moe_decode(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, 
     return status_of(launch_qmv_combine(d, bits, group_size, (const uint16_t*)scores, (const uint16_t*)shared, T,
                                         (int)top_k, (uint16_t*)out, s));
   // wider top_k: separate down projection and combine, through the caller's y
-  if (!y) return MOEGQ_ERR_NULL_ARG;
   uint16_t* yw = (uint16_t*)y;
   d.out = yw;
   if (launch_qmv(d, bits, group_size, false, P, s) != hipSuccess) return MOEGQ_ERR_LAUNCH;
   return status_of(launch_combine(yw, nullptr, (const uint16_t*)scores, (const uint16_t*)shared, nullptr, T,
                                   (int)top_k, H, (uint16_t*)out, s));
+}
+
+int moegq_moe_decode(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, const int32_t* idx,
+                     int64_t top_k, const void* scores, const void* shared, const void* wg, const void* sg,
+                     const void* bg, const void* wu, const void* su, const void* bu, const void* wd,
+                     const void* sd, const void* bd, int group_size, int bits, void* out, void* y,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_layer(x, T, H, I, E, idx, top_k, scores, shared, wg, sg, bg, wu, su, bu, wd, sd, bd, group_size,
+                      bits, out, y, (uint16_t*)workspace, workspace ? workspace_bytes : 0, S(stream));
+}
+
+}  // extern "C"
+
+namespace {
+// Scratch of the allocation-free decode entry point: the gate/up intermediate
+// h [T * top_k, I] bf16 lives in this file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is a stand-in, not a device address): the
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current.
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+std::atomic<void*> g_scratch_ptr[64];
+
+void* static_scratch(int* err) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    *err = MOEGQ_ERR_LAUNCH;
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  // several host threads may race here: each gets the same address
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+    *err = MOEGQ_ERR_LAUNCH;
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+}  // namespace
+
+extern "C" {
+
+size_t moegq_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+int moegq_moe_decode_static(const void* x, int64_t T, int64_t H, int64_t I, int64_t E, const int32_t* idx,
+                            int64_t top_k, const void* scores, const void* shared, const void* wg, const void* sg,
+                            const void* bg, const void* wu, const void* su, const void* bu, const void* wd,
+                            const void* sd, const void* bd, int group_size, int bits, void* out, void* y,
+                            void* stream) {
+  // sizes beyond the scratch are refused before the device is touched
+  if (T > 0 && top_k > 0 && I > 0 && T <= kMaxDim && top_k <= 64 && I <= kMaxDim &&
+      moegq_workspace_bytes(MOEGQ_OP_MOE_DECODE, T * top_k, E, I, 0) > kStaticScratchBytes)
+    return MOEGQ_ERR_WORKSPACE;
+  if (T == 0) return decode_layer(x, T, H, I, E, idx, top_k, scores, shared, wg, sg, bg, wu, su, bu, wd, sd, bd,
+                                  group_size, bits, out, y, nullptr, 0, S(stream));
+  int err = MOEGQ_OK;
+  void* h = static_scratch(&err);
+  if (!h) return err;
+  return decode_layer(x, T, H, I, E, idx, top_k, scores, shared, wg, sg, bg, wu, su, bu, wd, sd, bd, group_size,
+                      bits, out, y, (uint16_t*)h, kStaticScratchBytes, S(stream));
 }
 
 int moegq_moe_combine(const void* y, const int32_t* inv, const void* scores, const void* shared, int64_t T,

@@ -3,16 +3,22 @@
 Headline (``value``): MoE decode at hidden 4096, inter 2048, 288 experts,
 top-8, 4-bit weights with group size 64, one token: effective weight GB/s
 (tokens * top_k * bytes per expert / time, duplicates counted) over a chain of
-42 distinct index sets cycled step after step, so the experts come from HBM.
-A step is one MoE decode layer: gate/up gather + SiLU (one kernel), down
-gather, and the combine over top_k.
+42 layers with distinct index sets, so the experts come from HBM.  One layer
+is gate/up gather + SiLU (one kernel), then the down gather fused with the
+combine over top_k.  A step is one pass over the 42-layer chain, captured as
+one HIP graph; --steps sets how many replays are timed (each between its own
+HIP events; the median is reported with the min and max), --warmup how many
+untimed replays come first.
 
 Further legs reported in the same JSON line (not ``value``): the same decode
-at 4 tokens and isolated (one index set, L2/MALL-resident), the MoE-layer
-prefill at 2048 rows (hidden 2048, 256 experts, inter 512, gated shared
-expert, combine), the expert-aware vs naive tile schedules on the large
-prefill (hidden 4096, 288 experts, inter 2048) and the dense few-row chain
-(36 decoder layers, 8 weight sets).
+at 4 tokens, isolated (one index set, cache-resident) and isolated with cold
+caches; measured ceilings (streaming read, bf16 MFMA loop); the MoE-layer
+prefill at 128-4096 rows (hidden 2048, 256 experts, inter 512, gated shared
+expert, combine); the expert-aware vs naive tile schedules and the whole
+layer on the large prefill (hidden 4096, 288 experts, inter 2048) at
+713-16384 rows; the fused against the unfused combine; unquantized
+gather_mm; the vector-unit route; the dense few-row chain (36 decoder
+layers, 8 weight sets); and the oracle timed on the host (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs a,b,...]
 """
@@ -36,12 +42,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # decode legs: the 42-layer graph is replayed steps // 42 times in the timed
-    # region; 40 replays (about 45 ms) keep the run-to-run spread near 1%,
-    # where 4 replays spread over +-1 us per layer
-    ap.add_argument("--steps", type=int, default=42 * 40)
-    ap.add_argument("--warmup", type=int, default=42)
-    ap.add_argument("--legs", default="decode,prefill,large,combine,gather_mm,vec,dense,cpu")
+    # a step is one replay of the 42-layer decode chain (about 1 ms); each of
+    # the `steps` timed replays sits between its own events (median reported)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", default="decode,ceilings,prefill,large,combine,gather_mm,vec,dense,cpu")
     ap.add_argument("--prefill-rows", default="2048,128,512,4096", help="row counts of the prefill leg")
     ap.add_argument("--large-rows", default="713,4123,8192,16384", help="row counts of the large-prefill leg")
     ap.add_argument("--quiet", action="store_true")
@@ -75,10 +80,26 @@ class Timer:
 
 
 # ----------------------------------------------------------------------------- decode
-def graph_time_us(torch, fn, n, reps=3, check=None):
-    """Capture fn(0..n-1) into one HIP graph, verify replays against an eager
-    run (check() -> tensor), and return the average microseconds per call over
-    `reps` replays, timed with HIP events on the capturing stream."""
+class GraphStats:
+    """Per-call microseconds of a captured graph over its timed replays: each
+    replay is bracketed by its own HIP events on the replaying stream."""
+
+    def __init__(self, per_replay_us, calls):
+        v = np.asarray(per_replay_us, dtype=np.float64) / calls
+        self.replays = len(v)
+        self.median = float(np.median(v))
+        self.mean = float(v.mean())
+        self.min = float(v.min())
+        self.max = float(v.max())
+
+    def as_dict(self, scale=1.0, unit="us"):
+        return {f"median_{unit}": round(self.median * scale, 4), f"min_{unit}": round(self.min * scale, 4),
+                f"max_{unit}": round(self.max * scale, 4), "replays": self.replays}
+
+
+def capture(torch, fn, n, check=None):
+    """Capture fn(0..n-1) into one HIP graph and verify three replays against
+    an eager run (check() -> tensor)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -98,21 +119,44 @@ def graph_time_us(torch, fn, n, reps=3, check=None):
             torch.cuda.synchronize()
             if not torch.equal(check(), ref):
                 raise RuntimeError("graph replay differs from eager execution")
-    g.replay()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
+    return g
+
+
+def time_replays(torch, g, reps, warm=2, between=None):
+    """Event-timed replays of graph g: `warm` untimed replays, then `reps`
+    replays each between two events (between(): optional work enqueued before
+    each timed replay, outside its events).  Returns microseconds per replay."""
+    for _ in range(warm):
         g.replay()
-    e1.record()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * n)
+    for i in range(reps):
+        if between is not None:
+            between()
+        ev[2 * i].record()
+        g.replay()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    return [ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(reps)]
+
+
+def graph_stats(torch, fn, n, reps=10, check=None, warm=2):
+    """Capture fn(0..n-1) as one graph and time `reps` replays; per-call stats."""
+    g = capture(torch, fn, n, check)
+    return GraphStats(time_replays(torch, g, reps, warm), n)
+
+
+def graph_time_us(torch, fn, n, reps=10, check=None):
+    """Median microseconds per call of fn over `reps` replays of a graph of n calls."""
+    return graph_stats(torch, fn, n, reps, check).median
 
 
 def decode_leg(torch, m, synth, M, steps, warmup, n_sets=42, isolated=False, cfg=1):
-    """One MoE decode layer per step: gather gate/up + SiLU, then gather down
-    fused with the combine (scores 1/8, no shared expert)."""
+    """One MoE decode layer: gather gate/up + SiLU, then gather down fused with
+    the combine (scores 1/8, no shared expert).  A step is one pass over the
+    chain of n_sets layers with distinct index sets (MLX issue 4509's chained
+    x42 protocol), captured as one HIP graph; `steps` replays are timed one by
+    one with HIP events (median, min, max)."""
     sh = synth.DECODE
     dev = torch.device("cuda")
     gate, up, down = synth.device_expert_set(dev, cfg, sh.E, sh.H, sh.I, sh.gs, sh.bits)
@@ -127,34 +171,96 @@ def decode_leg(torch, m, synth, M, steps, warmup, n_sets=42, isolated=False, cfg
     def idx_of(i):
         return idx_sets[0 if isolated else i % n_sets]
 
-    def step(i):
+    def layer(i):
         m.moe_decode(x, idx_of(i), scores, gate, up, down, group_size=sh.gs, bits=sh.bits, out=out, workspace=ws)
 
     def k1(i):
         m.gather_qmm_glu(x, gate, up, idx_of(i).view(-1), lhs_div=sh.top_k, group_size=sh.gs, bits=sh.bits, out=h)
 
-    for i in range(warmup):
-        step(i)
+    for i in range(n_sets):
+        layer(i)
     torch.cuda.synchronize()
+    # the page's own protocol: host-timed eager calls, one synchronize at the end
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
+    for i in range(steps * n_sets):
+        layer(i)
     torch.cuda.synchronize()
-    el_eager = time.perf_counter() - t0
-    # headline timing: HIP graph of the whole 42-layer chain, replayed
-    layer_us = graph_time_us(torch, step, n_sets, reps=max(1, steps // n_sets), check=lambda: out)
-    k1_us = graph_time_us(torch, k1, n_sets, reps=max(1, steps // n_sets), check=lambda: h)
+    el_eager = (time.perf_counter() - t0) / (steps * n_sets)
+    chain = GraphStats(time_replays(torch, capture(torch, layer, n_sets, check=lambda: out), steps, warmup),
+                       n_sets)
+    kst = GraphStats(time_replays(torch, capture(torch, k1, n_sets, check=lambda: h), steps, warmup), n_sets)
     bpe = 3 * (sh.I * sh.H * sh.bits // 8 + 2 * sh.I * (sh.H // sh.gs) * 2)
     eff = M * sh.top_k * bpe
     k1_bytes = P * 2 * sh.I * (sh.H * sh.bits // 8 + 2 * (sh.H // sh.gs) * 2) + M * sh.H * 2 + P * sh.I * 2
     res = {
-        "tokens": M, "isolated": isolated, "ms_per_layer": layer_us * 1e-3,
-        "effective_gbs": eff / (layer_us * 1e-6) / 1e9, "timing": "hip graph of the 42-layer chain",
-        "eager_ms_per_layer": el_eager / steps * 1e3, "eager_effective_gbs": eff * steps / el_eager / 1e9,
-        "gate_up_us": k1_us, "down_combine_us_approx": layer_us - k1_us,
-        "gate_up_bytes": k1_bytes, "gate_up_gbs": k1_bytes / (k1_us * 1e-6) / 1e9, "bytes_per_expert": bpe,
+        "tokens": M, "isolated": isolated, "layers_per_step": n_sets,
+        "timing": f"hip graph of the {n_sets}-layer chain, {chain.replays} replays, each between its own events",
+        "ms_per_step": chain.median * n_sets * 1e-3,
+        "us_per_layer": chain.as_dict(),
+        "effective_gbs": eff / (chain.median * 1e-6) / 1e9,
+        "effective_gbs_range": [eff / (chain.max * 1e-6) / 1e9, eff / (chain.min * 1e-6) / 1e9],
+        "eager_us_per_layer": el_eager * 1e6, "eager_effective_gbs": eff / el_eager / 1e9,
+        "gate_up_us": kst.as_dict(), "down_combine_us_approx": chain.median - kst.median,
+        "gate_up_bytes": k1_bytes, "gate_up_gbs": k1_bytes / (kst.median * 1e-6) / 1e9, "bytes_per_expert": bpe,
+        "_layer_us": chain.median, "_k1_us": kst.median,
     }
     del gate, up, down
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_cold_leg(torch, m, synth, reps=20, M=1, cfg=1, flush_bytes=1 << 30):
+    """One isolated decode layer with cold caches: before each timed layer a
+    streaming read of a 1 GiB buffer (four times the 256 MB memory-side cache)
+    evicts its weights; the layer (one HIP graph) is timed between its own
+    events, the flush outside them."""
+    sh = synth.DECODE
+    dev = torch.device("cuda")
+    gate, up, down = synth.device_expert_set(dev, cfg, sh.E, sh.H, sh.I, sh.gs, sh.bits)
+    idx = torch.from_numpy(synth.sorted_topk(cfg, M, sh.E, sh.top_k, sub=0)).to(dev)
+    x = torch.from_numpy(synth.activations(cfg, M, sh.H).view(np.int16)).view(torch.bfloat16).to(dev)
+    scores = torch.full((M, sh.top_k), 0.125, dtype=torch.bfloat16, device=dev)
+    P = M * sh.top_k
+    out = torch.empty((M, sh.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(m.workspace_bytes(m.OP_MOE_DECODE, P, sh.E, sh.I), dtype=torch.uint8, device=dev)
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    layer = lambda i=0: m.moe_decode(x, idx, scores, gate, up, down, group_size=sh.gs, bits=sh.bits, out=out,
+                                     workspace=ws)
+    g = capture(torch, layer, 1, check=lambda: out)
+    us = time_replays(torch, g, reps, warm=1, between=lambda: m.probe_stream_read(flush, 2048, sink))
+    st = GraphStats(us, 1)
+    bpe = 3 * (sh.I * sh.H * sh.bits // 8 + 2 * sh.I * (sh.H // sh.gs) * 2)
+    eff = M * sh.top_k * bpe
+    del gate, up, down, flush
+    torch.cuda.empty_cache()
+    return {"tokens": M, "us_per_layer": st.as_dict(), "effective_gbs": eff / (st.median * 1e-6) / 1e9,
+            "timing": "one layer per replay after a 1 GiB streaming read outside the events"}
+
+
+def ceilings_leg(torch, m, reps=10):
+    """Measured ceilings: a plain streaming read of 2 GiB (128-bit loads, 8
+    workgroups of 256 threads per compute unit) and a plain bf16 MFMA loop
+    (8 independent v_mfma_f32_16x16x32_bf16 chains per wave, 2 workgroups of
+    4 waves per compute unit)."""
+    dev = torch.device("cuda")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {"compute_units": cus}
+    for per_cu in (4, 8, 16):
+        st = graph_stats(torch, lambda i: m.probe_stream_read(buf, per_cu * cus, sink), 1, reps=reps)
+        res[f"stream_read_{per_cu}wg_per_cu"] = {"us": st.as_dict(), "tb_s": nbytes / (st.median * 1e-6) / 1e12}
+    del buf
+    out = torch.zeros(1, dtype=torch.float32, device=dev)
+    iters = 4096
+    for per_cu in (1, 2):
+        flops = m.probe_mfma_bf16(iters, per_cu * cus, out)
+        st = graph_stats(torch, lambda i: m.probe_mfma_bf16(iters, per_cu * cus, out), 1, reps=reps)
+        res[f"mfma_bf16_{per_cu}wg_per_cu"] = {"us": st.as_dict(), "tflops": flops / (st.median * 1e-6) / 1e12,
+                                              "frac_of_2500": flops / (st.median * 1e-6) / 2.5e15}
     torch.cuda.empty_cache()
     return res
 
@@ -209,23 +315,25 @@ def prefill_leg(torch, m, synth, rows=(2048, 128, 512, 4096), steps=100, warmup=
             step()
         torch.cuda.synchronize()
         el_eager = (time.perf_counter() - t0) / steps
-        el = graph_time_us(torch, step, 10, reps=max(1, steps // 10), check=lambda: out) * 1e-6
+        lst = graph_stats(torch, step, 10, reps=max(10, steps // 10), check=lambda: out)
+        el = lst.median * 1e-6
         # the router on the GPU (fp32 logits of the same routing), alone and in front of the layer
         logits = torch.from_numpy(synth.zipf_logits(cfg, T, sh.E)).to(dev)
         ridx = torch.empty((T, sh.top_k), dtype=torch.int32, device=dev)
         rsc = torch.empty((T, sh.top_k), dtype=torch.bfloat16, device=dev)
         route = lambda i=0: m.route(logits, sh.top_k, idx=ridx, scores=rsc)
-        route_us = graph_time_us(torch, route, 10, reps=max(1, steps // 10), check=lambda: ridx)
+        route_us = graph_time_us(torch, route, 10, reps=max(10, steps // 10), check=lambda: ridx)
 
         def step_logits(i=0):
             route()
             m.moe_prefill(x, ridx, rsc, gate, up, down, shared=(sg, su, sd, grow), group_size=sh.gs,
                           bits=sh.bits, out=out, workspace=ws)
 
-        el_logits = graph_time_us(torch, step_logits, 10, reps=max(1, steps // 10), check=lambda: out) * 1e-6
+        el_logits = graph_time_us(torch, step_logits, 10, reps=max(10, steps // 10), check=lambda: out) * 1e-6
         flops, nbytes = layer_bytes_flops(sh, T, counts, True)
         r = {"rows": T, "active_experts": int((counts > 0).sum()), "max_load": int(counts.max()),
-             "ms_per_layer": el * 1e3, "eager_ms_per_layer": el_eager * 1e3, "timing": "hip graph of 10 layers",
+             "ms_per_layer": el * 1e3, "ms_per_layer_stats": lst.as_dict(1e-3, "ms"),
+             "eager_ms_per_layer": el_eager * 1e3, "timing": "hip graph of 10 layers, replays timed one by one",
              "router_us": route_us, "ms_per_layer_from_logits": el_logits * 1e3,
              "gflop": flops / 1e9, "bytes": nbytes,
              "mfma_util": flops / el / (MFMA_BF16_PEAK_TFLOPS * 1e12),
@@ -250,11 +358,33 @@ def hybrid_tile_count(counts, inter, small_max=32, big=128, slots=512):
     return int(nbig + sum(1 for c in counts if 0 < c < small_max))
 
 
-def large_leg(torch, m, synth, rows=(713, 4123, 8192, 16384), steps=4, warmup=2, cfg=4):
-    """Large MoE prefill (hidden 4096, 288 experts, top-8, inter 2048): the
-    expert-aware schedule against naive BM 16 row tiling at 4123 rows (tile and
-    K-pass counts, switch_glu time), and the whole layer (moe_prefill, no shared
-    expert) at each size, 4-bit GS 64 and, at 4123 rows, 8-bit GS 128."""
+def tile_counts(counts, bm, mode, inter):
+    """(tiles, K passes) of one pass of the sorted route for per-expert loads
+    `counts` (host arithmetic for the report): expert-aware tiles of bm rows,
+    naive fixed bm-row tiles (one K pass per expert present in a tile), or the
+    two-size schedule (bm 0)."""
+    if mode == "naive":
+        offs = np.concatenate([[0], np.cumsum(counts)])
+        P = int(offs[-1])
+        passes = 0
+        for r0 in range(0, P, bm):
+            r1 = min(P, r0 + bm)
+            passes += int(((offs[1:] > r0) & (offs[:-1] < r1) & (counts > 0)).sum())
+        return -(-P // bm), passes
+    if bm == 0:
+        n = hybrid_tile_count(counts, inter)
+        return n, n
+    n = int(sum(-(-int(c) // bm) for c in counts))
+    return n, n
+
+
+def large_leg(torch, m, synth, rows=(713, 4123, 8192, 16384), reps=10, cfg=4):
+    """Large MoE prefill (hidden 4096, 288 experts, top-8, inter 2048): at each
+    size the sorted SwitchGLU under the expert-aware schedule against naive
+    row tiling, both at BM 16 (MLX PR 4567's comparison: tile and K-pass
+    counts, ms), the expert-aware schedule at BM 64 and the two-size schedule
+    the library runs; and the whole layer (moe_prefill, no shared expert),
+    4-bit GS 64 and, at 4123 rows, 8-bit GS 128.  HIP-graph replays."""
     res = {}
     for bits in (4, 8):
         sh = synth.LARGE4 if bits == 4 else synth.LARGE8
@@ -267,49 +397,33 @@ def large_leg(torch, m, synth, rows=(713, 4123, 8192, 16384), steps=4, warmup=2,
             x = torch.from_numpy(synth.activations(cfg, T, sh.H).view(np.int16)).view(torch.bfloat16).to(dev)
             P = T * sh.top_k
             counts = np.bincount(idx_np.reshape(-1), minlength=sh.E)
-            r = {"rows": T, "bits": bits, "active_experts": int((counts > 0).sum())}
-            if bits == 4 and T == 4123:
+            r = {"rows": T, "bits": bits, "active_experts": int((counts > 0).sum()), "max_load": int(counts.max()),
+                 "experts_under_16_rows": int(((counts > 0) & (counts < 16)).sum())}
+            flops = P * 6 * sh.H * sh.I
+            if bits == 4:
                 y = torch.empty((P, sh.H), dtype=torch.bfloat16, device=dev)
                 inv = torch.empty(P, dtype=torch.int32, device=dev)
-                offs = np.concatenate([[0], np.cumsum(counts)])
                 for name, tmode, bm in (("scheduled_bm16", 0, 16), ("naive_bm16", 1, 16), ("scheduled_bm64", 0, 64),
-                                        ("scheduled_hybrid", 0, 0)):
-                    run = lambda: m.switch_glu(x, idx, gate, up, down, group_size=sh.gs, bits=sh.bits,
-                                               mode=m.MODE_SORTED, tile_mode=tmode, bm=bm, y=y, inv=inv)
-                    for _ in range(warmup):
-                        run()
-                    torch.cuda.synchronize()
-                    t0 = time.perf_counter()
-                    for _ in range(steps):
-                        run()
-                    torch.cuda.synchronize()
-                    ms = (time.perf_counter() - t0) / steps * 1e3
-                    if tmode == 0 and bm == 0:
-                        tiles = passes = hybrid_tile_count(counts, sh.I)
-                    elif tmode == 0:
-                        tiles = int(sum(-(-int(c) // bm) for c in counts))
-                        passes = tiles
-                    else:
-                        tiles = -(-P // bm)
-                        passes = 0
-                        for r0 in range(0, P, bm):
-                            r1 = min(P, r0 + bm)
-                            passes += int(((offs[1:] > r0) & (offs[:-1] < r1) & (counts > 0)).sum())
-                    flops = P * 6 * sh.H * sh.I
-                    r[name] = {"ms": ms, "tiles": tiles, "k_passes": passes,
-                               "mfma_util": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)}
+                                        ("two_size", 0, 0)):
+                    run = lambda i=0: m.switch_glu(x, idx, gate, up, down, group_size=sh.gs, bits=sh.bits,
+                                                   mode=m.MODE_SORTED, tile_mode=tmode, bm=bm, y=y, inv=inv)
+                    st = graph_stats(torch, run, 1, reps=reps if T <= 4123 else max(3, reps // 3), check=lambda: y)
+                    tiles, passes = tile_counts(counts, bm, "naive" if tmode else "scheduled", sh.I)
+                    r[name] = {"ms": st.median * 1e-3, "ms_stats": st.as_dict(1e-3, "ms"), "tiles": tiles,
+                               "k_passes": passes,
+                               "mfma_util": flops / (st.median * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12)}
                 del y, inv
             out = torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev)
             ws = torch.empty(m.moe_prefill_workspace_bytes(T, sh.top_k, sh.E, sh.H, sh.I, False),
                              dtype=torch.uint8, device=dev)
             layer = lambda i=0: m.moe_prefill(x, idx, scores, gate, up, down, shared=None, group_size=sh.gs,
                                               bits=sh.bits, out=out, workspace=ws)
-            for _ in range(warmup):
-                layer()
-            el = graph_time_us(torch, layer, 3, reps=max(1, steps // 2), check=lambda: out) * 1e-6
-            flops, nbytes = layer_bytes_flops(sh, T, counts, False)
-            r["layer"] = {"ms": el * 1e3, "timing": "hip graph of 3 layers", "gflop": flops / 1e9, "bytes": nbytes,
-                          "mfma_util": flops / el / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+            st = graph_stats(torch, layer, 3, reps=reps, check=lambda: out)
+            el = st.median * 1e-6
+            flops_l, nbytes = layer_bytes_flops(sh, T, counts, False)
+            r["layer"] = {"ms": el * 1e3, "ms_stats": st.as_dict(1e-3, "ms"), "timing": "hip graph of 3 layers",
+                          "gflop": flops_l / 1e9, "bytes": nbytes,
+                          "mfma_util": flops_l / el / (MFMA_BF16_PEAK_TFLOPS * 1e12),
                           "hbm_frac": nbytes / el / (HBM_PEAK_GBS * 1e9)}
             res[f"rows{T}_bits{bits}"] = r
             del ws, out
@@ -339,7 +453,7 @@ def gather_mm_leg(torch, m, synth, steps=20):
     P = T * top_k
     out = torch.empty((P, N), dtype=torch.bfloat16, device=dev)
     fn = lambda i=0: m.gather_mm(x, w, srhs, lhs_indices=lhs, sorted_indices=True, out=out)
-    us = graph_time_us(torch, fn, 10, reps=max(1, steps // 10), check=lambda: out)
+    us = graph_time_us(torch, fn, 10, reps=10, check=lambda: out)
     active = int(np.unique(flat).size)
     flops = 2.0 * P * N * K
     nbytes = active * N * K * 2 + T * K * 2 + P * N * 2
@@ -354,7 +468,7 @@ def gather_mm_leg(torch, m, synth, steps=20):
     x2 = torch.randn((1, K2), device=dev, generator=g).to(torch.bfloat16)
     out2 = torch.empty((8, N2), dtype=torch.bfloat16, device=dev)
     fn2 = lambda i=0: m.gather_mm(x2, w2, sets[i % 42], lhs_div=8, out=out2)
-    us2 = graph_time_us(torch, fn2, 42, reps=max(1, steps // 10), check=lambda: out2)
+    us2 = graph_time_us(torch, fn2, 42, reps=10, check=lambda: out2)
     b2 = 8 * N2 * K2 * 2
     res["decode_1tok_8pairs_n2048_k4096"] = {"us": us2, "gbs": b2 / us2 / 1e3,
                                              "hbm_frac": b2 / (us2 * 1e-6) / (HBM_PEAK_GBS * 1e9)}
@@ -398,7 +512,7 @@ def vec_leg(torch, m, synth, steps=42, cfg=1):
         fn = lambda i, x=x, w=w, s=s, b=b, tr=tr, out=out, ws=ws, bits=bits: m.gather_qmm(
             x, w, s, b, rhs_indices=sets[i % 42], transpose=tr, group_size=sh.gs, bits=bits, out=out,
             workspace=ws)
-        us = graph_time_us(torch, fn, 42, reps=max(1, steps // 42), check=lambda out=out: out)
+        us = graph_time_us(torch, fn, 42, reps=10, check=lambda out=out: out)
         nbytes = P * per_pair + H * x.element_size() + P * N * out.element_size()
         plan_ks = need // (P * N * 4)
         res[name] = {"us": us, "gbs": nbytes / us / 1e3, "hbm_frac": nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
@@ -419,7 +533,7 @@ def vec_leg(torch, m, synth, steps=42, cfg=1):
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         fn = lambda i, w=w, sc=sc, out=out, ws=ws, mode=mode: m.gather_qmm_mx(
             x, w, sc, rhs_indices=sets[i % 42], transpose=True, mode=mode, out=out, workspace=ws)
-        us = graph_time_us(torch, fn, 42, reps=max(1, steps // 42), check=lambda out=out: out)
+        us = graph_time_us(torch, fn, 42, reps=10, check=lambda out=out: out)
         nbytes = P * (I * H * bits // 8 + I * (H // 32)) + H * 2 + P * I * 2
         res[f"{mode}_transpose_bf16_1tok_8pairs_n2048_k4096"] = {
             "us": us, "gbs": nbytes / us / 1e3, "hbm_frac": nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
@@ -448,8 +562,8 @@ def combine_leg(torch, m, synth, reps=20, cfg=3):
     ws = torch.empty(m.workspace_bytes(m.OP_COMBINE_UNFUSED, P, 0, H, 0), dtype=torch.uint8, device=dev)
     fused = lambda i: m.moe_combine(y, inv, scores, shared, out=out_f)
     unfused = lambda i: m.moe_combine_unfused(y, inv, scores, shared, out=out_u, workspace=ws)
-    us_f = graph_time_us(torch, fused, 10, reps=max(1, reps // 10), check=lambda: out_f)
-    us_u = graph_time_us(torch, unfused, 10, reps=max(1, reps // 10), check=lambda: out_u)
+    us_f = graph_time_us(torch, fused, 10, reps=max(10, reps // 10), check=lambda: out_f)
+    us_u = graph_time_us(torch, unfused, 10, reps=max(10, reps // 10), check=lambda: out_u)
     torch.cuda.synchronize()
     if not torch.equal(out_f.view(torch.int16), out_u.view(torch.int16)):
         raise RuntimeError("fused combine differs from the unfused tail")
@@ -466,7 +580,7 @@ def combine_leg(torch, m, synth, reps=20, cfg=3):
 
 
 # ----------------------------------------------------------------------------- dense chain
-def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=5, warmup=2, cfg=2):
+def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=10, warmup=2, cfg=2):
     dev = torch.device("cuda")
     d = synth.DENSE
     sets = synth.device_dense_sets(dev, cfg, gs, bits, d)
@@ -510,8 +624,9 @@ def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=5, warmup=2,
         med = float(np.median(ts))
         # the same forward captured once as a HIP graph: kernel time without the
         # per-call host work of ~300 launches from Python
-        g_s = graph_time_us(torch, lambda i: fwd(), 1, reps=reps) * 1e-6
-        res[f"rows{M}"] = {"ms_per_forward": g_s * 1e3, "gbs": per_fwd / g_s / 1e9,
+        fst = graph_stats(torch, lambda i: fwd(), 1, reps=reps)
+        g_s = fst.median * 1e-6
+        res[f"rows{M}"] = {"ms_per_forward": g_s * 1e3, "ms_stats": fst.as_dict(1e-3, "ms"), "gbs": per_fwd / g_s / 1e9,
                            "hbm_frac": per_fwd / g_s / (HBM_PEAK_GBS * 1e9), "timing": "hip graph of one forward",
                            "eager_ms_per_forward": med * 1e3, "eager_gbs": per_fwd / med / 1e9}
     del sets
@@ -593,12 +708,13 @@ def cpu_baseline(torch, synth, n_layers=5, cfg=1):
     bpe = 3 * (sh.I * sh.H * sh.bits // 8 + 2 * sh.I * (sh.H // sh.gs) * 2)
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = 1
+        blas_threads = None
     del gate, up, down
     torch.cuda.empty_cache()
-    return {"value": n_layers * sh.top_k * bpe / tot / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+    return {"value": n_layers * sh.top_k * bpe / tot / 1e9, "unit": "GB/s", "cores": os.cpu_count(),
+            "blas_threads": blas_threads, "kind": "oracle",
             "sample": f"{n_layers} MoE decode layers (1 token, top-8 of 288 experts, hidden 4096, inter 2048, "
                       f"4-bit GS 64), {tot:.1f} s of CPU time", "seconds": tot}
 
@@ -615,13 +731,18 @@ def main():
     m.lib()
     legs = set(a.legs.split(","))
     torch.cuda.set_device(0)
-    log("decode M=1 chained")
+    log(f"decode M=1 chained: {a.steps} timed replays of the 42-layer chain")
     head = decode_leg(torch, m, synth, 1, a.steps, a.warmup)
     extra = {"decode_m1_chained": head}
     if "decode" in legs:
-        log("decode M=1 isolated, M=4 chained")
-        extra["decode_m1_isolated"] = decode_leg(torch, m, synth, 1, a.steps, a.warmup, isolated=True)
-        extra["decode_m4_chained"] = decode_leg(torch, m, synth, 4, a.steps, a.warmup)
+        log("decode M=1 isolated, M=1 isolated cold, M=4 chained")
+        reps = max(a.steps, 10)
+        extra["decode_m1_isolated"] = decode_leg(torch, m, synth, 1, reps, a.warmup, isolated=True)
+        extra["decode_m1_isolated_cold"] = decode_cold_leg(torch, m, synth, reps=max(reps, 20))
+        extra["decode_m4_chained"] = decode_leg(torch, m, synth, 4, reps, a.warmup)
+    if "ceilings" in legs:
+        log("measured ceilings")
+        extra["ceilings"] = ceilings_leg(torch, m)
     if "prefill" in legs:
         rows = tuple(int(v) for v in a.prefill_rows.split(","))
         log(f"prefill rows {rows}")
@@ -649,16 +770,21 @@ def main():
     if "cpu" in legs:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(torch, synth)
-    k1_us = head["gate_up_us"]
+    k1_us = head.pop("_k1_us")
+    head.pop("_layer_us")
+    for leg in ("decode_m1_isolated", "decode_m4_chained"):
+        if leg in extra:
+            extra[leg].pop("_k1_us")
+            extra[leg].pop("_layer_us")
     ach = head["gate_up_bytes"] / (k1_us * 1e-6) / 1e9
     line = {
         "metric": "effective weight GB/s (M=1/4 MoE decode) + MoE-layer ms at 2048-row prefill",
         "value": round(head["effective_gbs"], 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(head["ms_per_layer"], 5), "higher_is_better": True,
+        "warmup": a.warmup, "ms_per_step": round(head["ms_per_step"], 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "moe_decode_h4096_i2048_e288_top8_w4g64_m1_chain42", "hidden": 4096,
                    "inter": 2048, "experts": 288, "top_k": 8, "bits": 4, "group_size": 64, "tokens": 1,
-                   "index_sets": 42},
+                   "index_sets": 42, "step": "one pass over the 42-layer chain (42 MoE decode layers)"},
         "roofline": {"bound": "hbm", "kernel": "qmv_kernel<4,64,glu,2,2> (gathered gate+up, SiLU)", "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": counted_traffic(),
                      "bytes_per_launch": head["gate_up_bytes"], "avg_launch_us": round(k1_us, 3)},

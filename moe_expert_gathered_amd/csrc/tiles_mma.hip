@@ -205,32 +205,7 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
       if (lup) { ws = us; wb = ub; }
     }
   };
-  // fp16 weight columns: the owner lane of column (block lj, c16) finds the
-  // column's exponent from all its groups' scales and biases; ecj[j] is the
-  // exponent of this lane's column in block j (the picks), taken from its owner
   int ecol = 0, ecj[4] = {0, 0, 0, 0};
-  if constexpr (F16) {
-    constexpr float QMAX = (float)((1 << BITS) - 1);
-    const int nwin = G / 8;
-    float mx = 0.f;
-    for (int w0 = 0; w0 < nwin; w0 += 4) {        // four windows' loads in flight at a time
-      uint4 ws[4], wb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) load_win(min(w0 + i, nwin - 1), ws[i], wb[i]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t ds[4] = {ws[i].x, ws[i].y, ws[i].z, ws[i].w}, db[4] = {wb[i].x, wb[i].y, wb[i].z, wb[i].w};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          mx = fmaxf(mx, __builtin_fmaf(fabsf(bf16_lo(ds[d])), QMAX, fabsf(bf16_lo(db[d]))));
-          mx = fmaxf(mx, __builtin_fmaf(fabsf(bf16_hi(ds[d])), QMAX, fabsf(bf16_hi(db[d]))));
-        }
-      }
-    }
-    ecol = f16_exponent(mx);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ecj[j] = __shfl(ecol, 16 * j + c16, 64);
-  }
   // group of (lane group g, step ks) inside its window: e = (8 ks / WSTEPS + 32 g / GS) % 8;
   // the dword holding it is the same for every lane except at GS = 32
   auto sel4 = [](const uint4& v, int d) -> uint32_t {
@@ -357,6 +332,33 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
       if (t < PDA) issue_a(t, t % RA, part);
       if (t < PDB) issue_b(t, t % RB, part);
     }
+  // fp16 weight columns: the owner lane of column (block lj, c16) finds the
+  // column's exponent from all its groups' scales and biases; ecj[j] is the
+  // exponent of this lane's column in block j (the picks), taken from its
+  // owner.  Done after the prologue's loads are issued, so they are in flight
+  // meanwhile.
+  if constexpr (F16) {
+    constexpr float QMAX = (float)((1 << BITS) - 1);
+    const int nwin = G / 8;
+    float mx = 0.f;
+    for (int w0 = 0; w0 < nwin; w0 += 4) {        // four windows' loads in flight at a time
+      uint4 ws[4], wb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_win(min(w0 + i, nwin - 1), ws[i], wb[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t ds[4] = {ws[i].x, ws[i].y, ws[i].z, ws[i].w}, db[4] = {wb[i].x, wb[i].y, wb[i].z, wb[i].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          mx = fmaxf(mx, __builtin_fmaf(fabsf(bf16_lo(ds[d])), QMAX, fabsf(bf16_lo(db[d]))));
+          mx = fmaxf(mx, __builtin_fmaf(fabsf(bf16_hi(ds[d])), QMAX, fabsf(bf16_hi(db[d]))));
+        }
+      }
+    }
+    ecol = f16_exponent(mx);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ecj[j] = __shfl(ecol, 16 * j + c16, 64);
+  }
   using std::integral_constant;
   for (int ks = 0; ks < nK; ks += U) {
     step(ks, integral_constant<int, 0>{});

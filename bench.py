@@ -592,11 +592,16 @@ def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=10, warmup=2
         del L["q"], L["k"], L["v"]
     torch.cuda.empty_cache()
     nw = torch.ones(d["hidden"], dtype=torch.bfloat16, device=dev)
+    hid, nqkv, qo, inter = d["hidden"], nq + 2 * nk, d["q_out"], d["inter"]
     per_fwd = 0
     for name, (N, K) in synth.dense_dims(d).items():
         per_fwd += N * (K * bits // 8 + 2 * (K // gs) * 2)
     per_fwd *= d["layers"]
     res = {"bits": bits, "group_size": gs, "forward_weight_bytes": per_fwd}
+    # one zero-filled K-split workspace per product shape (its layout follows N, K)
+    ws = {k: m.affine_qmm_workspace(max(rows), n_, k_, glu, device=dev)
+          for k, (n_, k_, glu) in {"qkv": (nqkv, hid, False), "o": (hid, qo, False),
+                                   "gu": (inter, hid, True), "dn": (hid, inter, False)}.items()}
     for M in rows:
         h0 = torch.randn((M, d["hidden"]), device=dev).to(torch.bfloat16)
 
@@ -605,11 +610,12 @@ def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=10, warmup=2
             for li in range(d["layers"]):
                 L = sets[li % d["sets"]]
                 x = m.rms_norm(h, nw)
-                qkv = m.affine_qmm(x, *L["qkv"], group_size=gs, bits=bits)
-                h = m.affine_qmm(m.kv_feed_stacked(qkv, nq, nk, nk), *L["o"], group_size=gs, bits=bits, residual=h)
+                qkv = m.affine_qmm(x, *L["qkv"], group_size=gs, bits=bits, workspace=ws["qkv"])
+                h = m.affine_qmm(m.kv_feed_stacked(qkv, nq, nk, nk), *L["o"], group_size=gs, bits=bits, residual=h,
+                                 workspace=ws["o"])
                 x = m.rms_norm(h, nw)
-                a = m.affine_qmm_glu(x, L["g"], L["u"], group_size=gs, bits=bits)
-                h = m.affine_qmm(a, *L["dn"], group_size=gs, bits=bits, residual=h)
+                a = m.affine_qmm_glu(x, L["g"], L["u"], group_size=gs, bits=bits, workspace=ws["gu"])
+                h = m.affine_qmm(a, *L["dn"], group_size=gs, bits=bits, residual=h, workspace=ws["dn"])
             return h
 
         for _ in range(warmup):

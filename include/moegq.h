@@ -185,6 +185,29 @@ int moegq_affine_qmm(const void* x, int x_dtype, int64_t M, int64_t K,
                      const void* w, int w_dtype, const void* scales, const void* biases,
                      int64_t N, int transpose, int group_size, int bits,
                      const void* residual, void* out, void* stream);
+/*
+ * affine_qmm_ws / affine_qmm_glu_ws: the same products with a workspace that
+ * lets 2..16-row products with K a multiple of 128 split K over workgroups
+ * (so that products with few output columns still fill the machine):
+ * moegq_affine_qmm_workspace_bytes(M, N, K, glu) bytes, 16-byte aligned,
+ * ZERO-FILLED before its first use; every call leaves it in that state (its
+ * per-column-group counters return to zero, the fp32 partials are scratch).
+ * A NULL or smaller workspace runs the same kernel without the split.  The
+ * split's partial sums are added in split order, so results do not depend on
+ * timing; they can differ from the unsplit call's in the last bits of fp32
+ * (a different summation order), within the format's tolerance.  The layout
+ * (counters, then partials) depends on N, K and glu, not on M: one workspace
+ * serves every call with the same N, K and glu; a call of another shape may
+ * leave nonzero words where this shape keeps its counters, so each product
+ * shape takes a workspace of its own.  Calls that overlap (several streams)
+ * must not share one workspace.
+ */
+int moegq_affine_qmm_ws(const void* x, int x_dtype, int64_t M, int64_t K,
+                        const void* w, int w_dtype, const void* scales, const void* biases,
+                        int64_t N, int transpose, int group_size, int bits,
+                        const void* residual, void* out, void* workspace, size_t workspace_bytes,
+                        void* stream);
+size_t moegq_affine_qmm_workspace_bytes(int64_t M, int64_t N, int64_t K, int glu);
 
 /*
  * affine_qmm_glu: out = bf16( silu(x . Wg^T) * (x . Wu^T) ), the dense SwiGLU
@@ -195,6 +218,11 @@ int moegq_affine_qmm_glu(const void* x, int64_t M, int64_t K,
                          const void* wg, const void* sg, const void* bg,
                          const void* wu, const void* su, const void* bu,
                          int64_t N, int group_size, int bits, void* out, void* stream);
+int moegq_affine_qmm_glu_ws(const void* x, int64_t M, int64_t K,
+                            const void* wg, const void* sg, const void* bg,
+                            const void* wu, const void* su, const void* bu,
+                            int64_t N, int group_size, int bits, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * switch_glu: the routed-expert chain of a MoE layer (MLX issue 4509, moe():

@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = ["MoegqError", "lib", "library_path", "gather_qmm", "quantized_matmul", "gather_qmm_workspace_bytes",
-           "gather_qmm_mx", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu",
+           "gather_qmm_mx", "gather_qmm_glu", "affine_qmm", "affine_qmm_glu", "affine_qmm_workspace",
            "switch_glu", "switch_glu_mode", "moe_decode", "moe_decode_static", "static_scratch_bytes", "moe_prefill", "moe_prefill_workspace_bytes",
            "moe_prefill_layout", "moe_prefill_tables", "moe_combine", "moe_combine_gated", "moe_combine_unfused", "sort_pairs",
            "schedule_tiles", "rms_norm", "sigmoid_gate", "route", "gather_mm", "kv_feed", "kv_feed_stacked",
@@ -65,6 +65,10 @@ _SIGS = {
                               _i64, _int, _int, _int, _p, _p, _sz, _p], _int),
     "moegq_affine_qmm": ([_p, _int, _i64, _i64, _p, _int, _p, _p, _i64, _int, _int, _int, _p, _p, _p], _int),
     "moegq_affine_qmm_glu": ([_p, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _int, _int, _p, _p], _int),
+    "moegq_affine_qmm_ws": ([_p, _int, _i64, _i64, _p, _int, _p, _p, _i64, _int, _int, _int, _p, _p, _p, _sz, _p],
+                            _int),
+    "moegq_affine_qmm_glu_ws": ([_p, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _int, _int, _p, _p, _sz, _p], _int),
+    "moegq_affine_qmm_workspace_bytes": ([_i64, _i64, _i64, _int], _sz),
     "moegq_switch_glu": ([_p, _i64, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _int, _int,
                           _int, _int, _int, _p, _p, _p, _sz, _p], _int),
     "moegq_switch_glu_mode": ([_i64, _i64, _i64], _int),
@@ -391,34 +395,53 @@ def gather_qmm_glu(x, gate, up, rhs_indices, lhs_indices=None, lhs_div=1, group_
     return out
 
 
-def affine_qmm(x, w, scales, biases, group_size=64, bits=4, transpose=True, residual=None, out=None):
-    """out = x . dequant(w)^T (+ residual after rounding).  x [M, K], w [N, Kw]."""
+def affine_qmm_workspace(M: int, N: int, K: int, glu: bool = False, device="cuda"):
+    """A zero-filled workspace for affine_qmm / affine_qmm_glu at these sizes
+    (None when the product takes none): K split over workgroups at 2..16 rows.
+    Its layout depends on (N, K, glu) only: reusable by later calls with the
+    same N, K and glu (any M up to 16) on one stream, not by other shapes."""
+    n = int(lib().moegq_affine_qmm_workspace_bytes(M, N, K, int(bool(glu))))
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def affine_qmm(x, w, scales, biases, group_size=64, bits=4, transpose=True, residual=None, out=None,
+               workspace=None):
+    """out = x . dequant(w)^T (+ residual after rounding).  x [M, K], w [N, Kw].
+    workspace: optional (affine_qmm_workspace): lets 2..16-row products split K."""
     M, K = x.shape
     N = w.shape[0]
     _req(x, "x", _BF)
     _req_matrix((w, scales, biases), "w", N, K, bits, group_size)
     _req(residual, "residual", _BF, (M, N))
     _dev(x, w, scales, biases, residual)
+    _req(workspace, "workspace", (torch.uint8,))
+    _dev(workspace)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    st = lib().moegq_affine_qmm(_ptr(x), _dt(x), M, K, _ptr(w), _wdt(w), _ptr(scales), _ptr(biases), N,
-                                int(bool(transpose)), group_size, bits, _ptr(residual), _ptr(out), _stream())
+    wsb = 0 if workspace is None else workspace.numel()
+    st = lib().moegq_affine_qmm_ws(_ptr(x), _dt(x), M, K, _ptr(w), _wdt(w), _ptr(scales), _ptr(biases), N,
+                                   int(bool(transpose)), group_size, bits, _ptr(residual), _ptr(out),
+                                   _ptr(workspace), wsb, _stream())
     _check(st, "affine_qmm")
     return out
 
 
-def affine_qmm_glu(x, gate, up, group_size=64, bits=4, out=None):
-    """bf16(silu(x . Wg^T) * (x . Wu^T)); gate/up are (words, scales, biases)."""
+def affine_qmm_glu(x, gate, up, group_size=64, bits=4, out=None, workspace=None):
+    """bf16(silu(x . Wg^T) * (x . Wu^T)); gate/up are (words, scales, biases).
+    workspace: optional (affine_qmm_workspace(..., glu=True))."""
     M, K = x.shape
     N = gate[0].shape[0]
     _req(x, "x", _BF)
     _req_matrix(gate, "gate", N, K, bits, group_size)
     _req_matrix(up, "up", N, K, bits, group_size)
     _dev(x, *gate, *up)
+    _req(workspace, "workspace", (torch.uint8,))
+    _dev(workspace)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    st = lib().moegq_affine_qmm_glu(_ptr(x), M, K, *[_ptr(t) for t in gate], *[_ptr(t) for t in up], N,
-                                    group_size, bits, _ptr(out), _stream())
+    wsb = 0 if workspace is None else workspace.numel()
+    st = lib().moegq_affine_qmm_glu_ws(_ptr(x), M, K, *[_ptr(t) for t in gate], *[_ptr(t) for t in up], N,
+                                       group_size, bits, _ptr(out), _ptr(workspace), wsb, _stream())
     _check(st, "affine_qmm_glu")
     return out
 

@@ -200,6 +200,30 @@ __global__ void offsets_from_sorted_kernel(const int32_t* rhs, int64_t P, int E,
   offsets[e] = (int32_t)lo;
 }
 
+// few rows per pair (M <= 16): the exact-code matrix-core kernel when K is a
+// multiple of 128 and the scales and biases start 8-byte aligned (K split
+// over workgroups when ws holds its scratch: [counters | partials], counters
+// zero before the first call), else the fp16-operand kernel
+size_t few_ws_bytes(const FewPlan& pl) { return pl.KS > 1 ? align256(pl.counter_bytes) + pl.part_bytes : 0; }
+int few_rows(const SkinnyArgs& sa, bool glu, int64_t P, int bits, int gs, void* ws, size_t wsb, hipStream_t s) {
+  // the matrix-core kernel reads a chunk's scales and biases as one 32- or
+  // 64-bit word: their arrays must start 8-byte aligned
+  auto a8 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7u) == 0; };
+  const bool sb_ok = a8(sa.s0) && a8(sa.b0) && (!glu || (a8(sa.s1) && a8(sa.b1)));
+  if (!fewrow_supported(sa.M, sa.N, sa.K, bits) || !sb_ok) return status_of(launch_skinny(sa, bits, gs, glu, P, s));
+  FewPlan pl = fewrow_plan(P, sa.N, sa.K, glu, ws != nullptr);
+  if (few_ws_bytes(pl) > wsb || (pl.KS > 1 && !aligned16(ws))) pl = fewrow_plan(P, sa.N, sa.K, glu, false);
+  FewArgs f{};
+  f.x = sa.x; f.lhs = sa.lhs; f.lhs_div = sa.lhs_div; f.rhs = sa.rhs;
+  f.w0 = sa.w0; f.s0 = sa.s0; f.b0 = sa.b0; f.w1 = sa.w1; f.s1 = sa.s1; f.b1 = sa.b1;
+  f.M = sa.M; f.N = sa.N; f.K = sa.K; f.out = sa.out; f.residual = sa.residual;
+  if (pl.KS > 1) {
+    f.counters = (int32_t*)ws;
+    f.part = (float*)((char*)ws + align256(pl.counter_bytes));
+  }
+  return status_of(launch_fewrow(f, pl, bits, gs, glu, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -378,7 +402,7 @@ static int gather_impl(const void* x, int x_dtype, int64_t X, int64_t M, int64_t
     a.w0 = (const uint32_t*)w; a.s0 = (const uint16_t*)scales; a.b0 = (const uint16_t*)biases;
     a.w1 = (const uint32_t*)w1; a.s1 = (const uint16_t*)s1; a.b1 = (const uint16_t*)b1;
     a.M = (int)M; a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out;
-    return status_of(launch_skinny(a, bits, group_size, glu, P, s));
+    return few_rows(a, glu, P, bits, group_size, nullptr, 0, s);
   }
   // M > 16: per-pair tiles over pair-major virtual rows
   if (!workspace || workspace_bytes < need) return MOEGQ_ERR_WORKSPACE;
@@ -438,9 +462,24 @@ int moegq_gather_qmm_glu(const void* x, int x_dtype, int64_t X, int64_t M, int64
                      workspace_bytes, stream);
 }
 
+size_t moegq_affine_qmm_workspace_bytes(int64_t M, int64_t N, int64_t K, int glu) {
+  // the bit width is not an argument: sized as if the narrowest codes (the
+  // size only grows with the split, never with the bits)
+  if (M < 2 || M > 16 || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || !fewrow_supported(M, N, K, 1)) return 0;
+  return few_ws_bytes(fewrow_plan(1, N, K, glu != 0, true));
+}
+
 int moegq_affine_qmm(const void* x, int x_dtype, int64_t M, int64_t K, const void* w, int w_dtype,
                      const void* scales, const void* biases, int64_t N, int transpose, int group_size,
                      int bits, const void* residual, void* out, void* stream) {
+  return moegq_affine_qmm_ws(x, x_dtype, M, K, w, w_dtype, scales, biases, N, transpose, group_size, bits,
+                             residual, out, nullptr, 0, stream);
+}
+
+int moegq_affine_qmm_ws(const void* x, int x_dtype, int64_t M, int64_t K, const void* w, int w_dtype,
+                        const void* scales, const void* biases, int64_t N, int transpose, int group_size,
+                        int bits, const void* residual, void* out, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   int st;
   if ((st = check_act_dtype(x_dtype))) return st;
   if (w_dtype != MOEGQ_U32) return MOEGQ_ERR_DTYPE;
@@ -463,7 +502,7 @@ int moegq_affine_qmm(const void* x, int x_dtype, int64_t M, int64_t K, const voi
     a.x = (const uint16_t*)x; a.lhs_div = 1;
     a.w0 = (const uint32_t*)w; a.s0 = (const uint16_t*)scales; a.b0 = (const uint16_t*)biases;
     a.M = (int)M; a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out; a.residual = (const uint16_t*)residual;
-    return status_of(launch_skinny(a, bits, group_size, false, 1, s));
+    return few_rows(a, false, 1, bits, group_size, workspace, workspace ? workspace_bytes : 0, s);
   }
   if (residual) return MOEGQ_ERR_UNSUPPORTED;
   if (M >= kBigM) {
@@ -491,6 +530,13 @@ int moegq_affine_qmm(const void* x, int x_dtype, int64_t M, int64_t K, const voi
 int moegq_affine_qmm_glu(const void* x, int64_t M, int64_t K, const void* wg, const void* sg,
                          const void* bg, const void* wu, const void* su, const void* bu, int64_t N,
                          int group_size, int bits, void* out, void* stream) {
+  return moegq_affine_qmm_glu_ws(x, M, K, wg, sg, bg, wu, su, bu, N, group_size, bits, out, nullptr, 0, stream);
+}
+
+int moegq_affine_qmm_glu_ws(const void* x, int64_t M, int64_t K, const void* wg, const void* sg,
+                            const void* bg, const void* wu, const void* su, const void* bu, int64_t N,
+                            int group_size, int bits, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   int st;
   if ((st = check_quant(K, group_size, bits))) return st;
   if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return MOEGQ_ERR_SHAPE;
@@ -512,7 +558,7 @@ int moegq_affine_qmm_glu(const void* x, int64_t M, int64_t K, const void* wg, co
     a.w0 = (const uint32_t*)wg; a.s0 = (const uint16_t*)sg; a.b0 = (const uint16_t*)bg;
     a.w1 = (const uint32_t*)wu; a.s1 = (const uint16_t*)su; a.b1 = (const uint16_t*)bu;
     a.M = (int)M; a.N = (int)N; a.K = (int)K; a.out = (uint16_t*)out;
-    return status_of(launch_skinny(a, bits, group_size, true, 1, s));
+    return few_rows(a, true, 1, bits, group_size, workspace, workspace ? workspace_bytes : 0, s);
   }
   if (M >= kBigM) {
     TileArgs a{};

@@ -39,8 +39,14 @@ MOEGQ_DEV float fdot2_bf16(uint32_t a, uint32_t b, float c) {
 // Four bf16 pairs holding 128 + q for the eight 4-bit codes of a word w:
 // pair j = (128 + q_j, 128 + q_{j+4}).  0x4300 is bf16 128.0 and codes < 16
 // land in its low mantissa bits, so each lane is exactly 128 + q.
+// The empty asm statements emit nothing: they hide the two constants' values
+// from the compiler, which then keeps the mask in a VGPR and 0x4300 in an
+// SGPR and selects one v_and_or_b32 per pair (with the constants visible it
+// picks two VOP2 instructions with literal operands instead).
 MOEGQ_DEV void nib_pairs(uint32_t w, uint32_t p[4]) {
-  const uint32_t m = 0x000F000Fu, magic = 0x43004300u;
+  uint32_t m = 0x000F000Fu, magic = 0x43004300u;
+  asm("" : "+v"(m));
+  asm("" : "+s"(magic));
   p[0] = (w & m) | magic;
   p[1] = ((w >> 4) & m) | magic;
   p[2] = ((w >> 8) & m) | magic;

@@ -39,6 +39,32 @@ struct SkinnyArgs {
 };
 hipError_t launch_skinny(const SkinnyArgs& a, int bits, int gs, bool glu, int64_t P, hipStream_t st);
 
+// few-row products on the bf16 matrix cores with exact codes (1..16 rows per
+// pair, K a multiple of 128), K split over KS workgroups when a workspace
+// holds the fp32 partials and the per-column-group counters (zero before the
+// first call; every call leaves them zero)
+struct FewArgs {
+  const uint16_t* x;        // [X, M, K]
+  const int32_t* lhs; int64_t lhs_div;
+  const int32_t* rhs;
+  const uint32_t* w0; const uint16_t* s0; const uint16_t* b0;
+  const uint32_t* w1; const uint16_t* s1; const uint16_t* b1;
+  int M, N, K;
+  uint16_t* out;            // [P, M, N]
+  const uint16_t* residual; // null or [P, M, N]
+  float* part;              // [items, KS, ...] fp32 partials (KS > 1)
+  int32_t* counters;        // [items] (KS > 1)
+  int cps;                  // K chunks per split (set by launch_fewrow)
+};
+struct FewPlan {
+  int NB, KS, cps;          // column blocks per workgroup, splits, chunks per split
+  int64_t items;            // workgroups per split (pairs x column groups)
+  size_t part_bytes, counter_bytes;
+};
+FewPlan fewrow_plan(int64_t P, int64_t N, int64_t K, bool glu, bool split_allowed);
+bool fewrow_supported(int64_t M, int64_t N, int64_t K, int bits);
+hipError_t launch_fewrow(const FewArgs& a, const FewPlan& pl, int bits, int gs, bool glu, hipStream_t st);
+
 // expert sort + tile table (single workgroup)
 struct SortArgs {
   const int32_t* idx; int64_t P; int top_k; int E;

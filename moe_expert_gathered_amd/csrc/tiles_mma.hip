@@ -396,7 +396,7 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
 #pragma unroll
     for (int j = 0; j < (GLU ? 2 : 4); ++j) {
       const int f = (GLU ? block_base(2 * j) : block_base(j)) + 4 * g;
-      uint16_t o[4];
+      float v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (GLU) {
@@ -405,20 +405,40 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
             gv = __builtin_ldexpf(gv, xe + eo_col[2 * j][q]);
             uv = __builtin_ldexpf(uv, xe + eo_col[2 * j + 1][q]);
           }
-          o[q] = f32_to_bf16(glu(gv, uv));
+          v[q] = glu(gv, uv);
         } else {
-          o[q] = f32_to_bf16(acc[i][j][q]);
+          v[q] = acc[i][j][q];
         }
       }
+      // round to nearest even, two outputs per conversion
+      const uint32_t lo = pk_bf16(v[0], v[1]), hi = pk_bf16(v[2], v[3]);
       if (vec && f + 3 < N) {
-        *reinterpret_cast<uint2*>(orow + f) = make_uint2(o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16));
+        *reinterpret_cast<uint2*>(orow + f) = make_uint2(lo, hi);
       } else {
+        const uint16_t o[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (f + q < N) orow[f + q] = o[q];
       }
     }
   }
+}
+
+// With 4-bit codes, a 128-row tile with at most 32 (64) rows, often an
+// expert's last one, runs as a 32-row (64-row) tile: the MFMAs of the 16-row
+// blocks past its rows would compute outputs that are never stored.  The
+// smaller bodies need no more LDS than the 128-row one.  With 8-bit codes the
+// extra bodies push the kernel's registers into spills, so it keeps one body.
+template <int BITS, int GS, bool GLU, int MI>
+MOEGQ_DEV void tile_rows(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, int r1, int e, int n0) {
+  const int nrow = __builtin_amdgcn_readfirstlane(r1 - r0);
+  if constexpr (MI == 8 && BITS == 4) {
+    static_assert(MmaRing<4, BITS>::HALFS <= MmaRing<8, BITS>::HALFS &&
+                  MmaRing<2, BITS>::HALFS <= MmaRing<8, BITS>::HALFS, "LDS ring");
+    if (nrow <= 32) return tile_body<BITS, GS, GLU, 2>(A, lds, xe_s, r0, r1, e, n0);
+    if (nrow <= 64) return tile_body<BITS, GS, GLU, 4>(A, lds, xe_s, r0, r1, e, n0);
+  }
+  tile_body<BITS, GS, GLU, MI>(A, lds, xe_s, r0, r1, e, n0);
 }
 
 // XCD-contiguous ranges: the hardware deals workgroups to the 8 XCDs round
@@ -452,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
     const int32_t* t = A.tiles + 3 * tile;
     r0 = t[0]; e = t[1]; r1 = r0 + t[2];
   }
-  tile_body<BITS, GS, GLU, MI>(A, As, xe_s, r0, r1, e, n0);
+  tile_rows<BITS, GS, GLU, MI>(A, As, xe_s, r0, r1, e, n0);
 }
 
 // Both tile tables in one launch: blocks [0, n_big * NB) take the 128-row
@@ -474,7 +494,7 @@ __global__ __launch_bounds__(256, 2) void tile_mma_dual_kernel(TileArgs A) {
   if (b < nbig) {
     const int bid = xcd_remap(b, nbig);
     const int32_t* t = A.tiles + 3 * (bid / NB);
-    tile_body<BITS, GS, GLU, MIB>(A, As, xe_s, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
+    tile_rows<BITS, GS, GLU, MIB>(A, As, xe_s, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
   } else if (b < nbig + nsmall) {
     const int bid = b - nbig;
     const int32_t* t = A.tiles2 + 3 * (bid / NB);

@@ -56,13 +56,34 @@ constexpr int TM_K = 128;   // K per step
 // gfx950; a plain c ^ r still collides across lane groups).
 MOEGQ_DEV int lds_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
+// The fp16 gate/up operands of 4-bit codes use subnormal codes: a code byte
+// under a zero byte is the fp16 subnormal q * 2^-24, exactly, so with
+// S = s * 2^24 one fused multiply-add gives q * s + b rounded once: two
+// instructions per pair of codes (v_perm, v_pk_fma_f16), where the 1024 + q
+// encoding needs its offset subtracted first.  S stays finite because the
+// column's scaling puts every |s| * qmax below 2^-5.  The products are the
+// same bits as with the 1024 + q encoding (the two scalings differ by an
+// exact power of two).  8-bit codes keep the 1024 + q encoding (deq8_f16,
+// column maximum in [2^13, 2^14)): their subnormal variant spilled registers
+// and ran slower.
+constexpr bool subnormal_codes(int bits) { return bits == 4; }
+
 // eight codes (one 4-bit word, or two 8-bit words) -> one fp16 MFMA operand
-// (4-bit: in the order q0 q2 q4 q6 q1 q3 q5 q7; 8-bit: natural)
+// (4-bit: in the order q0 q2 q4 q6 q1 q3 q5 q7; 8-bit: natural).  s2 and b2
+// are the group's scale (4-bit: times 2^24) and bias after the column scaling.
 template <int BITS>
 MOEGQ_DEV f16x8_t deq_operand_f16(uint32_t w0, uint32_t w1, f16x2_t s2, f16x2_t b2) {
   uint32_t o[4];
-  if (BITS == 4) {
-    deq4_f16(w0, s2, b2, o);
+  if constexpr (subnormal_codes(BITS)) {
+    auto pair = [&](uint32_t codes, uint32_t sel) -> uint32_t {
+      const f16x2_t q = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0u, codes, sel));
+      return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
+    };
+    const uint32_t lo = w0 & 0x0F0F0F0Fu, hi = (w0 >> 4) & 0x0F0F0F0Fu;   // bytes q0 q2 q4 q6 / q1 q3 q5 q7
+    o[0] = pair(lo, 0x04010400u);
+    o[1] = pair(lo, 0x04030402u);
+    o[2] = pair(hi, 0x04010400u);
+    o[3] = pair(hi, 0x04030402u);
   } else {
     deq8_f16(w0, s2, b2, o);
     deq8_f16(w1, s2, b2, o + 2);
@@ -99,10 +120,15 @@ template <int MI, int BITS = 4> struct MmaRing {
 //    arrive as fp16 copies scaled by 2^-xexp[row] (launch_front / launch_prep:
 //    the row's largest magnitude lands in [2^13, 2^14)), and each weight
 //    column is scaled by 2^-ec, ec taken at the tile's start from the
-//    column's largest |s| * qmax + |b| over all its groups; the epilogue
-//    multiplies the fp32 result by 2^(xexp + ec).  The scalings are exact, so
-//    the products keep fp16's 11-bit weights (the precision silu(g) * u
-//    needs: it rounds g and u to bf16 first) over bf16's whole range.
+//    column's largest |s| * qmax + |b| over all its groups (it lands in
+//    [2^-6, 2^-5) for 4-bit codes, [2^13, 2^14) for 8-bit ones); the
+//    epilogue multiplies the fp32 result by 2^(xexp + ec).  The scalings are
+//    exact, so the products keep fp16's 11-bit weights (the precision
+//    silu(g) * u needs: it rounds g and u to bf16 first) over bf16's whole
+//    range.  A 4-bit dequantized weight more than about 2^9 below its
+//    column's largest one is an fp16 subnormal (the matrix cores take fp16
+//    subnormals as they are): rounded to a multiple of 2^-24, under 2^-19 of
+//    the column's largest weight.
 //  * down (and any pass without GLU): bf16 operands, the intermediate as
 //    stored, weights dequantized to bf16.
 //  * BITS = 16: the expert matrices are plain bf16 (no scales or biases);
@@ -281,7 +307,7 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if constexpr (F16) {
-          s2[j] = f16_splat(__builtin_ldexpf(pick(win_s, ks, j), -ecj[j]));
+          s2[j] = f16_splat(__builtin_ldexpf(pick(win_s, ks, j), (subnormal_codes(BITS) ? 24 : 0) - ecj[j]));
           b2[j] = f16_splat(__builtin_ldexpf(pick(win_b, ks, j), -ecj[j]));
         } else {
           sj[j] = pick(win_s, ks, j);
@@ -362,7 +388,10 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
         }
       }
     }
-    ecol = f16_exponent(mx);
+    // subnormal codes: mx * 2^-ecol in [2^-6, 2^-5), so S = s' * 2^24 < 2^19 / qmax
+    // is a finite fp16; else mx * 2^-ecol in [2^13, 2^14)
+    if constexpr (subnormal_codes(BITS)) ecol = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) + 5 : 0;
+    else ecol = f16_exponent(mx);
 #pragma unroll
     for (int j = 0; j < 4; ++j) ecj[j] = __shfl(ecol, 16 * j + c16, 64);
   }

@@ -18,7 +18,8 @@ expert, combine); the expert-aware vs naive tile schedules and the whole
 layer on the large prefill (hidden 4096, 288 experts, inter 2048) at
 713-16384 rows; the fused against the unfused combine; unquantized
 gather_mm; the vector-unit route; the dense few-row chain (36 decoder
-layers, 8 weight sets); and the oracle timed on the host (cpu_baseline).
+layers, 8 weight sets) and its sweep over rows 1-16, 4/8-bit codes and group
+sizes 32/64/128; and the oracle timed on the host (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs a,b,...]
 """
@@ -46,7 +47,7 @@ def parse():
     # the `steps` timed replays sits between its own events (median reported)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,ceilings,prefill,large,combine,gather_mm,vec,dense,cpu")
+    ap.add_argument("--legs", default="decode,ceilings,prefill,large,combine,gather_mm,vec,dense,fewrow,cpu")
     ap.add_argument("--prefill-rows", default="2048,128,512,4096", help="row counts of the prefill leg")
     ap.add_argument("--large-rows", default="713,4123,8192,16384", help="row counts of the large-prefill leg")
     ap.add_argument("--quiet", action="store_true")
@@ -580,7 +581,7 @@ def combine_leg(torch, m, synth, reps=20, cfg=3):
 
 
 # ----------------------------------------------------------------------------- dense chain
-def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=10, warmup=2, cfg=2):
+def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=10, warmup=2, cfg=2, eager=True):
     dev = torch.device("cuda")
     d = synth.DENSE
     sets = synth.device_dense_sets(dev, cfg, gs, bits, d)
@@ -622,22 +623,38 @@ def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=10, warmup=2
             fwd()
         torch.cuda.synchronize()
         ts = []
-        for _ in range(reps):
+        for _ in range(reps if eager else 0):
             t0 = time.perf_counter()
             fwd()
             torch.cuda.synchronize()
             ts.append(time.perf_counter() - t0)
-        med = float(np.median(ts))
         # the same forward captured once as a HIP graph: kernel time without the
         # per-call host work of ~300 launches from Python
         fst = graph_stats(torch, lambda i: fwd(), 1, reps=reps)
         g_s = fst.median * 1e-6
         res[f"rows{M}"] = {"ms_per_forward": g_s * 1e3, "ms_stats": fst.as_dict(1e-3, "ms"), "gbs": per_fwd / g_s / 1e9,
-                           "hbm_frac": per_fwd / g_s / (HBM_PEAK_GBS * 1e9), "timing": "hip graph of one forward",
-                           "eager_ms_per_forward": med * 1e3, "eager_gbs": per_fwd / med / 1e9}
+                           "hbm_frac": per_fwd / g_s / (HBM_PEAK_GBS * 1e9), "timing": "hip graph of one forward"}
+        if eager:
+            med = float(np.median(ts))
+            res[f"rows{M}"].update({"eager_ms_per_forward": med * 1e3, "eager_gbs": per_fwd / med / 1e9})
     del sets
     torch.cuda.empty_cache()
     return res
+
+
+def fewrow_sweep_leg(torch, m, synth, rows=(1, 2, 3, 4, 6, 8, 12, 16), reps=5):
+    """The dense 36-layer chain (MLX #4787's few-row regime) at every row count
+    1..16 of the sweep, for 4- and 8-bit codes and group sizes 32, 64, 128:
+    ms per forward (HIP graph, median of `reps` replays) and the fraction of
+    HBM peak that the forward's weight bytes would take."""
+    out = {}
+    for bits in (4, 8):
+        for gs in (32, 64, 128):
+            r = dense_leg(torch, m, synth, rows=rows, bits=bits, gs=gs, reps=reps, warmup=1, eager=False)
+            out[f"w{bits}g{gs}"] = {"forward_weight_bytes": r["forward_weight_bytes"],
+                                    "ms_per_forward": {M: round(r[f"rows{M}"]["ms_per_forward"], 4) for M in rows},
+                                    "hbm_frac": {M: round(r[f"rows{M}"]["hbm_frac"], 4) for M in rows}}
+    return out
 
 
 # ----------------------------------------------------------------------------- counter calibration
@@ -769,6 +786,9 @@ def main():
     if "dense" in legs:
         log("dense chain")
         extra["dense_chain"] = dense_leg(torch, m, synth)
+    if "fewrow" in legs:
+        log("few-row sweep: rows 1..16, bits 4/8, group sizes 32/64/128")
+        extra["fewrow_sweep"] = fewrow_sweep_leg(torch, m, synth)
     if "calib" in legs:
         log("counter calibration copy")
         extra["calib"] = calib_leg(torch)

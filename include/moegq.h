@@ -187,8 +187,9 @@ int moegq_affine_qmm(const void* x, int x_dtype, int64_t M, int64_t K,
                      const void* residual, void* out, void* stream);
 /*
  * affine_qmm_ws / affine_qmm_glu_ws: the same products with a workspace that
- * lets 2..16-row products with K a multiple of 128 split K over workgroups
- * (so that products with few output columns still fill the machine):
+ * lets 5..16-row products with K a multiple of 128 split K over workgroups
+ * (so that products with few output columns still fill the machine; 1..4
+ * rows run the matrix-vector kernel, which takes no workspace):
  * moegq_affine_qmm_workspace_bytes(M, N, K, glu) bytes, 16-byte aligned,
  * ZERO-FILLED before its first use; every call leaves it in that state (its
  * per-column-group counters return to zero, the fp32 partials are scratch).

@@ -397,7 +397,7 @@ def gather_qmm_glu(x, gate, up, rhs_indices, lhs_indices=None, lhs_div=1, group_
 
 def affine_qmm_workspace(M: int, N: int, K: int, glu: bool = False, device="cuda"):
     """A zero-filled workspace for affine_qmm / affine_qmm_glu at these sizes
-    (None when the product takes none): K split over workgroups at 2..16 rows.
+    (None when the product takes none): K split over workgroups at 5..16 rows.
     Its layout depends on (N, K, glu) only: reusable by later calls with the
     same N, K and glu (any M up to 16) on one stream, not by other shapes."""
     n = int(lib().moegq_affine_qmm_workspace_bytes(M, N, K, int(bool(glu))))
@@ -407,7 +407,7 @@ def affine_qmm_workspace(M: int, N: int, K: int, glu: bool = False, device="cuda
 def affine_qmm(x, w, scales, biases, group_size=64, bits=4, transpose=True, residual=None, out=None,
                workspace=None):
     """out = x . dequant(w)^T (+ residual after rounding).  x [M, K], w [N, Kw].
-    workspace: optional (affine_qmm_workspace): lets 2..16-row products split K."""
+    workspace: optional (affine_qmm_workspace): lets 5..16-row products split K."""
     M, K = x.shape
     N = w.shape[0]
     _req(x, "x", _BF)

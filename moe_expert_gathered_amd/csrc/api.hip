@@ -29,6 +29,8 @@ int status_of(hipError_t e) { return e == hipSuccess ? MOEGQ_OK : MOEGQ_ERR_LAUN
 // lie beyond that range: one matrix of codes stays at most 0x7FFFFFF0 bytes.
 constexpr int64_t kNoFetchOffset = 0x7FFFFFF0;
 bool one_row_fits(int64_t N, int64_t K, int bits) { return N * K * bits / 8 <= kNoFetchOffset; }
+// most activation rows per pair on the vector kernel (more go to the matrix cores)
+constexpr int64_t kQmvRowsMax = 4;
 
 // bit width / group size / quantized length checks
 int check_quant(int64_t K, int gs, int bits) {
@@ -200,12 +202,23 @@ __global__ void offsets_from_sorted_kernel(const int32_t* rhs, int64_t P, int E,
   offsets[e] = (int32_t)lo;
 }
 
-// few rows per pair (M <= 16): the exact-code matrix-core kernel when K is a
-// multiple of 128 and the scales and biases start 8-byte aligned (K split
-// over workgroups when ws holds its scratch: [counters | partials], counters
-// zero before the first call), else the fp16-operand kernel
+// few rows per pair (M <= 16): up to 4 rows the matrix-vector kernel with
+// every code applied to all the rows; else the exact-code matrix-core kernel
+// when K is a multiple of 128 and the scales and biases start 8-byte aligned
+// (K split over workgroups when ws holds its scratch: [counters | partials],
+// counters zero before the first call), else the fp16-operand kernel
 size_t few_ws_bytes(const FewPlan& pl) { return pl.KS > 1 ? align256(pl.counter_bytes) + pl.part_bytes : 0; }
 int few_rows(const SkinnyArgs& sa, bool glu, int64_t P, int bits, int gs, void* ws, size_t wsb, hipStream_t s) {
+  if (sa.M <= kQmvRowsMax && sa.K <= kMaxQmvK && one_row_fits(sa.N, sa.K, bits)) {
+    // 2..4 rows: the vector kernel with every code applied to all the pair's
+    // rows (its many one-wave workgroups keep more loads in flight than the
+    // matrix-core kernel's few four-wave ones)
+    QmvArgs a{};
+    a.x = sa.x; a.lhs = sa.lhs; a.lhs_div = sa.lhs_div; a.rhs = sa.rhs;
+    a.w0 = sa.w0; a.s0 = sa.s0; a.b0 = sa.b0; a.w1 = sa.w1; a.s1 = sa.s1; a.b1 = sa.b1;
+    a.N = sa.N; a.K = sa.K; a.out = sa.out; a.residual = sa.residual; a.rows = sa.M;
+    return status_of(launch_qmv(a, bits, gs, glu, P, s));
+  }
   // the matrix-core kernel reads a chunk's scales and biases as one 32- or
   // 64-bit word: their arrays must start 8-byte aligned
   auto a8 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7u) == 0; };

@@ -1,5 +1,6 @@
-// Few-row quantized products (2..16 activation rows per weight matrix) on
-// the bf16 matrix cores, with the codes entering the MFMA exactly.
+// Few-row quantized products (5..16 activation rows per weight matrix, and
+// 2..4 where the matrix-vector kernel does not take the shape) on the bf16
+// matrix cores, with the codes entering the MFMA exactly.
 //
 // MLX PR 4787: at 3-16 rows the weights should feed the matrix units rather
 // than a per-row vector loop.  This kernel keeps the weights as codes on the

@@ -15,8 +15,9 @@ struct QmvArgs {
   const uint32_t* w0; const uint16_t* s0; const uint16_t* b0;   // [E, N, Kw], [E, N, G]
   const uint32_t* w1; const uint16_t* s1; const uint16_t* b1;   // GLU: up projection
   int N, K;
-  uint16_t* out;            // [P, N]
-  const uint16_t* residual; // null or [P, N]
+  uint16_t* out;            // [P, N] ([P, rows, N] with several rows)
+  const uint16_t* residual; // null or shaped as out
+  int64_t rows;             // activation rows per pair (x [X, rows, K]); 0 or 1: one row, at most 4
 };
 hipError_t launch_qmv(const QmvArgs& a, int bits, int gs, bool glu, int64_t P, hipStream_t st);
 // unquantized bf16 expert rows [E, N, K] (a.w0), one activation row per pair; K % 8 == 0

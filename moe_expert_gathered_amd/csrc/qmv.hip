@@ -77,9 +77,15 @@ MOEGQ_DEV void reduce_wave(float (&a)[V]) {
 // the gate/up and plain kernels at fewer registers and more waves per SIMD
 // (measured faster there).  The down+combine kernel runs faster without it:
 // its arithmetic then starts as each row's loads land.
-template <int BITS, int GS, bool GLU, int RPW, int NS, bool SEL = true, int V = RPW * (GLU ? 2 : 1)>
+// MR > 1: each pair has A.rows (<= MR) activation rows, x rows xrow * rows + r,
+// and every code a lane loads is applied to all of them (rows past A.rows
+// repeat the last one and are never stored).  acc then holds value
+// (m * MR + r) * RPW + rr for matrix m, activation row r, output row rr.
+template <int BITS, int GS, bool GLU, int RPW, int NS, bool SEL = true, int MR = 1,
+          int V = RPW * (GLU ? 2 : 1) * MR>
 MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first, int step, float (&acc)[V]) {
   constexpr int NM = GLU ? 2 : 1;
+  constexpr int VC = RPW * NM;            // code rows of the wave
   constexpr int XV = BITS == 4 ? 4 : 2;   // uint4 of activations per lane per slice
   const int K = A.K, N = A.N;
   const int64_t xrow = A.lhs ? (int64_t)A.lhs[p] : (A.lhs_shift >= 0 ? p >> A.lhs_shift : p / A.lhs_div);
@@ -96,7 +102,15 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
     rs[NM - 1] = make_rsrc(A.s1 + e * N * (int64_t)G, (uint32_t)N * G * 2);
     rb[NM - 1] = make_rsrc(A.b1 + e * N * (int64_t)G, (uint32_t)N * G * 2);
   }
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(A.x + xrow * (int64_t)K, (uint32_t)K * 2);
+  __amdgpu_buffer_rsrc_t rx[MR];
+  if constexpr (MR == 1) {
+    rx[0] = make_rsrc(A.x + xrow * (int64_t)K, (uint32_t)K * 2);
+  } else {
+    const int64_t nr = A.rows;
+#pragma unroll
+    for (int r = 0; r < MR; ++r)
+      rx[r] = make_rsrc(A.x + (xrow * nr + min((int64_t)r, nr - 1)) * (int64_t)K, (uint32_t)K * 2);
+  }
 
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
@@ -108,8 +122,8 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
   const int n_it = (Kw + 255) / 256;
   constexpr uint32_t kNoFetch = 0x7FFFFFF0u;   // past every descriptor's range
   for (int it0 = first; it0 < n_it; it0 += step) {
-    uint4 c[NS][V], xv[NS][XV];
-    uint16_t sv[NS][V], bv[NS][V];
+    uint4 c[NS][VC], xv[NS][MR][XV];
+    uint16_t sv[NS][VC], bv[NS][VC];
     bool ok[NS];
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
@@ -127,7 +141,9 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
           bv[t][m * RPW + r] = buf_load2(rb[m], ok[t] ? g2 : kNoFetch, row * G * 2);
         }
 #pragma unroll
-      for (int j = 0; j < XV; ++j) xv[t][j] = buf_load16(rx, (uint32_t)(k0 + 8 * j) * 2, 0);
+      for (int r = 0; r < MR; ++r)
+#pragma unroll
+        for (int j = 0; j < XV; ++j) xv[t][r][j] = buf_load16(rx[r], (uint32_t)(k0 + 8 * j) * 2, 0);
     }
     // gate/up: a wave whose loads are all issued takes issue priority, so the
     // waves whose data has landed finish first and hand their slots to waves
@@ -135,12 +151,12 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
     if (GLU) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
-      if (BITS == 4) {
+      if (BITS == 4 && MR == 1) {
         // activations in the pair order (x0,x2) (x4,x6) (x1,x3) (x5,x7) per 8
         uint32_t xp[16];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint4 v = xv[t][j];
+          const uint4 v = xv[t][0][j];
           xp[4 * j + 0] = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);
           xp[4 * j + 1] = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
           xp[4 * j + 2] = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
@@ -165,11 +181,58 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
           const float b = (!SEL || ok[t]) ? bf16_to_f32(bv[t][i]) : 0.f;
           acc[i] = fmaf(s, d, fmaf(fmaf(-128.f, s, b), sx, acc[i]));
         }
-      } else {
+      } else if (BITS == 4) {
+        // several activation rows: each code pair is built once and applied to every row
+        uint32_t xp[MR][16];
+        float sx[MR];
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint4 v = xv[t][r][j];
+            xp[r][4 * j + 0] = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);
+            xp[r][4 * j + 1] = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
+            xp[r][4 * j + 2] = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
+            xp[r][4 * j + 3] = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
+          }
+          sx[r] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sx[r] = fdot2_bf16(xp[r][i], 0x3F803F80u, sx[r]);
+        }
+#pragma unroll
+        for (int i = 0; i < VC; ++i) {
+          const uint32_t cw[4] = {c[t][i].x, c[t][i].y, c[t][i].z, c[t][i].w};
+          float d[MR];
+#pragma unroll
+          for (int r = 0; r < MR; ++r) d[r] = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = cw[j] & 0x0F0F0F0Fu, hi = (cw[j] >> 4) & 0x0F0F0F0Fu;
+            const uint32_t q0 = __builtin_amdgcn_perm(C43, lo, 0x04010400u), q1 = __builtin_amdgcn_perm(C43, lo, 0x04030402u);
+            const uint32_t q2 = __builtin_amdgcn_perm(C43, hi, 0x04010400u), q3 = __builtin_amdgcn_perm(C43, hi, 0x04030402u);
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+              d[r] = fdot2_bf16(q0, xp[r][4 * j + 0], d[r]);
+              d[r] = fdot2_bf16(q1, xp[r][4 * j + 1], d[r]);
+              d[r] = fdot2_bf16(q2, xp[r][4 * j + 2], d[r]);
+              d[r] = fdot2_bf16(q3, xp[r][4 * j + 3], d[r]);
+            }
+          }
+          const float s = (!SEL || ok[t]) ? bf16_to_f32(sv[t][i]) : 0.f;
+          const float b = (!SEL || ok[t]) ? bf16_to_f32(bv[t][i]) : 0.f;
+          const float cb = fmaf(-128.f, s, b);
+          const int m = i / RPW, rr = i % RPW;
+#pragma unroll
+          for (int r = 0; r < MR; ++r) {
+            float& a = acc[(m * MR + r) * RPW + rr];
+            a = fmaf(s, d[r], fmaf(cb, sx[r], a));
+          }
+        }
+      } else if (MR == 1) {
         float xf[16];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const uint32_t d4[4] = {xv[t][j].x, xv[t][j].y, xv[t][j].z, xv[t][j].w};
+          const uint32_t d4[4] = {xv[t][0][j].x, xv[t][0][j].y, xv[t][0][j].z, xv[t][0][j].w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) { xf[8 * j + 2 * q] = bf16_lo(d4[q]); xf[8 * j + 2 * q + 1] = bf16_hi(d4[q]); }
         }
@@ -190,6 +253,47 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
           const float s = (!SEL || ok[t]) ? bf16_to_f32(sv[t][i]) : 0.f;
           const float b = (!SEL || ok[t]) ? bf16_to_f32(bv[t][i]) : 0.f;
           acc[i] = fmaf(s, d, fmaf(b, sx, acc[i]));
+        }
+      } else {
+        float xf[MR][16], sx[MR];
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint32_t d4[4] = {xv[t][r][j].x, xv[t][r][j].y, xv[t][r][j].z, xv[t][r][j].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { xf[r][8 * j + 2 * q] = bf16_lo(d4[q]); xf[r][8 * j + 2 * q + 1] = bf16_hi(d4[q]); }
+          }
+          sx[r] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sx[r] += xf[r][i];
+        }
+#pragma unroll
+        for (int i = 0; i < VC; ++i) {
+          const uint32_t cw[4] = {c[t][i].x, c[t][i].y, c[t][i].z, c[t][i].w};
+          float d[MR];
+#pragma unroll
+          for (int r = 0; r < MR; ++r) d[r] = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float q0 = (float)((cw[j] >> 0) & 0xFFu), q1 = (float)((cw[j] >> 8) & 0xFFu);
+            const float q2 = (float)((cw[j] >> 16) & 0xFFu), q3 = (float)((cw[j] >> 24) & 0xFFu);
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+              d[r] = fmaf(q0, xf[r][4 * j + 0], d[r]);
+              d[r] = fmaf(q1, xf[r][4 * j + 1], d[r]);
+              d[r] = fmaf(q2, xf[r][4 * j + 2], d[r]);
+              d[r] = fmaf(q3, xf[r][4 * j + 3], d[r]);
+            }
+          }
+          const float s = (!SEL || ok[t]) ? bf16_to_f32(sv[t][i]) : 0.f;
+          const float b = (!SEL || ok[t]) ? bf16_to_f32(bv[t][i]) : 0.f;
+          const int m = i / RPW, rr = i % RPW;
+#pragma unroll
+          for (int r = 0; r < MR; ++r) {
+            float& a = acc[(m * MR + r) * RPW + rr];
+            a = fmaf(s, d[r], fmaf(b, sx[r], a));
+          }
         }
       }
     }
@@ -219,16 +323,26 @@ MOEGQ_DEV bool reduce_waves(float (&acc)[V], int lane, int wave) {
 
 // A workgroup of S waves owns RPW output rows of one pair; wave w takes the
 // chunks w, w + S, .. of K (S > 1 when the grid alone would not keep enough
-// loads in flight: few pairs, few rows).
-template <int BITS, int GS, bool GLU, int RPW, int NS, int S>
+// loads in flight: few pairs, few rows).  MR > 1: the pair's A.rows (<= MR)
+// activation rows share every code the waves load (qmv_rows).
+template <int BITS, int GS, bool GLU, int RPW, int NS, int S, int MR = 1>
 __global__ __launch_bounds__(64 * S) void qmv_kernel(QmvArgs A, int64_t p_base) {
-  constexpr int V = RPW * (GLU ? 2 : 1);
+  constexpr int V = RPW * (GLU ? 2 : 1) * MR;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * RPW;
   const int64_t p = p_base + blockIdx.y;
   const int N = A.N;
   const int rowg = lane >> 4;
+  const int64_t nr = MR > 1 ? A.rows : 1;
+  // value q = rowg * V / 4 + j of this lane's row group, once the wave's sums
+  // are reduced, is output (activation row q / RPW, column n0 + q % RPW); in
+  // the GLU variant the gate values fill rows 0-1 and the up values rows 2-3
+  auto out_index = [&](int q, bool& ok) -> int64_t {
+    const int r = q / RPW, n = n0 + q % RPW;
+    ok = r < nr && n < N;
+    return (p * nr + min((int64_t)r, nr - 1)) * (int64_t)N + min(n, N - 1);
+  };
   // the residual of the values this lane writes is requested before the
   // weight stream (clamped addresses, 32-bit registers), so the epilogue
   // waits for no memory
@@ -237,33 +351,54 @@ __global__ __launch_bounds__(64 * S) void qmv_kernel(QmvArgs A, int64_t p_base) 
   for (int j = 0; j < V / 4; ++j) res_in[j] = 0;
   if (!GLU && A.residual && wave == 0) {
 #pragma unroll
-    for (int j = 0; j < V / 4; ++j) res_in[j] = A.residual[p * (int64_t)N + min(n0 + rowg * (V / 4) + j, N - 1)];
+    for (int j = 0; j < V / 4; ++j) {
+      if constexpr (MR == 1) {
+        res_in[j] = A.residual[p * (int64_t)N + min(n0 + rowg * (V / 4) + j, N - 1)];
+      } else {
+        bool ok;
+        res_in[j] = A.residual[out_index(rowg * (V / 4) + j, ok)];
+      }
+    }
   }
   float acc[V];
-  qmv_rows<BITS, GS, GLU, RPW, NS>(A, p, n0, lane, wave * NS, S * NS, acc);
+  qmv_rows<BITS, GS, GLU, RPW, NS, true, MR>(A, p, n0, lane, wave * NS, S * NS, acc);
   if (!reduce_waves<S>(acc, lane, wave)) return;
   // lane 16*r (r = 2*bit5 + bit4) holds values r*V/4 .. r*V/4 + V/4 - 1
   if (GLU) {
-    // gate values 0..RPW-1 sit in rows 0-1, up values RPW..2*RPW-1 in rows 2-3
+    // gate values sit in rows 0-1, up values in rows 2-3
     float u[V / 4];
 #pragma unroll
     for (int j = 0; j < V / 4; ++j) u[j] = __shfl_xor(acc[j], 32, 64);
     if ((lane & 15) == 0 && rowg < 2) {
 #pragma unroll
       for (int j = 0; j < V / 4; ++j) {
-        const int n = n0 + rowg * (V / 4) + j;
-        if (n < N) A.out[p * (int64_t)N + n] = f32_to_bf16(glu(acc[j], u[j]));
+        if constexpr (MR == 1) {
+          const int n = n0 + rowg * (V / 4) + j;
+          if (n < N) A.out[p * (int64_t)N + n] = f32_to_bf16(glu(acc[j], u[j]));
+        } else {
+          bool ok;
+          const int64_t o = out_index(rowg * (V / 4) + j, ok);
+          if (ok) A.out[o] = f32_to_bf16(glu(acc[j], u[j]));
+        }
       }
     }
   } else {
     if ((lane & 15) == 0) {
 #pragma unroll
       for (int j = 0; j < V / 4; ++j) {
-        const int n = n0 + rowg * (V / 4) + j;
-        if (n < N) {
+        bool ok;
+        int64_t o;
+        if constexpr (MR == 1) {
+          const int n = n0 + rowg * (V / 4) + j;
+          ok = n < N;
+          o = p * (int64_t)N + n;
+        } else {
+          o = out_index(rowg * (V / 4) + j, ok);
+        }
+        if (ok) {
           float y = acc[j];
           if (A.residual) y = bf16_to_f32(f32_to_bf16(y)) + bf16_to_f32((uint16_t)res_in[j]);
-          A.out[p * (int64_t)N + n] = f32_to_bf16(y);
+          A.out[o] = f32_to_bf16(y);
         }
       }
     }
@@ -413,21 +548,42 @@ hipError_t launch_qmv_combine(const QmvArgs& a_in, int bits, int gs, const uint1
   return hipErrorInvalidValue;
 }
 
-template <int BITS, int GS, bool GLU, int RPW, int NS, int S>
-static void launch_qmv_cfg(const QmvArgs& a, int64_t P, hipStream_t st) {
-  const unsigned nrb = (unsigned)((a.N + RPW - 1) / RPW);
-  for (int64_t p0 = 0; p0 < P; p0 += 65535) {
-    dim3 grid(nrb, (unsigned)(P - p0 < 65535 ? P - p0 : 65535));
-    hipLaunchKernelGGL((qmv_kernel<BITS, GS, GLU, RPW, NS, S>), grid, dim3(64 * S), 0, st, a, p0);
-  }
-}
-
 // Waves in flight wanted for the whole launch: with fewer, each wave's loads
 // are too few to cover the memory latency.
 constexpr int64_t kQmvWaves = 4096;
 
+template <int BITS, int GS, bool GLU, int RPW, int NS, int S, int MR = 1>
+static void launch_qmv_cfg(const QmvArgs& a, int64_t P, hipStream_t st) {
+  const unsigned nrb = (unsigned)((a.N + RPW - 1) / RPW);
+  for (int64_t p0 = 0; p0 < P; p0 += 65535) {
+    dim3 grid(nrb, (unsigned)(P - p0 < 65535 ? P - p0 : 65535));
+    hipLaunchKernelGGL((qmv_kernel<BITS, GS, GLU, RPW, NS, S, MR>), grid, dim3(64 * S), 0, st, a, p0);
+  }
+}
+
+// 2..4 activation rows per pair: one chunk of codes at a time (the rows'
+// activations take the registers a second chunk would), 2 (GLU) or 4 output
+// rows per wave, K split over up to 4 waves when the grid is small
+template <int BITS, int GS, bool GLU, int MR>
+static hipError_t launch_qmv_rows_t(const QmvArgs& a, int64_t P, hipStream_t st) {
+  if (GLU) {
+    launch_qmv_cfg<BITS, GS, true, 2, 1, 1, MR>(a, P, st);
+    return hipGetLastError();
+  }
+  const int n_it = (a.K * BITS / 32 + 255) / 256;
+  const int64_t w4 = (int64_t)((a.N + 3) / 4) * P;
+  int S = 1;
+  while (S < 4 && 2 * S <= n_it && w4 * S < kQmvWaves) S *= 2;
+  if (S == 4) launch_qmv_cfg<BITS, GS, false, 4, 1, 4, MR>(a, P, st);
+  else if (S == 2) launch_qmv_cfg<BITS, GS, false, 4, 1, 2, MR>(a, P, st);
+  else launch_qmv_cfg<BITS, GS, false, 4, 1, 1, MR>(a, P, st);
+  return hipGetLastError();
+}
+
 template <int BITS, int GS, bool GLU>
 static hipError_t launch_qmv_t(const QmvArgs& a, int64_t P, hipStream_t st) {
+  if (a.rows > 1) return a.rows <= 2 ? launch_qmv_rows_t<BITS, GS, GLU, 2>(a, P, st)
+                                     : launch_qmv_rows_t<BITS, GS, GLU, 4>(a, P, st);
   const int Kw = a.K * BITS / 32;
   const int n_it = (Kw + 255) / 256;
   const bool two = Kw > 256 && Kw <= 512 && (GLU || BITS == 4);   // the whole row in one chunk of 2 slices
@@ -465,6 +621,7 @@ static hipError_t launch_qmv_gs(const QmvArgs& a, int gs, int64_t P, hipStream_t
 
 hipError_t launch_qmv(const QmvArgs& a_in, int bits, int gs, bool glu, int64_t P, hipStream_t st) {
   if (P <= 0 || a_in.N <= 0) return hipSuccess;
+  if (a_in.rows > 4) return hipErrorInvalidValue;
   QmvArgs a = a_in;
   a.lhs_shift = -1;
   if (a.lhs_div > 0 && (a.lhs_div & (a.lhs_div - 1)) == 0) {

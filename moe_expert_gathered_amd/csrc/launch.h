@@ -86,7 +86,7 @@ struct SortArgs {
 };
 int64_t sort_blocks(int64_t P);
 hipError_t launch_sort(const SortArgs& a, hipStream_t st);
-// the scan and scatter launches of the block sort, once a.block_counts holds the block histograms
+// the ranking launch of the block sort, once a.block_counts holds the block histograms
 hipError_t launch_sort_rest(const SortArgs& a, hipStream_t st);
 hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int tile_mode, int32_t* tiles,
                            int32_t* n_tiles, hipStream_t st);

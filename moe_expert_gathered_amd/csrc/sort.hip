@@ -1,14 +1,15 @@
 // Expert sort of the (token, slot) pairs and the row-tile tables: the
 // kernels and their launcher (the device code is in sort_dev.h).
 //
-// Up to SORT_ONE_MAX_P pairs: one workgroup does everything.  Beyond: three
+// Up to SORT_ONE_MAX_P pairs: one workgroup does everything.  Beyond: two
 // launches over blocks of 1024 pairs:
 //  1. count: a per-block histogram of expert ids (one LDS atomic per distinct
 //     id per wave, after ballot matching);
-//  2. scan (one workgroup, one expert per thread): counts, exclusive offsets,
-//     the base row of every (block, expert) for the stable scatter, and the
-//     tile tables;
-//  3. scatter: each pair's row is its (block, expert) base plus its rank.
+//  2. rank: every block reads all the histograms (one expert per thread), so
+//     it has each expert's total, its exclusive offset (a workgroup scan) and
+//     the block's base row per expert (the counts of the blocks before it);
+//     a pair's row is that base plus its rank inside the block.  Block 0 also
+//     writes counts, offsets and the tile tables.
 #include "sort_dev.h"
 
 namespace moegq {
@@ -20,48 +21,34 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_count_kernel(const int32_t*
   sort_count_block(idx, P, E, bc, blockIdx.x);
 }
 
-__global__ __launch_bounds__(SORT_THREADS) void sort_scan_kernel(SortArgs A, int nblk) {
+__global__ __launch_bounds__(SORT_THREADS) void sort_rank_kernel(SortArgs A, int nblk) {
   __shared__ int wtot[SORT_WAVES];
-  const int tid = threadIdx.x;
+  __shared__ int base[SORT_MAXE];
+  __shared__ __attribute__((aligned(16))) uint8_t tab[SORT_WAVES][SORT_MAXE];
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int E = A.E;
-  const int64_t P = A.P;
-  // counts (16 independent loads in flight per batch)
-  int c = 0;
+  const int blk = blockIdx.x;
+  reinterpret_cast<uint4*>(&tab[0][0])[tid] = make_uint4(0, 0, 0, 0);   // 16 KiB = 1024 x 16 B
+  // expert tid: its total over all blocks and over the blocks before this one
+  // (16 independent loads in flight per batch)
+  int c = 0, before = 0;
   if (tid < E) {
-    for (int b0 = 0; b0 < nblk; b0 += 16) {
-      int v[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = b0 + j < nblk ? A.block_counts[(int64_t)(b0 + j) * E + tid] : 0;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) c += v[j];
-    }
-  }
-  int off;
-  block_excl_scan(c, wtot, off);
-  // per-block bases: the expert's first row plus the counts of the blocks before
-  if (tid < E) {
-    int run = off;
     for (int b0 = 0; b0 < nblk; b0 += 16) {
       int v[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) v[j] = b0 + j < nblk ? A.block_counts[(int64_t)(b0 + j) * E + tid] : 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        if (b0 + j < nblk) A.block_counts[(int64_t)(b0 + j) * E + tid] = run;
-        run += v[j];
+        c += v[j];
+        before += b0 + j < blk ? v[j] : 0;
       }
     }
   }
-  finish_tables(A, c, off, wtot);
-}
-
-__global__ __launch_bounds__(SORT_THREADS) void sort_scatter_kernel(SortArgs A) {
-  __shared__ __attribute__((aligned(16))) uint8_t tab[SORT_WAVES][SORT_MAXE];
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const int E = A.E;
-  reinterpret_cast<uint4*>(&tab[0][0])[tid] = make_uint4(0, 0, 0, 0);   // 16 KiB = 1024 x 16 B
-  __syncthreads();
-  const int64_t p = (int64_t)blockIdx.x * SORT_THREADS + tid;
+  int off;
+  block_excl_scan(c, wtot, off);   // synchronises: tab is clear after it
+  if (tid < E) base[tid] = off + before;
+  if (blk == 0) finish_tables(A, c, off, wtot);
+  const int64_t p = (int64_t)blk * SORT_THREADS + tid;
   const bool valid = p < A.P;
   const int e = valid ? min(max(A.idx[p], 0), E - 1) : 0;
   const uint64_t m = match_key(e, valid, key_bits(E));
@@ -69,7 +56,7 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_scatter_kernel(SortArgs A) 
   if (valid && rank == 0) tab[wave][e] = (uint8_t)__popcll(m);
   __syncthreads();
   if (!valid) return;
-  int pos = A.block_counts[(int64_t)blockIdx.x * E + e] + rank;
+  int pos = base[e] + rank;
   for (int w = 0; w < wave; ++w) pos += tab[w][e];
   write_pair(A, p, e, pos);
 }
@@ -78,8 +65,8 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_one_kernel(SortArgs A) { so
 
 hipError_t launch_sort_rest(const SortArgs& a, hipStream_t st) {
   const int64_t nb = sort_blocks(a.P);
-  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(SORT_THREADS), 0, st, a, (int)nb);
-  if (nb > 0) hipLaunchKernelGGL(sort_scatter_kernel, dim3((unsigned)nb), dim3(SORT_THREADS), 0, st, a);
+  // block 0 writes the tables, so the launch has at least one block
+  hipLaunchKernelGGL(sort_rank_kernel, dim3((unsigned)(nb > 0 ? nb : 1)), dim3(SORT_THREADS), 0, st, a, (int)nb);
   return hipGetLastError();
 }
 

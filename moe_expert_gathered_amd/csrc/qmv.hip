@@ -78,10 +78,11 @@ MOEGQ_DEV void reduce_wave(float (&a)[V]) {
 // (measured faster there).  The down+combine kernel runs faster without it:
 // its arithmetic then starts as each row's loads land.
 // MR > 1: each pair has A.rows (<= MR) activation rows, x rows xrow * rows + r,
-// and every code a lane loads is applied to all of them (rows past A.rows
-// repeat the last one and are never stored).  acc then holds value
-// (m * MR + r) * RPW + rr for matrix m, activation row r, output row rr.
-template <int BITS, int GS, bool GLU, int RPW, int NS, bool SEL = true, int MR = 1,
+// and every code a lane loads is applied to the first MRC of them (rows past
+// A.rows repeat the last one and are never stored).  acc then holds value
+// (m * MR + r) * RPW + rr for matrix m, activation row r, output row rr; the
+// values of rows MRC .. MR - 1 stay zero (MR keeps V a power of two).
+template <int BITS, int GS, bool GLU, int RPW, int NS, bool SEL = true, int MR = 1, int MRC = MR,
           int V = RPW * (GLU ? 2 : 1) * MR>
 MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first, int step, float (&acc)[V]) {
   constexpr int NM = GLU ? 2 : 1;
@@ -102,13 +103,13 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
     rs[NM - 1] = make_rsrc(A.s1 + e * N * (int64_t)G, (uint32_t)N * G * 2);
     rb[NM - 1] = make_rsrc(A.b1 + e * N * (int64_t)G, (uint32_t)N * G * 2);
   }
-  __amdgpu_buffer_rsrc_t rx[MR];
+  __amdgpu_buffer_rsrc_t rx[MRC];
   if constexpr (MR == 1) {
     rx[0] = make_rsrc(A.x + xrow * (int64_t)K, (uint32_t)K * 2);
   } else {
     const int64_t nr = A.rows;
 #pragma unroll
-    for (int r = 0; r < MR; ++r)
+    for (int r = 0; r < MRC; ++r)
       rx[r] = make_rsrc(A.x + (xrow * nr + min((int64_t)r, nr - 1)) * (int64_t)K, (uint32_t)K * 2);
   }
 
@@ -122,7 +123,7 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
   const int n_it = (Kw + 255) / 256;
   constexpr uint32_t kNoFetch = 0x7FFFFFF0u;   // past every descriptor's range
   for (int it0 = first; it0 < n_it; it0 += step) {
-    uint4 c[NS][VC], xv[NS][MR][XV];
+    uint4 c[NS][VC], xv[NS][MRC][XV];
     uint16_t sv[NS][VC], bv[NS][VC];
     bool ok[NS];
 #pragma unroll
@@ -141,7 +142,7 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
           bv[t][m * RPW + r] = buf_load2(rb[m], ok[t] ? g2 : kNoFetch, row * G * 2);
         }
 #pragma unroll
-      for (int r = 0; r < MR; ++r)
+      for (int r = 0; r < MRC; ++r)
 #pragma unroll
         for (int j = 0; j < XV; ++j) xv[t][r][j] = buf_load16(rx[r], (uint32_t)(k0 + 8 * j) * 2, 0);
     }
@@ -183,10 +184,10 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
         }
       } else if (BITS == 4) {
         // several activation rows: each code pair is built once and applied to every row
-        uint32_t xp[MR][16];
-        float sx[MR];
+        uint32_t xp[MRC][16];
+        float sx[MRC];
 #pragma unroll
-        for (int r = 0; r < MR; ++r) {
+        for (int r = 0; r < MRC; ++r) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const uint4 v = xv[t][r][j];
@@ -202,16 +203,16 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
 #pragma unroll
         for (int i = 0; i < VC; ++i) {
           const uint32_t cw[4] = {c[t][i].x, c[t][i].y, c[t][i].z, c[t][i].w};
-          float d[MR];
+          float d[MRC];
 #pragma unroll
-          for (int r = 0; r < MR; ++r) d[r] = 0.f;
+          for (int r = 0; r < MRC; ++r) d[r] = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const uint32_t lo = cw[j] & 0x0F0F0F0Fu, hi = (cw[j] >> 4) & 0x0F0F0F0Fu;
             const uint32_t q0 = __builtin_amdgcn_perm(C43, lo, 0x04010400u), q1 = __builtin_amdgcn_perm(C43, lo, 0x04030402u);
             const uint32_t q2 = __builtin_amdgcn_perm(C43, hi, 0x04010400u), q3 = __builtin_amdgcn_perm(C43, hi, 0x04030402u);
 #pragma unroll
-            for (int r = 0; r < MR; ++r) {
+            for (int r = 0; r < MRC; ++r) {
               d[r] = fdot2_bf16(q0, xp[r][4 * j + 0], d[r]);
               d[r] = fdot2_bf16(q1, xp[r][4 * j + 1], d[r]);
               d[r] = fdot2_bf16(q2, xp[r][4 * j + 2], d[r]);
@@ -223,7 +224,7 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
           const float cb = fmaf(-128.f, s, b);
           const int m = i / RPW, rr = i % RPW;
 #pragma unroll
-          for (int r = 0; r < MR; ++r) {
+          for (int r = 0; r < MRC; ++r) {
             float& a = acc[(m * MR + r) * RPW + rr];
             a = fmaf(s, d[r], fmaf(cb, sx[r], a));
           }
@@ -255,9 +256,9 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
           acc[i] = fmaf(s, d, fmaf(b, sx, acc[i]));
         }
       } else {
-        float xf[MR][16], sx[MR];
+        float xf[MRC][16], sx[MRC];
 #pragma unroll
-        for (int r = 0; r < MR; ++r) {
+        for (int r = 0; r < MRC; ++r) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const uint32_t d4[4] = {xv[t][r][j].x, xv[t][r][j].y, xv[t][r][j].z, xv[t][r][j].w};
@@ -271,15 +272,15 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
 #pragma unroll
         for (int i = 0; i < VC; ++i) {
           const uint32_t cw[4] = {c[t][i].x, c[t][i].y, c[t][i].z, c[t][i].w};
-          float d[MR];
+          float d[MRC];
 #pragma unroll
-          for (int r = 0; r < MR; ++r) d[r] = 0.f;
+          for (int r = 0; r < MRC; ++r) d[r] = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float q0 = (float)((cw[j] >> 0) & 0xFFu), q1 = (float)((cw[j] >> 8) & 0xFFu);
             const float q2 = (float)((cw[j] >> 16) & 0xFFu), q3 = (float)((cw[j] >> 24) & 0xFFu);
 #pragma unroll
-            for (int r = 0; r < MR; ++r) {
+            for (int r = 0; r < MRC; ++r) {
               d[r] = fmaf(q0, xf[r][4 * j + 0], d[r]);
               d[r] = fmaf(q1, xf[r][4 * j + 1], d[r]);
               d[r] = fmaf(q2, xf[r][4 * j + 2], d[r]);
@@ -290,7 +291,7 @@ MOEGQ_DEV void qmv_rows(const QmvArgs& A, int64_t p, int n0, int lane, int first
           const float b = (!SEL || ok[t]) ? bf16_to_f32(bv[t][i]) : 0.f;
           const int m = i / RPW, rr = i % RPW;
 #pragma unroll
-          for (int r = 0; r < MR; ++r) {
+          for (int r = 0; r < MRC; ++r) {
             float& a = acc[(m * MR + r) * RPW + rr];
             a = fmaf(s, d[r], fmaf(b, sx[r], a));
           }
@@ -325,7 +326,7 @@ MOEGQ_DEV bool reduce_waves(float (&acc)[V], int lane, int wave) {
 // chunks w, w + S, .. of K (S > 1 when the grid alone would not keep enough
 // loads in flight: few pairs, few rows).  MR > 1: the pair's A.rows (<= MR)
 // activation rows share every code the waves load (qmv_rows).
-template <int BITS, int GS, bool GLU, int RPW, int NS, int S, int MR = 1>
+template <int BITS, int GS, bool GLU, int RPW, int NS, int S, int MR = 1, int MRC = MR>
 __global__ __launch_bounds__(64 * S) void qmv_kernel(QmvArgs A, int64_t p_base) {
   constexpr int V = RPW * (GLU ? 2 : 1) * MR;
   const int lane = threadIdx.x & 63;
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(64 * S) void qmv_kernel(QmvArgs A, int64_t p_base) 
     }
   }
   float acc[V];
-  qmv_rows<BITS, GS, GLU, RPW, NS, true, MR>(A, p, n0, lane, wave * NS, S * NS, acc);
+  qmv_rows<BITS, GS, GLU, RPW, NS, true, MR, MRC>(A, p, n0, lane, wave * NS, S * NS, acc);
   if (!reduce_waves<S>(acc, lane, wave)) return;
   // lane 16*r (r = 2*bit5 + bit4) holds values r*V/4 .. r*V/4 + V/4 - 1
   if (GLU) {
@@ -552,38 +553,41 @@ hipError_t launch_qmv_combine(const QmvArgs& a_in, int bits, int gs, const uint1
 // are too few to cover the memory latency.
 constexpr int64_t kQmvWaves = 4096;
 
-template <int BITS, int GS, bool GLU, int RPW, int NS, int S, int MR = 1>
+template <int BITS, int GS, bool GLU, int RPW, int NS, int S, int MR = 1, int MRC = MR>
 static void launch_qmv_cfg(const QmvArgs& a, int64_t P, hipStream_t st) {
   const unsigned nrb = (unsigned)((a.N + RPW - 1) / RPW);
   for (int64_t p0 = 0; p0 < P; p0 += 65535) {
     dim3 grid(nrb, (unsigned)(P - p0 < 65535 ? P - p0 : 65535));
-    hipLaunchKernelGGL((qmv_kernel<BITS, GS, GLU, RPW, NS, S, MR>), grid, dim3(64 * S), 0, st, a, p0);
+    hipLaunchKernelGGL((qmv_kernel<BITS, GS, GLU, RPW, NS, S, MR, MRC>), grid, dim3(64 * S), 0, st, a, p0);
   }
 }
 
 // 2..4 activation rows per pair: one chunk of codes at a time (the rows'
-// activations take the registers a second chunk would), 2 (GLU) or 4 output
-// rows per wave, K split over up to 4 waves when the grid is small
-template <int BITS, int GS, bool GLU, int MR>
+// activations take the registers a second chunk would), 2 (GLU; one row of
+// each matrix per wave was slower) or 4 output rows per wave, K split over up
+// to 4 waves when the grid is small.  3 rows compute 3 and keep the 4-row
+// layout.
+template <int BITS, int GS, bool GLU, int MR, int MRC>
 static hipError_t launch_qmv_rows_t(const QmvArgs& a, int64_t P, hipStream_t st) {
   if (GLU) {
-    launch_qmv_cfg<BITS, GS, true, 2, 1, 1, MR>(a, P, st);
+    launch_qmv_cfg<BITS, GS, true, 2, 1, 1, MR, MRC>(a, P, st);
     return hipGetLastError();
   }
   const int n_it = (a.K * BITS / 32 + 255) / 256;
   const int64_t w4 = (int64_t)((a.N + 3) / 4) * P;
   int S = 1;
   while (S < 4 && 2 * S <= n_it && w4 * S < kQmvWaves) S *= 2;
-  if (S == 4) launch_qmv_cfg<BITS, GS, false, 4, 1, 4, MR>(a, P, st);
-  else if (S == 2) launch_qmv_cfg<BITS, GS, false, 4, 1, 2, MR>(a, P, st);
-  else launch_qmv_cfg<BITS, GS, false, 4, 1, 1, MR>(a, P, st);
+  if (S == 4) launch_qmv_cfg<BITS, GS, false, 4, 1, 4, MR, MRC>(a, P, st);
+  else if (S == 2) launch_qmv_cfg<BITS, GS, false, 4, 1, 2, MR, MRC>(a, P, st);
+  else launch_qmv_cfg<BITS, GS, false, 4, 1, 1, MR, MRC>(a, P, st);
   return hipGetLastError();
 }
 
 template <int BITS, int GS, bool GLU>
 static hipError_t launch_qmv_t(const QmvArgs& a, int64_t P, hipStream_t st) {
-  if (a.rows > 1) return a.rows <= 2 ? launch_qmv_rows_t<BITS, GS, GLU, 2>(a, P, st)
-                                     : launch_qmv_rows_t<BITS, GS, GLU, 4>(a, P, st);
+  if (a.rows > 1) return a.rows == 2   ? launch_qmv_rows_t<BITS, GS, GLU, 2, 2>(a, P, st)
+                         : a.rows == 3 ? launch_qmv_rows_t<BITS, GS, GLU, 4, 3>(a, P, st)
+                                       : launch_qmv_rows_t<BITS, GS, GLU, 4, 4>(a, P, st);
   const int Kw = a.K * BITS / 32;
   const int n_it = (Kw + 255) / 256;
   const bool two = Kw > 256 && Kw <= 512 && (GLU || BITS == 4);   // the whole row in one chunk of 2 slices

@@ -240,10 +240,11 @@ def decode_cold_leg(torch, m, synth, reps=20, M=1, cfg=1, flush_bytes=1 << 30):
 
 
 def ceilings_leg(torch, m, reps=10):
-    """Measured ceilings: a plain streaming read of 2 GiB (128-bit loads, 8
-    workgroups of 256 threads per compute unit) and a plain bf16 MFMA loop
-    (8 independent v_mfma_f32_16x16x32_bf16 chains per wave, 2 workgroups of
-    4 waves per compute unit)."""
+    """Measured ceilings: a plain streaming read of 2 GiB (128-bit loads, 4, 8
+    and 16 workgroups of 256 threads per compute unit), the same read at the
+    byte counts of single products, and a plain bf16 MFMA loop (8 independent
+    v_mfma_f32_16x16x32_bf16 chains per wave, 1 and 2 workgroups of 4 waves
+    per compute unit)."""
     dev = torch.device("cuda")
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     nbytes = 2 << 30
@@ -254,6 +255,25 @@ def ceilings_leg(torch, m, reps=10):
     for per_cu in (4, 8, 16):
         st = graph_stats(torch, lambda i: m.probe_stream_read(buf, per_cu * cus, sink), 1, reps=reps)
         res[f"stream_read_{per_cu}wg_per_cu"] = {"us": st.as_dict(), "tb_s": nbytes / (st.median * 1e-6) / 1e12}
+    # the same read at the byte counts of single products, one launch per
+    # product-sized slice of the 2 GiB buffer in one graph (the slices cycle
+    # through 8x the 256 MB memory-side cache, so each launch reads HBM), with
+    # one 4-load pass per thread or 8 grid-stride workgroups per compute unit
+    sizes = {"dense_o_2560x4096": 5898240, "dense_qkv_6144x2560": 8847360, "dense_down_2560x9728": 14008320,
+             "dense_gate_up_2x9728x2560": 28016640, "decode_down_8x4096x2048": 37748736,
+             "decode_gate_up_16x2048x4096": 75497472}
+    by_size = {}
+    for name, size in sizes.items():
+        stride = (size + 4095) // 4096 * 4096
+        n = min(64, nbytes // stride)
+        one_pass = -(-size // (16 * 4 * 256))
+        row = {"bytes": size, "launches_per_graph": n}
+        for label, blocks in (("one_pass", one_pass), ("8wg_per_cu", 8 * cus)):
+            st = graph_stats(torch, lambda i: m.probe_stream_read(buf[i * stride:i * stride + size], blocks, sink), n,
+                             reps=reps)
+            row[label] = {"blocks": blocks, "us": st.as_dict(), "tb_s": size / (st.median * 1e-6) / 1e12}
+        by_size[name] = row
+    res["stream_read_by_size"] = by_size
     del buf
     out = torch.zeros(1, dtype=torch.float32, device=dev)
     iters = 4096

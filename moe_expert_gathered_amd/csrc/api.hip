@@ -29,8 +29,14 @@ int status_of(hipError_t e) { return e == hipSuccess ? MOEGQ_OK : MOEGQ_ERR_LAUN
 // lie beyond that range: one matrix of codes stays at most 0x7FFFFFF0 bytes.
 constexpr int64_t kNoFetchOffset = 0x7FFFFFF0;
 bool one_row_fits(int64_t N, int64_t K, int bits) { return N * K * bits / 8 <= kNoFetchOffset; }
-// most activation rows per pair on the vector kernel (more go to the matrix cores)
-constexpr int64_t kQmvRowsMax = 4;
+// most activation rows per pair on the vector kernel (more go to the matrix
+// cores): 4, and 2 for 4-bit GLU pairs when the matrix-core kernel takes the
+// shape (it runs a 4-bit GLU pair of 3-16 rows at about the cost of 2 rows on
+// the vector kernel: 12.8-13.6 us for 2 x 9728 x 2560, against 16.6 at 3 rows
+// and 18.5 at 4 on the vector kernel).  Plain products, and 8-bit GLU pairs
+// (twice the code bytes per matrix-core step), stay on the vector kernel to
+// 4 rows: 6.2 against 8.2 us for 2560 x 4096 at 4 rows.
+constexpr int64_t kQmvRowsMax = 4, kQmvRowsMaxGlu4 = 2;
 
 // bit width / group size / quantized length checks
 int check_quant(int64_t K, int gs, int bits) {
@@ -202,16 +208,23 @@ __global__ void offsets_from_sorted_kernel(const int32_t* rhs, int64_t P, int E,
   offsets[e] = (int32_t)lo;
 }
 
-// few rows per pair (M <= 16): up to 4 rows the matrix-vector kernel with
-// every code applied to all the rows; else the exact-code matrix-core kernel
-// when K is a multiple of 128 and the scales and biases start 8-byte aligned
-// (K split over workgroups when ws holds its scratch: [counters | partials],
-// counters zero before the first call), else the fp16-operand kernel
+// few rows per pair (M <= 16): up to 4 rows (2 for 4-bit GLU pairs the
+// matrix-core kernel takes) the matrix-vector kernel with every code applied to all the
+// rows; else the exact-code matrix-core kernel when K is a multiple of 128 and
+// the scales and biases start 8-byte aligned (K split over workgroups when ws
+// holds its scratch: [counters | partials], counters zero before the first
+// call), else the fp16-operand kernel
 size_t few_ws_bytes(const FewPlan& pl) { return pl.KS > 1 ? align256(pl.counter_bytes) + pl.part_bytes : 0; }
 int few_rows(const SkinnyArgs& sa, bool glu, int64_t P, int bits, int gs, void* ws, size_t wsb, hipStream_t s) {
-  if (sa.M <= kQmvRowsMax && sa.K <= kMaxQmvK && one_row_fits(sa.N, sa.K, bits)) {
-    // 2..4 rows: the vector kernel with every code applied to all the pair's
-    // rows (its many one-wave workgroups keep more loads in flight than the
+  // the matrix-core kernel reads a chunk's scales and biases as one 32- or
+  // 64-bit word: their arrays must start 8-byte aligned
+  auto a8 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7u) == 0; };
+  const bool sb_ok = a8(sa.s0) && a8(sa.b0) && (!glu || (a8(sa.s1) && a8(sa.b1)));
+  const bool few_ok = fewrow_supported(sa.M, sa.N, sa.K, bits) && sb_ok;
+  const int64_t qmax = glu && bits == 4 && few_ok ? kQmvRowsMaxGlu4 : kQmvRowsMax;
+  if (sa.M <= qmax && sa.K <= kMaxQmvK && one_row_fits(sa.N, sa.K, bits)) {
+    // the vector kernel with every code applied to all the pair's rows (its
+    // many one-wave workgroups keep more loads in flight than the
     // matrix-core kernel's few four-wave ones)
     QmvArgs a{};
     a.x = sa.x; a.lhs = sa.lhs; a.lhs_div = sa.lhs_div; a.rhs = sa.rhs;
@@ -219,11 +232,7 @@ int few_rows(const SkinnyArgs& sa, bool glu, int64_t P, int bits, int gs, void* 
     a.N = sa.N; a.K = sa.K; a.out = sa.out; a.residual = sa.residual; a.rows = sa.M;
     return status_of(launch_qmv(a, bits, gs, glu, P, s));
   }
-  // the matrix-core kernel reads a chunk's scales and biases as one 32- or
-  // 64-bit word: their arrays must start 8-byte aligned
-  auto a8 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7u) == 0; };
-  const bool sb_ok = a8(sa.s0) && a8(sa.b0) && (!glu || (a8(sa.s1) && a8(sa.b1)));
-  if (!fewrow_supported(sa.M, sa.N, sa.K, bits) || !sb_ok) return status_of(launch_skinny(sa, bits, gs, glu, P, s));
+  if (!few_ok) return status_of(launch_skinny(sa, bits, gs, glu, P, s));
   FewPlan pl = fewrow_plan(P, sa.N, sa.K, glu, ws != nullptr);
   if (few_ws_bytes(pl) > wsb || (pl.KS > 1 && !aligned16(ws))) pl = fewrow_plan(P, sa.N, sa.K, glu, false);
   FewArgs f{};

@@ -21,9 +21,11 @@
 // workgroup (4 waves) owns 16 * NB columns of one pair and a range of
 // 128-wide K chunks, its waves taking interleaved chunks with the loads of
 // the next DEPTH chunks in flight; the waves' partial sums meet in LDS.
-// Loads are buffer loads: the pair's rows and expert matrices in the
-// descriptors, the lane's row or column as a 32-bit offset, the chunk as a
-// wave-uniform one.  With KS > 1 splits along K, each workgroup stores its
+// Loads are buffer loads (the pair's rows and expert matrices in the
+// descriptors, the chunk as a wave-uniform offset), coalesced: neighbouring
+// lanes read neighbouring bytes of one row, and each wave passes its chunk
+// through a staging area in LDS into the layout above.  With KS > 1 splits
+// along K, each workgroup stores its
 // fp32 partial and the last one of a column group to finish (counted with one
 // atomic per workgroup) adds the KS partials in split order and writes the
 // output, so the result does not depend on timing; it leaves its counter at
@@ -62,6 +64,9 @@ __global__ __launch_bounds__(256) void fewrow_kernel(FewArgs A) {
   constexpr float OFS = BITS == 4 ? 128.f : 0.f;       // code offset of the bf16 operand
   constexpr int SPG = GS / 32;                         // MFMA steps per group
   __shared__ f32x4_t red[3][NM][NB][64];
+  constexpr int PPR = 4 * (BITS / 4);                  // 16-byte code pieces per row and chunk
+  constexpr int XS = 16 * 16, CS = NM * NB * 16 * PPR; // a wave's staging area, in pieces
+  __shared__ uint4 few_stage[4 * (XS + CS)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
@@ -77,12 +82,18 @@ __global__ __launch_bounds__(256) void fewrow_kernel(FewArgs A) {
 
   const int64_t xb = A.lhs ? (int64_t)A.lhs[p] : p / A.lhs_div;
   const int64_t e = A.rhs ? (int64_t)A.rhs[p] : 0;
-  // Buffer descriptors over this pair's activation rows and expert matrices;
-  // per lane a 32-bit offset (its row / column), per chunk a wave-uniform
-  // offset.  Activation rows past M read row M - 1: their MFMA output rows
-  // are never stored.  Columns past N read column N - 1 (likewise).
+  // Buffer descriptors over this pair's activation rows and expert matrices.
+  // Loads are coalesced (neighbouring lanes read neighbouring bytes of one
+  // row) and pass through LDS into the MFMA layout, where the 16 lanes of a
+  // lane group hold 16 different rows: loaded in that layout directly, every
+  // 16-lane pass of every load touched 16 rows, and the loads' address
+  // processing, not HBM, set the kernel's time.  Activation rows past M read
+  // row M - 1 and columns past N column N - 1: their outputs are never stored.
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(A.x + xb * M * (int64_t)K, (uint32_t)(M * K * 2));
-  const uint32_t vx = (uint32_t)(min(r, M - 1) * K * 2 + 16 * g);
+  // activations, load i: row 4 i + lane / 16, 16-byte piece lane % 16 of the chunk's 256 bytes
+  uint32_t vx[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vx[i] = (uint32_t)(min(4 * i + (lane >> 4), M - 1) * K * 2 + 16 * (lane & 15));
   __amdgpu_buffer_rsrc_t rw[NM], rs[NM], rb[NM];
   {
     const uint32_t wbytes = (uint32_t)((int64_t)N * Kw * 4), sbytes = (uint32_t)((int64_t)N * G * 2);
@@ -95,13 +106,21 @@ __global__ __launch_bounds__(256) void fewrow_kernel(FewArgs A) {
       rb[NM - 1] = make_rsrc(A.b1 + e * N * (int64_t)G, sbytes);
     }
   }
-  uint32_t vw[NB], vs[NB];
+  // codes of column block b: row lane / 4, 16-byte piece lane % 4 of the
+  // row's chunk (and piece 4 + lane % 4 at 8 bits)
+  uint32_t vw[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int n = min(n0 + 16 * b + r, N - 1);
-    vw[b] = (uint32_t)(n * Kw * 4 + 4 * BITS * g);       // k = 32 g of the chunk
-    vs[b] = (uint32_t)(n * G * 2);
-  }
+  for (int b = 0; b < NB; ++b)
+    vw[b] = (uint32_t)(min(n0 + 16 * b + (lane >> 2), N - 1) * Kw * 4 + 16 * (lane & 3));
+  // scales and biases: in scale load i, lane group g takes combination
+  // k = 4 i + g of (array, matrix, column block b = k % NB), column
+  // n0 + 16 b + r; stage() hands each lane its column's values with
+  // ds_bpermute.  Lane groups of one load that read different matrices
+  // issue their own buffer loads (the other lanes at an offset past the
+  // range: nothing fetched, zeros).
+  constexpr int NCOMB = NM * NB * 2, NSI = (NCOMB + 3) / 4;
+  static_assert(NB == 1 || NB == 2, "one or two column blocks per workgroup");
+  const uint32_t vsb = (uint32_t)(min(n0 + 16 * (g % NB) + r, N - 1) * G * 2);
   // the residual values of the lane's outputs, requested before the K loop
   uint32_t res_in[NB][4] = {};
   if (!GLU && A.residual) {
@@ -120,40 +139,106 @@ __global__ __launch_bounds__(256) void fewrow_kernel(FewArgs A) {
   const uint32_t one2 = 0x3F803F80u;                     // bf16 (1, 1)
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(one2, one2, one2, one2));
 
-  // one chunk's operands.  Lane (g, r) loads its column's codes of k in
-  // [32 g, 32 g + 32) of the chunk as 128-bit words (one per column block
-  // at 4 bits, two at 8 bits: the four lane groups cover a column's chunk in
-  // one contiguous piece); a 4 x 4 transpose across the lane groups then
-  // gives it the codes of k = 32 s + 8 g + (0..7) for each MFMA step s.
+  // one chunk's loads, as loaded (coalesced); stage() turns them into the
+  // MFMA layout: lane (g, r) then holds activation row r's k in [32 s + 8 g,
+  // + 8) for step s, and its column's codes of k in [32 g, 32 g + 32) of the
+  // chunk (one 128-bit word at 4 bits, two at 8 bits; a 4 x 4 transpose
+  // across the lane groups then gives it the codes of k = 32 s + 8 g + (0..7)
+  // for each MFMA step s).
   struct Chunk {
-    uint4 xv[4];                         // activations of steps 0..3
-    uint4 cw[NM][NB][BITS / 4];          // codes as loaded
-    uint32_t sv[NM][NB][SW], bv[NM][NB][SW];   // the chunk's bf16 scales / biases, two per word
+    uint4 xl[4];                          // activations: 4 rows per load
+    uint4 cl[NM][NB][BITS / 4];           // codes: 16 rows per load
+    uint32_t sl[NSI][SW];                 // scale / bias combinations, two bf16 per word
   };
-  // chunk c's loads (none past the split's end: the chunk is then never used)
+  struct Operands {
+    uint4 xv[4];
+    uint4 cw[NM][NB][BITS / 4];
+    uint32_t sv[NM][NB][SW], bv[NM][NB][SW];
+  };
+  // chunk c's loads.  A chunk past the split's end (never computed) loads at
+  // a lane offset beyond every descriptor's range, which returns zeros
+  // without fetching, rather than being skipped: with no load under a branch the compiler's wait counts
+  // stay exact, so computing one chunk waits for that chunk's loads only.
   auto load = [&](int c, Chunk& d) {
-    if (c >= c_hi) return;
-    const uint32_t ox = (uint32_t)c * FR_CK * 2, ow = (uint32_t)c * FR_CK * BITS / 8;
-    const uint32_t os = (uint32_t)(c * FR_CK / GS) * 2;
+    constexpr uint32_t kNoFetch = 0x7FFFFFF0u;
+    const bool live = c < c_hi;
+    const uint32_t ox = live ? (uint32_t)c * FR_CK * 2 : 0u, ow = live ? (uint32_t)c * FR_CK * BITS / 8 : 0u;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) d.xv[s] = buf_load16(rx, vx + 64 * s, ox);
+    for (int i = 0; i < 4; ++i) d.xl[i] = buf_load16(rx, live ? vx[i] : kNoFetch, ox);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int h = 0; h < BITS / 4; ++h) d.cl[m][b][h] = buf_load16(rw[m], live ? vw[b] + 64 * h : kNoFetch, ow);
+    const uint32_t os = live ? (uint32_t)(c * NGC) * 2 : 0u;
+#pragma unroll
+    for (int i = 0; i < NSI; ++i) {
+#pragma unroll
+      for (int w = 0; w < SW; ++w) d.sl[i][w] = 0u;
+#pragma unroll
+      for (int dd = 0; dd < 2 * NM; ++dd) {             // descriptor: array dd / NM, matrix dd % NM
+        if (dd * NB > 4 * i + 3 || (dd + 1) * NB <= 4 * i) continue;   // no lane of this load reads it
+        const int k = 4 * i + g;
+        const __amdgpu_buffer_rsrc_t rd = dd / NM ? rb[dd % NM] : rs[dd % NM];
+        const uint32_t vo = (live && k < NCOMB && k / NB == dd) ? vsb : kNoFetch;
+        if (NGC == 4) {
+          const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rd, vo, os, 0);
+          d.sl[i][0] |= v2[0];
+          d.sl[i][SW - 1] |= v2[1];
+        } else if (NGC == 2) {
+          d.sl[i][0] |= __builtin_amdgcn_raw_buffer_load_b32(rd, vo, os, 0);
+        } else {
+          d.sl[i][0] |= __builtin_amdgcn_raw_buffer_load_b16(rd, vo, os, 0);
+        }
+      }
+    }
+  };
+  // the wave's staging area: the chunk's activations (16 rows of 16 pieces)
+  // then its codes (NM x NB blocks of 16 rows of PPR pieces), 16 bytes a
+  // piece, each row's pieces permuted so that both the coalesced writes and
+  // the MFMA-layout reads (16 rows at one piece) are free of bank conflicts
+  uint4* stg = few_stage + wave * (XS + CS);
+  auto csw = [](int row) { return BITS == 4 ? (row >> 2) & 3 : ((row >> 1) & 3) << 1; };
+  auto stage = [&](const Chunk& d, Operands& o) {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the previous chunk's reads came first
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * i + (lane >> 4), q = lane & 15;
+      stg[row * 16 + (q ^ row)] = d.xl[i];
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int h = 0; h < BITS / 4; ++h) {
+          const int row = lane >> 2, pc = 4 * h + (lane & 3);
+          stg[XS + ((m * NB + b) * 16 + row) * PPR + (pc ^ csw(row))] = d.cl[m][b][h];
+        }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int s = 0; s < 4; ++s) o.xv[s] = stg[r * 16 + ((4 * s + g) ^ r)];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int h = 0; h < BITS / 4; ++h) {
+          const int pc = BITS == 4 ? g : 2 * g + h;
+          o.cw[m][b][h] = stg[XS + ((m * NB + b) * 16 + r) * PPR + (pc ^ csw(r))];
+        }
+    // scale and bias of the lane's column: combination k sits in load k / 4
+    // at lane 16 (k % 4) + r
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
+        const int ks = m * NB + b, kb = (NM + m) * NB + b;
 #pragma unroll
-        for (int h = 0; h < BITS / 4; ++h) d.cw[m][b][h] = buf_load16(rw[m], vw[b] + 16 * h, ow);
-        if (NGC == 4) {
-          const auto sv2 = __builtin_amdgcn_raw_buffer_load_b64(rs[m], vs[b], os, 0);
-          const auto bv2 = __builtin_amdgcn_raw_buffer_load_b64(rb[m], vs[b], os, 0);
-          d.sv[m][b][0] = sv2[0]; d.sv[m][b][SW - 1] = sv2[1];
-          d.bv[m][b][0] = bv2[0]; d.bv[m][b][SW - 1] = bv2[1];
-        } else if (NGC == 2) {
-          d.sv[m][b][0] = __builtin_amdgcn_raw_buffer_load_b32(rs[m], vs[b], os, 0);
-          d.bv[m][b][0] = __builtin_amdgcn_raw_buffer_load_b32(rb[m], vs[b], os, 0);
-        } else {
-          d.sv[m][b][0] = __builtin_amdgcn_raw_buffer_load_b16(rs[m], vs[b], os, 0);
-          d.bv[m][b][0] = __builtin_amdgcn_raw_buffer_load_b16(rb[m], vs[b], os, 0);
+        for (int w = 0; w < SW; ++w) {
+          o.sv[m][b][w] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * (ks % 4) + r) * 4, (int)d.sl[ks / 4][w]);
+          o.bv[m][b][w] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * (kb % 4) + r) * 4, (int)d.sl[kb / 4][w]);
         }
       }
   };
@@ -176,7 +261,7 @@ __global__ __launch_bounds__(256) void fewrow_kernel(FewArgs A) {
       return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
     }
   };
-  auto compute = [&](const Chunk& d) {
+  auto compute = [&](const Operands& d) {
     // st[m][b][s]: the lane's codes for step s (one word at 4 bits, two at 8)
     uint32_t st[NM][NB][4][BITS / 4];
 #pragma unroll
@@ -238,16 +323,23 @@ __global__ __launch_bounds__(256) void fewrow_kernel(FewArgs A) {
   };
   // chunk c of the split belongs to wave (c - c_lo) % 4; the loads of the
   // wave's next DEPTH chunks are in flight while one is computed (a ring of
-  // DEPTH + 1 buffers, unrolled so that every buffer index is static)
+  // DEPTH + 1 buffers, unrolled so that every buffer index is static; the
+  // scheduling barriers keep each chunk's loads in ring order)
   Chunk buf[DEPTH + 1];
 #pragma unroll
-  for (int i = 0; i < DEPTH; ++i) load(c_lo + wave + 4 * i, buf[i]);
+  for (int i = 0; i < DEPTH; ++i) {
+    load(c_lo + wave + 4 * i, buf[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   for (int c = c_lo + wave; c < c_hi; c += 4 * (DEPTH + 1)) {
 #pragma unroll
     for (int i = 0; i <= DEPTH; ++i) {
+      load(c + 4 * (i + DEPTH), buf[(i + DEPTH) % (DEPTH + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
       if (c + 4 * i < c_hi) {
-        load(c + 4 * (i + DEPTH), buf[(i + DEPTH) % (DEPTH + 1)]);
-        compute(buf[i]);
+        Operands o;
+        stage(buf[i], o);
+        compute(o);
       }
     }
   }
@@ -344,7 +436,10 @@ constexpr int64_t kFewMinChunks = 2;
 
 FewPlan fewrow_plan(int64_t P, int64_t N, int64_t K, bool glu, bool split_allowed) {
   FewPlan pl{};
-  pl.NB = 2;
+  // GLU products take one 16-column block per workgroup (twice the
+  // workgroups; 13.4 against 15.4 us for the 16-row 2 x 9728 x 2560 gate/up),
+  // plain products two (one block measured equal or slower there)
+  pl.NB = glu ? 1 : 2;
   const int64_t ncg = (N + 16 * pl.NB - 1) / (16 * pl.NB);
   const int64_t nchunk = K / FR_CK;
   const int64_t items = P * ncg;
@@ -373,20 +468,23 @@ template <int BITS, bool GLU>
 constexpr int few_depth() { return GLU ? (BITS == 8 ? 1 : 2) : (BITS == 8 ? 2 : 3); }
 
 template <int BITS, int GS, bool GLU>
-static hipError_t launch_few_t(const FewArgs& a, int64_t items, int KS, hipStream_t st) {
-  hipLaunchKernelGGL((fewrow_kernel<BITS, GS, GLU, 2, few_depth<BITS, GLU>()>), dim3((unsigned)items, (unsigned)KS),
-                     dim3(256), 0, st, a);
+static hipError_t launch_few_t(const FewArgs& a, int64_t items, int KS, int NB, hipStream_t st) {
+  constexpr int D = few_depth<BITS, GLU>();
+  if (NB == 1)
+    hipLaunchKernelGGL((fewrow_kernel<BITS, GS, GLU, 1, D>), dim3((unsigned)items, (unsigned)KS), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((fewrow_kernel<BITS, GS, GLU, 2, D>), dim3((unsigned)items, (unsigned)KS), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fewrow(const FewArgs& a, const FewPlan& pl, int bits, int gs, bool glu, hipStream_t st) {
   if (pl.items <= 0) return hipSuccess;
-  if (pl.items >= ((int64_t)1 << 31) || pl.KS > 65535 || pl.NB != 2) return hipErrorInvalidValue;
+  if (pl.items >= ((int64_t)1 << 31) || pl.KS > 65535 || (pl.NB != 1 && pl.NB != 2)) return hipErrorInvalidValue;
   FewArgs b = a;
   b.cps = pl.cps;
 #define MOEGQ_FEW(B, G)                                                                                 \
   if (bits == B && gs == G)                                                                             \
-    return glu ? launch_few_t<B, G, true>(b, pl.items, pl.KS, st) : launch_few_t<B, G, false>(b, pl.items, pl.KS, st);
+    return glu ? launch_few_t<B, G, true>(b, pl.items, pl.KS, pl.NB, st) : launch_few_t<B, G, false>(b, pl.items, pl.KS, pl.NB, st);
   MOEGQ_FEW(4, 32) MOEGQ_FEW(4, 64) MOEGQ_FEW(4, 128) MOEGQ_FEW(8, 32) MOEGQ_FEW(8, 64) MOEGQ_FEW(8, 128)
 #undef MOEGQ_FEW
   return hipErrorInvalidValue;

@@ -1,9 +1,11 @@
-"""GPU parity of the vector kernel with 2-4 activation rows per weight matrix
-(every code it loads applied to all the rows) against the oracle: dense
-affine_qmm with and without the residual, the GLU pair, and gather_qmm with
-several rows per pair; both code widths, every group size, ragged output
-rows, K of one partial and of several 256-word slices, 3 rows (one padded
-row in the kernel)."""
+"""GPU parity of the products with 2-4 activation rows per weight matrix
+against the oracle: the vector kernel (every code it loads applied to all
+the rows) for dense affine_qmm with and without the residual, GLU pairs of 2
+rows and of 3-4 rows at 8 bits or with a K the matrix-core kernel does not
+take, and gather_qmm with several rows per pair; the matrix-core kernel for
+4-bit GLU pairs of 3-4 rows.  Both code widths, every group size, ragged
+output rows, K of one partial and of several 256-word slices, 3 rows (one
+padded row in the vector kernel)."""
 import numpy as np
 import pytest
 import torch
@@ -46,9 +48,15 @@ def test_affine_qmm_rows(mg, M, bits, gs, N, K):
 
 @pytest.mark.parametrize("M", [2, 3, 4])
 @pytest.mark.parametrize("bits,gs", [(4, 64), (8, 128), (4, 32)])
-def test_affine_qmm_glu_rows(mg, M, bits, gs):
-    g = np.random.default_rng(70 + M + bits + gs)
-    N, K = 150, 2560
+@pytest.mark.parametrize("K", [2560, 2624])
+def test_affine_qmm_glu_rows(mg, M, bits, gs, K):
+    """GLU pairs: at 4 bits K = 2560 sends 3 and 4 rows to the matrix-core
+    kernel, K = 2624 (not a multiple of 128) keeps them on the vector kernel;
+    8-bit pairs stay on the vector kernel."""
+    if K % gs:
+        pytest.skip("K must be a multiple of the group size")
+    g = np.random.default_rng(70 + M + bits + gs + K)
+    N = 150
     gate = synth.drawn_matrix(g, N, K, gs, bits)
     up = synth.drawn_matrix(g, N, K, gs, bits)
     x = synth.to_bf16(g.standard_normal((M, K)))

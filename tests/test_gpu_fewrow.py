@@ -2,14 +2,14 @@
 exact-code matrix-core kernel, with K split over workgroups through a
 workspace: against the oracle within tolerance, bit for bit on
 integer-exact inputs, repeatable bit for bit, and leaving the workspace's
-counters at zero."""
+counters at zero; gathered pairs with several rows each."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth
-from helpers import assert_parity, bf, host_bf, words
+from helpers import assert_parity, bf, host_bf, i32, words
 
 pytestmark = pytest.mark.gpu
 
@@ -23,8 +23,9 @@ def mg():
     return m
 
 
-def _counters_zero(ws, N):
-    items = -(-N // 32)
+def _counters_zero(ws, N, glu=False):
+    # one counter per column group: 16 columns for GLU pairs, 32 otherwise
+    items = -(-N // (16 if glu else 32))
     return not bool(ws[:4 * items].view(torch.int32).any())
 
 
@@ -81,7 +82,7 @@ def test_split_k_glu(mg, M, bits, gs):
     tr = lambda m: (words(m[0]), bf(m[1]), bf(m[2]))
     got = mg.affine_qmm_glu(bf(x), tr(gate), tr(up), group_size=gs, bits=bits, workspace=ws)
     assert_parity(host_bf(got), want, name=f"glu split M={M}")
-    assert _counters_zero(ws, N)
+    assert _counters_zero(ws, N, glu=True)
 
 
 def test_dense_shape_split(mg):
@@ -97,3 +98,33 @@ def test_dense_shape_split(mg):
     want = oracle.quantized_matmul(x, w[cols], s[cols], b[cols], True, 64, 4)
     assert_parity(got[:, cols], want, name="down shape")
     assert _counters_zero(ws, N)
+
+
+def _expert_set(g, E, N, K, gs, bits):
+    mats = [synth.drawn_matrix(g, N, K, gs, bits) for _ in range(E)]
+    return tuple(np.stack([m[i] for m in mats]) for i in range(3))
+
+
+@pytest.mark.parametrize("M", [3, 5, 16])
+@pytest.mark.parametrize("bits,gs", [(4, 64), (8, 128), (4, 32)])
+def test_gathered_few_rows(mg, M, bits, gs):
+    """gather_qmm and gather_qmm_glu with M rows per pair, explicit lhs and rhs
+    (one x batch used twice, one expert twice), ragged N: the matrix-core
+    kernel gathering each pair's rows and expert (GLU pairs from 3 rows at 4
+    bits, plain products from 5)."""
+    g = np.random.default_rng(900 + M + bits + gs)
+    E, N, K = 5, 72, 1024
+    w, s, b = _expert_set(g, E, N, K, gs, bits)
+    wu, su, bu = _expert_set(g, E, N, K, gs, bits)
+    x = synth.to_bf16(g.standard_normal((6, M, K)))
+    lhs, rhs = np.array([5, 0, 3, 3, 1]), np.array([4, 4, 0, 2, 1])
+    got = mg.gather_qmm(bf(x), words(w), bf(s), bf(b), rhs_indices=i32(rhs), lhs_indices=i32(lhs),
+                        group_size=gs, bits=bits)
+    assert got.shape == (5, M, N)
+    want = oracle.gather_qmm(x, w, s, b, lhs=lhs, rhs=rhs, gs=gs, bits=bits)
+    assert_parity(host_bf(got), want, name=f"gather M={M} {bits}/{gs}")
+    h = mg.gather_qmm_glu(bf(x), (words(w), bf(s), bf(b)), (words(wu), bf(su), bf(bu)), i32(rhs),
+                          lhs_indices=i32(lhs), group_size=gs, bits=bits)
+    gg = oracle.bf16_to_f64(want)
+    uu = oracle.bf16_to_f64(oracle.gather_qmm(x, wu, su, bu, lhs=lhs, rhs=rhs, gs=gs, bits=bits))
+    assert_parity(host_bf(h), oracle.f64_to_bf16(oracle.silu(gg) * uu), name=f"gather glu M={M} {bits}/{gs}")

@@ -18,9 +18,10 @@
 // Layout: lane (g = lane / 16, r = lane % 16) supplies activation row r and
 // weight column r of each 16-column block, k = 32 s + 8 g + (0..7) in MFMA
 // step s; it ends with outputs (rows 4 g .. 4 g + 3, column r).  A
-// workgroup (4 waves) owns 16 * NB columns of one pair and a range of
-// 128-wide K chunks, its waves taking interleaved chunks with the loads of
-// the next DEPTH chunks in flight; the waves' partial sums meet in LDS.
+// workgroup (W waves: 4 for GLU pairs, 8 for plain products) owns 16 * NB
+// columns of one pair and a range of 128-wide K chunks, its waves taking
+// interleaved chunks with the loads of the next DEPTH chunks in flight; the
+// waves' partial sums meet in LDS.
 // Loads are buffer loads (the pair's rows and expert matrices in the
 // descriptors, the chunk as a wave-uniform offset), coalesced: neighbouring
 // lanes read neighbouring bytes of one row, and each wave passes its chunk
@@ -56,17 +57,17 @@ MOEGQ_DEV void transpose4(uint32_t t[4]) {
   t[3] = d[1];
 }
 
-template <int BITS, int GS, bool GLU, int NB, int DEPTH>
-__global__ __launch_bounds__(256) void fewrow_kernel(FewArgs A) {
+template <int BITS, int GS, bool GLU, int NB, int DEPTH, int W>
+__global__ __launch_bounds__(64 * W) void fewrow_kernel(FewArgs A) {
   constexpr int NM = GLU ? 2 : 1;
   constexpr int NGC = FR_CK / GS;                      // groups per chunk
   constexpr int SW = (NGC + 1) / 2;                    // 32-bit words of one chunk's scales
   constexpr float OFS = BITS == 4 ? 128.f : 0.f;       // code offset of the bf16 operand
   constexpr int SPG = GS / 32;                         // MFMA steps per group
-  __shared__ f32x4_t red[3][NM][NB][64];
+  __shared__ f32x4_t red[W - 1][NM][NB][64];
   constexpr int PPR = 4 * (BITS / 4);                  // 16-byte code pieces per row and chunk
   constexpr int XS = 16 * 16, CS = NM * NB * 16 * PPR; // a wave's staging area, in pieces
-  __shared__ uint4 few_stage[4 * (XS + CS)];
+  __shared__ uint4 few_stage[W * (XS + CS)];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
@@ -321,22 +322,22 @@ __global__ __launch_bounds__(256) void fewrow_kernel(FewArgs A) {
       }
     }
   };
-  // chunk c of the split belongs to wave (c - c_lo) % 4; the loads of the
+  // chunk c of the split belongs to wave (c - c_lo) % W; the loads of the
   // wave's next DEPTH chunks are in flight while one is computed (a ring of
   // DEPTH + 1 buffers, unrolled so that every buffer index is static; the
   // scheduling barriers keep each chunk's loads in ring order)
   Chunk buf[DEPTH + 1];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) {
-    load(c_lo + wave + 4 * i, buf[i]);
+    load(c_lo + wave + W * i, buf[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int c = c_lo + wave; c < c_hi; c += 4 * (DEPTH + 1)) {
+  for (int c = c_lo + wave; c < c_hi; c += W * (DEPTH + 1)) {
 #pragma unroll
     for (int i = 0; i <= DEPTH; ++i) {
-      load(c + 4 * (i + DEPTH), buf[(i + DEPTH) % (DEPTH + 1)]);
+      load(c + W * (i + DEPTH), buf[(i + DEPTH) % (DEPTH + 1)]);
       __builtin_amdgcn_sched_barrier(0);
-      if (c + 4 * i < c_hi) {
+      if (c + W * i < c_hi) {
         Operands o;
         stage(buf[i], o);
         compute(o);
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(256) void fewrow_kernel(FewArgs A) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int w = 0; w < 3; ++w) acc[m][b] += red[w][m][b][lane];
+      for (int w = 0; w < W - 1; ++w) acc[m][b] += red[w][m][b][lane];
   if (KS > 1) {
     // store this split's partial; the last workgroup of the column group adds
     // all splits in order.  The partials travel as device-scope atomic stores
@@ -425,28 +426,37 @@ __global__ __launch_bounds__(256) void fewrow_kernel(FewArgs A) {
   }
 }
 
-// Splits along K: only when the column groups alone leave CUs idle, and then
-// up to about one workgroup per CU while every wave keeps at least
-// kFewMinChunks chunks to stream.  Each split adds the store / count / reload
-// tail to the critical path; measured on the dense chain's products, filling
-// two workgroups per CU with more splits was slower than one.
+// Workgroup shape and splits along K.  GLU pairs: 4 waves on one 16-column
+// block (twice the workgroups of two blocks: 13.4 against 15.4 us for the
+// 16-row 2 x 9728 x 2560 gate/up).  Plain products: 8 waves (K split over
+// more waves of one workgroup, summed in LDS; one such workgroup per CU is
+// resident) on one block while the blocks fit one workgroup per CU and no
+// wave would stream more than kFewMaxWaveChunks chunks, else on two blocks.
+// K splits over workgroups only when the column groups leave CUs idle, up to
+// about one workgroup per CU while every wave keeps at least kFewMinChunks
+// chunks: each split adds the store / count / reload tail to the critical
+// path.  Measured on the dense chain's 16-row products (us, against 4 waves
+// on two blocks with the split): 2560 x 4096 7.45 (one block, no split)
+// against 8.65, 2560 x 9728 10.66 (two blocks, 3 splits) against 11.31,
+// 6144 x 2560 8.02 (two blocks, no split) against 8.51.
 constexpr int64_t kFewCUs = 256;
-constexpr int64_t kFewResident = 256;
 constexpr int64_t kFewMinChunks = 2;
+constexpr int64_t kFewMaxWaveChunks = 6;
+
+constexpr int few_waves(bool glu) { return glu ? 4 : 8; }
 
 FewPlan fewrow_plan(int64_t P, int64_t N, int64_t K, bool glu, bool split_allowed) {
   FewPlan pl{};
-  // GLU products take one 16-column block per workgroup (twice the
-  // workgroups; 13.4 against 15.4 us for the 16-row 2 x 9728 x 2560 gate/up),
-  // plain products two (one block measured equal or slower there)
-  pl.NB = glu ? 1 : 2;
-  const int64_t ncg = (N + 16 * pl.NB - 1) / (16 * pl.NB);
+  const int64_t W = few_waves(glu);
   const int64_t nchunk = K / FR_CK;
-  const int64_t items = P * ncg;
+  const int64_t items1 = P * ((N + 15) / 16);
+  if (glu) pl.NB = 1;
+  else pl.NB = items1 <= kFewCUs && (nchunk <= W * kFewMaxWaveChunks || !split_allowed) ? 1 : 2;
+  const int64_t items = P * ((N + 16 * pl.NB - 1) / (16 * pl.NB));
   int64_t KS = 1;
-  if (split_allowed && items < kFewCUs) {
-    KS = std::max<int64_t>(1, kFewResident / items);
-    KS = std::min<int64_t>({KS, (int64_t)kFewMaxSplit, std::max<int64_t>(1, nchunk / (4 * kFewMinChunks))});
+  if (split_allowed && items < kFewCUs && (glu || pl.NB == 2)) {
+    KS = std::max<int64_t>(1, kFewCUs / items);
+    KS = std::min<int64_t>({KS, (int64_t)kFewMaxSplit, std::max<int64_t>(1, nchunk / (W * kFewMinChunks))});
   }
   pl.cps = (int)((nchunk + KS - 1) / KS);
   pl.KS = (int)((nchunk + pl.cps - 1) / pl.cps);
@@ -469,11 +479,16 @@ constexpr int few_depth() { return GLU ? (BITS == 8 ? 1 : 2) : (BITS == 8 ? 2 : 
 
 template <int BITS, int GS, bool GLU>
 static hipError_t launch_few_t(const FewArgs& a, int64_t items, int KS, int NB, hipStream_t st) {
-  constexpr int D = few_depth<BITS, GLU>();
-  if (NB == 1)
-    hipLaunchKernelGGL((fewrow_kernel<BITS, GS, GLU, 1, D>), dim3((unsigned)items, (unsigned)KS), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((fewrow_kernel<BITS, GS, GLU, 2, D>), dim3((unsigned)items, (unsigned)KS), dim3(256), 0, st, a);
+  constexpr int D = few_depth<BITS, GLU>(), W = few_waves(GLU);
+  const dim3 grid((unsigned)items, (unsigned)KS), block(64 * W);
+  if constexpr (GLU) {                       // GLU pairs always take one block
+    if (NB != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((fewrow_kernel<BITS, GS, GLU, 1, D, W>), grid, block, 0, st, a);
+  } else if (NB == 1) {
+    hipLaunchKernelGGL((fewrow_kernel<BITS, GS, GLU, 1, D, W>), grid, block, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((fewrow_kernel<BITS, GS, GLU, 2, D, W>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

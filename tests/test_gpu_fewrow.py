@@ -24,7 +24,10 @@ def mg():
 
 
 def _counters_zero(ws, N, glu=False):
-    # one counter per column group: 16 columns for GLU pairs, 32 otherwise
+    # one counter per column group: 16 columns for GLU pairs, 32 for the
+    # plain products that split K; shapes that never split need no workspace
+    if ws is None:
+        return True
     items = -(-N // (16 if glu else 32))
     return not bool(ws[:4 * items].view(torch.int32).any())
 
@@ -33,7 +36,9 @@ def _counters_zero(ws, N, glu=False):
 @pytest.mark.parametrize("bits,gs", [(4, 32), (4, 64), (4, 128), (8, 32), (8, 128)])
 def test_split_k_parity(mg, M, bits, gs):
     g = np.random.default_rng(M * 11 + bits + gs)
-    N, K = 96, 4096                       # 3 column groups, 32 K chunks: K split 8 ways
+    # 64 K chunks: two-block workgroups of plain products (3 column groups),
+    # K split 4 ways; without a workspace one block per workgroup, no split
+    N, K = 96, 8192
     w, s, b = synth.minmax_matrix(g, N, K, gs, bits, scale=1 / np.sqrt(K))
     x = synth.to_bf16(g.standard_normal((M, K)))
     want = oracle.quantized_matmul(x, w, s, b, True, gs, bits)
@@ -55,9 +60,12 @@ def test_split_k_parity(mg, M, bits, gs):
 
 @pytest.mark.parametrize("M", [2, 5, 16])
 @pytest.mark.parametrize("bits,gs", [(4, 64), (8, 128)])
-def test_split_k_integer_exact(mg, M, bits, gs):
-    g = np.random.default_rng(300 + M + bits)
-    N, K = 160, 2048
+@pytest.mark.parametrize("K", [2048, 8192])
+def test_split_k_integer_exact(mg, M, bits, gs, K):
+    """Bit for bit on integer-exact inputs: K = 2048 on one-block 8-wave
+    workgroups, K = 8192 split over two-block workgroups."""
+    g = np.random.default_rng(300 + M + bits + K)
+    N = 160
     w, s, b = synth.integer_exact(g, N, K, gs, bits)
     x = synth.integer_x(g, M, K, amp=3)
     want = oracle.quantized_matmul(x, w, s, b, True, gs, bits)

@@ -103,8 +103,9 @@ MOEGQ_DEV bf16x8_t deq_operand_bf16(uint32_t w0, uint32_t w1, float s, float c) 
   return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-// One tile: rows r0 .. r1 - 1 of expert e, MFMA columns n0 .. n0 + 255.  lds
-// holds the activation ring: RA stages of 16 * MI rows x TM_K 16-bit values.
+// One tile: rows r0 .. r1 - 1 of expert e, MFMA columns n0 .. n0 + 255.
+// Four distinct __shared__ arrays L[0..3] of LQ halfs each hold the
+// activation ring: RA stages of 16 * MI rows x TM_K 16-bit values.
 template <int MI, int BITS = 4> struct MmaRing {
   // K steps of activation (LDS) and code (register) prefetch: one for 128-row
   // tiles and for bf16 weights (register-bound), three for the shorter tiles
@@ -113,6 +114,7 @@ template <int MI, int BITS = 4> struct MmaRing {
   static constexpr int RA = PDA + 1, RB = PDB + 1;              // LDS and register ring stages
   static constexpr int U = (RA % RB == 0) ? RA : (RB % RA == 0) ? RB : RA * RB;   // steps per unrolled loop
   static constexpr int HALFS = RA * 16 * MI * TM_K;
+  static constexpr int LQ = (MI >= 8 ? 64 : 16 * MI) * TM_K;     // halfs per ring array
 };
 
 // Operand precision per pass:
@@ -135,24 +137,53 @@ template <int MI, int BITS = 4> struct MmaRing {
 //    their words go to the MFMA as loaded.
 // xe_s: LDS for 16 * MI row exponents (gate/up pass).
 template <int BITS, int GS, bool GLU, int MI>
-MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, int r1, int e, int n0) {
+MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* L0, uint16_t* L1, uint16_t* L2, uint16_t* L3, int* xe_s,
+                         int r0, int r1, int e, int n0) {
   constexpr bool W16 = BITS == 16;
   constexpr bool F16 = GLU && !W16;
   constexpr int CB = 4 * BITS;                    // code bytes per lane per K step (32 codes)
   using Ring = MmaRing<MI, BITS>;
   constexpr int PDA = Ring::PDA, PDB = Ring::PDB, RA = Ring::RA, RB = Ring::RB, U = Ring::U;
-  constexpr int STAGE = 16 * MI * TM_K;           // halfs per ring stage
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
+  // The ring in four quarters L[0..3] of LQ halfs, which the compiler keeps
+  // apart when it places its own waits if they are distinct __shared__
+  // arrays: with the ring in one array it made a step's LDS reads wait for
+  // the activation loads just issued into another stage, so the step's MFMAs
+  // waited for the next step's rows.  RA = 4 (32- and 64-row tiles): stage s
+  // in L[s].  RA = 2, 128 rows: stage s in L[2 s] (rows 0-63) and L[2 s + 1]
+  // (rows 64-127), and each wave fills 16 rows of each half (so that every
+  // load's array is a compile-time constant).  The 8-bit kernels, at the
+  // register limit, keep the ring in one array (L[k] its quarters), a wave
+  // filling 32 consecutive rows, the barrier's release fence and the window
+  // loads in the switching step: each of these changes moved their spills
+  // into the loop (3.37 against 2.96 ms for the 4123-row 8-bit layer).
+  static_assert(RA * 16 * MI <= 4 * (MI >= 8 ? 64 : 16 * MI) && (MI < 8 || RA == 2), "ring layout");
+  constexpr bool HALVES = MI >= 8 && BITS == 4;
+  auto ring = [&](int k) -> uint16_t* { return k == 0 ? L0 : k == 1 ? L1 : k == 2 ? L2 : L3; };
+  // row of the tile (without the lane group's g) that load v of this wave fills
+  auto row_of = [&](int v) -> int {
+    if constexpr (HALVES) return v < 4 ? 16 * wave + 4 * v : 64 + 16 * wave + 4 * (v - 4);
+    else return 4 * (MI * wave + v);
+  };
+  // destination of load v in stage st, and row block i (16 rows) of stage st
+  auto dma_dst = [&](int st, int v) -> uint16_t* {
+    if constexpr (HALVES) return ring(2 * st + v / 4) + (row_of(v) % 64) * TM_K;
+    else return ring(MI >= 8 ? 2 * st : st) + row_of(v) * TM_K;
+  };
+  auto row_blk = [&](int st, int i) -> const uint16_t* {
+    if constexpr (HALVES) return ring(2 * st + i / 4) + (i % 4) * 16 * TM_K;
+    else return ring(MI >= 8 ? 2 * st : st) + i * 16 * TM_K;
+  };
   const int N = A.N, K = A.K;
   const int Kw = K * BITS / 32, G = K / GS;
   r0 = __builtin_amdgcn_readfirstlane(r0);
   r1 = __builtin_amdgcn_readfirstlane(r1);
   e = __builtin_amdgcn_readfirstlane(e);
 
-  // ---- activation loads: wave w, load v covers rows 4 (MI w + v) .. + 3; lane
-  //      (g, c16) fetches chunk c16 ^ (row % 16) of row 4 (MI w + v) + g
+  // ---- activation loads: load v of a wave covers rows row_of(v) .. + 3; lane
+  //      (g, c16) fetches chunk c16 ^ lds_swz(row) of row row_of(v) + g
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A.x, 0xFFFFFFFFu);
   uint32_t a_off[8];                          // MI <= 8 entries used
   // virtual row rr = batch rr / rpb, row rr % rpb of it; the batch's x rows start at
@@ -164,7 +195,7 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
   const int rpb = batched ? (int)A.rows_per_batch : 1;
 #pragma unroll
   for (int v = 0; v < MI; ++v) {
-    rr[v] = min(r0 + 4 * (MI * wave + v) + g, r1 - 1);   // rows past the tile repeat a valid row (never stored)
+    rr[v] = min(r0 + row_of(v) + g, r1 - 1);   // rows past the tile repeat a valid row (never stored)
     bt[v] = batched ? rr[v] / rpb : rr[v];
   }
   if (A.lhs) {
@@ -177,11 +208,11 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
 #pragma unroll
   for (int v = 0; v < MI; ++v) {
     const int src = batched ? bt[v] * rpb + rr[v] % rpb : bt[v];
-    const int chunk = c16 ^ lds_swz(4 * (MI * wave + v) + g);
+    const int chunk = c16 ^ lds_swz(row_of(v) + g);
     a_off[v] = (uint32_t)src * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
     // the row exponents of the fp16 activations, for the epilogue (row-major
     // position in the tile; one lane per row writes)
-    if (F16 && c16 == 0) xe_s[4 * (MI * wave + v) + g] = A.xexp[src];
+    if (F16 && c16 == 0) xe_s[row_of(v) + g] = A.xexp[src];
   }
   // ---- code / scale loads: column block j of this wave
   const size_t wstride = (size_t)N * Kw, sstride = (size_t)N * G;
@@ -275,7 +306,7 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
     constexpr int AV = (MI + 3) / 4;
 #pragma unroll
     for (int v = part * AV; v < (part + 1) * AV && v < MI; ++v) {
-      uint16_t* dst = lds + sa * STAGE + 4 * (MI * wave + v) * TM_K;
+      uint16_t* dst = dma_dst(sa, v);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, a_off[v],
                                                (uint32_t)t * TM_K * 2u, 0, 0);
     }
@@ -293,16 +324,56 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
     // loads after them (the compiler may move a step's loads within the step's first
     // sub-step, never across the scheduling barrier that ends that sub-step; extra window
     // loads only lengthen the wait)
+    // Other waves read the rows this wave loaded, so its own loads of step ks
+    // must be complete before it reaches the barrier: nothing but this wait
+    // ensures that.  Steps past the end issue no loads, so near the end fewer
+    // loads follow step ks's and the count shrinks with them.  lgkmcnt(0)
+    // completes this wave's LDS writes (the row exponents) before the barrier.
     constexpr int VM = (PDA - 1) * LPS;
-    static_assert(VM < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (VM & 15) | ((VM >> 4) << 14));
-    __syncthreads();                      // every wave's rows landed; the stage of step ks - 1 is free
+    static_assert(VM < 64 && (PDA == 1 || PDA == 3), "vmcnt range");
+    auto wait_vm = [](auto n) {
+      constexpr int c = decltype(n)::value;
+      __builtin_amdgcn_s_waitcnt(0x0070 | (c & 15) | ((c >> 4) << 14));
+    };
+    if constexpr (BITS == 8) {
+      // the 8-bit kernels keep the barrier's release fence, which completes
+      // every load into LDS before the barrier anyway
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (VM & 15) | ((VM >> 4) << 14));
+    } else if (PDA == 1 || ks + PDA - 1 < nK) {
+      wait_vm(std::integral_constant<int, VM>{});
+    } else if (ks + 1 < nK) {
+      wait_vm(std::integral_constant<int, LPS>{});
+    } else {
+      wait_vm(std::integral_constant<int, 0>{});
+    }
+    // every wave's rows landed (each wave's own wait above) and every wave
+    // has consumed its reads of step ks - 1's stage (each LDS read feeds an
+    // MFMA of its step), so that stage is free.  The barrier takes no
+    // release fence (8-bit codes aside): one would make it wait for every
+    // LDS-bound load in flight, including those of later steps; the acquire
+    // keeps this step's LDS reads after the barrier.
+    if constexpr (BITS == 8) {
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
     f16x2_t s2[4], b2[4];
     float sj[4], cj[4];
     if constexpr (!W16) {
-      if (ks % WSTEPS == 0) {
+      // the next window is requested a step after the switch (8-bit codes
+      // aside): its loads then write nwin's registers directly (issued in the
+      // switching step, they went through temporaries whose copy waited for
+      // them)
+      if (BITS == 8) {
+        if (ks % WSTEPS == 0) {
+          win_s = nwin_s; win_b = nwin_b;
+          if ((ks + WSTEPS) < nK) load_win(ks / WSTEPS + 1, nwin_s, nwin_b);
+        }
+      } else if (ks % WSTEPS == 0) {
         win_s = nwin_s; win_b = nwin_b;
-        if ((ks + WSTEPS) < nK) load_win(ks / WSTEPS + 1, nwin_s, nwin_b);
+      } else if (ks % WSTEPS == 1 && (ks - 1 + WSTEPS) < nK) {
+        load_win(ks / WSTEPS + 1, nwin_s, nwin_b);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -315,7 +386,7 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
         }
       }
     }
-    const uint16_t* base = lds + sa * STAGE + c16 * TM_K;
+
     // every load of step ks + PD at the step's start, so that each has a
     // whole step to land (issued a quarter per sub-step, the last quarter
     // had a quarter of a step: 3% slower at the 2048-row layer)
@@ -339,7 +410,7 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
       const int slot = (4 * g + s) ^ lds_swz(c16);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        const uint4 a = *reinterpret_cast<const uint4*>(base + i * 16 * TM_K + slot * 8);
+        const uint4 a = *reinterpret_cast<const uint4*>(row_blk(sa, i) + c16 * TM_K + slot * 8);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (F16)
@@ -459,15 +530,16 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, in
 // smaller bodies need no more LDS than the 128-row one.  With 8-bit codes the
 // extra bodies push the kernel's registers into spills, so it keeps one body.
 template <int BITS, int GS, bool GLU, int MI>
-MOEGQ_DEV void tile_rows(const TileArgs& A, uint16_t* lds, int* xe_s, int r0, int r1, int e, int n0) {
+MOEGQ_DEV void tile_rows(const TileArgs& A, uint16_t* L0, uint16_t* L1, uint16_t* L2, uint16_t* L3, int* xe_s,
+                         int r0, int r1, int e, int n0) {
   const int nrow = __builtin_amdgcn_readfirstlane(r1 - r0);
   if constexpr (MI == 8 && BITS == 4) {
-    static_assert(MmaRing<4, BITS>::HALFS <= MmaRing<8, BITS>::HALFS &&
-                  MmaRing<2, BITS>::HALFS <= MmaRing<8, BITS>::HALFS, "LDS ring");
-    if (nrow <= 32) return tile_body<BITS, GS, GLU, 2>(A, lds, xe_s, r0, r1, e, n0);
-    if (nrow <= 64) return tile_body<BITS, GS, GLU, 4>(A, lds, xe_s, r0, r1, e, n0);
+    static_assert(MmaRing<4, BITS>::LQ <= MmaRing<8, BITS>::LQ && MmaRing<2, BITS>::LQ <= MmaRing<8, BITS>::LQ,
+                  "LDS ring");
+    if (nrow <= 32) return tile_body<BITS, GS, GLU, 2>(A, L0, L1, L2, L3, xe_s, r0, r1, e, n0);
+    if (nrow <= 64) return tile_body<BITS, GS, GLU, 4>(A, L0, L1, L2, L3, xe_s, r0, r1, e, n0);
   }
-  tile_body<BITS, GS, GLU, MI>(A, lds, xe_s, r0, r1, e, n0);
+  tile_body<BITS, GS, GLU, MI>(A, L0, L1, L2, L3, xe_s, r0, r1, e, n0);
 }
 
 // XCD-contiguous ranges: the hardware deals workgroups to the 8 XCDs round
@@ -479,12 +551,25 @@ MOEGQ_DEV int xcd_remap(int b, int total) {
   return b < 8 * q ? (b % 8) * q + b / 8 : b;
 }
 
+// The activation ring's quarters L0..L3 (tile_body): four distinct arrays,
+// or with 8-bit codes the quarters of one array.
+#define RING_ARRAYS(LQ)                                                            \
+  __shared__ __attribute__((aligned(16))) uint16_t RA0[BITS == 8 ? 4 * (LQ) : (LQ)]; \
+  __shared__ __attribute__((aligned(16))) uint16_t RA1[BITS == 8 ? 1 : (LQ)];        \
+  __shared__ __attribute__((aligned(16))) uint16_t RA2[BITS == 8 ? 1 : (LQ)];        \
+  __shared__ __attribute__((aligned(16))) uint16_t RA3[BITS == 8 ? 1 : (LQ)];        \
+  uint16_t* const L0 = RA0;                                                          \
+  uint16_t* const L1 = BITS == 8 ? RA0 + (LQ) : RA1;                                 \
+  uint16_t* const L2 = BITS == 8 ? RA0 + 2 * (LQ) : RA2;                             \
+  uint16_t* const L3 = BITS == 8 ? RA0 + 3 * (LQ) : RA3
+
 // register budget: 2 workgroups per CU (128 accumulators per lane at MI = 8;
 // the 32-row variant needs far fewer registers)
 template <int BITS, int GS, bool GLU, int MI>
 __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
   constexpr int NF = GLU ? TM_C / 2 : TM_C;      // output features per tile
-  __shared__ __attribute__((aligned(16))) uint16_t As[MmaRing<MI, BITS>::HALFS];
+  constexpr int LQ = MmaRing<MI, BITS>::LQ;
+  RING_ARRAYS(LQ);
   __shared__ int xe_s[16 * MI];
   const int NB = (A.N + NF - 1) / NF;
   const int total = A.tile_mode == 2 ? (int)gridDim.x : *A.n_tiles * NB;
@@ -501,7 +586,7 @@ __global__ __launch_bounds__(256, 2) void tile_mma_kernel(TileArgs A) {
     const int32_t* t = A.tiles + 3 * tile;
     r0 = t[0]; e = t[1]; r1 = r0 + t[2];
   }
-  tile_rows<BITS, GS, GLU, MI>(A, As, xe_s, r0, r1, e, n0);
+  tile_rows<BITS, GS, GLU, MI>(A, L0, L1, L2, L3, xe_s, r0, r1, e, n0);
 }
 
 // Both tile tables in one launch: blocks [0, n_big * NB) take the 128-row
@@ -513,9 +598,8 @@ template <int BITS, int GS, bool GLU>
 __global__ __launch_bounds__(256, 2) void tile_mma_dual_kernel(TileArgs A) {
   constexpr int NF = GLU ? TM_C / 2 : TM_C;
   constexpr int MIB = BITS == 16 ? 4 : 8;   // bf16 weights: 64-row big tiles (register budget)
-  constexpr int HALFS = MmaRing<MIB, BITS>::HALFS > MmaRing<2, BITS>::HALFS ? MmaRing<MIB, BITS>::HALFS
-                                                                           : MmaRing<2, BITS>::HALFS;
-  __shared__ __attribute__((aligned(16))) uint16_t As[HALFS];
+  constexpr int LQ = MmaRing<MIB, BITS>::LQ > MmaRing<2, BITS>::LQ ? MmaRing<MIB, BITS>::LQ : MmaRing<2, BITS>::LQ;
+  RING_ARRAYS(LQ);
   __shared__ int xe_s[16 * MIB];
   const int NB = (A.N + NF - 1) / NF;
   const int nbig = *A.n_tiles * NB, nsmall = *A.n_tiles2 * NB;
@@ -523,11 +607,11 @@ __global__ __launch_bounds__(256, 2) void tile_mma_dual_kernel(TileArgs A) {
   if (b < nbig) {
     const int bid = xcd_remap(b, nbig);
     const int32_t* t = A.tiles + 3 * (bid / NB);
-    tile_rows<BITS, GS, GLU, MIB>(A, As, xe_s, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
+    tile_rows<BITS, GS, GLU, MIB>(A, L0, L1, L2, L3, xe_s, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
   } else if (b < nbig + nsmall) {
     const int bid = b - nbig;
     const int32_t* t = A.tiles2 + 3 * (bid / NB);
-    tile_body<BITS, GS, GLU, 2>(A, As, xe_s, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
+    tile_body<BITS, GS, GLU, 2>(A, L0, L1, L2, L3, xe_s, t[0], t[0] + t[2], t[1], (bid % NB) * NF);
   }
 }
 

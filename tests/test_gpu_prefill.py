@@ -220,6 +220,52 @@ def test_moe_prefill_repeatable(mg):
         assert np.array_equal(o, outs[0])
 
 
+def test_large_hybrid_repeatable(mg):
+    """The sorted SwitchGLU at the large shape (713 rows: hot experts in
+    128-row tiles, partly filled tiles in the 64- and 32-row bodies, tail
+    experts in 32-row tiles) gives the same bits on every call, eager and
+    replayed as a HIP graph.  Regression: in the last steps of the short
+    tiles fewer loads follow a step's own, and a step wait that did not
+    shrink with them let a wave reach the barrier with its rows still in
+    flight into LDS, where the other waves read them."""
+    sh = synth.LARGE4
+    dev = torch.device("cuda")
+    gate, up, down = synth.device_expert_set(dev, 4, sh.E, sh.H, sh.I, sh.gs, sh.bits)
+    T = 713
+    idx_np, _ = synth.zipf_routing(4, T, sh.E, sh.top_k)
+    idx = torch.from_numpy(idx_np).to(dev)
+    x = bf(synth.activations(4, T, sh.H))
+    y = torch.empty((T * sh.top_k, sh.H), dtype=torch.bfloat16, device=dev)
+    inv = torch.empty(T * sh.top_k, dtype=torch.int32, device=dev)
+
+    def run():
+        mg.switch_glu(x, idx, gate, up, down, group_size=sh.gs, bits=sh.bits, mode=mg.MODE_SORTED,
+                      tile_mode=0, bm=0, y=y, inv=inv)
+
+    run()
+    torch.cuda.synchronize()
+    ref = y.clone()
+    for _ in range(6):
+        y.zero_()
+        run()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for _ in range(6):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
+
+
 @pytest.mark.parametrize("T", [1, 4, 37])
 def test_moe_prefill_few_tokens(mg, T):
     """The whole-layer entry point with fewer tokens than one tile (every

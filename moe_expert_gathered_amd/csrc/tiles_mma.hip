@@ -113,7 +113,6 @@ template <int MI, int BITS = 4> struct MmaRing {
   static constexpr int PDB = PDA;
   static constexpr int RA = PDA + 1, RB = PDB + 1;              // LDS and register ring stages
   static constexpr int U = (RA % RB == 0) ? RA : (RB % RA == 0) ? RB : RA * RB;   // steps per unrolled loop
-  static constexpr int HALFS = RA * 16 * MI * TM_K;
   static constexpr int LQ = (MI >= 8 ? 64 : 16 * MI) * TM_K;     // halfs per ring array
 };
 
@@ -386,7 +385,6 @@ MOEGQ_DEV void tile_body(const TileArgs& A, uint16_t* L0, uint16_t* L1, uint16_t
         }
       }
     }
-
     // every load of step ks + PD at the step's start, so that each has a
     // whole step to land (issued a quarter per sub-step, the last quarter
     // had a quarter of a step: 3% slower at the 2048-row layer)

@@ -625,6 +625,9 @@ def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=10, warmup=2
                                    "gu": (inter, hid, True), "dn": (hid, inter, False)}.items()}
     for M in rows:
         h0 = torch.randn((M, d["hidden"]), device=dev).to(torch.bfloat16)
+        # the last layer writes into a fixed buffer, so that graph replays can
+        # be checked against an eager forward
+        h_out = torch.empty((M, d["hidden"]), dtype=torch.bfloat16, device=dev)
 
         def fwd():
             h = h0.clone()
@@ -636,7 +639,8 @@ def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=10, warmup=2
                                  workspace=ws["o"])
                 x = m.rms_norm(h, nw)
                 a = m.affine_qmm_glu(x, L["g"], L["u"], group_size=gs, bits=bits, workspace=ws["gu"])
-                h = m.affine_qmm(a, *L["dn"], group_size=gs, bits=bits, residual=h, workspace=ws["dn"])
+                h = m.affine_qmm(a, *L["dn"], group_size=gs, bits=bits, residual=h, workspace=ws["dn"],
+                                 out=h_out if li == d["layers"] - 1 else None)
             return h
 
         for _ in range(warmup):
@@ -650,7 +654,7 @@ def dense_leg(torch, m, synth, rows=(1, 4, 16), bits=4, gs=64, reps=10, warmup=2
             ts.append(time.perf_counter() - t0)
         # the same forward captured once as a HIP graph: kernel time without the
         # per-call host work of ~300 launches from Python
-        fst = graph_stats(torch, lambda i: fwd(), 1, reps=reps)
+        fst = graph_stats(torch, lambda i: fwd(), 1, reps=reps, check=lambda: h_out)
         g_s = fst.median * 1e-6
         res[f"rows{M}"] = {"ms_per_forward": g_s * 1e3, "ms_stats": fst.as_dict(1e-3, "ms"), "gbs": per_fwd / g_s / 1e9,
                            "hbm_frac": per_fwd / g_s / (HBM_PEAK_GBS * 1e9), "timing": "hip graph of one forward"}

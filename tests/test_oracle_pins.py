@@ -623,6 +623,31 @@ def test_shared_expert_gate_closed_form():
     assert np.array_equal(full, oracle.f64_to_bf16(oracle.bf16_to_f64(swiglu) / 2))
 
 
+def test_shared_expert_gate_saturates_the_right_way():
+    # gate row with scale 0 and bias 1 -> z = sum_k x_k; a constant row x = +-0.3125 over
+    # H = 128 gives z = +-40 exactly.  sigmoid(40) = 1 - 4e-18, so the gated output is the
+    # SwiGLU output itself; sigmoid(-40) = 4e-18, so it is below 1e-17 of it (a sign slip
+    # in the exponent swaps the two)
+    g = np.random.default_rng(16)
+    H, I = 128, 64
+    gate, up, down, grow = (synth.drawn_matrix(g, I, H, 64, 4), synth.drawn_matrix(g, I, H, 64, 4),
+                            synth.drawn_matrix(g, H, I, 64, 4), synth.drawn_matrix(g, 1, H, 64, 4))
+    one = synth.to_bf16(np.ones(1))[0]
+    grow1 = (grow[0], np.zeros_like(grow[1]), np.full_like(grow[2], one))
+    experts = [tuple(a[None] for a in m) for m in (gate, up, down)]
+    for c in (0.3125, -0.3125):
+        x = synth.to_bf16(np.full((2, H), c))
+        assert np.array_equal(oracle.bf16_to_f64(oracle.quantized_matmul(x, *grow1, True, 64, 4)),
+                              np.full((2, 1), 128 * c))
+        full = oracle.bf16_to_f64(oracle.shared_expert(x, gate, up, down, grow1, 64, 4))
+        swiglu = oracle.bf16_to_f64(oracle.switch_glu(x, np.zeros((2, 1), np.int32), *experts, gs=64, bits=4)[:, 0])
+        assert np.abs(swiglu).max() > 0
+        if c > 0:
+            assert np.array_equal(full, swiglu)
+        else:
+            assert np.all(np.abs(full) <= 1e-17 * np.abs(swiglu))
+
+
 def test_dense_forward_constant_weights_closed_form():
     """One layer with constant weights (scale 0, bias c): every projection is
     c * sum(input) broadcast along N, so the chain reduces to scalars per row."""

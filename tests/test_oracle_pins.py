@@ -623,6 +623,18 @@ def test_shared_expert_gate_closed_form():
     assert np.array_equal(full, oracle.f64_to_bf16(oracle.bf16_to_f64(swiglu) / 2))
 
 
+def test_silu_against_torch():
+    # SwitchGLU's activation (MLX issue 4509, moe(): silu(gate) * up) against torch's float64
+    # silu over every bf16 value of magnitude up to 100, both signs
+    import torch
+    v = np.arange(0, 0x42C9, dtype=np.uint32).astype(np.uint16)
+    g = np.concatenate([oracle.bf16_to_f64(v), -oracle.bf16_to_f64(v)])
+    want = torch.nn.functional.silu(torch.from_numpy(g)).numpy()
+    got = oracle.silu(g)
+    assert np.all(np.abs(got - want) <= 4e-16 * np.abs(want) + 1e-300)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0 and oracle.silu(np.array([50.0]))[0] == 50.0
+
+
 def test_shared_expert_gate_saturates_the_right_way():
     # gate row with scale 0 and bias 1 -> z = sum_k x_k; a constant row x = +-0.3125 over
     # H = 128 gives z = +-40 exactly.  sigmoid(40) = 1 - 4e-18, so the gated output is the
